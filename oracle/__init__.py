@@ -1,0 +1,115 @@
+"""CPU oracle for the W4A16 skinny matmul -- TEST INFRASTRUCTURE ONLY.
+
+Thin ctypes wrappers over oracle/oracle.c (plain C, double precision).  Only
+tests/, the smoke check and the bench's CPU baseline leg may import this
+package; the GPU library never does, and the oracle never imports it.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(HERE, "liboracle.so")
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        lib.oracle_bf16.argtypes = [ctypes.c_uint16]
+        lib.oracle_bf16.restype = ctypes.c_double
+        lib.oracle_code.argtypes = [vp, i64]
+        lib.oracle_code.restype = i32
+        lib.oracle_matmul.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, i32]
+        lib.oracle_gather.argtypes = [vp, i64, vp, vp, i64, vp, i64, i32, vp, vp, i32]
+        lib.oracle_matmul_dequant_first.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+        lib.oracle_argmax.argtypes = [vp, vp, i64, i32, vp, vp, vp]
+        _lib = lib
+    return _lib
+
+
+def _c(a, dtype):
+    a = np.ascontiguousarray(a, dtype=dtype)
+    return a, a.ctypes.data
+
+
+def default_threads() -> int:
+    return max(1, os.cpu_count() or 1)
+
+
+def matmul(packed, scales, x, nthreads: int | None = None, want_abs: bool = True):
+    """y[T][N] (float64) and A[T][N] = sum_k |w*x| for the whole matrix."""
+    packed, pp = _c(packed, np.uint8)
+    scales, sp = _c(scales, np.uint16)
+    x, xp = _c(x, np.uint16)
+    N = packed.shape[0]
+    K = packed.shape[1] * 2
+    T = x.shape[0]
+    assert x.shape[1] == K and scales.shape == (N, K // 128)
+    y = np.empty((T, N), np.float64)
+    a = np.empty((T, N), np.float64) if want_abs else None
+    _load().oracle_matmul(pp, sp, xp, N, K, T, y.ctypes.data, a.ctypes.data if a is not None else None,
+                          nthreads or default_threads())
+    return y, a
+
+
+def gather(row_ids, packed, scales, x, nthreads: int | None = None):
+    """y[T][n_ids] and A[T][n_ids] for weight rows row_ids[i] (NaN if out of range)."""
+    row_ids, rp = _c(row_ids, np.int32)
+    packed, pp = _c(packed, np.uint8)
+    scales, sp = _c(scales, np.uint16)
+    x, xp = _c(x, np.uint16)
+    n_rows = packed.shape[0]
+    K = packed.shape[1] * 2
+    T = x.shape[0]
+    n = row_ids.shape[0]
+    y = np.empty((T, n), np.float64)
+    a = np.empty((T, n), np.float64)
+    _load().oracle_gather(rp, n, pp, sp, n_rows, xp, K, T, y.ctypes.data, a.ctypes.data,
+                          nthreads or default_threads())
+    return y, a
+
+
+def matmul_dequant_first(packed, scales, x):
+    packed, pp = _c(packed, np.uint8)
+    scales, sp = _c(scales, np.uint16)
+    x, xp = _c(x, np.uint16)
+    N = packed.shape[0]
+    K = packed.shape[1] * 2
+    T = x.shape[0]
+    y = np.empty((T, N), np.float64)
+    _load().oracle_matmul_dequant_first(pp, sp, xp, N, K, T, y.ctypes.data)
+    return y
+
+
+def argmax(y, ids=None):
+    """Per row t of y[T][n]: (id, value, gap to the best other id)."""
+    y, yp = _c(y, np.float64)
+    T, n = y.shape
+    if ids is not None:
+        ids, ip = _c(ids, np.int32)
+        assert ids.shape == (n,)
+    else:
+        ip = None
+    out_id = np.empty(T, np.int32)
+    out_val = np.empty(T, np.float64)
+    gap = np.empty(T, np.float64)
+    _load().oracle_argmax(yp, ip, n, T, out_id.ctypes.data, out_val.ctypes.data, gap.ctypes.data)
+    return out_id, out_val, gap
+
+
+def bf16(bits: int) -> float:
+    return float(_load().oracle_bf16(bits))
+
+
+def code(packed_row, k: int) -> int:
+    packed_row, p = _c(packed_row, np.uint8)
+    return int(_load().oracle_code(p, k))

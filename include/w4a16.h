@@ -1,0 +1,134 @@
+/*
+ * w4a16.h -- C ABI of the W4A16 skinny matmul for speculative-verify decode
+ * (AMD Instinct MI355X, gfx950).
+ *
+ * The operation.  Single-stream decode reads every weight once per cycle and
+ * verifies T = 1 + n_draft tokens against it (qwen-warp/llamAmpere article,
+ * "The arithmetic every claim answers to": decode is a weight read, and a
+ * verify pass costs about the same as a one-token pass when the kernel reads
+ * the weights once for all T rows).  Weights are W4A16 with group 128, in the
+ * format that article describes under "qwen-warp: keep the activations in
+ * bf16": 4-bit codes packed as little-endian words of eight nibbles, level =
+ * code - 8, one bf16 scale per 128 columns of a row.  For T activation rows
+ * x (bf16) the library computes, in fp32,
+ *
+ *     y[t][n] = sum_k (q[n][k] - 8) * scale[n][k/128] * x[t][k].
+ *
+ * Each level (q - 8) and each product with x is formed exactly; sums are fp32,
+ * with a fresh partial per 128-column group multiplied by that group's scale
+ * (the same section: the group scale is applied in fp32 after each group's
+ * accumulate).  Results agree with the exact sum within
+ * 1e-3 * sum_k |w*x| + 1e-6 per element.
+ *
+ * Layout (all row-major, all device memory owned by the caller):
+ *   packed_u4    uint8   [rows][K/2]    byte j of a row holds column 2j in bits
+ *                                       0-3 and column 2j+1 in bits 4-7
+ *   scales_bf16  uint16  [rows][K/128]  bf16 bit patterns
+ *   x_bf16       uint16  [T][K]         bf16 bit patterns
+ *   y_f32        float   [T][n_out]
+ *
+ * Conventions for every entry point:
+ *   - All work is enqueued on `stream` (0 = the null stream); the call returns
+ *     before the GPU finishes.  Results are valid after the caller synchronises.
+ *   - All arguments are checked on the host before anything is enqueued; on
+ *     any status other than W4A16_OK and W4A16_ERR_HIP nothing was enqueued.
+ *     W4A16_ERR_HIP means a HIP runtime call failed (the launch itself or a
+ *     device query).
+ *   - No allocation, no synchronisation, no printing, no state kept between
+ *     calls.  Outputs must not alias inputs or each other.
+ *   - Thread-safe; calls on different streams may run concurrently.
+ *   - Activations should be finite; a non-finite x gives non-finite outputs
+ *     for the rows it reaches.
+ */
+#ifndef W4A16_H
+#define W4A16_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#ifndef HIP_INCLUDE_HIP_HIP_RUNTIME_API_H
+typedef struct ihipStream_t* hipStream_t; /* same definition as the HIP runtime's */
+#endif
+
+#define W4A16_GROUP 128      /* columns per bf16 scale */
+#define W4A16_MAX_T 8        /* activation rows per weight read */
+#define W4A16_ABI_VERSION 1
+
+typedef enum {
+  W4A16_OK = 0,
+  W4A16_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
+  W4A16_ERR_BAD_SHAPE = 2,    /* a size is out of range (see each call) */
+  W4A16_ERR_MISALIGNED = 3,   /* packed_u4 / x_bf16 not 16-byte aligned, scales not 2, y / ids / argmax not 4 */
+  W4A16_ERR_WORKSPACE = 4,    /* argmax requested with no or too small a workspace */
+  W4A16_ERR_UNSUPPORTED = 5,  /* the current device is not gfx950 */
+  W4A16_ERR_HIP = 6,          /* a HIP runtime call returned an error */
+  W4A16_ERR_BAD_VARIANT = 7   /* unknown kernel variant */
+} w4a16_status;
+
+/* Kernel variants.  Both compute the same values within the tolerance above;
+ * AUTO picks per T the one measured faster on MI355X. */
+typedef enum {
+  W4A16_VARIANT_AUTO = 0,
+  W4A16_VARIANT_DOT = 1, /* VALU dot products, split-K across lanes, cross-lane reduction */
+  W4A16_VARIANT_MFMA = 2 /* fp16 matrix cores, tokens padded to 16, split-K across waves */
+} w4a16_variant;
+
+/*
+ * y = x * W^T for one weight matrix.
+ *   N  output rows, 1 <= N <= 2^31-1
+ *   K  reduction length, a multiple of 128, 128 <= K <= 2^20
+ *   T  activation rows, 1 <= T <= W4A16_MAX_T
+ */
+w4a16_status w4a16_matmul(const uint8_t* packed_u4, const uint16_t* scales_bf16, const uint16_t* x_bf16,
+                          float* y_f32, int64_t N, int64_t K, int32_t T, hipStream_t stream);
+
+/*
+ * Scores a subset of the rows of an output head (e.g. the lm_head) and
+ * optionally takes the per-row argmax.  Follows the draft head of the
+ * swift-qwen3.8-rtx3090 project page ("Body, heads and drafter": a slice of
+ * the lm_head with rows only for the draft-vocabulary tokens) and the OpenJet
+ * engine page ("How it gets its speed": the draft head restricted to a token
+ * list; verification still scores the full vocabulary).
+ *
+ *   row_ids   int32 [n_ids] device ids into [0, n_rows); output row i uses
+ *             weight row row_ids[i].  NULL means the identity, n_ids = n_rows
+ *             (the full head).  Duplicates are allowed.  An id outside
+ *             [0, n_rows) yields a NaN output row that never wins the argmax.
+ *   y_f32     [T][n_ids] in row_ids order, or NULL to skip writing scores.
+ *   argmax_id / argmax_val  [T] each, or both NULL.  For each t: the largest
+ *             non-NaN score and the lowest vocabulary id (row_ids value)
+ *             attaining it -- greedy acceptance is an argmax equality over the
+ *             verify rows (article section "What each one calls the same
+ *             answer").  No valid row: id -1, value NaN.
+ *   workspace device scratch of at least w4a16_workspace_bytes(n_ids, T) bytes
+ *             (16-byte aligned), required when argmax is requested; its
+ *             contents need no initialisation and are meaningless afterwards.
+ *   Shapes: 1 <= n_ids, n_rows <= 2^31-1; K and T as for w4a16_matmul.
+ *   At least one of y_f32 and argmax_id must be non-NULL.
+ */
+w4a16_status w4a16_head_gather(const int32_t* row_ids, int64_t n_ids, const uint8_t* packed_u4,
+                               const uint16_t* scales_bf16, int64_t n_rows, const uint16_t* x_bf16, int64_t K,
+                               int32_t T, float* y_f32, int32_t* argmax_id, float* argmax_val, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream);
+
+/* Workspace bytes w4a16_head_gather needs for n_out scored rows at T
+ * (0 for arguments out of range). */
+size_t w4a16_workspace_bytes(int64_t n_out, int32_t T);
+
+/* Selects the kernel variant for subsequent calls in this process (initially
+ * taken from the environment variable W4A16_VARIANT = auto|dot|mfma). */
+w4a16_status w4a16_set_variant(int32_t variant);
+int32_t w4a16_get_variant(void);
+
+const char* w4a16_status_string(int32_t status);
+int32_t w4a16_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* W4A16_H */

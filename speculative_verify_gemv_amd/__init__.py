@@ -1,0 +1,163 @@
+"""Python binding of libw4a16 (the W4A16 skinny matmul for MI355X).
+
+Argument marshalling only: every step of the computation runs in the gfx950
+kernels behind the C ABI declared in include/w4a16.h.  PyTorch provides device
+memory and the current stream.  There is no fallback: if the library is not
+built, or the device is not gfx950, calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libw4a16.so")
+
+GROUP = 128
+MAX_T = 8
+VARIANTS = {"auto": 0, "dot": 1, "mfma": 2}
+
+_lib = None
+
+
+class W4A16Error(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {status_string(status)} (status {status})")
+
+
+def load_library():
+    """Loads libw4a16.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with __graft_entry__.build() "
+                               "(speculative_verify_gemv_amd/build.py)")
+        lib = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+        lib.w4a16_matmul.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
+        lib.w4a16_matmul.restype = i32
+        lib.w4a16_head_gather.argtypes = [vp, i64, vp, vp, i64, vp, i64, i32, vp, vp, vp, vp, sz, vp]
+        lib.w4a16_head_gather.restype = i32
+        lib.w4a16_workspace_bytes.argtypes = [i64, i32]
+        lib.w4a16_workspace_bytes.restype = sz
+        lib.w4a16_set_variant.argtypes = [i32]
+        lib.w4a16_set_variant.restype = i32
+        lib.w4a16_get_variant.argtypes = []
+        lib.w4a16_get_variant.restype = i32
+        lib.w4a16_status_string.argtypes = [i32]
+        lib.w4a16_status_string.restype = ctypes.c_char_p
+        lib.w4a16_abi_version.argtypes = []
+        lib.w4a16_abi_version.restype = i32
+        _lib = lib
+    return _lib
+
+
+def status_string(status: int) -> str:
+    return load_library().w4a16_status_string(status).decode()
+
+
+def abi_version() -> int:
+    return load_library().w4a16_abi_version()
+
+
+def set_variant(name: str) -> None:
+    s = load_library().w4a16_set_variant(VARIANTS[name])
+    if s:
+        raise W4A16Error(s, "set_variant")
+
+
+def get_variant() -> str:
+    v = load_library().w4a16_get_variant()
+    return {i: n for n, i in VARIANTS.items()}[v]
+
+
+def workspace_bytes(n_out: int, T: int) -> int:
+    return int(load_library().w4a16_workspace_bytes(n_out, T))
+
+
+def _ptr(t) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream
+
+
+def _check_bits(t: torch.Tensor, what: str) -> None:
+    if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
+        raise TypeError(f"{what} must hold bf16 bit patterns (bfloat16/int16/uint16), got {t.dtype}")
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{what} must be a contiguous CUDA tensor")
+
+
+def _check_weight(packed: torch.Tensor, scales: torch.Tensor):
+    if packed.dtype != torch.uint8 or packed.dim() != 2 or not (packed.is_cuda and packed.is_contiguous()):
+        raise ValueError("packed must be a contiguous CUDA uint8 tensor [rows][K/2]")
+    _check_bits(scales, "scales")
+    rows, kh = packed.shape
+    K = 2 * kh
+    if scales.shape != (rows, K // GROUP):
+        raise ValueError(f"scales must be [rows][K/128] = {(rows, K // GROUP)}, got {tuple(scales.shape)}")
+    return rows, K
+
+
+def matmul(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, out: torch.Tensor | None = None,
+           stream=None) -> torch.Tensor:
+    """y[T][N] (float32) = x * W^T with W given by packed int4 codes and bf16 group scales."""
+    N, K = _check_weight(packed, scales)
+    _check_bits(x, "x")
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [T][{K}]")
+    T = x.shape[0]
+    if out is None:
+        out = torch.empty((T, N), dtype=torch.float32, device=packed.device)
+    elif out.dtype != torch.float32 or out.shape != (T, N) or not out.is_contiguous():
+        raise ValueError("out must be a contiguous float32 tensor [T][N]")
+    s = load_library().w4a16_matmul(_ptr(packed), _ptr(scales), _ptr(x), _ptr(out), N, K, T, _stream(stream))
+    if s:
+        raise W4A16Error(s, "w4a16_matmul")
+    return out
+
+
+def head_gather(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, row_ids: torch.Tensor | None = None,
+                scores: bool = True, argmax: bool = False, out: torch.Tensor | None = None,
+                workspace: torch.Tensor | None = None, stream=None):
+    """Scores rows row_ids (all rows if None) of an output head; optional per-row argmax.
+
+    Returns (y [T][n] float32 or None, argmax_id [T] int32 or None, argmax_val [T] float32 or None).
+    """
+    n_rows, K = _check_weight(packed, scales)
+    _check_bits(x, "x")
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [T][{K}]")
+    T = x.shape[0]
+    if row_ids is not None:
+        if row_ids.dtype != torch.int32 or row_ids.dim() != 1 or not (row_ids.is_cuda and row_ids.is_contiguous()):
+            raise ValueError("row_ids must be a contiguous CUDA int32 vector")
+        n = row_ids.shape[0]
+    else:
+        n = n_rows
+    dev = packed.device
+    y = None
+    if scores:
+        y = out if out is not None else torch.empty((T, n), dtype=torch.float32, device=dev)
+    ids = vals = None
+    ws_bytes = 0
+    if argmax:
+        ids = torch.empty(T, dtype=torch.int32, device=dev)
+        vals = torch.empty(T, dtype=torch.float32, device=dev)
+        ws_bytes = workspace_bytes(n, T)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    s = load_library().w4a16_head_gather(_ptr(row_ids), n, _ptr(packed), _ptr(scales), n_rows, _ptr(x), K, T,
+                                         _ptr(y), _ptr(ids), _ptr(vals), _ptr(workspace), ws_bytes,
+                                         _stream(stream))
+    if s:
+        raise W4A16Error(s, "w4a16_head_gather")
+    return y, ids, vals

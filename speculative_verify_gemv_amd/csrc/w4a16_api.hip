@@ -1,0 +1,169 @@
+// C ABI of libw4a16: argument checking, device check, variant selection and
+// launch of the gfx950 kernels.  Every check runs on the host before any HIP
+// call, so a rejected call touches no device state.
+#include <atomic>
+#include <cstdlib>
+#include <cstring>
+#include <mutex>
+
+#include "../../include/w4a16.h"
+#include "w4a16_internal.h"
+
+namespace {
+
+constexpr int64_t kMaxRows = 2147483647LL;
+constexpr int64_t kMaxK = 1LL << 20;
+
+std::atomic<int32_t> g_variant{-1};
+std::once_flag g_env_once;
+
+void read_env_variant() {
+  int32_t v = W4A16_VARIANT_AUTO;
+  if (const char* e = std::getenv("W4A16_VARIANT")) {
+    if (std::strcmp(e, "dot") == 0) v = W4A16_VARIANT_DOT;
+    if (std::strcmp(e, "mfma") == 0) v = W4A16_VARIANT_MFMA;
+  }
+  int32_t expected = -1;
+  g_variant.compare_exchange_strong(expected, v);
+}
+
+int32_t current_variant() {
+  std::call_once(g_env_once, read_env_variant);
+  return g_variant.load();
+}
+
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+constexpr int kMaxDevices = 64;
+std::atomic<int> g_arch[kMaxDevices];
+
+w4a16_status check_device() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return W4A16_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return W4A16_ERR_UNSUPPORTED;
+  int known = g_arch[dev].load();
+  if (known == 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return W4A16_ERR_HIP;
+    known = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    g_arch[dev].store(known);
+  }
+  return known == 1 ? W4A16_OK : W4A16_ERR_UNSUPPORTED;
+}
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+w4a16_status check_kt(int64_t K, int32_t T) {
+  if (K < W4A16_GROUP || K > kMaxK || K % W4A16_GROUP != 0) return W4A16_ERR_BAD_SHAPE;
+  if (T < 1 || T > W4A16_MAX_T) return W4A16_ERR_BAD_SHAPE;
+  return W4A16_OK;
+}
+
+// The variant AUTO resolves to for T activation rows.
+int resolve_variant(int32_t v, int32_t T) {
+  if (v == W4A16_VARIANT_DOT || v == W4A16_VARIANT_MFMA) return v;
+  (void)T;
+  return W4A16_VARIANT_MFMA;
+}
+
+w4a16::Plan make_plan(w4a16::GemvArgs& a, int32_t T) {
+  const int v = resolve_variant(current_variant(), T);
+  return v == W4A16_VARIANT_DOT ? w4a16::plan_dot(a, T) : w4a16::plan_mfma(a, T);
+}
+
+}  // namespace
+
+extern "C" {
+
+w4a16_status w4a16_matmul(const uint8_t* packed_u4, const uint16_t* scales_bf16, const uint16_t* x_bf16,
+                          float* y_f32, int64_t N, int64_t K, int32_t T, hipStream_t stream) {
+  if (!packed_u4 || !scales_bf16 || !x_bf16 || !y_f32) return W4A16_ERR_NULL_POINTER;
+  if (N < 1 || N > kMaxRows) return W4A16_ERR_BAD_SHAPE;
+  if (w4a16_status s = check_kt(K, T)) return s;
+  if (!aligned(packed_u4, 16) || !aligned(x_bf16, 16) || !aligned(scales_bf16, 2) || !aligned(y_f32, 4))
+    return W4A16_ERR_MISALIGNED;
+  if (w4a16_status s = check_device()) return s;
+
+  w4a16::GemvArgs a{};
+  a.packed = packed_u4;
+  a.scales = scales_bf16;
+  a.x = x_bf16;
+  a.y = y_f32;
+  a.n_out = N;
+  a.n_rows = N;
+  a.K = (int32_t)K;
+  a.G = (int32_t)(K / W4A16_GROUP);
+  const w4a16::Plan p = make_plan(a, T);
+  return w4a16::launch(a, p, T, stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+}
+
+size_t w4a16_workspace_bytes(int64_t n_out, int32_t T) {
+  if (n_out < 1 || n_out > kMaxRows || T < 1 || T > W4A16_MAX_T) return 0;
+  return (size_t)w4a16::max_workgroups(n_out) * (size_t)T * sizeof(int2);
+}
+
+w4a16_status w4a16_head_gather(const int32_t* row_ids, int64_t n_ids, const uint8_t* packed_u4,
+                               const uint16_t* scales_bf16, int64_t n_rows, const uint16_t* x_bf16, int64_t K,
+                               int32_t T, float* y_f32, int32_t* argmax_id, float* argmax_val, void* workspace,
+                               size_t workspace_bytes, hipStream_t stream) {
+  if (!packed_u4 || !scales_bf16 || !x_bf16) return W4A16_ERR_NULL_POINTER;
+  if (!y_f32 && !argmax_id) return W4A16_ERR_NULL_POINTER;
+  if (argmax_val && !argmax_id) return W4A16_ERR_NULL_POINTER;
+  if (n_ids < 1 || n_ids > kMaxRows || n_rows < 1 || n_rows > kMaxRows) return W4A16_ERR_BAD_SHAPE;
+  if (!row_ids && n_ids != n_rows) return W4A16_ERR_BAD_SHAPE;
+  if (w4a16_status s = check_kt(K, T)) return s;
+  if (!aligned(packed_u4, 16) || !aligned(x_bf16, 16) || !aligned(scales_bf16, 2) || !aligned(y_f32, 4) ||
+      !aligned(row_ids, 4) || !aligned(argmax_id, 4) || !aligned(argmax_val, 4))
+    return W4A16_ERR_MISALIGNED;
+  const bool want_argmax = argmax_id != nullptr;
+  if (want_argmax) {
+    if (!workspace || workspace_bytes < w4a16_workspace_bytes(n_ids, T) || !aligned(workspace, 16))
+      return W4A16_ERR_WORKSPACE;
+  }
+  if (w4a16_status s = check_device()) return s;
+
+  w4a16::GemvArgs a{};
+  a.packed = packed_u4;
+  a.scales = scales_bf16;
+  a.x = x_bf16;
+  a.y = y_f32;
+  a.row_ids = row_ids;
+  a.partial = want_argmax ? static_cast<int2*>(workspace) : nullptr;
+  a.n_out = n_ids;
+  a.n_rows = n_rows;
+  a.K = (int32_t)K;
+  a.G = (int32_t)(K / W4A16_GROUP);
+  const w4a16::Plan p = make_plan(a, T);
+  if (w4a16::launch(a, p, T, stream) != hipSuccess) return W4A16_ERR_HIP;
+  if (want_argmax &&
+      w4a16::launch_argmax_final(a.partial, p.grid, T, argmax_id, argmax_val, stream) != hipSuccess)
+    return W4A16_ERR_HIP;
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_set_variant(int32_t variant) {
+  if (variant != W4A16_VARIANT_AUTO && variant != W4A16_VARIANT_DOT && variant != W4A16_VARIANT_MFMA)
+    return W4A16_ERR_BAD_VARIANT;
+  std::call_once(g_env_once, read_env_variant);
+  g_variant.store(variant);
+  return W4A16_OK;
+}
+
+int32_t w4a16_get_variant(void) { return current_variant(); }
+
+const char* w4a16_status_string(int32_t status) {
+  switch (status) {
+    case W4A16_OK: return "ok";
+    case W4A16_ERR_NULL_POINTER: return "a required pointer is NULL";
+    case W4A16_ERR_BAD_SHAPE: return "a size is out of range";
+    case W4A16_ERR_MISALIGNED: return "a pointer is not aligned as required";
+    case W4A16_ERR_WORKSPACE: return "argmax requested without a large enough 16-byte aligned workspace";
+    case W4A16_ERR_UNSUPPORTED: return "the current device is not gfx950";
+    case W4A16_ERR_HIP: return "a HIP runtime call failed";
+    case W4A16_ERR_BAD_VARIANT: return "unknown kernel variant";
+    default: return "unknown status";
+  }
+}
+
+int32_t w4a16_abi_version(void) { return W4A16_ABI_VERSION; }
+
+}  // extern "C"

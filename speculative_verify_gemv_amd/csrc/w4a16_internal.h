@@ -1,0 +1,48 @@
+// Internal interface between the C-ABI layer (w4a16_api.hip) and the gfx950
+// kernels (w4a16_kernels.hip).  Not installed; not part of the ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace w4a16 {
+
+// One weight matrix (or a gathered subset of its rows) against T activation rows.
+struct GemvArgs {
+  const uint8_t* packed;   // [n_rows][K/2]
+  const uint16_t* scales;  // [n_rows][K/128] bf16 bits
+  const uint16_t* x;       // [T][K] bf16 bits
+  float* y;                // [T][n_out] or nullptr
+  const int32_t* row_ids;  // [n_out] or nullptr (identity)
+  int2* partial;           // argmax partials [grid][T] (value bits, id) or nullptr
+  int64_t n_out;
+  int64_t n_rows;
+  int32_t K;
+  int32_t G;  // K / 128
+  // tiling, filled by the planner
+  int32_t gpw;          // groups per wave (split-K share)
+  int32_t sk;           // groups per staged activation slice
+  int32_t xs_stride;    // halves per staged token row
+  int32_t wave_lds;     // bytes of LDS per wave
+  int32_t fin_offset;   // byte offset of the final-value area
+};
+
+struct Plan {
+  int variant;  // 1 dot, 2 mfma
+  int rt;       // 16-row tiles per workgroup (mfma) / rows per wave (dot)
+  int nw;       // waves per workgroup
+  int64_t grid; // workgroups
+  int lds;      // dynamic LDS bytes
+};
+
+// Fills the tiling fields of `a` and returns the launch plan.
+Plan plan_mfma(GemvArgs& a, int T);
+Plan plan_dot(GemvArgs& a, int T);
+
+hipError_t launch(const GemvArgs& a, const Plan& p, int T, hipStream_t s);
+hipError_t launch_argmax_final(const int2* partial, int64_t nparts, int T, int32_t* id, float* val, hipStream_t s);
+
+// Upper bound of the workgroups any plan uses for n_out rows (sizes the argmax workspace).
+int64_t max_workgroups(int64_t n_out);
+
+}  // namespace w4a16

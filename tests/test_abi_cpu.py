@@ -1,0 +1,126 @@
+"""The C-ABI library on a machine without a GPU: it loads, exports every
+function include/w4a16.h declares, and rejects bad arguments on the host
+(nothing reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "w4a16.h")
+LIB = os.path.join(ROOT, "speculative_verify_gemv_amd", "libw4a16.so")
+
+OK, NULLP, SHAPE, ALIGN, WS, UNSUP, HIP, VARIANT = range(8)
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(w4a16_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.skip("libw4a16.so not built")
+    l = ctypes.CDLL(LIB)
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    l.w4a16_matmul.argtypes = [vp, vp, vp, vp, i64, i64, i32, vp]
+    l.w4a16_matmul.restype = i32
+    l.w4a16_head_gather.argtypes = [vp, i64, vp, vp, i64, vp, i64, i32, vp, vp, vp, vp, sz, vp]
+    l.w4a16_head_gather.restype = i32
+    l.w4a16_workspace_bytes.argtypes = [i64, i32]
+    l.w4a16_workspace_bytes.restype = sz
+    l.w4a16_status_string.argtypes = [i32]
+    l.w4a16_status_string.restype = ctypes.c_char_p
+    l.w4a16_set_variant.argtypes = [i32]
+    l.w4a16_set_variant.restype = i32
+    l.w4a16_get_variant.restype = i32
+    return l
+
+
+def test_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"w4a16_matmul", "w4a16_head_gather", "w4a16_workspace_bytes"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), f"{n} declared in w4a16.h but not exported"
+
+
+def test_abi_version_and_strings(lib):
+    assert lib.w4a16_abi_version() == 1
+    for s in range(8):
+        assert lib.w4a16_status_string(s)
+    assert lib.w4a16_status_string(99) == b"unknown status"
+
+
+A = 0x10000  # fake, suitably aligned device addresses: never dereferenced on a rejected call
+
+
+def mm(lib, p=A, s=A, x=A, y=A, N=64, K=256, T=1):
+    return lib.w4a16_matmul(p, s, x, y, N, K, T, None)
+
+
+def test_matmul_rejections(lib):
+    assert mm(lib, p=None) == NULLP
+    assert mm(lib, s=None) == NULLP
+    assert mm(lib, x=None) == NULLP
+    assert mm(lib, y=None) == NULLP
+    assert mm(lib, N=0) == SHAPE
+    assert mm(lib, N=2**31) == SHAPE
+    assert mm(lib, K=0) == SHAPE
+    assert mm(lib, K=100) == SHAPE
+    assert mm(lib, K=129) == SHAPE
+    assert mm(lib, K=2**21) == SHAPE
+    assert mm(lib, T=0) == SHAPE
+    assert mm(lib, T=9) == SHAPE
+    assert mm(lib, p=A + 8) == ALIGN
+    assert mm(lib, x=A + 2) == ALIGN
+    assert mm(lib, s=A + 1) == ALIGN
+    assert mm(lib, y=A + 2) == ALIGN
+
+
+def hg(lib, ids=A, n_ids=10, p=A, s=A, n_rows=100, x=A, K=256, T=2, y=A, am=None, av=None, ws=None, wsb=0):
+    return lib.w4a16_head_gather(ids, n_ids, p, s, n_rows, x, K, T, y, am, av, ws, wsb, None)
+
+
+def test_head_gather_rejections(lib):
+    assert hg(lib, p=None) == NULLP
+    assert hg(lib, y=None, am=None) == NULLP
+    assert hg(lib, av=A) == NULLP                  # value without id
+    assert hg(lib, n_ids=0) == SHAPE
+    assert hg(lib, n_rows=0) == SHAPE
+    assert hg(lib, ids=None, n_ids=10, n_rows=100) == SHAPE   # identity needs n_ids == n_rows
+    assert hg(lib, T=9) == SHAPE
+    assert hg(lib, K=200) == SHAPE
+    assert hg(lib, ids=A + 2) == ALIGN
+    assert hg(lib, am=A + 1) == ALIGN
+    assert hg(lib, am=A) == WS                     # argmax without workspace
+    need = lib.w4a16_workspace_bytes(10, 2)
+    assert need > 0
+    assert hg(lib, am=A, ws=A, wsb=need - 1) == WS
+    assert hg(lib, am=A, ws=A + 8, wsb=need) == WS  # workspace must be 16-byte aligned
+
+
+def test_workspace_bytes(lib):
+    assert lib.w4a16_workspace_bytes(0, 1) == 0
+    assert lib.w4a16_workspace_bytes(10, 0) == 0
+    assert lib.w4a16_workspace_bytes(10, 9) == 0
+    assert lib.w4a16_workspace_bytes(248320, 4) == 248320 // 16 * 4 * 8
+    assert lib.w4a16_workspace_bytes(17, 1) == 2 * 8
+
+
+def test_variant_selection(lib):
+    assert lib.w4a16_set_variant(7) == VARIANT
+    for v in (1, 2, 0):
+        assert lib.w4a16_set_variant(v) == OK and lib.w4a16_get_variant() == v
+
+
+def test_valid_call_without_gpu_fails_cleanly(lib):
+    try:
+        import torch
+        if torch.cuda.is_available():
+            pytest.skip("a GPU is present")
+    except ImportError:
+        pass
+    assert mm(lib) in (HIP, UNSUP)

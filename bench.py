@@ -1,0 +1,233 @@
+"""Benchmark: the decode weight pass of a 27B-class model on one MI355X.
+
+One step is one verify cycle's weight read: 64 layers x {qkv, o, gate_up,
+down} W4A16 projections at T = 4 (1 + 3 drafts), each with its own seeded
+weights and activations, run as one grouped launch, then the 248,320-row
+lm_head with per-row argmax.  Weights stay resident in HBM; nothing is
+cached between steps (11.6 GB per step, far beyond the 256 MB Infinity
+Cache).
+
+Reported (one JSON line): weight GB/s of the whole step (value), decode
+cycles/s, the grouped body kernel's achieved bandwidth against the 8 TB/s
+HBM peak (roofline, timed with HIP events on the launch stream), the body
+pass at T = 1, 4, 8, and the CPU oracle's rate on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import numpy as np  # noqa: E402
+
+import synth  # noqa: E402
+from speculative_verify_gemv_amd import metrics  # noqa: E402
+
+METRIC = "weight GB/s and % of HBM peak at T=1/4/8 (27B-class shapes); decode cycles/s"
+PEAK_GBPS = 8000.0
+WORKLOAD = "decode_weight_pass_64x(qkv,o,gate_up,down)+lm_head_T4"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--T", type=int, default=4)
+    ap.add_argument("--layers", type=int, default=synth.LAYERS)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-per-t", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
+    return ap.parse_args()
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def to_dev(a, torch):
+    t = torch.from_numpy(np.ascontiguousarray(a))
+    if t.dtype == torch.uint16:
+        t = t.view(torch.int16)
+    return t.cuda()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (got --gpus {args.gpus}); the W4A16 pass is measured on a single "
+              "MI355X and is not sharded here.", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import speculative_verify_gemv_amd as w4a16
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    w4a16.load_library()
+    T = args.T
+    L = args.layers
+    t0 = time.time()
+
+    # ---- resident weights: 64 layers x 4 projections + lm_head (seeded) ----
+    weights = []  # (name, layer, packed_dev, scales_dev)
+    for layer in range(L):
+        for proj in synth.PROJ_ORDER:
+            N, K = synth.PROJECTIONS[proj]
+            p, s = synth.weight(synth.tid_layer(layer, proj), N, K)
+            weights.append((proj, layer, to_dev(p, torch), to_dev(s, torch)))
+    hn, hk = synth.LM_HEAD
+    hp, hs = synth.weight(synth.TID_LM_HEAD, hn, hk)
+    head_p, head_s = to_dev(hp, torch), to_dev(hs, torch)
+    del hp, hs
+    torch.cuda.synchronize()
+    log(f"weights resident after {time.time() - t0:.1f} s")
+
+    body_bytes = sum(metrics.weight_bytes(*synth.PROJECTIONS[w[0]]) for w in weights)
+    head_bytes = metrics.weight_bytes(hn, hk)
+
+    def make_pass(Tp):
+        probs = []
+        for proj, layer, pd, sd in weights:
+            N, K = synth.PROJECTIONS[proj]
+            x = to_dev(synth.activations(synth.tid_layer(layer, proj), Tp, K), torch)
+            y = torch.empty((Tp, N), dtype=torch.float32, device="cuda")
+            probs.append((pd, sd, x, y))
+        return w4a16.Batch(probs, Tp), probs
+
+    batch, probs = make_pass(T)
+    head_x = to_dev(synth.activations(synth.TID_LM_HEAD, T, hk), torch)
+    head_y = torch.empty((T, hn), dtype=torch.float32, device="cuda")
+    head_ws = torch.empty(w4a16.workspace_bytes(hn, T), dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        batch.run(stream)
+        w4a16.head_gather(head_p, head_s, head_x, scores=True, argmax=True, out=head_y, workspace=head_ws,
+                          stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K_steps = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K_steps)]
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(K_steps):
+        ev[i][0].record(stream)
+        batch.run(stream)
+        ev[i][1].record(stream)
+        w4a16.head_gather(head_p, head_s, head_x, scores=True, argmax=True, out=head_y, workspace=head_ws,
+                          stream=stream)
+    end.record(stream)
+    torch.cuda.synchronize()
+    ms_total = start.elapsed_time(end)
+    ms_step = ms_total / K_steps
+    body_ms = [a.elapsed_time(b) for a, b in ev]
+    body_ms_avg = float(np.mean(body_ms))
+    step_bytes = body_bytes + head_bytes
+    value = metrics.gbps(step_bytes, ms_step)
+    achieved = metrics.gbps(body_bytes, body_ms_avg)
+    log(f"step {ms_step:.4f} ms, body kernel {body_ms_avg:.4f} ms (min {min(body_ms):.4f}), "
+        f"{value:.0f} GB/s per step, body {achieved:.0f} GB/s")
+
+    # ---- body pass at T = 1, 4, 8 (same weights, grouped launch) ----
+    per_t = {}
+    if not args.no_per_t:
+        for Tp in (1, 4, 8):
+            b, _ = (batch, probs) if Tp == T else make_pass(Tp)
+            for _ in range(2):
+                b.run(stream)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            reps = 5
+            e0.record(stream)
+            for _ in range(reps):
+                b.run(stream)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / reps
+            g = metrics.gbps(body_bytes, ms)
+            per_t[f"T{Tp}"] = {"body_ms": round(ms, 4), "weight_GBps": round(g, 1),
+                              "pct_hbm_peak": round(100 * g / PEAK_GBPS, 2)}
+            log(f"body pass T={Tp}: {ms:.4f} ms, {g:.0f} GB/s ({100 * g / PEAK_GBPS:.1f}% of 8 TB/s)")
+
+    # ---- CPU baseline: the oracle on a bounded sample of the same pass ----
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(T, args.cpu_seconds)
+
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int4 weights x bf16 activations (exact fp16 products), fp32 accumulate",
+        "data": "synthetic (seeded)",
+        "config": {
+            "workload": WORKLOAD,
+            "T": T,
+            "layers": L,
+            "projections": {k: list(v) for k, v in synth.PROJECTIONS.items()},
+            "lm_head": [hn, hk],
+            "group": 128,
+            "weight_bytes_per_step": step_bytes,
+        },
+        "cycles_per_s": round(1000.0 / ms_step, 2),
+        "pct_hbm_peak": round(100 * value / PEAK_GBPS, 2),
+        "per_T_body_pass": per_t,
+        "roofline": {
+            "kernel": "grouped body pass (64 x 4 projections, one launch)",
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": body_bytes,
+            "avg_launch_ms": round(body_ms_avg, 4),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+def cpu_baseline(T, target_s):
+    """The oracle (plain C, fp64) on the host cores, on whole layers of the same
+    pass until about target_s seconds of work, reported as weight GB/s."""
+    import oracle
+
+    threads = oracle.default_threads()
+    done_bytes = 0
+    spent = 0.0
+    layers = 0
+    for layer in range(synth.LAYERS):
+        for proj in synth.PROJ_ORDER:
+            N, K = synth.PROJECTIONS[proj]
+            p, s = synth.weight(synth.tid_layer(layer, proj), N, K)
+            x = synth.activations(synth.tid_layer(layer, proj), T, K)
+            t = time.time()
+            oracle.matmul(p, s, x, nthreads=threads, want_abs=False)
+            spent += time.time() - t
+            done_bytes += metrics.weight_bytes(N, K)
+        layers += 1
+        if spent >= target_s:
+            break
+    g = done_bytes / spent / 1e9
+    log(f"CPU oracle: {layers} layers at T={T} in {spent:.1f} s on {threads} threads: {g:.3f} GB/s")
+    return {"value": round(g, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{layers} of 64 layers (qkv, o, gate_up, down) at T={T}, fp64 oracle, {spent:.1f} s"}
+
+
+if __name__ == "__main__":
+    main()

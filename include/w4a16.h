@@ -63,7 +63,7 @@ typedef enum {
   W4A16_ERR_NULL_POINTER = 1, /* a required pointer is NULL */
   W4A16_ERR_BAD_SHAPE = 2,    /* a size is out of range (see each call) */
   W4A16_ERR_MISALIGNED = 3,   /* packed_u4 / x_bf16 not 16-byte aligned, scales not 2, y / ids / argmax not 4 */
-  W4A16_ERR_WORKSPACE = 4,    /* argmax requested with no or too small a workspace */
+  W4A16_ERR_WORKSPACE = 4,    /* argmax workspace (or batch table buffer) missing or too small */
   W4A16_ERR_UNSUPPORTED = 5,  /* the current device is not gfx950 */
   W4A16_ERR_HIP = 6,          /* a HIP runtime call returned an error */
   W4A16_ERR_BAD_VARIANT = 7   /* unknown kernel variant */
@@ -99,7 +99,8 @@ w4a16_status w4a16_matmul(const uint8_t* packed_u4, const uint16_t* scales_bf16,
  *             (the full head).  Duplicates are allowed.  An id outside
  *             [0, n_rows) yields a NaN output row that never wins the argmax.
  *   y_f32     [T][n_ids] in row_ids order, or NULL to skip writing scores.
- *   argmax_id / argmax_val  [T] each, or both NULL.  For each t: the largest
+ *   argmax_id [T] or NULL (no argmax); argmax_val [T] or NULL (needs
+ *             argmax_id).  For each t: the largest
  *             non-NaN score and the lowest vocabulary id (row_ids value)
  *             attaining it -- greedy acceptance is an argmax equality over the
  *             verify rows (article section "What each one calls the same
@@ -118,6 +119,45 @@ w4a16_status w4a16_head_gather(const int32_t* row_ids, int64_t n_ids, const uint
 /* Workspace bytes w4a16_head_gather needs for n_out scored rows at T
  * (0 for arguments out of range). */
 size_t w4a16_workspace_bytes(int64_t n_out, int32_t T);
+
+/*
+ * Grouped launch: many independent matmuls with the same T in one kernel
+ * launch, so a whole decode weight pass (e.g. 64 layers x 4 projections) runs
+ * without launch gaps or per-kernel ramp-up and tail.  The pages run a verify
+ * cycle as one CUDA graph (qwen-warp section) or one persistent launch
+ * (OpenJet engine page, "How it works"), and name ~1300 small launches per
+ * token as the P100 build's decode bottleneck (P100 patch page, "Persistent
+ * layer kernels").
+ *
+ * Use: w4a16_batch_plan() (host only, no HIP call) checks every problem and
+ * writes a launch table into caller-owned host memory of
+ * w4a16_batch_table_bytes(count) bytes; the caller copies those bytes to
+ * device memory (16-byte aligned) and then calls w4a16_matmul_batch() with
+ * both copies, as often as it likes.  The device copy must hold exactly the
+ * bytes of the host copy and stay unchanged while launches that use it run.
+ * Problems run in list order as far as the GPU schedules them; their outputs
+ * must not overlap each other or any input.  The pointers and sizes of each
+ * problem follow w4a16_matmul.
+ */
+typedef struct {
+  const uint8_t* packed_u4;    /* [N][K/2] */
+  const uint16_t* scales_bf16; /* [N][K/128] */
+  const uint16_t* x_bf16;      /* [T][K] */
+  float* y_f32;                /* [T][N] */
+  int64_t N;
+  int64_t K;
+} w4a16_problem;
+
+#define W4A16_MAX_BATCH 65536
+
+/* Table bytes for `count` problems (0 if count is out of [1, W4A16_MAX_BATCH]). */
+size_t w4a16_batch_table_bytes(int32_t count);
+
+w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int32_t T, void* table_host,
+                              size_t table_bytes);
+
+/* W4A16_ERR_BAD_SHAPE if table_host is not a table written by w4a16_batch_plan. */
+w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, hipStream_t stream);
 
 /* Selects the kernel variant for subsequent calls in this process (initially
  * taken from the environment variable W4A16_VARIANT = auto|dot|mfma). */

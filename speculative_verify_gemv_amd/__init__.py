@@ -51,6 +51,12 @@ def load_library():
         lib.w4a16_status_string.restype = ctypes.c_char_p
         lib.w4a16_abi_version.argtypes = []
         lib.w4a16_abi_version.restype = i32
+        lib.w4a16_batch_table_bytes.argtypes = [i32]
+        lib.w4a16_batch_table_bytes.restype = sz
+        lib.w4a16_batch_plan.argtypes = [vp, i32, i32, vp, sz]
+        lib.w4a16_batch_plan.restype = i32
+        lib.w4a16_matmul_batch.argtypes = [vp, vp, vp]
+        lib.w4a16_matmul_batch.restype = i32
         _lib = lib
     return _lib
 
@@ -161,3 +167,44 @@ def head_gather(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, row
     if s:
         raise W4A16Error(s, "w4a16_head_gather")
     return y, ids, vals
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("packed_u4", ctypes.c_void_p), ("scales_bf16", ctypes.c_void_p), ("x_bf16", ctypes.c_void_p),
+                ("y_f32", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+
+
+class Batch:
+    """A planned grouped launch over independent matmuls with the same T.
+
+    problems: list of (packed, scales, x, y) CUDA tensors.  The tensors must
+    stay alive and in place while the batch is used; the plan is a host table
+    plus its device copy (both held here).
+    """
+
+    def __init__(self, problems, T: int):
+        lib = load_library()
+        arr = (_Problem * len(problems))()
+        self._keep = []
+        for i, (packed, scales, x, y) in enumerate(problems):
+            N, K = _check_weight(packed, scales)
+            _check_bits(x, "x")
+            if x.shape != (T, K) or y.dtype != torch.float32 or y.shape != (T, N) or not y.is_contiguous():
+                raise ValueError(f"problem {i}: x must be [T][K] and y float32 [T][N]")
+            arr[i] = _Problem(packed.data_ptr(), scales.data_ptr(), x.data_ptr(), y.data_ptr(), N, K)
+            self._keep.append((packed, scales, x, y))
+        nbytes = lib.w4a16_batch_table_bytes(len(problems))
+        if nbytes == 0:
+            raise ValueError("batch size out of range")
+        self.host = torch.empty(nbytes, dtype=torch.uint8)
+        s = lib.w4a16_batch_plan(ctypes.cast(arr, ctypes.c_void_p), len(problems), T, self.host.data_ptr(), nbytes)
+        if s:
+            raise W4A16Error(s, "w4a16_batch_plan")
+        self.device = self.host.to(problems[0][0].device, non_blocking=False)
+        self.T = T
+        self.count = len(problems)
+
+    def run(self, stream=None) -> None:
+        s = load_library().w4a16_matmul_batch(self.host.data_ptr(), self.device.data_ptr(), _stream(stream))
+        if s:
+            raise W4A16Error(s, "w4a16_matmul_batch")

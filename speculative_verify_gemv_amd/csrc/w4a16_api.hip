@@ -1,7 +1,9 @@
 // C ABI of libw4a16: argument checking, device check, variant selection and
 // launch of the gfx950 kernels.  Every check runs on the host before any HIP
 // call, so a rejected call touches no device state.
+#include <algorithm>
 #include <atomic>
+#include <cstdio>
 #include <cstdlib>
 #include <cstring>
 #include <mutex>
@@ -72,6 +74,53 @@ w4a16::Plan make_plan(w4a16::GemvArgs& a, int32_t T) {
 
 }  // namespace
 
+// Grouped launches: table layout and tile choice.
+namespace {
+
+constexpr uint32_t kTableMagic = 0x57344231u;  // "W4B1"
+
+struct TableHeader {
+  uint32_t magic;
+  uint32_t version;
+  int32_t count;
+  int32_t T;
+  int32_t variant;
+  int32_t rt;
+  int32_t pd;
+  int32_t threads;
+  int32_t lds;
+  int32_t reserved0;
+  int64_t grid;
+  int64_t reserved[2];
+};
+static_assert(sizeof(TableHeader) == 64, "table header size");
+
+// Kernel of grouped launches: the streaming matrix-core kernel, four 16-row
+// tiles per workgroup, 8 groups of each row in flight.  W4A16_BATCH_TILE =
+// "stream,pd" or "split,rt,pd,nw" overrides it (for measurement).
+struct BatchTile {
+  int variant = 3, rt = 1, pd = 8, nw = 4;
+};
+
+BatchTile batch_tile() {
+  BatchTile b;
+  if (const char* e = std::getenv("W4A16_BATCH_TILE")) {
+    int x = 0, y = 0, z = 0;
+    if (std::sscanf(e, "stream,%d", &x) == 1 && (x == 8 || x == 16)) {
+      b.pd = x;
+    } else if (std::sscanf(e, "split,%d,%d,%d", &x, &y, &z) == 3 && (x == 1 || x == 4) &&
+               (y == 2 || y == 4 || y == 8) && !(x == 4 && y == 8) && z >= 1 && z <= 8) {
+      b.variant = 2;
+      b.rt = x;
+      b.pd = y;
+      b.nw = z;
+    }
+  }
+  return b;
+}
+
+}  // namespace
+
 extern "C" {
 
 w4a16_status w4a16_matmul(const uint8_t* packed_u4, const uint16_t* scales_bf16, const uint16_t* x_bf16,
@@ -138,6 +187,78 @@ w4a16_status w4a16_head_gather(const int32_t* row_ids, int64_t n_ids, const uint
       w4a16::launch_argmax_final(a.partial, p.grid, T, argmax_id, argmax_val, stream) != hipSuccess)
     return W4A16_ERR_HIP;
   return W4A16_OK;
+}
+
+size_t w4a16_batch_table_bytes(int32_t count) {
+  if (count < 1 || count > W4A16_MAX_BATCH) return 0;
+  return sizeof(TableHeader) + (size_t)count * sizeof(w4a16::GemvArgs);
+}
+
+w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int32_t T, void* table_host,
+                              size_t table_bytes) {
+  if (!problems || !table_host) return W4A16_ERR_NULL_POINTER;
+  if (count < 1 || count > W4A16_MAX_BATCH || T < 1 || T > W4A16_MAX_T) return W4A16_ERR_BAD_SHAPE;
+  if (table_bytes < w4a16_batch_table_bytes(count) || !aligned(table_host, 8)) return W4A16_ERR_WORKSPACE;
+  for (int32_t i = 0; i < count; ++i) {
+    const w4a16_problem& q = problems[i];
+    if (!q.packed_u4 || !q.scales_bf16 || !q.x_bf16 || !q.y_f32) return W4A16_ERR_NULL_POINTER;
+    if (q.N < 1 || q.N > kMaxRows) return W4A16_ERR_BAD_SHAPE;
+    if (w4a16_status s = check_kt(q.K, T)) return s;
+    if (!aligned(q.packed_u4, 16) || !aligned(q.x_bf16, 16) || !aligned(q.scales_bf16, 2) || !aligned(q.y_f32, 4))
+      return W4A16_ERR_MISALIGNED;
+  }
+  const BatchTile bt = batch_tile();
+  auto* hdr = static_cast<TableHeader*>(table_host);
+  auto* args = reinterpret_cast<w4a16::GemvArgs*>(hdr + 1);
+  int64_t grid = 0;
+  int lds = 0, nw = 1;
+  for (int32_t i = 0; i < count; ++i) {
+    const w4a16_problem& q = problems[i];
+    w4a16::GemvArgs a{};
+    a.packed = q.packed_u4;
+    a.scales = q.scales_bf16;
+    a.x = q.x_bf16;
+    a.y = q.y_f32;
+    a.n_out = q.N;
+    a.n_rows = q.N;
+    a.K = (int32_t)q.K;
+    a.G = (int32_t)(q.K / W4A16_GROUP);
+    int l = 0;
+    int64_t g = 0;
+    if (bt.variant == 3)
+      w4a16::plan_stream(a, T, bt.pd, bt.nw, &l, &g);
+    else
+      w4a16::plan_mfma_fixed(a, T, bt.rt, bt.pd, bt.nw, &l, &g);
+    a.wg_start = grid;
+    grid += g;
+    lds = std::max(lds, l);
+    nw = std::max(nw, (int)a.nw);
+    args[i] = a;
+  }
+  if (grid > 0x7fffffffLL) return W4A16_ERR_BAD_SHAPE;
+  *hdr = TableHeader{kTableMagic, W4A16_ABI_VERSION, count, T, bt.variant, bt.rt, bt.pd, nw * 64, lds, 0, grid,
+                     {0, 0}};
+  return W4A16_OK;
+}
+
+w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, hipStream_t stream) {
+  if (!table_host || !table_dev) return W4A16_ERR_NULL_POINTER;
+  if (!aligned(table_dev, 16) || !aligned(table_host, 8)) return W4A16_ERR_MISALIGNED;
+  const auto* hdr = static_cast<const TableHeader*>(table_host);
+  if (hdr->magic != kTableMagic || hdr->version != W4A16_ABI_VERSION || hdr->count < 1 ||
+      hdr->count > W4A16_MAX_BATCH || hdr->T < 1 || hdr->T > W4A16_MAX_T || hdr->grid < 1)
+    return W4A16_ERR_BAD_SHAPE;
+  if (w4a16_status s = check_device()) return s;
+  w4a16::Plan p{};
+  if (hdr->variant != 2 && hdr->variant != 3) return W4A16_ERR_BAD_SHAPE;
+  p.variant = hdr->variant;
+  p.rt = hdr->rt;
+  p.pd = hdr->pd;
+  p.threads = hdr->threads;
+  p.grid = hdr->grid;
+  p.lds = hdr->lds;
+  const auto* args = reinterpret_cast<const w4a16::GemvArgs*>(static_cast<const TableHeader*>(table_dev) + 1);
+  return w4a16::launch_batch(args, hdr->count, p, hdr->T, stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
 w4a16_status w4a16_set_variant(int32_t variant) {

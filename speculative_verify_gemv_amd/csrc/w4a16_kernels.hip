@@ -41,6 +41,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <type_traits>
 
 #include "w4a16_internal.h"
 
@@ -55,6 +56,8 @@ typedef unsigned short us2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kGroup = 128;
 constexpr int kLdsCap = 65536;  // dynamic LDS per workgroup
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt = 0 only.
+constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
 
@@ -64,15 +67,22 @@ __device__ __forceinline__ unsigned as_u32(V h) {
   return __builtin_bit_cast(unsigned, h);
 }
 
+// (w & m) | c in one VALU operation (v_and_or_b32: one SGPR operand, one VGPR).
+__device__ __forceinline__ unsigned and_or(unsigned w, unsigned m, unsigned c) {
+  unsigned r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(m), "v"(c));
+  return r;
+}
+
 // Eight exact fp16 levels (q - 8) of one word, slot order 0,4,1,5,2,6,3,7.
 __device__ __forceinline__ u4_t levels8(unsigned w) {
   const unsigned w8 = w >> 8;
   const h2_t lo_bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const h2_t hi_bias = {(_Float16)-72.0f, (_Float16)-72.0f};
-  const h2_t a = __builtin_bit_cast(h2_t, (w & 0x000F000Fu) | 0x64006400u) + lo_bias;
-  const h2_t b = __builtin_bit_cast(h2_t, (w & 0x00F000F0u) | 0x54005400u) + hi_bias;
-  const h2_t c = __builtin_bit_cast(h2_t, (w8 & 0x000F000Fu) | 0x64006400u) + lo_bias;
-  const h2_t d = __builtin_bit_cast(h2_t, (w8 & 0x00F000F0u) | 0x54005400u) + hi_bias;
+  const h2_t a = __builtin_bit_cast(h2_t, and_or(w, 0x000F000Fu, 0x64006400u)) + lo_bias;
+  const h2_t b = __builtin_bit_cast(h2_t, and_or(w, 0x00F000F0u, 0x54005400u)) + hi_bias;
+  const h2_t c = __builtin_bit_cast(h2_t, and_or(w8, 0x000F000Fu, 0x64006400u)) + lo_bias;
+  const h2_t d = __builtin_bit_cast(h2_t, and_or(w8, 0x00F000F0u, 0x54005400u)) + hi_bias;
   return u4_t{as_u32(a), as_u32(b), as_u32(c), as_u32(d)};
 }
 
@@ -152,7 +162,7 @@ __device__ __forceinline__ int64_t weight_row(const GemvArgs& a, int64_t o) {
 // final values fin[(rt*TT + t)*16 + r] of rows row0 + rt*16 + r (rows < nrows).
 template <int TT>
 __device__ __forceinline__ void workgroup_argmax(const GemvArgs& a, const float* fin, int64_t row0, int nrows,
-                                                 int lane) {
+                                                 int lane, int64_t wg) {
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
     float bv = __builtin_nanf("");
@@ -167,7 +177,7 @@ __device__ __forceinline__ void workgroup_argmax(const GemvArgs& a, const float*
       }
     }
     wave_argmax(bv, bi);
-    if (lane == 0) a.partial[(int64_t)blockIdx.x * TT + t] = int2{__float_as_int(bv), bi};
+    if (lane == 0) a.partial[wg * TT + t] = int2{__float_as_int(bv), bi};
   }
 }
 
@@ -205,114 +215,123 @@ __device__ __forceinline__ void fold_slice(float (&acc)[RT][4], float (&accs)[RT
   }
 }
 
-template <int TT, int RT>
-__global__ void __launch_bounds__(512) w4a16_mfma_kernel(GemvArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  constexpr int PD = (RT == 1) ? 4 : 2;  // groups of weight loads kept in flight per wave
+// One workgroup of the mfma variant: output rows [wg*RT*16, +RT*16) of problem
+// `a`, K split over a.nw waves in ranges of a.gpw groups.  Each wave keeps PD
+// groups of weight loads in flight in a register ring; the body of the
+// streaming loop is straight-line so every wait names exactly the group it
+// needs.  Loads past the wave's last group re-read that group and are masked
+// by a zero scale.
+template <int TT, int RT, int PD>
+__device__ __forceinline__ void mfma_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int nw = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar control flow
   const int r16 = lane & 15;  // output row of the B operand / token row of the A operand
   const int kq = lane >> 4;   // quarter of the 128-column group
-  const int64_t row0 = (int64_t)blockIdx.x * (RT * 16);
+  const int trow = min(r16, TT - 1);  // A rows >= TT only feed D rows that are never read
+  const int64_t row0 = wg * (RT * 16);
   const int64_t kh = a.K >> 1;
 
-  const u4_t* cp[RT];
-  const uint16_t* sp[RT];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    int64_t w = weight_row(a, row0 + rt * 16 + r16);
-    if (w < 0) w = 0;  // read a valid row; the output is masked below
-    cp[rt] = reinterpret_cast<const u4_t*>(a.packed + w * kh) + kq;
-    sp[rt] = a.scales + w * a.G;
-  }
-
   const int g_begin = wave * a.gpw;
-  const int g_end = min(a.G, g_begin + a.gpw);
-  _Float16* xs = reinterpret_cast<_Float16*>(smem + wave * a.wave_lds);
+  const int n = (wave < a.nw) ? min(a.G - g_begin, a.gpw) : 0;  // wave-uniform
 
-  float acc[RT][4], accs[RT][4];
+  float acc[RT][4];
 #pragma unroll
   for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[rt][r] = accs[rt][r] = 0.0f;
-  int E[TT];
-#pragma unroll
-  for (int t = 0; t < TT; ++t) E[t] = 0;
+    for (int r = 0; r < 4; ++r) acc[rt][r] = 0.0f;
 
-  u4_t q[PD][RT];
-  unsigned short sq[PD][RT];
+  if (n > 0) {
+    const u4_t* cp[RT];
+    const uint16_t* sp[RT];
 #pragma unroll
-  for (int s = 0; s < PD; ++s)
-    if (g_begin + s < g_end)
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        q[s][rt] = __builtin_nontemporal_load(cp[rt] + 4 * (g_begin + s));
-        sq[s][rt] = sp[rt][g_begin + s];
-      }
-
-  int slice_begin = g_begin, slice_end = g_begin;
-  for (int gb = g_begin; gb < g_end; gb += PD) {
-    if (gb >= slice_end) {
-      if (gb > g_begin) fold_slice<TT, RT>(acc, accs, E, kq);
-      lds_fence();
-      slice_begin = gb;
-      slice_end = min(g_end, gb + a.sk);
-      stage_wave<TT>(a, xs, slice_begin, slice_end, lane, E);
-      lds_fence();
+    for (int rt = 0; rt < RT; ++rt) {
+      int64_t w = weight_row(a, row0 + rt * 16 + r16);
+      if (w < 0) w = 0;  // read a valid row; the output is masked later
+      cp[rt] = reinterpret_cast<const u4_t*>(a.packed + w * kh) + kq + 4 * (int64_t)g_begin;
+      sp[rt] = a.scales + w * a.G + g_begin;
     }
+    _Float16* xs = reinterpret_cast<_Float16*>(smem + wave * a.wave_lds);
+    float accs[RT][4];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) accs[rt][r] = 0.0f;
+    int E[TT];
+
+    u4_t q[PD][RT];
+    unsigned short sq[PD][RT];
 #pragma unroll
     for (int s = 0; s < PD; ++s) {
-      const int g = gb + s;
-      if (g < g_end) {
-        h8_t xa[4];
-        const _Float16* xr = xs + r16 * a.xs_stride + (g - slice_begin) * kGroup + kq * 32;
+      const int g = min(s, n - 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (r16 < TT)
-            xa[j] = *reinterpret_cast<const h8_t*>(xr + 8 * j);
-          else
-            xa[j] = h8_t{};
-        }
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) {
-          const float sc = bf16_to_f32(sq[s][rt]);
-          f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], __builtin_bit_cast(h8_t, levels8(q[s][rt].x)), d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], __builtin_bit_cast(h8_t, levels8(q[s][rt].y)), d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], __builtin_bit_cast(h8_t, levels8(q[s][rt].z)), d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], __builtin_bit_cast(h8_t, levels8(q[s][rt].w)), d, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) accs[rt][r] = fmaf(d[r], sc, accs[rt][r]);
-        }
-        if (g + PD < g_end)
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            q[s][rt] = __builtin_nontemporal_load(cp[rt] + 4 * (g + PD));
-            sq[s][rt] = sp[rt][g + PD];
-          }
+      for (int rt = 0; rt < RT; ++rt) {
+        q[s][rt] = __builtin_nontemporal_load(cp[rt] + 4 * g);
+        sq[s][rt] = sp[rt][g];
       }
     }
+
+    for (int sb = 0; sb < n; sb += a.sk) {
+      const int se = min(n, sb + a.sk);
+      if (sb > 0) fold_slice<TT, RT>(acc, accs, E, kq);
+      lds_fence();
+      stage_wave<TT>(a, xs, g_begin + sb, g_begin + se, lane, E);
+      // Staging already waited for its activation loads, issued after the
+      // weight loads in flight; saying so lets the loop below wait for exactly
+      // one group of weights at a time.
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+      lds_fence();
+      const _Float16* xr0 = xs + trow * a.xs_stride + kq * 32;
+      for (int gi = sb; gi < se; gi += PD) {
+#pragma unroll
+        for (int s = 0; s < PD; ++s) {
+          const int g = gi + s;
+          const bool live = g < se;
+          const _Float16* xr = xr0 + (min(g, se - 1) - sb) * kGroup;
+          h8_t xa[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xr + 8 * j);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            const float sc = live ? bf16_to_f32(sq[s][rt]) : 0.0f;
+            f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], __builtin_bit_cast(h8_t, levels8(q[s][rt].x)), d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], __builtin_bit_cast(h8_t, levels8(q[s][rt].y)), d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], __builtin_bit_cast(h8_t, levels8(q[s][rt].z)), d, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], __builtin_bit_cast(h8_t, levels8(q[s][rt].w)), d, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) accs[rt][r] = fmaf(d[r], sc, accs[rt][r]);
+          }
+          const int gn = min(g + PD, n - 1);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) {
+            q[s][rt] = __builtin_nontemporal_load(cp[rt] + 4 * gn);
+            sq[s][rt] = sp[rt][gn];
+          }
+        }
+      }
+    }
+    fold_slice<TT, RT>(acc, accs, E, kq);
   }
-  if (g_end > g_begin) fold_slice<TT, RT>(acc, accs, E, kq);
 
   // Split-K partials of this wave -> its own LDS area: red[(rt*TT + t)*16 + row].
   lds_fence();
   float* red = reinterpret_cast<float*>(smem + wave * a.wave_lds);
+  if (wave < a.nw) {
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
+    for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = kq * 4 + r;
-      if (t < TT) red[(rt * TT + t) * 16 + r16] = acc[rt][r];
-    }
+      for (int r = 0; r < 4; ++r) {
+        const int t = kq * 4 + r;
+        if (t < TT) red[(rt * TT + t) * 16 + r16] = acc[rt][r];
+      }
+  }
   __syncthreads();
 
   float* fin = reinterpret_cast<float*>(smem + a.fin_offset);
   constexpr int kOut = RT * TT * 16;
   for (int o = threadIdx.x; o < kOut; o += blockDim.x) {
     float v = 0.0f;
-    for (int w = 0; w < nw; ++w) v += reinterpret_cast<const float*>(smem + w * a.wave_lds)[o];
+    for (int w = 0; w < a.nw; ++w) v += reinterpret_cast<const float*>(smem + w * a.wave_lds)[o];
     const int rt = o / (TT * 16), t = (o >> 4) % TT, r = o & 15;
     const int64_t orow = row0 + rt * 16 + r;
     if (orow < a.n_out) {
@@ -323,8 +342,32 @@ __global__ void __launch_bounds__(512) w4a16_mfma_kernel(GemvArgs a) {
   }
   if (a.partial) {
     __syncthreads();
-    if (wave == 0) workgroup_argmax<TT>(a, fin, row0, RT * 16, lane);
+    if (wave == 0) workgroup_argmax<TT>(a, fin, row0, RT * 16, lane, wg);
   }
+}
+
+template <int TT, int RT, int PD>
+__global__ void __launch_bounds__(512) w4a16_mfma_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  mfma_workgroup<TT, RT, PD>(a, blockIdx.x, smem);
+}
+
+// Grouped launch: workgroup b runs tile b - wg_start of the last problem whose
+// wg_start <= b.
+template <int TT, int RT, int PD>
+__global__ void __launch_bounds__(512) w4a16_mfma_batch_kernel(const GemvArgs* __restrict__ table, int count) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int64_t b = blockIdx.x;
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (table[mid].wg_start <= b)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const GemvArgs a = table[lo];
+  mfma_workgroup<TT, RT, PD>(a, b - a.wg_start, smem);
 }
 
 // ----------------------------------------------------------------- dot ----
@@ -334,7 +377,8 @@ template <int TT>
 __device__ __forceinline__ void stage_block(const GemvArgs& a, _Float16* xs, unsigned* maxbuf, int gs, int ge,
                                             int (&E)[TT]) {
   const int n8 = (ge - gs) * (kGroup / 8);
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
     const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)t * a.K + (int64_t)gs * kGroup);
@@ -364,7 +408,7 @@ __global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
   constexpr int L = 64 / RW;
   constexpr int CPL = 8;
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nw = blockDim.x >> 6;
   const int sub = lane / L, li = lane % L;
   const int64_t row0 = (int64_t)blockIdx.x * nw * RW;
@@ -445,8 +489,147 @@ __global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
   }
   if (a.partial) {
     __syncthreads();
-    if (wave == 0) workgroup_argmax<TT>(a, fin, row0, nw * RW, lane);
+    if (wave == 0) workgroup_argmax<TT>(a, fin, row0, nw * RW, lane, blockIdx.x);
   }
+}
+
+// -------------------------------------------------------------- stream ----
+
+// Streaming variant of the matrix-core path: each wave owns one 16-row tile
+// over all of K and keeps PD groups of its rows in flight (PD x 64 bytes of
+// every row requested together, which is what lets the 16-row x 64-byte
+// access pattern of the MFMA operand layout stream at full HBM rate); the
+// waves of a workgroup share one staged copy of the activations per K slice,
+// so the fp16 conversion is paid once per 16 * (waves) rows.  No split-K:
+// every output comes straight from one wave's registers.
+template <int TT, int PD>
+__device__ __forceinline__ void stream_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwv = blockDim.x >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int trow = min(r16, TT - 1);
+  const int64_t tile0 = (wg * nwv + wave) * 16;
+  const int64_t kh = a.K >> 1;
+  const int G = a.G;
+  int64_t w = weight_row(a, tile0 + r16);
+  if (w < 0) w = 0;
+  const u4_t* cp = reinterpret_cast<const u4_t*>(a.packed + w * kh) + kq;
+  const uint16_t* sp = a.scales + w * G;
+  _Float16* xs = reinterpret_cast<_Float16*>(smem);
+  unsigned* maxbuf = reinterpret_cast<unsigned*>(smem + a.fin_offset);
+
+  float acc[1][4], accs[1][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) acc[0][r] = accs[0][r] = 0.0f;
+  int E[TT];
+
+  // The first slice is staged before any weight load is issued.
+  int se = min(G, a.sk);
+  stage_block<TT>(a, xs, maxbuf, 0, se, E);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  u4_t q[PD];
+  unsigned short sq[PD];
+#pragma unroll
+  for (int s = 0; s < PD; ++s) {
+    const int g = min(s, G - 1);
+    q[s] = __builtin_nontemporal_load(cp + 4 * g);
+    sq[s] = sp[g];
+  }
+  for (int sb = 0; sb < G; sb += a.sk) {
+    se = min(G, sb + a.sk);
+    if (sb > 0) {
+      fold_slice<TT, 1>(acc, accs, E, kq);
+      __syncthreads();  // every wave is done with the previous slice
+      stage_block<TT>(a, xs, maxbuf, sb, se, E);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+    const _Float16* xr0 = xs + trow * a.xs_stride + kq * 32;
+    for (int gi = sb; gi < se; gi += PD) {
+#pragma unroll
+      for (int s = 0; s < PD; ++s) {
+        const int g = gi + s;
+        const _Float16* xr = xr0 + (min(g, se - 1) - sb) * kGroup;
+        h8_t xa[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xr + 8 * j);
+        const float sc = (g < se) ? bf16_to_f32(sq[s]) : 0.0f;
+        f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], __builtin_bit_cast(h8_t, levels8(q[s].x)), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], __builtin_bit_cast(h8_t, levels8(q[s].y)), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], __builtin_bit_cast(h8_t, levels8(q[s].z)), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], __builtin_bit_cast(h8_t, levels8(q[s].w)), d, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accs[0][r] = fmaf(d[r], sc, accs[0][r]);
+        const int gn = min(g + PD, G - 1);
+        q[s] = __builtin_nontemporal_load(cp + 4 * gn);
+        sq[s] = sp[gn];
+      }
+    }
+  }
+  fold_slice<TT, 1>(acc, accs, E, kq);
+
+  const int64_t orow = tile0 + r16;
+  const bool in_range = orow < a.n_out;
+  const bool bad = in_range && weight_row(a, orow) < 0;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = kq * 4 + r;
+    if (t < TT && in_range && a.y) a.y[(int64_t)t * a.n_out + orow] = bad ? __builtin_nanf("") : acc[0][r];
+  }
+  if (a.partial) {
+    // per t: best (value, id) of this wave's 16 rows, then of the workgroup
+    int2* fin = reinterpret_cast<int2*>(smem + a.fin_offset);
+    __syncthreads();  // staging area and max buffer are free now
+    const int64_t vid = (in_range && !bad) ? (a.row_ids ? (int64_t)a.row_ids[orow] : orow) : -1;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      const int r = t & 3;
+      float v = acc[0][0];
+#pragma unroll
+      for (int i = 1; i < 4; ++i) v = (r == i) ? acc[0][i] : v;
+      int id = (kq == (t >> 2) && vid >= 0 && !__builtin_isnan(v)) ? (int)vid : -1;
+      if (id < 0) v = __builtin_nanf("");
+      wave_argmax(v, id);
+      if (lane == 0) fin[wave * TT + t] = int2{__float_as_int(v), id};
+    }
+    __syncthreads();
+    if (wave == 0 && lane < TT) {
+      float bv = __builtin_nanf("");
+      int bi = -1;
+      for (int w2 = 0; w2 < nwv; ++w2) {
+        const int2 c = fin[w2 * TT + lane];
+        if (better(__int_as_float(c.x), c.y, bv, bi)) {
+          bv = __int_as_float(c.x);
+          bi = c.y;
+        }
+      }
+      a.partial[wg * TT + lane] = int2{__float_as_int(bv), bi};
+    }
+  }
+}
+
+template <int TT, int PD>
+__global__ void __launch_bounds__(256) w4a16_stream_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  stream_workgroup<TT, PD>(a, blockIdx.x, smem);
+}
+
+template <int TT, int PD>
+__global__ void __launch_bounds__(256) w4a16_stream_batch_kernel(const GemvArgs* __restrict__ table, int count) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int64_t b = blockIdx.x;
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (table[mid].wg_start <= b)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const GemvArgs a = table[lo];
+  stream_workgroup<TT, PD>(a, b - a.wg_start, smem);
 }
 
 // ---------------------------------------------------------- argmax final ----
@@ -486,72 +669,140 @@ __global__ void __launch_bounds__(256) w4a16_argmax_final(const int2* partial, i
 
 // ------------------------------------------------------------- dispatch ----
 
+// (RT, PD) pairs the mfma kernels are built for.
+#define W4A16_MFMA_SHAPES(X) X(1, 2) X(1, 4) X(1, 8) X(4, 2) X(4, 4)
+
 template <int TT>
-hipError_t launch_t(const GemvArgs& a, const Plan& p, hipStream_t s) {
-  const dim3 grid((unsigned)p.grid), block((unsigned)(p.nw * 64));
+hipError_t launch_t(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
   if (p.variant == 2) {
-    switch (p.rt) {
-      case 1: hipLaunchKernelGGL((w4a16_mfma_kernel<TT, 1>), grid, block, p.lds, s, a); break;
-      case 2: hipLaunchKernelGGL((w4a16_mfma_kernel<TT, 2>), grid, block, p.lds, s, a); break;
-      case 4: hipLaunchKernelGGL((w4a16_mfma_kernel<TT, 4>), grid, block, p.lds, s, a); break;
-      default: return hipErrorInvalidValue;
-    }
-  } else {
-    switch (p.rt) {
-      case 1: hipLaunchKernelGGL((w4a16_dot_kernel<TT, 1>), grid, block, p.lds, s, a); break;
-      case 2: hipLaunchKernelGGL((w4a16_dot_kernel<TT, 2>), grid, block, p.lds, s, a); break;
-      case 4: hipLaunchKernelGGL((w4a16_dot_kernel<TT, 4>), grid, block, p.lds, s, a); break;
-      default: return hipErrorInvalidValue;
-    }
+#define W4A16_CASE(R, D)                                                                                \
+  if (p.rt == R && p.pd == D) {                                                                         \
+    if (table)                                                                                          \
+      hipLaunchKernelGGL((w4a16_mfma_batch_kernel<TT, R, D>), grid, block, p.lds, s, table, count);     \
+    else                                                                                                \
+      hipLaunchKernelGGL((w4a16_mfma_kernel<TT, R, D>), grid, block, p.lds, s, a);                      \
+    return hipGetLastError();                                                                           \
   }
+    W4A16_MFMA_SHAPES(W4A16_CASE)
+#undef W4A16_CASE
+    return hipErrorInvalidValue;
+  }
+  if (p.variant == 3) {
+#define W4A16_CASE(D)                                                                                   \
+  if (p.pd == D) {                                                                                      \
+    if (table)                                                                                          \
+      hipLaunchKernelGGL((w4a16_stream_batch_kernel<TT, D>), grid, block, p.lds, s, table, count);      \
+    else                                                                                                \
+      hipLaunchKernelGGL((w4a16_stream_kernel<TT, D>), grid, block, p.lds, s, a);                       \
+    return hipGetLastError();                                                                           \
+  }
+    W4A16_CASE(8)
+    W4A16_CASE(16)
+#undef W4A16_CASE
+    return hipErrorInvalidValue;
+  }
+  if (table || p.rt != 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((w4a16_dot_kernel<TT, 2>), grid, block, p.lds, s, a);
   return hipGetLastError();
+}
+
+template <typename F>
+hipError_t for_t(int T, F&& f) {
+  switch (T) {
+    case 1: return f(std::integral_constant<int, 1>{});
+    case 2: return f(std::integral_constant<int, 2>{});
+    case 3: return f(std::integral_constant<int, 3>{});
+    case 4: return f(std::integral_constant<int, 4>{});
+    case 5: return f(std::integral_constant<int, 5>{});
+    case 6: return f(std::integral_constant<int, 6>{});
+    case 7: return f(std::integral_constant<int, 7>{});
+    case 8: return f(std::integral_constant<int, 8>{});
+    default: return hipErrorInvalidValue;
+  }
 }
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 }  // namespace
 
-// Tiling of the mfma variant.  Enough workgroups to cover the 256 CUs
-// (16-row tiles, grouped by 2 or 4 for large heads so activations are staged
-// once per 32 or 64 rows); the waves of a workgroup split K so that a small
-// matrix still puts ~12 waves of weight loads on every CU.
-Plan plan_mfma(GemvArgs& a, int T) {
-  Plan p{};
-  p.variant = 2;
-  const int64_t tiles = cdiv(a.n_out, 16);
-  p.rt = tiles >= 2048 ? 4 : (tiles >= 768 ? 2 : 1);
-  p.grid = cdiv(tiles, p.rt);
-  const int pd = (p.rt == 1) ? 4 : 2;  // prefetch depth of the kernel; slices are multiples of it
-  const int fin_bytes = p.rt * T * 16 * 4;
-  int nw = (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(3072, p.grid)));
-  nw = std::min(nw, a.G);
-  int gpw = 0, sk = 0;
+// Tiling of one problem for a fixed tile height (rt), prefetch depth (pd)
+// and at most nw_max waves.  K is split into per-wave ranges of gpw groups, a
+// multiple of pd (the last wave may hold fewer); the activation slice staged
+// in LDS holds sk groups (all of a wave's range when 64 KB allow it, else a
+// multiple of pd).
+void plan_mfma_fixed(GemvArgs& a, int T, int rt, int pd, int nw_max, int* lds, int64_t* grid) {
+  const int fin_bytes = rt * T * 16 * 4;
+  int nw = std::max(1, std::min(nw_max, a.G));
+  int gpw = 0, nw_eff = 0, sk = 0;
   for (;; --nw) {
-    gpw = (int)cdiv(a.G, nw);
-    const int nw_eff = (int)cdiv(a.G, gpw);
+    gpw = (int)(cdiv(cdiv(a.G, nw), pd) * pd);
+    nw_eff = (int)cdiv(a.G, gpw);
     const int per_wave = (kLdsCap - fin_bytes) / nw_eff;
     sk = (per_wave / T - 16) / (kGroup * 2);
     if (sk >= gpw) {
       sk = gpw;
-      nw = nw_eff;
       break;
     }
     if (sk >= pd || nw == 1) {
       sk = std::max(pd, sk - sk % pd);
-      nw = nw_eff;
       break;
     }
   }
-  p.nw = nw;
+  a.nw = nw_eff;
   a.gpw = gpw;
   a.sk = sk;
   a.xs_stride = sk * kGroup + 8;  // 16-byte pad between token rows
-  int wave_lds = T * a.xs_stride * 2;
-  wave_lds = std::max(wave_lds, p.rt * T * 16 * 4);
+  int wave_lds = std::max(T * a.xs_stride * 2, rt * T * 16 * 4);
   a.wave_lds = (wave_lds + 15) & ~15;
-  a.fin_offset = nw * a.wave_lds;
-  p.lds = a.fin_offset + fin_bytes;
+  a.fin_offset = nw_eff * a.wave_lds;
+  *lds = a.fin_offset + fin_bytes;
+  *grid = cdiv(cdiv(a.n_out, 16), rt);
+}
+
+// Tiling of a single matrix-core launch.  Tall matrices (>= 1024 tiles of
+// 16 rows) stream: one wave per 16-row tile over all of K, four waves per
+// workgroup sharing the staged activations.  Shorter ones split K over the
+// waves of a workgroup (16 rows per workgroup) so that they still put ~12
+// waves of weight loads on every CU; the prefetch depth is the largest the
+// per-wave K range fills.
+Plan plan_mfma(GemvArgs& a, int T) {
+  Plan p{};
+  const int64_t tiles = cdiv(a.n_out, 16);
+  if (tiles >= 1024) {
+    p.variant = 3;
+    p.rt = 1;
+    p.pd = (a.G % 16 == 0) ? 16 : 8;
+    plan_stream(a, T, p.pd, 4, &p.lds, &p.grid);
+    p.threads = 4 * 64;
+    return p;
+  }
+  p.variant = 2;
+  p.rt = 1;
+  const int nw_max = (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(3072, tiles)));
+  const int gpw_est = (int)cdiv(a.G, std::min(nw_max, a.G));
+  p.pd = gpw_est >= 8 ? 8 : (gpw_est >= 4 ? 4 : 2);
+  plan_mfma_fixed(a, T, p.rt, p.pd, nw_max, &p.lds, &p.grid);
+  p.threads = a.nw * 64;
   return p;
+}
+
+// Tiling of the streaming variant: nwv waves (16-row tiles) per workgroup,
+// the activation slice staged in LDS holds sk groups (all of K when 64 KB
+// allow it, else a multiple of pd).
+void plan_stream(GemvArgs& a, int T, int pd, int nwv, int* lds, int64_t* grid) {
+  const int small = std::max(nwv * T * 4, nwv * T * 8);  // max buffer / argmax partials
+  int sk = ((kLdsCap - small - 16) / T - 16) / (kGroup * 2);
+  if (sk < a.G) sk = std::max(pd, sk - sk % pd);
+  else sk = a.G;
+  a.nw = nwv;
+  a.gpw = a.G;
+  a.sk = sk;
+  a.xs_stride = sk * kGroup + 8;
+  a.wave_lds = 0;
+  a.fin_offset = (T * a.xs_stride * 2 + 15) & ~15;
+  *lds = a.fin_offset + small;
+  *grid = cdiv(a.n_out, 16LL * nwv);
 }
 
 // Tiling of the dot variant: 2 rows per wave (32 lanes per row), 8 waves,
@@ -560,37 +811,34 @@ Plan plan_dot(GemvArgs& a, int T) {
   Plan p{};
   p.variant = 1;
   p.rt = 2;  // rows per wave
-  p.nw = 8;
+  const int nw = 8;
+  p.threads = nw * 64;
   const int L = 64 / p.rt;
-  p.grid = cdiv(a.n_out, (int64_t)p.rt * p.nw);
+  p.grid = cdiv(a.n_out, (int64_t)p.rt * nw);
   const int max_sk_regs = 8 * L / 4;  // CPL chunks per lane, 4 chunks per group
-  const int fin_bytes = std::max(p.nw * T * 4, (int)cdiv(p.nw * p.rt, 16) * T * 16 * 4);
+  const int fin_bytes = std::max(nw * T * 4, (int)cdiv(nw * p.rt, 16) * T * 16 * 4);
   int sk_lds = ((kLdsCap - fin_bytes) / T - 16) / (kGroup * 2);
+  a.nw = nw;
   a.sk = std::max(1, std::min({a.G, max_sk_regs, sk_lds}));
   a.gpw = a.G;
   a.xs_stride = a.sk * kGroup + 8;
   a.wave_lds = 0;
   int xs_bytes = T * a.xs_stride * 2;
-  xs_bytes = std::max(xs_bytes, (int)cdiv(p.nw * p.rt, 16) * T * 16 * 4);  // also holds final values
-  a.fin_offset = (xs_bytes + 15) & ~15;                                  // max buffer follows
-  p.lds = a.fin_offset + p.nw * T * 4;
+  xs_bytes = std::max(xs_bytes, (int)cdiv(nw * p.rt, 16) * T * 16 * 4);  // also holds final values
+  a.fin_offset = (xs_bytes + 15) & ~15;                                 // max buffer follows
+  p.lds = a.fin_offset + nw * T * 4;
   return p;
 }
 
 int64_t max_workgroups(int64_t n_out) { return cdiv(n_out, 16); }
 
 hipError_t launch(const GemvArgs& a, const Plan& p, int T, hipStream_t s) {
-  switch (T) {
-    case 1: return launch_t<1>(a, p, s);
-    case 2: return launch_t<2>(a, p, s);
-    case 3: return launch_t<3>(a, p, s);
-    case 4: return launch_t<4>(a, p, s);
-    case 5: return launch_t<5>(a, p, s);
-    case 6: return launch_t<6>(a, p, s);
-    case 7: return launch_t<7>(a, p, s);
-    case 8: return launch_t<8>(a, p, s);
-    default: return hipErrorInvalidValue;
-  }
+  return for_t(T, [&](auto tt) { return launch_t<decltype(tt)::value>(a, nullptr, 0, p, s); });
+}
+
+hipError_t launch_batch(const GemvArgs* table_dev, int count, const Plan& p, int T, hipStream_t s) {
+  GemvArgs unused{};
+  return for_t(T, [&](auto tt) { return launch_t<decltype(tt)::value>(unused, table_dev, count, p, s); });
 }
 
 hipError_t launch_argmax_final(const int2* partial, int64_t nparts, int T, int32_t* id, float* val, hipStream_t s) {

@@ -1,0 +1,82 @@
+"""GPU parity of the grouped launch (many matmuls in one kernel launch)."""
+import os
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import assert_parity, dev, host, say, sample_rows
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+SHAPES = [(1024, 1024), (300, 5120), (17, 128), (4099, 1280), (2000, 17408), (7168, 5120)]
+
+
+@pytest.fixture(scope="module")
+def w4():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import speculative_verify_gemv_amd as w4a16
+    w4a16.load_library()
+    return w4a16
+
+
+def build_case(T, seed0):
+    probs, host_side = [], []
+    for i, (N, K) in enumerate(SHAPES):
+        tid = seed0 + i
+        p, s = synth.weight(tid, N, K)
+        x = synth.activations(tid, T, K)
+        y = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda")
+        probs.append((dev(p), dev(s), dev(x), y))
+        host_side.append((p, s, x))
+    return probs, host_side
+
+
+def check_outputs(probs, host_side, what):
+    for (pd, sd, xd, y), (p, s, x) in zip(probs, host_side):
+        N = p.shape[0]
+        rows = sample_rows(N, 256, seed=N) if N > 2048 else np.arange(N, dtype=np.int32)
+        y_ref, a_ref = oracle.gather(rows, p, s, x)
+        assert_parity(host(y)[:, rows], y_ref, a_ref, f"{what} N={N} K={p.shape[1] * 2}")
+
+
+@pytest.mark.parametrize("tile", [None, "stream,16", "split,1,4,4", "split,4,4,4"])
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_batch_matches_oracle(w4, tile, T, monkeypatch):
+    if tile is not None:
+        monkeypatch.setenv("W4A16_BATCH_TILE", tile)
+    else:
+        monkeypatch.delenv("W4A16_BATCH_TILE", raising=False)
+    say(f"batch tile={tile} T={T}")
+    probs, host_side = build_case(T, 600 + 10 * T)
+    b = w4.Batch(probs, T)
+    b.run()
+    check_outputs(probs, host_side, f"batch {tile} T={T}")
+    first = [host(y).copy() for *_, y in probs]
+    b.run()
+    for f, (*_, y) in zip(first, probs):
+        assert np.array_equal(f, host(y)), "second run differs"
+
+
+def test_batch_equals_single_launch_within_tolerance(w4):
+    T = 4
+    probs, host_side = build_case(T, 700)
+    w4.Batch(probs, T).run()
+    for (pd, sd, xd, y), (p, s, x) in zip(probs, host_side):
+        y1 = host(w4.matmul(pd, sd, xd))
+        yb = host(y)
+        # same arithmetic up to fp32 summation order
+        y_ref, a_ref = oracle.matmul(p, s, x) if p.shape[0] <= 2048 else (None, None)
+        if y_ref is not None:
+            assert_parity(y1, y_ref, a_ref, "single")
+            assert_parity(yb, y_ref, a_ref, "batch")
+
+
+def test_batch_rejects_bad_tables(w4):
+    lib = w4.load_library()
+    junk = torch.zeros(256, dtype=torch.uint8)
+    junk_dev = junk.cuda()
+    assert lib.w4a16_matmul_batch(junk.data_ptr(), junk_dev.data_ptr(), None) == 2  # not a table

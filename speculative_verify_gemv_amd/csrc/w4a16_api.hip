@@ -106,8 +106,9 @@ BatchTile batch_tile() {
   BatchTile b;
   if (const char* e = std::getenv("W4A16_BATCH_TILE")) {
     int x = 0, y = 0, z = 0;
-    if (std::sscanf(e, "stream,%d", &x) == 1 && (x == 8 || x == 16)) {
+    if (std::sscanf(e, "stream,%d,%d", &x, &y) == 2 && (x == 8 || x == 16) && y >= 1 && y <= 4) {
       b.pd = x;
+      b.nw = y;
     } else if (std::sscanf(e, "split,%d,%d,%d", &x, &y, &z) == 3 && (x == 1 || x == 4) &&
                (y == 2 || y == 4 || y == 8) && !(x == 4 && y == 8) && z >= 1 && z <= 8) {
       b.variant = 2;

@@ -28,6 +28,8 @@ struct GemvArgs {
   int32_t xs_stride;       // halves per staged token row
   int32_t wave_lds;        // bytes of LDS per wave
   int32_t fin_offset;      // byte offset of the final-value area
+  int32_t vec_scales;      // 1: scale rows are 16-byte aligned and G % 8 == 0 (8 scales per load)
+  int32_t reserved;
 };
 
 struct Plan {

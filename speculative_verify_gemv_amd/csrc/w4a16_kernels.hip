@@ -41,6 +41,8 @@
 #include <math.h>
 
 #include <algorithm>
+#include <cstdio>
+#include <cstdlib>
 #include <type_traits>
 
 #include "w4a16_internal.h"
@@ -268,6 +270,7 @@ __device__ __forceinline__ void mfma_workgroup(const GemvArgs& a, int64_t wg, un
         q[s][rt] = __builtin_nontemporal_load(cp[rt] + 4 * g);
         sq[s][rt] = sp[rt][g];
       }
+      __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
     }
 
     for (int sb = 0; sb < n; sb += a.sk) {
@@ -307,6 +310,7 @@ __device__ __forceinline__ void mfma_workgroup(const GemvArgs& a, int64_t wg, un
             q[s][rt] = __builtin_nontemporal_load(cp[rt] + 4 * gn);
             sq[s][rt] = sp[rt][gn];
           }
+          __builtin_amdgcn_sched_barrier(0);  // keep this slot's reloads here
         }
       }
     }
@@ -495,6 +499,106 @@ __global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
 
 // -------------------------------------------------------------- stream ----
 
+// Weight-code load of the streaming kernel.  Default cache policy: the two
+// 64-byte halves of a 128-byte line (groups g and g+1 of a row) then merge
+// into one L2 request in the vector L1; the nontemporal hint would send each
+// half on its own and double the requests in flight.
+__device__ __forceinline__ u4_t load_codes(const u4_t* p) { return *p; }
+
+// bf16 scale e of eight packed in v (element order = memory order) -> fp32.
+__device__ __forceinline__ float scale_of(u4_t v, int e) {
+  const unsigned w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+  return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
+// The K loop of one wave of the streaming kernel: PD groups of codes in
+// flight.  VS: the row's scales are read eight groups (16 bytes) at a time,
+// one load per 8 groups instead of one per group (needs G % 8 == 0 and
+// 16-byte aligned scale rows); otherwise one 2-byte load per group.
+template <int TT, int PD, bool VS>
+__device__ __forceinline__ void stream_rows(const GemvArgs& a, const u4_t* cp, const uint16_t* sp, _Float16* xs,
+                                            unsigned* maxbuf, int trow, int kq, float (&acc)[1][4]) {
+  constexpr int NV = VS ? PD / 8 : 1;  // scale vectors per ring cycle
+  static_assert(!VS || PD % 8 == 0, "vector scales need PD % 8 == 0");
+  const int G = a.G;
+  float accs[1][4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) accs[0][r] = 0.0f;
+  int E[TT];
+
+  // The first slice is staged before any weight load is issued.
+  int se = min(G, a.sk);
+  stage_block<TT>(a, xs, maxbuf, 0, se, E);
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+  const u4_t* svp = reinterpret_cast<const u4_t*>(sp);
+  const int nvec = G / 8;
+  u4_t sv[NV];
+  if constexpr (VS) {
+#pragma unroll
+    for (int c = 0; c < NV; ++c) sv[c] = svp[min(c, nvec - 1)];
+  }
+  u4_t q[PD];
+  unsigned short sq[PD];
+#pragma unroll
+  for (int s = 0; s < PD; ++s) {
+    const int g = min(s, G - 1);
+    if constexpr (!VS) sq[s] = sp[g];
+    q[s] = load_codes(cp + 4 * g);
+    __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
+  }
+  for (int sb = 0; sb < G; sb += a.sk) {
+    se = min(G, sb + a.sk);
+    if (sb > 0) {
+      fold_slice<TT, 1>(acc, accs, E, kq);
+      __syncthreads();  // every wave is done with the previous slice
+      stage_block<TT>(a, xs, maxbuf, sb, se, E);
+      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    }
+    const _Float16* xr0 = xs + trow * a.xs_stride + kq * 32;
+    for (int gi = sb; gi < se; gi += PD) {
+      u4_t svn[NV];
+      if constexpr (VS) {
+#pragma unroll
+        for (int c = 0; c < NV; ++c) svn[c] = svp[min(gi / 8 + NV + c, nvec - 1)];
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int s = 0; s < PD; ++s) {
+        const int g = gi + s;
+        const _Float16* xr = xr0 + (min(g, se - 1) - sb) * kGroup;
+        h8_t xa[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xr + 8 * j);
+        float sc;
+        if constexpr (VS)
+          sc = scale_of(sv[s / 8], s % 8);
+        else
+          sc = bf16_to_f32(sq[s]);
+        sc = (g < se) ? sc : 0.0f;
+        f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], __builtin_bit_cast(h8_t, levels8(q[s].x)), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], __builtin_bit_cast(h8_t, levels8(q[s].y)), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], __builtin_bit_cast(h8_t, levels8(q[s].z)), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], __builtin_bit_cast(h8_t, levels8(q[s].w)), d, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accs[0][r] = fmaf(d[r], sc, accs[0][r]);
+        const int gn = min(g + PD, G - 1);
+        if constexpr (!VS) sq[s] = sp[gn];
+        q[s] = load_codes(cp + 4 * gn);
+        // keep this slot's reload here: sunk to the end of the loop, the
+        // reloads would make every iteration wait for the whole ring
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (VS) {
+#pragma unroll
+        for (int c = 0; c < NV; ++c) sv[c] = svn[c];
+      }
+    }
+  }
+  fold_slice<TT, 1>(acc, accs, E, kq);
+}
+
 // Streaming variant of the matrix-core path: each wave owns one 16-row tile
 // over all of K and keeps PD groups of its rows in flight (PD x 64 bytes of
 // every row requested together, which is what lets the 16-row x 64-byte
@@ -511,64 +615,20 @@ __device__ __forceinline__ void stream_workgroup(const GemvArgs& a, int64_t wg, 
   const int trow = min(r16, TT - 1);
   const int64_t tile0 = (wg * nwv + wave) * 16;
   const int64_t kh = a.K >> 1;
-  const int G = a.G;
   int64_t w = weight_row(a, tile0 + r16);
   if (w < 0) w = 0;
   const u4_t* cp = reinterpret_cast<const u4_t*>(a.packed + w * kh) + kq;
-  const uint16_t* sp = a.scales + w * G;
+  const uint16_t* sp = a.scales + w * a.G;
   _Float16* xs = reinterpret_cast<_Float16*>(smem);
   unsigned* maxbuf = reinterpret_cast<unsigned*>(smem + a.fin_offset);
 
-  float acc[1][4], accs[1][4];
+  float acc[1][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) acc[0][r] = accs[0][r] = 0.0f;
-  int E[TT];
-
-  // The first slice is staged before any weight load is issued.
-  int se = min(G, a.sk);
-  stage_block<TT>(a, xs, maxbuf, 0, se, E);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-
-  u4_t q[PD];
-  unsigned short sq[PD];
-#pragma unroll
-  for (int s = 0; s < PD; ++s) {
-    const int g = min(s, G - 1);
-    q[s] = __builtin_nontemporal_load(cp + 4 * g);
-    sq[s] = sp[g];
-  }
-  for (int sb = 0; sb < G; sb += a.sk) {
-    se = min(G, sb + a.sk);
-    if (sb > 0) {
-      fold_slice<TT, 1>(acc, accs, E, kq);
-      __syncthreads();  // every wave is done with the previous slice
-      stage_block<TT>(a, xs, maxbuf, sb, se, E);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    }
-    const _Float16* xr0 = xs + trow * a.xs_stride + kq * 32;
-    for (int gi = sb; gi < se; gi += PD) {
-#pragma unroll
-      for (int s = 0; s < PD; ++s) {
-        const int g = gi + s;
-        const _Float16* xr = xr0 + (min(g, se - 1) - sb) * kGroup;
-        h8_t xa[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xr + 8 * j);
-        const float sc = (g < se) ? bf16_to_f32(sq[s]) : 0.0f;
-        f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], __builtin_bit_cast(h8_t, levels8(q[s].x)), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], __builtin_bit_cast(h8_t, levels8(q[s].y)), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], __builtin_bit_cast(h8_t, levels8(q[s].z)), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], __builtin_bit_cast(h8_t, levels8(q[s].w)), d, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) accs[0][r] = fmaf(d[r], sc, accs[0][r]);
-        const int gn = min(g + PD, G - 1);
-        q[s] = __builtin_nontemporal_load(cp + 4 * gn);
-        sq[s] = sp[gn];
-      }
-    }
-  }
-  fold_slice<TT, 1>(acc, accs, E, kq);
+  for (int r = 0; r < 4; ++r) acc[0][r] = 0.0f;
+  if (a.vec_scales)
+    stream_rows<TT, PD, true>(a, cp, sp, xs, maxbuf, trow, kq, acc);
+  else
+    stream_rows<TT, PD, false>(a, cp, sp, xs, maxbuf, trow, kq, acc);
 
   const int64_t orow = tile0 + r16;
   const bool in_range = orow < a.n_out;
@@ -724,6 +784,17 @@ hipError_t for_t(int T, F&& f) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// W4A16_STREAM="pd,waves" overrides the streaming tile (for measurement).
+void stream_override(int* pd, int* nwv) {
+  if (const char* e = std::getenv("W4A16_STREAM")) {
+    int x = 0, y = 0;
+    if (std::sscanf(e, "%d,%d", &x, &y) == 2 && (x == 8 || x == 16) && y >= 1 && y <= 4) {
+      *pd = x;
+      *nwv = y;
+    }
+  }
+}
+
 }  // namespace
 
 // Tiling of one problem for a fixed tile height (rt), prefetch depth (pd)
@@ -773,8 +844,10 @@ Plan plan_mfma(GemvArgs& a, int T) {
     p.variant = 3;
     p.rt = 1;
     p.pd = (a.G % 16 == 0) ? 16 : 8;
-    plan_stream(a, T, p.pd, 4, &p.lds, &p.grid);
-    p.threads = 4 * 64;
+    int nwv = 4;
+    stream_override(&p.pd, &nwv);
+    plan_stream(a, T, p.pd, nwv, &p.lds, &p.grid);
+    p.threads = nwv * 64;
     return p;
   }
   p.variant = 2;
@@ -791,6 +864,7 @@ Plan plan_mfma(GemvArgs& a, int T) {
 // the activation slice staged in LDS holds sk groups (all of K when 64 KB
 // allow it, else a multiple of pd).
 void plan_stream(GemvArgs& a, int T, int pd, int nwv, int* lds, int64_t* grid) {
+  a.vec_scales = (a.G % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15) == 0) ? 1 : 0;
   const int small = std::max(nwv * T * 4, nwv * T * 8);  // max buffer / argmax partials
   int sk = ((kLdsCap - small - 16) / T - 16) / (kGroup * 2);
   if (sk < a.G) sk = std::max(pd, sk - sk % pd);

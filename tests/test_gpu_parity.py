@@ -49,7 +49,10 @@ def test_small_matrix_all_t(w4, variant):
 
 
 RAGGED = [(1, 128, 1), (17, 384, 3), (33, 1152, 8), (100, 256, 5), (1003, 640, 2), (4099, 1280, 4),
-          (257, 5120, 7), (31, 17408, 8), (2049, 128, 6)]
+          (257, 5120, 7), (31, 17408, 8), (2049, 128, 6),
+          # tall enough for the streaming kernel: 8-group scale loads, and the
+          # one-scale-per-load path (G = 9 groups, not a multiple of 8)
+          (16400, 1024, 1), (17003, 1152, 3), (16413, 2304, 8)]
 
 
 @pytest.mark.parametrize("variant", VARIANTS)
@@ -149,6 +152,20 @@ def test_rows_permute_bitwise_and_identical_rows(w4, variant):
     perm = np.random.default_rng(1).permutation(N)
     yp = run_matmul(w4, variant, dev(p[perm]), dev(s[perm]), x)
     assert np.array_equal(yp, y[:, perm])
+
+
+@pytest.mark.parametrize("variant", VARIANTS)
+def test_misaligned_scale_rows(w4, variant):
+    """Scales starting 2 bytes past a 16-byte boundary (allowed by the ABI)."""
+    N, K, T = 16500, 1024, 4
+    p, s = synth.weight(48, N, K)
+    x = synth.activations(48, T, K)
+    buf = torch.zeros(s.size + 8, dtype=torch.int16, device="cuda")
+    sd = buf[1:1 + s.size].view(N, K // 128)
+    sd.copy_(torch.from_numpy(s.view(np.int16)).cuda())
+    assert sd.data_ptr() % 16 == 2
+    y_ref, a_ref = oracle.matmul(p, s, x)
+    assert_parity(run_matmul(w4, variant, dev(p), sd, x), y_ref, a_ref, "misaligned scales")
 
 
 @pytest.mark.parametrize("variant", VARIANTS)

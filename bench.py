@@ -10,13 +10,19 @@ Cache).
 Reported (one JSON line): weight GB/s of the whole step (value), decode
 cycles/s, the grouped body kernel's achieved bandwidth against the 8 TB/s
 HBM peak (roofline, timed with HIP events on the launch stream), the body
-pass at T = 1, 4, 8, and the CPU oracle's rate on a bounded sample.
+pass at T = 1, 4, 8, the same step as 257 separate launches replayed from
+a captured HIP graph, and the CPU oracle's rate on a bounded sample.
+
+--pmc-pass runs one untimed body pass and one lm_head call after a 1 GiB
+device copy (the calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE).
 """
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -31,6 +37,9 @@ from speculative_verify_gemv_amd import metrics  # noqa: E402
 METRIC = "weight GB/s and % of HBM peak at T=1/4/8 (27B-class shapes); decode cycles/s"
 PEAK_GBPS = 8000.0
 WORKLOAD = "decode_weight_pass_64x(qkv,o,gate_up,down)+lm_head_T4"
+KERNEL_SOURCE = os.path.join(ROOT, "speculative_verify_gemv_amd", "csrc", "w4a16_kernels.hip")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_body_pass_T4.md")
+COPY_BYTES = 1 << 30
 
 
 def parse():
@@ -42,6 +51,8 @@ def parse():
     ap.add_argument("--layers", type=int, default=synth.LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-t", action="store_true")
+    ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--pmc-pass", action="store_true", help="one untimed pass for counter collection")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     return ap.parse_args()
 
@@ -55,6 +66,31 @@ def to_dev(a, torch):
     if t.dtype == torch.uint16:
         t = t.view(torch.int16)
     return t.cuda()
+
+
+def kernel_source_hash():
+    """sha256 of the kernel source with comments and blank space removed (a
+    comment edit does not change the kernels the counters were taken on)."""
+    with open(KERNEL_SOURCE) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(line.strip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per body-pass launch from the committed counter summary, or
+    None when it is absent or was taken on a different kernel source."""
+    try:
+        text = open(TRAFFIC_FILE).read()
+    except OSError:
+        return None
+    h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
+    b = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
+    if not h or not b or h.group(1) != kernel_source_hash():
+        return None
+    return int(b.group(1))
 
 
 def main():
@@ -104,13 +140,22 @@ def main():
     head_ws = torch.empty(w4a16.workspace_bytes(hn, T), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
-    def step():
+    def head(s):
+        w4a16.head_gather(head_p, head_s, head_x, scores=True, argmax=True, out=head_y, workspace=head_ws, stream=s)
+
+    if args.pmc_pass:
+        src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)  # calibration: reads and writes exactly 1 GiB
         batch.run(stream)
-        w4a16.head_gather(head_p, head_s, head_x, scores=True, argmax=True, out=head_y, workspace=head_ws,
-                          stream=stream)
+        head(stream)
+        torch.cuda.synchronize()
+        log(f"pmc pass done: copy {COPY_BYTES} B, body pass {body_bytes} B, lm_head {head_bytes} B")
+        return
 
     for _ in range(args.warmup):
-        step()
+        batch.run(stream)
+        head(stream)
     torch.cuda.synchronize()
 
     K_steps = args.steps
@@ -122,8 +167,7 @@ def main():
         ev[i][0].record(stream)
         batch.run(stream)
         ev[i][1].record(stream)
-        w4a16.head_gather(head_p, head_s, head_x, scores=True, argmax=True, out=head_y, workspace=head_ws,
-                          stream=stream)
+        head(stream)
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
@@ -156,6 +200,14 @@ def main():
                               "pct_hbm_peak": round(100 * g / PEAK_GBPS, 2)}
             log(f"body pass T={Tp}: {ms:.4f} ms, {g:.0f} GB/s ({100 * g / PEAK_GBPS:.1f}% of 8 TB/s)")
 
+    # ---- the same step as 257 separate launches, replayed from a HIP graph ----
+    graph_pass = None
+    if not args.no_graph:
+        graph_pass = graph_step(torch, w4a16, probs, head, reps=5)
+        g = metrics.gbps(step_bytes, graph_pass["ms_per_step"])
+        graph_pass["weight_GBps"] = round(g, 1)
+        log(f"257-launch graph step: {graph_pass['ms_per_step']:.4f} ms, {g:.0f} GB/s")
+
     # ---- CPU baseline: the oracle on a bounded sample of the same pass ----
     cpu = None
     if not args.no_cpu_baseline:
@@ -186,6 +238,7 @@ def main():
         "cycles_per_s": round(1000.0 / ms_step, 2),
         "pct_hbm_peak": round(100 * value / PEAK_GBPS, 2),
         "per_T_body_pass": per_t,
+        "graph_257_launches": graph_pass,
         "roofline": {
             "kernel": "grouped body pass (64 x 4 projections, one launch)",
             "bound": "hbm",
@@ -193,13 +246,41 @@ def main():
             "peak": PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": body_bytes,
             "avg_launch_ms": round(body_ms_avg, 4),
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def graph_step(torch, w4a16, probs, head, reps):
+    """One step as 256 matmul launches plus the lm_head call, captured once
+    into a HIP graph and replayed (launch overhead off the host)."""
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        for pd, sd, x, y in probs:  # warm the plans and the device check outside capture
+            w4a16.matmul(pd, sd, x, out=y)
+        head(side)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        s = torch.cuda.current_stream()
+        for pd, sd, x, y in probs:
+            w4a16.matmul(pd, sd, x, out=y, stream=s)
+        head(s)
+    g.replay()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    return {"ms_per_step": round(e0.elapsed_time(e1) / reps, 4), "launches": len(probs) + 2}
 
 
 def cpu_baseline(T, target_s):

@@ -74,7 +74,7 @@ typedef enum {
 typedef enum {
   W4A16_VARIANT_AUTO = 0,
   W4A16_VARIANT_DOT = 1, /* VALU dot products, split-K across lanes, cross-lane reduction */
-  W4A16_VARIANT_MFMA = 2 /* fp16 matrix cores, tokens padded to 16, split-K across waves */
+  W4A16_VARIANT_MFMA = 2 /* fp16 matrix cores, tokens padded to 16 rows */
 } w4a16_variant;
 
 /*

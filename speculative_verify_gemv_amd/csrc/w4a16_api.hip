@@ -86,7 +86,7 @@ struct TableHeader {
   int32_t T;
   int32_t variant;
   int32_t rt;
-  int32_t pd;
+  int32_t reserved1;
   int32_t threads;
   int32_t lds;
   int32_t reserved0;
@@ -95,29 +95,15 @@ struct TableHeader {
 };
 static_assert(sizeof(TableHeader) == 64, "table header size");
 
-// Kernel of grouped launches: the streaming matrix-core kernel, four 16-row
-// tiles per workgroup, 8 groups of each row in flight.  W4A16_BATCH_TILE =
-// "stream,pd" or "split,rt,pd,nw" overrides it (for measurement).
-struct BatchTile {
-  int variant = 3, rt = 1, pd = 8, nw = 4;
-};
-
-BatchTile batch_tile() {
-  BatchTile b;
-  if (const char* e = std::getenv("W4A16_BATCH_TILE")) {
-    int x = 0, y = 0, z = 0;
-    if (std::sscanf(e, "stream,%d,%d", &x, &y) == 2 && (x == 8 || x == 16) && y >= 1 && y <= 4) {
-      b.pd = x;
-      b.nw = y;
-    } else if (std::sscanf(e, "split,%d,%d,%d", &x, &y, &z) == 3 && (x == 1 || x == 4) &&
-               (y == 2 || y == 4 || y == 8) && !(x == 4 && y == 8) && z >= 1 && z <= 8) {
-      b.variant = 2;
-      b.rt = x;
-      b.pd = y;
-      b.nw = z;
-    }
-  }
-  return b;
+// Tile of grouped launches: shared workgroups; at T <= 2 four waves of two
+// 16-row tiles, above that eight waves of four (the larger workgroup shares
+// one staged copy of the bigger activation block among more rows).
+// W4A16_BATCH_TILE = "split|shared,rt,waves" overrides it (for measurement).
+w4a16::Tile batch_tile(int T) {
+  w4a16::Tile t = T <= 2 ? w4a16::Tile{w4a16::kShared, 2, 4} : w4a16::Tile{w4a16::kShared, 4, 8};
+  w4a16::Tile o;
+  if (w4a16::parse_tile(std::getenv("W4A16_BATCH_TILE"), &o)) t = o;
+  return t;
 }
 
 }  // namespace
@@ -208,11 +194,11 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
     if (!aligned(q.packed_u4, 16) || !aligned(q.x_bf16, 16) || !aligned(q.scales_bf16, 2) || !aligned(q.y_f32, 4))
       return W4A16_ERR_MISALIGNED;
   }
-  const BatchTile bt = batch_tile();
+  const w4a16::Tile bt = batch_tile(T);
   auto* hdr = static_cast<TableHeader*>(table_host);
   auto* args = reinterpret_cast<w4a16::GemvArgs*>(hdr + 1);
   int64_t grid = 0;
-  int lds = 0, nw = 1;
+  int lds = 0, threads = 64;
   for (int32_t i = 0; i < count; ++i) {
     const w4a16_problem& q = problems[i];
     w4a16::GemvArgs a{};
@@ -224,20 +210,15 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
     a.n_rows = q.N;
     a.K = (int32_t)q.K;
     a.G = (int32_t)(q.K / W4A16_GROUP);
-    int l = 0;
-    int64_t g = 0;
-    if (bt.variant == 3)
-      w4a16::plan_stream(a, T, bt.pd, bt.nw, &l, &g);
-    else
-      w4a16::plan_mfma_fixed(a, T, bt.rt, bt.pd, bt.nw, &l, &g);
+    const w4a16::Plan p = w4a16::plan_tile(a, T, bt);
     a.wg_start = grid;
-    grid += g;
-    lds = std::max(lds, l);
-    nw = std::max(nw, (int)a.nw);
+    grid += p.grid;
+    lds = std::max(lds, p.lds);
+    threads = std::max(threads, p.threads);
     args[i] = a;
   }
   if (grid > 0x7fffffffLL) return W4A16_ERR_BAD_SHAPE;
-  *hdr = TableHeader{kTableMagic, W4A16_ABI_VERSION, count, T, bt.variant, bt.rt, bt.pd, nw * 64, lds, 0, grid,
+  *hdr = TableHeader{kTableMagic, W4A16_ABI_VERSION, count, T, bt.shape, bt.rt, 0, threads, lds, 0, grid,
                      {0, 0}};
   return W4A16_OK;
 }
@@ -251,10 +232,12 @@ w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, h
     return W4A16_ERR_BAD_SHAPE;
   if (w4a16_status s = check_device()) return s;
   w4a16::Plan p{};
-  if (hdr->variant != 2 && hdr->variant != 3) return W4A16_ERR_BAD_SHAPE;
+  if (hdr->variant != w4a16::kSplit && hdr->variant != w4a16::kShared) return W4A16_ERR_BAD_SHAPE;
+  if (hdr->rt != 1 && hdr->rt != 2 && hdr->rt != 4) return W4A16_ERR_BAD_SHAPE;
+  if (hdr->threads < 64 || hdr->threads > 512 || hdr->threads % 64 || hdr->lds < 0 || hdr->lds > 65536)
+    return W4A16_ERR_BAD_SHAPE;
   p.variant = hdr->variant;
   p.rt = hdr->rt;
-  p.pd = hdr->pd;
   p.threads = hdr->threads;
   p.grid = hdr->grid;
   p.lds = hdr->lds;

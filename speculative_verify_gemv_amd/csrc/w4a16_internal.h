@@ -32,21 +32,33 @@ struct GemvArgs {
   int32_t reserved;
 };
 
+// Kernel shapes.  Dot: lanes split each row's K (v_dot2).  Split: matrix-core
+// workgroup whose waves split K over the same 16-row tiles.  Shared:
+// matrix-core workgroup whose waves own different tiles over all of K.
+constexpr int kDot = 1, kSplit = 2, kShared = 3;
+
+// Matrix-core tile choice: shape, 16-row tiles per wave, waves per workgroup.
+struct Tile {
+  int shape;
+  int rt;
+  int nw;
+};
+
 struct Plan {
-  int variant;   // 1 dot, 2 mfma (split-K), 3 mfma (streaming)
-  int rt;        // 16-row tiles per workgroup (mfma) / rows per wave (dot)
-  int pd;        // groups of weight loads in flight per wave (mfma)
+  int variant;   // kDot, kSplit or kShared
+  int rt;        // 16-row tiles per wave (matrix core) / rows per wave (dot)
   int threads;   // threads per workgroup
   int64_t grid;  // workgroups
   int lds;       // dynamic LDS bytes
 };
 
+// Parse "split,rt,waves" or "shared,rt,waves" (rt 1, 2 or 4; waves 1-8).
+bool parse_tile(const char* text, Tile* t);
+
 // Fill the tiling fields of `a` and return the launch plan.
-Plan plan_mfma(GemvArgs& a, int T);
+Plan plan_mfma(GemvArgs& a, int T);  // default matrix-core tile for one launch
 Plan plan_dot(GemvArgs& a, int T);
-// Tiling of one problem of a grouped launch whose rt, pd and wave count are fixed.
-void plan_mfma_fixed(GemvArgs& a, int T, int rt, int pd, int nw, int* lds, int64_t* grid);
-void plan_stream(GemvArgs& a, int T, int pd, int nwv, int* lds, int64_t* grid);
+Plan plan_tile(GemvArgs& a, int T, const Tile& t);
 
 hipError_t launch(const GemvArgs& a, const Plan& p, int T, hipStream_t s);
 hipError_t launch_batch(const GemvArgs* table_dev, int count, const Plan& p, int T, hipStream_t s);

@@ -25,13 +25,16 @@
 // exact in fp32; sums are fp32.
 //
 // Two variants:
-//  * mfma: tokens are the A operand of v_mfma_f32_16x16x32_f16 (T padded to
-//    16 rows with zeros), weights the B operand (16 output rows x 32 k).  A
+//  * matrix core: tokens are the A operand of v_mfma_f32_16x16x32_f16 (T
+//    padded to 16 rows), weights the B operand (16 output rows x 32 k).  A
 //    lane owns one output row and a quarter of each 128-column group, loads
-//    its 16 bytes of that group with one nontemporal 128-bit load, and feeds
-//    the four words to four MFMAs.  Each 128-column group gets a fresh
-//    accumulator that is then scaled in fp32.  The waves of a workgroup split
-//    K; their partials are summed through LDS in wave order.
+//    its 16 bytes of that group with one 128-bit load, and feeds the four
+//    words to four MFMAs.  Each 128-column group gets a fresh accumulator
+//    that is then scaled in fp32.  A wave streams RT 16-row tiles one after
+//    the other with eight groups of loads in flight.  In a "shared"
+//    workgroup the waves own different tiles and share one staged copy of
+//    the activations; in a "split" workgroup they split K over the same
+//    tiles and add their partial sums through LDS in wave order.
 //  * dot: lanes split a row's K in 16-byte chunks; v_dot2_f32_f16 forms each
 //    chunk's partial, which is scaled by its group scale; lanes are reduced
 //    with a butterfly across the wavefront.
@@ -43,6 +46,7 @@
 #include <algorithm>
 #include <cstdio>
 #include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "w4a16_internal.h"
@@ -183,7 +187,7 @@ __device__ __forceinline__ void workgroup_argmax(const GemvArgs& a, const float*
   }
 }
 
-// ---------------------------------------------------------------- mfma ----
+// ---------------------------------------------------------- staging ----
 
 // Stages x[t][gs*128 .. ge*128) of all TT token rows into this wave's LDS
 // area as scaled fp16 in slot order; E[t] receives each row's exponent.
@@ -199,179 +203,6 @@ __device__ __forceinline__ void stage_wave(const GemvArgs& a, _Float16* xs, int 
     u4_t* dst = reinterpret_cast<u4_t*>(xs + t * a.xs_stride);
     for (int b = lane; b < n8; b += 64) dst[b] = convert8(src[b], E[t]);
   }
-}
-
-template <int TT, int RT>
-__device__ __forceinline__ void fold_slice(float (&acc)[RT][4], float (&accs)[RT][4], const int (&E)[TT], int kq) {
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = kq * 4 + r;
-    int e = E[0];
-#pragma unroll
-    for (int i = 1; i < TT; ++i) e = (t == i) ? E[i] : e;
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      acc[rt][r] += ldexpf(accs[rt][r], -e);
-      accs[rt][r] = 0.0f;
-    }
-  }
-}
-
-// One workgroup of the mfma variant: output rows [wg*RT*16, +RT*16) of problem
-// `a`, K split over a.nw waves in ranges of a.gpw groups.  Each wave keeps PD
-// groups of weight loads in flight in a register ring; the body of the
-// streaming loop is straight-line so every wait names exactly the group it
-// needs.  Loads past the wave's last group re-read that group and are masked
-// by a zero scale.
-template <int TT, int RT, int PD>
-__device__ __forceinline__ void mfma_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // uniform: scalar control flow
-  const int r16 = lane & 15;  // output row of the B operand / token row of the A operand
-  const int kq = lane >> 4;   // quarter of the 128-column group
-  const int trow = min(r16, TT - 1);  // A rows >= TT only feed D rows that are never read
-  const int64_t row0 = wg * (RT * 16);
-  const int64_t kh = a.K >> 1;
-
-  const int g_begin = wave * a.gpw;
-  const int n = (wave < a.nw) ? min(a.G - g_begin, a.gpw) : 0;  // wave-uniform
-
-  float acc[RT][4];
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[rt][r] = 0.0f;
-
-  if (n > 0) {
-    const u4_t* cp[RT];
-    const uint16_t* sp[RT];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      int64_t w = weight_row(a, row0 + rt * 16 + r16);
-      if (w < 0) w = 0;  // read a valid row; the output is masked later
-      cp[rt] = reinterpret_cast<const u4_t*>(a.packed + w * kh) + kq + 4 * (int64_t)g_begin;
-      sp[rt] = a.scales + w * a.G + g_begin;
-    }
-    _Float16* xs = reinterpret_cast<_Float16*>(smem + wave * a.wave_lds);
-    float accs[RT][4];
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) accs[rt][r] = 0.0f;
-    int E[TT];
-
-    u4_t q[PD][RT];
-    unsigned short sq[PD][RT];
-#pragma unroll
-    for (int s = 0; s < PD; ++s) {
-      const int g = min(s, n - 1);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        q[s][rt] = __builtin_nontemporal_load(cp[rt] + 4 * g);
-        sq[s][rt] = sp[rt][g];
-      }
-      __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
-    }
-
-    for (int sb = 0; sb < n; sb += a.sk) {
-      const int se = min(n, sb + a.sk);
-      if (sb > 0) fold_slice<TT, RT>(acc, accs, E, kq);
-      lds_fence();
-      stage_wave<TT>(a, xs, g_begin + sb, g_begin + se, lane, E);
-      // Staging already waited for its activation loads, issued after the
-      // weight loads in flight; saying so lets the loop below wait for exactly
-      // one group of weights at a time.
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-      lds_fence();
-      const _Float16* xr0 = xs + trow * a.xs_stride + kq * 32;
-      for (int gi = sb; gi < se; gi += PD) {
-#pragma unroll
-        for (int s = 0; s < PD; ++s) {
-          const int g = gi + s;
-          const bool live = g < se;
-          const _Float16* xr = xr0 + (min(g, se - 1) - sb) * kGroup;
-          h8_t xa[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xr + 8 * j);
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            const float sc = live ? bf16_to_f32(sq[s][rt]) : 0.0f;
-            f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], __builtin_bit_cast(h8_t, levels8(q[s][rt].x)), d, 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], __builtin_bit_cast(h8_t, levels8(q[s][rt].y)), d, 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], __builtin_bit_cast(h8_t, levels8(q[s][rt].z)), d, 0, 0, 0);
-            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], __builtin_bit_cast(h8_t, levels8(q[s][rt].w)), d, 0, 0, 0);
-#pragma unroll
-            for (int r = 0; r < 4; ++r) accs[rt][r] = fmaf(d[r], sc, accs[rt][r]);
-          }
-          const int gn = min(g + PD, n - 1);
-#pragma unroll
-          for (int rt = 0; rt < RT; ++rt) {
-            q[s][rt] = __builtin_nontemporal_load(cp[rt] + 4 * gn);
-            sq[s][rt] = sp[rt][gn];
-          }
-          __builtin_amdgcn_sched_barrier(0);  // keep this slot's reloads here
-        }
-      }
-    }
-    fold_slice<TT, RT>(acc, accs, E, kq);
-  }
-
-  // Split-K partials of this wave -> its own LDS area: red[(rt*TT + t)*16 + row].
-  lds_fence();
-  float* red = reinterpret_cast<float*>(smem + wave * a.wave_lds);
-  if (wave < a.nw) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = kq * 4 + r;
-        if (t < TT) red[(rt * TT + t) * 16 + r16] = acc[rt][r];
-      }
-  }
-  __syncthreads();
-
-  float* fin = reinterpret_cast<float*>(smem + a.fin_offset);
-  constexpr int kOut = RT * TT * 16;
-  for (int o = threadIdx.x; o < kOut; o += blockDim.x) {
-    float v = 0.0f;
-    for (int w = 0; w < a.nw; ++w) v += reinterpret_cast<const float*>(smem + w * a.wave_lds)[o];
-    const int rt = o / (TT * 16), t = (o >> 4) % TT, r = o & 15;
-    const int64_t orow = row0 + rt * 16 + r;
-    if (orow < a.n_out) {
-      if (weight_row(a, orow) < 0) v = __builtin_nanf("");
-      if (a.y) a.y[(int64_t)t * a.n_out + orow] = v;
-    }
-    fin[o] = v;
-  }
-  if (a.partial) {
-    __syncthreads();
-    if (wave == 0) workgroup_argmax<TT>(a, fin, row0, RT * 16, lane, wg);
-  }
-}
-
-template <int TT, int RT, int PD>
-__global__ void __launch_bounds__(512) w4a16_mfma_kernel(GemvArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  mfma_workgroup<TT, RT, PD>(a, blockIdx.x, smem);
-}
-
-// Grouped launch: workgroup b runs tile b - wg_start of the last problem whose
-// wg_start <= b.
-template <int TT, int RT, int PD>
-__global__ void __launch_bounds__(512) w4a16_mfma_batch_kernel(const GemvArgs* __restrict__ table, int count) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  const int64_t b = blockIdx.x;
-  int lo = 0, hi = count - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (table[mid].wg_start <= b)
-      lo = mid;
-    else
-      hi = mid - 1;
-  }
-  const GemvArgs a = table[lo];
-  mfma_workgroup<TT, RT, PD>(a, b - a.wg_start, smem);
 }
 
 // ----------------------------------------------------------------- dot ----
@@ -497,12 +328,11 @@ __global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
   }
 }
 
-// -------------------------------------------------------------- stream ----
+// ---------------------------------------------------------- matrix core ----
 
-// Weight-code load of the streaming kernel.  Default cache policy: the two
-// 64-byte halves of a 128-byte line (groups g and g+1 of a row) then merge
-// into one L2 request in the vector L1; the nontemporal hint would send each
-// half on its own and double the requests in flight.
+// Weight-code load.  Default cache policy: the two 64-byte halves of a
+// 128-byte line (groups g and g+1 of a row) then merge into one L2 request in
+// the vector L1; the nontemporal hint would send each half on its own.
 __device__ __forceinline__ u4_t load_codes(const u4_t* p) { return *p; }
 
 // bf16 scale e of eight packed in v (element order = memory order) -> fp32.
@@ -511,173 +341,300 @@ __device__ __forceinline__ float scale_of(u4_t v, int e) {
   return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
 }
 
-// The K loop of one wave of the streaming kernel: PD groups of codes in
-// flight.  VS: the row's scales are read eight groups (16 bytes) at a time,
-// one load per 8 groups instead of one per group (needs G % 8 == 0 and
-// 16-byte aligned scale rows); otherwise one 2-byte load per group.
-template <int TT, int PD, bool VS>
-__device__ __forceinline__ void stream_rows(const GemvArgs& a, const u4_t* cp, const uint16_t* sp, _Float16* xs,
-                                            unsigned* maxbuf, int trow, int kq, float (&acc)[1][4]) {
-  constexpr int NV = VS ? PD / 8 : 1;  // scale vectors per ring cycle
-  static_assert(!VS || PD % 8 == 0, "vector scales need PD % 8 == 0");
-  const int G = a.G;
-  float accs[1][4];
-#pragma unroll
-  for (int r = 0; r < 4; ++r) accs[0][r] = 0.0f;
+constexpr int kRing = 8;  // groups of weight codes in flight per wave
+
+// The K loop of one wave: groups [g_begin, g_end) of RT 16-row tiles.  The
+// range is cut into slices that fit the staged activations; within a slice
+// the wave streams tile 0's groups, then tile 1's, ... with kRing groups of
+// codes in flight and the ring running across tile boundaries.  A lane owns
+// output row r16 of a tile and quarter kq of each 128-column group: one
+// 16-byte load per group feeds four MFMAs (tokens as the A operand, padded to
+// 16 rows; weights as the B operand), whose sum gets the group's scale.
+// SHARED: the slice is staged once for the whole workgroup (stage_block);
+// otherwise each wave stages its own range (stage_wave, no barrier).
+// VS: scales are read eight groups (16 bytes) per load (needs G % 8 == 0,
+// 16-byte aligned scale rows and g_begin % 8 == 0); otherwise one 2-byte
+// load per group.
+template <int TT, int RT, bool VS, bool SHARED>
+__device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* const (&cp)[RT],
+                                             const uint16_t* const (&sp)[RT], _Float16* xs, unsigned* maxbuf,
+                                             int g_begin, int g_end, int lane, int trow, int kq,
+                                             float (&acc)[RT][4]) {
+  constexpr int PD = kRing;
   int E[TT];
-
-  // The first slice is staged before any weight load is issued.
-  int se = min(G, a.sk);
-  stage_block<TT>(a, xs, maxbuf, 0, se, E);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-
-  const u4_t* svp = reinterpret_cast<const u4_t*>(sp);
-  const int nvec = G / 8;
-  u4_t sv[NV];
-  if constexpr (VS) {
-#pragma unroll
-    for (int c = 0; c < NV; ++c) sv[c] = svp[min(c, nvec - 1)];
-  }
   u4_t q[PD];
   unsigned short sq[PD];
+  u4_t sv;
+  for (int sb = g_begin; sb < g_end; sb += a.sk) {
+    const int se = min(g_end, sb + a.sk);
+    const int n = se - sb;                  // groups of this slice
+    const int np = (n + PD - 1) / PD * PD;  // padded to whole ring cycles
+    // Ring prologue (tile 0 of the slice), issued before the activations are
+    // staged so that the weight latency overlaps the activation round trip.
+    if constexpr (VS) sv = reinterpret_cast<const u4_t*>(sp[0])[sb / 8];
 #pragma unroll
-  for (int s = 0; s < PD; ++s) {
-    const int g = min(s, G - 1);
-    if constexpr (!VS) sq[s] = sp[g];
-    q[s] = load_codes(cp + 4 * g);
-    __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
-  }
-  for (int sb = 0; sb < G; sb += a.sk) {
-    se = min(G, sb + a.sk);
-    if (sb > 0) {
-      fold_slice<TT, 1>(acc, accs, E, kq);
-      __syncthreads();  // every wave is done with the previous slice
+    for (int s = 0; s < PD; ++s) {
+      const int g = sb + min(s, n - 1);
+      if constexpr (!VS) sq[s] = sp[0][g];
+      q[s] = load_codes(cp[0] + 4 * g);
+      __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
+    }
+    if constexpr (SHARED) {
       stage_block<TT>(a, xs, maxbuf, sb, se, E);
-      __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    } else {
+      lds_fence();
+      stage_wave<TT>(a, xs, sb, se, lane, E);
+      lds_fence();
     }
+    // Staging waited for its activation loads, issued after the weight loads
+    // in flight; saying so lets the loop wait for exactly one group at a time.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     const _Float16* xr0 = xs + trow * a.xs_stride + kq * 32;
-    for (int gi = sb; gi < se; gi += PD) {
-      u4_t svn[NV];
-      if constexpr (VS) {
 #pragma unroll
-        for (int c = 0; c < NV; ++c) svn[c] = svp[min(gi / 8 + NV + c, nvec - 1)];
-        __builtin_amdgcn_sched_barrier(0);
+    for (int tl = 0; tl < RT; ++tl) {
+      // next tile of the ring (the last tile re-reads its own last group)
+      const u4_t* cpn = cp[tl + 1 < RT ? tl + 1 : tl];
+      const uint16_t* spn = sp[tl + 1 < RT ? tl + 1 : tl];
+      const bool has_next = tl + 1 < RT;
+      float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int fi = 0; fi < np; fi += PD) {
+        const bool last = fi + PD >= np;  // uniform: this cycle prefetches the next tile
+        u4_t svn;
+        if constexpr (VS) {
+          const uint16_t* base = (last && has_next) ? spn : sp[tl];
+          const int gv = last ? (has_next ? sb : sb + fi) : sb + fi + PD;
+          svn = reinterpret_cast<const u4_t*>(base)[gv / 8];
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int s = 0; s < PD; ++s) {
+          const int gl = fi + s;
+          const _Float16* xr = xr0 + min(gl, n - 1) * kGroup;
+          h8_t xa[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xr + 8 * j);
+          float sc;
+          if constexpr (VS)
+            sc = scale_of(sv, s);
+          else
+            sc = bf16_to_f32(sq[s]);
+          sc = (gl < n) ? sc : 0.0f;
+          f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], __builtin_bit_cast(h8_t, levels8(q[s].x)), d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], __builtin_bit_cast(h8_t, levels8(q[s].y)), d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], __builtin_bit_cast(h8_t, levels8(q[s].z)), d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], __builtin_bit_cast(h8_t, levels8(q[s].w)), d, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) accs[r] = fmaf(d[r], sc, accs[r]);
+          // reload this slot with the group PD positions ahead
+          const int tgt = gl + PD;
+          const bool nxt = tgt >= np;
+          const u4_t* cpl = (nxt && has_next) ? cpn : cp[tl];
+          const int gg = sb + (nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1));
+          if constexpr (!VS) sq[s] = ((nxt && has_next) ? spn : sp[tl])[gg];
+          q[s] = load_codes(cpl + 4 * gg);
+          // keep this slot's reload here: sunk to the end of the loop, the
+          // reloads would make every iteration wait for the whole ring
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (VS) sv = svn;
       }
+      // fold this tile's slice sum, undoing the activations' power of two
 #pragma unroll
-      for (int s = 0; s < PD; ++s) {
-        const int g = gi + s;
-        const _Float16* xr = xr0 + (min(g, se - 1) - sb) * kGroup;
-        h8_t xa[4];
+      for (int r = 0; r < 4; ++r) {
+        const int t = kq * 4 + r;
+        int e = E[0];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xr + 8 * j);
-        float sc;
-        if constexpr (VS)
-          sc = scale_of(sv[s / 8], s % 8);
-        else
-          sc = bf16_to_f32(sq[s]);
-        sc = (g < se) ? sc : 0.0f;
-        f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], __builtin_bit_cast(h8_t, levels8(q[s].x)), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], __builtin_bit_cast(h8_t, levels8(q[s].y)), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], __builtin_bit_cast(h8_t, levels8(q[s].z)), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], __builtin_bit_cast(h8_t, levels8(q[s].w)), d, 0, 0, 0);
-#pragma unroll
-        for (int r = 0; r < 4; ++r) accs[0][r] = fmaf(d[r], sc, accs[0][r]);
-        const int gn = min(g + PD, G - 1);
-        if constexpr (!VS) sq[s] = sp[gn];
-        q[s] = load_codes(cp + 4 * gn);
-        // keep this slot's reload here: sunk to the end of the loop, the
-        // reloads would make every iteration wait for the whole ring
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      if constexpr (VS) {
-#pragma unroll
-        for (int c = 0; c < NV; ++c) sv[c] = svn[c];
+        for (int i = 1; i < TT; ++i) e = (t == i) ? E[i] : e;
+        acc[tl][r] += ldexpf(accs[r], -e);
       }
     }
   }
-  fold_slice<TT, 1>(acc, accs, E, kq);
 }
 
-// Streaming variant of the matrix-core path: each wave owns one 16-row tile
-// over all of K and keeps PD groups of its rows in flight (PD x 64 bytes of
-// every row requested together, which is what lets the 16-row x 64-byte
-// access pattern of the MFMA operand layout stream at full HBM rate); the
-// waves of a workgroup share one staged copy of the activations per K slice,
-// so the fp16 conversion is paid once per 16 * (waves) rows.  No split-K:
-// every output comes straight from one wave's registers.
-template <int TT, int PD>
-__device__ __forceinline__ void stream_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
+// Row pointers of the RT tiles starting at output row row0 for this lane.
+template <int RT>
+__device__ __forceinline__ void tile_pointers(const GemvArgs& a, int64_t row0, int r16, int kq,
+                                              const u4_t* (&cp)[RT], const uint16_t* (&sp)[RT]) {
+  const int64_t kh = a.K >> 1;
+#pragma unroll
+  for (int tl = 0; tl < RT; ++tl) {
+    int64_t w = weight_row(a, row0 + tl * 16 + r16);
+    if (w < 0) w = 0;  // read a valid row; the output is masked later
+    cp[tl] = reinterpret_cast<const u4_t*>(a.packed + w * kh) + kq;
+    sp[tl] = a.scales + w * a.G;
+  }
+}
+
+// Split workgroup: its a.nw waves own the same RT tiles (rows wg*16*RT ..) and
+// split K into ranges of a.gpw groups; each wave stages its own range; the
+// partial sums are added through LDS in wave order.
+template <int TT, int RT>
+__device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int trow = min(r16, TT - 1);  // A rows >= TT only feed D rows that are never read
+  const int64_t row0 = wg * (RT * 16);
+  const u4_t* cp[RT];
+  const uint16_t* sp[RT];
+  tile_pointers<RT>(a, row0, r16, kq, cp, sp);
+  const int g_begin = wave * a.gpw;
+  const int g_end = (wave < a.nw) ? min(a.G, g_begin + a.gpw) : g_begin;  // uniform
+  _Float16* xs = reinterpret_cast<_Float16*>(smem + wave * a.wave_lds);
+
+  float acc[RT][4];
+#pragma unroll
+  for (int tl = 0; tl < RT; ++tl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[tl][r] = 0.0f;
+  if (g_end > g_begin) {
+    if (a.vec_scales)
+      stream_tiles<TT, RT, true, false>(a, cp, sp, xs, nullptr, g_begin, g_end, lane, trow, kq, acc);
+    else
+      stream_tiles<TT, RT, false, false>(a, cp, sp, xs, nullptr, g_begin, g_end, lane, trow, kq, acc);
+  }
+
+  // Split-K partials of this wave -> its own LDS area: red[(tl*TT + t)*16 + row].
+  lds_fence();
+  float* red = reinterpret_cast<float*>(smem + wave * a.wave_lds);
+  if (wave < a.nw) {
+#pragma unroll
+    for (int tl = 0; tl < RT; ++tl)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = kq * 4 + r;
+        if (t < TT) red[(tl * TT + t) * 16 + r16] = acc[tl][r];
+      }
+  }
+  __syncthreads();
+
+  float* fin = reinterpret_cast<float*>(smem + a.fin_offset);
+  constexpr int kOut = RT * TT * 16;
+  for (int o = threadIdx.x; o < kOut; o += blockDim.x) {
+    float v = 0.0f;
+    for (int w = 0; w < a.nw; ++w) v += reinterpret_cast<const float*>(smem + w * a.wave_lds)[o];
+    const int tl = o / (TT * 16), t = (o >> 4) % TT, r = o & 15;
+    const int64_t orow = row0 + tl * 16 + r;
+    if (orow < a.n_out) {
+      if (weight_row(a, orow) < 0) v = __builtin_nanf("");
+      if (a.y) a.y[(int64_t)t * a.n_out + orow] = v;
+    }
+    fin[o] = v;
+  }
+  if (a.partial) {
+    __syncthreads();
+    if (wave == 0) workgroup_argmax<TT>(a, fin, row0, RT * 16, lane, wg);
+  }
+}
+
+// Shared workgroup: each of its waves owns RT tiles of its own over all of K
+// (rows (wg*waves + wave)*16*RT ..); the waves share one staged copy of the
+// activations per K slice, so the fp16 conversion is paid once per
+// 16 * RT * waves rows.  Every output comes straight from one wave.
+template <int TT, int RT>
+__device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwv = blockDim.x >> 6;
   const int r16 = lane & 15, kq = lane >> 4;
   const int trow = min(r16, TT - 1);
-  const int64_t tile0 = (wg * nwv + wave) * 16;
-  const int64_t kh = a.K >> 1;
-  int64_t w = weight_row(a, tile0 + r16);
-  if (w < 0) w = 0;
-  const u4_t* cp = reinterpret_cast<const u4_t*>(a.packed + w * kh) + kq;
-  const uint16_t* sp = a.scales + w * a.G;
+  const int64_t row_w = (wg * nwv + wave) * (int64_t)(RT * 16);  // first row of this wave
+  const u4_t* cp[RT];
+  const uint16_t* sp[RT];
+  tile_pointers<RT>(a, row_w, r16, kq, cp, sp);
   _Float16* xs = reinterpret_cast<_Float16*>(smem);
   unsigned* maxbuf = reinterpret_cast<unsigned*>(smem + a.fin_offset);
 
-  float acc[1][4];
+  float acc[RT][4];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) acc[0][r] = 0.0f;
+  for (int tl = 0; tl < RT; ++tl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[tl][r] = 0.0f;
   if (a.vec_scales)
-    stream_rows<TT, PD, true>(a, cp, sp, xs, maxbuf, trow, kq, acc);
+    stream_tiles<TT, RT, true, true>(a, cp, sp, xs, maxbuf, 0, a.G, lane, trow, kq, acc);
   else
-    stream_rows<TT, PD, false>(a, cp, sp, xs, maxbuf, trow, kq, acc);
+    stream_tiles<TT, RT, false, true>(a, cp, sp, xs, maxbuf, 0, a.G, lane, trow, kq, acc);
 
-  const int64_t orow = tile0 + r16;
-  const bool in_range = orow < a.n_out;
-  const bool bad = in_range && weight_row(a, orow) < 0;
+  float bv[TT];
+  int bi[TT];
 #pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int t = kq * 4 + r;
-    if (t < TT && in_range && a.y) a.y[(int64_t)t * a.n_out + orow] = bad ? __builtin_nanf("") : acc[0][r];
+  for (int t = 0; t < TT; ++t) {
+    bv[t] = __builtin_nanf("");
+    bi[t] = -1;
+  }
+#pragma unroll
+  for (int tl = 0; tl < RT; ++tl) {
+    const int64_t orow = row_w + tl * 16 + r16;
+    const bool in_range = orow < a.n_out;
+    const int64_t wr = in_range ? weight_row(a, orow) : -1;
+    const bool bad = in_range && wr < 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = kq * 4 + r;
+      if (t < TT && in_range && a.y) a.y[(int64_t)t * a.n_out + orow] = bad ? __builtin_nanf("") : acc[tl][r];
+    }
+    if (a.partial) {
+      // this lane's candidate for token rows t = 4*kq + r
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        const int r = t & 3;
+        float v = acc[tl][0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) v = (r == i) ? acc[tl][i] : v;
+        const int id = (kq == (t >> 2) && wr >= 0 && !__builtin_isnan(v)) ? (int)wr : -1;
+        if (better(v, id, bv[t], bi[t])) {
+          bv[t] = v;
+          bi[t] = id;
+        }
+      }
+    }
   }
   if (a.partial) {
-    // per t: best (value, id) of this wave's 16 rows, then of the workgroup
+    // per t: best (value, id) of this wave's rows, then of the workgroup
     int2* fin = reinterpret_cast<int2*>(smem + a.fin_offset);
     __syncthreads();  // staging area and max buffer are free now
-    const int64_t vid = (in_range && !bad) ? (a.row_ids ? (int64_t)a.row_ids[orow] : orow) : -1;
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
-      const int r = t & 3;
-      float v = acc[0][0];
-#pragma unroll
-      for (int i = 1; i < 4; ++i) v = (r == i) ? acc[0][i] : v;
-      int id = (kq == (t >> 2) && vid >= 0 && !__builtin_isnan(v)) ? (int)vid : -1;
-      if (id < 0) v = __builtin_nanf("");
+      float v = bv[t];
+      int id = bi[t];
       wave_argmax(v, id);
       if (lane == 0) fin[wave * TT + t] = int2{__float_as_int(v), id};
     }
     __syncthreads();
     if (wave == 0 && lane < TT) {
-      float bv = __builtin_nanf("");
-      int bi = -1;
+      float b = __builtin_nanf("");
+      int i = -1;
       for (int w2 = 0; w2 < nwv; ++w2) {
         const int2 c = fin[w2 * TT + lane];
-        if (better(__int_as_float(c.x), c.y, bv, bi)) {
-          bv = __int_as_float(c.x);
-          bi = c.y;
+        if (better(__int_as_float(c.x), c.y, b, i)) {
+          b = __int_as_float(c.x);
+          i = c.y;
         }
       }
-      a.partial[wg * TT + lane] = int2{__float_as_int(bv), bi};
+      a.partial[wg * TT + lane] = int2{__float_as_int(b), i};
     }
   }
 }
 
-template <int TT, int PD>
-__global__ void __launch_bounds__(256) w4a16_stream_kernel(GemvArgs a) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  stream_workgroup<TT, PD>(a, blockIdx.x, smem);
+template <int TT, int RT, bool SHARED>
+__device__ __forceinline__ void tile_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
+  if constexpr (SHARED)
+    shared_workgroup<TT, RT>(a, wg, smem);
+  else
+    split_workgroup<TT, RT>(a, wg, smem);
 }
 
-template <int TT, int PD>
-__global__ void __launch_bounds__(256) w4a16_stream_batch_kernel(const GemvArgs* __restrict__ table, int count) {
+template <int TT, int RT, bool SHARED>
+__global__ void __launch_bounds__(512) w4a16_tile_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  tile_workgroup<TT, RT, SHARED>(a, blockIdx.x, smem);
+}
+
+// Grouped launch: workgroup b runs tile b - wg_start of the last problem whose
+// wg_start <= b.
+template <int TT, int RT, bool SHARED>
+__global__ void __launch_bounds__(512) w4a16_tile_batch_kernel(const GemvArgs* __restrict__ table, int count) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int64_t b = blockIdx.x;
   int lo = 0, hi = count - 1;
@@ -689,7 +646,7 @@ __global__ void __launch_bounds__(256) w4a16_stream_batch_kernel(const GemvArgs*
       hi = mid - 1;
   }
   const GemvArgs a = table[lo];
-  stream_workgroup<TT, PD>(a, b - a.wg_start, smem);
+  tile_workgroup<TT, RT, SHARED>(a, b - a.wg_start, smem);
 }
 
 // ---------------------------------------------------------- argmax final ----
@@ -729,41 +686,32 @@ __global__ void __launch_bounds__(256) w4a16_argmax_final(const int2* partial, i
 
 // ------------------------------------------------------------- dispatch ----
 
-// (RT, PD) pairs the mfma kernels are built for.
-#define W4A16_MFMA_SHAPES(X) X(1, 2) X(1, 4) X(1, 8) X(4, 2) X(4, 4)
+template <int TT, int RT, bool SHARED>
+hipError_t launch_tiles(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
+  if (table)
+    hipLaunchKernelGGL((w4a16_tile_batch_kernel<TT, RT, SHARED>), grid, block, p.lds, s, table, count);
+  else
+    hipLaunchKernelGGL((w4a16_tile_kernel<TT, RT, SHARED>), grid, block, p.lds, s, a);
+  return hipGetLastError();
+}
+
+template <int TT, bool SHARED>
+hipError_t launch_rt(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
+  switch (p.rt) {
+    case 1: return launch_tiles<TT, 1, SHARED>(a, table, count, p, s);
+    case 2: return launch_tiles<TT, 2, SHARED>(a, table, count, p, s);
+    case 4: return launch_tiles<TT, 4, SHARED>(a, table, count, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
 
 template <int TT>
 hipError_t launch_t(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
-  const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
-  if (p.variant == 2) {
-#define W4A16_CASE(R, D)                                                                                \
-  if (p.rt == R && p.pd == D) {                                                                         \
-    if (table)                                                                                          \
-      hipLaunchKernelGGL((w4a16_mfma_batch_kernel<TT, R, D>), grid, block, p.lds, s, table, count);     \
-    else                                                                                                \
-      hipLaunchKernelGGL((w4a16_mfma_kernel<TT, R, D>), grid, block, p.lds, s, a);                      \
-    return hipGetLastError();                                                                           \
-  }
-    W4A16_MFMA_SHAPES(W4A16_CASE)
-#undef W4A16_CASE
-    return hipErrorInvalidValue;
-  }
-  if (p.variant == 3) {
-#define W4A16_CASE(D)                                                                                   \
-  if (p.pd == D) {                                                                                      \
-    if (table)                                                                                          \
-      hipLaunchKernelGGL((w4a16_stream_batch_kernel<TT, D>), grid, block, p.lds, s, table, count);      \
-    else                                                                                                \
-      hipLaunchKernelGGL((w4a16_stream_kernel<TT, D>), grid, block, p.lds, s, a);                       \
-    return hipGetLastError();                                                                           \
-  }
-    W4A16_CASE(8)
-    W4A16_CASE(16)
-#undef W4A16_CASE
-    return hipErrorInvalidValue;
-  }
-  if (table || p.rt != 2) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((w4a16_dot_kernel<TT, 2>), grid, block, p.lds, s, a);
+  if (p.variant == kSplit) return launch_rt<TT, false>(a, table, count, p, s);
+  if (p.variant == kShared) return launch_rt<TT, true>(a, table, count, p, s);
+  if (table || p.variant != kDot || p.rt != 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((w4a16_dot_kernel<TT, 2>), dim3((unsigned)p.grid), dim3((unsigned)p.threads), p.lds, s, a);
   return hipGetLastError();
 }
 
@@ -784,106 +732,116 @@ hipError_t for_t(int T, F&& f) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
-// W4A16_STREAM="pd,waves" overrides the streaming tile (for measurement).
-void stream_override(int* pd, int* nwv) {
-  if (const char* e = std::getenv("W4A16_STREAM")) {
-    int x = 0, y = 0;
-    if (std::sscanf(e, "%d,%d", &x, &y) == 2 && (x == 8 || x == 16) && y >= 1 && y <= 4) {
-      *pd = x;
-      *nwv = y;
-    }
-  }
-}
-
 }  // namespace
 
-// Tiling of one problem for a fixed tile height (rt), prefetch depth (pd)
-// and at most nw_max waves.  K is split into per-wave ranges of gpw groups, a
-// multiple of pd (the last wave may hold fewer); the activation slice staged
-// in LDS holds sk groups (all of a wave's range when 64 KB allow it, else a
-// multiple of pd).
-void plan_mfma_fixed(GemvArgs& a, int T, int rt, int pd, int nw_max, int* lds, int64_t* grid) {
+bool parse_tile(const char* text, Tile* t) {
+  char kind[16] = {0};
+  int rt = 0, nw = 0;
+  if (!text || std::sscanf(text, "%15[a-z],%d,%d", kind, &rt, &nw) != 3) return false;
+  const bool split = std::strcmp(kind, "split") == 0, shared = std::strcmp(kind, "shared") == 0;
+  if (!(split || shared) || !(rt == 1 || rt == 2 || rt == 4) || nw < 1 || nw > 8) return false;
+  *t = Tile{split ? kSplit : kShared, rt, nw};
+  return true;
+}
+
+// Split tiling: rt 16-row tiles per workgroup; K is cut into per-wave ranges
+// of gpw groups (a multiple of the 8-group ring, so that 8-scale vector loads
+// stay aligned; the last wave may hold fewer) over at most nw_max waves.  A
+// wave's LDS area holds its staged activation slice of sk groups (the whole
+// range when 64 KB allow it, else a multiple of 8) and later its partial
+// sums; the final values follow the wave areas.
+static void plan_split(GemvArgs& a, int T, int rt, int nw_max, Plan* p) {
   const int fin_bytes = rt * T * 16 * 4;
-  int nw = std::max(1, std::min(nw_max, a.G));
-  int gpw = 0, nw_eff = 0, sk = 0;
-  for (;; --nw) {
-    gpw = (int)(cdiv(cdiv(a.G, nw), pd) * pd);
-    nw_eff = (int)cdiv(a.G, gpw);
-    const int per_wave = (kLdsCap - fin_bytes) / nw_eff;
-    sk = (per_wave / T - 16) / (kGroup * 2);
-    if (sk >= gpw) {
-      sk = gpw;
-      break;
-    }
-    if (sk >= pd || nw == 1) {
-      sk = std::max(pd, sk - sk % pd);
-      break;
-    }
+  for (int nw = std::max(1, std::min(nw_max, a.G));; --nw) {
+    const int gpw = (int)(cdiv(cdiv(a.G, nw), kRing) * kRing);
+    const int nw_eff = (int)cdiv(a.G, gpw);
+    const int per_wave = ((kLdsCap - fin_bytes) / nw_eff) & ~15;
+    int sk = (per_wave / (2 * T) - 8) / kGroup;
+    if (sk >= gpw)
+      sk = std::min(gpw, a.G);
+    else if (sk >= kRing)
+      sk -= sk % kRing;
+    else if (nw > 1)
+      continue;
+    else
+      sk = kRing;  // unreachable for T <= 8: one wave always fits 24 groups
+    a.nw = nw_eff;
+    a.gpw = gpw;
+    a.sk = sk;
+    a.xs_stride = sk * kGroup + 8;  // 16-byte pad between token rows
+    const int wave_lds = std::max(T * a.xs_stride * 2, rt * T * 16 * 4);
+    a.wave_lds = (wave_lds + 15) & ~15;
+    a.fin_offset = nw_eff * a.wave_lds;
+    p->lds = a.fin_offset + fin_bytes;
+    if (p->lds > kLdsCap && nw > 1) continue;
+    p->threads = nw_eff * 64;
+    p->grid = cdiv(a.n_out, 16LL * rt);
+    return;
   }
-  a.nw = nw_eff;
-  a.gpw = gpw;
-  a.sk = sk;
-  a.xs_stride = sk * kGroup + 8;  // 16-byte pad between token rows
-  int wave_lds = std::max(T * a.xs_stride * 2, rt * T * 16 * 4);
-  a.wave_lds = (wave_lds + 15) & ~15;
-  a.fin_offset = nw_eff * a.wave_lds;
-  *lds = a.fin_offset + fin_bytes;
-  *grid = cdiv(cdiv(a.n_out, 16), rt);
 }
 
-// Tiling of a single matrix-core launch.  Tall matrices (>= 1024 tiles of
-// 16 rows) stream: one wave per 16-row tile over all of K, four waves per
-// workgroup sharing the staged activations.  Shorter ones split K over the
-// waves of a workgroup (16 rows per workgroup) so that they still put ~12
-// waves of weight loads on every CU; the prefetch depth is the largest the
-// per-wave K range fills.
-Plan plan_mfma(GemvArgs& a, int T) {
-  Plan p{};
-  const int64_t tiles = cdiv(a.n_out, 16);
-  if (tiles >= 1024) {
-    p.variant = 3;
-    p.rt = 1;
-    p.pd = (a.G % 16 == 0) ? 16 : 8;
-    int nwv = 4;
-    stream_override(&p.pd, &nwv);
-    plan_stream(a, T, p.pd, nwv, &p.lds, &p.grid);
-    p.threads = nwv * 64;
-    return p;
-  }
-  p.variant = 2;
-  p.rt = 1;
-  const int nw_max = (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(3072, tiles)));
-  const int gpw_est = (int)cdiv(a.G, std::min(nw_max, a.G));
-  p.pd = gpw_est >= 8 ? 8 : (gpw_est >= 4 ? 4 : 2);
-  plan_mfma_fixed(a, T, p.rt, p.pd, nw_max, &p.lds, &p.grid);
-  p.threads = a.nw * 64;
-  return p;
-}
-
-// Tiling of the streaming variant: nwv waves (16-row tiles) per workgroup,
-// the activation slice staged in LDS holds sk groups (all of K when 64 KB
-// allow it, else a multiple of pd).
-void plan_stream(GemvArgs& a, int T, int pd, int nwv, int* lds, int64_t* grid) {
-  a.vec_scales = (a.G % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15) == 0) ? 1 : 0;
-  const int small = std::max(nwv * T * 4, nwv * T * 8);  // max buffer / argmax partials
+// Shared tiling: nwv waves of rt 16-row tiles per workgroup over all of K; the
+// activation slice staged in LDS holds sk groups (all of K when 64 KB allow
+// it, else a multiple of the 8-group ring), followed by a small area for the
+// slice maxima and the argmax partials of the waves.
+static void plan_shared(GemvArgs& a, int T, int rt, int nwv, Plan* p) {
+  const int small = nwv * T * 8;
   int sk = ((kLdsCap - small - 16) / T - 16) / (kGroup * 2);
-  if (sk < a.G) sk = std::max(pd, sk - sk % pd);
-  else sk = a.G;
+  if (sk < a.G)
+    sk = std::max(kRing, sk - sk % kRing);
+  else
+    sk = a.G;
   a.nw = nwv;
   a.gpw = a.G;
   a.sk = sk;
   a.xs_stride = sk * kGroup + 8;
   a.wave_lds = 0;
   a.fin_offset = (T * a.xs_stride * 2 + 15) & ~15;
-  *lds = a.fin_offset + small;
-  *grid = cdiv(a.n_out, 16LL * nwv);
+  p->lds = a.fin_offset + small;
+  p->threads = nwv * 64;
+  p->grid = cdiv(a.n_out, 16LL * nwv * rt);
+}
+
+Plan plan_tile(GemvArgs& a, int T, const Tile& t) {
+  Plan p{};
+  p.variant = t.shape;
+  p.rt = t.rt;
+  a.vec_scales = (a.G % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15) == 0) ? 1 : 0;
+  if (t.shape == kShared)
+    plan_shared(a, T, t.rt, t.nw, &p);
+  else
+    plan_split(a, T, t.rt, t.nw, &p);
+  return p;
+}
+
+// Default matrix-core tiling of a single launch.  Tall matrices (>= 1024
+// tiles of 16 rows) use shared workgroups: the full vocabulary head (15,520
+// tiles) measured best with eight waves of four tiles each, mid-size
+// matrices with four waves of one tile.  Shorter ones split K over the waves
+// of a workgroup so that they still put ~12 waves of weight loads on every
+// CU.  W4A16_TILE="split|shared,rt,waves" overrides the choice (for
+// measurement).
+Plan plan_mfma(GemvArgs& a, int T) {
+  const int64_t tiles = cdiv(a.n_out, 16);
+  Tile t;
+  if (tiles >= 8192)
+    t = Tile{kShared, 4, 8};
+  else if (tiles >= 4096)
+    t = Tile{kShared, 2, 8};
+  else if (tiles >= 1024)
+    t = Tile{kShared, 1, 4};
+  else
+    t = Tile{kSplit, 1, (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(3072, tiles)))};
+  Tile o;
+  if (parse_tile(std::getenv("W4A16_TILE"), &o)) t = o;
+  return plan_tile(a, T, t);
 }
 
 // Tiling of the dot variant: 2 rows per wave (32 lanes per row), 8 waves,
 // activations staged per workgroup in slices of at most 8 chunks per lane.
 Plan plan_dot(GemvArgs& a, int T) {
   Plan p{};
-  p.variant = 1;
+  p.variant = kDot;
   p.rt = 2;  // rows per wave
   const int nw = 8;
   p.threads = nw * 64;

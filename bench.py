@@ -3,15 +3,17 @@
 One step is one verify cycle's weight read: 64 layers x {qkv, o, gate_up,
 down} W4A16 projections at T = 4 (1 + 3 drafts), each with its own seeded
 weights and activations, run as one grouped launch, then the 248,320-row
-lm_head with per-row argmax.  Weights stay resident in HBM; nothing is
-cached between steps (11.6 GB per step, far beyond the 256 MB Infinity
-Cache).
+lm_head with per-row argmax.  Weights are repacked once at load into the
+tiled layout (same codes and scales, one contiguous 1 KB block per 16 rows x
+128 columns) and stay resident in HBM; nothing is cached between steps
+(11.6 GB per step, far beyond the 256 MB Infinity Cache).
 
 Reported (one JSON line): weight GB/s of the whole step (value), decode
 cycles/s, the grouped body kernel's achieved bandwidth against the 8 TB/s
 HBM peak (roofline, timed with HIP events on the launch stream), the body
-pass at T = 1, 4, 8, the same step as 257 separate launches replayed from
-a captured HIP graph, and the CPU oracle's rate on a bounded sample.
+pass at T = 1, 4, 8 in both layouts (tiled and the pages' row-major one),
+the same step as 257 separate launches replayed from a captured HIP graph,
+and the CPU oracle's rate on a bounded sample.
 
 --pmc-pass runs one untimed body pass and one lm_head call after a 1 GiB
 device copy (the calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE).
@@ -109,29 +111,31 @@ def main():
     t0 = time.time()
 
     # ---- resident weights: 64 layers x 4 projections + lm_head (seeded) ----
-    weights = []  # (name, layer, packed_dev, scales_dev)
+    weights = []  # (name, layer, packed_dev, scales_dev, tiled)
     for layer in range(L):
         for proj in synth.PROJ_ORDER:
             N, K = synth.PROJECTIONS[proj]
             p, s = synth.weight(synth.tid_layer(layer, proj), N, K)
-            weights.append((proj, layer, to_dev(p, torch), to_dev(s, torch)))
+            pd, sd = to_dev(p, torch), to_dev(s, torch)
+            weights.append((proj, layer, pd, sd, w4a16.repack_tiled(pd, sd)))
     hn, hk = synth.LM_HEAD
     hp, hs = synth.weight(synth.TID_LM_HEAD, hn, hk)
     head_p, head_s = to_dev(hp, torch), to_dev(hs, torch)
+    head_tw = w4a16.repack_tiled(head_p, head_s)
     del hp, hs
     torch.cuda.synchronize()
-    log(f"weights resident after {time.time() - t0:.1f} s")
+    log(f"weights resident (row-major and tiled) after {time.time() - t0:.1f} s")
 
     body_bytes = sum(metrics.weight_bytes(*synth.PROJECTIONS[w[0]]) for w in weights)
     head_bytes = metrics.weight_bytes(hn, hk)
 
-    def make_pass(Tp):
+    def make_pass(Tp, tiled=True):
         probs = []
-        for proj, layer, pd, sd in weights:
+        for proj, layer, pd, sd, tw in weights:
             N, K = synth.PROJECTIONS[proj]
             x = to_dev(synth.activations(synth.tid_layer(layer, proj), Tp, K), torch)
             y = torch.empty((Tp, N), dtype=torch.float32, device="cuda")
-            probs.append((pd, sd, x, y))
+            probs.append((tw, None, x, y) if tiled else (pd, sd, x, y))
         return w4a16.Batch(probs, Tp), probs
 
     batch, probs = make_pass(T)
@@ -141,7 +145,7 @@ def main():
     stream = torch.cuda.current_stream()
 
     def head(s):
-        w4a16.head_gather(head_p, head_s, head_x, scores=True, argmax=True, out=head_y, workspace=head_ws, stream=s)
+        w4a16.head_gather_tiled(head_tw, head_x, scores=True, argmax=True, out=head_y, workspace=head_ws, stream=s)
 
     if args.pmc_pass:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
@@ -180,25 +184,28 @@ def main():
     log(f"step {ms_step:.4f} ms, body kernel {body_ms_avg:.4f} ms (min {min(body_ms):.4f}), "
         f"{value:.0f} GB/s per step, body {achieved:.0f} GB/s")
 
-    # ---- body pass at T = 1, 4, 8 (same weights, grouped launch) ----
-    per_t = {}
+    # ---- body pass at T = 1, 4, 8 (same weights, grouped launch), both layouts ----
+    per_t, per_t_rm = {}, {}
     if not args.no_per_t:
-        for Tp in (1, 4, 8):
-            b, _ = (batch, probs) if Tp == T else make_pass(Tp)
-            for _ in range(2):
-                b.run(stream)
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            reps = 5
-            e0.record(stream)
-            for _ in range(reps):
-                b.run(stream)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            ms = e0.elapsed_time(e1) / reps
-            g = metrics.gbps(body_bytes, ms)
-            per_t[f"T{Tp}"] = {"body_ms": round(ms, 4), "weight_GBps": round(g, 1),
-                              "pct_hbm_peak": round(100 * g / PEAK_GBPS, 2)}
-            log(f"body pass T={Tp}: {ms:.4f} ms, {g:.0f} GB/s ({100 * g / PEAK_GBPS:.1f}% of 8 TB/s)")
+        for tiled, table in ((True, per_t), (False, per_t_rm)):
+            for Tp in (1, 4, 8):
+                b, _ = (batch, probs) if (Tp == T and tiled) else make_pass(Tp, tiled)
+                for _ in range(2):
+                    b.run(stream)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                reps = 5
+                e0.record(stream)
+                for _ in range(reps):
+                    b.run(stream)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ms = e0.elapsed_time(e1) / reps
+                g = metrics.gbps(body_bytes, ms)
+                table[f"T{Tp}"] = {"body_ms": round(ms, 4), "weight_GBps": round(g, 1),
+                                   "pct_hbm_peak": round(100 * g / PEAK_GBPS, 2)}
+                log(f"body pass {'tiled' if tiled else 'row-major'} T={Tp}: {ms:.4f} ms, {g:.0f} GB/s "
+                    f"({100 * g / PEAK_GBPS:.1f}% of 8 TB/s)")
+                del b
 
     # ---- the same step as 257 separate launches, replayed from a HIP graph ----
     graph_pass = None
@@ -234,13 +241,15 @@ def main():
             "lm_head": [hn, hk],
             "group": 128,
             "weight_bytes_per_step": step_bytes,
+            "layout": "tiled (load-time repack of the row-major codes and scales)",
         },
         "cycles_per_s": round(1000.0 / ms_step, 2),
         "pct_hbm_peak": round(100 * value / PEAK_GBPS, 2),
         "per_T_body_pass": per_t,
+        "per_T_body_pass_row_major": per_t_rm,
         "graph_257_launches": graph_pass,
         "roofline": {
-            "kernel": "grouped body pass (64 x 4 projections, one launch)",
+            "kernel": "grouped body pass (64 x 4 projections, one launch, tiled layout)",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_GBPS,
@@ -261,16 +270,16 @@ def graph_step(torch, w4a16, probs, head, reps):
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):
-        for pd, sd, x, y in probs:  # warm the plans and the device check outside capture
-            w4a16.matmul(pd, sd, x, out=y)
+        for tw, _, x, y in probs:  # warm the plans and the device check outside capture
+            w4a16.matmul_tiled(tw, x, out=y)
         head(side)
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g):
         s = torch.cuda.current_stream()
-        for pd, sd, x, y in probs:
-            w4a16.matmul(pd, sd, x, out=y, stream=s)
+        for tw, _, x, y in probs:
+            w4a16.matmul_tiled(tw, x, out=y, stream=s)
         head(s)
     g.replay()
     torch.cuda.synchronize()

@@ -56,7 +56,7 @@ typedef struct ihipStream_t* hipStream_t; /* same definition as the HIP runtime'
 
 #define W4A16_GROUP 128      /* columns per bf16 scale */
 #define W4A16_MAX_T 8        /* activation rows per weight read */
-#define W4A16_ABI_VERSION 1
+#define W4A16_ABI_VERSION 2
 
 typedef enum {
   W4A16_OK = 0,
@@ -121,6 +121,51 @@ w4a16_status w4a16_head_gather(const int32_t* row_ids, int64_t n_ids, const uint
 size_t w4a16_workspace_bytes(int64_t n_out, int32_t T);
 
 /*
+ * Tiled weight layout: a one-time repack of the same codes and scales so
+ * that each group of 16 rows x 128 columns is one contiguous 1 KB block and
+ * each row's scales travel with its codes.  Follows the OpenJet engine page
+ * ("How it gets its speed"): some weight formats are re-laid-out once at load
+ * time, values unchanged, so every lane does aligned wide loads and a block's
+ * scales arrive with its data.  On MI355X a wave's 16-byte-per-lane load then
+ * covers one contiguous 1 KB block instead of 64 bytes of 16 rows.
+ *
+ * Definition (G = K/128 groups, rows padded to a multiple of 16 with zero
+ * bytes): for tile i (rows 16i .. 16i+15), chunk c (groups 8c .. 8c+ng-1,
+ * ng = min(8, G - 8c)), group g of the chunk and row r of the tile:
+ *   tile i starts at byte   i * w4a16_tiled_tile_bytes(K)
+ *   chunk c starts at byte  c * (8 * 1024 + 256) within the tile
+ *   codes of (g, r): 64 bytes at  chunk + (g - 8c) * 1024 + 64 * r, equal to
+ *                    bytes 64g .. 64g+63 of row 16i + r in packed_u4
+ *   scales of (c, r): 16 bytes at chunk + ng * 1024 + 16 * r: the bf16 scales
+ *                    of groups 8c .. 8c+7 of row 16i + r (zero past G)
+ * so a tile takes G * 1024 + ceil(G/8) * 256 bytes (0.515625 B per weight
+ * when G % 8 == 0, the same as the row-major pair).
+ */
+
+/* Bytes per 16-row tile, and of the whole tiled layout (0 if out of range). */
+size_t w4a16_tiled_tile_bytes(int64_t K);
+size_t w4a16_tiled_bytes(int64_t N, int64_t K);
+
+/*
+ * Writes the tiled layout of a row-major weight (packed_u4 [N][K/2],
+ * scales_bf16 [N][K/128]) into `tiled` (device, 16-byte aligned, at least
+ * w4a16_tiled_bytes(N, K) bytes, must not overlap the inputs).  Shapes as
+ * for w4a16_matmul.  W4A16_ERR_WORKSPACE if tiled_bytes is too small.
+ */
+w4a16_status w4a16_repack_tiled(const uint8_t* packed_u4, const uint16_t* scales_bf16, int64_t N, int64_t K,
+                                void* tiled, size_t tiled_bytes, hipStream_t stream);
+
+/* w4a16_matmul and w4a16_head_gather on a tiled weight (`tiled` 16-byte
+ * aligned, written by w4a16_repack_tiled for the same N / n_rows and K).
+ * Same results within the tolerance; always the matrix-core kernels. */
+w4a16_status w4a16_matmul_tiled(const void* tiled, const uint16_t* x_bf16, float* y_f32, int64_t N, int64_t K,
+                                int32_t T, hipStream_t stream);
+w4a16_status w4a16_head_gather_tiled(const int32_t* row_ids, int64_t n_ids, const void* tiled, int64_t n_rows,
+                                     const uint16_t* x_bf16, int64_t K, int32_t T, float* y_f32, int32_t* argmax_id,
+                                     float* argmax_val, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream);
+
+/*
  * Grouped launch: many independent matmuls with the same T in one kernel
  * launch, so a whole decode weight pass (e.g. 64 layers x 4 projections) runs
  * without launch gaps or per-kernel ramp-up and tail.  The pages run a verify
@@ -140,13 +185,18 @@ size_t w4a16_workspace_bytes(int64_t n_out, int32_t T);
  * problem follow w4a16_matmul.
  */
 typedef struct {
-  const uint8_t* packed_u4;    /* [N][K/2] */
-  const uint16_t* scales_bf16; /* [N][K/128] */
+  const uint8_t* packed_u4;    /* [N][K/2], or the tiled layout when layout = 1 */
+  const uint16_t* scales_bf16; /* [N][K/128]; ignored (may be NULL) when layout = 1 */
   const uint16_t* x_bf16;      /* [T][K] */
   float* y_f32;                /* [T][N] */
   int64_t N;
   int64_t K;
+  int32_t layout;              /* W4A16_LAYOUT_ROW_MAJOR or W4A16_LAYOUT_TILED */
+  int32_t reserved;            /* must be 0 */
 } w4a16_problem;
+
+#define W4A16_LAYOUT_ROW_MAJOR 0
+#define W4A16_LAYOUT_TILED 1
 
 #define W4A16_MAX_BATCH 65536
 

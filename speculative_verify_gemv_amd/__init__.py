@@ -57,6 +57,16 @@ def load_library():
         lib.w4a16_batch_plan.restype = i32
         lib.w4a16_matmul_batch.argtypes = [vp, vp, vp]
         lib.w4a16_matmul_batch.restype = i32
+        lib.w4a16_tiled_tile_bytes.argtypes = [i64]
+        lib.w4a16_tiled_tile_bytes.restype = sz
+        lib.w4a16_tiled_bytes.argtypes = [i64, i64]
+        lib.w4a16_tiled_bytes.restype = sz
+        lib.w4a16_repack_tiled.argtypes = [vp, vp, i64, i64, vp, sz, vp]
+        lib.w4a16_repack_tiled.restype = i32
+        lib.w4a16_matmul_tiled.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+        lib.w4a16_matmul_tiled.restype = i32
+        lib.w4a16_head_gather_tiled.argtypes = [vp, i64, vp, i64, vp, i64, i32, vp, vp, vp, vp, sz, vp]
+        lib.w4a16_head_gather_tiled.restype = i32
         _lib = lib
     return _lib
 
@@ -130,6 +140,30 @@ def matmul(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, out: tor
     return out
 
 
+def _gather_outputs(n: int, T: int, device, scores: bool, argmax: bool, out, workspace):
+    y = None
+    if scores:
+        y = out if out is not None else torch.empty((T, n), dtype=torch.float32, device=device)
+    ids = vals = None
+    ws_bytes = 0
+    if argmax:
+        ids = torch.empty(T, dtype=torch.int32, device=device)
+        vals = torch.empty(T, dtype=torch.float32, device=device)
+        ws_bytes = workspace_bytes(n, T)
+        if workspace is None:
+            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=device)
+        ws_bytes = workspace.numel() * workspace.element_size()
+    return y, ids, vals, workspace, ws_bytes
+
+
+def _row_ids(row_ids, n_rows: int) -> int:
+    if row_ids is None:
+        return n_rows
+    if row_ids.dtype != torch.int32 or row_ids.dim() != 1 or not (row_ids.is_cuda and row_ids.is_contiguous()):
+        raise ValueError("row_ids must be a contiguous CUDA int32 vector")
+    return row_ids.shape[0]
+
+
 def head_gather(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, row_ids: torch.Tensor | None = None,
                 scores: bool = True, argmax: bool = False, out: torch.Tensor | None = None,
                 workspace: torch.Tensor | None = None, stream=None):
@@ -142,25 +176,8 @@ def head_gather(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, row
     if x.dim() != 2 or x.shape[1] != K:
         raise ValueError(f"x must be [T][{K}]")
     T = x.shape[0]
-    if row_ids is not None:
-        if row_ids.dtype != torch.int32 or row_ids.dim() != 1 or not (row_ids.is_cuda and row_ids.is_contiguous()):
-            raise ValueError("row_ids must be a contiguous CUDA int32 vector")
-        n = row_ids.shape[0]
-    else:
-        n = n_rows
-    dev = packed.device
-    y = None
-    if scores:
-        y = out if out is not None else torch.empty((T, n), dtype=torch.float32, device=dev)
-    ids = vals = None
-    ws_bytes = 0
-    if argmax:
-        ids = torch.empty(T, dtype=torch.int32, device=dev)
-        vals = torch.empty(T, dtype=torch.float32, device=dev)
-        ws_bytes = workspace_bytes(n, T)
-        if workspace is None:
-            workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=dev)
-        ws_bytes = workspace.numel() * workspace.element_size()
+    n = _row_ids(row_ids, n_rows)
+    y, ids, vals, workspace, ws_bytes = _gather_outputs(n, T, packed.device, scores, argmax, out, workspace)
     s = load_library().w4a16_head_gather(_ptr(row_ids), n, _ptr(packed), _ptr(scales), n_rows, _ptr(x), K, T,
                                          _ptr(y), _ptr(ids), _ptr(vals), _ptr(workspace), ws_bytes,
                                          _stream(stream))
@@ -169,17 +186,76 @@ def head_gather(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, row
     return y, ids, vals
 
 
+class TiledWeight:
+    """A weight in the tiled layout (one uint8 device buffer) with its shape."""
+
+    def __init__(self, data: torch.Tensor, N: int, K: int):
+        self.data, self.N, self.K = data, N, K
+
+    @property
+    def device(self):
+        return self.data.device
+
+
+def tiled_bytes(N: int, K: int) -> int:
+    return int(load_library().w4a16_tiled_bytes(N, K))
+
+
+def repack_tiled(packed: torch.Tensor, scales: torch.Tensor, stream=None) -> TiledWeight:
+    """Tiled-layout copy of a row-major weight (runs on the GPU)."""
+    N, K = _check_weight(packed, scales)
+    nbytes = tiled_bytes(N, K)
+    data = torch.empty(nbytes, dtype=torch.uint8, device=packed.device)
+    s = load_library().w4a16_repack_tiled(_ptr(packed), _ptr(scales), N, K, _ptr(data), nbytes, _stream(stream))
+    if s:
+        raise W4A16Error(s, "w4a16_repack_tiled")
+    return TiledWeight(data, N, K)
+
+
+def matmul_tiled(w: TiledWeight, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:
+    """matmul() on a tiled weight."""
+    _check_bits(x, "x")
+    if x.dim() != 2 or x.shape[1] != w.K:
+        raise ValueError(f"x must be [T][{w.K}]")
+    T = x.shape[0]
+    y = out if out is not None else torch.empty((T, w.N), dtype=torch.float32, device=w.device)
+    if y.dtype != torch.float32 or y.shape != (T, w.N) or not (y.is_cuda and y.is_contiguous()):
+        raise ValueError("out must be a contiguous CUDA float32 tensor [T][N]")
+    s = load_library().w4a16_matmul_tiled(_ptr(w.data), _ptr(x), _ptr(y), w.N, w.K, T, _stream(stream))
+    if s:
+        raise W4A16Error(s, "w4a16_matmul_tiled")
+    return y
+
+
+def head_gather_tiled(w: TiledWeight, x: torch.Tensor, row_ids: torch.Tensor | None = None, scores: bool = True,
+                      argmax: bool = False, out: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, stream=None):
+    """head_gather() on a tiled weight."""
+    _check_bits(x, "x")
+    if x.dim() != 2 or x.shape[1] != w.K:
+        raise ValueError(f"x must be [T][{w.K}]")
+    T = x.shape[0]
+    n = _row_ids(row_ids, w.N)
+    y, ids, vals, workspace, ws_bytes = _gather_outputs(n, T, w.device, scores, argmax, out, workspace)
+    s = load_library().w4a16_head_gather_tiled(_ptr(row_ids), n, _ptr(w.data), w.N, _ptr(x), w.K, T, _ptr(y),
+                                               _ptr(ids), _ptr(vals), _ptr(workspace), ws_bytes, _stream(stream))
+    if s:
+        raise W4A16Error(s, "w4a16_head_gather_tiled")
+    return y, ids, vals
+
+
 class _Problem(ctypes.Structure):
     _fields_ = [("packed_u4", ctypes.c_void_p), ("scales_bf16", ctypes.c_void_p), ("x_bf16", ctypes.c_void_p),
-                ("y_f32", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64)]
+                ("y_f32", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("layout", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
 
 
 class Batch:
     """A planned grouped launch over independent matmuls with the same T.
 
-    problems: list of (packed, scales, x, y) CUDA tensors.  The tensors must
-    stay alive and in place while the batch is used; the plan is a host table
-    plus its device copy (both held here).
+    problems: list of (packed, scales, x, y) CUDA tensors, or (TiledWeight,
+    None, x, y).  The tensors must stay alive and in place while the batch is
+    used; the plan is a host table plus its device copy (both held here).
     """
 
     def __init__(self, problems, T: int):
@@ -187,11 +263,15 @@ class Batch:
         arr = (_Problem * len(problems))()
         self._keep = []
         for i, (packed, scales, x, y) in enumerate(problems):
-            N, K = _check_weight(packed, scales)
+            if isinstance(packed, TiledWeight):
+                N, K, layout, pp, sp = packed.N, packed.K, 1, packed.data.data_ptr(), None
+            else:
+                N, K = _check_weight(packed, scales)
+                layout, pp, sp = 0, packed.data_ptr(), scales.data_ptr()
             _check_bits(x, "x")
             if x.shape != (T, K) or y.dtype != torch.float32 or y.shape != (T, N) or not y.is_contiguous():
                 raise ValueError(f"problem {i}: x must be [T][K] and y float32 [T][N]")
-            arr[i] = _Problem(packed.data_ptr(), scales.data_ptr(), x.data_ptr(), y.data_ptr(), N, K)
+            arr[i] = _Problem(pp, sp, x.data_ptr(), y.data_ptr(), N, K, layout, 0)
             self._keep.append((packed, scales, x, y))
         nbytes = lib.w4a16_batch_table_bytes(len(problems))
         if nbytes == 0:
@@ -200,7 +280,7 @@ class Batch:
         s = lib.w4a16_batch_plan(ctypes.cast(arr, ctypes.c_void_p), len(problems), T, self.host.data_ptr(), nbytes)
         if s:
             raise W4A16Error(s, "w4a16_batch_plan")
-        self.device = self.host.to(problems[0][0].device, non_blocking=False)
+        self.device = self.host.to(problems[0][2].device, non_blocking=False)
         self.T = T
         self.count = len(problems)
 

@@ -34,9 +34,12 @@ int32_t current_variant() {
   return g_variant.load();
 }
 
-// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other.
+// Per-device result of the architecture check: 0 unknown, 1 gfx950, 2 other;
+// and the device's compute-unit count (sizes the split-K plans).
 constexpr int kMaxDevices = 64;
 std::atomic<int> g_arch[kMaxDevices];
+std::atomic<int> g_cus[kMaxDevices];
+thread_local int t_cus = 256;  // CUs of the device of this thread's last checked call
 
 w4a16_status check_device() {
   int dev = 0;
@@ -46,9 +49,11 @@ w4a16_status check_device() {
   if (known == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return W4A16_ERR_HIP;
+    g_cus[dev].store(prop.multiProcessorCount > 0 ? prop.multiProcessorCount : 1);
     known = (std::strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
     g_arch[dev].store(known);
   }
+  t_cus = g_cus[dev].load();
   return known == 1 ? W4A16_OK : W4A16_ERR_UNSUPPORTED;
 }
 
@@ -69,7 +74,53 @@ int resolve_variant(int32_t v, int32_t T) {
 
 w4a16::Plan make_plan(w4a16::GemvArgs& a, int32_t T) {
   const int v = resolve_variant(current_variant(), T);
-  return v == W4A16_VARIANT_DOT ? w4a16::plan_dot(a, T) : w4a16::plan_mfma(a, T);
+  return v == W4A16_VARIANT_DOT ? w4a16::plan_dot(a, T) : w4a16::plan_mfma(a, T, t_cus);
+}
+
+w4a16::GemvArgs gemv_args(const uint8_t* packed, const uint16_t* scales, bool tiled, const uint16_t* x, float* y,
+                          const int32_t* row_ids, int64_t n_out, int64_t n_rows, int64_t K) {
+  w4a16::GemvArgs a{};
+  a.packed = packed;
+  a.scales = scales;
+  a.x = x;
+  a.y = y;
+  a.row_ids = row_ids;
+  a.n_out = n_out;
+  a.n_rows = n_rows;
+  a.K = (int32_t)K;
+  a.G = (int32_t)(K / W4A16_GROUP);
+  a.tiled = tiled ? 1 : 0;
+  a.tile_bytes = tiled ? w4a16::tiled_tile_bytes(a.G) : 0;
+  return a;
+}
+
+// Checks shared by both layouts of the gathered head.
+w4a16_status check_gather(const int32_t* row_ids, int64_t n_ids, int64_t n_rows, const uint16_t* x_bf16, int64_t K,
+                          int32_t T, float* y_f32, int32_t* argmax_id, float* argmax_val, void* workspace,
+                          size_t workspace_bytes) {
+  if (!x_bf16) return W4A16_ERR_NULL_POINTER;
+  if (!y_f32 && !argmax_id) return W4A16_ERR_NULL_POINTER;
+  if (argmax_val && !argmax_id) return W4A16_ERR_NULL_POINTER;
+  if (n_ids < 1 || n_ids > kMaxRows || n_rows < 1 || n_rows > kMaxRows) return W4A16_ERR_BAD_SHAPE;
+  if (!row_ids && n_ids != n_rows) return W4A16_ERR_BAD_SHAPE;
+  if (w4a16_status s = check_kt(K, T)) return s;
+  if (!aligned(x_bf16, 16) || !aligned(y_f32, 4) || !aligned(row_ids, 4) || !aligned(argmax_id, 4) ||
+      !aligned(argmax_val, 4))
+    return W4A16_ERR_MISALIGNED;
+  if (argmax_id) {
+    const int64_t need = (int64_t)w4a16::max_workgroups(n_ids) * T * (int64_t)sizeof(int2);
+    if (!workspace || workspace_bytes < (size_t)need || !aligned(workspace, 16)) return W4A16_ERR_WORKSPACE;
+  }
+  return check_device();
+}
+
+// Launches the planned kernel and, when argmax_id is set, the argmax reduction.
+w4a16_status run(w4a16::GemvArgs& a, int32_t T, int32_t* argmax_id, float* argmax_val, const w4a16::Plan& p,
+                 hipStream_t stream) {
+  if (w4a16::launch(a, p, T, stream) != hipSuccess) return W4A16_ERR_HIP;
+  if (argmax_id && w4a16::launch_argmax_final(a.partial, p.grid, T, argmax_id, argmax_val, stream) != hipSuccess)
+    return W4A16_ERR_HIP;
+  return W4A16_OK;
 }
 
 }  // namespace
@@ -95,12 +146,15 @@ struct TableHeader {
 };
 static_assert(sizeof(TableHeader) == 64, "table header size");
 
-// Tile of grouped launches: shared workgroups; at T <= 2 four waves of two
-// 16-row tiles, above that eight waves of four (the larger workgroup shares
-// one staged copy of the bigger activation block among more rows).
+// Tile of grouped launches, from the MI355X sweeps: all problems tiled ->
+// eight waves of one tile; otherwise at T <= 2 four waves of two 16-row
+// tiles, above that eight waves of four (the larger workgroup shares one
+// staged copy of the bigger activation block among more rows).
 // W4A16_BATCH_TILE = "split|shared,rt,waves" overrides it (for measurement).
-w4a16::Tile batch_tile(int T) {
-  w4a16::Tile t = T <= 2 ? w4a16::Tile{w4a16::kShared, 2, 4} : w4a16::Tile{w4a16::kShared, 4, 8};
+w4a16::Tile batch_tile(int T, bool all_tiled) {
+  w4a16::Tile t = all_tiled ? w4a16::Tile{w4a16::kShared, 1, 8}
+                  : T <= 2  ? w4a16::Tile{w4a16::kShared, 2, 4}
+                            : w4a16::Tile{w4a16::kShared, 4, 8};
   w4a16::Tile o;
   if (w4a16::parse_tile(std::getenv("W4A16_BATCH_TILE"), &o)) t = o;
   return t;
@@ -118,18 +172,22 @@ w4a16_status w4a16_matmul(const uint8_t* packed_u4, const uint16_t* scales_bf16,
   if (!aligned(packed_u4, 16) || !aligned(x_bf16, 16) || !aligned(scales_bf16, 2) || !aligned(y_f32, 4))
     return W4A16_ERR_MISALIGNED;
   if (w4a16_status s = check_device()) return s;
-
-  w4a16::GemvArgs a{};
-  a.packed = packed_u4;
-  a.scales = scales_bf16;
-  a.x = x_bf16;
-  a.y = y_f32;
-  a.n_out = N;
-  a.n_rows = N;
-  a.K = (int32_t)K;
-  a.G = (int32_t)(K / W4A16_GROUP);
+  w4a16::GemvArgs a = gemv_args(packed_u4, scales_bf16, false, x_bf16, y_f32, nullptr, N, N, K);
   const w4a16::Plan p = make_plan(a, T);
-  return w4a16::launch(a, p, T, stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+  return run(a, T, nullptr, nullptr, p, stream);
+}
+
+w4a16_status w4a16_matmul_tiled(const void* tiled, const uint16_t* x_bf16, float* y_f32, int64_t N, int64_t K,
+                                int32_t T, hipStream_t stream) {
+  if (!tiled || !x_bf16 || !y_f32) return W4A16_ERR_NULL_POINTER;
+  if (N < 1 || N > kMaxRows) return W4A16_ERR_BAD_SHAPE;
+  if (w4a16_status s = check_kt(K, T)) return s;
+  if (!aligned(tiled, 16) || !aligned(x_bf16, 16) || !aligned(y_f32, 4)) return W4A16_ERR_MISALIGNED;
+  if (w4a16_status s = check_device()) return s;
+  w4a16::GemvArgs a =
+      gemv_args(static_cast<const uint8_t*>(tiled), nullptr, true, x_bf16, y_f32, nullptr, N, N, K);
+  const w4a16::Plan p = w4a16::plan_mfma(a, T, t_cus);
+  return run(a, T, nullptr, nullptr, p, stream);
 }
 
 size_t w4a16_workspace_bytes(int64_t n_out, int32_t T) {
@@ -141,39 +199,55 @@ w4a16_status w4a16_head_gather(const int32_t* row_ids, int64_t n_ids, const uint
                                const uint16_t* scales_bf16, int64_t n_rows, const uint16_t* x_bf16, int64_t K,
                                int32_t T, float* y_f32, int32_t* argmax_id, float* argmax_val, void* workspace,
                                size_t workspace_bytes, hipStream_t stream) {
-  if (!packed_u4 || !scales_bf16 || !x_bf16) return W4A16_ERR_NULL_POINTER;
-  if (!y_f32 && !argmax_id) return W4A16_ERR_NULL_POINTER;
-  if (argmax_val && !argmax_id) return W4A16_ERR_NULL_POINTER;
-  if (n_ids < 1 || n_ids > kMaxRows || n_rows < 1 || n_rows > kMaxRows) return W4A16_ERR_BAD_SHAPE;
-  if (!row_ids && n_ids != n_rows) return W4A16_ERR_BAD_SHAPE;
-  if (w4a16_status s = check_kt(K, T)) return s;
-  if (!aligned(packed_u4, 16) || !aligned(x_bf16, 16) || !aligned(scales_bf16, 2) || !aligned(y_f32, 4) ||
-      !aligned(row_ids, 4) || !aligned(argmax_id, 4) || !aligned(argmax_val, 4))
-    return W4A16_ERR_MISALIGNED;
-  const bool want_argmax = argmax_id != nullptr;
-  if (want_argmax) {
-    if (!workspace || workspace_bytes < w4a16_workspace_bytes(n_ids, T) || !aligned(workspace, 16))
-      return W4A16_ERR_WORKSPACE;
-  }
-  if (w4a16_status s = check_device()) return s;
-
-  w4a16::GemvArgs a{};
-  a.packed = packed_u4;
-  a.scales = scales_bf16;
-  a.x = x_bf16;
-  a.y = y_f32;
-  a.row_ids = row_ids;
-  a.partial = want_argmax ? static_cast<int2*>(workspace) : nullptr;
-  a.n_out = n_ids;
-  a.n_rows = n_rows;
-  a.K = (int32_t)K;
-  a.G = (int32_t)(K / W4A16_GROUP);
+  if (!packed_u4 || !scales_bf16) return W4A16_ERR_NULL_POINTER;
+  if (!aligned(packed_u4, 16) || !aligned(scales_bf16, 2)) return W4A16_ERR_MISALIGNED;
+  if (w4a16_status s = check_gather(row_ids, n_ids, n_rows, x_bf16, K, T, y_f32, argmax_id, argmax_val, workspace,
+                                    workspace_bytes))
+    return s;
+  w4a16::GemvArgs a = gemv_args(packed_u4, scales_bf16, false, x_bf16, y_f32, row_ids, n_ids, n_rows, K);
+  a.partial = argmax_id ? static_cast<int2*>(workspace) : nullptr;
   const w4a16::Plan p = make_plan(a, T);
-  if (w4a16::launch(a, p, T, stream) != hipSuccess) return W4A16_ERR_HIP;
-  if (want_argmax &&
-      w4a16::launch_argmax_final(a.partial, p.grid, T, argmax_id, argmax_val, stream) != hipSuccess)
-    return W4A16_ERR_HIP;
-  return W4A16_OK;
+  return run(a, T, argmax_id, argmax_val, p, stream);
+}
+
+w4a16_status w4a16_head_gather_tiled(const int32_t* row_ids, int64_t n_ids, const void* tiled, int64_t n_rows,
+                                     const uint16_t* x_bf16, int64_t K, int32_t T, float* y_f32, int32_t* argmax_id,
+                                     float* argmax_val, void* workspace, size_t workspace_bytes,
+                                     hipStream_t stream) {
+  if (!tiled) return W4A16_ERR_NULL_POINTER;
+  if (!aligned(tiled, 16)) return W4A16_ERR_MISALIGNED;
+  if (w4a16_status s = check_gather(row_ids, n_ids, n_rows, x_bf16, K, T, y_f32, argmax_id, argmax_val, workspace,
+                                    workspace_bytes))
+    return s;
+  w4a16::GemvArgs a =
+      gemv_args(static_cast<const uint8_t*>(tiled), nullptr, true, x_bf16, y_f32, row_ids, n_ids, n_rows, K);
+  a.partial = argmax_id ? static_cast<int2*>(workspace) : nullptr;
+  const w4a16::Plan p = w4a16::plan_mfma(a, T, t_cus);
+  return run(a, T, argmax_id, argmax_val, p, stream);
+}
+
+size_t w4a16_tiled_tile_bytes(int64_t K) {
+  if (K < W4A16_GROUP || K > kMaxK || K % W4A16_GROUP != 0) return 0;
+  return (size_t)w4a16::tiled_tile_bytes(K / W4A16_GROUP);
+}
+
+size_t w4a16_tiled_bytes(int64_t N, int64_t K) {
+  if (N < 1 || N > kMaxRows) return 0;
+  return (size_t)((N + 15) / 16) * w4a16_tiled_tile_bytes(K);
+}
+
+w4a16_status w4a16_repack_tiled(const uint8_t* packed_u4, const uint16_t* scales_bf16, int64_t N, int64_t K,
+                                void* tiled, size_t tiled_bytes, hipStream_t stream) {
+  if (!packed_u4 || !scales_bf16 || !tiled) return W4A16_ERR_NULL_POINTER;
+  if (N < 1 || N > kMaxRows) return W4A16_ERR_BAD_SHAPE;
+  if (w4a16_status s = check_kt(K, 1)) return s;
+  if (!aligned(packed_u4, 16) || !aligned(scales_bf16, 2) || !aligned(tiled, 16)) return W4A16_ERR_MISALIGNED;
+  if (tiled_bytes < w4a16_tiled_bytes(N, K)) return W4A16_ERR_WORKSPACE;
+  if (w4a16_status s = check_device()) return s;
+  return w4a16::launch_repack(packed_u4, scales_bf16, N, (int32_t)K, static_cast<uint8_t*>(tiled), stream) ==
+                 hipSuccess
+             ? W4A16_OK
+             : W4A16_ERR_HIP;
 }
 
 size_t w4a16_batch_table_bytes(int32_t count) {
@@ -188,28 +262,28 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
   if (table_bytes < w4a16_batch_table_bytes(count) || !aligned(table_host, 8)) return W4A16_ERR_WORKSPACE;
   for (int32_t i = 0; i < count; ++i) {
     const w4a16_problem& q = problems[i];
-    if (!q.packed_u4 || !q.scales_bf16 || !q.x_bf16 || !q.y_f32) return W4A16_ERR_NULL_POINTER;
+    if (q.layout != W4A16_LAYOUT_ROW_MAJOR && q.layout != W4A16_LAYOUT_TILED) return W4A16_ERR_BAD_SHAPE;
+    if (q.reserved != 0) return W4A16_ERR_BAD_SHAPE;
+    const bool tiled = q.layout == W4A16_LAYOUT_TILED;
+    if (!q.packed_u4 || (!tiled && !q.scales_bf16) || !q.x_bf16 || !q.y_f32) return W4A16_ERR_NULL_POINTER;
     if (q.N < 1 || q.N > kMaxRows) return W4A16_ERR_BAD_SHAPE;
     if (w4a16_status s = check_kt(q.K, T)) return s;
-    if (!aligned(q.packed_u4, 16) || !aligned(q.x_bf16, 16) || !aligned(q.scales_bf16, 2) || !aligned(q.y_f32, 4))
+    if (!aligned(q.packed_u4, 16) || !aligned(q.x_bf16, 16) || (!tiled && !aligned(q.scales_bf16, 2)) ||
+        !aligned(q.y_f32, 4))
       return W4A16_ERR_MISALIGNED;
   }
-  const w4a16::Tile bt = batch_tile(T);
   auto* hdr = static_cast<TableHeader*>(table_host);
   auto* args = reinterpret_cast<w4a16::GemvArgs*>(hdr + 1);
+  bool all_tiled = true;
+  for (int32_t i = 0; i < count; ++i) all_tiled = all_tiled && problems[i].layout == W4A16_LAYOUT_TILED;
+  const w4a16::Tile bt = batch_tile(T, all_tiled);
   int64_t grid = 0;
   int lds = 0, threads = 64;
   for (int32_t i = 0; i < count; ++i) {
     const w4a16_problem& q = problems[i];
-    w4a16::GemvArgs a{};
-    a.packed = q.packed_u4;
-    a.scales = q.scales_bf16;
-    a.x = q.x_bf16;
-    a.y = q.y_f32;
-    a.n_out = q.N;
-    a.n_rows = q.N;
-    a.K = (int32_t)q.K;
-    a.G = (int32_t)(q.K / W4A16_GROUP);
+    const bool tiled = q.layout == W4A16_LAYOUT_TILED;
+    w4a16::GemvArgs a = gemv_args(q.packed_u4, tiled ? nullptr : q.scales_bf16, tiled, q.x_bf16, q.y_f32, nullptr,
+                                  q.N, q.N, q.K);
     const w4a16::Plan p = w4a16::plan_tile(a, T, bt);
     a.wg_start = grid;
     grid += p.grid;

@@ -28,9 +28,22 @@ struct GemvArgs {
   int32_t xs_stride;       // halves per staged token row
   int32_t wave_lds;        // bytes of LDS per wave
   int32_t fin_offset;      // byte offset of the final-value area
-  int32_t vec_scales;      // 1: scale rows are 16-byte aligned and G % 8 == 0 (8 scales per load)
-  int32_t reserved;
+  int32_t vec_scales;      // 1: eight scales per 16-byte load (tiled layout, or row-major rows
+                           //    16-byte aligned with G % 8 == 0)
+  int32_t tiled;           // 1: packed points at the tiled layout (scales inside it)
+  int64_t tile_bytes;      // tiled layout: bytes per 16-row tile
 };
+
+// Tiled weight layout (see include/w4a16.h): per 16-row tile, chunks of up
+// to eight 128-column groups; a group is 16 rows x 64 code bytes in row
+// order, and a chunk's codes are followed by 16 rows x 8 bf16 scales.
+constexpr int kTileGroupBytes = 16 * 64;
+constexpr int kTileChunkGroups = 8;
+constexpr int kTileScaleBytes = 16 * kTileChunkGroups * 2;
+constexpr int kTileChunkBytes = kTileChunkGroups * kTileGroupBytes + kTileScaleBytes;
+inline int64_t tiled_tile_bytes(int64_t G) {
+  return G * kTileGroupBytes + (G + kTileChunkGroups - 1) / kTileChunkGroups * kTileScaleBytes;
+}
 
 // Kernel shapes.  Dot: lanes split each row's K (v_dot2).  Split: matrix-core
 // workgroup whose waves split K over the same 16-row tiles.  Shared:
@@ -56,12 +69,15 @@ struct Plan {
 bool parse_tile(const char* text, Tile* t);
 
 // Fill the tiling fields of `a` and return the launch plan.
-Plan plan_mfma(GemvArgs& a, int T);  // default matrix-core tile for one launch
+Plan plan_mfma(GemvArgs& a, int T, int cus);  // default matrix-core tiling of one launch (cus: CUs of the device)
 Plan plan_dot(GemvArgs& a, int T);
 Plan plan_tile(GemvArgs& a, int T, const Tile& t);
 
+
 hipError_t launch(const GemvArgs& a, const Plan& p, int T, hipStream_t s);
 hipError_t launch_batch(const GemvArgs* table_dev, int count, const Plan& p, int T, hipStream_t s);
+hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, int64_t N, int32_t K, uint8_t* tiled,
+                         hipStream_t s);
 hipError_t launch_argmax_final(const int2* partial, int64_t nparts, int T, int32_t* id, float* val, hipStream_t s);
 
 // Upper bound of the workgroups any plan uses for n_out rows (sizes the argmax workspace).

@@ -205,6 +205,93 @@ __device__ __forceinline__ void stage_wave(const GemvArgs& a, _Float16* xs, int 
   }
 }
 
+// Eight bf16 (natural order) -> eight fp16 in slot order, unscaled; exact
+// for every value that passes range8.
+__device__ __forceinline__ u4_t convert8_exact(u4_t v) {
+  const float x0 = __uint_as_float(v.x << 16), x1 = __uint_as_float(v.x & 0xFFFF0000u);
+  const float x2 = __uint_as_float(v.y << 16), x3 = __uint_as_float(v.y & 0xFFFF0000u);
+  const float x4 = __uint_as_float(v.z << 16), x5 = __uint_as_float(v.z & 0xFFFF0000u);
+  const float x6 = __uint_as_float(v.w << 16), x7 = __uint_as_float(v.w & 0xFFFF0000u);
+  return u4_t{as_u32(__builtin_amdgcn_cvt_pkrtz(x0, x4)), as_u32(__builtin_amdgcn_cvt_pkrtz(x1, x5)),
+              as_u32(__builtin_amdgcn_cvt_pkrtz(x2, x6)), as_u32(__builtin_amdgcn_cvt_pkrtz(x3, x7))};
+}
+
+// Running range of the bf16 magnitudes m of eight values: mx = max m, mn =
+// min (m - 1) mod 2^16 (a zero wraps to 0xFFFF and never counts as small).
+__device__ __forceinline__ void range8(u4_t v, us2_t& mx, us2_t& mn) {
+  const us2_t one = {1, 1};
+  const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const us2_t m = __builtin_bit_cast(us2_t, w[i] & 0x7FFF7FFFu);
+    mx = __builtin_elementwise_max(mx, m);
+    mn = __builtin_elementwise_min(mn, m - one);
+  }
+}
+
+// A bf16 converts to fp16 exactly, with no scaling, when it is zero or its
+// magnitude lies in [2^-17, 65280] (8 significant bits: fp16 normals from
+// 2^-14, subnormals keep 8 bits down to 2^-17).
+__device__ __forceinline__ bool range_ok(us2_t mx, us2_t mn) {
+  return max((unsigned)mx.x, (unsigned)mx.y) <= 0x477Fu && min((unsigned)mn.x, (unsigned)mn.y) >= 0x36FFu;
+}
+
+// One-pass staging of x[t][gs*128 .. ge*128) by threads tid = 0..nthreads-1:
+// four 16-byte chunks per thread in flight at a time, converted to fp16
+// without scaling.  Returns true when some value of this thread's chunks is
+// not exact that way (the caller then stages again with a power-of-two
+// scale per token row; both give the same products, scaled by 2^E).
+template <int TT>
+__device__ __forceinline__ bool stage_direct(const GemvArgs& a, _Float16* xs, int gs, int ge, int tid,
+                                             int nthreads) {
+  constexpr int kBatch = 4;
+  const int n8 = (ge - gs) * (kGroup / 8);  // chunks per token row
+  const int total = TT * n8;
+  const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)gs * kGroup);
+  u4_t* dst = reinterpret_cast<u4_t*>(xs);
+  const int src_row = a.K / 8, dst_row = a.xs_stride / 8;
+  us2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+  int t = 0, b = tid;  // chunk (t, b) has index t * n8 + b
+  while (b >= n8 && t < TT) {
+    b -= n8;
+    ++t;
+  }
+  for (int base = tid; base < total; base += kBatch * nthreads) {
+    u4_t v[kBatch];
+    int d[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      d[i] = t < TT ? t * dst_row + b : -1;
+      if (t < TT) v[i] = src[t * src_row + b];
+      b += nthreads;
+      while (b >= n8 && t < TT) {
+        b -= n8;
+        ++t;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (d[i] >= 0) {
+        range8(v[i], mx, mn);
+        dst[d[i]] = convert8_exact(v[i]);
+      }
+    }
+  }
+  return !range_ok(mx, mn);
+}
+
+// True on every thread of the workgroup when pred holds on any of them
+// (flags[] holds one word per wave; ends with a barrier).
+__device__ __forceinline__ bool workgroup_any(bool pred, unsigned* flags) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool w = __ballot(pred) != 0;
+  if ((threadIdx.x & 63) == 0) flags[wave] = w ? 1u : 0u;
+  __syncthreads();
+  unsigned any = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) any |= flags[i];
+  return any != 0;
+}
+
 // ----------------------------------------------------------------- dot ----
 
 // Workgroup-cooperative staging of x[t][gs*128 .. ge*128) for the dot path.
@@ -341,6 +428,18 @@ __device__ __forceinline__ float scale_of(u4_t v, int e) {
   return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
 }
 
+// Offset, in 16-byte units, of group g's codes from a lane's code pointer.
+__device__ __forceinline__ int code_off(const GemvArgs& a, int g) {
+  return a.tiled ? (g >> 3) * (kTileChunkBytes / 16) + (g & 7) * (kTileGroupBytes / 16) : 4 * g;
+}
+
+// Offset, in 16-byte units, of the eight scales of groups g .. g+7 (g a
+// multiple of 8) from a lane's scale pointer.
+__device__ __forceinline__ int scale_off(const GemvArgs& a, int g) {
+  return a.tiled ? (g >> 3) * (kTileChunkBytes / 16) + min(kTileChunkGroups, a.G - g) * (kTileGroupBytes / 16)
+                 : g >> 3;
+}
+
 constexpr int kRing = 8;  // groups of weight codes in flight per wave
 
 // The K loop of one wave: groups [g_begin, g_end) of RT 16-row tiles.  The
@@ -350,8 +449,10 @@ constexpr int kRing = 8;  // groups of weight codes in flight per wave
 // output row r16 of a tile and quarter kq of each 128-column group: one
 // 16-byte load per group feeds four MFMAs (tokens as the A operand, padded to
 // 16 rows; weights as the B operand), whose sum gets the group's scale.
-// SHARED: the slice is staged once for the whole workgroup (stage_block);
-// otherwise each wave stages its own range (stage_wave, no barrier).
+// SHARED: the slice is staged once for the whole workgroup; otherwise each
+// wave stages its own range (no barrier).  Staging is one pass without
+// scaling when every activation converts to fp16 exactly, else the scaled
+// two-pass staging (stage_block / stage_wave).
 // VS: scales are read eight groups (16 bytes) per load (needs G % 8 == 0,
 // 16-byte aligned scale rows and g_begin % 8 == 0); otherwise one 2-byte
 // load per group.
@@ -371,19 +472,34 @@ __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* cons
     const int np = (n + PD - 1) / PD * PD;  // padded to whole ring cycles
     // Ring prologue (tile 0 of the slice), issued before the activations are
     // staged so that the weight latency overlaps the activation round trip.
-    if constexpr (VS) sv = reinterpret_cast<const u4_t*>(sp[0])[sb / 8];
+    if constexpr (VS) sv = reinterpret_cast<const u4_t*>(sp[0])[scale_off(a, sb)];
 #pragma unroll
     for (int s = 0; s < PD; ++s) {
       const int g = sb + min(s, n - 1);
       if constexpr (!VS) sq[s] = sp[0][g];
-      q[s] = load_codes(cp[0] + 4 * g);
+      q[s] = load_codes(cp[0] + code_off(a, g));
       __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
     }
     if constexpr (SHARED) {
-      stage_block<TT>(a, xs, maxbuf, sb, se, E);
+      if (sb != g_begin) __syncthreads();  // every wave is done with the previous slice
+      const bool bad = stage_direct<TT>(a, xs, sb, se, threadIdx.x, blockDim.x);
+      if (workgroup_any(bad, maxbuf)) {
+        __syncthreads();  // every wave has read the flags before the max buffer is reused
+        stage_block<TT>(a, xs, maxbuf, sb, se, E);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) E[t] = 0;
+      }
     } else {
       lds_fence();
-      stage_wave<TT>(a, xs, sb, se, lane, E);
+      const bool bad = stage_direct<TT>(a, xs, sb, se, lane, 64);
+      if (__ballot(bad) != 0) {
+        lds_fence();
+        stage_wave<TT>(a, xs, sb, se, lane, E);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) E[t] = 0;
+      }
       lds_fence();
     }
     // Staging waited for its activation loads, issued after the weight loads
@@ -403,7 +519,7 @@ __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* cons
         if constexpr (VS) {
           const uint16_t* base = (last && has_next) ? spn : sp[tl];
           const int gv = last ? (has_next ? sb : sb + fi) : sb + fi + PD;
-          svn = reinterpret_cast<const u4_t*>(base)[gv / 8];
+          svn = reinterpret_cast<const u4_t*>(base)[scale_off(a, gv)];
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
@@ -432,7 +548,7 @@ __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* cons
           const u4_t* cpl = (nxt && has_next) ? cpn : cp[tl];
           const int gg = sb + (nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1));
           if constexpr (!VS) sq[s] = ((nxt && has_next) ? spn : sp[tl])[gg];
-          q[s] = load_codes(cpl + 4 * gg);
+          q[s] = load_codes(cpl + code_off(a, gg));
           // keep this slot's reload here: sunk to the end of the loop, the
           // reloads would make every iteration wait for the whole ring
           __builtin_amdgcn_sched_barrier(0);
@@ -452,7 +568,10 @@ __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* cons
   }
 }
 
-// Row pointers of the RT tiles starting at output row row0 for this lane.
+// Code and scale pointers of the RT tiles starting at output row row0 for
+// this lane.  Row-major: the row's codes and scales.  Tiled: the lane's
+// 16 bytes in the first group block of the row's tile, and the row's 16
+// bytes in the first scale block.
 template <int RT>
 __device__ __forceinline__ void tile_pointers(const GemvArgs& a, int64_t row0, int r16, int kq,
                                               const u4_t* (&cp)[RT], const uint16_t* (&sp)[RT]) {
@@ -461,8 +580,14 @@ __device__ __forceinline__ void tile_pointers(const GemvArgs& a, int64_t row0, i
   for (int tl = 0; tl < RT; ++tl) {
     int64_t w = weight_row(a, row0 + tl * 16 + r16);
     if (w < 0) w = 0;  // read a valid row; the output is masked later
-    cp[tl] = reinterpret_cast<const u4_t*>(a.packed + w * kh) + kq;
-    sp[tl] = a.scales + w * a.G;
+    if (a.tiled) {
+      const uint8_t* tb = a.packed + (w >> 4) * a.tile_bytes;
+      cp[tl] = reinterpret_cast<const u4_t*>(tb) + 4 * (w & 15) + kq;
+      sp[tl] = reinterpret_cast<const uint16_t*>(tb) + 8 * (w & 15);
+    } else {
+      cp[tl] = reinterpret_cast<const u4_t*>(a.packed + w * kh) + kq;
+      sp[tl] = a.scales + w * a.G;
+    }
   }
 }
 
@@ -626,7 +751,7 @@ __device__ __forceinline__ void tile_workgroup(const GemvArgs& a, int64_t wg, un
 }
 
 template <int TT, int RT, bool SHARED>
-__global__ void __launch_bounds__(512) w4a16_tile_kernel(GemvArgs a) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SHARED && RT == 1 ? 4 : 1))) w4a16_tile_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   tile_workgroup<TT, RT, SHARED>(a, blockIdx.x, smem);
 }
@@ -634,7 +759,7 @@ __global__ void __launch_bounds__(512) w4a16_tile_kernel(GemvArgs a) {
 // Grouped launch: workgroup b runs tile b - wg_start of the last problem whose
 // wg_start <= b.
 template <int TT, int RT, bool SHARED>
-__global__ void __launch_bounds__(512) w4a16_tile_batch_kernel(const GemvArgs* __restrict__ table, int count) {
+__global__ void __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(SHARED && RT == 1 ? 4 : 1))) w4a16_tile_batch_kernel(const GemvArgs* __restrict__ table, int count) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int64_t b = blockIdx.x;
   int lo = 0, hi = count - 1;
@@ -647,6 +772,46 @@ __global__ void __launch_bounds__(512) w4a16_tile_batch_kernel(const GemvArgs* _
   }
   const GemvArgs a = table[lo];
   tile_workgroup<TT, RT, SHARED>(a, b - a.wg_start, smem);
+}
+
+// ---------------------------------------------------------------- repack ----
+
+// Row-major codes and scales -> tiled layout, one thread per 16 output bytes.
+// Per tile the thread index runs over G * 64 code pieces (group g, row r,
+// quarter q: bytes 64g + 16q .. of row 16*tile + r) and then ceil(G/8) * 16
+// scale pieces (chunk c, row r: the bf16 scales of groups 8c .. 8c+7).
+// Rows past N and groups past G are written as zeros.
+__global__ void __launch_bounds__(256) w4a16_repack_kernel(const uint8_t* __restrict__ packed,
+                                                           const uint16_t* __restrict__ scales, int64_t N, int K,
+                                                           uint8_t* __restrict__ tiled, int64_t tile_bytes,
+                                                           int64_t total) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= total) return;
+  const int G = K / kGroup;
+  const int chunks = (G + kTileChunkGroups - 1) / kTileChunkGroups;
+  const int64_t per_tile = (int64_t)G * 64 + (int64_t)chunks * 16;
+  const int64_t tile = i / per_tile;
+  const int64_t rem = i - tile * per_tile;
+  uint8_t* tb = tiled + tile * tile_bytes;
+  u4_t v = {0u, 0u, 0u, 0u};
+  if (rem < (int64_t)G * 64) {
+    const int g = (int)(rem >> 6), r = (int)(rem >> 2) & 15, q = (int)rem & 3;
+    const int64_t row = tile * 16 + r;
+    if (row < N) v = *reinterpret_cast<const u4_t*>(packed + row * (K / 2) + g * 64 + q * 16);
+    *reinterpret_cast<u4_t*>(tb + (int64_t)(g >> 3) * kTileChunkBytes + (g & 7) * kTileGroupBytes + r * 64 +
+                             q * 16) = v;
+  } else {
+    const int j = (int)(rem - (int64_t)G * 64);
+    const int c = j >> 4, r = j & 15;
+    const int64_t row = tile * 16 + r;
+    const int ng = min(kTileChunkGroups, G - c * kTileChunkGroups);
+    unsigned short sc[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sc[e] = (row < N && e < ng) ? scales[row * G + c * kTileChunkGroups + e] : 0;
+    v = u4_t{sc[0] | ((unsigned)sc[1] << 16), sc[2] | ((unsigned)sc[3] << 16), sc[4] | ((unsigned)sc[5] << 16),
+             sc[6] | ((unsigned)sc[7] << 16)};
+    *reinterpret_cast<u4_t*>(tb + (int64_t)c * kTileChunkBytes + ng * kTileGroupBytes + r * 16) = v;
+  }
 }
 
 // ---------------------------------------------------------- argmax final ----
@@ -806,7 +971,7 @@ Plan plan_tile(GemvArgs& a, int T, const Tile& t) {
   Plan p{};
   p.variant = t.shape;
   p.rt = t.rt;
-  a.vec_scales = (a.G % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15) == 0) ? 1 : 0;
+  a.vec_scales = (a.tiled || (a.G % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15) == 0)) ? 1 : 0;
   if (t.shape == kShared)
     plan_shared(a, T, t.rt, t.nw, &p);
   else
@@ -814,24 +979,27 @@ Plan plan_tile(GemvArgs& a, int T, const Tile& t) {
   return p;
 }
 
-// Default matrix-core tiling of a single launch.  Tall matrices (>= 1024
-// tiles of 16 rows) use shared workgroups: the full vocabulary head (15,520
-// tiles) measured best with eight waves of four tiles each, mid-size
-// matrices with four waves of one tile.  Shorter ones split K over the waves
-// of a workgroup so that they still put ~12 waves of weight loads on every
-// CU.  W4A16_TILE="split|shared,rt,waves" overrides the choice (for
-// measurement).
-Plan plan_mfma(GemvArgs& a, int T) {
+// Default matrix-core tiling of a single launch (cus: compute units of the
+// device), from the MI355X sweeps.  Tall matrices (>= 1024 tiles of 16 rows)
+// use shared workgroups.  Row-major weights: the full vocabulary head
+// (15,520 tiles) is fastest with eight waves of four tiles each.  Tiled
+// weights: one tile per wave, eight waves per workgroup for the head, four
+// for mid-size matrices.  Shorter matrices split K over the waves of a
+// workgroup so that they still put ~12 waves of weight loads on every CU.
+// W4A16_TILE="split|shared,rt,waves" overrides the choice (for measurement).
+Plan plan_mfma(GemvArgs& a, int T, int cus) {
   const int64_t tiles = cdiv(a.n_out, 16);
   Tile t;
-  if (tiles >= 8192)
+  if (tiles >= 4096 && a.tiled)
+    t = Tile{kShared, 1, 8};
+  else if (tiles >= 8192)
     t = Tile{kShared, 4, 8};
   else if (tiles >= 4096)
     t = Tile{kShared, 2, 8};
   else if (tiles >= 1024)
     t = Tile{kShared, 1, 4};
   else
-    t = Tile{kSplit, 1, (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(3072, tiles)))};
+    t = Tile{kSplit, 1, (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(12LL * std::max(cus, 1), tiles)))};
   Tile o;
   if (parse_tile(std::getenv("W4A16_TILE"), &o)) t = o;
   return plan_tile(a, T, t);
@@ -871,6 +1039,16 @@ hipError_t launch(const GemvArgs& a, const Plan& p, int T, hipStream_t s) {
 hipError_t launch_batch(const GemvArgs* table_dev, int count, const Plan& p, int T, hipStream_t s) {
   GemvArgs unused{};
   return for_t(T, [&](auto tt) { return launch_t<decltype(tt)::value>(unused, table_dev, count, p, s); });
+}
+
+hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, int64_t N, int32_t K, uint8_t* tiled,
+                         hipStream_t s) {
+  const int G = K / kGroup;
+  const int64_t tiles = cdiv(N, 16);
+  const int64_t total = tiles * ((int64_t)G * 64 + cdiv(G, kTileChunkGroups) * 16);
+  hipLaunchKernelGGL(w4a16_repack_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, packed, scales, N, K,
+                     tiled, tiled_tile_bytes(G), total);
+  return hipGetLastError();
 }
 
 hipError_t launch_argmax_final(const int2* partial, int64_t nparts, int T, int32_t* id, float* val, hipStream_t s) {

@@ -37,6 +37,20 @@ def lib():
     l.w4a16_set_variant.argtypes = [i32]
     l.w4a16_set_variant.restype = i32
     l.w4a16_get_variant.restype = i32
+    l.w4a16_tiled_tile_bytes.argtypes = [i64]
+    l.w4a16_tiled_tile_bytes.restype = sz
+    l.w4a16_tiled_bytes.argtypes = [i64, i64]
+    l.w4a16_tiled_bytes.restype = sz
+    l.w4a16_repack_tiled.argtypes = [vp, vp, i64, i64, vp, sz, vp]
+    l.w4a16_repack_tiled.restype = i32
+    l.w4a16_matmul_tiled.argtypes = [vp, vp, vp, i64, i64, i32, vp]
+    l.w4a16_matmul_tiled.restype = i32
+    l.w4a16_head_gather_tiled.argtypes = [vp, i64, vp, i64, vp, i64, i32, vp, vp, vp, vp, sz, vp]
+    l.w4a16_head_gather_tiled.restype = i32
+    l.w4a16_batch_table_bytes.argtypes = [i32]
+    l.w4a16_batch_table_bytes.restype = sz
+    l.w4a16_batch_plan.argtypes = [vp, i32, i32, vp, sz]
+    l.w4a16_batch_plan.restype = i32
     return l
 
 
@@ -48,7 +62,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.w4a16_abi_version() == 1
+    assert lib.w4a16_abi_version() == 2
     for s in range(8):
         assert lib.w4a16_status_string(s)
     assert lib.w4a16_status_string(99) == b"unknown status"
@@ -124,3 +138,59 @@ def test_valid_call_without_gpu_fails_cleanly(lib):
     except ImportError:
         pass
     assert mm(lib) in (HIP, UNSUP)
+
+
+def test_tiled_byte_counts(lib):
+    # a tile: G blocks of 16 rows x 64 code bytes, plus 256 scale bytes per 8 groups
+    assert lib.w4a16_tiled_tile_bytes(5120) == 40 * 1024 + 5 * 256
+    assert lib.w4a16_tiled_tile_bytes(1152) == 9 * 1024 + 2 * 256      # G = 9: a short last chunk
+    assert lib.w4a16_tiled_tile_bytes(128) == 1024 + 256
+    assert lib.w4a16_tiled_tile_bytes(100) == 0
+    # G % 8 == 0: exactly the row-major codes + scales (0.515625 B per weight)
+    assert lib.w4a16_tiled_bytes(248320, 5120) == 248320 * 5120 // 2 + 2 * 248320 * 40
+    assert lib.w4a16_tiled_bytes(17, 128) == 2 * (1024 + 256)           # rows padded to 32
+    assert lib.w4a16_tiled_bytes(0, 128) == 0
+
+
+def test_tiled_rejections(lib):
+    need = lib.w4a16_tiled_bytes(64, 256)
+    rp = lambda p=A, s=A, N=64, K=256, t=A, tb=need: lib.w4a16_repack_tiled(p, s, N, K, t, tb, None)
+    assert rp(p=None) == NULLP and rp(s=None) == NULLP and rp(t=None) == NULLP
+    assert rp(N=0) == SHAPE and rp(K=200) == SHAPE
+    assert rp(t=A + 8) == ALIGN and rp(p=A + 8) == ALIGN and rp(s=A + 1) == ALIGN
+    assert rp(tb=need - 1) == WS
+    mt = lambda w=A, x=A, y=A, N=64, K=256, T=2: lib.w4a16_matmul_tiled(w, x, y, N, K, T, None)
+    assert mt(w=None) == NULLP and mt(x=None) == NULLP and mt(y=None) == NULLP
+    assert mt(N=0) == SHAPE and mt(K=129) == SHAPE and mt(T=9) == SHAPE
+    assert mt(w=A + 4) == ALIGN and mt(x=A + 2) == ALIGN and mt(y=A + 2) == ALIGN
+    gt = lambda ids=A, n_ids=10, w=A, n_rows=100, x=A, K=256, T=2, y=A, am=None, av=None, ws=None, wsb=0: \
+        lib.w4a16_head_gather_tiled(ids, n_ids, w, n_rows, x, K, T, y, am, av, ws, wsb, None)
+    assert gt(w=None) == NULLP and gt(y=None) == NULLP and gt(av=A) == NULLP
+    assert gt(w=A + 8) == ALIGN and gt(ids=A + 2) == ALIGN
+    assert gt(n_ids=0) == SHAPE and gt(ids=None) == SHAPE
+    assert gt(am=A) == WS
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("packed_u4", ctypes.c_void_p), ("scales_bf16", ctypes.c_void_p), ("x_bf16", ctypes.c_void_p),
+                ("y_f32", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("layout", ctypes.c_int32),
+                ("reserved", ctypes.c_int32)]
+
+
+def plan(lib, probs, T=4):
+    arr = (Problem * len(probs))(*probs)
+    nbytes = lib.w4a16_batch_table_bytes(len(probs))
+    buf = (ctypes.c_uint64 * (nbytes // 8 + 1))()
+    return lib.w4a16_batch_plan(ctypes.cast(arr, ctypes.c_void_p), len(probs), T, ctypes.addressof(buf), nbytes)
+
+
+def test_batch_plan_layouts(lib):
+    """Planning is host-only, so it runs here: both layouts accepted, bad fields rejected."""
+    assert ctypes.sizeof(Problem) == 56
+    row = Problem(A, A, A, A, 7168, 5120, 0, 0)
+    tiled = Problem(A, None, A, A, 5120, 17408, 1, 0)
+    assert plan(lib, [row, tiled]) == OK
+    assert plan(lib, [Problem(A, None, A, A, 64, 256, 0, 0)]) == NULLP      # row-major needs scales
+    assert plan(lib, [Problem(A, A, A, A, 64, 256, 2, 0)]) == SHAPE         # unknown layout
+    assert plan(lib, [Problem(A, A, A, A, 64, 256, 1, 5)]) == SHAPE         # reserved must be 0
+    assert plan(lib, [Problem(A + 8, None, A, A, 64, 256, 1, 0)]) == ALIGN  # tiled buffer 16-byte aligned

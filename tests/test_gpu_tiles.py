@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import assert_parity, dev, host, say, weight_dev
+from gpu_util import assert_parity, dev, host, say, sample_rows, weight_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu

@@ -39,7 +39,9 @@ from speculative_verify_gemv_amd import metrics  # noqa: E402
 METRIC = "weight GB/s and % of HBM peak at T=1/4/8 (27B-class shapes); decode cycles/s"
 PEAK_GBPS = 8000.0
 WORKLOAD = "decode_weight_pass_64x(qkv,o,gate_up,down)+lm_head_T4"
-KERNEL_SOURCE = os.path.join(ROOT, "speculative_verify_gemv_amd", "csrc", "w4a16_kernels.hip")
+KERNEL_SOURCES = [os.path.join(ROOT, "speculative_verify_gemv_amd", "csrc", f)
+                  for f in ("w4a16_device.h", "w4a16_internal.h", "w4a16_kernels.hip", "w4a16_kernels_tt.hip",
+                            "w4a16_api.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_body_pass_T4.md")
 COPY_BYTES = 1 << 30
 
@@ -71,10 +73,12 @@ def to_dev(a, torch):
 
 
 def kernel_source_hash():
-    """sha256 of the kernel source with comments and blank space removed (a
+    """sha256 of the kernel sources with comments and blank space removed (a
     comment edit does not change the kernels the counters were taken on)."""
-    with open(KERNEL_SOURCE) as f:
-        text = f.read()
+    text = ""
+    for path in KERNEL_SOURCES:
+        with open(path) as f:
+            text += f.read() + "\n"
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     text = re.sub(r"//[^\n]*", "", text)
     code = "\n".join(line.strip() for line in text.splitlines() if line.strip())
@@ -190,10 +194,10 @@ def main():
         for tiled, table in ((True, per_t), (False, per_t_rm)):
             for Tp in (1, 4, 8):
                 b, _ = (batch, probs) if (Tp == T and tiled) else make_pass(Tp, tiled)
-                for _ in range(2):
+                for _ in range(3):
                     b.run(stream)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                reps = 5
+                reps = 10
                 e0.record(stream)
                 for _ in range(reps):
                     b.run(stream)

@@ -1,20 +1,29 @@
-"""Compile the HIP library libw4a16.so for gfx950 (hipcc, in-tree)."""
+"""Compile the HIP library libw4a16.so for gfx950 (hipcc, in-tree).
+
+The kernel templates are instantiated once per activation-row count T
+(w4a16_kernels_tt.hip built eight times with -DW4A16_TT=1..8); those
+objects, the planning / dispatch unit and the C ABI unit compile in
+parallel and are linked into one shared library.
+"""
 import os
 import subprocess
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a16.so")
-SOURCES = ["w4a16_kernels.hip", "w4a16_api.hip"]
+OBJ_DIR = os.path.join(ROOT, "_build", "w4a16")
+MAX_T = 8
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in generated code.
 HIPCC_FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
     "-Wall", "-Wno-unused-command-line-argument",
 ]
+NOISE = "is not a recognized feature for this target"
 
 
 def hipcc() -> str:
@@ -23,20 +32,47 @@ def hipcc() -> str:
     return path if os.path.exists(path) else "hipcc"
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), *HIPCC_FLAGS, *extra, "-I", os.path.join(ROOT, "include"), "-o", tmp, *srcs]
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
-    noise = "is not a recognized feature for this target"
-    err = "\n".join(l for l in r.stderr.splitlines() if noise not in l)
-    if r.returncode != 0:
-        sys.stderr.write(err + "\n")
+    err = "\n".join(l for l in r.stderr.splitlines() if NOISE not in l)
+    return r.returncode, err
+
+
+def _units():
+    """(source, object, extra flags) of every translation unit."""
+    units = [(os.path.join(CSRC, "w4a16_kernels_tt.hip"), os.path.join(OBJ_DIR, f"kernels_t{t}.o"),
+              [f"-DW4A16_TT={t}"]) for t in range(1, MAX_T + 1)]
+    units.append((os.path.join(CSRC, "w4a16_kernels.hip"), os.path.join(OBJ_DIR, "kernels.o"), []))
+    units.append((os.path.join(CSRC, "w4a16_api.hip"), os.path.join(OBJ_DIR, "api.o"), []))
+    return units
+
+
+def build(verbose: bool = False, extra=()) -> str:
+    os.makedirs(OBJ_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(ROOT, "include")]
+    jobs = []
+    for src, obj, flags in _units():
+        jobs.append([hipcc(), *HIPCC_FLAGS, *extra, *flags, *inc, "-c", "-o", obj, src])
+    workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
+    with ThreadPoolExecutor(max_workers=workers) as pool:
+        results = list(pool.map(lambda c: _run(c, verbose), jobs))
+    failed = [(c, e) for c, (rc, e) in zip(jobs, results) if rc != 0]
+    for c, e in failed:
+        sys.stderr.write(f"{c[-1]}:\n{e}\n")
+    if failed:
         raise RuntimeError("hipcc failed building libw4a16.so")
-    if verbose and err.strip():
+    if verbose:
+        for rc, e in results:
+            if e.strip():
+                sys.stderr.write(e + "\n")
+    tmp = LIB + ".tmp"
+    rc, err = _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
+                    *[obj for _, obj, _ in _units()]], verbose)
+    if rc != 0:
         sys.stderr.write(err + "\n")
+        raise RuntimeError("hipcc failed linking libw4a16.so")
     os.replace(tmp, LIB)
     return LIB
 

@@ -137,7 +137,7 @@ struct TableHeader {
   int32_t T;
   int32_t variant;
   int32_t rt;
-  int32_t reserved1;
+  int32_t tiled;  // 1: every problem tiled (tiled-layout kernels, one tile per wave)
   int32_t threads;
   int32_t lds;
   int32_t reserved0;
@@ -147,12 +147,13 @@ struct TableHeader {
 static_assert(sizeof(TableHeader) == 64, "table header size");
 
 // Tile of grouped launches, from the MI355X sweeps: all problems tiled ->
-// eight waves of one tile; otherwise at T <= 2 four waves of two 16-row
-// tiles, above that eight waves of four (the larger workgroup shares one
-// staged copy of the bigger activation block among more rows).
-// W4A16_BATCH_TILE = "split|shared,rt,waves" overrides it (for measurement).
-w4a16::Tile batch_tile(int T, bool all_tiled) {
-  w4a16::Tile t = all_tiled ? w4a16::Tile{w4a16::kShared, 1, 8}
+// one tile per wave, shared_waves(T, largest K) waves per workgroup;
+// otherwise at T <= 2 four waves of two 16-row tiles, above that eight waves
+// of four (the larger workgroup shares one staged copy of the bigger
+// activation block among more rows).  W4A16_BATCH_TILE = "split|shared,rt,waves" overrides it (for
+// measurement).
+w4a16::Tile batch_tile(int T, bool all_tiled, int64_t kmax) {
+  w4a16::Tile t = all_tiled ? w4a16::Tile{w4a16::kShared, 1, w4a16::shared_waves(T, kmax)}
                   : T <= 2  ? w4a16::Tile{w4a16::kShared, 2, 4}
                             : w4a16::Tile{w4a16::kShared, 4, 8};
   w4a16::Tile o;
@@ -275,8 +276,12 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
   auto* hdr = static_cast<TableHeader*>(table_host);
   auto* args = reinterpret_cast<w4a16::GemvArgs*>(hdr + 1);
   bool all_tiled = true;
-  for (int32_t i = 0; i < count; ++i) all_tiled = all_tiled && problems[i].layout == W4A16_LAYOUT_TILED;
-  const w4a16::Tile bt = batch_tile(T, all_tiled);
+  int64_t kmax = 0;
+  for (int32_t i = 0; i < count; ++i) {
+    all_tiled = all_tiled && problems[i].layout == W4A16_LAYOUT_TILED;
+    kmax = std::max(kmax, problems[i].K);
+  }
+  const w4a16::Tile bt = batch_tile(T, all_tiled, kmax);
   int64_t grid = 0;
   int lds = 0, threads = 64;
   for (int32_t i = 0; i < count; ++i) {
@@ -284,7 +289,7 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
     const bool tiled = q.layout == W4A16_LAYOUT_TILED;
     w4a16::GemvArgs a = gemv_args(q.packed_u4, tiled ? nullptr : q.scales_bf16, tiled, q.x_bf16, q.y_f32, nullptr,
                                   q.N, q.N, q.K);
-    const w4a16::Plan p = w4a16::plan_tile(a, T, bt);
+    const w4a16::Plan p = w4a16::plan_tile(a, T, bt, all_tiled);
     a.wg_start = grid;
     grid += p.grid;
     lds = std::max(lds, p.lds);
@@ -292,7 +297,8 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
     args[i] = a;
   }
   if (grid > 0x7fffffffLL) return W4A16_ERR_BAD_SHAPE;
-  *hdr = TableHeader{kTableMagic, W4A16_ABI_VERSION, count, T, bt.shape, bt.rt, 0, threads, lds, 0, grid,
+  *hdr = TableHeader{kTableMagic, W4A16_ABI_VERSION, count, T, bt.shape, all_tiled ? 1 : bt.rt, all_tiled ? 1 : 0,
+                     threads, lds, 0, grid,
                      {0, 0}};
   return W4A16_OK;
 }
@@ -308,10 +314,12 @@ w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, h
   w4a16::Plan p{};
   if (hdr->variant != w4a16::kSplit && hdr->variant != w4a16::kShared) return W4A16_ERR_BAD_SHAPE;
   if (hdr->rt != 1 && hdr->rt != 2 && hdr->rt != 4) return W4A16_ERR_BAD_SHAPE;
-  if (hdr->threads < 64 || hdr->threads > 512 || hdr->threads % 64 || hdr->lds < 0 || hdr->lds > 65536)
+  if (hdr->threads < 64 || hdr->threads > 1024 || hdr->threads % 64 || hdr->lds < 0 || hdr->lds > 163840)
     return W4A16_ERR_BAD_SHAPE;
+  if (hdr->tiled != 0 && (hdr->tiled != 1 || hdr->rt != 1)) return W4A16_ERR_BAD_SHAPE;
   p.variant = hdr->variant;
   p.rt = hdr->rt;
+  p.tiled = hdr->tiled == 1;
   p.threads = hdr->threads;
   p.grid = hdr->grid;
   p.lds = hdr->lds;

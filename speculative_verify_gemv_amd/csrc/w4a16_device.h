@@ -1,0 +1,851 @@
+// Device code of libw4a16 for gfx950 (CDNA4), shared by the translation
+// units that instantiate it: w4a16_kernels_tt.hip builds launch_t<TT> for
+// one activation-row count TT per object, so the kernels compile in
+// parallel; w4a16_kernels.hip holds the planning, the dispatch and the
+// non-template kernels.
+//
+// W4A16 skinny matmul kernels for AMD Instinct MI355X (gfx950, CDNA4).
+//
+// y[t][n] = sum_k (q[n][k] - 8) * scale[n][k/128] * x[t][k]   (fp32 out)
+//
+// The weight format -- little-endian words of eight nibbles, level = nibble
+// minus 8, one bf16 scale per 128 columns applied after the group's sum -- is
+// the one the qwen-warp/llamAmpere article gives under "qwen-warp: keep the
+// activations in bf16".  That engine turns a nibble pair into exact bf16
+// levels with one OR and one packed bf16 FMA; gfx950 has no packed bf16 add
+// or FMA, so here the exact levels are formed in fp16 instead:
+//
+//   (w & 0x000F000F) | 0x6400_6400  is the fp16 pair (1024 + q0, 1024 + q4)
+//   (w & 0x00F000F0) | 0x5400_5400  is the fp16 pair (  64 + q1,   64 + q5)
+//
+// (at 1024 the fp16 spacing is 1, at 64 it is 1/16 and the nibble sits four
+// bits higher), and one v_pk_add_f16 with -1032 / -72 gives (q - 8) exactly.
+// A 32-bit word of codes becomes eight exact fp16 levels in the slot order
+// k+0, k+4, k+1, k+5, k+2, k+6, k+3, k+7 with 9 VALU operations.
+//
+// Activations are converted once per workgroup slice to fp16 in the same
+// slot order, scaled by 2^E (E chosen per token row and slice from the
+// largest |x|), so every bf16 value that matters is represented exactly; the
+// power of two is removed again when the slice's partial sums are folded, so
+// the result equals the unscaled fp32 arithmetic.  Every product (q-8)*x is
+// exact in fp32; sums are fp32.
+//
+// Two variants:
+//  * matrix core: tokens are the A operand of v_mfma_f32_16x16x32_f16 (T
+//    padded to 16 rows), weights the B operand (16 output rows x 32 k).  A
+//    lane owns one output row and a quarter of each 128-column group, loads
+//    its 16 bytes of that group with one 128-bit load, and feeds the four
+//    words to four MFMAs.  Each 128-column group gets a fresh accumulator
+//    that is then scaled in fp32.  A wave streams RT 16-row tiles one after
+//    the other with eight groups of loads in flight.  In a "shared"
+//    workgroup the waves own different tiles and share one staged copy of
+//    the activations; in a "split" workgroup they split K over the same
+//    tiles and add their partial sums through LDS in wave order.
+//  * dot: lanes split a row's K in 16-byte chunks; v_dot2_f32_f16 forms each
+//    chunk's partial, which is scaled by its group scale; lanes are reduced
+//    with a butterfly across the wavefront.
+//
+// Both reduce in an order fixed by (K, tiling) only, so results are
+// deterministic, and identical weight rows give identical outputs.
+#pragma once
+#include <math.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <type_traits>
+
+#include "w4a16_internal.h"
+
+namespace w4a16 {
+namespace {
+
+typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
+typedef __fp16 h8_t __attribute__((ext_vector_type(8)));  // the MFMA builtin's operand type
+typedef float f4_t __attribute__((ext_vector_type(4)));
+typedef unsigned u4_t __attribute__((ext_vector_type(4)));
+typedef unsigned short us2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kGroup = 128;
+constexpr int kLdsCap = 65536;  // dynamic LDS per workgroup (several workgroups per CU)
+constexpr int kCuLds = 163840;  // LDS of a CU (one workgroup per CU)
+// s_waitcnt immediate (gfx9 encoding) waiting for vmcnt = 0 only.
+constexpr int kWaitVmcnt0 = 0x0F70;
+
+__device__ __forceinline__ float bf16_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
+
+template <typename V>
+__device__ __forceinline__ unsigned as_u32(V h) {
+  static_assert(sizeof(V) == 4, "packed pair");
+  return __builtin_bit_cast(unsigned, h);
+}
+
+// (w & m) | c in one VALU operation (v_and_or_b32: one SGPR operand, one VGPR).
+__device__ __forceinline__ unsigned and_or(unsigned w, unsigned m, unsigned c) {
+  unsigned r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(m), "v"(c));
+  return r;
+}
+
+// Eight exact fp16 levels (q - 8) of one word, slot order 0,4,1,5,2,6,3,7.
+__device__ __forceinline__ u4_t levels8(unsigned w) {
+  const unsigned w8 = w >> 8;
+  const h2_t lo_bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
+  const h2_t hi_bias = {(_Float16)-72.0f, (_Float16)-72.0f};
+  const h2_t a = __builtin_bit_cast(h2_t, and_or(w, 0x000F000Fu, 0x64006400u)) + lo_bias;
+  const h2_t b = __builtin_bit_cast(h2_t, and_or(w, 0x00F000F0u, 0x54005400u)) + hi_bias;
+  const h2_t c = __builtin_bit_cast(h2_t, and_or(w8, 0x000F000Fu, 0x64006400u)) + lo_bias;
+  const h2_t d = __builtin_bit_cast(h2_t, and_or(w8, 0x00F000F0u, 0x54005400u)) + hi_bias;
+  return u4_t{as_u32(a), as_u32(b), as_u32(c), as_u32(d)};
+}
+
+// Largest bf16 magnitude (bit pattern) among the eight values of v.
+__device__ __forceinline__ unsigned absmax8(u4_t v) {
+  us2_t m = __builtin_bit_cast(us2_t, v.x & 0x7FFF7FFFu);
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(us2_t, v.y & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(us2_t, v.z & 0x7FFF7FFFu));
+  m = __builtin_elementwise_max(m, __builtin_bit_cast(us2_t, v.w & 0x7FFF7FFFu));
+  return max((unsigned)m.x, (unsigned)m.y);
+}
+
+__device__ __forceinline__ unsigned wave_max(unsigned m) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off));
+  return m;
+}
+
+// Power-of-two exponent E that maps the largest |x| (bf16 magnitude bits)
+// into [2^14, 2^15): every bf16 within 2^-28 of the maximum is then an exact
+// fp16 normal.  0 for an all-zero or non-finite slice.
+__device__ __forceinline__ int slice_exponent(unsigned mag) {
+  const int e = (int)(mag >> 7);
+  if (mag == 0 || e == 255) return 0;
+  const int unbiased = (e == 0) ? -127 : e - 127;
+  return 14 - unbiased;
+}
+
+// Eight bf16 (natural order) -> eight fp16 scaled by 2^E in slot order.
+__device__ __forceinline__ u4_t convert8(u4_t v, int E) {
+  const float x0 = ldexpf(__uint_as_float(v.x << 16), E), x1 = ldexpf(__uint_as_float(v.x & 0xFFFF0000u), E);
+  const float x2 = ldexpf(__uint_as_float(v.y << 16), E), x3 = ldexpf(__uint_as_float(v.y & 0xFFFF0000u), E);
+  const float x4 = ldexpf(__uint_as_float(v.z << 16), E), x5 = ldexpf(__uint_as_float(v.z & 0xFFFF0000u), E);
+  const float x6 = ldexpf(__uint_as_float(v.w << 16), E), x7 = ldexpf(__uint_as_float(v.w & 0xFFFF0000u), E);
+  return u4_t{as_u32(__builtin_amdgcn_cvt_pkrtz(x0, x4)), as_u32(__builtin_amdgcn_cvt_pkrtz(x1, x5)),
+              as_u32(__builtin_amdgcn_cvt_pkrtz(x2, x6)), as_u32(__builtin_amdgcn_cvt_pkrtz(x3, x7))};
+}
+
+// v_dot2_f32_f16 on two words of packed fp16 pairs: c + a.lo*b.lo + a.hi*b.hi.
+__device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
+  typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2_t, a), __builtin_bit_cast(fp16x2_t, b), c, false);
+}
+
+__device__ __forceinline__ void lds_fence() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Argmax candidate order: a valid id beats an invalid one; larger value wins;
+// equal values go to the lower id.
+__device__ __forceinline__ bool better(float v1, int i1, float v2, int i2) {
+  return i1 >= 0 && (i2 < 0 || v1 > v2 || (v1 == v2 && i1 < i2));
+}
+
+__device__ __forceinline__ void wave_argmax(float& v, int& id) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    const float ov = __shfl_xor(v, off);
+    const int oi = __shfl_xor(id, off);
+    if (better(ov, oi, v, id)) {
+      v = ov;
+      id = oi;
+    }
+  }
+}
+
+// Vocabulary id of output row o, or -1 if o is past the end or its id is out of range.
+__device__ __forceinline__ int64_t weight_row(const GemvArgs& a, int64_t o) {
+  if (o >= a.n_out) return -1;
+  const int64_t w = a.row_ids ? (int64_t)a.row_ids[o] : o;
+  return (w < 0 || w >= a.n_rows) ? -1 : w;
+}
+
+// Writes the per-workgroup argmax partial for token rows 0..TT-1 from the
+// final values fin[(rt*TT + t)*16 + r] of rows row0 + rt*16 + r (rows < nrows).
+template <int TT>
+__device__ __forceinline__ void workgroup_argmax(const GemvArgs& a, const float* fin, int64_t row0, int nrows,
+                                                 int lane, int64_t wg) {
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    float bv = __builtin_nanf("");
+    int bi = -1;
+    for (int r = lane; r < nrows; r += 64) {
+      const int64_t o = row0 + r;
+      const int64_t w = weight_row(a, o);
+      const float v = fin[((r >> 4) * TT + t) * 16 + (r & 15)];
+      if (w >= 0 && !__builtin_isnan(v) && better(v, (int)w, bv, bi)) {
+        bv = v;
+        bi = (int)w;
+      }
+    }
+    wave_argmax(bv, bi);
+    if (lane == 0) a.partial[wg * TT + t] = int2{__float_as_int(bv), bi};
+  }
+}
+
+// ---------------------------------------------------------- staging ----
+
+// Stages x[t][gs*128 .. ge*128) of all TT token rows into this wave's LDS
+// area as scaled fp16 in slot order; E[t] receives each row's exponent.
+template <int TT>
+__device__ __forceinline__ void stage_wave(const GemvArgs& a, _Float16* xs, int gs, int ge, int lane, int (&E)[TT]) {
+  const int n8 = (ge - gs) * (kGroup / 8);
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)t * a.K + (int64_t)gs * kGroup);
+    unsigned m = 0;
+    for (int b = lane; b < n8; b += 64) m = max(m, absmax8(src[b]));
+    E[t] = slice_exponent(wave_max(m));
+    u4_t* dst = reinterpret_cast<u4_t*>(xs + t * a.xs_stride);
+    for (int b = lane; b < n8; b += 64) dst[b] = convert8(src[b], E[t]);
+  }
+}
+
+// Eight bf16 (natural order) -> eight fp16 in slot order, unscaled; exact
+// for every value that passes range8.
+__device__ __forceinline__ u4_t convert8_exact(u4_t v) {
+  const float x0 = __uint_as_float(v.x << 16), x1 = __uint_as_float(v.x & 0xFFFF0000u);
+  const float x2 = __uint_as_float(v.y << 16), x3 = __uint_as_float(v.y & 0xFFFF0000u);
+  const float x4 = __uint_as_float(v.z << 16), x5 = __uint_as_float(v.z & 0xFFFF0000u);
+  const float x6 = __uint_as_float(v.w << 16), x7 = __uint_as_float(v.w & 0xFFFF0000u);
+  return u4_t{as_u32(__builtin_amdgcn_cvt_pkrtz(x0, x4)), as_u32(__builtin_amdgcn_cvt_pkrtz(x1, x5)),
+              as_u32(__builtin_amdgcn_cvt_pkrtz(x2, x6)), as_u32(__builtin_amdgcn_cvt_pkrtz(x3, x7))};
+}
+
+// Running range of the bf16 magnitudes m of eight values: mx = max m, mn =
+// min (m - 1) mod 2^16 (a zero wraps to 0xFFFF and never counts as small).
+__device__ __forceinline__ void range8(u4_t v, us2_t& mx, us2_t& mn) {
+  const us2_t one = {1, 1};
+  const unsigned w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const us2_t m = __builtin_bit_cast(us2_t, w[i] & 0x7FFF7FFFu);
+    mx = __builtin_elementwise_max(mx, m);
+    mn = __builtin_elementwise_min(mn, m - one);
+  }
+}
+
+// A bf16 converts to fp16 exactly, with no scaling, when it is zero or its
+// magnitude lies in [2^-17, 65280] (8 significant bits: fp16 normals from
+// 2^-14, subnormals keep 8 bits down to 2^-17).
+__device__ __forceinline__ bool range_ok(us2_t mx, us2_t mn) {
+  return max((unsigned)mx.x, (unsigned)mx.y) <= 0x477Fu && min((unsigned)mn.x, (unsigned)mn.y) >= 0x36FFu;
+}
+
+// One-pass staging of x[t][gs*128 .. ge*128) by threads tid = 0..nthreads-1:
+// four 16-byte chunks per thread in flight at a time, converted to fp16
+// without scaling.  Returns true when some value of this thread's chunks is
+// not exact that way (the caller then stages again with a power-of-two
+// scale per token row; both give the same products, scaled by 2^E).
+template <int TT>
+__device__ __forceinline__ bool stage_direct(const GemvArgs& a, _Float16* xs, int gs, int ge, int tid,
+                                             int nthreads) {
+  constexpr int kBatch = 4;
+  const int n8 = (ge - gs) * (kGroup / 8);  // chunks per token row
+  const int total = TT * n8;
+  const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)gs * kGroup);
+  u4_t* dst = reinterpret_cast<u4_t*>(xs);
+  const int src_row = a.K / 8, dst_row = a.xs_stride / 8;
+  us2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+  int t = 0, b = tid;  // chunk (t, b) has index t * n8 + b
+  while (b >= n8 && t < TT) {
+    b -= n8;
+    ++t;
+  }
+  for (int base = tid; base < total; base += kBatch * nthreads) {
+    u4_t v[kBatch];
+    int d[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      d[i] = t < TT ? t * dst_row + b : -1;
+      if (t < TT) v[i] = src[t * src_row + b];
+      b += nthreads;
+      while (b >= n8 && t < TT) {
+        b -= n8;
+        ++t;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      if (d[i] >= 0) {
+        range8(v[i], mx, mn);
+        dst[d[i]] = convert8_exact(v[i]);
+      }
+    }
+  }
+  return !range_ok(mx, mn);
+}
+
+// True on every thread of the workgroup when pred holds on any of them
+// (flags[] holds one word per wave; ends with a barrier).
+__device__ __forceinline__ bool workgroup_any(bool pred, unsigned* flags) {
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool w = __ballot(pred) != 0;
+  if ((threadIdx.x & 63) == 0) flags[wave] = w ? 1u : 0u;
+  __syncthreads();
+  unsigned any = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) any |= flags[i];
+  return any != 0;
+}
+
+// ----------------------------------------------------------------- dot ----
+
+// Workgroup-cooperative staging of x[t][gs*128 .. ge*128) for the dot path.
+template <int TT>
+__device__ __forceinline__ void stage_block(const GemvArgs& a, _Float16* xs, unsigned* maxbuf, int gs, int ge,
+                                            int (&E)[TT]) {
+  const int n8 = (ge - gs) * (kGroup / 8);
+  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)t * a.K + (int64_t)gs * kGroup);
+    unsigned m = 0;
+    for (int b = threadIdx.x; b < n8; b += blockDim.x) m = max(m, absmax8(src[b]));
+    m = wave_max(m);
+    if (lane == 0) maxbuf[wave * TT + t] = m;
+  }
+  __syncthreads();
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    unsigned m = 0;
+    for (int w = 0; w < nw; ++w) m = max(m, maxbuf[w * TT + t]);
+    E[t] = slice_exponent(m);
+    const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)t * a.K + (int64_t)gs * kGroup);
+    u4_t* dst = reinterpret_cast<u4_t*>(xs + t * a.xs_stride);
+    for (int b = threadIdx.x; b < n8; b += blockDim.x) dst[b] = convert8(src[b], E[t]);
+  }
+  __syncthreads();
+}
+
+// RW rows per wave, L = 64/RW lanes per row; a lane takes the row's 16-byte
+// chunks li, li+L, li+2L, ...; CPL bounds the chunks per lane per slice.
+template <int TT, int RW>
+__global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  constexpr int L = 64 / RW;
+  constexpr int CPL = 8;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nw = blockDim.x >> 6;
+  const int sub = lane / L, li = lane % L;
+  const int64_t row0 = (int64_t)blockIdx.x * nw * RW;
+  const int64_t orow = row0 + wave * RW + sub;
+  int64_t w = weight_row(a, orow);
+  const bool bad = w < 0;
+  if (bad) w = 0;
+  const u4_t* cp = reinterpret_cast<const u4_t*>(a.packed + w * (int64_t)(a.K >> 1));
+  const uint16_t* sp = a.scales + w * a.G;
+  _Float16* xs = reinterpret_cast<_Float16*>(smem);
+  unsigned* maxbuf = reinterpret_cast<unsigned*>(smem + a.fin_offset);
+
+  float acc[TT], accs[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) acc[t] = accs[t] = 0.0f;
+  int E[TT];
+
+  for (int gs = 0; gs < a.G; gs += a.sk) {
+    const int ge = min(a.G, gs + a.sk);
+    const int c0 = gs * 4, nc = (ge - gs) * 4;  // 16-byte chunks of this slice
+    u4_t q[CPL];
+    unsigned short sq[CPL];
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = li + i * L;
+      if (c < nc) {
+        q[i] = __builtin_nontemporal_load(cp + c0 + c);
+        sq[i] = sp[(c0 + c) >> 2];
+      }
+    }
+    if (gs > 0) __syncthreads();  // every wave is done with the previous slice
+    stage_block<TT>(a, xs, maxbuf, gs, ge, E);
+#pragma unroll
+    for (int i = 0; i < CPL; ++i) {
+      const int c = li + i * L;
+      if (c < nc) {
+        const u4_t lv[4] = {levels8(q[i].x), levels8(q[i].y), levels8(q[i].z), levels8(q[i].w)};
+        const float sc = bf16_to_f32(sq[i]);
+#pragma unroll
+        for (int t = 0; t < TT; ++t) {
+          const u4_t* xv = reinterpret_cast<const u4_t*>(xs + t * a.xs_stride + c * 32);
+          float p = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const u4_t xw = xv[j];
+            p = dot2(lv[j].x, xw.x, p);
+            p = dot2(lv[j].y, xw.y, p);
+            p = dot2(lv[j].z, xw.z, p);
+            p = dot2(lv[j].w, xw.w, p);
+          }
+          accs[t] = fmaf(p, sc, accs[t]);
+        }
+      }
+    }
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      acc[t] += ldexpf(accs[t], -E[t]);
+      accs[t] = 0.0f;
+    }
+  }
+
+  // Butterfly across the L lanes of a row (fixed order).
+#pragma unroll
+  for (int t = 0; t < TT; ++t)
+#pragma unroll
+    for (int off = L / 2; off >= 1; off >>= 1) acc[t] += __shfl_xor(acc[t], off);
+
+  float* fin = reinterpret_cast<float*>(smem);  // reused after the last slice
+  __syncthreads();
+  if (li == 0) {
+    const int r = wave * RW + sub;  // row within the workgroup
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      float v = bad ? __builtin_nanf("") : acc[t];
+      if (orow < a.n_out && a.y) a.y[(int64_t)t * a.n_out + orow] = v;
+      fin[((r >> 4) * TT + t) * 16 + (r & 15)] = v;
+    }
+  }
+  if (a.partial) {
+    __syncthreads();
+    if (wave == 0) workgroup_argmax<TT>(a, fin, row0, nw * RW, lane, blockIdx.x);
+  }
+}
+
+// ---------------------------------------------------------- matrix core ----
+
+// Layout template argument: kLayAny reads either layout (a.tiled decides at
+// run time); kLayTiled is compiled for the tiled layout only.
+constexpr int kLayAny = 0, kLayTiled = 1;
+
+// Weight-code load.  Row-major codes use the default cache policy: the two
+// 64-byte halves of a 128-byte line (groups g and g+1 of a row) then merge
+// into one L2 request in the vector L1, which the nontemporal hint would
+// prevent (measured 20% slower).  A tiled wave load covers whole lines of a
+// 1 KB block that is read once, so it is marked nontemporal (measured 5-9%
+// faster).
+template <int LAY>
+__device__ __forceinline__ u4_t load_codes(const u4_t* p) {
+  if constexpr (LAY == kLayTiled)
+    return __builtin_nontemporal_load(p);
+  else
+    return *p;
+}
+
+// bf16 scale e of eight packed in v (element order = memory order) -> fp32.
+__device__ __forceinline__ float scale_of(u4_t v, int e) {
+  const unsigned w = (e >> 1) == 0 ? v.x : (e >> 1) == 1 ? v.y : (e >> 1) == 2 ? v.z : v.w;
+  return __uint_as_float((e & 1) ? (w & 0xFFFF0000u) : (w << 16));
+}
+
+// Offset, in 16-byte units, of group g's codes from a lane's code pointer.
+template <int LAY>
+__device__ __forceinline__ int code_off(const GemvArgs& a, int g) {
+  return (LAY == kLayTiled || a.tiled) ? (g >> 3) * (kTileChunkBytes / 16) + (g & 7) * (kTileGroupBytes / 16)
+                                       : 4 * g;
+}
+
+// Offset, in 16-byte units, of the eight scales of groups g .. g+7 (g a
+// multiple of 8) from a lane's scale pointer.
+template <int LAY>
+__device__ __forceinline__ int scale_off(const GemvArgs& a, int g) {
+  return (LAY == kLayTiled || a.tiled)
+             ? (g >> 3) * (kTileChunkBytes / 16) + min(kTileChunkGroups, a.G - g) * (kTileGroupBytes / 16)
+             : g >> 3;
+}
+
+constexpr int kRing = 8;  // groups of weight codes in flight per wave
+
+// The K loop of one wave: groups [g_begin, g_end) of RT 16-row tiles.  The
+// range is cut into slices that fit the staged activations; within a slice
+// the wave streams tile 0's groups, then tile 1's, ... with kRing groups of
+// codes in flight and the ring running across tile boundaries.  A lane owns
+// output row r16 of a tile and quarter kq of each 128-column group: one
+// 16-byte load per group feeds four MFMAs (tokens as the A operand, padded to
+// 16 rows; weights as the B operand), whose sum gets the group's scale.
+// SHARED: the slice is staged once for the whole workgroup; otherwise each
+// wave stages its own range (no barrier).  Staging is one pass without
+// scaling when every activation converts to fp16 exactly, else the scaled
+// two-pass staging (stage_block / stage_wave).
+// VS: scales are read eight groups (16 bytes) per load (needs G % 8 == 0,
+// 16-byte aligned scale rows and g_begin % 8 == 0); otherwise one 2-byte
+// load per group.
+template <int TT, int RT, bool VS, bool SHARED, int LAY>
+__device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* const (&cp)[RT],
+                                             const uint16_t* const (&sp)[RT], _Float16* xs, unsigned* maxbuf,
+                                             int g_begin, int g_end, int lane, int trow, int kq,
+                                             float (&acc)[RT][4]) {
+  constexpr int PD = kRing;
+  int E[TT];
+  u4_t q[PD];
+  unsigned short sq[PD];
+  u4_t sv;
+  for (int sb = g_begin; sb < g_end; sb += a.sk) {
+    const int se = min(g_end, sb + a.sk);
+    const int n = se - sb;                  // groups of this slice
+    const int np = (n + PD - 1) / PD * PD;  // padded to whole ring cycles
+    // Ring prologue (tile 0 of the slice), issued before the activations are
+    // staged so that the weight latency overlaps the activation round trip.
+    if constexpr (VS) sv = reinterpret_cast<const u4_t*>(sp[0])[scale_off<LAY>(a, sb)];
+#pragma unroll
+    for (int s = 0; s < PD; ++s) {
+      const int g = sb + min(s, n - 1);
+      if constexpr (!VS) sq[s] = sp[0][g];
+      q[s] = load_codes<LAY>(cp[0] + code_off<LAY>(a, g));
+      __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
+    }
+    if constexpr (SHARED) {
+      if (sb != g_begin) __syncthreads();  // every wave is done with the previous slice
+      const bool bad = stage_direct<TT>(a, xs, sb, se, threadIdx.x, blockDim.x);
+      if (workgroup_any(bad, maxbuf)) {
+        __syncthreads();  // every wave has read the flags before the max buffer is reused
+        stage_block<TT>(a, xs, maxbuf, sb, se, E);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) E[t] = 0;
+      }
+    } else {
+      lds_fence();
+      const bool bad = stage_direct<TT>(a, xs, sb, se, lane, 64);
+      if (__ballot(bad) != 0) {
+        lds_fence();
+        stage_wave<TT>(a, xs, sb, se, lane, E);
+      } else {
+#pragma unroll
+        for (int t = 0; t < TT; ++t) E[t] = 0;
+      }
+      lds_fence();
+    }
+    // Staging waited for its activation loads, issued after the weight loads
+    // in flight; saying so lets the loop wait for exactly one group at a time.
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    const _Float16* xr0 = xs + trow * a.xs_stride + kq * 32;
+#pragma unroll
+    for (int tl = 0; tl < RT; ++tl) {
+      // next tile of the ring (the last tile re-reads its own last group)
+      const u4_t* cpn = cp[tl + 1 < RT ? tl + 1 : tl];
+      const uint16_t* spn = sp[tl + 1 < RT ? tl + 1 : tl];
+      const bool has_next = tl + 1 < RT;
+      float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      for (int fi = 0; fi < np; fi += PD) {
+        const bool last = fi + PD >= np;  // uniform: this cycle prefetches the next tile
+        u4_t svn;
+        if constexpr (VS) {
+          const uint16_t* base = (last && has_next) ? spn : sp[tl];
+          const int gv = last ? (has_next ? sb : sb + fi) : sb + fi + PD;
+          svn = reinterpret_cast<const u4_t*>(base)[scale_off<LAY>(a, gv)];
+          __builtin_amdgcn_sched_barrier(0);
+        }
+#pragma unroll
+        for (int s = 0; s < PD; ++s) {
+          const int gl = fi + s;
+          const _Float16* xr = xr0 + min(gl, n - 1) * kGroup;
+          h8_t xa[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xr + 8 * j);
+          float sc;
+          if constexpr (VS)
+            sc = scale_of(sv, s);
+          else
+            sc = bf16_to_f32(sq[s]);
+          sc = (gl < n) ? sc : 0.0f;
+          f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], __builtin_bit_cast(h8_t, levels8(q[s].x)), d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], __builtin_bit_cast(h8_t, levels8(q[s].y)), d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], __builtin_bit_cast(h8_t, levels8(q[s].z)), d, 0, 0, 0);
+          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], __builtin_bit_cast(h8_t, levels8(q[s].w)), d, 0, 0, 0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) accs[r] = fmaf(d[r], sc, accs[r]);
+          // reload this slot with the group PD positions ahead
+          const int tgt = gl + PD;
+          const bool nxt = tgt >= np;
+          const u4_t* cpl = (nxt && has_next) ? cpn : cp[tl];
+          const int gg = sb + (nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1));
+          if constexpr (!VS) sq[s] = ((nxt && has_next) ? spn : sp[tl])[gg];
+          q[s] = load_codes<LAY>(cpl + code_off<LAY>(a, gg));
+          // keep this slot's reload here: sunk to the end of the loop, the
+          // reloads would make every iteration wait for the whole ring
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        if constexpr (VS) sv = svn;
+      }
+      // fold this tile's slice sum, undoing the activations' power of two
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = kq * 4 + r;
+        int e = E[0];
+#pragma unroll
+        for (int i = 1; i < TT; ++i) e = (t == i) ? E[i] : e;
+        acc[tl][r] += ldexpf(accs[r], -e);
+      }
+    }
+  }
+}
+
+// Code and scale pointers of the RT tiles starting at output row row0 for
+// this lane.  Row-major: the row's codes and scales.  Tiled: the lane's
+// 16 bytes in the first group block of the row's tile, and the row's 16
+// bytes in the first scale block.
+template <int RT, int LAY>
+__device__ __forceinline__ void tile_pointers(const GemvArgs& a, int64_t row0, int r16, int kq,
+                                              const u4_t* (&cp)[RT], const uint16_t* (&sp)[RT]) {
+  const int64_t kh = a.K >> 1;
+#pragma unroll
+  for (int tl = 0; tl < RT; ++tl) {
+    int64_t w = weight_row(a, row0 + tl * 16 + r16);
+    if (w < 0) w = 0;  // read a valid row; the output is masked later
+    if (LAY == kLayTiled || a.tiled) {
+      const uint8_t* tb = a.packed + (w >> 4) * a.tile_bytes;
+      cp[tl] = reinterpret_cast<const u4_t*>(tb) + 4 * (w & 15) + kq;
+      sp[tl] = reinterpret_cast<const uint16_t*>(tb) + 8 * (w & 15);
+    } else {
+      cp[tl] = reinterpret_cast<const u4_t*>(a.packed + w * kh) + kq;
+      sp[tl] = a.scales + w * a.G;
+    }
+  }
+}
+
+// Split workgroup: its a.nw waves own the same RT tiles (rows wg*16*RT ..) and
+// split K into ranges of a.gpw groups; each wave stages its own range; the
+// partial sums are added through LDS in wave order.
+template <int TT, int RT, int LAY>
+__device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int trow = min(r16, TT - 1);  // A rows >= TT only feed D rows that are never read
+  const int64_t row0 = wg * (RT * 16);
+  const u4_t* cp[RT];
+  const uint16_t* sp[RT];
+  tile_pointers<RT, LAY>(a, row0, r16, kq, cp, sp);
+  const int g_begin = wave * a.gpw;
+  const int g_end = (wave < a.nw) ? min(a.G, g_begin + a.gpw) : g_begin;  // uniform
+  _Float16* xs = reinterpret_cast<_Float16*>(smem + wave * a.wave_lds);
+
+  float acc[RT][4];
+#pragma unroll
+  for (int tl = 0; tl < RT; ++tl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[tl][r] = 0.0f;
+  if (g_end > g_begin) {
+    if (LAY == kLayTiled || a.vec_scales)
+      stream_tiles<TT, RT, true, false, LAY>(a, cp, sp, xs, nullptr, g_begin, g_end, lane, trow, kq, acc);
+    else if constexpr (LAY != kLayTiled)
+      stream_tiles<TT, RT, false, false, LAY>(a, cp, sp, xs, nullptr, g_begin, g_end, lane, trow, kq, acc);
+  }
+
+  // Split-K partials of this wave -> its own LDS area: red[(tl*TT + t)*16 + row].
+  lds_fence();
+  float* red = reinterpret_cast<float*>(smem + wave * a.wave_lds);
+  if (wave < a.nw) {
+#pragma unroll
+    for (int tl = 0; tl < RT; ++tl)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int t = kq * 4 + r;
+        if (t < TT) red[(tl * TT + t) * 16 + r16] = acc[tl][r];
+      }
+  }
+  __syncthreads();
+
+  float* fin = reinterpret_cast<float*>(smem + a.fin_offset);
+  constexpr int kOut = RT * TT * 16;
+  for (int o = threadIdx.x; o < kOut; o += blockDim.x) {
+    float v = 0.0f;
+    for (int w = 0; w < a.nw; ++w) v += reinterpret_cast<const float*>(smem + w * a.wave_lds)[o];
+    const int tl = o / (TT * 16), t = (o >> 4) % TT, r = o & 15;
+    const int64_t orow = row0 + tl * 16 + r;
+    if (orow < a.n_out) {
+      if (weight_row(a, orow) < 0) v = __builtin_nanf("");
+      if (a.y) a.y[(int64_t)t * a.n_out + orow] = v;
+    }
+    fin[o] = v;
+  }
+  if (a.partial) {
+    __syncthreads();
+    if (wave == 0) workgroup_argmax<TT>(a, fin, row0, RT * 16, lane, wg);
+  }
+}
+
+// Shared workgroup: each of its waves owns RT tiles of its own over all of K
+// (rows (wg*waves + wave)*16*RT ..); the waves share one staged copy of the
+// activations per K slice, so the fp16 conversion is paid once per
+// 16 * RT * waves rows.  Every output comes straight from one wave.
+template <int TT, int RT, int LAY>
+__device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwv = blockDim.x >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int trow = min(r16, TT - 1);
+  const int64_t row_w = (wg * nwv + wave) * (int64_t)(RT * 16);  // first row of this wave
+  const u4_t* cp[RT];
+  const uint16_t* sp[RT];
+  tile_pointers<RT, LAY>(a, row_w, r16, kq, cp, sp);
+  _Float16* xs = reinterpret_cast<_Float16*>(smem);
+  unsigned* maxbuf = reinterpret_cast<unsigned*>(smem + a.fin_offset);
+
+  float acc[RT][4];
+#pragma unroll
+  for (int tl = 0; tl < RT; ++tl)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[tl][r] = 0.0f;
+  if (LAY == kLayTiled || a.vec_scales)
+    stream_tiles<TT, RT, true, true, LAY>(a, cp, sp, xs, maxbuf, 0, a.G, lane, trow, kq, acc);
+  else if constexpr (LAY != kLayTiled)
+    stream_tiles<TT, RT, false, true, LAY>(a, cp, sp, xs, maxbuf, 0, a.G, lane, trow, kq, acc);
+
+  float bv[TT];
+  int bi[TT];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    bv[t] = __builtin_nanf("");
+    bi[t] = -1;
+  }
+#pragma unroll
+  for (int tl = 0; tl < RT; ++tl) {
+    const int64_t orow = row_w + tl * 16 + r16;
+    const bool in_range = orow < a.n_out;
+    const int64_t wr = in_range ? weight_row(a, orow) : -1;
+    const bool bad = in_range && wr < 0;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = kq * 4 + r;
+      if (t < TT && in_range && a.y) a.y[(int64_t)t * a.n_out + orow] = bad ? __builtin_nanf("") : acc[tl][r];
+    }
+    if (a.partial) {
+      // this lane's candidate for token rows t = 4*kq + r
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        const int r = t & 3;
+        float v = acc[tl][0];
+#pragma unroll
+        for (int i = 1; i < 4; ++i) v = (r == i) ? acc[tl][i] : v;
+        const int id = (kq == (t >> 2) && wr >= 0 && !__builtin_isnan(v)) ? (int)wr : -1;
+        if (better(v, id, bv[t], bi[t])) {
+          bv[t] = v;
+          bi[t] = id;
+        }
+      }
+    }
+  }
+  if (a.partial) {
+    // per t: best (value, id) of this wave's rows, then of the workgroup
+    int2* fin = reinterpret_cast<int2*>(smem + a.fin_offset);
+    __syncthreads();  // staging area and max buffer are free now
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      float v = bv[t];
+      int id = bi[t];
+      wave_argmax(v, id);
+      if (lane == 0) fin[wave * TT + t] = int2{__float_as_int(v), id};
+    }
+    __syncthreads();
+    if (wave == 0 && lane < TT) {
+      float b = __builtin_nanf("");
+      int i = -1;
+      for (int w2 = 0; w2 < nwv; ++w2) {
+        const int2 c = fin[w2 * TT + lane];
+        if (better(__int_as_float(c.x), c.y, b, i)) {
+          b = __int_as_float(c.x);
+          i = c.y;
+        }
+      }
+      a.partial[wg * TT + lane] = int2{__float_as_int(b), i};
+    }
+  }
+}
+
+template <int TT, int RT, bool SHARED, int LAY>
+__device__ __forceinline__ void tile_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
+  if constexpr (SHARED)
+    shared_workgroup<TT, RT, LAY>(a, wg, smem);
+  else
+    split_workgroup<TT, RT, LAY>(a, wg, smem);
+}
+
+template <int TT, int RT, bool SHARED, int LAY>
+__global__ void __launch_bounds__(SHARED && RT == 1 ? 1024 : 512)
+    __attribute__((amdgpu_waves_per_eu(SHARED && RT == 1 ? 4 : 1))) w4a16_tile_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  tile_workgroup<TT, RT, SHARED, LAY>(a, blockIdx.x, smem);
+}
+
+// Grouped launch: workgroup b runs tile b - wg_start of the last problem whose
+// wg_start <= b.
+template <int TT, int RT, bool SHARED, int LAY>
+__global__ void __launch_bounds__(SHARED && RT == 1 ? 1024 : 512)
+    __attribute__((amdgpu_waves_per_eu(SHARED && RT == 1 ? 4 : 1))) w4a16_tile_batch_kernel(const GemvArgs* __restrict__ table,
+                                                                                    int count) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int64_t b = blockIdx.x;
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (table[mid].wg_start <= b)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const GemvArgs a = table[lo];
+  tile_workgroup<TT, RT, SHARED, LAY>(a, b - a.wg_start, smem);
+}
+
+// ------------------------------------------------------------- dispatch ----
+
+template <int TT, int RT, bool SHARED, int LAY>
+hipError_t launch_tiles(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
+  if (p.lds > kLdsCap) {  // above 64 KB of dynamic LDS the kernel has to opt in
+    const void* fn = table ? reinterpret_cast<const void*>(&w4a16_tile_batch_kernel<TT, RT, SHARED, LAY>)
+                           : reinterpret_cast<const void*>(&w4a16_tile_kernel<TT, RT, SHARED, LAY>);
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds);
+    if (e != hipSuccess) return e;
+  }
+  if (table)
+    hipLaunchKernelGGL((w4a16_tile_batch_kernel<TT, RT, SHARED, LAY>), grid, block, p.lds, s, table, count);
+  else
+    hipLaunchKernelGGL((w4a16_tile_kernel<TT, RT, SHARED, LAY>), grid, block, p.lds, s, a);
+  return hipGetLastError();
+}
+
+template <int TT, bool SHARED>
+hipError_t launch_rt(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
+  if (p.tiled) {  // tiled-only kernels are built with one tile per wave
+    if (p.rt != 1) return hipErrorInvalidValue;
+    return launch_tiles<TT, 1, SHARED, kLayTiled>(a, table, count, p, s);
+  }
+  switch (p.rt) {
+    case 1: return launch_tiles<TT, 1, SHARED, kLayAny>(a, table, count, p, s);
+    case 2: return launch_tiles<TT, 2, SHARED, kLayAny>(a, table, count, p, s);
+    case 4: return launch_tiles<TT, 4, SHARED, kLayAny>(a, table, count, p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace
+
+// Launches the kernel of plan p for TT activation rows: one problem (a) or,
+// with table set, a grouped launch over `count` problems.
+template <int TT>
+hipError_t launch_t(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
+  if (p.variant == kSplit) return launch_rt<TT, false>(a, table, count, p, s);
+  if (p.variant == kShared) return launch_rt<TT, true>(a, table, count, p, s);
+  if (table || p.variant != kDot || p.rt != 2) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((w4a16_dot_kernel<TT, 2>), dim3((unsigned)p.grid), dim3((unsigned)p.threads), p.lds, s, a);
+  return hipGetLastError();
+}
+
+
+}  // namespace w4a16

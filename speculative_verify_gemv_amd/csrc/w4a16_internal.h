@@ -63,15 +63,24 @@ struct Plan {
   int threads;   // threads per workgroup
   int64_t grid;  // workgroups
   int lds;       // dynamic LDS bytes
+  bool tiled;    // every problem is in the tiled layout: kernels built for it alone
 };
 
-// Parse "split,rt,waves" or "shared,rt,waves" (rt 1, 2 or 4; waves 1-8).
+// Parse "split,rt,waves" or "shared,rt,waves" (rt 1, 2 or 4; waves 1-8, or
+// 1-16 for shared workgroups of one tile per wave).
 bool parse_tile(const char* text, Tile* t);
 
 // Fill the tiling fields of `a` and return the launch plan.
 Plan plan_mfma(GemvArgs& a, int T, int cus);  // default matrix-core tiling of one launch (cus: CUs of the device)
 Plan plan_dot(GemvArgs& a, int T);
-Plan plan_tile(GemvArgs& a, int T, const Tile& t);
+// tiled_kernel: the launch runs the kernels built for the tiled layout only
+// (every problem tiled; one tile per wave), else the kernels that read
+// either layout.
+Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel);
+// Waves of a shared workgroup of one tile per wave: 16 (one workgroup per CU,
+// up to 160 KB of LDS) when T rows of K activations need more than 64 KB,
+// else 4 at T <= 2 and 8 above (MI355X sweeps of the tiled layout).
+int shared_waves(int T, int64_t K);
 
 
 hipError_t launch(const GemvArgs& a, const Plan& p, int T, hipStream_t s);

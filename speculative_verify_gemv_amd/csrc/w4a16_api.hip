@@ -146,16 +146,20 @@ struct TableHeader {
 };
 static_assert(sizeof(TableHeader) == 64, "table header size");
 
-// Tile of grouped launches, from the MI355X sweeps: all problems tiled ->
-// one tile per wave, shared_waves(T, largest K) waves per workgroup;
-// otherwise at T <= 2 four waves of two 16-row tiles, above that eight waves
-// of four (the larger workgroup shares one staged copy of the bigger
-// activation block among more rows).  W4A16_BATCH_TILE = "split|shared,rt,waves" overrides it (for
-// measurement).
+// Tile of grouped launches, from the MI355X sweeps.  All problems tiled:
+// at T <= 2 shared workgroups of one tile per wave; above, run workgroups of
+// four tiles per wave (eight waves at T <= 4, sixteen above), a problem whose
+// activations do not fit running shared workgroups inside the same kernel.
+// Otherwise (some row-major problem) at T <= 2 four waves of two 16-row
+// tiles, above that eight waves of four.  W4A16_BATCH_TILE =
+// "split|shared|run,rt,waves" overrides it (for measurement).
 w4a16::Tile batch_tile(int T, bool all_tiled, int64_t kmax) {
-  w4a16::Tile t = all_tiled ? w4a16::Tile{w4a16::kShared, 1, w4a16::shared_waves(T, kmax)}
-                  : T <= 2  ? w4a16::Tile{w4a16::kShared, 2, 4}
-                            : w4a16::Tile{w4a16::kShared, 4, 8};
+  w4a16::Tile t;
+  if (all_tiled)
+    t = T <= 2 ? w4a16::Tile{w4a16::kShared, 1, w4a16::shared_waves(T, kmax)}
+               : w4a16::Tile{w4a16::kRun, 4, T <= 4 ? 8 : 16};
+  else
+    t = T <= 2 ? w4a16::Tile{w4a16::kShared, 2, 4} : w4a16::Tile{w4a16::kShared, 4, 8};
   w4a16::Tile o;
   if (w4a16::parse_tile(std::getenv("W4A16_BATCH_TILE"), &o)) t = o;
   return t;
@@ -281,26 +285,38 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
     all_tiled = all_tiled && problems[i].layout == W4A16_LAYOUT_TILED;
     kmax = std::max(kmax, problems[i].K);
   }
-  const w4a16::Tile bt = batch_tile(T, all_tiled, kmax);
-  int64_t grid = 0;
-  int lds = 0, threads = 64;
-  for (int32_t i = 0; i < count; ++i) {
-    const w4a16_problem& q = problems[i];
-    const bool tiled = q.layout == W4A16_LAYOUT_TILED;
-    w4a16::GemvArgs a = gemv_args(q.packed_u4, tiled ? nullptr : q.scales_bf16, tiled, q.x_bf16, q.y_f32, nullptr,
-                                  q.N, q.N, q.K);
-    const w4a16::Plan p = w4a16::plan_tile(a, T, bt, all_tiled);
-    a.wg_start = grid;
-    grid += p.grid;
-    lds = std::max(lds, p.lds);
-    threads = std::max(threads, p.threads);
-    args[i] = a;
+  w4a16::Tile bt = batch_tile(T, all_tiled, kmax);
+  // Every problem runs the same kernel (a run problem whose activations do
+  // not fit runs shared workgroups inside the run kernel); a plan that still
+  // differs between problems falls back to shared workgroups.
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    int64_t grid = 0;
+    int lds = 0, threads = 64, rt = 0;
+    bool uniform = true;
+    for (int32_t i = 0; i < count; ++i) {
+      const w4a16_problem& q = problems[i];
+      const bool tiled = q.layout == W4A16_LAYOUT_TILED;
+      w4a16::GemvArgs a = gemv_args(q.packed_u4, tiled ? nullptr : q.scales_bf16, tiled, q.x_bf16, q.y_f32,
+                                    nullptr, q.N, q.N, q.K);
+      const w4a16::Plan p = w4a16::plan_tile(a, T, bt, all_tiled, true);
+      uniform = uniform && p.variant == bt.shape;
+      rt = p.rt;
+      a.wg_start = grid;
+      grid += p.grid;
+      lds = std::max(lds, p.lds);
+      threads = std::max(threads, p.threads);
+      args[i] = a;
+    }
+    if (!uniform) {
+      bt = w4a16::Tile{w4a16::kShared, 1, std::min(bt.nw, all_tiled ? 16 : 8)};
+      continue;
+    }
+    if (grid > 0x7fffffffLL) return W4A16_ERR_BAD_SHAPE;
+    *hdr = TableHeader{kTableMagic, W4A16_ABI_VERSION, count, T, bt.shape, rt, all_tiled ? 1 : 0, threads, lds, 0,
+                       grid, {0, 0}};
+    return W4A16_OK;
   }
-  if (grid > 0x7fffffffLL) return W4A16_ERR_BAD_SHAPE;
-  *hdr = TableHeader{kTableMagic, W4A16_ABI_VERSION, count, T, bt.shape, all_tiled ? 1 : bt.rt, all_tiled ? 1 : 0,
-                     threads, lds, 0, grid,
-                     {0, 0}};
-  return W4A16_OK;
+  return W4A16_ERR_BAD_SHAPE;  // not reached: shared tiles always plan
 }
 
 w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, hipStream_t stream) {
@@ -312,7 +328,8 @@ w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, h
     return W4A16_ERR_BAD_SHAPE;
   if (w4a16_status s = check_device()) return s;
   w4a16::Plan p{};
-  if (hdr->variant != w4a16::kSplit && hdr->variant != w4a16::kShared) return W4A16_ERR_BAD_SHAPE;
+  if (hdr->variant != w4a16::kSplit && hdr->variant != w4a16::kShared && hdr->variant != w4a16::kRun)
+    return W4A16_ERR_BAD_SHAPE;
   if (hdr->rt != 1 && hdr->rt != 2 && hdr->rt != 4) return W4A16_ERR_BAD_SHAPE;
   if (hdr->threads < 64 || hdr->threads > 1024 || hdr->threads % 64 || hdr->lds < 0 || hdr->lds > 163840)
     return W4A16_ERR_BAD_SHAPE;

@@ -767,6 +767,226 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
   }
 }
 
+// ------------------------------------------------------------- tile runs ----
+
+// The K loop of one wave over a run of whole tiles: v, v + step, ... (< v_end),
+// one tile at a time over all of K (one staged slice), with the ring running
+// from each tile into the next, so a workgroup pays its start (activation
+// staging, ring fill) once for several tiles per wave.  Eight scales per load.
+// The caller issued the first tile's ring (ring_prologue with cp, sp).  Each
+// tile's outputs are written when its last group is done; with a.partial
+// set, the lane keeps its best (value, id) for token rows t = 4 kq + r in
+// bv[r] / bi[r].
+
+// Code and scale pointers of tile v (rows 16v .. 16v+15) for this lane; returns
+// the lane's weight row (-1: past the end or an invalid id).
+template <int LAY>
+__device__ __forceinline__ int tile_ptr(const GemvArgs& a, int64_t v, int r16, int kq, const u4_t*& cp,
+                                        const uint16_t*& sp) {
+  const int64_t w_out = weight_row(a, v * 16 + r16);
+  const int64_t w = w_out < 0 ? 0 : w_out;  // read a valid row; the output is masked
+  if (LAY == kLayTiled || a.tiled) {
+    const uint8_t* tb = a.packed + (w >> 4) * a.tile_bytes;
+    cp = reinterpret_cast<const u4_t*>(tb) + 4 * (w & 15) + kq;
+    sp = reinterpret_cast<const uint16_t*>(tb) + 8 * (w & 15);
+  } else {
+    cp = reinterpret_cast<const u4_t*>(a.packed + w * (int64_t)(a.K >> 1)) + kq;
+    sp = a.scales + w * a.G;
+  }
+  return (int)w_out;
+}
+
+template <int LAY>
+__device__ __forceinline__ void ring_prologue(const GemvArgs& a, const u4_t* cp, const uint16_t* sp,
+                                              u4_t (&q)[kRing], u4_t& sv) {
+  sv = reinterpret_cast<const u4_t*>(sp)[scale_off<LAY>(a, 0)];
+#pragma unroll
+  for (int s = 0; s < kRing; ++s) {
+    q[s] = load_codes<LAY>(cp + code_off<LAY>(a, min(s, a.G - 1)));
+    __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
+  }
+}
+
+template <int TT, int LAY>
+__device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t v_end, int step, const _Float16* xs,
+                                          const int (&E)[TT], int r16, int kq, int trow, const u4_t* cp,
+                                          const uint16_t* sp, u4_t (&q)[kRing], u4_t& sv, float (&bv)[4],
+                                          int (&bi)[4]) {
+  constexpr int PD = kRing;
+  const int n = a.G;
+  const int np = (n + PD - 1) / PD * PD;
+  const _Float16* xr0 = xs + trow * a.xs_stride + kq * 32;
+  int w_cur = (int)weight_row(a, v * 16 + r16);
+  while (v < v_end) {  // uniform
+    const int64_t vn = v + step;
+    const bool has_next = vn < v_end;
+    const u4_t* cpn = cp;
+    const uint16_t* spn = sp;
+    int w_next = -1;
+    if (has_next) w_next = tile_ptr<LAY>(a, vn, r16, kq, cpn, spn);
+    float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int fi = 0; fi < np; fi += PD) {
+      const bool last = fi + PD >= np;  // uniform: this cycle prefetches the next tile
+      const uint16_t* sbase = (last && has_next) ? spn : sp;
+      const int gv = last ? (has_next ? 0 : fi) : fi + PD;
+      const u4_t svn = reinterpret_cast<const u4_t*>(sbase)[scale_off<LAY>(a, gv)];
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int s = 0; s < PD; ++s) {
+        const int gl = fi + s;
+        const _Float16* xr = xr0 + min(gl, n - 1) * kGroup;
+        h8_t xa[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xr + 8 * j);
+        const float sc = (gl < n) ? scale_of(sv, s) : 0.0f;
+        f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], __builtin_bit_cast(h8_t, levels8(q[s].x)), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], __builtin_bit_cast(h8_t, levels8(q[s].y)), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], __builtin_bit_cast(h8_t, levels8(q[s].z)), d, 0, 0, 0);
+        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], __builtin_bit_cast(h8_t, levels8(q[s].w)), d, 0, 0, 0);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accs[r] = fmaf(d[r], sc, accs[r]);
+        // reload this slot with the group PD positions ahead (the next
+        // tile's first groups in the last cycle)
+        const int tgt = gl + PD;
+        const bool nxt = tgt >= np;
+        const u4_t* cpl = (nxt && has_next) ? cpn : cp;
+        const int gg = nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1);
+        q[s] = load_codes<LAY>(cpl + code_off<LAY>(a, gg));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      sv = svn;
+    }
+    // tile v done: this lane's row for t = 4 kq + r
+    const int64_t orow = v * 16 + r16;
+    const bool in_range = orow < a.n_out;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int t = kq * 4 + r;
+      int e = E[0];
+#pragma unroll
+      for (int i = 1; i < TT; ++i) e = (t == i) ? E[i] : e;
+      const float val = ldexpf(accs[r], -e);
+      if (t < TT && in_range && a.y) a.y[(int64_t)t * a.n_out + orow] = w_cur < 0 ? __builtin_nanf("") : val;
+      if (a.partial && t < TT && w_cur >= 0 && !__builtin_isnan(val) && better(val, w_cur, bv[r], bi[r])) {
+        bv[r] = val;
+        bi[r] = w_cur;
+      }
+    }
+    v = vn;
+    cp = cpn;
+    sp = spn;
+    w_cur = w_next;
+  }
+}
+
+// Run workgroup: a.run_tiles tiles per wave.  Workgroup b owns tiles
+// [b*waves*nt, (b+1)*waves*nt); wave i streams tiles i, i + waves, ... of them,
+// so the waves stay on adjacent tiles.  All of K is staged once (the planner
+// guarantees it fits).
+template <int TT, int LAY>
+__device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int nwv = blockDim.x >> 6;
+  const int r16 = lane & 15, kq = lane >> 4;
+  const int trow = min(r16, TT - 1);
+  const int64_t tiles = (a.n_out + 15) / 16;
+  const int64_t span = (int64_t)nwv * a.run_tiles;
+  const int64_t v0 = wg * span + wave, v_end = min(tiles, (wg + 1) * span);
+  _Float16* xs = reinterpret_cast<_Float16*>(smem);
+  unsigned* maxbuf = reinterpret_cast<unsigned*>(smem + a.fin_offset);
+  const u4_t* cp = nullptr;
+  const uint16_t* sp = nullptr;
+  u4_t q[kRing];
+  u4_t sv;
+  if (v0 < v_end) {  // the first tile's ring, issued before the staging
+    tile_ptr<LAY>(a, v0, r16, kq, cp, sp);
+    ring_prologue<LAY>(a, cp, sp, q, sv);
+  }
+  int E[TT];
+  const bool bad = stage_direct<TT>(a, xs, 0, a.G, threadIdx.x, blockDim.x);
+  if (workgroup_any(bad, maxbuf)) {
+    __syncthreads();  // every wave has read the flags before the max buffer is reused
+    stage_block<TT>(a, xs, maxbuf, 0, a.G, E);
+  } else {
+#pragma unroll
+    for (int t = 0; t < TT; ++t) E[t] = 0;
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  float bv[4];
+  int bi[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    bv[r] = __builtin_nanf("");
+    bi[r] = -1;
+  }
+  if (v0 < v_end) run_tiles<TT, LAY>(a, v0, v_end, nwv, xs, E, r16, kq, trow, cp, sp, q, sv, bv, bi);
+  if (a.partial) {
+    // per t: best of the lanes, of the waves, then of the workgroup
+    int2* fin = reinterpret_cast<int2*>(smem + a.fin_offset);
+    __syncthreads();  // the staging area and the flag words are free now
+#pragma unroll
+    for (int t = 0; t < TT; ++t) {
+      // token row t lives in slot t % 4 of the lanes with kq = t / 4
+      float val = bv[0];
+      int id = bi[0];
+#pragma unroll
+      for (int r = 1; r < 4; ++r)
+        if ((t & 3) == r) {
+          val = bv[r];
+          id = bi[r];
+        }
+      if (kq != (t >> 2)) id = -1;
+      wave_argmax(val, id);
+      if (lane == 0) fin[wave * TT + t] = int2{__float_as_int(val), id};
+    }
+    __syncthreads();
+    if (wave == 0 && lane < TT) {
+      float b = __builtin_nanf("");
+      int i = -1;
+      for (int w2 = 0; w2 < nwv; ++w2) {
+        const int2 c = fin[w2 * TT + lane];
+        if (better(__int_as_float(c.x), c.y, b, i)) {
+          b = __int_as_float(c.x);
+          i = c.y;
+        }
+      }
+      a.partial[wg * TT + lane] = int2{__float_as_int(b), i};
+    }
+  }
+}
+
+template <int TT, int LAY>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4))) w4a16_run_kernel(GemvArgs a) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  run_workgroup<TT, LAY>(a, blockIdx.x, smem);
+}
+
+// Grouped launch of run workgroups: workgroup b runs workgroup b - wg_start of
+// the last problem whose wg_start <= b; a problem planned without a run
+// (its activations do not fit the LDS at once) runs a shared workgroup of one
+// tile per wave instead.
+template <int TT, int LAY>
+__global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
+w4a16_run_batch_kernel(const GemvArgs* __restrict__ table, int count) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  const int64_t b = blockIdx.x;
+  int lo = 0, hi = count - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (table[mid].wg_start <= b)
+      lo = mid;
+    else
+      hi = mid - 1;
+  }
+  const GemvArgs a = table[lo];
+  if (a.run_tiles > 0)
+    run_workgroup<TT, LAY>(a, b - a.wg_start, smem);
+  else  // activations too large for one staging: whole-K slices, one tile per wave
+    shared_workgroup<TT, 1, LAY>(a, b - a.wg_start, smem);
+}
+
 template <int TT, int RT, bool SHARED, int LAY>
 __device__ __forceinline__ void tile_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
   if constexpr (SHARED)
@@ -834,18 +1054,35 @@ hipError_t launch_rt(const GemvArgs& a, const GemvArgs* table, int count, const 
   }
 }
 
+template <int TT, int LAY>
+hipError_t launch_run(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
+  const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
+  if (p.lds > kLdsCap) {  // above 64 KB of dynamic LDS the kernel has to opt in
+    const void* fn = table ? reinterpret_cast<const void*>(&w4a16_run_batch_kernel<TT, LAY>)
+                           : reinterpret_cast<const void*>(&w4a16_run_kernel<TT, LAY>);
+    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds);
+    if (e != hipSuccess) return e;
+  }
+  if (table)
+    hipLaunchKernelGGL((w4a16_run_batch_kernel<TT, LAY>), grid, block, p.lds, s, table, count);
+  else
+    hipLaunchKernelGGL((w4a16_run_kernel<TT, LAY>), grid, block, p.lds, s, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 // Launches the kernel of plan p for TT activation rows: one problem (a) or,
 // with table set, a grouped launch over `count` problems.
 template <int TT>
 hipError_t launch_t(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
+  if (p.variant == kRun)
+    return p.tiled ? launch_run<TT, kLayTiled>(a, table, count, p, s) : launch_run<TT, kLayAny>(a, table, count, p, s);
   if (p.variant == kSplit) return launch_rt<TT, false>(a, table, count, p, s);
   if (p.variant == kShared) return launch_rt<TT, true>(a, table, count, p, s);
   if (table || p.variant != kDot || p.rt != 2) return hipErrorInvalidValue;
   hipLaunchKernelGGL((w4a16_dot_kernel<TT, 2>), dim3((unsigned)p.grid), dim3((unsigned)p.threads), p.lds, s, a);
   return hipGetLastError();
 }
-
 
 }  // namespace w4a16

@@ -32,6 +32,8 @@ struct GemvArgs {
                            //    16-byte aligned with G % 8 == 0)
   int32_t tiled;           // 1: packed points at the tiled layout (scales inside it)
   int64_t tile_bytes;      // tiled layout: bytes per 16-row tile
+  int32_t run_tiles;       // run workgroups: tiles per wave
+  int32_t reserved;
 };
 
 // Tiled weight layout (see include/w4a16.h): per 16-row tile, chunks of up
@@ -47,8 +49,10 @@ inline int64_t tiled_tile_bytes(int64_t G) {
 
 // Kernel shapes.  Dot: lanes split each row's K (v_dot2).  Split: matrix-core
 // workgroup whose waves split K over the same 16-row tiles.  Shared:
-// matrix-core workgroup whose waves own different tiles over all of K.
-constexpr int kDot = 1, kSplit = 2, kShared = 3;
+// matrix-core workgroup whose waves own different tiles over all of K.  Run:
+// a shared workgroup whose waves stream several whole tiles each, the load
+// ring running from one tile into the next (all of K staged once).
+constexpr int kDot = 1, kSplit = 2, kShared = 3, kRun = 4;
 
 // Matrix-core tile choice: shape, 16-row tiles per wave, waves per workgroup.
 struct Tile {
@@ -67,7 +71,8 @@ struct Plan {
 };
 
 // Parse "split,rt,waves" or "shared,rt,waves" (rt 1, 2 or 4; waves 1-8, or
-// 1-16 for shared workgroups of one tile per wave).
+// 1-16 for shared workgroups of one tile per wave), or "run,tiles,waves"
+// (tiles per wave 1-16, waves 1-16).
 bool parse_tile(const char* text, Tile* t);
 
 // Fill the tiling fields of `a` and return the launch plan.
@@ -76,7 +81,9 @@ Plan plan_dot(GemvArgs& a, int T);
 // tiled_kernel: the launch runs the kernels built for the tiled layout only
 // (every problem tiled; one tile per wave), else the kernels that read
 // either layout.
-Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel);
+// batch: planning one problem of a grouped launch (a run tile whose
+// activations do not fit stays a run-kernel problem with run_tiles = 0).
+Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel, bool batch);
 // Waves of a shared workgroup of one tile per wave: 16 (one workgroup per CU,
 // up to 160 KB of LDS) when T rows of K activations need more than 64 KB,
 // else 4 at T <= 2 and 8 above (MI355X sweeps of the tiled layout).

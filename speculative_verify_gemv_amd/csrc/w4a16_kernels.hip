@@ -114,6 +114,11 @@ bool parse_tile(const char* text, Tile* t) {
   char kind[16] = {0};
   int rt = 0, nw = 0;
   if (!text || std::sscanf(text, "%15[a-z],%d,%d", kind, &rt, &nw) != 3) return false;
+  if (std::strcmp(kind, "run") == 0) {
+    if (rt < 1 || rt > 16 || nw < 1 || nw > 16) return false;
+    *t = Tile{kRun, rt, nw};
+    return true;
+  }
   const bool split = std::strcmp(kind, "split") == 0, shared = std::strcmp(kind, "shared") == 0;
   if (!(split || shared) || !(rt == 1 || rt == 2 || rt == 4) || nw < 1) return false;
   if (nw > (shared && rt == 1 ? 16 : 8)) return false;
@@ -182,12 +187,46 @@ static void plan_shared(GemvArgs& a, int T, int rt, int nwv, Plan* p) {
   p->grid = cdiv(a.n_out, 16LL * nwv * rt);
 }
 
-Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel) {
+// Run tiling: nwv waves of nt whole tiles each; all of K staged once (as a
+// shared workgroup with sk = G), so it needs the activations to fit (up to
+// 8 waves: 64 KB, more: the CU's 160 KB) and eight scales per load.
+// Returns false otherwise.
+static bool plan_run(GemvArgs& a, int T, int nt, int nwv, Plan* p) {
+  if (!a.vec_scales) return false;
+  const int small = nwv * T * 8;
+  const int cap = nwv > 8 ? kCuLds : kLdsCap;
+  const int64_t xs_bytes = ((int64_t)T * (a.K + 8) * 2 + 15) & ~15LL;
+  if (xs_bytes + small > cap) return false;
+  a.nw = nwv;
+  a.gpw = a.G;
+  a.sk = a.G;
+  a.xs_stride = a.K + 8;
+  a.wave_lds = 0;
+  a.run_tiles = nt;
+  a.fin_offset = (int32_t)xs_bytes;
+  p->lds = (int)xs_bytes + small;
+  p->threads = nwv * 64;
+  p->grid = cdiv(cdiv(a.n_out, 16), (int64_t)nwv * nt);
+  return true;
+}
+
+Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel, bool batch) {
   Plan p{};
   p.variant = t.shape;
   p.rt = tiled_kernel ? 1 : t.rt;  // the tiled-layout kernels stream one tile per wave
   p.tiled = tiled_kernel;
   a.vec_scales = (a.tiled || (a.G % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15) == 0)) ? 1 : 0;
+  if (t.shape == kRun) {
+    p.rt = 1;
+    if (plan_run(a, T, t.rt, t.nw, &p)) return p;
+    // The activations do not fit: a shared workgroup of one tile per wave
+    // stages K in slices.  A grouped launch keeps the run kernel (which
+    // runs such problems this way, run_tiles = 0); a single launch switches.
+    a.run_tiles = 0;
+    plan_shared(a, T, 1, t.nw, &p);
+    p.variant = batch ? kRun : kShared;
+    return p;
+  }
   if (t.shape == kShared)
     plan_shared(a, T, p.rt, t.nw, &p);
   else
@@ -213,7 +252,7 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
   const int64_t tiles = cdiv(a.n_out, 16);
   Tile t;
   if (tiles >= 4096 && a.tiled)
-    t = Tile{kShared, 1, shared_waves(T, a.K)};
+    t = T <= 2 ? Tile{kShared, 1, shared_waves(T, a.K)} : Tile{kRun, 4, 16};
   else if (tiles >= 8192)
     t = Tile{kShared, 4, 8};
   else if (tiles >= 4096)
@@ -224,7 +263,7 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
     t = Tile{kSplit, 1, (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(12LL * std::max(cus, 1), tiles)))};
   Tile o;
   if (parse_tile(std::getenv("W4A16_TILE"), &o)) t = o;
-  return plan_tile(a, T, t, a.tiled != 0);
+  return plan_tile(a, T, t, a.tiled != 0, false);
 }
 
 // Tiling of the dot variant: 2 rows per wave (32 lanes per row), 8 waves,

@@ -43,7 +43,7 @@ def check_outputs(probs, host_side, what):
         assert_parity(host(y)[:, rows], y_ref, a_ref, f"{what} N={N} K={p.shape[1] * 2}")
 
 
-@pytest.mark.parametrize("tile", [None, "shared,1,4", "split,1,4", "split,4,2", "split,2,8", "shared,1,16"])
+@pytest.mark.parametrize("tile", [None, "shared,1,4", "split,1,4", "split,4,2", "split,2,8", "shared,1,16", "run,2,8", "run,3,16"])
 @pytest.mark.parametrize("T", [1, 4, 8])
 def test_batch_matches_oracle(w4, tile, T, monkeypatch):
     if tile is not None:

@@ -17,7 +17,8 @@ from gpu_util import assert_parity, dev, host, say, sample_rows, weight_dev
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
 
-TILES = ["split,1,1", "split,1,8", "split,2,3", "split,4,2", "shared,1,1", "shared,2,3", "shared,4,4", "shared,1,16"]
+TILES = ["split,1,1", "split,1,8", "split,2,3", "split,4,2", "shared,1,1", "shared,2,3", "shared,4,4", "shared,1,16",
+         "run,3,4", "run,2,16"]
 
 # (N, K, T): single group; odd rows; several slices at T = 8 (G = 136); a
 # ragged tile tail; G = 18 (one scale per load); a tall K = 5120 case.

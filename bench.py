@@ -50,7 +50,7 @@ def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--T", type=int, default=4)
     ap.add_argument("--layers", type=int, default=synth.LAYERS)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -194,10 +194,10 @@ def main():
         for tiled, table in ((True, per_t), (False, per_t_rm)):
             for Tp in (1, 4, 8):
                 b, _ = (batch, probs) if (Tp == T and tiled) else make_pass(Tp, tiled)
-                for _ in range(3):
+                for _ in range(20):  # ~40 ms of work: past the clock ramp after the host-side set-up
                     b.run(stream)
                 e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                reps = 10
+                reps = 20
                 e0.record(stream)
                 for _ in range(reps):
                     b.run(stream)
@@ -214,7 +214,7 @@ def main():
     # ---- the same step as 257 separate launches, replayed from a HIP graph ----
     graph_pass = None
     if not args.no_graph:
-        graph_pass = graph_step(torch, w4a16, probs, head, reps=5)
+        graph_pass = graph_step(torch, w4a16, probs, head, reps=10)
         g = metrics.gbps(step_bytes, graph_pass["ms_per_step"])
         graph_pass["weight_GBps"] = round(g, 1)
         log(f"257-launch graph step: {graph_pass['ms_per_step']:.4f} ms, {g:.0f} GB/s")
@@ -285,7 +285,8 @@ def graph_step(torch, w4a16, probs, head, reps):
         for tw, _, x, y in probs:
             w4a16.matmul_tiled(tw, x, out=y, stream=s)
         head(s)
-    g.replay()
+    for _ in range(5):
+        g.replay()
     torch.cuda.synchronize()
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     e0.record()

@@ -148,8 +148,9 @@ static_assert(sizeof(TableHeader) == 64, "table header size");
 
 // Tile of grouped launches, from the MI355X sweeps.  All problems tiled:
 // at T <= 2 shared workgroups of one tile per wave; above, run workgroups of
-// four tiles per wave (eight waves at T <= 4, sixteen above), a problem whose
-// activations do not fit running shared workgroups inside the same kernel.
+// four tiles per wave, eight waves at T <= 4 and sixteen above, a problem
+// whose activations do not fit running shared workgroups inside the same
+// kernel.
 // Otherwise (some row-major problem) at T <= 2 four waves of two 16-row
 // tiles, above that eight waves of four.  W4A16_BATCH_TILE =
 // "split|shared|run,rt,waves" overrides it (for measurement).

@@ -70,10 +70,34 @@ typedef unsigned short us2_t __attribute__((ext_vector_type(2)));
 constexpr int kGroup = 128;
 constexpr int kLdsCap = 65536;  // dynamic LDS per workgroup (several workgroups per CU)
 constexpr int kCuLds = 163840;  // LDS of a CU (one workgroup per CU)
+constexpr int kRing = 8;        // groups of weight codes in flight per wave
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt = 0 only.
 constexpr int kWaitVmcnt0 = 0x0F70;
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
+
+// Reads through a pointer known to address global memory.  Pointers taken
+// from a grouped launch's device table are generic to the compiler, which
+// then emits flat loads; those also count against the LDS wait counter, so
+// each wait for the staged activations would wait for the weight loads in
+// flight too.
+template <typename V>
+__device__ __forceinline__ V ld_global(const V* p) {
+  return *(const __attribute__((address_space(1))) V*)p;
+}
+template <typename V>
+__device__ __forceinline__ V ld_global_nt(const V* p) {
+  return __builtin_nontemporal_load((const __attribute__((address_space(1))) V*)p);
+}
+template <typename V>
+__device__ __forceinline__ void st_global(V* p, V v) {
+  *(__attribute__((address_space(1))) V*)p = v;
+}
+// An argmax partial (value bits, id) as one 8-byte store.
+__device__ __forceinline__ void st_partial(int2* p, float v, int id) {
+  st_global(reinterpret_cast<unsigned long long*>(p),
+            (unsigned long long)__float_as_uint(v) | ((unsigned long long)(unsigned)id << 32));
+}
 
 template <typename V>
 __device__ __forceinline__ unsigned as_u32(V h) {
@@ -168,7 +192,7 @@ __device__ __forceinline__ void wave_argmax(float& v, int& id) {
 // Vocabulary id of output row o, or -1 if o is past the end or its id is out of range.
 __device__ __forceinline__ int64_t weight_row(const GemvArgs& a, int64_t o) {
   if (o >= a.n_out) return -1;
-  const int64_t w = a.row_ids ? (int64_t)a.row_ids[o] : o;
+  const int64_t w = a.row_ids ? (int64_t)ld_global(a.row_ids + o) : o;
   return (w < 0 || w >= a.n_rows) ? -1 : w;
 }
 
@@ -191,11 +215,24 @@ __device__ __forceinline__ void workgroup_argmax(const GemvArgs& a, const float*
       }
     }
     wave_argmax(bv, bi);
-    if (lane == 0) a.partial[wg * TT + t] = int2{__float_as_int(bv), bi};
+    if (lane == 0) st_partial(a.partial + wg * TT + t, bv, bi);
   }
 }
 
 // ---------------------------------------------------------- staging ----
+//
+// A staged slice holds token row t at xs + t * xs_stride as a run of 16-byte
+// chunks (eight fp16 in slot order, 16 chunks per 128-column group).  Chunk c
+// of row t sits at position c ^ g(t) of the row, g(t) = bits 0-1 of t plus
+// bit 2 of t moved to bit 3.  A lane (row r, quarter kq) of the matrix-core
+// loop reads chunk 4 kq + j of its row; with g, the 32 lanes of quarters
+// 0-1 (or 2-3) over eight token rows read 16 different chunk positions, i.e.
+// all 64 LDS banks once, so the rows need no padding: T rows of K
+// activations take exactly T * K * 2 bytes (at T = 8, K = 5120 two workgroups
+// fit in a CU's 160 KB).  The XOR stays inside the aligned 16 chunks of one
+// group.
+
+__device__ __forceinline__ int swz(int t, int c) { return c ^ ((t & 3) | ((t & 4) << 1)); }
 
 // Stages x[t][gs*128 .. ge*128) of all TT token rows into this wave's LDS
 // area as scaled fp16 in slot order; E[t] receives each row's exponent.
@@ -206,10 +243,26 @@ __device__ __forceinline__ void stage_wave(const GemvArgs& a, _Float16* xs, int 
   for (int t = 0; t < TT; ++t) {
     const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)t * a.K + (int64_t)gs * kGroup);
     unsigned m = 0;
-    for (int b = lane; b < n8; b += 64) m = max(m, absmax8(src[b]));
+    for (int b = lane; b < n8; b += 64) m = max(m, absmax8(ld_global(src + b)));
     E[t] = slice_exponent(wave_max(m));
     u4_t* dst = reinterpret_cast<u4_t*>(xs + t * a.xs_stride);
-    for (int b = lane; b < n8; b += 64) dst[b] = convert8(src[b], E[t]);
+    for (int b = lane; b < n8; b += 64) dst[swz(t, b)] = convert8(ld_global(src + b), E[t]);
+  }
+}
+
+// Zeroes groups [n, next multiple of 8) of every staged row: the load ring
+// runs whole cycles of eight groups, and its padded slots read these (their
+// scale is zero, so zero activations keep their products finite and zero).
+template <int TT>
+__device__ __forceinline__ void zero_pad(const GemvArgs& a, _Float16* xs, int n, int tid, int nthreads) {
+  const int b0 = n * (kGroup / 8), b1 = ((n + kRing - 1) / kRing) * kRing * (kGroup / 8);
+  const int per_row = b1 - b0;
+  if (per_row == 0) return;
+  u4_t* dst = reinterpret_cast<u4_t*>(xs);
+  const int dst_row = a.xs_stride / 8;
+  for (int i = tid; i < TT * per_row; i += nthreads) {
+    const int t = i / per_row, b = b0 + i % per_row;
+    dst[t * dst_row + swz(t, b)] = u4_t{0u, 0u, 0u, 0u};
   }
 }
 
@@ -248,10 +301,13 @@ __device__ __forceinline__ bool range_ok(us2_t mx, us2_t mn) {
 // four 16-byte chunks per thread in flight at a time, converted to fp16
 // without scaling.  Returns true when some value of this thread's chunks is
 // not exact that way (the caller then stages again with a power-of-two
-// scale per token row; both give the same products, scaled by 2^E).
+// scale per token row; both give the same products, scaled by 2^E).  A chunk
+// whose position is in [hold_from, hold_from + 4) is not stored but returned
+// in held / held_at (a thread meets at most one: they are four of one
+// group's 16 chunks and nthreads >= 64).
 template <int TT>
-__device__ __forceinline__ bool stage_direct(const GemvArgs& a, _Float16* xs, int gs, int ge, int tid,
-                                             int nthreads) {
+__device__ __forceinline__ bool stage_direct(const GemvArgs& a, _Float16* xs, int gs, int ge, int tid, int nthreads,
+                                             int hold_from, u4_t& held, int& held_at) {
   constexpr int kBatch = 4;
   const int n8 = (ge - gs) * (kGroup / 8);  // chunks per token row
   const int total = TT * n8;
@@ -269,8 +325,8 @@ __device__ __forceinline__ bool stage_direct(const GemvArgs& a, _Float16* xs, in
     int d[kBatch];
 #pragma unroll
     for (int i = 0; i < kBatch; ++i) {
-      d[i] = t < TT ? t * dst_row + b : -1;
-      if (t < TT) v[i] = src[t * src_row + b];
+      d[i] = t < TT ? t * dst_row + swz(t, b) : -1;
+      if (t < TT) v[i] = ld_global(src + t * src_row + b);
       b += nthreads;
       while (b >= n8 && t < TT) {
         b -= n8;
@@ -281,28 +337,25 @@ __device__ __forceinline__ bool stage_direct(const GemvArgs& a, _Float16* xs, in
     for (int i = 0; i < kBatch; ++i) {
       if (d[i] >= 0) {
         range8(v[i], mx, mn);
-        dst[d[i]] = convert8_exact(v[i]);
+        const u4_t c = convert8_exact(v[i]);
+        if (d[i] >= hold_from) {
+          held = c;
+          held_at = d[i];
+        } else {
+          dst[d[i]] = c;
+        }
       }
     }
   }
   return !range_ok(mx, mn);
 }
 
-// True on every thread of the workgroup when pred holds on any of them
-// (flags[] holds one word per wave; ends with a barrier).
-__device__ __forceinline__ bool workgroup_any(bool pred, unsigned* flags) {
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const bool w = __ballot(pred) != 0;
-  if ((threadIdx.x & 63) == 0) flags[wave] = w ? 1u : 0u;
-  __syncthreads();
-  unsigned any = 0;
-  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) any |= flags[i];
-  return any != 0;
-}
-
 // ----------------------------------------------------------------- dot ----
 
-// Workgroup-cooperative staging of x[t][gs*128 .. ge*128) for the dot path.
+// Workgroup-cooperative staging of x[t][gs*128 .. ge*128) with a power-of-two
+// scale per token row (E[t]).  maxbuf (waves * TT words) may lie inside the
+// staged block: it is read into registers before any chunk is stored.  Ends
+// with a barrier.
 template <int TT>
 __device__ __forceinline__ void stage_block(const GemvArgs& a, _Float16* xs, unsigned* maxbuf, int gs, int ge,
                                             int (&E)[TT]) {
@@ -313,7 +366,7 @@ __device__ __forceinline__ void stage_block(const GemvArgs& a, _Float16* xs, uns
   for (int t = 0; t < TT; ++t) {
     const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)t * a.K + (int64_t)gs * kGroup);
     unsigned m = 0;
-    for (int b = threadIdx.x; b < n8; b += blockDim.x) m = max(m, absmax8(src[b]));
+    for (int b = threadIdx.x; b < n8; b += blockDim.x) m = max(m, absmax8(ld_global(src + b)));
     m = wave_max(m);
     if (lane == 0) maxbuf[wave * TT + t] = m;
   }
@@ -323,10 +376,49 @@ __device__ __forceinline__ void stage_block(const GemvArgs& a, _Float16* xs, uns
     unsigned m = 0;
     for (int w = 0; w < nw; ++w) m = max(m, maxbuf[w * TT + t]);
     E[t] = slice_exponent(m);
+  }
+  __syncthreads();  // every wave has read the maxima before the block is written
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
     const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)t * a.K + (int64_t)gs * kGroup);
     u4_t* dst = reinterpret_cast<u4_t*>(xs + t * a.xs_stride);
-    for (int b = threadIdx.x; b < n8; b += blockDim.x) dst[b] = convert8(src[b], E[t]);
+    for (int b = threadIdx.x; b < n8; b += blockDim.x) dst[swz(t, b)] = convert8(ld_global(src + b), E[t]);
   }
+  __syncthreads();
+}
+
+// Stages x[t][gs*128 .. ge*128) of all TT token rows once for the whole
+// workgroup, plus the zeroed ring padding (zero_pad).  One pass without
+// scaling when every value of the slice converts exactly, else the scaled
+// two-pass staging.  The workgroup-wide decision needs one word per wave; the
+// words are borrowed from the last four chunks of the last row, whose values
+// the threads that own them hold back until the decision is made, so the
+// staged block needs no LDS beyond its own T * xs_stride halves.  Ends with
+// a barrier.
+template <int TT>
+__device__ __forceinline__ void stage_shared(const GemvArgs& a, _Float16* xs, int gs, int ge, int (&E)[TT]) {
+  const int n8 = (ge - gs) * (kGroup / 8);
+  const int flag_at = (TT - 1) * (a.xs_stride / 8) + n8 - 4;  // chunk position of the flag words
+  u4_t held = {0u, 0u, 0u, 0u};
+  int held_at = -1;
+  const bool bad = stage_direct<TT>(a, xs, gs, ge, threadIdx.x, blockDim.x, flag_at, held, held_at);
+  u4_t* dst = reinterpret_cast<u4_t*>(xs);
+  unsigned* flags = reinterpret_cast<unsigned*>(dst + flag_at);  // 16 words: up to 16 waves
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bool wave_bad = __ballot(bad) != 0;
+  if ((threadIdx.x & 63) == 0) flags[wave] = wave_bad ? 1u : 0u;
+  __syncthreads();
+  unsigned any = 0;
+  for (int i = 0; i < (int)(blockDim.x >> 6); ++i) any |= flags[i];
+  __syncthreads();  // every wave has read the flags before they are overwritten
+  if (any == 0) {
+    if (held_at >= 0) dst[held_at] = held;
+#pragma unroll
+    for (int t = 0; t < TT; ++t) E[t] = 0;
+  } else {
+    stage_block<TT>(a, xs, reinterpret_cast<unsigned*>(xs), gs, ge, E);
+  }
+  zero_pad<TT>(a, xs, ge - gs, threadIdx.x, blockDim.x);
   __syncthreads();
 }
 
@@ -379,11 +471,11 @@ __global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
         const float sc = bf16_to_f32(sq[i]);
 #pragma unroll
         for (int t = 0; t < TT; ++t) {
-          const u4_t* xv = reinterpret_cast<const u4_t*>(xs + t * a.xs_stride + c * 32);
+          const u4_t* xv = reinterpret_cast<const u4_t*>(xs + t * a.xs_stride);
           float p = 0.0f;
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            const u4_t xw = xv[j];
+            const u4_t xw = xv[swz(t, c * 4 + j)];
             p = dot2(lv[j].x, xw.x, p);
             p = dot2(lv[j].y, xw.y, p);
             p = dot2(lv[j].z, xw.z, p);
@@ -413,7 +505,7 @@ __global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       float v = bad ? __builtin_nanf("") : acc[t];
-      if (orow < a.n_out && a.y) a.y[(int64_t)t * a.n_out + orow] = v;
+      if (orow < a.n_out && a.y) st_global(a.y + (int64_t)t * a.n_out + orow, v);
       fin[((r >> 4) * TT + t) * 16 + (r & 15)] = v;
     }
   }
@@ -438,9 +530,9 @@ constexpr int kLayAny = 0, kLayTiled = 1;
 template <int LAY>
 __device__ __forceinline__ u4_t load_codes(const u4_t* p) {
   if constexpr (LAY == kLayTiled)
-    return __builtin_nontemporal_load(p);
+    return ld_global_nt(p);
   else
-    return *p;
+    return ld_global(p);
 }
 
 // bf16 scale e of eight packed in v (element order = memory order) -> fp32.
@@ -465,7 +557,6 @@ __device__ __forceinline__ int scale_off(const GemvArgs& a, int g) {
              : g >> 3;
 }
 
-constexpr int kRing = 8;  // groups of weight codes in flight per wave
 
 // The K loop of one wave: groups [g_begin, g_end) of RT 16-row tiles.  The
 // range is cut into slices that fit the staged activations; within a slice
@@ -474,18 +565,17 @@ constexpr int kRing = 8;  // groups of weight codes in flight per wave
 // output row r16 of a tile and quarter kq of each 128-column group: one
 // 16-byte load per group feeds four MFMAs (tokens as the A operand, padded to
 // 16 rows; weights as the B operand), whose sum gets the group's scale.
-// SHARED: the slice is staged once for the whole workgroup; otherwise each
-// wave stages its own range (no barrier).  Staging is one pass without
-// scaling when every activation converts to fp16 exactly, else the scaled
-// two-pass staging (stage_block / stage_wave).
+// SHARED: the slice is staged once for the whole workgroup (stage_shared);
+// otherwise each wave stages its own range (no barrier).  Staging is one pass
+// without scaling when every activation converts to fp16 exactly, else the
+// scaled two-pass staging (stage_block / stage_wave).
 // VS: scales are read eight groups (16 bytes) per load (needs G % 8 == 0,
 // 16-byte aligned scale rows and g_begin % 8 == 0); otherwise one 2-byte
 // load per group.
 template <int TT, int RT, bool VS, bool SHARED, int LAY>
 __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* const (&cp)[RT],
-                                             const uint16_t* const (&sp)[RT], _Float16* xs, unsigned* maxbuf,
-                                             int g_begin, int g_end, int lane, int trow, int kq,
-                                             float (&acc)[RT][4]) {
+                                             const uint16_t* const (&sp)[RT], _Float16* xs, int g_begin, int g_end,
+                                             int lane, int trow, int kq, float (&acc)[RT][4]) {
   constexpr int PD = kRing;
   int E[TT];
   u4_t q[PD];
@@ -497,27 +587,22 @@ __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* cons
     const int np = (n + PD - 1) / PD * PD;  // padded to whole ring cycles
     // Ring prologue (tile 0 of the slice), issued before the activations are
     // staged so that the weight latency overlaps the activation round trip.
-    if constexpr (VS) sv = reinterpret_cast<const u4_t*>(sp[0])[scale_off<LAY>(a, sb)];
+    if constexpr (VS) sv = ld_global(reinterpret_cast<const u4_t*>(sp[0]) + scale_off<LAY>(a, sb));
 #pragma unroll
     for (int s = 0; s < PD; ++s) {
       const int g = sb + min(s, n - 1);
-      if constexpr (!VS) sq[s] = sp[0][g];
+      if constexpr (!VS) sq[s] = ld_global(sp[0] + g);
       q[s] = load_codes<LAY>(cp[0] + code_off<LAY>(a, g));
       __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
     }
     if constexpr (SHARED) {
       if (sb != g_begin) __syncthreads();  // every wave is done with the previous slice
-      const bool bad = stage_direct<TT>(a, xs, sb, se, threadIdx.x, blockDim.x);
-      if (workgroup_any(bad, maxbuf)) {
-        __syncthreads();  // every wave has read the flags before the max buffer is reused
-        stage_block<TT>(a, xs, maxbuf, sb, se, E);
-      } else {
-#pragma unroll
-        for (int t = 0; t < TT; ++t) E[t] = 0;
-      }
+      stage_shared<TT>(a, xs, sb, se, E);
     } else {
       lds_fence();
-      const bool bad = stage_direct<TT>(a, xs, sb, se, lane, 64);
+      u4_t held;
+      int held_at = -1;
+      const bool bad = stage_direct<TT>(a, xs, sb, se, lane, 64, 0x7fffffff, held, held_at);
       if (__ballot(bad) != 0) {
         lds_fence();
         stage_wave<TT>(a, xs, sb, se, lane, E);
@@ -525,12 +610,17 @@ __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* cons
 #pragma unroll
         for (int t = 0; t < TT; ++t) E[t] = 0;
       }
+      zero_pad<TT>(a, xs, n, lane, 64);
       lds_fence();
     }
     // Staging waited for its activation loads, issued after the weight loads
     // in flight; saying so lets the loop wait for exactly one group at a time.
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    const _Float16* xr0 = xs + trow * a.xs_stride + kq * 32;
+    // this lane's four 16-byte activation chunks of group 0 (row trow, chunks
+    // 4 kq .. 4 kq + 3 of the group, swizzled)
+    const _Float16* xb[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) xb[j] = xs + trow * a.xs_stride + swz(trow, kq * 4 + j) * 8;
 #pragma unroll
     for (int tl = 0; tl < RT; ++tl) {
       // next tile of the ring (the last tile re-reads its own last group)
@@ -544,16 +634,15 @@ __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* cons
         if constexpr (VS) {
           const uint16_t* base = (last && has_next) ? spn : sp[tl];
           const int gv = last ? (has_next ? sb : sb + fi) : sb + fi + PD;
-          svn = reinterpret_cast<const u4_t*>(base)[scale_off<LAY>(a, gv)];
+          svn = ld_global(reinterpret_cast<const u4_t*>(base) + scale_off<LAY>(a, gv));
           __builtin_amdgcn_sched_barrier(0);
         }
 #pragma unroll
         for (int s = 0; s < PD; ++s) {
-          const int gl = fi + s;
-          const _Float16* xr = xr0 + min(gl, n - 1) * kGroup;
+          const int gl = fi + s;  // groups past n read the zeroed padding
           h8_t xa[4];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xr + 8 * j);
+          for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xb[j] + gl * kGroup);
           float sc;
           if constexpr (VS)
             sc = scale_of(sv, s);
@@ -572,7 +661,7 @@ __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* cons
           const bool nxt = tgt >= np;
           const u4_t* cpl = (nxt && has_next) ? cpn : cp[tl];
           const int gg = sb + (nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1));
-          if constexpr (!VS) sq[s] = ((nxt && has_next) ? spn : sp[tl])[gg];
+          if constexpr (!VS) sq[s] = ld_global(((nxt && has_next) ? spn : sp[tl]) + gg);
           q[s] = load_codes<LAY>(cpl + code_off<LAY>(a, gg));
           // keep this slot's reload here: sunk to the end of the loop, the
           // reloads would make every iteration wait for the whole ring
@@ -640,9 +729,9 @@ __device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, u
     for (int r = 0; r < 4; ++r) acc[tl][r] = 0.0f;
   if (g_end > g_begin) {
     if (LAY == kLayTiled || a.vec_scales)
-      stream_tiles<TT, RT, true, false, LAY>(a, cp, sp, xs, nullptr, g_begin, g_end, lane, trow, kq, acc);
+      stream_tiles<TT, RT, true, false, LAY>(a, cp, sp, xs, g_begin, g_end, lane, trow, kq, acc);
     else if constexpr (LAY != kLayTiled)
-      stream_tiles<TT, RT, false, false, LAY>(a, cp, sp, xs, nullptr, g_begin, g_end, lane, trow, kq, acc);
+      stream_tiles<TT, RT, false, false, LAY>(a, cp, sp, xs, g_begin, g_end, lane, trow, kq, acc);
   }
 
   // Split-K partials of this wave -> its own LDS area: red[(tl*TT + t)*16 + row].
@@ -668,7 +757,7 @@ __device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, u
     const int64_t orow = row0 + tl * 16 + r;
     if (orow < a.n_out) {
       if (weight_row(a, orow) < 0) v = __builtin_nanf("");
-      if (a.y) a.y[(int64_t)t * a.n_out + orow] = v;
+      if (a.y) st_global(a.y + (int64_t)t * a.n_out + orow, v);
     }
     fin[o] = v;
   }
@@ -694,7 +783,6 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
   const uint16_t* sp[RT];
   tile_pointers<RT, LAY>(a, row_w, r16, kq, cp, sp);
   _Float16* xs = reinterpret_cast<_Float16*>(smem);
-  unsigned* maxbuf = reinterpret_cast<unsigned*>(smem + a.fin_offset);
 
   float acc[RT][4];
 #pragma unroll
@@ -702,9 +790,9 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[tl][r] = 0.0f;
   if (LAY == kLayTiled || a.vec_scales)
-    stream_tiles<TT, RT, true, true, LAY>(a, cp, sp, xs, maxbuf, 0, a.G, lane, trow, kq, acc);
+    stream_tiles<TT, RT, true, true, LAY>(a, cp, sp, xs, 0, a.G, lane, trow, kq, acc);
   else if constexpr (LAY != kLayTiled)
-    stream_tiles<TT, RT, false, true, LAY>(a, cp, sp, xs, maxbuf, 0, a.G, lane, trow, kq, acc);
+    stream_tiles<TT, RT, false, true, LAY>(a, cp, sp, xs, 0, a.G, lane, trow, kq, acc);
 
   float bv[TT];
   int bi[TT];
@@ -722,7 +810,7 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = kq * 4 + r;
-      if (t < TT && in_range && a.y) a.y[(int64_t)t * a.n_out + orow] = bad ? __builtin_nanf("") : acc[tl][r];
+      if (t < TT && in_range && a.y) st_global(a.y + (int64_t)t * a.n_out + orow, bad ? __builtin_nanf("") : acc[tl][r]);
     }
     if (a.partial) {
       // this lane's candidate for token rows t = 4*kq + r
@@ -742,8 +830,8 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
   }
   if (a.partial) {
     // per t: best (value, id) of this wave's rows, then of the workgroup
-    int2* fin = reinterpret_cast<int2*>(smem + a.fin_offset);
-    __syncthreads();  // staging area and max buffer are free now
+    int2* fin = reinterpret_cast<int2*>(smem);
+    __syncthreads();  // the staging area is free now
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       float v = bv[t];
@@ -762,7 +850,7 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
           i = c.y;
         }
       }
-      a.partial[wg * TT + lane] = int2{__float_as_int(b), i};
+      st_partial(a.partial + wg * TT + lane, b, i);
     }
   }
 }
@@ -799,7 +887,7 @@ __device__ __forceinline__ int tile_ptr(const GemvArgs& a, int64_t v, int r16, i
 template <int LAY>
 __device__ __forceinline__ void ring_prologue(const GemvArgs& a, const u4_t* cp, const uint16_t* sp,
                                               u4_t (&q)[kRing], u4_t& sv) {
-  sv = reinterpret_cast<const u4_t*>(sp)[scale_off<LAY>(a, 0)];
+  sv = ld_global(reinterpret_cast<const u4_t*>(sp) + scale_off<LAY>(a, 0));
 #pragma unroll
   for (int s = 0; s < kRing; ++s) {
     q[s] = load_codes<LAY>(cp + code_off<LAY>(a, min(s, a.G - 1)));
@@ -815,7 +903,9 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
   constexpr int PD = kRing;
   const int n = a.G;
   const int np = (n + PD - 1) / PD * PD;
-  const _Float16* xr0 = xs + trow * a.xs_stride + kq * 32;
+  const _Float16* xb[4];  // this lane's activation chunks of group 0 (see stream_tiles)
+#pragma unroll
+  for (int j = 0; j < 4; ++j) xb[j] = xs + trow * a.xs_stride + swz(trow, kq * 4 + j) * 8;
   int w_cur = (int)weight_row(a, v * 16 + r16);
   while (v < v_end) {  // uniform
     const int64_t vn = v + step;
@@ -829,15 +919,14 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
       const bool last = fi + PD >= np;  // uniform: this cycle prefetches the next tile
       const uint16_t* sbase = (last && has_next) ? spn : sp;
       const int gv = last ? (has_next ? 0 : fi) : fi + PD;
-      const u4_t svn = reinterpret_cast<const u4_t*>(sbase)[scale_off<LAY>(a, gv)];
+      const u4_t svn = ld_global(reinterpret_cast<const u4_t*>(sbase) + scale_off<LAY>(a, gv));
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int s = 0; s < PD; ++s) {
-        const int gl = fi + s;
-        const _Float16* xr = xr0 + min(gl, n - 1) * kGroup;
+        const int gl = fi + s;  // groups past n read the zeroed padding
         h8_t xa[4];
 #pragma unroll
-        for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xr + 8 * j);
+        for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xb[j] + gl * kGroup);
         const float sc = (gl < n) ? scale_of(sv, s) : 0.0f;
         f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
         d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], __builtin_bit_cast(h8_t, levels8(q[s].x)), d, 0, 0, 0);
@@ -867,7 +956,7 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
 #pragma unroll
       for (int i = 1; i < TT; ++i) e = (t == i) ? E[i] : e;
       const float val = ldexpf(accs[r], -e);
-      if (t < TT && in_range && a.y) a.y[(int64_t)t * a.n_out + orow] = w_cur < 0 ? __builtin_nanf("") : val;
+      if (t < TT && in_range && a.y) st_global(a.y + (int64_t)t * a.n_out + orow, w_cur < 0 ? __builtin_nanf("") : val);
       if (a.partial && t < TT && w_cur >= 0 && !__builtin_isnan(val) && better(val, w_cur, bv[r], bi[r])) {
         bv[r] = val;
         bi[r] = w_cur;
@@ -895,7 +984,6 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
   const int64_t span = (int64_t)nwv * a.run_tiles;
   const int64_t v0 = wg * span + wave, v_end = min(tiles, (wg + 1) * span);
   _Float16* xs = reinterpret_cast<_Float16*>(smem);
-  unsigned* maxbuf = reinterpret_cast<unsigned*>(smem + a.fin_offset);
   const u4_t* cp = nullptr;
   const uint16_t* sp = nullptr;
   u4_t q[kRing];
@@ -905,14 +993,7 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
     ring_prologue<LAY>(a, cp, sp, q, sv);
   }
   int E[TT];
-  const bool bad = stage_direct<TT>(a, xs, 0, a.G, threadIdx.x, blockDim.x);
-  if (workgroup_any(bad, maxbuf)) {
-    __syncthreads();  // every wave has read the flags before the max buffer is reused
-    stage_block<TT>(a, xs, maxbuf, 0, a.G, E);
-  } else {
-#pragma unroll
-    for (int t = 0; t < TT; ++t) E[t] = 0;
-  }
+  stage_shared<TT>(a, xs, 0, a.G, E);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   float bv[4];
   int bi[4];
@@ -924,8 +1005,8 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
   if (v0 < v_end) run_tiles<TT, LAY>(a, v0, v_end, nwv, xs, E, r16, kq, trow, cp, sp, q, sv, bv, bi);
   if (a.partial) {
     // per t: best of the lanes, of the waves, then of the workgroup
-    int2* fin = reinterpret_cast<int2*>(smem + a.fin_offset);
-    __syncthreads();  // the staging area and the flag words are free now
+    int2* fin = reinterpret_cast<int2*>(smem);
+    __syncthreads();  // the staging area is free now
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       // token row t lives in slot t % 4 of the lanes with kq = t / 4
@@ -952,7 +1033,7 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
           i = c.y;
         }
       }
-      a.partial[wg * TT + lane] = int2{__float_as_int(b), i};
+      st_partial(a.partial + wg * TT + lane, b, i);
     }
   }
 }

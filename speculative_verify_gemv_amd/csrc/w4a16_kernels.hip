@@ -108,6 +108,10 @@ hipError_t for_t(int T, F&& f) {
 
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// Groups rounded up to whole cycles of the load ring (the staged rows hold
+// the ring's padded slots too).
+int ring_groups(int g) { return (int)(cdiv(g, kRing) * kRing); }
+
 }  // namespace
 
 bool parse_tile(const char* text, Tile* t) {
@@ -150,7 +154,7 @@ static void plan_split(GemvArgs& a, int T, int rt, int nw_max, Plan* p) {
     a.nw = nw_eff;
     a.gpw = gpw;
     a.sk = sk;
-    a.xs_stride = sk * kGroup + 8;  // 16-byte pad between token rows
+    a.xs_stride = ring_groups(sk) * kGroup + 8;  // 16-byte pad between token rows
     const int wave_lds = std::max(T * a.xs_stride * 2, rt * T * 16 * 4);
     a.wave_lds = (wave_lds + 15) & ~15;
     a.fin_offset = nw_eff * a.wave_lds;
@@ -162,49 +166,45 @@ static void plan_split(GemvArgs& a, int T, int rt, int nw_max, Plan* p) {
   }
 }
 
+// LDS of a workgroup that stages activations for all its waves: up to eight
+// waves it may take half a CU (two such workgroups per CU), above that all
+// of it.
+static int shared_cap(int nwv) { return nwv > 8 ? kCuLds : kCuLds / 2; }
+
 // Shared tiling: nwv waves of rt 16-row tiles per workgroup over all of K; the
 // activation slice staged in LDS holds sk groups (all of K when the LDS
-// allows it, else a multiple of the 8-group ring), followed by a small area
-// for the slice maxima and the argmax partials of the waves.  Up to eight
-// waves a workgroup takes at most 64 KB (several per CU); with more it takes
-// up to the CU's 160 KB.
+// allows it, else a multiple of the 8-group ring) of every token row, and
+// nothing else: the staging's flag words, the slice maxima and the argmax
+// partials of the waves reuse the staging area.
 static void plan_shared(GemvArgs& a, int T, int rt, int nwv, Plan* p) {
-  const int small = nwv * T * 8;
-  const int cap = nwv > 8 ? kCuLds : kLdsCap;  // more than 8 waves: one workgroup per CU
-  int sk = ((cap - small - 16) / T - 16) / (kGroup * 2);
-  if (sk < a.G)
-    sk = std::max(kRing, sk - sk % kRing);
-  else
-    sk = a.G;
+  const int sk_cap = shared_cap(nwv) / (T * kGroup * 2);
+  const int sk = ring_groups(a.G) <= sk_cap ? a.G : std::max(kRing, sk_cap - sk_cap % kRing);
   a.nw = nwv;
   a.gpw = a.G;
   a.sk = sk;
-  a.xs_stride = sk * kGroup + 8;
+  a.xs_stride = ring_groups(sk) * kGroup;
   a.wave_lds = 0;
-  a.fin_offset = (T * a.xs_stride * 2 + 15) & ~15;
-  p->lds = a.fin_offset + small;
+  a.fin_offset = 0;
+  p->lds = std::max(T * a.xs_stride * 2, nwv * T * 8);
   p->threads = nwv * 64;
   p->grid = cdiv(a.n_out, 16LL * nwv * rt);
 }
 
 // Run tiling: nwv waves of nt whole tiles each; all of K staged once (as a
-// shared workgroup with sk = G), so it needs the activations to fit (up to
-// 8 waves: 64 KB, more: the CU's 160 KB) and eight scales per load.
-// Returns false otherwise.
+// shared workgroup with sk = G), so it needs the activations to fit
+// (shared_cap) and eight scales per load.  Returns false otherwise.
 static bool plan_run(GemvArgs& a, int T, int nt, int nwv, Plan* p) {
   if (!a.vec_scales) return false;
-  const int small = nwv * T * 8;
-  const int cap = nwv > 8 ? kCuLds : kLdsCap;
-  const int64_t xs_bytes = ((int64_t)T * (a.K + 8) * 2 + 15) & ~15LL;
-  if (xs_bytes + small > cap) return false;
+  const int64_t xs_bytes = (int64_t)T * ring_groups(a.G) * kGroup * 2;
+  if (xs_bytes > shared_cap(nwv)) return false;
   a.nw = nwv;
   a.gpw = a.G;
   a.sk = a.G;
-  a.xs_stride = a.K + 8;
+  a.xs_stride = ring_groups(a.G) * kGroup;
   a.wave_lds = 0;
   a.run_tiles = nt;
-  a.fin_offset = (int32_t)xs_bytes;
-  p->lds = (int)xs_bytes + small;
+  a.fin_offset = 0;
+  p->lds = std::max((int)xs_bytes, nwv * T * 8);
   p->threads = nwv * 64;
   p->grid = cdiv(cdiv(a.n_out, 16), (int64_t)nwv * nt);
   return true;
@@ -235,7 +235,7 @@ Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel, bool batch)
 }
 
 int shared_waves(int T, int64_t K) {
-  if ((int64_t)T * (K + 8) * 2 + 16 * T * 8 > kLdsCap) return 16;
+  if ((int64_t)T * ring_groups((int)(K / kGroup)) * kGroup * 2 > shared_cap(8)) return 16;
   return T <= 2 ? 4 : 8;
 }
 

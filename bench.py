@@ -11,7 +11,7 @@ tiled layout (same codes and scales, one contiguous 1 KB block per 16 rows x
 Reported (one JSON line): weight GB/s of the whole step (value), decode
 cycles/s, the grouped body kernel's achieved bandwidth against the 8 TB/s
 HBM peak (roofline, timed with HIP events on the launch stream), the body
-pass at T = 1, 4, 8 in both layouts (tiled and the pages' row-major one),
+pass at T = 1, 4, 8 and 16 in both layouts (tiled and the pages' row-major one),
 the same step as 257 separate launches replayed from a captured HIP graph,
 and the CPU oracle's rate on a bounded sample.
 
@@ -188,11 +188,11 @@ def main():
     log(f"step {ms_step:.4f} ms, body kernel {body_ms_avg:.4f} ms (min {min(body_ms):.4f}), "
         f"{value:.0f} GB/s per step, body {achieved:.0f} GB/s")
 
-    # ---- body pass at T = 1, 4, 8 (same weights, grouped launch), both layouts ----
+    # ---- body pass at T = 1, 4, 8, 16 (same weights, grouped launch), both layouts ----
     per_t, per_t_rm = {}, {}
     if not args.no_per_t:
         for tiled, table in ((True, per_t), (False, per_t_rm)):
-            for Tp in (1, 4, 8):
+            for Tp in (1, 4, 8, 16):
                 b, _ = (batch, probs) if (Tp == T and tiled) else make_pass(Tp, tiled)
                 for _ in range(20):  # ~40 ms of work: past the clock ramp after the host-side set-up
                     b.run(stream)

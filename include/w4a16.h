@@ -55,8 +55,8 @@ typedef struct ihipStream_t* hipStream_t; /* same definition as the HIP runtime'
 #endif
 
 #define W4A16_GROUP 128      /* columns per bf16 scale */
-#define W4A16_MAX_T 8        /* activation rows per weight read */
-#define W4A16_ABI_VERSION 2
+#define W4A16_MAX_T 16       /* activation rows per weight read */
+#define W4A16_ABI_VERSION 3
 
 typedef enum {
   W4A16_OK = 0,
@@ -70,7 +70,9 @@ typedef enum {
 } w4a16_status;
 
 /* Kernel variants.  Both compute the same values within the tolerance above;
- * AUTO picks per T the one measured faster on MI355X. */
+ * AUTO picks per T the one measured faster on MI355X.  The dot variant covers
+ * T <= 8; calls with more activation rows run the matrix-core kernels
+ * whatever the selection. */
 typedef enum {
   W4A16_VARIANT_AUTO = 0,
   W4A16_VARIANT_DOT = 1, /* VALU dot products, split-K across lanes, cross-lane reduction */

@@ -16,7 +16,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libw4a16.so")
 
 GROUP = 128
-MAX_T = 8
+MAX_T = 16
 VARIANTS = {"auto": 0, "dot": 1, "mfma": 2}
 
 _lib = None

@@ -1,7 +1,7 @@
 """Compile the HIP library libw4a16.so for gfx950 (hipcc, in-tree).
 
 The kernel templates are instantiated once per activation-row count T
-(w4a16_kernels_tt.hip built eight times with -DW4A16_TT=1..8); those
+(w4a16_kernels_tt.hip built sixteen times with -DW4A16_TT=1..16); those
 objects, the planning / dispatch unit and the C ABI unit compile in
 parallel and are linked into one shared library.
 """
@@ -15,7 +15,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libw4a16.so")
 OBJ_DIR = os.path.join(ROOT, "_build", "w4a16")
-MAX_T = 8
+MAX_T = 16
 
 # -packed-fp32-ops: no v_pk_{add,mul,fma}_f32 in generated code.
 HIPCC_FLAGS = [

@@ -65,10 +65,11 @@ w4a16_status check_kt(int64_t K, int32_t T) {
   return W4A16_OK;
 }
 
-// The variant AUTO resolves to for T activation rows.
+// The variant a call with T activation rows runs: the selection, except
+// that the dot kernel is built for T <= kDotMaxT only; AUTO is the matrix
+// cores (measured faster at every T on MI355X).
 int resolve_variant(int32_t v, int32_t T) {
-  if (v == W4A16_VARIANT_DOT || v == W4A16_VARIANT_MFMA) return v;
-  (void)T;
+  if (v == W4A16_VARIANT_DOT && T <= w4a16::kDotMaxT) return v;
   return W4A16_VARIANT_MFMA;
 }
 

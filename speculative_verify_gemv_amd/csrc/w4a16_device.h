@@ -223,16 +223,16 @@ __device__ __forceinline__ void workgroup_argmax(const GemvArgs& a, const float*
 //
 // A staged slice holds token row t at xs + t * xs_stride as a run of 16-byte
 // chunks (eight fp16 in slot order, 16 chunks per 128-column group).  Chunk c
-// of row t sits at position c ^ g(t) of the row, g(t) = bits 0-1 of t plus
-// bit 2 of t moved to bit 3.  A lane (row r, quarter kq) of the matrix-core
+// of row t sits at position c ^ g(t) of the row, where g keeps bits 0-1 of t
+// and swaps bits 2 and 3.  A lane (row r, quarter kq) of the matrix-core
 // loop reads chunk 4 kq + j of its row; with g, the 32 lanes of quarters
 // 0-1 (or 2-3) over eight token rows read 16 different chunk positions, i.e.
-// all 64 LDS banks once, so the rows need no padding: T rows of K
-// activations take exactly T * K * 2 bytes (at T = 8, K = 5120 two workgroups
-// fit in a CU's 160 KB).  The XOR stays inside the aligned 16 chunks of one
-// group.
+// all 64 LDS banks once, and the 16 lanes of one quarter over sixteen rows
+// do the same, so the rows need no padding: T rows of K activations take
+// exactly T * K * 2 bytes (T = 16, K = 5120 is a CU's whole 160 KB).  The
+// XOR stays inside the aligned 16 chunks of one group.
 
-__device__ __forceinline__ int swz(int t, int c) { return c ^ ((t & 3) | ((t & 4) << 1)); }
+__device__ __forceinline__ int swz(int t, int c) { return c ^ ((t & 3) | ((t & 4) << 1) | ((t & 8) >> 1)); }
 
 // Stages x[t][gs*128 .. ge*128) of all TT token rows into this wave's LDS
 // area as scaled fp16 in slot order; E[t] receives each row's exponent.
@@ -424,6 +424,8 @@ __device__ __forceinline__ void stage_shared(const GemvArgs& a, _Float16* xs, in
 
 // RW rows per wave, L = 64/RW lanes per row; a lane takes the row's 16-byte
 // chunks li, li+L, li+2L, ...; CPL bounds the chunks per lane per slice.
+// Built for TT <= kDotMaxT (its per-lane sums grow with TT; more rows go to
+// the matrix cores).
 template <int TT, int RW>
 __global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -1162,8 +1164,12 @@ hipError_t launch_t(const GemvArgs& a, const GemvArgs* table, int count, const P
   if (p.variant == kSplit) return launch_rt<TT, false>(a, table, count, p, s);
   if (p.variant == kShared) return launch_rt<TT, true>(a, table, count, p, s);
   if (table || p.variant != kDot || p.rt != 2) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((w4a16_dot_kernel<TT, 2>), dim3((unsigned)p.grid), dim3((unsigned)p.threads), p.lds, s, a);
-  return hipGetLastError();
+  if constexpr (TT <= kDotMaxT) {
+    hipLaunchKernelGGL((w4a16_dot_kernel<TT, 2>), dim3((unsigned)p.grid), dim3((unsigned)p.threads), p.lds, s, a);
+    return hipGetLastError();
+  } else {
+    return hipErrorInvalidValue;  // the planner never picks the dot kernel above kDotMaxT
+  }
 }
 
 }  // namespace w4a16

@@ -53,6 +53,7 @@ inline int64_t tiled_tile_bytes(int64_t G) {
 // a shared workgroup whose waves stream several whole tiles each, the load
 // ring running from one tile into the next (all of K staged once).
 constexpr int kDot = 1, kSplit = 2, kShared = 3, kRun = 4;
+constexpr int kDotMaxT = 8;  // the dot kernel is built for T <= 8
 
 // Matrix-core tile choice: shape, 16-row tiles per wave, waves per workgroup.
 struct Tile {

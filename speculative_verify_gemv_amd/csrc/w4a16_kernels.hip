@@ -13,6 +13,14 @@ extern template hipError_t launch_t<5>(const GemvArgs&, const GemvArgs*, int, co
 extern template hipError_t launch_t<6>(const GemvArgs&, const GemvArgs*, int, const Plan&, hipStream_t);
 extern template hipError_t launch_t<7>(const GemvArgs&, const GemvArgs*, int, const Plan&, hipStream_t);
 extern template hipError_t launch_t<8>(const GemvArgs&, const GemvArgs*, int, const Plan&, hipStream_t);
+extern template hipError_t launch_t<9>(const GemvArgs&, const GemvArgs*, int, const Plan&, hipStream_t);
+extern template hipError_t launch_t<10>(const GemvArgs&, const GemvArgs*, int, const Plan&, hipStream_t);
+extern template hipError_t launch_t<11>(const GemvArgs&, const GemvArgs*, int, const Plan&, hipStream_t);
+extern template hipError_t launch_t<12>(const GemvArgs&, const GemvArgs*, int, const Plan&, hipStream_t);
+extern template hipError_t launch_t<13>(const GemvArgs&, const GemvArgs*, int, const Plan&, hipStream_t);
+extern template hipError_t launch_t<14>(const GemvArgs&, const GemvArgs*, int, const Plan&, hipStream_t);
+extern template hipError_t launch_t<15>(const GemvArgs&, const GemvArgs*, int, const Plan&, hipStream_t);
+extern template hipError_t launch_t<16>(const GemvArgs&, const GemvArgs*, int, const Plan&, hipStream_t);
 
 namespace {
 
@@ -102,6 +110,14 @@ hipError_t for_t(int T, F&& f) {
     case 6: return f(std::integral_constant<int, 6>{});
     case 7: return f(std::integral_constant<int, 7>{});
     case 8: return f(std::integral_constant<int, 8>{});
+    case 9: return f(std::integral_constant<int, 9>{});
+    case 10: return f(std::integral_constant<int, 10>{});
+    case 11: return f(std::integral_constant<int, 11>{});
+    case 12: return f(std::integral_constant<int, 12>{});
+    case 13: return f(std::integral_constant<int, 13>{});
+    case 14: return f(std::integral_constant<int, 14>{});
+    case 15: return f(std::integral_constant<int, 15>{});
+    case 16: return f(std::integral_constant<int, 16>{});
     default: return hipErrorInvalidValue;
   }
 }
@@ -150,7 +166,7 @@ static void plan_split(GemvArgs& a, int T, int rt, int nw_max, Plan* p) {
     else if (nw > 1)
       continue;
     else
-      sk = kRing;  // unreachable for T <= 8: one wave always fits 24 groups
+      sk = kRing;  // unreachable for T <= 16: one wave always fits 15 groups
     a.nw = nw_eff;
     a.gpw = gpw;
     a.sk = sk;

@@ -1,9 +1,9 @@
-// One object per activation-row count: W4A16_TT (1..8) selects which
+// One object per activation-row count: W4A16_TT (1..16) selects which
 // instantiation of the kernels this translation unit builds.
 #include "w4a16_device.h"
 
 #ifndef W4A16_TT
-#error "build with -DW4A16_TT=<1..8>"
+#error "build with -DW4A16_TT=<1..16>"
 #endif
 
 namespace w4a16 {

@@ -62,7 +62,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.w4a16_abi_version() == 2
+    assert lib.w4a16_abi_version() == 3
     for s in range(8):
         assert lib.w4a16_status_string(s)
     assert lib.w4a16_status_string(99) == b"unknown status"
@@ -87,7 +87,7 @@ def test_matmul_rejections(lib):
     assert mm(lib, K=129) == SHAPE
     assert mm(lib, K=2**21) == SHAPE
     assert mm(lib, T=0) == SHAPE
-    assert mm(lib, T=9) == SHAPE
+    assert mm(lib, T=17) == SHAPE
     assert mm(lib, p=A + 8) == ALIGN
     assert mm(lib, x=A + 2) == ALIGN
     assert mm(lib, s=A + 1) == ALIGN
@@ -105,7 +105,7 @@ def test_head_gather_rejections(lib):
     assert hg(lib, n_ids=0) == SHAPE
     assert hg(lib, n_rows=0) == SHAPE
     assert hg(lib, ids=None, n_ids=10, n_rows=100) == SHAPE   # identity needs n_ids == n_rows
-    assert hg(lib, T=9) == SHAPE
+    assert hg(lib, T=17) == SHAPE
     assert hg(lib, K=200) == SHAPE
     assert hg(lib, ids=A + 2) == ALIGN
     assert hg(lib, am=A + 1) == ALIGN
@@ -119,7 +119,7 @@ def test_head_gather_rejections(lib):
 def test_workspace_bytes(lib):
     assert lib.w4a16_workspace_bytes(0, 1) == 0
     assert lib.w4a16_workspace_bytes(10, 0) == 0
-    assert lib.w4a16_workspace_bytes(10, 9) == 0
+    assert lib.w4a16_workspace_bytes(10, 17) == 0
     assert lib.w4a16_workspace_bytes(248320, 4) == 248320 // 16 * 4 * 8
     assert lib.w4a16_workspace_bytes(17, 1) == 2 * 8
 
@@ -161,7 +161,7 @@ def test_tiled_rejections(lib):
     assert rp(tb=need - 1) == WS
     mt = lambda w=A, x=A, y=A, N=64, K=256, T=2: lib.w4a16_matmul_tiled(w, x, y, N, K, T, None)
     assert mt(w=None) == NULLP and mt(x=None) == NULLP and mt(y=None) == NULLP
-    assert mt(N=0) == SHAPE and mt(K=129) == SHAPE and mt(T=9) == SHAPE
+    assert mt(N=0) == SHAPE and mt(K=129) == SHAPE and mt(T=17) == SHAPE
     assert mt(w=A + 4) == ALIGN and mt(x=A + 2) == ALIGN and mt(y=A + 2) == ALIGN
     gt = lambda ids=A, n_ids=10, w=A, n_rows=100, x=A, K=256, T=2, y=A, am=None, av=None, ws=None, wsb=0: \
         lib.w4a16_head_gather_tiled(ids, n_ids, w, n_rows, x, K, T, y, am, av, ws, wsb, None)

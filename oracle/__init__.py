@@ -32,6 +32,8 @@ def _load():
         lib.oracle_gather.argtypes = [vp, i64, vp, vp, i64, vp, i64, i32, vp, vp, i32]
         lib.oracle_matmul_dequant_first.argtypes = [vp, vp, vp, i64, i64, i32, vp]
         lib.oracle_argmax.argtypes = [vp, vp, i64, i32, vp, vp, vp]
+        lib.oracle_topk.argtypes = [vp, vp, i64, i32, i32, vp, vp]
+        lib.oracle_greedy_accept.argtypes = [vp, vp, i32, i32, vp, vp]
         _lib = lib
     return _lib
 
@@ -113,3 +115,31 @@ def bf16(bits: int) -> float:
 def code(packed_row, k: int) -> int:
     packed_row, p = _c(packed_row, np.uint8)
     return int(_load().oracle_code(p, k))
+
+
+def topk(y, k: int, ids=None):
+    """Per row t of y[T][n]: the k best (id, value) pairs, score descending,
+    equal scores by ascending id; NaN scores never count; (-1, NaN) padding."""
+    y, yp = _c(y, np.float64)
+    T, n = y.shape
+    if ids is not None:
+        ids, ip = _c(ids, np.int32)
+        assert ids.shape == (n,)
+    else:
+        ip = None
+    out_id = np.empty((T, k), np.int32)
+    out_val = np.empty((T, k), np.float64)
+    _load().oracle_topk(yp, ip, n, T, k, out_id.ctypes.data, out_val.ctypes.data)
+    return out_id, out_val
+
+
+def greedy_accept(target, draft, n_seq: int, rows: int):
+    """Accepted drafts per sequence and the emitted tokens (target choices of
+    rows 0..a, then -1)."""
+    target, tp = _c(target, np.int32)
+    draft, dp = _c(draft, np.int32)
+    assert target.size == n_seq * rows and draft.size == n_seq * (rows - 1)
+    acc = np.empty(n_seq, np.int32)
+    tok = np.empty((n_seq, rows), np.int32)
+    _load().oracle_greedy_accept(tp, dp if draft.size else None, n_seq, rows, acc.ctypes.data, tok.ctypes.data)
+    return acc, tok

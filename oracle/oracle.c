@@ -201,3 +201,75 @@ void oracle_argmax(const double* y, const int32_t* ids, int64_t n, int T, int32_
     if (gap_out) gap_out[t] = have_second ? row[best] - second : INFINITY;
   }
 }
+
+/* ------------------------------------------------------ verify epilogue ----
+ *
+ * Per-row top-k.  The OpenJet engine page ("How it gets its speed") keeps
+ * the 32 best logits of each verified row for its sampler, and the
+ * qwen-warp article ("What each one calls the same answer") rescores the
+ * quantized head's 16 best candidates.  Definition used here: for each
+ * activation row t of y[T][n], the k largest non-NaN scores with their
+ * vocabulary ids (ids[i], or i when ids is NULL), in descending order of
+ * score, equal scores in ascending order of id -- so entry 0 is the argmax
+ * defined above.  -0 and +0 are equal scores.  With fewer than k non-NaN
+ * scores the rest of the row is id -1, value NaN.  The implementation is
+ * the definition: collect, sort everything, take the first k.
+ */
+typedef struct {
+  double v;
+  int64_t id;
+} cand_t;
+
+static int cand_before(const void* pa, const void* pb) {
+  const cand_t* a = (const cand_t*)pa;
+  const cand_t* b = (const cand_t*)pb;
+  if (a->v > b->v) return -1;
+  if (a->v < b->v) return 1;
+  return (a->id < b->id) ? -1 : (a->id > b->id) ? 1 : 0;
+}
+
+void oracle_topk(const double* y, const int32_t* ids, int64_t n, int T, int k, int32_t* id_out, double* val_out) {
+  cand_t* c = (cand_t*)malloc(sizeof(cand_t) * (size_t)(n > 0 ? n : 1));
+  if (!c) return;
+  for (int t = 0; t < T; ++t) {
+    const double* row = y + (int64_t)t * n;
+    int64_t m = 0;
+    for (int64_t i = 0; i < n; ++i) {
+      if (isnan(row[i])) continue;
+      c[m].v = row[i];
+      c[m].id = ids ? (int64_t)ids[i] : i;
+      ++m;
+    }
+    qsort(c, (size_t)m, sizeof(cand_t), cand_before);
+    for (int j = 0; j < k; ++j) {
+      id_out[(int64_t)t * k + j] = j < m ? (int32_t)c[j].id : -1;
+      val_out[(int64_t)t * k + j] = j < m ? c[j].v : NAN;
+    }
+  }
+  free(c);
+}
+
+/* Greedy verification.  qwen-warp article, "What each one calls the same
+ * answer": greedy acceptance is an argmax equality over the verify rows;
+ * OpenJet engine page, "How it works": verification runs on the device and
+ * the host reads back only the accepted tokens.
+ *
+ * n_seq sequences of `rows` verify rows each.  Row r of sequence s carries
+ * the target model's greedy choice target[s*rows + r] for the token after
+ * position r; draft[s*(rows-1) + j] is the drafted token fed as the input of
+ * row j+1.  Draft j is accepted when drafts 0..j-1 were and
+ * target[s*rows + j] equals it (a negative target, i.e. no valid row, never
+ * matches).  With a accepted drafts the cycle emits the target choices of
+ * rows 0..a: the accepted drafts themselves followed by one more token of
+ * the target model.  accepted[s] = a; tokens[s*rows + r] = target[s*rows + r]
+ * for r <= a and -1 after.
+ */
+void oracle_greedy_accept(const int32_t* target, const int32_t* draft, int n_seq, int rows, int32_t* accepted,
+                          int32_t* tokens) {
+  for (int s = 0; s < n_seq; ++s) {
+    int a = 0;
+    while (a < rows - 1 && target[s * rows + a] >= 0 && target[s * rows + a] == draft[s * (rows - 1) + a]) ++a;
+    accepted[s] = a;
+    for (int r = 0; r < rows; ++r) tokens[s * rows + r] = r <= a ? target[s * rows + r] : -1;
+  }
+}

@@ -303,3 +303,104 @@ def test_planted_mistakes_are_caught():
     y_ok, _ = oracle.matmul(p2, sc, fill_bf16((1, 256), 1.0))
     y_tr, _ = oracle.matmul(p2, np.ascontiguousarray(sc.T), fill_bf16((1, 256), 1.0))
     assert y_ok[0, 0] == h["y"] and y_tr[0, 0] != h["y"]
+
+
+# ------------------------------------------------------- verify epilogue ----
+
+def _num(v):
+    return float("nan") if v == "nan" else (-0.0 if v == "-0" else float(v))
+
+
+def test_topk_hand_example():
+    g = load("verify_epilogue.json")["topk"]
+    y = np.array([[_num(v) for v in r] for r in g["scores"]])
+    got_id, got_val = oracle.topk(y, g["k"], np.array(g["ids"], np.int32))
+    assert got_id.tolist() == g["top_ids"]
+    want = np.array([[_num(v) for v in r] for r in g["top_vals"]])
+    assert np.array_equal(got_val, want, equal_nan=True)
+
+
+def test_topk_entry_zero_is_the_argmax():
+    rng = np.random.default_rng(11)
+    for _ in range(100):
+        n = int(rng.integers(1, 40))
+        y = rng.integers(-4, 5, size=(3, n)).astype(np.float64)  # many ties
+        y[rng.random((3, n)) < 0.2] = np.nan
+        ids = rng.permutation(1000)[:n].astype(np.int32)
+        top_id, top_val = oracle.topk(y, 5, ids)
+        am, av, _ = oracle.argmax(y, ids)
+        assert np.array_equal(top_id[:, 0], am)
+        assert np.array_equal(top_val[:, 0], av, equal_nan=True)
+
+
+def test_topk_equals_a_library_sort():
+    """numpy's lexsort over (id ascending within score descending) gives the
+    same k pairs on random data with ties and NaNs."""
+    rng = np.random.default_rng(12)
+    for _ in range(50):
+        n = int(rng.integers(1, 300))
+        k = int(rng.integers(1, 33))
+        y = np.round(rng.normal(size=(2, n)) * 4) / 4
+        y[rng.random((2, n)) < 0.1] = np.nan
+        ids = rng.permutation(5 * n)[:n].astype(np.int32)
+        got_id, got_val = oracle.topk(y, k, ids)
+        for t in range(2):
+            ok = ~np.isnan(y[t])
+            order = np.lexsort((ids[ok], -y[t][ok]))[:k]
+            want_id = np.full(k, -1, np.int32)
+            want_val = np.full(k, np.nan)
+            want_id[:order.size] = ids[ok][order]
+            want_val[:order.size] = y[t][ok][order]
+            assert np.array_equal(got_id[t], want_id)
+            assert np.array_equal(got_val[t], want_val, equal_nan=True)
+
+
+def test_topk_is_permutation_invariant_and_identity_ids():
+    rng = np.random.default_rng(13)
+    y = np.round(rng.normal(size=(3, 500)) * 8) / 8
+    perm = rng.permutation(500)
+    a_id, a_val = oracle.topk(y, 32)
+    b_id, b_val = oracle.topk(y[:, perm], 32, perm.astype(np.int32))
+    assert np.array_equal(a_id, b_id) and np.array_equal(a_val, b_val)
+
+
+def test_greedy_hand_examples():
+    for case in load("verify_epilogue.json")["greedy"]:
+        acc, tok = oracle.greedy_accept(np.array(case["target"], np.int32), np.array(case["draft"], np.int32), 1,
+                                        case["rows"])
+        assert acc[0] == case["accepted"] and tok[0].tolist() == case["tokens"], case
+
+
+def test_greedy_accepts_exactly_the_longest_matching_prefix():
+    """Properties of the definition on random sequences: every accepted draft
+    matches its row's choice, the first unaccepted one does not, and the
+    emitted tokens are the choices of rows 0..a."""
+    rng = np.random.default_rng(14)
+    S, R = 64, 5
+    target = rng.integers(0, 4, size=(S, R)).astype(np.int32)
+    draft = np.where(rng.random((S, R - 1)) < 0.7, target[:, :R - 1], rng.integers(0, 4, size=(S, R - 1)))
+    acc, tok = oracle.greedy_accept(target, draft.astype(np.int32), S, R)
+    for s in range(S):
+        a = acc[s]
+        assert np.array_equal(target[s, :a], draft[s, :a])
+        assert a == R - 1 or target[s, a] != draft[s, a]
+        assert tok[s, :a + 1].tolist() == target[s, :a + 1].tolist() and np.all(tok[s, a + 1:] == -1)
+
+
+def test_planted_epilogue_mistakes_are_caught():
+    g = load("verify_epilogue.json")
+    y = np.array([[_num(v) for v in g["topk"]["scores"][0]]])
+    ids = np.array(g["topk"]["ids"], np.int32)
+    # ties broken towards the higher id: the fixture's first two ids swap
+    keep = ~np.isnan(y[0])
+    wrong = np.lexsort((-ids[keep], -y[0][keep]))[:2]
+    assert ids[keep][wrong].tolist() == g["topk"]["reversed_tie_order_would_give_row0_first2"]
+    assert ids[keep][wrong].tolist() != oracle.topk(y, 2, ids)[0][0].tolist()
+    # acceptance that counts every matching draft instead of the matching prefix
+    case = g["greedy"][1]
+    t, d = np.array(case["target"]), np.array(case["draft"])
+    assert int(np.sum(t[:-1] == d)) == 2 and case["accepted"] == 0
+    case = g["greedy"][2]
+    t, d = np.array(case["target"]), np.array(case["draft"])
+    off_by_one = int(np.argmin(np.append(t[:-1] == d, False))) + 1
+    assert off_by_one == g["off_by_one_would_give_accepted_for_case_2"] != case["accepted"]

@@ -211,6 +211,11 @@ def main():
                     f"({100 * g / PEAK_GBPS:.1f}% of 8 TB/s)")
                 del b
 
+    # ---- verify epilogue on the head's scores: top-32 per row, greedy acceptance ----
+    epilogue = verify_epilogue(torch, w4a16, head_y, T, stream)
+    log(f"verify epilogue at T={T}: top-32 of {hn} scores {epilogue['topk32_us']:.1f} us, "
+        f"greedy acceptance {epilogue['greedy_us']:.1f} us")
+
     # ---- the same step as 257 separate launches, replayed from a HIP graph ----
     graph_pass = None
     if not args.no_graph:
@@ -252,6 +257,7 @@ def main():
         "per_T_body_pass": per_t,
         "per_T_body_pass_row_major": per_t_rm,
         "graph_257_launches": graph_pass,
+        "verify_epilogue": epilogue,
         "roofline": {
             "kernel": "grouped body pass (64 x 4 projections, one launch, tiled layout)",
             "bound": "hbm",
@@ -266,6 +272,29 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def verify_epilogue(torch, w4a16, head_y, T, stream, reps=50):
+    """Per-row top-32 of the lm_head scores (two launches) and greedy
+    acceptance of T - 1 drafts (one launch), timed on the launch stream."""
+    k = 32
+    ws = torch.empty(w4a16.topk_workspace_bytes(head_y.shape[1], T, k), dtype=torch.uint8, device="cuda")
+    target = torch.zeros(T, dtype=torch.int32, device="cuda")
+    draft = torch.zeros(max(T - 1, 1), dtype=torch.int32, device="cuda")
+    out = {}
+    for name, fn in (("topk32_us", lambda: w4a16.topk(head_y, k, workspace=ws, stream=stream)),
+                     ("greedy_us", lambda: w4a16.greedy_accept(target, draft[:T - 1] if T > 1 else None, 1, T,
+                                                               stream=stream))):
+        for _ in range(5):
+            fn()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        out[name] = round(1000.0 * e0.elapsed_time(e1) / reps, 2)
+    return out
 
 
 def graph_step(torch, w4a16, probs, head, reps):

@@ -211,6 +211,56 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
 /* W4A16_ERR_BAD_SHAPE if table_host is not a table written by w4a16_batch_plan. */
 w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, hipStream_t stream);
 
+/*
+ * Verify epilogue: what a speculative cycle does with the head's scores
+ * before the host reads anything back (OpenJet engine page, "How it works":
+ * verification on the device, only the accepted tokens go to the host).
+ *
+ * Per-row top-k.  The OpenJet page ("How it gets its speed") keeps the 32
+ * best logits of each verified row for its sampler; the qwen-warp article
+ * ("What each one calls the same answer") rescores the quantized head's 16
+ * best candidates.  For each activation row t of scores [T][n] (e.g. the y
+ * of w4a16_head_gather): the k largest non-NaN scores and their vocabulary
+ * ids, score descending, equal scores by ascending id, so entry 0 is the
+ * argmax of w4a16_head_gather.  -0 and +0 are equal.  Position i has
+ * vocabulary id row_ids[i] (NULL: i); a NaN score or a negative id never
+ * counts.  With fewer than k countable entries the rest of the row is id -1,
+ * value NaN.
+ *   scores    float [T][n] device; 1 <= n <= 2^31-1, 1 <= T <= W4A16_MAX_T
+ *   row_ids   int32 [n] device or NULL
+ *   k         1 <= k <= W4A16_MAX_TOPK
+ *   top_ids   int32 [T][k] device (required); top_vals float [T][k] or NULL
+ *   workspace device, 16-byte aligned, at least
+ *             w4a16_topk_workspace_bytes(n, T, k) bytes (no initialisation)
+ */
+#define W4A16_MAX_TOPK 32
+
+size_t w4a16_topk_workspace_bytes(int64_t n, int32_t T, int32_t k);
+
+w4a16_status w4a16_topk(const float* scores, int64_t n, int32_t T, const int32_t* row_ids, int32_t k,
+                        int32_t* top_ids, float* top_vals, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream);
+
+/*
+ * Greedy acceptance (qwen-warp article, "What each one calls the same
+ * answer": greedy acceptance is an argmax equality over the verify rows).
+ * n_seq sequences of `rows` verify rows each, e.g. the T = n_seq * rows rows
+ * of one head call.  Row r of sequence s carries the target model's greedy
+ * choice target_ids[s*rows + r] (the argmax ids of w4a16_head_gather) for
+ * the token after position r; draft_ids[s*(rows-1) + j] is the drafted token
+ * that was the input of row j+1.  Draft j is accepted when drafts 0..j-1
+ * were and target_ids[s*rows + j] equals it (a negative target id never
+ * matches).  n_accepted[s] = a, the accepted drafts; tokens[s*rows + r] =
+ * target_ids[s*rows + r] for r <= a (the accepted drafts followed by the
+ * target model's next token) and -1 after.
+ *   target_ids int32 [n_seq*rows] device; draft_ids int32 [n_seq*(rows-1)]
+ *   device (may be NULL when rows = 1); n_accepted int32 [n_seq] device;
+ *   tokens int32 [n_seq*rows] device or NULL.
+ *   1 <= n_seq <= W4A16_MAX_BATCH, 1 <= rows <= W4A16_MAX_T.
+ */
+w4a16_status w4a16_greedy_accept(const int32_t* target_ids, const int32_t* draft_ids, int32_t n_seq, int32_t rows,
+                                 int32_t* n_accepted, int32_t* tokens, hipStream_t stream);
+
 /* Selects the kernel variant for subsequent calls in this process (initially
  * taken from the environment variable W4A16_VARIANT = auto|dot|mfma). */
 w4a16_status w4a16_set_variant(int32_t variant);

@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(HERE, "libw4a16.so")
 
 GROUP = 128
 MAX_T = 16
+MAX_TOPK = 32
 VARIANTS = {"auto": 0, "dot": 1, "mfma": 2}
 
 _lib = None
@@ -67,6 +68,12 @@ def load_library():
         lib.w4a16_matmul_tiled.restype = i32
         lib.w4a16_head_gather_tiled.argtypes = [vp, i64, vp, i64, vp, i64, i32, vp, vp, vp, vp, sz, vp]
         lib.w4a16_head_gather_tiled.restype = i32
+        lib.w4a16_topk_workspace_bytes.argtypes = [i64, i32, i32]
+        lib.w4a16_topk_workspace_bytes.restype = sz
+        lib.w4a16_topk.argtypes = [vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]
+        lib.w4a16_topk.restype = i32
+        lib.w4a16_greedy_accept.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+        lib.w4a16_greedy_accept.restype = i32
         _lib = lib
     return _lib
 
@@ -288,3 +295,52 @@ class Batch:
         s = load_library().w4a16_matmul_batch(self.host.data_ptr(), self.device.data_ptr(), _stream(stream))
         if s:
             raise W4A16Error(s, "w4a16_matmul_batch")
+
+
+def topk_workspace_bytes(n: int, T: int, k: int) -> int:
+    return int(load_library().w4a16_topk_workspace_bytes(n, T, k))
+
+
+def topk(scores: torch.Tensor, k: int, row_ids: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+         stream=None):
+    """Per row t of scores [T][n] (float32): the k best (id, value) pairs,
+    score descending, equal scores by ascending vocabulary id (row_ids[i], or
+    i); NaN scores and negative ids never count; (-1, NaN) padding.
+    Returns (ids [T][k] int32, values [T][k] float32)."""
+    if scores.dtype != torch.float32 or scores.dim() != 2 or not (scores.is_cuda and scores.is_contiguous()):
+        raise ValueError("scores must be a contiguous CUDA float32 tensor [T][n]")
+    T, n = scores.shape
+    if row_ids is not None and (row_ids.dtype != torch.int32 or row_ids.shape != (n,) or not row_ids.is_cuda
+                                or not row_ids.is_contiguous()):
+        raise ValueError("row_ids must be a contiguous CUDA int32 vector of n entries")
+    nbytes = topk_workspace_bytes(n, T, k)
+    if nbytes == 0:
+        raise ValueError("topk: size out of range")
+    if workspace is None:
+        workspace = torch.empty(nbytes, dtype=torch.uint8, device=scores.device)
+    ids = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+    vals = torch.empty((T, k), dtype=torch.float32, device=scores.device)
+    st = load_library().w4a16_topk(scores.data_ptr(), n, T, _ptr(row_ids), k, ids.data_ptr(), vals.data_ptr(),
+                                   workspace.data_ptr(), workspace.numel() * workspace.element_size(),
+                                   _stream(stream))
+    if st:
+        raise W4A16Error(st, "w4a16_topk")
+    return ids, vals
+
+
+def greedy_accept(target_ids: torch.Tensor, draft_ids: torch.Tensor | None, n_seq: int, rows: int, stream=None):
+    """Greedy verification of n_seq sequences of `rows` verify rows: returns
+    (accepted drafts [n_seq] int32, emitted tokens [n_seq][rows] int32, -1 after
+    the target model's token)."""
+    for t, what in ((target_ids, "target_ids"), (draft_ids, "draft_ids")):
+        if t is not None and (t.dtype != torch.int32 or not (t.is_cuda and t.is_contiguous())):
+            raise ValueError(f"{what} must be a contiguous CUDA int32 tensor")
+    if target_ids.numel() != n_seq * rows or (draft_ids is not None and draft_ids.numel() != n_seq * (rows - 1)):
+        raise ValueError("target_ids must hold n_seq*rows ids and draft_ids n_seq*(rows-1)")
+    acc = torch.empty(n_seq, dtype=torch.int32, device=target_ids.device)
+    tok = torch.empty((n_seq, rows), dtype=torch.int32, device=target_ids.device)
+    st = load_library().w4a16_greedy_accept(target_ids.data_ptr(), _ptr(draft_ids), n_seq, rows, acc.data_ptr(),
+                                            tok.data_ptr(), _stream(stream))
+    if st:
+        raise W4A16Error(st, "w4a16_greedy_accept")
+    return acc, tok

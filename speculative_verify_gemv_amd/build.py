@@ -45,6 +45,7 @@ def _units():
     units = [(os.path.join(CSRC, "w4a16_kernels_tt.hip"), os.path.join(OBJ_DIR, f"kernels_t{t}.o"),
               [f"-DW4A16_TT={t}"]) for t in range(1, MAX_T + 1)]
     units.append((os.path.join(CSRC, "w4a16_kernels.hip"), os.path.join(OBJ_DIR, "kernels.o"), []))
+    units.append((os.path.join(CSRC, "w4a16_epilogue.hip"), os.path.join(OBJ_DIR, "epilogue.o"), []))
     units.append((os.path.join(CSRC, "w4a16_api.hip"), os.path.join(OBJ_DIR, "api.o"), []))
     return units
 

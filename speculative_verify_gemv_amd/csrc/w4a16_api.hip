@@ -346,6 +346,38 @@ w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, h
   return w4a16::launch_batch(args, hdr->count, p, hdr->T, stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
 }
 
+size_t w4a16_topk_workspace_bytes(int64_t n, int32_t T, int32_t k) {
+  if (n < 1 || n > kMaxRows || T < 1 || T > W4A16_MAX_T || k < 1 || k > W4A16_MAX_TOPK) return 0;
+  return (size_t)T * (size_t)w4a16::topk_chunks(n) * (size_t)k * 8u;
+}
+
+w4a16_status w4a16_topk(const float* scores, int64_t n, int32_t T, const int32_t* row_ids, int32_t k,
+                        int32_t* top_ids, float* top_vals, void* workspace, size_t workspace_bytes,
+                        hipStream_t stream) {
+  if (!scores || !top_ids) return W4A16_ERR_NULL_POINTER;
+  if (n < 1 || n > kMaxRows || T < 1 || T > W4A16_MAX_T || k < 1 || k > W4A16_MAX_TOPK) return W4A16_ERR_BAD_SHAPE;
+  if (!aligned(scores, 4) || !aligned(row_ids, 4) || !aligned(top_ids, 4) || !aligned(top_vals, 4))
+    return W4A16_ERR_MISALIGNED;
+  if (!workspace || !aligned(workspace, 16) || workspace_bytes < w4a16_topk_workspace_bytes(n, T, k))
+    return W4A16_ERR_WORKSPACE;
+  if (w4a16_status s = check_device()) return s;
+  return w4a16::launch_topk(scores, n, T, row_ids, k, top_ids, top_vals, workspace, stream) == hipSuccess
+             ? W4A16_OK
+             : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_greedy_accept(const int32_t* target_ids, const int32_t* draft_ids, int32_t n_seq, int32_t rows,
+                                 int32_t* n_accepted, int32_t* tokens, hipStream_t stream) {
+  if (!target_ids || !n_accepted || (rows > 1 && !draft_ids)) return W4A16_ERR_NULL_POINTER;
+  if (n_seq < 1 || n_seq > W4A16_MAX_BATCH || rows < 1 || rows > W4A16_MAX_T) return W4A16_ERR_BAD_SHAPE;
+  if (!aligned(target_ids, 4) || !aligned(draft_ids, 4) || !aligned(n_accepted, 4) || !aligned(tokens, 4))
+    return W4A16_ERR_MISALIGNED;
+  if (w4a16_status s = check_device()) return s;
+  return w4a16::launch_greedy(target_ids, draft_ids, n_seq, rows, n_accepted, tokens, stream) == hipSuccess
+             ? W4A16_OK
+             : W4A16_ERR_HIP;
+}
+
 w4a16_status w4a16_set_variant(int32_t variant) {
   if (variant != W4A16_VARIANT_AUTO && variant != W4A16_VARIANT_DOT && variant != W4A16_VARIANT_MFMA)
     return W4A16_ERR_BAD_VARIANT;

@@ -100,4 +100,12 @@ hipError_t launch_argmax_final(const int2* partial, int64_t nparts, int T, int32
 // Upper bound of the workgroups any plan uses for n_out rows (sizes the argmax workspace).
 int64_t max_workgroups(int64_t n_out);
 
+// Verify epilogue (w4a16_epilogue.hip).  The top-k workspace holds
+// T * topk_chunks(n) * k candidate keys of 8 bytes.
+int64_t topk_chunks(int64_t n);
+hipError_t launch_topk(const float* scores, int64_t n, int T, const int32_t* row_ids, int k, int32_t* top_ids,
+                       float* top_vals, void* workspace, hipStream_t s);
+hipError_t launch_greedy(const int32_t* target, const int32_t* draft, int n_seq, int rows, int32_t* accepted,
+                         int32_t* tokens, hipStream_t s);
+
 }  // namespace w4a16

@@ -194,3 +194,28 @@ def test_batch_plan_layouts(lib):
     assert plan(lib, [Problem(A, A, A, A, 64, 256, 2, 0)]) == SHAPE         # unknown layout
     assert plan(lib, [Problem(A, A, A, A, 64, 256, 1, 5)]) == SHAPE         # reserved must be 0
     assert plan(lib, [Problem(A + 8, None, A, A, 64, 256, 1, 0)]) == ALIGN  # tiled buffer 16-byte aligned
+
+
+def test_epilogue_arguments_rejected_on_the_host(lib):
+    vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_size_t
+    lib.w4a16_topk_workspace_bytes.argtypes = [i64, i32, i32]
+    lib.w4a16_topk_workspace_bytes.restype = sz
+    lib.w4a16_topk.argtypes = [vp, i64, i32, vp, i32, vp, vp, vp, sz, vp]
+    lib.w4a16_topk.restype = i32
+    lib.w4a16_greedy_accept.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    lib.w4a16_greedy_accept.restype = i32
+    wsb = lib.w4a16_topk_workspace_bytes
+    assert wsb(248320, 4, 32) == 4 * 122 * 32 * 8      # 2048 scores per first-stage chunk
+    assert wsb(1, 1, 1) == 8
+    assert wsb(0, 1, 1) == 0 and wsb(10, 17, 1) == 0 and wsb(10, 1, 33) == 0 and wsb(10, 1, 0) == 0
+    need = wsb(1000, 2, 8)
+    tk = lambda s=A, n=1000, T=2, ids=None, k=8, ti=A, tv=A, ws=A, b=need: \
+        lib.w4a16_topk(s, n, T, ids, k, ti, tv, ws, b, None)
+    assert tk(s=None) == NULLP and tk(ti=None) == NULLP
+    assert tk(n=0) == SHAPE and tk(T=0) == SHAPE and tk(T=17) == SHAPE and tk(k=0) == SHAPE and tk(k=33) == SHAPE
+    assert tk(s=A + 2) == ALIGN and tk(ids=A + 1) == ALIGN and tk(ti=A + 2) == ALIGN
+    assert tk(ws=None) == WS and tk(b=need - 1) == WS and tk(ws=A + 8) == WS
+    ga = lambda t=A, d=A, S=4, R=4, acc=A, tok=A: lib.w4a16_greedy_accept(t, d, S, R, acc, tok, None)
+    assert ga(t=None) == NULLP and ga(acc=None) == NULLP and ga(d=None) == NULLP
+    assert ga(S=0) == SHAPE and ga(R=0) == SHAPE and ga(R=17) == SHAPE
+    assert ga(t=A + 2) == ALIGN and ga(tok=A + 1) == ALIGN

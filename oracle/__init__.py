@@ -34,6 +34,8 @@ def _load():
         lib.oracle_argmax.argtypes = [vp, vp, i64, i32, vp, vp, vp]
         lib.oracle_topk.argtypes = [vp, vp, i64, i32, i32, vp, vp]
         lib.oracle_greedy_accept.argtypes = [vp, vp, i32, i32, vp, vp]
+        lib.oracle_draft_union.argtypes = [vp, i64, vp, i64, i64, vp]
+        lib.oracle_draft_union.restype = i64
         _lib = lib
     return _lib
 
@@ -143,3 +145,14 @@ def greedy_accept(target, draft, n_seq: int, rows: int):
     tok = np.empty((n_seq, rows), np.int32)
     _load().oracle_greedy_accept(tp, dp if draft.size else None, n_seq, rows, acc.ctypes.data, tok.ctypes.data)
     return acc, tok
+
+
+def draft_union(base, seq, n_rows: int):
+    """(ids of n_base + n_seq slots, union length): the base list, then the
+    in-range sequence ids not seen before in order of first appearance; -1 after."""
+    base, bp = _c(base, np.int32)
+    seq, sp = _c(seq, np.int32)
+    out = np.empty(base.size + seq.size, np.int32)
+    m = _load().oracle_draft_union(bp if base.size else None, base.size, sp if seq.size else None, seq.size, n_rows,
+                                   out.ctypes.data)
+    return out, int(m)

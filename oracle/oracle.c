@@ -273,3 +273,31 @@ void oracle_greedy_accept(const int32_t* target, const int32_t* draft, int n_seq
     for (int r = 0; r < rows; ++r) tokens[s * rows + r] = r <= a ? target[s * rows + r] : -1;
   }
 }
+
+/* Draft-head id list with the sequence's tokens.  OpenJet engine page ("How
+ * it gets its speed"): the draft lm_head is restricted to the 32,768 most
+ * frequent tokens plus the tokens of the current sequence missing from that
+ * list, added on the fly; verification still uses the full vocabulary.
+ * Definition used here: the base list as given, then every id of seq in
+ * order of first appearance that lies in [0, n_rows) and is neither in the
+ * base list nor already added.  out has n_base + n_seq slots; the slots
+ * after the union are -1.  Returns the length of the union. */
+int64_t oracle_draft_union(const int32_t* base, int64_t n_base, const int32_t* seq, int64_t n_seq, int64_t n_rows,
+                           int32_t* out) {
+  unsigned char* seen = (unsigned char*)calloc((size_t)(n_rows > 0 ? n_rows : 1), 1);
+  if (!seen) return -1;
+  int64_t m = 0;
+  for (int64_t i = 0; i < n_base; ++i) {
+    out[m++] = base[i];
+    if (base[i] >= 0 && base[i] < n_rows) seen[base[i]] = 1;
+  }
+  for (int64_t i = 0; i < n_seq; ++i) {
+    int32_t id = seq[i];
+    if (id < 0 || id >= n_rows || seen[id]) continue;
+    seen[id] = 1;
+    out[m++] = id;
+  }
+  for (int64_t i = m; i < n_base + n_seq; ++i) out[i] = -1;
+  free(seen);
+  return m;
+}

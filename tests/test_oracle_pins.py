@@ -404,3 +404,28 @@ def test_planted_epilogue_mistakes_are_caught():
     t, d = np.array(case["target"]), np.array(case["draft"])
     off_by_one = int(np.argmin(np.append(t[:-1] == d, False))) + 1
     assert off_by_one == g["off_by_one_would_give_accepted_for_case_2"] != case["accepted"]
+
+
+def test_draft_union_hand_example():
+    g = load("verify_epilogue.json")["draft_union"]
+    ids, m = oracle.draft_union(np.array(g["base"], np.int32), np.array(g["seq"], np.int32), g["n_rows"])
+    assert ids.tolist() == g["ids"] and m == g["length"]
+
+
+def test_draft_union_properties():
+    """Set equality with base | valid seq, no repeats among the added ids, base
+    kept verbatim, added ids in order of first appearance, -1 padding."""
+    rng = np.random.default_rng(15)
+    for _ in range(200):
+        n_rows = int(rng.integers(1, 60))
+        base = rng.permutation(n_rows)[:int(rng.integers(0, n_rows + 1))].astype(np.int32)
+        seq = rng.integers(-3, n_rows + 3, size=int(rng.integers(0, 40))).astype(np.int32)
+        ids, m = oracle.draft_union(base, seq, n_rows)
+        assert ids.size == base.size + seq.size and np.all(ids[m:] == -1)
+        assert ids[:base.size].tolist() == base.tolist()
+        added = ids[base.size:m]
+        valid = [int(v) for v in seq if 0 <= v < n_rows]
+        assert set(ids[:m].tolist()) == set(base.tolist()) | set(valid)
+        assert len(set(added.tolist())) == added.size and not set(added.tolist()) & set(base.tolist())
+        first = [valid.index(int(v)) for v in added]
+        assert first == sorted(first)

@@ -214,7 +214,7 @@ def main():
     # ---- verify epilogue on the head's scores: top-32 per row, greedy acceptance ----
     epilogue = verify_epilogue(torch, w4a16, head_y, T, stream)
     log(f"verify epilogue at T={T}: top-32 of {hn} scores {epilogue['topk32_us']:.1f} us, "
-        f"greedy acceptance {epilogue['greedy_us']:.1f} us")
+        f"greedy acceptance {epilogue['greedy_us']:.1f} us, draft-head id list {epilogue['draft_union_us']:.1f} us")
 
     # ---- the same step as 257 separate launches, replayed from a HIP graph ----
     graph_pass = None
@@ -275,16 +275,21 @@ def main():
 
 
 def verify_epilogue(torch, w4a16, head_y, T, stream, reps=50):
-    """Per-row top-32 of the lm_head scores (two launches) and greedy
-    acceptance of T - 1 drafts (one launch), timed on the launch stream."""
+    """Per-row top-32 of the lm_head scores (two launches), greedy acceptance
+    of T - 1 drafts (one launch) and the draft-head id list of 32,768 base
+    ids plus 4,096 sequence ids (one launch), timed on the launch stream."""
     k = 32
-    ws = torch.empty(w4a16.topk_workspace_bytes(head_y.shape[1], T, k), dtype=torch.uint8, device="cuda")
+    n_rows = head_y.shape[1]
+    ws = torch.empty(w4a16.topk_workspace_bytes(n_rows, T, k), dtype=torch.uint8, device="cuda")
     target = torch.zeros(T, dtype=torch.int32, device="cuda")
     draft = torch.zeros(max(T - 1, 1), dtype=torch.int32, device="cuda")
+    base = to_dev(synth.distinct_ids(synth.RID_DRAFT, synth.DRAFT_IDS, n_rows), torch)
+    seq = to_dev(np.random.default_rng(0).integers(0, n_rows, 4096).astype(np.int32), torch)
     out = {}
     for name, fn in (("topk32_us", lambda: w4a16.topk(head_y, k, workspace=ws, stream=stream)),
                      ("greedy_us", lambda: w4a16.greedy_accept(target, draft[:T - 1] if T > 1 else None, 1, T,
-                                                               stream=stream))):
+                                                               stream=stream)),
+                     ("draft_union_us", lambda: w4a16.draft_union(base, seq, n_rows, stream=stream))):
         for _ in range(5):
             fn()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)

@@ -261,6 +261,29 @@ w4a16_status w4a16_topk(const float* scores, int64_t n, int32_t T, const int32_t
 w4a16_status w4a16_greedy_accept(const int32_t* target_ids, const int32_t* draft_ids, int32_t n_seq, int32_t rows,
                                  int32_t* n_accepted, int32_t* tokens, hipStream_t stream);
 
+/*
+ * Draft-head id list with the sequence's tokens (OpenJet engine page, "How
+ * it gets its speed": the draft lm_head covers the 32,768 most frequent
+ * tokens plus the tokens of the current sequence missing from them, added
+ * on the fly; verification still scores the full vocabulary).  Writes into
+ * union_ids [n_base + n_seq]: base_ids verbatim, then every id of seq_ids in
+ * order of first appearance that lies in [0, n_rows) and is neither in the
+ * base list nor already added, then -1 in the remaining slots; *n_union (one
+ * int32 on the device) receives the length of the list.  Built for one
+ * gathered pass of known size: w4a16_head_gather with row_ids = union_ids
+ * and n_ids = n_base + n_seq scores the list, the -1 slots giving NaN rows
+ * that no argmax or top-k counts (their loads all hit one cached row).
+ *   base_ids int32 [n_base] device (NULL when n_base = 0), taken as given;
+ *   seq_ids int32 [n_seq] device (NULL when n_seq = 0), any values;
+ *   0 <= n_seq <= W4A16_MAX_SEQ_IDS, 0 <= n_base, 1 <= n_base + n_seq <= 2^31-1,
+ *   1 <= n_rows <= W4A16_MAX_UNION_VOCAB.
+ */
+#define W4A16_MAX_SEQ_IDS 4096
+#define W4A16_MAX_UNION_VOCAB 524288
+
+w4a16_status w4a16_draft_union(const int32_t* base_ids, int32_t n_base, const int32_t* seq_ids, int32_t n_seq,
+                               int64_t n_rows, int32_t* union_ids, int32_t* n_union, hipStream_t stream);
+
 /* Selects the kernel variant for subsequent calls in this process (initially
  * taken from the environment variable W4A16_VARIANT = auto|dot|mfma). */
 w4a16_status w4a16_set_variant(int32_t variant);

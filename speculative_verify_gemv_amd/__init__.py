@@ -74,6 +74,8 @@ def load_library():
         lib.w4a16_topk.restype = i32
         lib.w4a16_greedy_accept.argtypes = [vp, vp, i32, i32, vp, vp, vp]
         lib.w4a16_greedy_accept.restype = i32
+        lib.w4a16_draft_union.argtypes = [vp, i32, vp, i32, i64, vp, vp, vp]
+        lib.w4a16_draft_union.restype = i32
         _lib = lib
     return _lib
 
@@ -344,3 +346,22 @@ def greedy_accept(target_ids: torch.Tensor, draft_ids: torch.Tensor | None, n_se
     if st:
         raise W4A16Error(st, "w4a16_greedy_accept")
     return acc, tok
+
+
+def draft_union(base_ids: torch.Tensor | None, seq_ids: torch.Tensor | None, n_rows: int, stream=None):
+    """Draft-head id list on the device: base ids, then the sequence's new
+    in-range ids in order of first appearance, then -1.  Returns (ids
+    [n_base + n_seq] int32, length [1] int32), both on the device."""
+    for t, what in ((base_ids, "base_ids"), (seq_ids, "seq_ids")):
+        if t is not None and (t.dtype != torch.int32 or t.dim() != 1 or not (t.is_cuda and t.is_contiguous())):
+            raise ValueError(f"{what} must be a contiguous CUDA int32 vector")
+    nb = 0 if base_ids is None else base_ids.numel()
+    ns = 0 if seq_ids is None else seq_ids.numel()
+    device = (base_ids if base_ids is not None else seq_ids).device
+    out = torch.empty(nb + ns, dtype=torch.int32, device=device)
+    length = torch.empty(1, dtype=torch.int32, device=device)
+    st = load_library().w4a16_draft_union(_ptr(base_ids) if nb else None, nb, _ptr(seq_ids) if ns else None, ns,
+                                          n_rows, out.data_ptr(), length.data_ptr(), _stream(stream))
+    if st:
+        raise W4A16Error(st, "w4a16_draft_union")
+    return out, length

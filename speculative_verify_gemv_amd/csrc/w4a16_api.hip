@@ -378,6 +378,23 @@ w4a16_status w4a16_greedy_accept(const int32_t* target_ids, const int32_t* draft
              : W4A16_ERR_HIP;
 }
 
+w4a16_status w4a16_draft_union(const int32_t* base_ids, int32_t n_base, const int32_t* seq_ids, int32_t n_seq,
+                               int64_t n_rows, int32_t* union_ids, int32_t* n_union, hipStream_t stream) {
+  static_assert(W4A16_MAX_SEQ_IDS == w4a16::kMaxSeqIds && W4A16_MAX_UNION_VOCAB == w4a16::kMaxUnionVocab,
+                "limits of the union kernel");
+  if (!union_ids || !n_union || (n_base > 0 && !base_ids) || (n_seq > 0 && !seq_ids)) return W4A16_ERR_NULL_POINTER;
+  if (n_base < 0 || n_seq < 0 || n_seq > W4A16_MAX_SEQ_IDS || (int64_t)n_base + n_seq < 1 ||
+      (int64_t)n_base + n_seq > kMaxRows || n_rows < 1 || n_rows > W4A16_MAX_UNION_VOCAB)
+    return W4A16_ERR_BAD_SHAPE;
+  if (!aligned(base_ids, 4) || !aligned(seq_ids, 4) || !aligned(union_ids, 4) || !aligned(n_union, 4))
+    return W4A16_ERR_MISALIGNED;
+  if (w4a16_status s = check_device()) return s;
+  return w4a16::launch_draft_union(base_ids, n_base, seq_ids, n_seq, (int)n_rows, union_ids, n_union, stream) ==
+                 hipSuccess
+             ? W4A16_OK
+             : W4A16_ERR_HIP;
+}
+
 w4a16_status w4a16_set_variant(int32_t variant) {
   if (variant != W4A16_VARIANT_AUTO && variant != W4A16_VARIANT_DOT && variant != W4A16_VARIANT_MFMA)
     return W4A16_ERR_BAD_VARIANT;

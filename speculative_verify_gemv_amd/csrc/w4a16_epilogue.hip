@@ -17,6 +17,14 @@
 // Greedy acceptance.  The same article section: greedy acceptance is an
 // argmax equality over the verify rows; the OpenJet page ("How it works"):
 // the host reads back only the accepted tokens.  One thread per sequence.
+//
+// Draft-head id list.  The OpenJet page ("How it gets its speed"): the draft
+// head covers the 32,768 most frequent tokens plus the tokens of the current
+// sequence missing from them, added on the fly.  One workgroup: the base
+// ids go into a vocabulary bitmap in LDS; the sequence's (id, position)
+// pairs are sorted in LDS so that the first appearance of each id is the
+// first of its run; a prefix count over positions then places the new ids
+// in order of first appearance after the base list.
 #include "w4a16_internal.h"
 
 namespace w4a16 {
@@ -47,18 +55,18 @@ __device__ __forceinline__ void key_decode(u64 key, int32_t& id, float& v) {
   id = (int32_t)(0x7fffffffu - (unsigned)(key & 0xffffffffu));
 }
 
-// Sorts s[0..N) (N a power of two) into descending order with all threads
-// of the workgroup; ends with a barrier.
-template <int N>
-__device__ __forceinline__ void bitonic_desc(u64* s) {
+// Sorts s[0..N) (N a power of two) into descending (DESC) or ascending
+// order with all threads of the workgroup; ends with a barrier.
+template <int N, bool DESC = true>
+__device__ __forceinline__ void bitonic_sort(u64* s) {
   for (int size = 2; size <= N; size <<= 1) {
     for (int stride = size >> 1; stride > 0; stride >>= 1) {
       for (int i = threadIdx.x; i < N / 2; i += blockDim.x) {
         const int lo = 2 * i - (i & (stride - 1));
         const int hi = lo + stride;
-        const bool desc = (lo & size) == 0;
+        const bool desc = ((lo & size) == 0) == DESC;  // this pair's block runs descending
         const u64 a = s[lo], b = s[hi];
-        if ((a < b) == desc) {
+        if (desc ? (a < b) : (a > b)) {
           s[lo] = b;
           s[hi] = a;
         }
@@ -84,7 +92,7 @@ __global__ void __launch_bounds__(kChunkThreads) w4a16_topk_chunks(const float* 
     s[i] = key;
   }
   __syncthreads();
-  bitonic_desc<kChunk>(s);
+  bitonic_sort<kChunk>(s);
   for (int j = threadIdx.x; j < k; j += blockDim.x) part[((int64_t)t * nchunks + c) * k + j] = s[j];
 }
 
@@ -103,7 +111,7 @@ __global__ void __launch_bounds__(kMergeThreads) w4a16_topk_merge(const u64* __r
       s[i] = j < m ? cand[j] : 0ull;
     }
     __syncthreads();
-    bitonic_desc<kMerge>(s);
+    bitonic_sort<kMerge>(s);
     if (b + (kMerge - k) >= m) break;
   }
   for (int j = threadIdx.x; j < k; j += blockDim.x) {
@@ -129,6 +137,92 @@ __global__ void __launch_bounds__(64) w4a16_greedy(const int32_t* __restrict__ t
     for (int r = 0; r < rows; ++r) tokens[(int64_t)s * rows + r] = r <= a ? tg[r] : -1;
 }
 
+constexpr int kUnionThreads = 1024;
+
+// LDS of the union kernel: the vocabulary bitmap, then kMaxSeqIds sort keys,
+// then kMaxSeqIds marks (the id a position adds, or -1), then the wave sums.
+__host__ __device__ constexpr int union_keys_offset(int64_t n_rows) {
+  return (int)((((n_rows + 31) / 32) * 4 + 15) / 16 * 16);
+}
+__host__ __device__ constexpr int union_lds(int64_t n_rows) {
+  return union_keys_offset(n_rows) + kMaxSeqIds * 8 + kMaxSeqIds * 4 + (kUnionThreads / 64 + 1) * 4;
+}
+
+__global__ void __launch_bounds__(kUnionThreads) w4a16_draft_union(const int32_t* __restrict__ base, int n_base,
+                                                                   const int32_t* __restrict__ seq, int n_seq,
+                                                                   int n_rows, int32_t* __restrict__ out,
+                                                                   int32_t* __restrict__ n_out) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  unsigned* bits = reinterpret_cast<unsigned*>(smem);
+  u64* keys = reinterpret_cast<u64*>(smem + union_keys_offset(n_rows));
+  int32_t* mark = reinterpret_cast<int32_t*>(keys + kMaxSeqIds);
+  int* wsum = reinterpret_cast<int*>(mark + kMaxSeqIds);
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int words = (n_rows + 31) >> 5;
+  for (int i = tid; i < words; i += nt) bits[i] = 0u;
+  __syncthreads();
+  // the base list, verbatim, and its in-range ids in the bitmap
+  for (int i = tid; i < n_base; i += nt) {
+    const int32_t id = base[i];
+    out[i] = id;
+    if (id >= 0 && id < n_rows) atomicOr(&bits[id >> 5], 1u << (id & 31));
+  }
+  // (id, position) of every in-range sequence id; the rest sort to the end
+  for (int i = tid; i < kMaxSeqIds; i += nt) {
+    u64 key = ~0ull;
+    if (i < n_seq) {
+      const int32_t id = seq[i];
+      if (id >= 0 && id < n_rows) key = ((u64)(unsigned)id << 32) | (unsigned)i;
+    }
+    keys[i] = key;
+    mark[i] = -1;
+  }
+  __syncthreads();
+  bitonic_sort<kMaxSeqIds, false>(keys);
+  // the first position of each id adds it unless the base list has it
+  for (int j = tid; j < kMaxSeqIds; j += nt) {
+    const u64 key = keys[j];
+    if (key == ~0ull) continue;
+    const unsigned id = (unsigned)(key >> 32);
+    const bool first = j == 0 || (unsigned)(keys[j - 1] >> 32) != id;
+    if (first && !((bits[id >> 5] >> (id & 31)) & 1u)) mark[(unsigned)(key & 0xffffffffu)] = (int32_t)id;
+  }
+  __syncthreads();
+  // prefix count of the adding positions, in position order
+  constexpr int kPer = kMaxSeqIds / kUnionThreads;
+  int c = 0;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) c += mark[tid * kPer + q] >= 0 ? 1 : 0;
+  const int lane = tid & 63, wave = tid >> 6;
+  int incl = c;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int v = __shfl_up(incl, off);
+    if (lane >= off) incl += v;
+  }
+  if (lane == 63) wsum[wave] = incl;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int w = 0; w < nt / 64; ++w) {
+      const int v = wsum[w];
+      wsum[w] = run;
+      run += v;
+    }
+    wsum[nt / 64] = run;
+  }
+  __syncthreads();
+  int at = n_base + wsum[wave] + incl - c;
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int32_t id = mark[tid * kPer + q];
+    if (id >= 0) out[at++] = id;
+  }
+  const int total = n_base + wsum[nt / 64];
+  for (int i = total + tid; i < n_base + n_seq; i += nt) out[i] = -1;
+  if (tid == 0) *n_out = total;
+}
+
 }  // namespace
 
 int64_t topk_chunks(int64_t n) { return (n + kChunk - 1) / kChunk; }
@@ -149,6 +243,23 @@ hipError_t launch_greedy(const int32_t* target, const int32_t* draft, int n_seq,
                          int32_t* tokens, hipStream_t s) {
   hipLaunchKernelGGL(w4a16_greedy, dim3((unsigned)((n_seq + 63) / 64)), dim3(64), 0, s, target, draft, n_seq, rows,
                      accepted, tokens);
+  return hipGetLastError();
+}
+
+}  // namespace w4a16
+
+namespace w4a16 {
+
+hipError_t launch_draft_union(const int32_t* base, int n_base, const int32_t* seq, int n_seq, int n_rows,
+                              int32_t* out, int32_t* n_out, hipStream_t s) {
+  const int lds = union_lds(n_rows);
+  if (lds > 65536) {  // above 64 KB of dynamic LDS the kernel has to opt in
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&w4a16_draft_union),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL(w4a16_draft_union, dim3(1), dim3(kUnionThreads), lds, s, base, n_base, seq, n_seq, n_rows, out,
+                     n_out);
   return hipGetLastError();
 }
 

@@ -107,5 +107,11 @@ hipError_t launch_topk(const float* scores, int64_t n, int T, const int32_t* row
                        float* top_vals, void* workspace, hipStream_t s);
 hipError_t launch_greedy(const int32_t* target, const int32_t* draft, int n_seq, int rows, int32_t* accepted,
                          int32_t* tokens, hipStream_t s);
+// Draft-head id list: at most kMaxSeqIds sequence ids, vocabularies of at
+// most kMaxUnionVocab ids (its bitmap lives in LDS).
+constexpr int kMaxSeqIds = 4096;
+constexpr int64_t kMaxUnionVocab = 524288;
+hipError_t launch_draft_union(const int32_t* base, int n_base, const int32_t* seq, int n_seq, int n_rows,
+                              int32_t* out, int32_t* n_out, hipStream_t s);
 
 }  // namespace w4a16

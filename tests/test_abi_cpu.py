@@ -219,3 +219,14 @@ def test_epilogue_arguments_rejected_on_the_host(lib):
     assert ga(t=None) == NULLP and ga(acc=None) == NULLP and ga(d=None) == NULLP
     assert ga(S=0) == SHAPE and ga(R=0) == SHAPE and ga(R=17) == SHAPE
     assert ga(t=A + 2) == ALIGN and ga(tok=A + 1) == ALIGN
+
+
+def test_draft_union_arguments_rejected_on_the_host(lib):
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    lib.w4a16_draft_union.argtypes = [vp, i32, vp, i32, i64, vp, vp, vp]
+    lib.w4a16_draft_union.restype = i32
+    du = lambda b=A, nb=32768, s=A, ns=100, n=248320, o=A, m=A: lib.w4a16_draft_union(b, nb, s, ns, n, o, m, None)
+    assert du(o=None) == NULLP and du(m=None) == NULLP and du(b=None) == NULLP and du(s=None) == NULLP
+    assert du(nb=-1) == SHAPE and du(ns=4097) == SHAPE and du(nb=0, ns=0) == SHAPE
+    assert du(n=0) == SHAPE and du(n=524289) == SHAPE
+    assert du(b=A + 2) == ALIGN and du(o=A + 1) == ALIGN and du(m=A + 2) == ALIGN

@@ -133,3 +133,49 @@ def test_verify_cycle_four_sequences_of_four_rows(w4):
     ref_acc, ref_tok = oracle.greedy_accept(own_id, draft.ravel(), S, L)
     assert np.array_equal(host(acc), ref_acc) and np.array_equal(host(tok), ref_tok)
     assert host(acc).tolist() == [0, 1, 2, 3]
+
+
+@pytest.mark.parametrize("n_base,n_seq,n_rows", [(32768, 4096, 248320), (0, 10, 100), (5, 0, 100), (1, 4096, 524288),
+                                                 (1000, 1, 1000), (3, 4000, 17)])
+def test_draft_union_matches_oracle(w4, n_base, n_seq, n_rows):
+    say(f"draft union base={n_base} seq={n_seq} vocab={n_rows}")
+    rng = np.random.default_rng(n_base + n_seq)
+    base = synth.distinct_ids(synth.RID_DRAFT + 1, n_base, n_rows) if n_base else np.empty(0, np.int32)
+    pick = rng.random(n_seq)
+    seq = np.where(pick < 0.4, rng.integers(0, n_rows, n_seq),                           # anywhere
+                   np.where(pick < 0.7, base[rng.integers(0, max(n_base, 1), n_seq)] if n_base
+                            else rng.integers(0, n_rows, n_seq),                          # in the base list
+                            rng.integers(-5, n_rows + 5, n_seq))).astype(np.int32)        # some out of range
+    if n_seq > 8:
+        seq[n_seq // 2:n_seq // 2 + 4] = seq[1]                                           # repeats
+    ids, length = w4.draft_union(dev(base) if n_base else None, dev(seq) if n_seq else None, n_rows)
+    ref, m = oracle.draft_union(base, seq, n_rows)
+    assert np.array_equal(host(ids), ref) and int(host(length)[0]) == m
+
+
+def test_draft_head_with_sequence_tokens(w4):
+    """Union list -> one gathered pass over the full head (capacity n_base +
+    n_seq rows): the listed rows match the oracle, the -1 slots are NaN, and
+    argmax and top-k count only listed rows."""
+    from test_gpu_parity import lm_head
+
+    T, k = 4, 32
+    p, s, pd, sd = lm_head()
+    n_rows, K = synth.LM_HEAD
+    base = synth.distinct_ids(synth.RID_DRAFT, synth.DRAFT_IDS, n_rows)
+    rng = np.random.default_rng(99)
+    seq = np.concatenate([base[rng.integers(0, base.size, 300)], rng.integers(0, n_rows, 700)]).astype(np.int32)
+    ids_d, length = w4.draft_union(dev(base), dev(seq), n_rows)
+    ids = host(ids_d)
+    m = int(host(length)[0])
+    x = synth.activations(synth.TID_LM_HEAD + 55, T, K)
+    y, am, av = w4.head_gather_tiled(w4.repack_tiled(pd, sd), dev(x), row_ids=ids_d, scores=True, argmax=True)
+    y, am = host(y), host(am)
+    assert np.all(np.isnan(y[:, m:])) and not np.any(np.isnan(y[:, :m]))
+    rows = np.concatenate([np.arange(0, m, 97), np.arange(synth.DRAFT_IDS - 3, m)]).astype(np.int64)
+    y_ref, a_ref = oracle.gather(ids[rows], p, s, x)
+    from gpu_util import assert_parity
+    assert_parity(y[:, rows], y_ref, a_ref, "draft head with sequence tokens")
+    own, _, _ = oracle.argmax(y.astype(np.float64), ids)
+    assert np.array_equal(am, own)
+    check_topk_exact(w4, y, k, ids, "union top-k")

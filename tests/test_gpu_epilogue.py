@@ -62,6 +62,22 @@ def test_topk_gathered_ids_negative_ids_and_all_nan(w4):
     assert np.all(got_id[2] == -1) and np.all(np.isnan(got_val[2]))
 
 
+def test_topk_fallback_paths(w4):
+    """Both sort fallbacks: duplicated (id, score) keys fill a chunk's
+    candidate list (chunk sort); ascending scores put every top chunk list
+    above the bound (row merge by sorting)."""
+    n = 5000
+    y = np.full((2, n), 1.5, np.float32)
+    ids = np.full(n, 77, np.int32)
+    ids[4321] = 12                                        # one lower id with the same score
+    check_topk_exact(w4, y, 32, ids, "duplicated keys")
+    y = np.tile(np.arange(100_000, dtype=np.float32), (3, 1))
+    y[1] *= -1.0                                          # and descending
+    y[2, ::7] = np.nan
+    check_topk_exact(w4, y, 32, what="monotone scores")
+    check_topk_exact(w4, y, 5, what="monotone scores k=5")
+
+
 def test_topk_of_the_lm_head_t4(w4):
     """k = 32 of the full 248,320-row head: exact on the GPU's scores, entry 0
     equal to the head kernel's argmax, and stable against the oracle's scores."""

@@ -13,7 +13,9 @@ cycles/s, the grouped body kernel's achieved bandwidth against the 8 TB/s
 HBM peak (roofline, timed with HIP events on the launch stream), the body
 pass at T = 1, 4, 8 and 16 in both layouts (tiled and the pages' row-major one),
 the same step as 257 separate launches replayed from a captured HIP graph,
-and the CPU oracle's rate on a bounded sample.
+single launches of each workload shape (the small matrix, every projection
+at T = 1, 4, 8, the lm_head with argmax, the draft head), the verify
+epilogue, and the CPU oracle's rate on a bounded sample.
 
 --pmc-pass runs one untimed body pass and one lm_head call after a 1 GiB
 device copy (the calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE).
@@ -56,6 +58,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-per-t", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
+    ap.add_argument("--no-singles", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true", help="one untimed pass for counter collection")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     return ap.parse_args()
@@ -211,6 +214,11 @@ def main():
                     f"({100 * g / PEAK_GBPS:.1f}% of 8 TB/s)")
                 del b
 
+    # ---- single launches of each workload shape (configs of the task's workload list) ----
+    singles = None
+    if not args.no_singles:
+        singles = single_launches(torch, w4a16, weights, head_p, head_s, head_tw, stream)
+
     # ---- verify epilogue on the head's scores: top-32 per row, greedy acceptance ----
     epilogue = verify_epilogue(torch, w4a16, head_y, T, stream)
     log(f"verify epilogue at T={T}: top-32 of {hn} scores {epilogue['topk32_us']:.1f} us, "
@@ -258,6 +266,7 @@ def main():
         "per_T_body_pass_row_major": per_t_rm,
         "graph_257_launches": graph_pass,
         "verify_epilogue": epilogue,
+        "single_launches": singles,
         "roofline": {
             "kernel": "grouped body pass (64 x 4 projections, one launch, tiled layout)",
             "bound": "hbm",
@@ -272,6 +281,85 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def time_rotating(torch, fns, stream, rounds=4):
+    """Average µs per call of fns called round-robin (distinct weight copies,
+    so that the 256 MB Infinity Cache cannot serve a repeat), after one
+    untimed round per copy and enough calls to leave the clock ramp."""
+    n = len(fns)
+    warm = max(3 * n, 30)
+    for i in range(warm):
+        fns[i % n]()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    reps = max(rounds * n, 40)
+    e0.record(stream)
+    for i in range(reps):
+        fns[i % n]()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return 1000.0 * e0.elapsed_time(e1) / reps
+
+
+def single_launches(torch, w4a16, weights, head_p, head_s, head_tw, stream):
+    """One launch per call, back to back on one stream, for each single-matmul
+    workload: the 1024 x 1024 matrix (T = 1), each 27B-class projection at
+    T = 1, 4, 8 (tiled, copies from all 64 layers rotated), the lm_head at
+    T = 1 and 4 with argmax, and the 32,768-row draft head at T = 1, gathered
+    from the head and repacked once as its own matrix."""
+    out = {}
+    # small matrix: too small for any cache effect to matter; its figure is latency
+    p, s = synth.weight(synth.TID_SMALL, *synth.SMALL)
+    tw = w4a16.repack_tiled(to_dev(p, torch), to_dev(s, torch))
+    x = to_dev(synth.activations(synth.TID_SMALL, 1, synth.SMALL[1]), torch)
+    y = torch.empty((1, synth.SMALL[0]), dtype=torch.float32, device="cuda")
+    us = time_rotating(torch, [lambda: w4a16.matmul_tiled(tw, x, out=y, stream=stream)], stream)
+    out["small_1024x1024_T1"] = {"us": round(us, 2),
+                                 "weight_GBps": round(metrics.gbps(metrics.weight_bytes(*synth.SMALL), us / 1000), 1)}
+    for proj in synth.PROJ_ORDER:
+        N, K = synth.PROJECTIONS[proj]
+        tws = [w[4] for w in weights if w[0] == proj]
+        wb = metrics.weight_bytes(N, K)
+        for T in (1, 4, 8):
+            x = to_dev(synth.activations(synth.tid_layer(0, proj), T, K), torch)
+            y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+            fns = [lambda tw=tw: w4a16.matmul_tiled(tw, x, out=y, stream=stream) for tw in tws]
+            us = time_rotating(torch, fns, stream)
+            out[f"{proj}_T{T}"] = {"us": round(us, 2), "weight_GBps": round(metrics.gbps(wb, us / 1000), 1)}
+    hn, hk = synth.LM_HEAD
+    head_tw2 = w4a16.repack_tiled(head_p, head_s)  # a second copy: 1.3 GB rotated
+    for T in (1, 4):
+        x = to_dev(synth.activations(synth.TID_LM_HEAD + 1, T, hk), torch)
+        y = torch.empty((T, hn), dtype=torch.float32, device="cuda")
+        ws = torch.empty(w4a16.workspace_bytes(hn, T), dtype=torch.uint8, device="cuda")
+        fns = [lambda t=t: w4a16.head_gather_tiled(t, x, scores=True, argmax=True, out=y, workspace=ws, stream=stream)
+               for t in (head_tw, head_tw2)]
+        us = time_rotating(torch, fns, stream)
+        out[f"lm_head_argmax_T{T}"] = {"us": round(us, 2),
+                                       "weight_GBps": round(metrics.gbps(metrics.weight_bytes(hn, hk), us / 1000), 1)}
+    ids = [to_dev(synth.distinct_ids(synth.RID_DRAFT + i, synth.DRAFT_IDS, hn), torch) for i in range(4)]
+    x = to_dev(synth.activations(synth.TID_LM_HEAD + 2, 1, hk), torch)
+    y = torch.empty((1, synth.DRAFT_IDS), dtype=torch.float32, device="cuda")
+    ws = torch.empty(w4a16.workspace_bytes(synth.DRAFT_IDS, 1), dtype=torch.uint8, device="cuda")
+    fns = [lambda t=t, r=r: w4a16.head_gather_tiled(t, x, row_ids=r, scores=True, argmax=True, out=y, workspace=ws,
+                                                    stream=stream) for t in (head_tw, head_tw2) for r in ids]
+    us = time_rotating(torch, fns, stream)
+    out["draft_head_32768_argmax_T1"] = {"us": round(us, 2), "weight_GBps": round(
+        metrics.gbps(metrics.weight_bytes(synth.DRAFT_IDS, hk), us / 1000), 1)}
+    # the same draft head repacked once into its own tiled matrix (ascending
+    # ids, so the argmax position indexes them); 12 copies rotated (1 GB)
+    sid = [torch.sort(r)[0] for r in ids[:1]]
+    compact = [w4a16.repack_tiled_rows(head_p, head_s, sid[0]) for _ in range(12)]
+    fns = [lambda t=t: w4a16.head_gather_tiled(t, x, scores=True, argmax=True, out=y, workspace=ws, stream=stream)
+           for t in compact]
+    us = time_rotating(torch, fns, stream)
+    out["draft_head_compact_32768_argmax_T1"] = {"us": round(us, 2), "weight_GBps": round(
+        metrics.gbps(metrics.weight_bytes(synth.DRAFT_IDS, hk), us / 1000), 1)}
+    del head_tw2, compact
+    for k, v in out.items():
+        log(f"single launch {k}: {v['us']:.1f} us, {v['weight_GBps']:.0f} GB/s")
+    return out
 
 
 def verify_epilogue(torch, w4a16, head_y, T, stream, reps=50):

@@ -157,6 +157,25 @@ size_t w4a16_tiled_bytes(int64_t N, int64_t K);
 w4a16_status w4a16_repack_tiled(const uint8_t* packed_u4, const uint16_t* scales_bf16, int64_t N, int64_t K,
                                 void* tiled, size_t tiled_bytes, hipStream_t stream);
 
+/*
+ * The tiled layout of a subset of a weight's rows: output row i holds input
+ * row row_ids[i] of packed_u4 [n_rows][K/2] / scales_bf16 [n_rows][K/128].
+ * For a head restricted to a fixed id list (the swift-qwen3.8-rtx3090 page,
+ * "Body, heads and drafter": the draft head is a slice of the lm_head with
+ * rows only for the draft-vocabulary tokens), built once at load: the slice
+ * is then a plain tiled matrix of n_ids rows, read in whole 1 KB blocks
+ * instead of 64-byte pieces of scattered rows.  Scores and argmax of calls on
+ * it are by position i; the vocabulary id is row_ids[i] (with row_ids in
+ * ascending order, the lowest-position tie rule is the lowest-id rule).
+ *   row_ids  int32 [n_ids] device, each in [0, n_rows) (an id outside gives
+ *            an all-zero row, i.e. scores of 0); duplicates allowed.
+ *   tiled    device, 16-byte aligned, >= w4a16_tiled_bytes(n_ids, K) bytes.
+ *   Shapes: 1 <= n_rows, n_ids <= 2^31-1; K as for w4a16_matmul.
+ */
+w4a16_status w4a16_repack_tiled_rows(const uint8_t* packed_u4, const uint16_t* scales_bf16, int64_t n_rows, int64_t K,
+                                     const int32_t* row_ids, int64_t n_ids, void* tiled, size_t tiled_bytes,
+                                     hipStream_t stream);
+
 /* w4a16_matmul and w4a16_head_gather on a tiled weight (`tiled` 16-byte
  * aligned, written by w4a16_repack_tiled for the same N / n_rows and K).
  * Same results within the tolerance; always the matrix-core kernels. */

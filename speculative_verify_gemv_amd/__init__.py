@@ -64,6 +64,8 @@ def load_library():
         lib.w4a16_tiled_bytes.restype = sz
         lib.w4a16_repack_tiled.argtypes = [vp, vp, i64, i64, vp, sz, vp]
         lib.w4a16_repack_tiled.restype = i32
+        lib.w4a16_repack_tiled_rows.argtypes = [vp, vp, i64, i64, vp, i64, vp, sz, vp]
+        lib.w4a16_repack_tiled_rows.restype = i32
         lib.w4a16_matmul_tiled.argtypes = [vp, vp, vp, i64, i64, i32, vp]
         lib.w4a16_matmul_tiled.restype = i32
         lib.w4a16_head_gather_tiled.argtypes = [vp, i64, vp, i64, vp, i64, i32, vp, vp, vp, vp, sz, vp]
@@ -219,6 +221,22 @@ def repack_tiled(packed: torch.Tensor, scales: torch.Tensor, stream=None) -> Til
     if s:
         raise W4A16Error(s, "w4a16_repack_tiled")
     return TiledWeight(data, N, K)
+
+
+def repack_tiled_rows(packed: torch.Tensor, scales: torch.Tensor, row_ids: torch.Tensor, stream=None) -> TiledWeight:
+    """Tiled-layout copy of rows row_ids of a row-major weight (a fixed-list
+    head slice); row i of the result is input row row_ids[i]."""
+    n_rows, K = _check_weight(packed, scales)
+    if row_ids.dtype != torch.int32 or row_ids.dim() != 1 or not (row_ids.is_cuda and row_ids.is_contiguous()):
+        raise ValueError("row_ids must be a contiguous CUDA int32 vector")
+    n = row_ids.shape[0]
+    nbytes = tiled_bytes(n, K)
+    data = torch.empty(nbytes, dtype=torch.uint8, device=packed.device)
+    s = load_library().w4a16_repack_tiled_rows(_ptr(packed), _ptr(scales), n_rows, K, _ptr(row_ids), n, _ptr(data),
+                                               nbytes, _stream(stream))
+    if s:
+        raise W4A16Error(s, "w4a16_repack_tiled_rows")
+    return TiledWeight(data, n, K)
 
 
 def matmul_tiled(w: TiledWeight, x: torch.Tensor, out: torch.Tensor | None = None, stream=None) -> torch.Tensor:

@@ -251,8 +251,24 @@ w4a16_status w4a16_repack_tiled(const uint8_t* packed_u4, const uint16_t* scales
   if (!aligned(packed_u4, 16) || !aligned(scales_bf16, 2) || !aligned(tiled, 16)) return W4A16_ERR_MISALIGNED;
   if (tiled_bytes < w4a16_tiled_bytes(N, K)) return W4A16_ERR_WORKSPACE;
   if (w4a16_status s = check_device()) return s;
-  return w4a16::launch_repack(packed_u4, scales_bf16, N, (int32_t)K, static_cast<uint8_t*>(tiled), stream) ==
-                 hipSuccess
+  return w4a16::launch_repack(packed_u4, scales_bf16, nullptr, N, N, (int32_t)K, static_cast<uint8_t*>(tiled),
+                              stream) == hipSuccess
+             ? W4A16_OK
+             : W4A16_ERR_HIP;
+}
+
+w4a16_status w4a16_repack_tiled_rows(const uint8_t* packed_u4, const uint16_t* scales_bf16, int64_t n_rows, int64_t K,
+                                     const int32_t* row_ids, int64_t n_ids, void* tiled, size_t tiled_bytes,
+                                     hipStream_t stream) {
+  if (!packed_u4 || !scales_bf16 || !row_ids || !tiled) return W4A16_ERR_NULL_POINTER;
+  if (n_rows < 1 || n_rows > kMaxRows || n_ids < 1 || n_ids > kMaxRows) return W4A16_ERR_BAD_SHAPE;
+  if (w4a16_status s = check_kt(K, 1)) return s;
+  if (!aligned(packed_u4, 16) || !aligned(scales_bf16, 2) || !aligned(row_ids, 4) || !aligned(tiled, 16))
+    return W4A16_ERR_MISALIGNED;
+  if (tiled_bytes < w4a16_tiled_bytes(n_ids, K)) return W4A16_ERR_WORKSPACE;
+  if (w4a16_status s = check_device()) return s;
+  return w4a16::launch_repack(packed_u4, scales_bf16, row_ids, n_rows, n_ids, (int32_t)K,
+                              static_cast<uint8_t*>(tiled), stream) == hipSuccess
              ? W4A16_OK
              : W4A16_ERR_HIP;
 }

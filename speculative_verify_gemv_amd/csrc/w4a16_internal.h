@@ -93,8 +93,10 @@ int shared_waves(int T, int64_t K);
 
 hipError_t launch(const GemvArgs& a, const Plan& p, int T, hipStream_t s);
 hipError_t launch_batch(const GemvArgs* table_dev, int count, const Plan& p, int T, hipStream_t s);
-hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, int64_t N, int32_t K, uint8_t* tiled,
-                         hipStream_t s);
+// Tiled layout of rows row_ids[0..N) of an n_rows-row weight (all N rows
+// when row_ids is null, n_rows = N).
+hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, const int32_t* row_ids, int64_t n_rows,
+                         int64_t N, int32_t K, uint8_t* tiled, hipStream_t s);
 hipError_t launch_argmax_final(const int2* partial, int64_t nparts, int T, int32_t* id, float* val, hipStream_t s);
 
 // Upper bound of the workgroups any plan uses for n_out rows (sizes the argmax workspace).

@@ -28,13 +28,16 @@ namespace {
 
 // Row-major codes and scales -> tiled layout, one thread per 16 output bytes.
 // Per tile the thread index runs over G * 64 code pieces (group g, row r,
-// quarter q: bytes 64g + 16q .. of row 16*tile + r) and then ceil(G/8) * 16
-// scale pieces (chunk c, row r: the bf16 scales of groups 8c .. 8c+7).
-// Rows past N and groups past G are written as zeros.
+// quarter q: bytes 64g + 16q .. of output row 16*tile + r) and then
+// ceil(G/8) * 16 scale pieces (chunk c, row r: the bf16 scales of groups
+// 8c .. 8c+7).  Output row o is input row row_ids[o] (o itself when row_ids
+// is null); rows past N and ids outside [0, n_rows) are written as zeros, as
+// are groups past G.
 __global__ void __launch_bounds__(256) w4a16_repack_kernel(const uint8_t* __restrict__ packed,
-                                                           const uint16_t* __restrict__ scales, int64_t N, int K,
-                                                           uint8_t* __restrict__ tiled, int64_t tile_bytes,
-                                                           int64_t total) {
+                                                           const uint16_t* __restrict__ scales,
+                                                           const int32_t* __restrict__ row_ids, int64_t n_rows,
+                                                           int64_t N, int K, uint8_t* __restrict__ tiled,
+                                                           int64_t tile_bytes, int64_t total) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= total) return;
   const int G = K / kGroup;
@@ -46,18 +49,21 @@ __global__ void __launch_bounds__(256) w4a16_repack_kernel(const uint8_t* __rest
   u4_t v = {0u, 0u, 0u, 0u};
   if (rem < (int64_t)G * 64) {
     const int g = (int)(rem >> 6), r = (int)(rem >> 2) & 15, q = (int)rem & 3;
-    const int64_t row = tile * 16 + r;
-    if (row < N) v = *reinterpret_cast<const u4_t*>(packed + row * (K / 2) + g * 64 + q * 16);
+    const int64_t o = tile * 16 + r;
+    const int64_t row = o >= N ? -1 : row_ids ? (int64_t)row_ids[o] : o;
+    if (row >= 0 && row < n_rows) v = *reinterpret_cast<const u4_t*>(packed + row * (K / 2) + g * 64 + q * 16);
     *reinterpret_cast<u4_t*>(tb + (int64_t)(g >> 3) * kTileChunkBytes + (g & 7) * kTileGroupBytes + r * 64 +
                              q * 16) = v;
   } else {
     const int j = (int)(rem - (int64_t)G * 64);
     const int c = j >> 4, r = j & 15;
-    const int64_t row = tile * 16 + r;
+    const int64_t o = tile * 16 + r;
+    const int64_t row = o >= N ? -1 : row_ids ? (int64_t)row_ids[o] : o;
+    const bool ok = row >= 0 && row < n_rows;
     const int ng = min(kTileChunkGroups, G - c * kTileChunkGroups);
     unsigned short sc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sc[e] = (row < N && e < ng) ? scales[row * G + c * kTileChunkGroups + e] : 0;
+    for (int e = 0; e < 8; ++e) sc[e] = (ok && e < ng) ? scales[row * G + c * kTileChunkGroups + e] : 0;
     v = u4_t{sc[0] | ((unsigned)sc[1] << 16), sc[2] | ((unsigned)sc[3] << 16), sc[4] | ((unsigned)sc[5] << 16),
              sc[6] | ((unsigned)sc[7] << 16)};
     *reinterpret_cast<u4_t*>(tb + (int64_t)c * kTileChunkBytes + ng * kTileGroupBytes + r * 16) = v;
@@ -256,19 +262,19 @@ int shared_waves(int T, int64_t K) {
 }
 
 // Default matrix-core tiling of a single launch (cus: compute units of the
-// device), from the MI355X sweeps.  Tall matrices (>= 1024 tiles of 16 rows)
-// use shared workgroups.  Row-major weights: the full vocabulary head
-// (15,520 tiles) is fastest with eight waves of four tiles each.  Tiled
-// weights: one tile per wave; for the head eight waves per workgroup, or
-// sixteen (a whole CU's LDS) when the activations need more than 64 KB;
-// four waves for mid-size matrices.  Shorter matrices split K over the waves of a
-// workgroup so that they still put ~12 waves of weight loads on every CU.
-// W4A16_TILE="split|shared,rt,waves" overrides the choice (for measurement).
+// device), from the MI355X sweeps.  Tiled weights of at least 4,096 tiles
+// (the vocabulary head) run workgroups of 16 waves x 4 tiles at every T
+// (with the argmax too); mid-size tiled matrices shared workgroups of four
+// waves of one tile.  Row-major weights: the full vocabulary head (15,520
+// tiles) is fastest with eight waves of four tiles each.  Shorter matrices
+// split K over the waves of a workgroup so that they still put ~12 waves of
+// weight loads on every CU.  W4A16_TILE="split|shared|run,rt,waves"
+// overrides the choice (for measurement).
 Plan plan_mfma(GemvArgs& a, int T, int cus) {
   const int64_t tiles = cdiv(a.n_out, 16);
   Tile t;
   if (tiles >= 4096 && a.tiled)
-    t = T <= 2 ? Tile{kShared, 1, shared_waves(T, a.K)} : Tile{kRun, 4, 16};
+    t = Tile{kRun, 4, 16};
   else if (tiles >= 8192)
     t = Tile{kShared, 4, 8};
   else if (tiles >= 4096)
@@ -318,13 +324,13 @@ hipError_t launch_batch(const GemvArgs* table_dev, int count, const Plan& p, int
   return for_t(T, [&](auto tt) { return launch_t<decltype(tt)::value>(unused, table_dev, count, p, s); });
 }
 
-hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, int64_t N, int32_t K, uint8_t* tiled,
-                         hipStream_t s) {
+hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, const int32_t* row_ids, int64_t n_rows,
+                         int64_t N, int32_t K, uint8_t* tiled, hipStream_t s) {
   const int G = K / kGroup;
   const int64_t tiles = cdiv(N, 16);
   const int64_t total = tiles * ((int64_t)G * 64 + cdiv(G, kTileChunkGroups) * 16);
-  hipLaunchKernelGGL(w4a16_repack_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, packed, scales, N, K,
-                     tiled, tiled_tile_bytes(G), total);
+  hipLaunchKernelGGL(w4a16_repack_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, packed, scales, row_ids,
+                     n_rows, N, K, tiled, tiled_tile_bytes(G), total);
   return hipGetLastError();
 }
 

@@ -170,3 +170,43 @@ def test_batch_mixed_layouts(w4, T):
         rows = sample_rows(N, 256, seed=N) if N > 2048 else np.arange(N, dtype=np.int32)
         y_ref, a_ref = oracle.gather(rows, p, s, x)
         assert_parity(host(y)[:, rows], y_ref, a_ref, f"batch mixed T={T} N={N}")
+
+
+@pytest.mark.parametrize("N,K,n_ids", [(300, 5120, 77), (37, 1152, 1), (1000, 2304, 2500)])
+def test_repack_rows_matches_layout_of_gathered_rows(w4, N, K, n_ids):
+    """The gathered repack is the layout of the host-gathered rows, byte for
+    byte (duplicates included); an id outside [0, N) gives an all-zero row."""
+    p, s, pd, sd = weight_dev(4300 + N + K, N, K)
+    rng = np.random.default_rng(n_ids)
+    ids = rng.integers(0, N, n_ids).astype(np.int32)
+    ids[0] = N - 1
+    tw = w4.repack_tiled_rows(pd, sd, dev(ids))
+    assert tw.N == n_ids and tw.data.numel() == w4.tiled_bytes(n_ids, K)
+    want = layout_by_definition(p[ids], s[ids])
+    assert np.array_equal(host(tw.data), want)
+    bad = ids.copy()
+    bad[min(1, n_ids - 1)] = N + 5
+    pz, sz = p[ids].copy(), s[ids].copy()
+    pz[min(1, n_ids - 1)] = 0
+    sz[min(1, n_ids - 1)] = 0
+    assert np.array_equal(host(w4.repack_tiled_rows(pd, sd, dev(bad)).data), layout_by_definition(pz, sz))
+
+
+@pytest.mark.parametrize("T", [1, 4])
+def test_compact_draft_head_matches_oracle(w4, T):
+    """The 32,768-id draft head repacked once into its own tiled matrix:
+    scores equal the oracle's gathered rows; the argmax position maps to the
+    vocabulary id of the (ascending) id list and equals the host argmax."""
+    from test_gpu_parity import lm_head
+
+    p, s, pd, sd = lm_head()
+    n_rows, K = synth.LM_HEAD
+    ids = np.sort(synth.distinct_ids(synth.RID_DRAFT, synth.DRAFT_IDS, n_rows))
+    x = synth.activations(synth.TID_LM_HEAD + 66, T, K)
+    tw = w4.repack_tiled_rows(pd, sd, dev(ids))
+    y, am, _ = w4.head_gather_tiled(tw, dev(x), scores=True, argmax=True)
+    y, am = host(y), host(am)
+    y_ref, a_ref = oracle.gather(ids, p, s, x)
+    assert_parity(y, y_ref, a_ref, f"compact draft head T={T}")
+    own, _, _ = oracle.argmax(y.astype(np.float64), ids)
+    assert np.array_equal(ids[am], own)

@@ -750,7 +750,9 @@ __device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, u
   }
   __syncthreads();
 
-  float* fin = reinterpret_cast<float*>(smem + a.fin_offset);
+  // The final values overwrite wave 0's partials: output o is read (all
+  // waves) and then written by one thread only.
+  float* fin = reinterpret_cast<float*>(smem);
   constexpr int kOut = RT * TT * 16;
   for (int o = threadIdx.x; o < kOut; o += blockDim.x) {
     float v = 0.0f;

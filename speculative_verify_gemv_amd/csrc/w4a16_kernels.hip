@@ -156,15 +156,17 @@ bool parse_tile(const char* text, Tile* t) {
 // of gpw groups (a multiple of the 8-group ring, so that 8-scale vector loads
 // stay aligned; the last wave may hold fewer) over at most nw_max waves.  A
 // wave's LDS area holds its staged activation slice of sk groups (the whole
-// range when 64 KB allow it, else a multiple of 8) and later its partial
-// sums; the final values follow the wave areas.
+// range when half a CU's LDS allows it, else a multiple of 8; swizzled
+// chunks, no padding between token rows) and later its partial sums; the
+// final values overwrite wave 0's partials in place.  At most half a CU, so
+// that two workgroups share a CU.
 static void plan_split(GemvArgs& a, int T, int rt, int nw_max, Plan* p) {
-  const int fin_bytes = rt * T * 16 * 4;
+  const int cap = kCuLds / 2;
   for (int nw = std::max(1, std::min(nw_max, a.G));; --nw) {
     const int gpw = (int)(cdiv(cdiv(a.G, nw), kRing) * kRing);
     const int nw_eff = (int)cdiv(a.G, gpw);
-    const int per_wave = ((kLdsCap - fin_bytes) / nw_eff) & ~15;
-    int sk = (per_wave / (2 * T) - 8) / kGroup;
+    const int per_wave = (cap / nw_eff) & ~15;
+    int sk = per_wave / (2 * T) / kGroup;
     if (sk >= gpw)
       sk = std::min(gpw, a.G);
     else if (sk >= kRing)
@@ -172,16 +174,16 @@ static void plan_split(GemvArgs& a, int T, int rt, int nw_max, Plan* p) {
     else if (nw > 1)
       continue;
     else
-      sk = kRing;  // unreachable for T <= 16: one wave always fits 15 groups
+      sk = kRing;  // unreachable for T <= 16: one wave always fits 20 groups
     a.nw = nw_eff;
     a.gpw = gpw;
     a.sk = sk;
-    a.xs_stride = ring_groups(sk) * kGroup + 8;  // 16-byte pad between token rows
+    a.xs_stride = ring_groups(sk) * kGroup;
     const int wave_lds = std::max(T * a.xs_stride * 2, rt * T * 16 * 4);
     a.wave_lds = (wave_lds + 15) & ~15;
-    a.fin_offset = nw_eff * a.wave_lds;
-    p->lds = a.fin_offset + fin_bytes;
-    if (p->lds > kLdsCap && nw > 1) continue;
+    a.fin_offset = 0;
+    p->lds = nw_eff * a.wave_lds;
+    if (p->lds > cap && nw > 1) continue;
     p->threads = nw_eff * 64;
     p->grid = cdiv(a.n_out, 16LL * rt);
     return;
@@ -268,7 +270,8 @@ int shared_waves(int T, int64_t K) {
 // waves of one tile.  Row-major weights: the full vocabulary head (15,520
 // tiles) is fastest with eight waves of four tiles each.  Shorter matrices
 // split K over the waves of a workgroup so that they still put ~12 waves of
-// weight loads on every CU.  W4A16_TILE="split|shared|run,rt,waves"
+// weight loads on every CU, up to 8 token rows; above that a wave's staged
+// slice would hold too few groups, and shared workgroups of four waves win.  W4A16_TILE="split|shared|run,rt,waves"
 // overrides the choice (for measurement).
 Plan plan_mfma(GemvArgs& a, int T, int cus) {
   const int64_t tiles = cdiv(a.n_out, 16);
@@ -279,7 +282,7 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
     t = Tile{kShared, 4, 8};
   else if (tiles >= 4096)
     t = Tile{kShared, 2, 8};
-  else if (tiles >= 1024)
+  else if (tiles >= 1024 || T > 8)  // above 8 rows a split wave stages too little K per slice
     t = Tile{kShared, 1, 4};
   else
     t = Tile{kSplit, 1, (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(12LL * std::max(cus, 1), tiles)))};

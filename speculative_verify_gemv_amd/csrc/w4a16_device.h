@@ -24,8 +24,9 @@
 // k+0, k+4, k+1, k+5, k+2, k+6, k+3, k+7 with 9 VALU operations.
 //
 // Activations are converted once per workgroup slice to fp16 in the same
-// slot order, scaled by 2^E (E chosen per token row and slice from the
-// largest |x|), so every bf16 value that matters is represented exactly; the
+// slot order, scaled by 2^E (a fixed E when that is exact for every value of
+// the slice, else E chosen per token row and slice from the largest |x|), so
+// every bf16 value that matters is represented exactly; the
 // power of two is removed again when the slice's partial sums are folded, so
 // the result equals the unscaled fp32 arithmetic.  Every product (q-8)*x is
 // exact in fp32; sums are fp32.
@@ -266,13 +267,22 @@ __device__ __forceinline__ void zero_pad(const GemvArgs& a, _Float16* xs, int n,
   }
 }
 
-// Eight bf16 (natural order) -> eight fp16 in slot order, unscaled; exact
-// for every value that passes range8.
+// Power of two of the one-pass staging: x * 2^kDirectE is an exact fp16 for
+// every bf16 magnitude in [2^-21, 4080].  Scaling by a power of two changes
+// no rounding of the products or sums (it is undone exactly at the end), so
+// it only moves the window of magnitudes that need no per-row scale: with
+// N(0,1) activations, 2^-17 (unscaled) is undershot by some value in a
+// quarter of the 8 x 5120 blocks, 2^-21 in about 1.5%.
+constexpr int kDirectE = 4;
+
+// Eight bf16 (natural order) -> eight fp16 in slot order, scaled by
+// 2^kDirectE; exact for every value that passes range8 / range_ok.
 __device__ __forceinline__ u4_t convert8_exact(u4_t v) {
-  const float x0 = __uint_as_float(v.x << 16), x1 = __uint_as_float(v.x & 0xFFFF0000u);
-  const float x2 = __uint_as_float(v.y << 16), x3 = __uint_as_float(v.y & 0xFFFF0000u);
-  const float x4 = __uint_as_float(v.z << 16), x5 = __uint_as_float(v.z & 0xFFFF0000u);
-  const float x6 = __uint_as_float(v.w << 16), x7 = __uint_as_float(v.w & 0xFFFF0000u);
+  constexpr float k = (float)(1 << kDirectE);
+  const float x0 = __uint_as_float(v.x << 16) * k, x1 = __uint_as_float(v.x & 0xFFFF0000u) * k;
+  const float x2 = __uint_as_float(v.y << 16) * k, x3 = __uint_as_float(v.y & 0xFFFF0000u) * k;
+  const float x4 = __uint_as_float(v.z << 16) * k, x5 = __uint_as_float(v.z & 0xFFFF0000u) * k;
+  const float x6 = __uint_as_float(v.w << 16) * k, x7 = __uint_as_float(v.w & 0xFFFF0000u) * k;
   return u4_t{as_u32(__builtin_amdgcn_cvt_pkrtz(x0, x4)), as_u32(__builtin_amdgcn_cvt_pkrtz(x1, x5)),
               as_u32(__builtin_amdgcn_cvt_pkrtz(x2, x6)), as_u32(__builtin_amdgcn_cvt_pkrtz(x3, x7))};
 }
@@ -290,17 +300,20 @@ __device__ __forceinline__ void range8(u4_t v, us2_t& mx, us2_t& mn) {
   }
 }
 
-// A bf16 converts to fp16 exactly, with no scaling, when it is zero or its
-// magnitude lies in [2^-17, 65280] (8 significant bits: fp16 normals from
-// 2^-14, subnormals keep 8 bits down to 2^-17).
+// A bf16 times 2^kDirectE converts to fp16 exactly when it is zero or its
+// magnitude lies in [2^-21, 4080] (8 significant bits: scaled, fp16 normals
+// from 2^-14, subnormals keep 8 bits down to 2^-17, and the largest bf16
+// below 2^16 is 65280).  As bf16 magnitude bits: 2^-21 is 0x3500 (mn holds
+// m - 1), 4080 is 0x457F.
+static_assert(kDirectE == 4, "range_ok's bounds are written for 2^4");
 __device__ __forceinline__ bool range_ok(us2_t mx, us2_t mn) {
-  return max((unsigned)mx.x, (unsigned)mx.y) <= 0x477Fu && min((unsigned)mn.x, (unsigned)mn.y) >= 0x36FFu;
+  return max((unsigned)mx.x, (unsigned)mx.y) <= 0x457Fu && min((unsigned)mn.x, (unsigned)mn.y) >= 0x34FFu;
 }
 
 // One-pass staging of x[t][gs*128 .. ge*128) by threads tid = 0..nthreads-1:
 // four 16-byte chunks per thread in flight at a time, converted to fp16
-// without scaling.  Returns true when some value of this thread's chunks is
-// not exact that way (the caller then stages again with a power-of-two
+// with the fixed scale 2^kDirectE.  Returns true when some value of this
+// thread's chunks is not exact that way (the caller then stages again with a power-of-two
 // scale per token row; both give the same products, scaled by 2^E).  A chunk
 // whose position is in [hold_from, hold_from + 4) is not stored but returned
 // in held / held_at (a thread meets at most one: they are four of one
@@ -388,8 +401,9 @@ __device__ __forceinline__ void stage_block(const GemvArgs& a, _Float16* xs, uns
 }
 
 // Stages x[t][gs*128 .. ge*128) of all TT token rows once for the whole
-// workgroup, plus the zeroed ring padding (zero_pad).  One pass without
-// scaling when every value of the slice converts exactly, else the scaled
+// workgroup, plus the zeroed ring padding (zero_pad).  One pass with the
+// fixed 2^kDirectE when every value of the slice converts exactly, else the
+// per-row scaled
 // two-pass staging.  The workgroup-wide decision needs one word per wave; the
 // words are borrowed from the last four chunks of the last row, whose values
 // the threads that own them hold back until the decision is made, so the
@@ -414,7 +428,7 @@ __device__ __forceinline__ void stage_shared(const GemvArgs& a, _Float16* xs, in
   if (any == 0) {
     if (held_at >= 0) dst[held_at] = held;
 #pragma unroll
-    for (int t = 0; t < TT; ++t) E[t] = 0;
+    for (int t = 0; t < TT; ++t) E[t] = kDirectE;
   } else {
     stage_block<TT>(a, xs, reinterpret_cast<unsigned*>(xs), gs, ge, E);
   }
@@ -569,8 +583,9 @@ __device__ __forceinline__ int scale_off(const GemvArgs& a, int g) {
 // 16 rows; weights as the B operand), whose sum gets the group's scale.
 // SHARED: the slice is staged once for the whole workgroup (stage_shared);
 // otherwise each wave stages its own range (no barrier).  Staging is one pass
-// without scaling when every activation converts to fp16 exactly, else the
-// scaled two-pass staging (stage_block / stage_wave).
+// with the fixed 2^kDirectE when every activation converts to fp16 exactly
+// that way, else the per-row scaled two-pass staging (stage_block /
+// stage_wave).
 // VS: scales are read eight groups (16 bytes) per load (needs G % 8 == 0,
 // 16-byte aligned scale rows and g_begin % 8 == 0); otherwise one 2-byte
 // load per group.
@@ -610,7 +625,7 @@ __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* cons
         stage_wave<TT>(a, xs, sb, se, lane, E);
       } else {
 #pragma unroll
-        for (int t = 0; t < TT; ++t) E[t] = 0;
+        for (int t = 0; t < TT; ++t) E[t] = kDirectE;
       }
       zero_pad<TT>(a, xs, n, lane, 64);
       lds_fence();

@@ -14,11 +14,14 @@ HBM peak (roofline, timed with HIP events on the launch stream), the body
 pass at T = 1, 4, 8 and 16 in both layouts (tiled and the pages' row-major one),
 the same step as 257 separate launches replayed from a captured HIP graph,
 single launches of each workload shape (the small matrix, every projection
-at T = 1, 4, 8, the lm_head with argmax, the draft head), the verify
-epilogue, and the CPU oracle's rate on a bounded sample.
+at T = 1, 4, 8, the lm_head with argmax, the draft head), the dot-product
+variant against the matrix-core one on the same single launches, the
+achievable streaming-read rate, the verify epilogue, and the CPU oracle's
+rate on a bounded sample.
 
 --pmc-pass runs one untimed body pass and one lm_head call after a 1 GiB
-device copy (the calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE).
+device copy (the calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE);
+--variants-pass one untimed launch per shape, T and variant.
 """
 from __future__ import annotations
 
@@ -59,7 +62,10 @@ def parse():
     ap.add_argument("--no-per-t", action="store_true")
     ap.add_argument("--no-graph", action="store_true")
     ap.add_argument("--no-singles", action="store_true")
+    ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true", help="one untimed pass for counter collection")
+    ap.add_argument("--variants-pass", action="store_true",
+                    help="one untimed launch per shape, T and kernel variant (dot / matrix core), for counters")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     return ap.parse_args()
 
@@ -154,6 +160,10 @@ def main():
     def head(s):
         w4a16.head_gather_tiled(head_tw, head_x, scores=True, argmax=True, out=head_y, workspace=head_ws, stream=s)
 
+    if args.variants_pass:
+        variants_pass(torch, w4a16, weights, head_p, head_s, stream)
+        return
+
     if args.pmc_pass:
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -219,6 +229,16 @@ def main():
     if not args.no_singles:
         singles = single_launches(torch, w4a16, weights, head_p, head_s, head_tw, stream)
 
+    # ---- the dot-product variant against the matrix-core one (row-major weights) ----
+    variants = None
+    if not args.no_variants:
+        variants = variant_launches(torch, w4a16, weights, head_p, head_s, stream)
+
+    # ---- achievable streaming-read ceiling (context for the 8 TB/s peak) ----
+    ceiling = read_ceiling(torch, w4a16, stream)
+    log(f"streaming-read ceiling: {ceiling['GBps']:.0f} GB/s ({ceiling['bytes'] >> 30} GiB, "
+        f"{ceiling['workgroups']} workgroups)")
+
     # ---- verify epilogue on the head's scores: top-32 per row, greedy acceptance ----
     epilogue = verify_epilogue(torch, w4a16, head_y, T, stream)
     log(f"verify epilogue at T={T}: top-32 of {hn} scores {epilogue['topk32_us']:.1f} us, "
@@ -267,6 +287,8 @@ def main():
         "graph_257_launches": graph_pass,
         "verify_epilogue": epilogue,
         "single_launches": singles,
+        "variants_dot_vs_matrix_core": variants,
+        "read_ceiling": ceiling,
         "roofline": {
             "kernel": "grouped body pass (64 x 4 projections, one launch, tiled layout)",
             "bound": "hbm",
@@ -360,6 +382,94 @@ def single_launches(torch, w4a16, weights, head_p, head_s, head_tw, stream):
     for k, v in out.items():
         log(f"single launch {k}: {v['us']:.1f} us, {v['weight_GBps']:.0f} GB/s")
     return out
+
+
+VARIANT_SHAPES = ("qkv", "o", "gate_up", "down")
+
+
+def variant_launches(torch, w4a16, weights, head_p, head_s, stream):
+    """Single launches on row-major weights (the layout the dot-product
+    variant reads) of each projection and of the lm_head with argmax at
+    T = 1, 4, 8, once with the dot-product variant (v_dot2_f32_f16, lanes
+    split K) and once with the matrix-core one; weight copies rotated as in
+    single_launches."""
+    out = {}
+    hn, hk = synth.LM_HEAD
+    head2 = (head_p.clone(), head_s.clone())  # two copies: 1.3 GB rotated
+    try:
+        for T in (1, 4, 8):
+            for proj in VARIANT_SHAPES + ("lm_head",):
+                if proj == "lm_head":
+                    N, K = hn, hk
+                    x = to_dev(synth.activations(synth.TID_LM_HEAD + 3, T, K), torch)
+                    y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+                    ws = torch.empty(w4a16.workspace_bytes(N, T), dtype=torch.uint8, device="cuda")
+                    fns = [lambda p=p, sc=sc: w4a16.head_gather(p, sc, x, scores=True, argmax=True, out=y,
+                                                                  workspace=ws, stream=stream)
+                           for p, sc in ((head_p, head_s), head2)]
+                else:
+                    N, K = synth.PROJECTIONS[proj]
+                    x = to_dev(synth.activations(synth.tid_layer(0, proj), T, K), torch)
+                    y = torch.empty((T, N), dtype=torch.float32, device="cuda")
+                    fns = [lambda p=w[2], sc=w[3]: w4a16.matmul(p, sc, x, out=y, stream=stream)
+                           for w in weights if w[0] == proj]
+                wb = metrics.weight_bytes(N, K)
+                row = {}
+                for v in ("dot", "mfma"):
+                    w4a16.set_variant(v)
+                    us = time_rotating(torch, fns, stream)
+                    row[f"{v}_us"] = round(us, 2)
+                    row[f"{v}_GBps"] = round(metrics.gbps(wb, us / 1000), 1)
+                out[f"{proj}_T{T}"] = row
+                log(f"variant {proj} T={T}: dot {row['dot_us']:.1f} us ({row['dot_GBps']:.0f} GB/s), "
+                    f"matrix core {row['mfma_us']:.1f} us ({row['mfma_GBps']:.0f} GB/s)")
+    finally:
+        w4a16.set_variant("auto")
+    return out
+
+
+def variants_pass(torch, w4a16, weights, head_p, head_s, stream):
+    """Untimed: for T = 1, 4, 8, each projection (layer 0) and the lm_head
+    with argmax, one launch with the dot-product variant, then one with the
+    matrix-core variant (counter collection)."""
+    hn, hk = synth.LM_HEAD
+    try:
+        for T in (1, 4, 8):
+            for v in ("dot", "mfma"):
+                w4a16.set_variant(v)
+                for proj in VARIANT_SHAPES:
+                    N, K = synth.PROJECTIONS[proj]
+                    w = next(w for w in weights if w[0] == proj)
+                    x = to_dev(synth.activations(synth.tid_layer(0, proj), T, K), torch)
+                    w4a16.matmul(w[2], w[3], x, stream=stream)
+                x = to_dev(synth.activations(synth.TID_LM_HEAD + 3, T, hk), torch)
+                w4a16.head_gather(head_p, head_s, x, scores=True, argmax=True, stream=stream)
+        torch.cuda.synchronize()
+    finally:
+        w4a16.set_variant("auto")
+    log("variants pass done: T = 1, 4, 8 x {dot, matrix core} x {qkv, o, gate_up, down, lm_head}")
+
+
+def read_ceiling(torch, w4a16, stream, gib=4, reps=10):
+    """The library's plain streaming-read kernel over a 4 GiB buffer (16-byte
+    nontemporal loads, 8 workgroups per CU): the achievable read rate."""
+    n = gib << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    wg = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(wg * 256, dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        w4a16.stream_read(src, sink, wg, stream=stream)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        w4a16.stream_read(src, sink, wg, stream=stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, sink
+    return {"GBps": round(metrics.gbps(n, ms), 1), "bytes": n, "workgroups": wg, "ms": round(ms, 4)}
 
 
 def verify_epilogue(torch, w4a16, head_y, T, stream, reps=50):

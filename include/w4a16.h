@@ -303,6 +303,19 @@ w4a16_status w4a16_greedy_accept(const int32_t* target_ids, const int32_t* draft
 w4a16_status w4a16_draft_union(const int32_t* base_ids, int32_t n_base, const int32_t* seq_ids, int32_t n_seq,
                                int64_t n_rows, int32_t* union_ids, int32_t* n_union, hipStream_t stream);
 
+/* Measurement helper (not a step of the path): reads `bytes` of device
+ * memory at src once with 16-byte nontemporal loads spread over
+ * `workgroups` workgroups of 256 threads, each taking one contiguous share,
+ * and writes one XOR-folded word per thread to sink.  Its rate is the
+ * achievable streaming-read ceiling that the matmul's weight bandwidth is
+ * set beside (the peak it is measured against stays the nominal 8 TB/s).
+ *   src 16-byte aligned, bytes a positive multiple of 16;
+ *   sink uint32 [workgroups * 256] device, 4-byte aligned;
+ *   1 <= workgroups <= 65536.
+ */
+w4a16_status w4a16_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                               hipStream_t stream);
+
 /* Selects the kernel variant for subsequent calls in this process (initially
  * taken from the environment variable W4A16_VARIANT = auto|dot|mfma). */
 w4a16_status w4a16_set_variant(int32_t variant);

@@ -78,6 +78,8 @@ def load_library():
         lib.w4a16_greedy_accept.restype = i32
         lib.w4a16_draft_union.argtypes = [vp, i32, vp, i32, i64, vp, vp, vp]
         lib.w4a16_draft_union.restype = i32
+        lib.w4a16_stream_read.argtypes = [vp, sz, vp, i32, vp]
+        lib.w4a16_stream_read.restype = i32
         _lib = lib
     return _lib
 
@@ -383,3 +385,18 @@ def draft_union(base_ids: torch.Tensor | None, seq_ids: torch.Tensor | None, n_r
     if st:
         raise W4A16Error(st, "w4a16_draft_union")
     return out, length
+
+
+def stream_read(src: torch.Tensor, sink: torch.Tensor, workgroups: int, stream=None) -> None:
+    """Measurement helper: read all of src (a contiguous CUDA tensor whose
+    byte size is a multiple of 16) once with nontemporal 16-byte loads over
+    `workgroups` workgroups; sink is a CUDA int32 tensor of at least
+    workgroups * 256 elements.  Its rate is the streaming-read ceiling."""
+    if not (src.is_cuda and src.is_contiguous() and sink.is_cuda and sink.dtype == torch.int32):
+        raise ValueError("src must be a contiguous CUDA tensor and sink a CUDA int32 tensor")
+    if sink.numel() < workgroups * 256:
+        raise ValueError("sink must hold workgroups * 256 words")
+    nbytes = src.numel() * src.element_size()
+    st = load_library().w4a16_stream_read(src.data_ptr(), nbytes, sink.data_ptr(), workgroups, _stream(stream))
+    if st:
+        raise W4A16Error(st, "w4a16_stream_read")

@@ -421,6 +421,17 @@ w4a16_status w4a16_set_variant(int32_t variant) {
 
 int32_t w4a16_get_variant(void) { return current_variant(); }
 
+w4a16_status w4a16_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
+                               hipStream_t stream) {
+  if (!src || !sink) return W4A16_ERR_NULL_POINTER;
+  if (bytes == 0 || bytes % 16 != 0 || bytes > ((size_t)1 << 50) || workgroups < 1 || workgroups > 65536)
+    return W4A16_ERR_BAD_SHAPE;
+  if (!aligned(src, 16) || !aligned(sink, 4)) return W4A16_ERR_MISALIGNED;
+  if (w4a16_status s = check_device()) return s;
+  return w4a16::launch_stream_read(src, (int64_t)bytes, sink, workgroups, stream) == hipSuccess ? W4A16_OK
+                                                                                                   : W4A16_ERR_HIP;
+}
+
 const char* w4a16_status_string(int32_t status) {
   switch (status) {
     case W4A16_OK: return "ok";

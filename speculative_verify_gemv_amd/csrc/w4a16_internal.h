@@ -99,6 +99,10 @@ hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, const in
                          int64_t N, int32_t K, uint8_t* tiled, hipStream_t s);
 hipError_t launch_argmax_final(const int2* partial, int64_t nparts, int T, int32_t* id, float* val, hipStream_t s);
 
+// Streaming read of bytes (a multiple of 16) over `workgroups` workgroups
+// of 256 threads; sink holds workgroups * 256 words.
+hipError_t launch_stream_read(const void* src, int64_t bytes, unsigned* sink, int workgroups, hipStream_t s);
+
 // Upper bound of the workgroups any plan uses for n_out rows (sizes the argmax workspace).
 int64_t max_workgroups(int64_t n_out);
 

@@ -271,8 +271,9 @@ int shared_waves(int T, int64_t K) {
 // tiles) is fastest with eight waves of four tiles each.  Shorter matrices
 // split K over the waves of a workgroup so that they still put ~12 waves of
 // weight loads on every CU, up to 8 token rows; above that a wave's staged
-// slice would hold too few groups, and shared workgroups of four waves win.  W4A16_TILE="split|shared|run,rt,waves"
-// overrides the choice (for measurement).
+// slice would hold too few groups, and shared workgroups of four waves win.
+// W4A16_TILE="split|shared|run,rt,waves" overrides the choice (for
+// measurement).
 Plan plan_mfma(GemvArgs& a, int T, int cus) {
   const int64_t tiles = cdiv(a.n_out, 16);
   Tile t;
@@ -314,6 +315,39 @@ Plan plan_dot(GemvArgs& a, int T) {
   a.fin_offset = (xs_bytes + 15) & ~15;                                 // max buffer follows
   p.lds = a.fin_offset + nw * T * 4;
   return p;
+}
+
+namespace {
+
+// Measurement: every 16-byte word of src read once, four nontemporal loads
+// in flight per thread, workgroup b over the b-th contiguous share.  The
+// words are folded by XOR into one value per thread, stored to sink, so that
+// no load can be dropped.
+__global__ void __launch_bounds__(256) w4a16_stream_read_kernel(const u4_t* __restrict__ src, int64_t n16,
+                                                                unsigned* __restrict__ sink) {
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t b = (int64_t)blockIdx.x * per, e = min(n16, b + per);
+  unsigned acc = 0;
+  int64_t i = b + threadIdx.x;
+  for (; i + 3 * 256 < e; i += 4 * 256) {
+    const u4_t v0 = ld_global_nt(src + i), v1 = ld_global_nt(src + i + 256);
+    const u4_t v2 = ld_global_nt(src + i + 512), v3 = ld_global_nt(src + i + 768);
+    acc ^= (v0.x ^ v0.y ^ v0.z ^ v0.w) ^ (v1.x ^ v1.y ^ v1.z ^ v1.w) ^ (v2.x ^ v2.y ^ v2.z ^ v2.w) ^
+           (v3.x ^ v3.y ^ v3.z ^ v3.w);
+  }
+  for (; i < e; i += 256) {
+    const u4_t v = ld_global_nt(src + i);
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  st_global(sink + (int64_t)blockIdx.x * 256 + threadIdx.x, acc);
+}
+
+}  // namespace
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, unsigned* sink, int workgroups, hipStream_t s) {
+  hipLaunchKernelGGL(w4a16_stream_read_kernel, dim3((unsigned)workgroups), dim3(256), 0, s,
+                     static_cast<const u4_t*>(src), bytes / 16, sink);
+  return hipGetLastError();
 }
 
 int64_t max_workgroups(int64_t n_out) { return cdiv(n_out, 16); }

@@ -230,3 +230,13 @@ def test_draft_union_arguments_rejected_on_the_host(lib):
     assert du(nb=-1) == SHAPE and du(ns=4097) == SHAPE and du(nb=0, ns=0) == SHAPE
     assert du(n=0) == SHAPE and du(n=524289) == SHAPE
     assert du(b=A + 2) == ALIGN and du(o=A + 1) == ALIGN and du(m=A + 2) == ALIGN
+
+
+def test_stream_read_arguments_rejected_on_the_host(lib):
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.w4a16_stream_read.argtypes = [vp, sz, vp, i32, vp]
+    lib.w4a16_stream_read.restype = i32
+    sr = lambda s=A, n=1 << 20, k=A, w=2048: lib.w4a16_stream_read(s, n, k, w, None)
+    assert sr(s=None) == NULLP and sr(k=None) == NULLP
+    assert sr(n=0) == SHAPE and sr(n=1000) == SHAPE and sr(w=0) == SHAPE and sr(w=65537) == SHAPE
+    assert sr(s=A + 8) == ALIGN and sr(k=A + 2) == ALIGN

@@ -20,7 +20,8 @@ achievable streaming-read rate, the verify epilogue, and the CPU oracle's
 rate on a bounded sample.
 
 --pmc-pass runs one untimed body pass and one lm_head call after a 1 GiB
-device copy (the calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE);
+device copy (the calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE),
+then one body pass at each of T = 1, 8, 16;
 --variants-pass one untimed launch per shape, T and variant.
 """
 from __future__ import annotations
@@ -170,8 +171,14 @@ def main():
         dst.copy_(src)  # calibration: reads and writes exactly 1 GiB
         batch.run(stream)
         head(stream)
+        for Tp in (1, 8, 16):  # the body pass at the other verify widths, after the T = 4 one
+            b, _ = make_pass(Tp)
+            b.run(stream)
+            torch.cuda.synchronize()
+            del b
         torch.cuda.synchronize()
-        log(f"pmc pass done: copy {COPY_BYTES} B, body pass {body_bytes} B, lm_head {head_bytes} B")
+        log(f"pmc pass done: copy {COPY_BYTES} B, body pass {body_bytes} B at T = {T}, lm_head {head_bytes} B, "
+            f"body pass at T = 1, 8, 16")
         return
 
     for _ in range(args.warmup):

@@ -1,27 +1,28 @@
 """Benchmark: the decode weight pass of a 27B-class model on one MI355X.
 
 One step is one verify cycle's weight read: 64 layers x {qkv, o, gate_up,
-down} W4A16 projections at T = 4 (1 + 3 drafts), each with its own seeded
-weights and activations, run as one grouped launch, then the 248,320-row
-lm_head with per-row argmax.  Weights are repacked once at load into the
-tiled layout (same codes and scales, one contiguous 1 KB block per 16 rows x
-128 columns) and stay resident in HBM; nothing is cached between steps
-(11.6 GB per step, far beyond the 256 MB Infinity Cache).
+down} W4A16 projections and the 248,320-row lm_head with per-row argmax, at
+T = 4 (1 + 3 drafts), each matrix with its own seeded weights and
+activations, all in one grouped launch (followed by the argmax reduction, a
+launch of T workgroups).  Weights are repacked once at load into the tiled
+layout (same codes and scales, one contiguous 1 KB block per 16 rows x 128
+columns) and stay resident in HBM; nothing is cached between steps (11.6 GB
+per step, far beyond the 256 MB Infinity Cache).
 
 Reported (one JSON line): weight GB/s of the whole step (value), decode
-cycles/s, the grouped body kernel's achieved bandwidth against the 8 TB/s
-HBM peak (roofline, timed with HIP events on the launch stream), the body
-pass at T = 1, 4, 8 and 16 in both layouts (tiled and the pages' row-major one),
-the same step as 257 separate launches replayed from a captured HIP graph,
-single launches of each workload shape (the small matrix, every projection
-at T = 1, 4, 8, the lm_head with argmax, the draft head), the dot-product
-variant against the matrix-core one on the same single launches, the
-achievable streaming-read rate, the verify epilogue, and the CPU oracle's
-rate on a bounded sample.
+cycles/s, the grouped kernel's achieved bandwidth against the 8 TB/s HBM
+peak (roofline, timed with HIP events on the launch stream), the same step
+as two launches (body pass, then the lm_head) and as 257 separate launches
+replayed from a captured HIP graph, the body pass alone at T = 1, 4, 8 and
+16 in both layouts (tiled and the pages' row-major one), single launches of
+each workload shape (the small matrix, every projection at T = 1, 4, 8, the
+lm_head with argmax, the draft head), the dot-product variant against the
+matrix-core one on the same single launches, the achievable streaming-read
+rate, the verify epilogue, and the CPU oracle's rate on a bounded sample.
 
---pmc-pass runs one untimed body pass and one lm_head call after a 1 GiB
-device copy (the calibration kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE),
-then one body pass at each of T = 1, 8, 16;
+--pmc-pass runs one untimed step after a 1 GiB device copy (the calibration
+kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE), then one body pass alone at
+each of T = 1, 4, 8, 16;
 --variants-pass one untimed launch per shape, T and variant.
 """
 from __future__ import annotations
@@ -158,8 +159,15 @@ def main():
     head_ws = torch.empty(w4a16.workspace_bytes(hn, T), dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 
+    head_id = torch.empty(T, dtype=torch.int32, device="cuda")
+    head_val = torch.empty(T, dtype=torch.float32, device="cuda")
+
     def head(s):
         w4a16.head_gather_tiled(head_tw, head_x, scores=True, argmax=True, out=head_y, workspace=head_ws, stream=s)
+
+    # the step: the 256 projections and the lm_head with its argmax in one
+    # grouped launch (then the argmax reduction, a small launch of T workgroups)
+    step = w4a16.Batch(probs + [(head_tw, None, head_x, head_y, head_id, head_val, head_ws)], T)
 
     if args.variants_pass:
         variants_pass(torch, w4a16, weights, head_p, head_s, stream)
@@ -169,21 +177,19 @@ def main():
         src = torch.empty(COPY_BYTES, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
         dst.copy_(src)  # calibration: reads and writes exactly 1 GiB
-        batch.run(stream)
-        head(stream)
-        for Tp in (1, 8, 16):  # the body pass at the other verify widths, after the T = 4 one
-            b, _ = make_pass(Tp)
+        step.run(stream)
+        for Tp in (1, 4, 8, 16):  # the body pass alone at each verify width
+            b, _ = (batch, probs) if Tp == T else make_pass(Tp)
             b.run(stream)
             torch.cuda.synchronize()
             del b
         torch.cuda.synchronize()
-        log(f"pmc pass done: copy {COPY_BYTES} B, body pass {body_bytes} B at T = {T}, lm_head {head_bytes} B, "
-            f"body pass at T = 1, 8, 16")
+        log(f"pmc pass done: copy {COPY_BYTES} B, step {body_bytes + head_bytes} B at T = {T}, "
+            f"body pass at T = 1, 4, 8, 16")
         return
 
     for _ in range(args.warmup):
-        batch.run(stream)
-        head(stream)
+        step.run(stream)
     torch.cuda.synchronize()
 
     K_steps = args.steps
@@ -193,20 +199,33 @@ def main():
     start.record(stream)
     for i in range(K_steps):
         ev[i][0].record(stream)
-        batch.run(stream)
+        step.run(stream)
         ev[i][1].record(stream)
-        head(stream)
     end.record(stream)
     torch.cuda.synchronize()
     ms_total = start.elapsed_time(end)
     ms_step = ms_total / K_steps
-    body_ms = [a.elapsed_time(b) for a, b in ev]
-    body_ms_avg = float(np.mean(body_ms))
+    launch_ms = [a.elapsed_time(b) for a, b in ev]
+    launch_ms_avg = float(np.mean(launch_ms))
     step_bytes = body_bytes + head_bytes
     value = metrics.gbps(step_bytes, ms_step)
-    achieved = metrics.gbps(body_bytes, body_ms_avg)
-    log(f"step {ms_step:.4f} ms, body kernel {body_ms_avg:.4f} ms (min {min(body_ms):.4f}), "
-        f"{value:.0f} GB/s per step, body {achieved:.0f} GB/s")
+    achieved = metrics.gbps(step_bytes, launch_ms_avg)
+    log(f"step {ms_step:.4f} ms, grouped launch + argmax reduction {launch_ms_avg:.4f} ms "
+        f"(min {min(launch_ms):.4f}), {value:.0f} GB/s per step, kernel {achieved:.0f} GB/s")
+
+    # the same step as two launches (body pass, then the lm_head with argmax)
+    for _ in range(5):
+        batch.run(stream)
+        head(stream)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(K_steps):
+        batch.run(stream)
+        head(stream)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms_two = e0.elapsed_time(e1) / K_steps
+    log(f"step as body pass + separate lm_head launch: {ms_two:.4f} ms, {metrics.gbps(step_bytes, ms_two):.0f} GB/s")
 
     # ---- body pass at T = 1, 4, 8, 16 (same weights, grouped launch), both layouts ----
     per_t, per_t_rm = {}, {}
@@ -291,21 +310,24 @@ def main():
         "pct_hbm_peak": round(100 * value / PEAK_GBPS, 2),
         "per_T_body_pass": per_t,
         "per_T_body_pass_row_major": per_t_rm,
+        "step_two_launches": {"ms_per_step": round(ms_two, 4),
+                              "weight_GBps": round(metrics.gbps(step_bytes, ms_two), 1)},
         "graph_257_launches": graph_pass,
         "verify_epilogue": epilogue,
         "single_launches": singles,
         "variants_dot_vs_matrix_core": variants,
         "read_ceiling": ceiling,
         "roofline": {
-            "kernel": "grouped body pass (64 x 4 projections, one launch, tiled layout)",
+            "kernel": "grouped launch of the step (64 x 4 projections + lm_head with argmax, tiled layout); "
+                      "the launch time includes the argmax reduction launched after it",
             "bound": "hbm",
             "achieved": round(achieved, 1),
             "peak": PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBPS, 4),
             "traffic": measured_traffic(),
-            "algorithmic_bytes_per_launch": body_bytes,
-            "avg_launch_ms": round(body_ms_avg, 4),
+            "algorithmic_bytes_per_launch": step_bytes,
+            "avg_launch_ms": round(launch_ms_avg, 4),
         },
         "cpu_baseline": cpu,
     }

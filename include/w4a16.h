@@ -56,7 +56,7 @@ typedef struct ihipStream_t* hipStream_t; /* same definition as the HIP runtime'
 
 #define W4A16_GROUP 128      /* columns per bf16 scale */
 #define W4A16_MAX_T 16       /* activation rows per weight read */
-#define W4A16_ABI_VERSION 3
+#define W4A16_ABI_VERSION 4
 
 typedef enum {
   W4A16_OK = 0,
@@ -69,10 +69,11 @@ typedef enum {
   W4A16_ERR_BAD_VARIANT = 7   /* unknown kernel variant */
 } w4a16_status;
 
-/* Kernel variants.  Both compute the same values within the tolerance above;
- * AUTO picks per T the one measured faster on MI355X.  The dot variant covers
- * T <= 8; calls with more activation rows run the matrix-core kernels
- * whatever the selection. */
+/* Kernel variants.  Both compute the same values within the tolerance above.
+ * AUTO runs the matrix-core kernels, measured faster on MI355X at every T
+ * (about even with the dot variant at T = 1 on short matrices, 1.7-12x faster
+ * from T = 4).  The dot variant covers T <= 8; calls with more activation
+ * rows run the matrix-core kernels whatever the selection. */
 typedef enum {
   W4A16_VARIANT_AUTO = 0,
   W4A16_VARIANT_DOT = 1, /* VALU dot products, split-K across lanes, cross-lane reduction */
@@ -203,7 +204,10 @@ w4a16_status w4a16_head_gather_tiled(const int32_t* row_ids, int64_t n_ids, cons
  * bytes of the host copy and stay unchanged while launches that use it run.
  * Problems run in list order as far as the GPU schedules them; their outputs
  * must not overlap each other or any input.  The pointers and sizes of each
- * problem follow w4a16_matmul.
+ * problem follow w4a16_matmul.  A problem may also take the per-row argmax
+ * of its outputs, as w4a16_head_gather does (the lm_head of a verify pass in
+ * the same launch as the layers; the argmax reduction then runs as one small
+ * launch per such problem after the grouped one, on the same stream).
  */
 typedef struct {
   const uint8_t* packed_u4;    /* [N][K/2], or the tiled layout when layout = 1 */
@@ -214,6 +218,10 @@ typedef struct {
   int64_t K;
   int32_t layout;              /* W4A16_LAYOUT_ROW_MAJOR or W4A16_LAYOUT_TILED */
   int32_t reserved;            /* must be 0 */
+  int32_t* argmax_id;          /* [T] device, or NULL: no argmax for this problem */
+  float* argmax_val;           /* [T] device, or NULL (needs argmax_id) */
+  void* workspace;             /* with argmax_id: device, 16-byte aligned, at least */
+  size_t workspace_bytes;      /*   w4a16_workspace_bytes(N, T) bytes, one per problem */
 } w4a16_problem;
 
 #define W4A16_LAYOUT_ROW_MAJOR 0

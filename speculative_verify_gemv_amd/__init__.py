@@ -276,22 +276,28 @@ def head_gather_tiled(w: TiledWeight, x: torch.Tensor, row_ids: torch.Tensor | N
 class _Problem(ctypes.Structure):
     _fields_ = [("packed_u4", ctypes.c_void_p), ("scales_bf16", ctypes.c_void_p), ("x_bf16", ctypes.c_void_p),
                 ("y_f32", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("layout", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("reserved", ctypes.c_int32), ("argmax_id", ctypes.c_void_p), ("argmax_val", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 class Batch:
     """A planned grouped launch over independent matmuls with the same T.
 
     problems: list of (packed, scales, x, y) CUDA tensors, or (TiledWeight,
-    None, x, y).  The tensors must stay alive and in place while the batch is
-    used; the plan is a host table plus its device copy (both held here).
+    None, x, y); either may carry three more entries (argmax_id int32 [T],
+    argmax_val float32 [T] or None, workspace uint8 of workspace_bytes(N, T))
+    for the per-row argmax of that problem's outputs.  The tensors must stay
+    alive and in place while the batch is used; the plan is a host table plus
+    its device copy (both held here).
     """
 
     def __init__(self, problems, T: int):
         lib = load_library()
         arr = (_Problem * len(problems))()
         self._keep = []
-        for i, (packed, scales, x, y) in enumerate(problems):
+        for i, prob in enumerate(problems):
+            packed, scales, x, y = prob[:4]
+            am_id, am_val, ws = (tuple(prob[4:7]) + (None, None, None))[:3]
             if isinstance(packed, TiledWeight):
                 N, K, layout, pp, sp = packed.N, packed.K, 1, packed.data.data_ptr(), None
             else:
@@ -300,8 +306,17 @@ class Batch:
             _check_bits(x, "x")
             if x.shape != (T, K) or y.dtype != torch.float32 or y.shape != (T, N) or not y.is_contiguous():
                 raise ValueError(f"problem {i}: x must be [T][K] and y float32 [T][N]")
-            arr[i] = _Problem(pp, sp, x.data_ptr(), y.data_ptr(), N, K, layout, 0)
-            self._keep.append((packed, scales, x, y))
+            if am_id is not None:
+                if am_id.dtype != torch.int32 or am_id.numel() != T or not am_id.is_cuda:
+                    raise ValueError(f"problem {i}: argmax_id must be a CUDA int32 tensor of T entries")
+                if am_val is not None and (am_val.dtype != torch.float32 or am_val.numel() != T):
+                    raise ValueError(f"problem {i}: argmax_val must be a CUDA float32 tensor of T entries")
+                if ws is None or not ws.is_cuda:
+                    raise ValueError(f"problem {i}: argmax needs a CUDA workspace")
+            arr[i] = _Problem(pp, sp, x.data_ptr(), y.data_ptr(), N, K, layout, 0,
+                              _ptr(am_id), _ptr(am_val), _ptr(ws),
+                              0 if ws is None else ws.numel() * ws.element_size())
+            self._keep.append(tuple(prob))
         nbytes = lib.w4a16_batch_table_bytes(len(problems))
         if nbytes == 0:
             raise ValueError("batch size out of range")

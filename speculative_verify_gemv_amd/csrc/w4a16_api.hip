@@ -141,11 +141,20 @@ struct TableHeader {
   int32_t tiled;  // 1: every problem tiled (tiled-layout kernels, one tile per wave)
   int32_t threads;
   int32_t lds;
-  int32_t reserved0;
+  int32_t n_argmax;  // argmax records after the count argument records (host copy)
   int64_t grid;
   int64_t reserved[2];
 };
 static_assert(sizeof(TableHeader) == 64, "table header size");
+
+// A grouped problem's argmax reduction, launched after the grouped kernel.
+struct ArgmaxRecord {
+  const int2* partial;
+  int64_t nparts;  // the problem's workgroups
+  int32_t* id;
+  float* val;
+};
+static_assert(sizeof(ArgmaxRecord) == 32 && sizeof(w4a16::GemvArgs) == 128, "batch table record sizes");
 
 // Tile of grouped launches, from the MI355X sweeps.  All problems tiled:
 // at T <= 2 shared workgroups of one tile per wave; above, run workgroups of
@@ -275,7 +284,7 @@ w4a16_status w4a16_repack_tiled_rows(const uint8_t* packed_u4, const uint16_t* s
 
 size_t w4a16_batch_table_bytes(int32_t count) {
   if (count < 1 || count > W4A16_MAX_BATCH) return 0;
-  return sizeof(TableHeader) + (size_t)count * sizeof(w4a16::GemvArgs);
+  return sizeof(TableHeader) + (size_t)count * (sizeof(w4a16::GemvArgs) + sizeof(ArgmaxRecord));
 }
 
 w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int32_t T, void* table_host,
@@ -292,11 +301,16 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
     if (q.N < 1 || q.N > kMaxRows) return W4A16_ERR_BAD_SHAPE;
     if (w4a16_status s = check_kt(q.K, T)) return s;
     if (!aligned(q.packed_u4, 16) || !aligned(q.x_bf16, 16) || (!tiled && !aligned(q.scales_bf16, 2)) ||
-        !aligned(q.y_f32, 4))
+        !aligned(q.y_f32, 4) || !aligned(q.argmax_id, 4) || !aligned(q.argmax_val, 4))
       return W4A16_ERR_MISALIGNED;
+    if (q.argmax_val && !q.argmax_id) return W4A16_ERR_NULL_POINTER;
+    if (q.argmax_id && (!q.workspace || !aligned(q.workspace, 16) ||
+                        q.workspace_bytes < w4a16_workspace_bytes(q.N, T)))
+      return W4A16_ERR_WORKSPACE;
   }
   auto* hdr = static_cast<TableHeader*>(table_host);
   auto* args = reinterpret_cast<w4a16::GemvArgs*>(hdr + 1);
+  auto* recs = reinterpret_cast<ArgmaxRecord*>(args + count);
   bool all_tiled = true;
   int64_t kmax = 0;
   for (int32_t i = 0; i < count; ++i) {
@@ -309,13 +323,14 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
   // differs between problems falls back to shared workgroups.
   for (int attempt = 0; attempt < 2; ++attempt) {
     int64_t grid = 0;
-    int lds = 0, threads = 64, rt = 0;
+    int lds = 0, threads = 64, rt = 0, n_argmax = 0;
     bool uniform = true;
     for (int32_t i = 0; i < count; ++i) {
       const w4a16_problem& q = problems[i];
       const bool tiled = q.layout == W4A16_LAYOUT_TILED;
       w4a16::GemvArgs a = gemv_args(q.packed_u4, tiled ? nullptr : q.scales_bf16, tiled, q.x_bf16, q.y_f32,
                                     nullptr, q.N, q.N, q.K);
+      a.partial = q.argmax_id ? static_cast<int2*>(q.workspace) : nullptr;
       const w4a16::Plan p = w4a16::plan_tile(a, T, bt, all_tiled, true);
       uniform = uniform && p.variant == bt.shape;
       rt = p.rt;
@@ -324,14 +339,15 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
       lds = std::max(lds, p.lds);
       threads = std::max(threads, p.threads);
       args[i] = a;
+      if (q.argmax_id) recs[n_argmax++] = ArgmaxRecord{a.partial, p.grid, q.argmax_id, q.argmax_val};
     }
     if (!uniform) {
       bt = w4a16::Tile{w4a16::kShared, 1, std::min(bt.nw, all_tiled ? 16 : 8)};
       continue;
     }
     if (grid > 0x7fffffffLL) return W4A16_ERR_BAD_SHAPE;
-    *hdr = TableHeader{kTableMagic, W4A16_ABI_VERSION, count, T, bt.shape, rt, all_tiled ? 1 : 0, threads, lds, 0,
-                       grid, {0, 0}};
+    *hdr = TableHeader{kTableMagic, W4A16_ABI_VERSION, count, T, bt.shape, rt, all_tiled ? 1 : 0, threads, lds,
+                       n_argmax, grid, {0, 0}};
     return W4A16_OK;
   }
   return W4A16_ERR_BAD_SHAPE;  // not reached: shared tiles always plan
@@ -358,8 +374,16 @@ w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, h
   p.threads = hdr->threads;
   p.grid = hdr->grid;
   p.lds = hdr->lds;
+  if (hdr->n_argmax < 0 || hdr->n_argmax > hdr->count) return W4A16_ERR_BAD_SHAPE;
   const auto* args = reinterpret_cast<const w4a16::GemvArgs*>(static_cast<const TableHeader*>(table_dev) + 1);
-  return w4a16::launch_batch(args, hdr->count, p, hdr->T, stream) == hipSuccess ? W4A16_OK : W4A16_ERR_HIP;
+  if (w4a16::launch_batch(args, hdr->count, p, hdr->T, stream) != hipSuccess) return W4A16_ERR_HIP;
+  const auto* recs = reinterpret_cast<const ArgmaxRecord*>(reinterpret_cast<const w4a16::GemvArgs*>(hdr + 1) +
+                                                           hdr->count);
+  for (int32_t i = 0; i < hdr->n_argmax; ++i)
+    if (w4a16::launch_argmax_final(recs[i].partial, recs[i].nparts, hdr->T, recs[i].id, recs[i].val, stream) !=
+        hipSuccess)
+      return W4A16_ERR_HIP;
+  return W4A16_OK;
 }
 
 size_t w4a16_topk_workspace_bytes(int64_t n, int32_t T, int32_t k) {

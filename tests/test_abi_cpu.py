@@ -62,7 +62,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.w4a16_abi_version() == 3
+    assert lib.w4a16_abi_version() == 4
     for s in range(8):
         assert lib.w4a16_status_string(s)
     assert lib.w4a16_status_string(99) == b"unknown status"
@@ -174,7 +174,8 @@ def test_tiled_rejections(lib):
 class Problem(ctypes.Structure):
     _fields_ = [("packed_u4", ctypes.c_void_p), ("scales_bf16", ctypes.c_void_p), ("x_bf16", ctypes.c_void_p),
                 ("y_f32", ctypes.c_void_p), ("N", ctypes.c_int64), ("K", ctypes.c_int64), ("layout", ctypes.c_int32),
-                ("reserved", ctypes.c_int32)]
+                ("reserved", ctypes.c_int32), ("argmax_id", ctypes.c_void_p), ("argmax_val", ctypes.c_void_p),
+                ("workspace", ctypes.c_void_p), ("workspace_bytes", ctypes.c_size_t)]
 
 
 def plan(lib, probs, T=4):
@@ -186,7 +187,7 @@ def plan(lib, probs, T=4):
 
 def test_batch_plan_layouts(lib):
     """Planning is host-only, so it runs here: both layouts accepted, bad fields rejected."""
-    assert ctypes.sizeof(Problem) == 56
+    assert ctypes.sizeof(Problem) == 88
     row = Problem(A, A, A, A, 7168, 5120, 0, 0)
     tiled = Problem(A, None, A, A, 5120, 17408, 1, 0)
     assert plan(lib, [row, tiled]) == OK
@@ -194,6 +195,23 @@ def test_batch_plan_layouts(lib):
     assert plan(lib, [Problem(A, A, A, A, 64, 256, 2, 0)]) == SHAPE         # unknown layout
     assert plan(lib, [Problem(A, A, A, A, 64, 256, 1, 5)]) == SHAPE         # reserved must be 0
     assert plan(lib, [Problem(A + 8, None, A, A, 64, 256, 1, 0)]) == ALIGN  # tiled buffer 16-byte aligned
+
+
+def test_batch_plan_argmax_fields(lib):
+    """A problem's argmax: workspace of w4a16_workspace_bytes(N, T) bytes,
+    16-byte aligned; argmax_val needs argmax_id; ids and values 4-byte aligned."""
+    T, N, K = 4, 248320, 5120
+    need = lib.w4a16_workspace_bytes(N, T)
+    assert need == (N + 15) // 16 * T * 8
+    head = lambda am=A, av=A, ws=A, wb=need: Problem(A, None, A, A, N, K, 1, 0, am, av, ws, wb)
+    body = Problem(A, None, A, A, 7168, 5120, 1, 0)
+    assert plan(lib, [body, head()], T) == OK
+    assert plan(lib, [body, head(av=None)], T) == OK
+    assert plan(lib, [body, head(am=None, av=None, ws=None, wb=0)], T) == OK   # no argmax: workspace unused
+    assert plan(lib, [head(am=None)], T) == NULLP                              # value without id
+    assert plan(lib, [head(ws=None)], T) == WS and plan(lib, [head(wb=need - 1)], T) == WS
+    assert plan(lib, [head(ws=A + 8)], T) == WS
+    assert plan(lib, [head(am=A + 2)], T) == ALIGN and plan(lib, [head(av=A + 1)], T) == ALIGN
 
 
 def test_epilogue_arguments_rejected_on_the_host(lib):

@@ -80,3 +80,44 @@ def test_batch_rejects_bad_tables(w4):
     junk = torch.zeros(256, dtype=torch.uint8)
     junk_dev = junk.cuda()
     assert lib.w4a16_matmul_batch(junk.data_ptr(), junk_dev.data_ptr(), None) == 2  # not a table
+
+
+@pytest.mark.parametrize("T,tiled", [(1, True), (4, True), (8, True), (4, False), (16, True)])
+def test_batch_with_lm_head_argmax(w4, T, tiled):
+    """A verify pass in one grouped launch: some projections plus the full
+    lm_head with its per-row argmax.  The head's scores equal a single
+    head_gather launch's bit for bit (the same per-tile arithmetic), its
+    argmax equals that launch's and the host argmax of the scores, and the
+    other problems match the oracle."""
+    from test_gpu_parity import lm_head
+
+    say(f"batch + lm_head argmax T={T} tiled={tiled}")
+    p, s, pd, sd = lm_head()
+    n, k = synth.LM_HEAD
+    x = dev(synth.activations(synth.TID_LM_HEAD + 60 + T, T, k))
+    hw = w4.repack_tiled(pd, sd) if tiled else None
+    probs, host_side = build_case(T, 800 + T)
+    if tiled:
+        probs = [(w4.repack_tiled(pp, ss), None, xx, yy) for pp, ss, xx, yy in probs]
+    y = torch.full((T, n), float("nan"), dtype=torch.float32, device="cuda")
+    am_id = torch.full((T,), -7, dtype=torch.int32, device="cuda")
+    am_val = torch.full((T,), 7.0, dtype=torch.float32, device="cuda")
+    ws = torch.empty(w4.workspace_bytes(n, T), dtype=torch.uint8, device="cuda")
+    head = (hw, None, x, y, am_id, am_val, ws) if tiled else (pd, sd, x, y, am_id, am_val, ws)
+    b = w4.Batch(probs[:3] + [head] + probs[3:], T)
+    b.run()
+    if tiled:
+        y1, i1, v1 = w4.head_gather_tiled(hw, x, scores=True, argmax=True)
+    else:
+        y1, i1, v1 = w4.head_gather(pd, sd, x, scores=True, argmax=True)
+    yh = host(y)
+    assert np.array_equal(yh, host(y1)), "scores differ from the single launch"
+    assert np.array_equal(host(am_id), host(i1)) and np.array_equal(host(am_val), host(v1))
+    own, _, _ = oracle.argmax(yh.astype(np.float64))
+    assert np.array_equal(host(am_id), own)
+    assert np.array_equal(host(am_val), yh[np.arange(T), host(am_id)])
+    check_outputs([(None, None, None, yy) for *_, yy in probs], host_side, f"batch with head T={T}")
+    # replay: the same ids again (the workspace holds no state between launches)
+    am_id.fill_(-7)
+    b.run()
+    assert np.array_equal(host(am_id), host(i1))

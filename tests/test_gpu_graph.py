@@ -2,7 +2,8 @@
 
 The library enqueues only kernels (no memset, no allocation, no
 synchronisation), so its calls can be captured.  The graph holds single
-matmuls in both layouts, a grouped launch, the gathered head with argmax,
+matmuls in both layouts, grouped launches (one with a problem's argmax),
+the gathered head with argmax,
 the top-k and greedy acceptance; it is replayed several times with eager
 work and synchronisations between the replays, and every replay is compared
 bit for bit with the eager run of the same calls.
@@ -47,6 +48,12 @@ def test_graph_replays_match_eager(w4):
     tws = torch.empty(w4.topk_workspace_bytes(9000, T, 32), dtype=torch.uint8, device="cuda")
     draft = dev(np.array([1, 2, 3], np.int32))
     batch = w4.Batch([(pd1, sd1, x1, yb1), (pd2, sd2, x2, yb2)], T)
+    yba = torch.empty((T, 40000), dtype=torch.float32, device="cuda")
+    ba_id = torch.empty(T, dtype=torch.int32, device="cuda")
+    ba_val = torch.empty(T, dtype=torch.float32, device="cuda")
+    ba_ws = torch.empty(w4.workspace_bytes(40000, T), dtype=torch.uint8, device="cuda")
+    yb1t = torch.empty_like(yb1)
+    batch_am = w4.Batch([(tw1, None, x1, yb1t), (twh, None, xh, yba, ba_id, ba_val, ba_ws)], T)
     state = {}
 
     def calls(stream):
@@ -54,11 +61,12 @@ def test_graph_replays_match_eager(w4):
         w4.matmul_tiled(tw1, x1, out=y1t, stream=stream)
         w4.matmul(pd2, sd2, x2, out=y2, stream=stream)
         batch.run(stream)
+        batch_am.run(stream)
         _, am, av = w4.head_gather_tiled(twh, xh, row_ids=ids, scores=True, argmax=True, out=yh, workspace=ws,
                                          stream=stream)
         ti, tv = w4.topk(yh, 32, row_ids=ids, workspace=tws, stream=stream)
         acc, tok = w4.greedy_accept(am, draft, 1, T, stream=stream)
-        state["out"] = (am, av, ti, tv, acc, tok)
+        state["out"] = (am, av, ti, tv, acc, tok, yb1t, yba, ba_id, ba_val)
 
     def snapshot():
         torch.cuda.synchronize()

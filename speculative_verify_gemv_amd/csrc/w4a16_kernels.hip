@@ -266,8 +266,10 @@ int shared_waves(int T, int64_t K) {
 // Default matrix-core tiling of a single launch (cus: compute units of the
 // device), from the MI355X sweeps.  Tiled weights of at least 4,096 tiles
 // (the vocabulary head) run workgroups of 16 waves x 4 tiles at every T
-// (with the argmax too); mid-size tiled matrices shared workgroups of four
-// waves of one tile.  Row-major weights: the full vocabulary head (15,520
+// (with the argmax too); mid-size matrices shared workgroups of one tile
+// per wave, four waves at small T and sixteen from T = 5 (tiled) or T = 8
+// (row-major), where one staging of the activations then serves 16 tiles
+// (gate_up at T = 8: 27 us against 34, at T = 16: 31 against 53).  Row-major weights: the full vocabulary head (15,520
 // tiles) is fastest with eight waves of four tiles each.  Shorter matrices
 // split K over the waves of a workgroup so that they still put ~12 waves of
 // weight loads on every CU, up to 8 token rows; above that a wave's staged
@@ -283,6 +285,8 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
     t = Tile{kShared, 4, 8};
   else if (tiles >= 4096)
     t = Tile{kShared, 2, 8};
+  else if (tiles >= 1024 && (a.tiled ? T > 4 : T >= 8))  // 16 waves share one staging of the activations
+    t = Tile{kShared, 1, 16};
   else if (tiles >= 1024 || T > 8)  // above 8 rows a split wave stages too little K per slice
     t = Tile{kShared, 1, 4};
   else

@@ -159,7 +159,8 @@ bool parse_tile(const char* text, Tile* t) {
 // range when half a CU's LDS allows it, else a multiple of 8; swizzled
 // chunks, no padding between token rows) and later its partial sums; the
 // final values overwrite wave 0's partials in place.  At most half a CU, so
-// that two workgroups share a CU.
+// that two workgroups share a CU (the split kernels are built for at most
+// eight waves).
 static void plan_split(GemvArgs& a, int T, int rt, int nw_max, Plan* p) {
   const int cap = kCuLds / 2;
   for (int nw = std::max(1, std::min(nw_max, a.G));; --nw) {

@@ -211,3 +211,25 @@ def test_draft_head_t16(w4):
     y, am = host(y), host(am)
     assert_parity(y, y_ref, a_ref, "draft head T=16")
     check_argmax(am, y, y_ref, ids, "draft head T=16")
+
+
+@pytest.mark.parametrize("T", [1, 8, 16])
+def test_maximum_k(w4, T):
+    """K = 2^20, the largest the ABI accepts (8,192 groups: hundreds of
+    staged slices per wave), on a ragged 37-row matrix: every output against
+    the oracle in both layouts, and with the dot variant where it applies."""
+    N, K = 37, 1 << 20
+    say(f"maximum K={K} T={T}")
+    p, s = synth.weight(5600 + T, N, K)
+    x = synth.activations(5600 + T, T, K)
+    y_ref, a_ref = oracle.matmul(p, s, x)
+    y_rm, y_t = both_layouts(w4, p, s, x)
+    assert_parity(y_rm, y_ref, a_ref, f"max K row-major T={T}")
+    assert_parity(y_t, y_ref, a_ref, f"max K tiled T={T}")
+    if T <= 8:
+        w4.set_variant("dot")
+        try:
+            y_dot = host(w4.matmul(dev(p), dev(s), dev(x)))
+        finally:
+            w4.set_variant("auto")
+        assert_parity(y_dot, y_ref, a_ref, f"max K dot T={T}")

@@ -70,10 +70,11 @@ typedef enum {
 } w4a16_status;
 
 /* Kernel variants.  Both compute the same values within the tolerance above.
- * AUTO runs the matrix-core kernels, measured faster on MI355X at every T
- * (about even with the dot variant at T = 1 on short matrices, 1.7-12x faster
- * from T = 4).  The dot variant covers T <= 8; calls with more activation
- * rows run the matrix-core kernels whatever the selection. */
+ * AUTO runs the matrix-core kernels: on MI355X they are faster at every T
+ * except on short matrices at T = 1 (where the dot variant is a few percent
+ * faster), and 1.7-11x faster from T = 4.  The dot variant covers T <= 8;
+ * calls with more activation rows run the matrix-core kernels whatever the
+ * selection. */
 typedef enum {
   W4A16_VARIANT_AUTO = 0,
   W4A16_VARIANT_DOT = 1, /* VALU dot products, split-K across lanes, cross-lane reduction */

@@ -43,8 +43,8 @@
 //    the activations; in a "split" workgroup they split K over the same
 //    tiles and add their partial sums through LDS in wave order.
 //  * dot: lanes split a row's K in 16-byte chunks; v_dot2_f32_f16 forms each
-//    chunk's partial, which is scaled by its group scale; lanes are reduced
-//    with a butterfly across the wavefront.
+//    chunk's partial, which is scaled by its group scale; the 32 lanes of a
+//    row are reduced with DPP row operations and one ds_swizzle.
 //
 // Both reduce in an order fixed by (K, tiling) only, so results are
 // deterministic, and identical weight rows give identical outputs.
@@ -132,6 +132,27 @@ __device__ __forceinline__ unsigned absmax8(u4_t v) {
   m = __builtin_elementwise_max(m, __builtin_bit_cast(us2_t, v.z & 0x7FFF7FFFu));
   m = __builtin_elementwise_max(m, __builtin_bit_cast(us2_t, v.w & 0x7FFF7FFFu));
   return max((unsigned)m.x, (unsigned)m.y);
+}
+
+// One DPP lane move (row-local control; every lane of every row written).
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 32 lanes of each half-wave, every lane receiving the same
+// total: within each 16-lane DPP row, row_mirror (lane i with 15 - i), then
+// row_half_mirror (i with 7 - i in each half row), then quad_perm xor 2 and
+// xor 1, each an add fused with the lane move; then the two rows' totals
+// meet through ds_swizzle (xor 16 within 32 lanes).  A fixed order, and by
+// symmetry the same value in every lane.
+__device__ __forceinline__ float sum32(float v) {
+  v += dpp_move<0x140>(v);  // row_mirror
+  v += dpp_move<0x141>(v);  // row_half_mirror
+  v += dpp_move<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_move<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  // ds_swizzle bit mode: and_mask 0x1F, or_mask 0, xor_mask 0x10
+  return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
 }
 
 __device__ __forceinline__ unsigned wave_max(unsigned m) {
@@ -508,11 +529,10 @@ __global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
     }
   }
 
-  // Butterfly across the L lanes of a row (fixed order).
+  // Sum across the L = 32 lanes of a row (fixed order).
+  static_assert(L == 32, "the lane reduction covers 32 lanes per row");
 #pragma unroll
-  for (int t = 0; t < TT; ++t)
-#pragma unroll
-    for (int off = L / 2; off >= 1; off >>= 1) acc[t] += __shfl_xor(acc[t], off);
+  for (int t = 0; t < TT; ++t) acc[t] = sum32(acc[t]);
 
   float* fin = reinterpret_cast<float*>(smem);  // reused after the last slice
   __syncthreads();

@@ -56,7 +56,7 @@ typedef struct ihipStream_t* hipStream_t; /* same definition as the HIP runtime'
 
 #define W4A16_GROUP 128      /* columns per bf16 scale */
 #define W4A16_MAX_T 16       /* activation rows per weight read */
-#define W4A16_ABI_VERSION 4
+#define W4A16_ABI_VERSION 5
 
 typedef enum {
   W4A16_OK = 0,
@@ -238,6 +238,27 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
 
 /* W4A16_ERR_BAD_SHAPE if table_host is not a table written by w4a16_batch_plan. */
 w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, hipStream_t stream);
+
+/*
+ * The same grouped launch with a device workspace for the activations: from
+ * T = 9 on, the plan converts every problem's activations once per launch
+ * (a small kernel before the grouped one, on the same stream) into the
+ * workspace, and the workgroups copy them from there straight into LDS
+ * instead of each converting its own copy (exact fp16 times a power of two
+ * per activation row, chosen over the row's whole K; results within the
+ * tolerance of w4a16_matmul, and bit for bit those of w4a16_matmul_batch
+ * unless a row's values span more than about 2^28 and the workgroups stage
+ * its K in slices, each with its own power of two).  w4a16_batch_workspace_bytes(table_host) gives
+ * the size (0 when the plan stages without one, and for a table that is not
+ * one): T * K * 2 + 16 bytes per problem, plus 16.  The workspace is device
+ * memory, 16-byte aligned, needs no initialisation, holds nothing between
+ * launches, and must not be shared by launches that may run concurrently.
+ * With a size-0 plan, workspace may be NULL and the call is
+ * w4a16_matmul_batch.
+ */
+size_t w4a16_batch_workspace_bytes(const void* table_host);
+w4a16_status w4a16_matmul_batch_ws(const void* table_host, const void* table_dev, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /*
  * Verify epilogue: what a speculative cycle does with the head's scores

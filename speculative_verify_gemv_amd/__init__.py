@@ -78,6 +78,10 @@ def load_library():
         lib.w4a16_greedy_accept.restype = i32
         lib.w4a16_draft_union.argtypes = [vp, i32, vp, i32, i64, vp, vp, vp]
         lib.w4a16_draft_union.restype = i32
+        lib.w4a16_batch_workspace_bytes.argtypes = [vp]
+        lib.w4a16_batch_workspace_bytes.restype = sz
+        lib.w4a16_matmul_batch_ws.argtypes = [vp, vp, vp, sz, vp]
+        lib.w4a16_matmul_batch_ws.restype = i32
         lib.w4a16_stream_read.argtypes = [vp, sz, vp, i32, vp]
         lib.w4a16_stream_read.restype = i32
         _lib = lib
@@ -327,9 +331,19 @@ class Batch:
         self.device = self.host.to(problems[0][2].device, non_blocking=False)
         self.T = T
         self.count = len(problems)
+        wsb = lib.w4a16_batch_workspace_bytes(self.host.data_ptr())
+        self.workspace = torch.empty(wsb, dtype=torch.uint8, device=self.device.device) if wsb else None
 
-    def run(self, stream=None) -> None:
-        s = load_library().w4a16_matmul_batch(self.host.data_ptr(), self.device.data_ptr(), _stream(stream))
+    def run(self, stream=None, staged: bool = True) -> None:
+        """One grouped launch.  staged: with the plan's activation workspace
+        (w4a16_matmul_batch_ws) when it has one; False: every workgroup
+        converts its own activations (w4a16_matmul_batch)."""
+        lib = load_library()
+        if staged and self.workspace is not None:
+            s = lib.w4a16_matmul_batch_ws(self.host.data_ptr(), self.device.data_ptr(), self.workspace.data_ptr(),
+                                          self.workspace.numel(), _stream(stream))
+        else:
+            s = lib.w4a16_matmul_batch(self.host.data_ptr(), self.device.data_ptr(), _stream(stream))
         if s:
             raise W4A16Error(s, "w4a16_matmul_batch")
 

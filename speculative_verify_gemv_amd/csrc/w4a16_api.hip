@@ -143,7 +143,8 @@ struct TableHeader {
   int32_t lds;
   int32_t n_argmax;  // argmax records after the count argument records (host copy)
   int64_t grid;
-  int64_t reserved[2];
+  int64_t ws_bytes;  // workspace w4a16_matmul_batch_ws uses (0: none)
+  int64_t reserved;
 };
 static_assert(sizeof(TableHeader) == 64, "table header size");
 
@@ -154,7 +155,14 @@ struct ArgmaxRecord {
   int32_t* id;
   float* val;
 };
-static_assert(sizeof(ArgmaxRecord) == 32 && sizeof(w4a16::GemvArgs) == 128, "batch table record sizes");
+static_assert(sizeof(ArgmaxRecord) == 32 && sizeof(w4a16::GemvArgs) == 144, "batch table record sizes");
+
+// Grouped launches from this many activation rows on stage the activations
+// from a workspace converted once per launch (direct global-to-LDS copies
+// in the workgroups); below it the workgroups convert their own.  Measured
+// on the 27B-class body pass: +0.6% at T = 12, +2.5% at T = 16; at T = 8 the
+// conversion launch costs what the copies save.
+constexpr int kWorkspaceMinT = 9;
 
 // Tile of grouped launches, from the MI355X sweeps.  All problems tiled:
 // at T <= 2 shared workgroups of one tile per wave; above, run workgroups of
@@ -174,6 +182,59 @@ w4a16::Tile batch_tile(int T, bool all_tiled, int64_t kmax) {
   w4a16::Tile o;
   if (w4a16::parse_tile(std::getenv("W4A16_BATCH_TILE"), &o)) t = o;
   return t;
+}
+
+// The header of a table written by w4a16_batch_plan, or null.
+const TableHeader* valid_table(const void* table_host) {
+  if (!table_host || !aligned(table_host, 8)) return nullptr;
+  const auto* hdr = static_cast<const TableHeader*>(table_host);
+  if (hdr->magic != kTableMagic || hdr->version != W4A16_ABI_VERSION || hdr->count < 1 ||
+      hdr->count > W4A16_MAX_BATCH || hdr->T < 1 || hdr->T > W4A16_MAX_T || hdr->grid < 1 || hdr->ws_bytes < 0 ||
+      hdr->n_argmax < 0 || hdr->n_argmax > hdr->count)
+    return nullptr;
+  return hdr;
+}
+
+// A planned grouped launch: with_ws (w4a16_matmul_batch_ws) and a table that
+// plans a workspace convert the activations into it first.
+w4a16_status run_batch(const void* table_host, const void* table_dev, void* workspace, size_t workspace_bytes,
+                       bool with_ws, hipStream_t stream) {
+  if (!table_host || !table_dev) return W4A16_ERR_NULL_POINTER;
+  if (!aligned(table_dev, 16) || !aligned(table_host, 8)) return W4A16_ERR_MISALIGNED;
+  const TableHeader* hdr = valid_table(table_host);
+  if (!hdr) return W4A16_ERR_BAD_SHAPE;
+  const bool staged = with_ws && hdr->ws_bytes > 0;
+  if (staged && (!workspace || !aligned(workspace, 16) || workspace_bytes < (size_t)hdr->ws_bytes))
+    return W4A16_ERR_WORKSPACE;
+  w4a16::Plan p{};
+  if (hdr->variant != w4a16::kSplit && hdr->variant != w4a16::kShared && hdr->variant != w4a16::kRun)
+    return W4A16_ERR_BAD_SHAPE;
+  if (hdr->rt != 1 && hdr->rt != 2 && hdr->rt != 4) return W4A16_ERR_BAD_SHAPE;
+  if (hdr->threads < 64 || hdr->threads > 1024 || hdr->threads % 64 || hdr->lds < 0 || hdr->lds > 163840)
+    return W4A16_ERR_BAD_SHAPE;
+  if (hdr->tiled != 0 && (hdr->tiled != 1 || hdr->rt != 1)) return W4A16_ERR_BAD_SHAPE;
+  if (w4a16_status s = check_device()) return s;
+  p.variant = hdr->variant;
+  p.rt = hdr->rt;
+  p.tiled = hdr->tiled == 1;
+  p.threads = hdr->threads;
+  p.grid = hdr->grid;
+  p.lds = hdr->lds;
+  const auto* args = reinterpret_cast<const w4a16::GemvArgs*>(static_cast<const TableHeader*>(table_dev) + 1);
+  if (staged) {
+    p.ws = static_cast<const unsigned char*>(workspace);
+    if (w4a16::launch_stage_x(args, hdr->count, hdr->T, static_cast<unsigned char*>(workspace), stream) !=
+        hipSuccess)
+      return W4A16_ERR_HIP;
+  }
+  if (w4a16::launch_batch(args, hdr->count, p, hdr->T, stream) != hipSuccess) return W4A16_ERR_HIP;
+  const auto* recs = reinterpret_cast<const ArgmaxRecord*>(reinterpret_cast<const w4a16::GemvArgs*>(hdr + 1) +
+                                                           hdr->count);
+  for (int32_t i = 0; i < hdr->n_argmax; ++i)
+    if (w4a16::launch_argmax_final(recs[i].partial, recs[i].nparts, hdr->T, recs[i].id, recs[i].val, stream) !=
+        hipSuccess)
+      return W4A16_ERR_HIP;
+  return W4A16_OK;
 }
 
 }  // namespace
@@ -322,7 +383,7 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
   // not fit runs shared workgroups inside the run kernel); a plan that still
   // differs between problems falls back to shared workgroups.
   for (int attempt = 0; attempt < 2; ++attempt) {
-    int64_t grid = 0;
+    int64_t grid = 0, ws_bytes = 16;  // the workspace starts with 16 zero bytes
     int lds = 0, threads = 64, rt = 0, n_argmax = 0;
     bool uniform = true;
     for (int32_t i = 0; i < count; ++i) {
@@ -331,6 +392,9 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
       w4a16::GemvArgs a = gemv_args(q.packed_u4, tiled ? nullptr : q.scales_bf16, tiled, q.x_bf16, q.y_f32,
                                     nullptr, q.N, q.N, q.K);
       a.partial = q.argmax_id ? static_cast<int2*>(q.workspace) : nullptr;
+      a.x16_off = ws_bytes;  // pre-converted activations, then the row exponents
+      a.e_off = ws_bytes + (int64_t)T * q.K * 2;
+      ws_bytes = a.e_off + (((int64_t)T * 4 + 15) & ~15LL);
       const w4a16::Plan p = w4a16::plan_tile(a, T, bt, all_tiled, true);
       uniform = uniform && p.variant == bt.shape;
       rt = p.rt;
@@ -347,43 +411,24 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
     }
     if (grid > 0x7fffffffLL) return W4A16_ERR_BAD_SHAPE;
     *hdr = TableHeader{kTableMagic, W4A16_ABI_VERSION, count, T, bt.shape, rt, all_tiled ? 1 : 0, threads, lds,
-                       n_argmax, grid, {0, 0}};
+                       n_argmax, grid, T >= kWorkspaceMinT && bt.shape != w4a16::kSplit ? ws_bytes : 0, 0};
     return W4A16_OK;
   }
   return W4A16_ERR_BAD_SHAPE;  // not reached: shared tiles always plan
 }
 
+size_t w4a16_batch_workspace_bytes(const void* table_host) {
+  const TableHeader* hdr = valid_table(table_host);
+  return hdr ? (size_t)hdr->ws_bytes : 0;
+}
+
 w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, hipStream_t stream) {
-  if (!table_host || !table_dev) return W4A16_ERR_NULL_POINTER;
-  if (!aligned(table_dev, 16) || !aligned(table_host, 8)) return W4A16_ERR_MISALIGNED;
-  const auto* hdr = static_cast<const TableHeader*>(table_host);
-  if (hdr->magic != kTableMagic || hdr->version != W4A16_ABI_VERSION || hdr->count < 1 ||
-      hdr->count > W4A16_MAX_BATCH || hdr->T < 1 || hdr->T > W4A16_MAX_T || hdr->grid < 1)
-    return W4A16_ERR_BAD_SHAPE;
-  if (w4a16_status s = check_device()) return s;
-  w4a16::Plan p{};
-  if (hdr->variant != w4a16::kSplit && hdr->variant != w4a16::kShared && hdr->variant != w4a16::kRun)
-    return W4A16_ERR_BAD_SHAPE;
-  if (hdr->rt != 1 && hdr->rt != 2 && hdr->rt != 4) return W4A16_ERR_BAD_SHAPE;
-  if (hdr->threads < 64 || hdr->threads > 1024 || hdr->threads % 64 || hdr->lds < 0 || hdr->lds > 163840)
-    return W4A16_ERR_BAD_SHAPE;
-  if (hdr->tiled != 0 && (hdr->tiled != 1 || hdr->rt != 1)) return W4A16_ERR_BAD_SHAPE;
-  p.variant = hdr->variant;
-  p.rt = hdr->rt;
-  p.tiled = hdr->tiled == 1;
-  p.threads = hdr->threads;
-  p.grid = hdr->grid;
-  p.lds = hdr->lds;
-  if (hdr->n_argmax < 0 || hdr->n_argmax > hdr->count) return W4A16_ERR_BAD_SHAPE;
-  const auto* args = reinterpret_cast<const w4a16::GemvArgs*>(static_cast<const TableHeader*>(table_dev) + 1);
-  if (w4a16::launch_batch(args, hdr->count, p, hdr->T, stream) != hipSuccess) return W4A16_ERR_HIP;
-  const auto* recs = reinterpret_cast<const ArgmaxRecord*>(reinterpret_cast<const w4a16::GemvArgs*>(hdr + 1) +
-                                                           hdr->count);
-  for (int32_t i = 0; i < hdr->n_argmax; ++i)
-    if (w4a16::launch_argmax_final(recs[i].partial, recs[i].nparts, hdr->T, recs[i].id, recs[i].val, stream) !=
-        hipSuccess)
-      return W4A16_ERR_HIP;
-  return W4A16_OK;
+  return run_batch(table_host, table_dev, nullptr, 0, false, stream);
+}
+
+w4a16_status w4a16_matmul_batch_ws(const void* table_host, const void* table_dev, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream) {
+  return run_batch(table_host, table_dev, workspace, workspace_bytes, true, stream);
 }
 
 size_t w4a16_topk_workspace_bytes(int64_t n, int32_t T, int32_t k) {

@@ -457,6 +457,39 @@ __device__ __forceinline__ void stage_shared(const GemvArgs& a, _Float16* xs, in
   __syncthreads();
 }
 
+// Staging from a grouped launch's workspace: the activations were converted
+// once for the whole launch (w4a16_stage_x_kernel): row t of the problem is
+// K/8 16-byte chunks of fp16 in slot order, scaled by 2^E[t].  The chunks of
+// slice [gs, ge) go straight from global memory into LDS
+// (global_load_lds_dwordx4: no registers, no conversion, no decision to
+// share), each wave filling 64 consecutive chunk positions of one staged
+// row: position p of row t takes chunk swz(t, p) (the swizzle is its own
+// inverse), and the ring padding takes the workspace's zero chunk.  Ends
+// with a barrier.
+template <int TT>
+__device__ __forceinline__ void stage_dma(const GemvArgs& a, const unsigned char* ws, _Float16* xs, int gs, int ge,
+                                          int (&E)[TT]) {
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int n8 = a.K / 8, n = (ge - gs) * (kGroup / 8);
+  const int dst_row = a.xs_stride / 8, total = TT * dst_row;  // dst_row: a multiple of 128 chunks
+  const u4_t* src = reinterpret_cast<const u4_t*>(ws + a.x16_off) + gs * (kGroup / 8);
+  const u4_t* zero = reinterpret_cast<const u4_t*>(ws);
+  unsigned char* lds = reinterpret_cast<unsigned char*>(xs);
+  for (int base = wave * 64; base < total; base += (int)blockDim.x) {
+    const int t = base / dst_row;
+    const int c = swz(t, base - t * dst_row + lane);
+    const u4_t* from = c < n ? src + t * n8 + c : zero;
+    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(from),
+                                     (__attribute__((address_space(3))) void*)(lds + (int64_t)base * 16), 16, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  __syncthreads();
+  const int* ep = reinterpret_cast<const int*>(ws + a.e_off);
+#pragma unroll
+  for (int t = 0; t < TT; ++t) E[t] = __builtin_amdgcn_readfirstlane(ep[t]);
+}
+
 // RW rows per wave, L = 64/RW lanes per row; a lane takes the row's 16-byte
 // chunks li, li+L, li+2L, ...; CPL bounds the chunks per lane per slice.
 // Built for TT <= kDotMaxT (its per-lane sums grow with TT; more rows go to
@@ -612,7 +645,8 @@ __device__ __forceinline__ int scale_off(const GemvArgs& a, int g) {
 template <int TT, int RT, bool VS, bool SHARED, int LAY>
 __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* const (&cp)[RT],
                                              const uint16_t* const (&sp)[RT], _Float16* xs, int g_begin, int g_end,
-                                             int lane, int trow, int kq, float (&acc)[RT][4]) {
+                                             int lane, int trow, int kq, float (&acc)[RT][4],
+                                             const unsigned char* ws = nullptr) {
   constexpr int PD = kRing;
   int E[TT];
   u4_t q[PD];
@@ -634,7 +668,10 @@ __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* cons
     }
     if constexpr (SHARED) {
       if (sb != g_begin) __syncthreads();  // every wave is done with the previous slice
-      stage_shared<TT>(a, xs, sb, se, E);
+      if (ws)
+        stage_dma<TT>(a, ws, xs, sb, se, E);
+      else
+        stage_shared<TT>(a, xs, sb, se, E);
     } else {
       lds_fence();
       u4_t held;
@@ -811,7 +848,8 @@ __device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, u
 // activations per K slice, so the fp16 conversion is paid once per
 // 16 * RT * waves rows.  Every output comes straight from one wave.
 template <int TT, int RT, int LAY>
-__device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
+__device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem,
+                                                 const unsigned char* ws = nullptr) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwv = blockDim.x >> 6;
@@ -829,9 +867,9 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[tl][r] = 0.0f;
   if (LAY == kLayTiled || a.vec_scales)
-    stream_tiles<TT, RT, true, true, LAY>(a, cp, sp, xs, 0, a.G, lane, trow, kq, acc);
+    stream_tiles<TT, RT, true, true, LAY>(a, cp, sp, xs, 0, a.G, lane, trow, kq, acc, ws);
   else if constexpr (LAY != kLayTiled)
-    stream_tiles<TT, RT, false, true, LAY>(a, cp, sp, xs, 0, a.G, lane, trow, kq, acc);
+    stream_tiles<TT, RT, false, true, LAY>(a, cp, sp, xs, 0, a.G, lane, trow, kq, acc, ws);
 
   float bv[TT];
   int bi[TT];
@@ -1013,7 +1051,8 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
 // so the waves stay on adjacent tiles.  All of K is staged once (the planner
 // guarantees it fits).
 template <int TT, int LAY>
-__device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
+__device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem,
+                                              const unsigned char* ws = nullptr) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwv = blockDim.x >> 6;
@@ -1032,7 +1071,10 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
     ring_prologue<LAY>(a, cp, sp, q, sv);
   }
   int E[TT];
-  stage_shared<TT>(a, xs, 0, a.G, E);
+  if (ws)
+    stage_dma<TT>(a, ws, xs, 0, a.G, E);
+  else
+    stage_shared<TT>(a, xs, 0, a.G, E);
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
   float bv[4];
   int bi[4];
@@ -1086,10 +1128,11 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4))) 
 // Grouped launch of run workgroups: workgroup b runs workgroup b - wg_start of
 // the last problem whose wg_start <= b; a problem planned without a run
 // (its activations do not fit the LDS at once) runs a shared workgroup of one
-// tile per wave instead.
+// tile per wave instead.  With ws set, the activations come pre-converted
+// from that workspace (stage_dma).
 template <int TT, int LAY>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
-w4a16_run_batch_kernel(const GemvArgs* __restrict__ table, int count) {
+w4a16_run_batch_kernel(const GemvArgs* __restrict__ table, int count, const unsigned char* __restrict__ ws) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int64_t b = blockIdx.x;
   int lo = 0, hi = count - 1;
@@ -1102,15 +1145,16 @@ w4a16_run_batch_kernel(const GemvArgs* __restrict__ table, int count) {
   }
   const GemvArgs a = table[lo];
   if (a.run_tiles > 0)
-    run_workgroup<TT, LAY>(a, b - a.wg_start, smem);
+    run_workgroup<TT, LAY>(a, b - a.wg_start, smem, ws);
   else  // activations too large for one staging: whole-K slices, one tile per wave
-    shared_workgroup<TT, 1, LAY>(a, b - a.wg_start, smem);
+    shared_workgroup<TT, 1, LAY>(a, b - a.wg_start, smem, ws);
 }
 
 template <int TT, int RT, bool SHARED, int LAY>
-__device__ __forceinline__ void tile_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
+__device__ __forceinline__ void tile_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem,
+                                               const unsigned char* ws = nullptr) {
   if constexpr (SHARED)
-    shared_workgroup<TT, RT, LAY>(a, wg, smem);
+    shared_workgroup<TT, RT, LAY>(a, wg, smem, ws);
   else
     split_workgroup<TT, RT, LAY>(a, wg, smem);
 }
@@ -1123,11 +1167,12 @@ __global__ void __launch_bounds__(SHARED && RT == 1 ? 1024 : 512)
 }
 
 // Grouped launch: workgroup b runs tile b - wg_start of the last problem whose
-// wg_start <= b.
+// wg_start <= b (shared workgroups stage from the workspace ws when it is set).
 template <int TT, int RT, bool SHARED, int LAY>
 __global__ void __launch_bounds__(SHARED && RT == 1 ? 1024 : 512)
     __attribute__((amdgpu_waves_per_eu(SHARED && RT == 1 ? 4 : 1))) w4a16_tile_batch_kernel(const GemvArgs* __restrict__ table,
-                                                                                    int count) {
+                                                                                    int count,
+                                                                                    const unsigned char* __restrict__ ws) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int64_t b = blockIdx.x;
   int lo = 0, hi = count - 1;
@@ -1139,7 +1184,7 @@ __global__ void __launch_bounds__(SHARED && RT == 1 ? 1024 : 512)
       hi = mid - 1;
   }
   const GemvArgs a = table[lo];
-  tile_workgroup<TT, RT, SHARED, LAY>(a, b - a.wg_start, smem);
+  tile_workgroup<TT, RT, SHARED, LAY>(a, b - a.wg_start, smem, ws);
 }
 
 // ------------------------------------------------------------- dispatch ----
@@ -1154,7 +1199,7 @@ hipError_t launch_tiles(const GemvArgs& a, const GemvArgs* table, int count, con
     if (e != hipSuccess) return e;
   }
   if (table)
-    hipLaunchKernelGGL((w4a16_tile_batch_kernel<TT, RT, SHARED, LAY>), grid, block, p.lds, s, table, count);
+    hipLaunchKernelGGL((w4a16_tile_batch_kernel<TT, RT, SHARED, LAY>), grid, block, p.lds, s, table, count, p.ws);
   else
     hipLaunchKernelGGL((w4a16_tile_kernel<TT, RT, SHARED, LAY>), grid, block, p.lds, s, a);
   return hipGetLastError();
@@ -1184,7 +1229,7 @@ hipError_t launch_run(const GemvArgs& a, const GemvArgs* table, int count, const
     if (e != hipSuccess) return e;
   }
   if (table)
-    hipLaunchKernelGGL((w4a16_run_batch_kernel<TT, LAY>), grid, block, p.lds, s, table, count);
+    hipLaunchKernelGGL((w4a16_run_batch_kernel<TT, LAY>), grid, block, p.lds, s, table, count, p.ws);
   else
     hipLaunchKernelGGL((w4a16_run_kernel<TT, LAY>), grid, block, p.lds, s, a);
   return hipGetLastError();

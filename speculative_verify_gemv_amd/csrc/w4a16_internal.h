@@ -34,6 +34,8 @@ struct GemvArgs {
   int64_t tile_bytes;      // tiled layout: bytes per 16-row tile
   int32_t run_tiles;       // run workgroups: tiles per wave
   int32_t reserved;
+  int64_t x16_off;         // grouped launch with a workspace: byte offsets in it of this
+  int64_t e_off;           //    problem's pre-converted activations and their row exponents
 };
 
 // Tiled weight layout (see include/w4a16.h): per 16-row tile, chunks of up
@@ -69,6 +71,7 @@ struct Plan {
   int64_t grid;  // workgroups
   int lds;       // dynamic LDS bytes
   bool tiled;    // every problem is in the tiled layout: kernels built for it alone
+  const unsigned char* ws = nullptr;  // grouped launch: workspace with pre-converted activations
 };
 
 // Parse "split,rt,waves" or "shared,rt,waves" (rt 1, 2 or 4; waves 1-8, or
@@ -98,6 +101,9 @@ hipError_t launch_batch(const GemvArgs* table_dev, int count, const Plan& p, int
 hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, const int32_t* row_ids, int64_t n_rows,
                          int64_t N, int32_t K, uint8_t* tiled, hipStream_t s);
 hipError_t launch_argmax_final(const int2* partial, int64_t nparts, int T, int32_t* id, float* val, hipStream_t s);
+// Grouped launch with a workspace: every problem's activations converted
+// once (stage_x_kernel) into the workspace, T rows per problem.
+hipError_t launch_stage_x(const GemvArgs* table_dev, int count, int T, unsigned char* ws, hipStream_t s);
 
 // Streaming read of bytes (a multiple of 16) over `workgroups` workgroups
 // of 256 threads; sink holds workgroups * 256 words.

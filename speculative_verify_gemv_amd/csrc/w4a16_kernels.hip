@@ -105,6 +105,59 @@ __global__ void __launch_bounds__(256) w4a16_argmax_final(const int2* partial, i
   }
 }
 
+// -------------------------------------------------- activation staging ----
+
+// The activations of every problem of a grouped launch, converted once into
+// the launch's workspace: workgroup b converts row t = b % T of problem
+// b / T to fp16 in slot order (chunk c of the row at 16-byte index c from
+// a.x16_off), scaled by 2^E with E = kDirectE when every value of the row
+// converts exactly that way, else the row's own exponent from its largest
+// magnitude (slice_exponent), and stores E at a.e_off + 4t.  The same
+// conversions as the workgroups' own staging, decided per row over all of K.
+// Workgroup 0 also writes the 16 zero bytes at the start of the workspace
+// that the staging's ring padding reads.
+__global__ void __launch_bounds__(256) w4a16_stage_x_kernel(const GemvArgs* __restrict__ table, int T,
+                                                            unsigned char* __restrict__ ws) {
+  __shared__ unsigned any_bad;
+  __shared__ unsigned wave_m[4];
+  const int i = blockIdx.x / T, t = blockIdx.x % T;
+  const GemvArgs& a = table[i];
+  const int n8 = a.K / 8;
+  const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)t * a.K);
+  u4_t* dst = reinterpret_cast<u4_t*>(ws + a.x16_off) + (int64_t)t * n8;
+  if (blockIdx.x == 0 && threadIdx.x == 0) st_global(reinterpret_cast<u4_t*>(ws), u4_t{0u, 0u, 0u, 0u});
+  if (threadIdx.x == 0) any_bad = 0;
+  __syncthreads();
+  us2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+  constexpr int kInFlight = 4;  // independent 16-byte loads per thread at a time
+  for (int c0 = threadIdx.x; c0 < n8; c0 += kInFlight * 256) {
+    u4_t v[kInFlight];
+#pragma unroll
+    for (int j = 0; j < kInFlight; ++j)
+      if (c0 + j * 256 < n8) v[j] = ld_global(src + c0 + j * 256);
+#pragma unroll
+    for (int j = 0; j < kInFlight; ++j)
+      if (c0 + j * 256 < n8) {
+        range8(v[j], mx, mn);
+        st_global(dst + c0 + j * 256, convert8_exact(v[j]));
+      }
+  }
+  if (!range_ok(mx, mn)) atomicOr(&any_bad, 1u);
+  __syncthreads();
+  int E = kDirectE;
+  if (any_bad) {  // uniform: the row again with its own power of two
+    unsigned m = 0;
+    for (int c = threadIdx.x; c < n8; c += 256) m = max(m, absmax8(ld_global(src + c)));
+    m = wave_max(m);
+    if ((threadIdx.x & 63) == 0) wave_m[threadIdx.x >> 6] = m;
+    __syncthreads();
+    m = max(max(wave_m[0], wave_m[1]), max(wave_m[2], wave_m[3]));
+    E = slice_exponent(m);
+    for (int c = threadIdx.x; c < n8; c += 256) st_global(dst + c, convert8(ld_global(src + c), E));
+  }
+  if (threadIdx.x == 0) st_global(reinterpret_cast<int*>(ws + a.e_off) + t, E);
+}
+
 template <typename F>
 hipError_t for_t(int T, F&& f) {
   switch (T) {
@@ -373,6 +426,11 @@ hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, const in
   const int64_t total = tiles * ((int64_t)G * 64 + cdiv(G, kTileChunkGroups) * 16);
   hipLaunchKernelGGL(w4a16_repack_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, packed, scales, row_ids,
                      n_rows, N, K, tiled, tiled_tile_bytes(G), total);
+  return hipGetLastError();
+}
+
+hipError_t launch_stage_x(const GemvArgs* table_dev, int count, int T, unsigned char* ws, hipStream_t s) {
+  hipLaunchKernelGGL(w4a16_stage_x_kernel, dim3((unsigned)(count * T)), dim3(256), 0, s, table_dev, T, ws);
   return hipGetLastError();
 }
 

@@ -62,7 +62,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.w4a16_abi_version() == 4
+    assert lib.w4a16_abi_version() == 5
     for s in range(8):
         assert lib.w4a16_status_string(s)
     assert lib.w4a16_status_string(99) == b"unknown status"
@@ -258,3 +258,38 @@ def test_stream_read_arguments_rejected_on_the_host(lib):
     assert sr(s=None) == NULLP and sr(k=None) == NULLP
     assert sr(n=0) == SHAPE and sr(n=1000) == SHAPE and sr(w=0) == SHAPE and sr(w=65537) == SHAPE
     assert sr(s=A + 8) == ALIGN and sr(k=A + 2) == ALIGN
+
+
+def test_batch_workspace_planning_and_checks(lib):
+    """The activation workspace of a grouped launch: planned from T = 9 on,
+    T * K * 2 + 16 bytes per problem (activations, then the row exponents
+    padded to 16 bytes) after 16 zero bytes; w4a16_matmul_batch_ws rejects a
+    missing, misaligned or short workspace before touching the device."""
+    vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    lib.w4a16_batch_workspace_bytes.argtypes = [vp]
+    lib.w4a16_batch_workspace_bytes.restype = sz
+    lib.w4a16_matmul_batch_ws.argtypes = [vp, vp, vp, sz, vp]
+    lib.w4a16_matmul_batch_ws.restype = i32
+    shapes = [(7168, 5120), (5120, 17408), (17, 128)]
+    probs = [Problem(A, None, A, A, n, k, 1, 0) for n, k in shapes]
+
+    def table(T):
+        arr = (Problem * len(probs))(*probs)
+        nbytes = lib.w4a16_batch_table_bytes(len(probs))
+        buf = (ctypes.c_uint64 * (nbytes // 8 + 1))()
+        assert lib.w4a16_batch_plan(ctypes.cast(arr, vp), len(probs), T, ctypes.addressof(buf), nbytes) == OK
+        return buf
+
+    for T in (9, 12, 16):
+        need = 16 + sum(T * k * 2 + (T * 4 + 15) // 16 * 16 for _, k in shapes)
+        tb = table(T)
+        assert lib.w4a16_batch_workspace_bytes(ctypes.addressof(tb)) == need
+        run = lambda ws=A, n=need, t=ctypes.addressof(tb), d=A: lib.w4a16_matmul_batch_ws(t, d, ws, n, None)
+        assert run(ws=None) == WS and run(ws=A + 8) == WS and run(n=need - 1) == WS
+        assert run(t=None) == NULLP and run(d=None) == NULLP and run(d=A + 8) == ALIGN
+        assert run() in (UNSUP, HIP)                      # arguments fine: the device check is next
+    for T in (1, 4, 8):
+        assert lib.w4a16_batch_workspace_bytes(ctypes.addressof(table(T))) == 0
+    junk = (ctypes.c_uint64 * 16)()
+    assert lib.w4a16_batch_workspace_bytes(ctypes.addressof(junk)) == 0
+    assert lib.w4a16_batch_workspace_bytes(None) == 0

@@ -44,7 +44,7 @@ def check_outputs(probs, host_side, what):
 
 
 @pytest.mark.parametrize("tile", [None, "shared,1,4", "split,1,4", "split,4,2", "split,2,8", "shared,1,16", "run,2,8", "run,3,16"])
-@pytest.mark.parametrize("T", [1, 4, 8])
+@pytest.mark.parametrize("T", [1, 4, 8, 16])
 def test_batch_matches_oracle(w4, tile, T, monkeypatch):
     if tile is not None:
         monkeypatch.setenv("W4A16_BATCH_TILE", tile)
@@ -121,3 +121,54 @@ def test_batch_with_lm_head_argmax(w4, T, tiled):
     am_id.fill_(-7)
     b.run()
     assert np.array_equal(host(am_id), host(i1))
+
+
+@pytest.mark.parametrize("T", [9, 12, 16])
+def test_batch_workspace_staging_equals_workgroup_staging(w4, T):
+    """From T = 9 the grouped launch converts the activations once into its
+    workspace and the workgroups copy them straight into LDS.  Same products
+    and sums as the workgroups' own staging, so the outputs are equal bit for
+    bit; rows that need their own power of two (values scaled by 2^40 and
+    2^-40, a row far below the fixed window) included, in both layouts, with
+    a problem's argmax, and all against the oracle."""
+    say(f"workspace staging T={T}")
+    shapes = [(1000, 5120), (2000, 17408), (300, 1152), (17, 128)]
+    probs, host_side = [], []
+    for i, (N, K) in enumerate(shapes):
+        tid = 900 + 10 * T + i
+        p, s = synth.weight(tid, N, K)
+        xf = synth.bf16_to_f32(synth.activations(tid, T, K)).astype(np.float64)
+        xf[0] *= 2.0 ** 40
+        xf[T - 1] *= 2.0 ** -40
+        xf[T // 2, : K // 2] *= 2.0 ** -20
+        x = np.array([synth.bf16_from_double(v) for v in xf.ravel()], np.uint16).reshape(T, K)
+        y = torch.full((T, N), float("nan"), dtype=torch.float32, device="cuda")
+        pd, sd = dev(p), dev(s)
+        w = w4.repack_tiled(pd, sd) if i % 2 == 0 else pd
+        probs.append((w, None if i % 2 == 0 else sd, dev(x), y))
+        host_side.append((p, s, x))
+    n_h = 1000
+    am_id = torch.empty(T, dtype=torch.int32, device="cuda")
+    am_val = torch.empty(T, dtype=torch.float32, device="cuda")
+    ws = torch.empty(w4.workspace_bytes(n_h, T), dtype=torch.uint8, device="cuda")
+    probs[0] = probs[0] + (am_id, am_val, ws)
+    b = w4.Batch(probs, T)
+    assert b.workspace is not None
+    b.run(staged=True)
+    staged = [host(pr[3]).copy() for pr in probs] + [host(am_id).copy(), host(am_val).copy()]
+    for pr in probs:
+        pr[3].fill_(-1.0)
+    b.run(staged=False)
+    plain = [host(pr[3]).copy() for pr in probs] + [host(am_id).copy(), host(am_val).copy()]
+    for i, (a_, b_) in enumerate(zip(staged, plain)):
+        if i == 1:
+            # the down-sized problem is staged in K slices by its workgroups, each slice
+            # with its own power of two; the workspace takes one per row over all of K.
+            # Row T // 2 spans 2^20 across K, so its smallest values round differently.
+            keep = np.arange(T) != T // 2
+            a_, b_ = a_[keep], b_[keep]
+        assert np.array_equal(a_, b_, equal_nan=True), f"output {i} differs between the staging paths"
+    check_outputs([(None, None, None, pr[3]) for pr in probs], host_side, f"workspace staging T={T}")
+    for pr, out in zip(probs, plain):
+        pr[3].copy_(torch.from_numpy(out))
+    check_outputs([(None, None, None, pr[3]) for pr in probs], host_side, f"workgroup staging T={T}")

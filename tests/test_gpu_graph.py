@@ -54,6 +54,13 @@ def test_graph_replays_match_eager(w4):
     ba_ws = torch.empty(w4.workspace_bytes(40000, T), dtype=torch.uint8, device="cuda")
     yb1t = torch.empty_like(yb1)
     batch_am = w4.Batch([(tw1, None, x1, yb1t), (twh, None, xh, yba, ba_id, ba_val, ba_ws)], T)
+    T8 = 12  # T >= 9: a grouped launch that converts its activations into its workspace first
+    x8a = dev(synth.activations(6005, T8, 5120))
+    x8b = dev(synth.activations(6006, T8, 17408))
+    y8a = torch.empty((T8, 7168), dtype=torch.float32, device="cuda")
+    y8b = torch.empty((T8, 5120), dtype=torch.float32, device="cuda")
+    batch8 = w4.Batch([(tw1, None, x8a, y8a), (pd2, sd2, x8b, y8b)], T8)
+    assert batch8.workspace is not None
     state = {}
 
     def calls(stream):
@@ -62,11 +69,12 @@ def test_graph_replays_match_eager(w4):
         w4.matmul(pd2, sd2, x2, out=y2, stream=stream)
         batch.run(stream)
         batch_am.run(stream)
+        batch8.run(stream)
         _, am, av = w4.head_gather_tiled(twh, xh, row_ids=ids, scores=True, argmax=True, out=yh, workspace=ws,
                                          stream=stream)
         ti, tv = w4.topk(yh, 32, row_ids=ids, workspace=tws, stream=stream)
         acc, tok = w4.greedy_accept(am, draft, 1, T, stream=stream)
-        state["out"] = (am, av, ti, tv, acc, tok, yb1t, yba, ba_id, ba_val)
+        state["out"] = (am, av, ti, tv, acc, tok, yb1t, yba, ba_id, ba_val, y8a, y8b)
 
     def snapshot():
         torch.cuda.synchronize()

@@ -165,10 +165,12 @@ static_assert(sizeof(ArgmaxRecord) == 32 && sizeof(w4a16::GemvArgs) == 144, "bat
 constexpr int kWorkspaceMinT = 9;
 
 // Tile of grouped launches, from the MI355X sweeps.  All problems tiled:
-// at T <= 2 shared workgroups of one tile per wave; above, run workgroups of
-// four tiles per wave, eight waves at T <= 4 and sixteen above, a problem
-// whose activations do not fit running shared workgroups inside the same
-// kernel.
+// at T <= 2 shared workgroups of one tile per wave; above, run workgroups
+// of eight waves, four tiles per wave at T <= 4 and six at T <= 8 (two such
+// workgroups share a CU while all of K = 5120 fits in half its LDS; the
+// 27B-class body pass: +2.8% at T = 5, +0.8% at T = 8 against sixteen waves
+// of four), sixteen waves of four above T = 8, a problem whose activations
+// do not fit running shared workgroups inside the same kernel.
 // Otherwise (some row-major problem) at T <= 2 four waves of two 16-row
 // tiles, above that eight waves of four.  W4A16_BATCH_TILE =
 // "split|shared|run,rt,waves" overrides it (for measurement).
@@ -176,7 +178,7 @@ w4a16::Tile batch_tile(int T, bool all_tiled, int64_t kmax) {
   w4a16::Tile t;
   if (all_tiled)
     t = T <= 2 ? w4a16::Tile{w4a16::kShared, 1, w4a16::shared_waves(T, kmax)}
-               : w4a16::Tile{w4a16::kRun, 4, T <= 4 ? 8 : 16};
+               : w4a16::Tile{w4a16::kRun, T <= 4 ? 4 : T <= 8 ? 6 : 4, T <= 8 ? 8 : 16};
   else
     t = T <= 2 ? w4a16::Tile{w4a16::kShared, 2, 4} : w4a16::Tile{w4a16::kShared, 4, 8};
   w4a16::Tile o;

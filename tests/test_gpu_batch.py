@@ -43,7 +43,7 @@ def check_outputs(probs, host_side, what):
         assert_parity(host(y)[:, rows], y_ref, a_ref, f"{what} N={N} K={p.shape[1] * 2}")
 
 
-@pytest.mark.parametrize("tile", [None, "shared,1,4", "split,1,4", "split,4,2", "split,2,8", "shared,1,16", "run,2,8", "run,3,16"])
+@pytest.mark.parametrize("tile", [None, "shared,1,4", "split,1,4", "split,4,2", "split,2,8", "shared,1,16", "run,2,8", "run,6,8", "run,3,16"])
 @pytest.mark.parametrize("T", [1, 4, 8, 16])
 def test_batch_matches_oracle(w4, tile, T, monkeypatch):
     if tile is not None:
@@ -59,6 +59,19 @@ def test_batch_matches_oracle(w4, tile, T, monkeypatch):
     b.run()
     for f, (*_, y) in zip(first, probs):
         assert np.array_equal(f, host(y)), "second run differs"
+
+
+@pytest.mark.parametrize("T", [3, 5, 6, 7, 8])
+def test_batch_tiled_default_matches_oracle(w4, T, monkeypatch):
+    """The grouped launch's own tiling for tiled weights around the switch
+    between four and six tiles per wave (eight-wave run workgroups; the
+    17,408-column problem runs sliced shared workgroups in the same kernel)."""
+    monkeypatch.delenv("W4A16_BATCH_TILE", raising=False)
+    say(f"batch tiled default T={T}")
+    probs, host_side = build_case(T, 650 + T)
+    probs = [(w4.repack_tiled(pp, ss), None, xx, yy) for pp, ss, xx, yy in probs]
+    w4.Batch(probs, T).run()
+    check_outputs(probs, host_side, f"batch tiled T={T}")
 
 
 def test_batch_equals_single_launch_within_tolerance(w4):

@@ -34,8 +34,9 @@
  *     any status other than W4A16_OK and W4A16_ERR_HIP nothing was enqueued.
  *     W4A16_ERR_HIP means a HIP runtime call failed (the launch itself or a
  *     device query).
- *   - No allocation, no synchronisation, no printing, no state kept between
- *     calls.  Outputs must not alias inputs or each other.
+ *   - No allocation, no synchronisation, no printing, and no state kept
+ *     between calls apart from the process-wide variant selection
+ *     (w4a16_set_variant).  Outputs must not alias inputs or each other.
  *   - Thread-safe; calls on different streams may run concurrently.
  *   - Activations should be finite; a non-finite x gives non-finite outputs
  *     for the rows it reaches.

@@ -94,6 +94,18 @@ template <typename V>
 __device__ __forceinline__ void st_global(V* p, V v) {
   *(__attribute__((address_space(1))) V*)p = v;
 }
+// Output store of a kernel for TT activation rows.  Up to 4 rows the outputs
+// are written nontemporal, so that fewer dirty lines wait in L2 for the
+// write-back at the end of the launch (27B-class step at T = 4: +1.0%,
+// body pass at T = 1: +0.3%); from 8 rows on plain stores measured faster
+// (T = 8: 0.2%, T = 16: 1.4%).
+template <int TT>
+__device__ __forceinline__ void st_out(float* p, float v) {
+  if constexpr (TT <= 4)
+    __builtin_nontemporal_store(v, (__attribute__((address_space(1))) float*)p);
+  else
+    st_global(p, v);
+}
 // An argmax partial (value bits, id) as one 8-byte store.
 __device__ __forceinline__ void st_partial(int2* p, float v, int id) {
   st_global(reinterpret_cast<unsigned long long*>(p),
@@ -574,7 +586,7 @@ __global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       float v = bad ? __builtin_nanf("") : acc[t];
-      if (orow < a.n_out && a.y) st_global(a.y + (int64_t)t * a.n_out + orow, v);
+      if (orow < a.n_out && a.y) st_out<TT>(a.y + (int64_t)t * a.n_out + orow, v);
       fin[((r >> 4) * TT + t) * 16 + (r & 15)] = v;
     }
   }
@@ -833,7 +845,7 @@ __device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, u
     const int64_t orow = row0 + tl * 16 + r;
     if (orow < a.n_out) {
       if (weight_row(a, orow) < 0) v = __builtin_nanf("");
-      if (a.y) st_global(a.y + (int64_t)t * a.n_out + orow, v);
+      if (a.y) st_out<TT>(a.y + (int64_t)t * a.n_out + orow, v);
     }
     fin[o] = v;
   }
@@ -887,7 +899,7 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = kq * 4 + r;
-      if (t < TT && in_range && a.y) st_global(a.y + (int64_t)t * a.n_out + orow, bad ? __builtin_nanf("") : acc[tl][r]);
+      if (t < TT && in_range && a.y) st_out<TT>(a.y + (int64_t)t * a.n_out + orow, bad ? __builtin_nanf("") : acc[tl][r]);
     }
     if (a.partial) {
       // this lane's candidate for token rows t = 4*kq + r
@@ -1033,7 +1045,7 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
 #pragma unroll
       for (int i = 1; i < TT; ++i) e = (t == i) ? E[i] : e;
       const float val = ldexpf(accs[r], -e);
-      if (t < TT && in_range && a.y) st_global(a.y + (int64_t)t * a.n_out + orow, w_cur < 0 ? __builtin_nanf("") : val);
+      if (t < TT && in_range && a.y) st_out<TT>(a.y + (int64_t)t * a.n_out + orow, w_cur < 0 ? __builtin_nanf("") : val);
       if (a.partial && t < TT && w_cur >= 0 && !__builtin_isnan(val) && better(val, w_cur, bv[r], bi[r])) {
         bv[r] = val;
         bi[r] = w_cur;

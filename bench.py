@@ -317,6 +317,7 @@ def main():
         "single_launches": singles,
         "variants_dot_vs_matrix_core": variants,
         "read_ceiling": ceiling,
+        "device": device_info(torch),
         "roofline": {
             "kernel": "grouped launch of the step (64 x 4 projections + lm_head with argmax, tiled layout); "
                       "the launch time includes the argmax reduction launched after it",
@@ -332,6 +333,18 @@ def main():
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def device_info(torch):
+    """Name, architecture and size of the GPU the figures were measured on
+    (box-to-box spread of the same library is several percent)."""
+    p = torch.cuda.get_device_properties(0)
+    info = {"name": p.name, "arch": getattr(p, "gcnArchName", None), "compute_units": p.multi_processor_count,
+            "memory_GiB": round(p.total_memory / 2**30, 1)}
+    for attr in ("clock_rate", "memory_clock_rate", "L2_cache_size"):
+        if getattr(p, attr, None) is not None:
+            info[attr] = getattr(p, attr)
+    return info
 
 
 def time_rotating(torch, fns, stream, rounds=4):

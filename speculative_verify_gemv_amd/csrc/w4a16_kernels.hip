@@ -319,8 +319,8 @@ int shared_waves(int T, int64_t K) {
 
 // Default matrix-core tiling of a single launch (cus: compute units of the
 // device), from the MI355X sweeps.  Tiled weights of at least 4,096 tiles
-// (the vocabulary head) run workgroups of 16 waves x 4 tiles at every T
-// (with the argmax too); mid-size matrices shared workgroups of one tile
+// run workgroups of 16 waves x 4 tiles at every T (with the argmax too) when
+// that fills the CUs (the vocabulary head), else 8 waves x 2 tiles; mid-size matrices shared workgroups of one tile
 // per wave, four waves at small T and sixteen from T = 5 (tiled) or T = 8
 // (row-major), where one staging of the activations then serves 16 tiles
 // (gate_up at T = 8: 27 us against 34, at T = 16: 31 against 53).  Row-major weights: the full vocabulary head (15,520
@@ -334,7 +334,11 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
   const int64_t tiles = cdiv(a.n_out, 16);
   Tile t;
   if (tiles >= 4096 && a.tiled)
-    t = Tile{kRun, 4, 16};
+    // one round of 16-wave runs of 4 tiles when it fills nine tenths of the
+    // CUs (the vocabulary head: 243 workgroups); shorter matrices run 8-wave
+    // runs of 2 tiles, two workgroups per CU (65,536 x 5,120: 32 us against
+    // 73 us for the 64 workgroups of 4 x 16; 131,072 rows: 58 against 89)
+    t = cdiv(tiles, 64) * 10 >= 9LL * std::max(cus, 1) ? Tile{kRun, 4, 16} : Tile{kRun, 2, 8};
   else if (tiles >= 8192)
     t = Tile{kShared, 4, 8};
   else if (tiles >= 4096)

@@ -152,6 +152,31 @@ def test_lm_head_tiled_argmax_and_draft_head(w4, T):
         assert np.array_equal(amd, own_d)
 
 
+@pytest.mark.parametrize("T", [1, 5, 8])
+def test_tall_tiled_below_head_size(w4, T):
+    """A tall tiled matrix that one round of 16-wave runs would not fill
+    (70,001 rows: 4,376 tiles) runs the 8-wave runs of 2 tiles: every score
+    against the oracle, and its argmax, bit for bit against the host argmax
+    of the scores and against the oracle's unless a near-tie."""
+    N, K = 70001, 1024
+    p, s, pd, sd = weight_dev(4500, N, K)
+    tw = w4.repack_tiled(pd, sd)
+    x = synth.activations(4500 + T, T, K)
+    say(f"tall tiled {N}x{K} T={T}")
+    y, am, av = w4.head_gather_tiled(tw, dev(x), argmax=True)
+    y, am, av = host(y), host(am), host(av)
+    y_ref, a_ref = oracle.matmul(p, s, x)
+    assert_parity(y, y_ref, a_ref, f"tall tiled T={T}")
+    own, _, _ = oracle.argmax(y.astype(np.float64))
+    assert np.array_equal(am, own) and np.array_equal(av, y[np.arange(T), am])
+    ref_id, _, gap = oracle.argmax(y_ref)
+    for t in range(T):
+        if am[t] != ref_id[t]:
+            err = abs(y[t, am[t]] - y_ref[t, am[t]]) + abs(y[t, ref_id[t]] - y_ref[t, ref_id[t]])
+            assert gap[t] < err, f"t={t}: {am[t]} vs oracle {ref_id[t]}"
+    assert np.array_equal(host(w4.matmul_tiled(tw, dev(x))), y), "matmul and head scores differ"
+
+
 @pytest.mark.parametrize("T", [1, 4, 8])
 def test_batch_mixed_layouts(w4, T):
     shapes = [(1024, 1024), (300, 5120), (17, 1152), (4099, 1280), (2000, 17408)]

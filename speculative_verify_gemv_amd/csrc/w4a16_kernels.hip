@@ -318,33 +318,49 @@ int shared_waves(int T, int64_t K) {
 }
 
 // Default matrix-core tiling of a single launch (cus: compute units of the
-// device), from the MI355X sweeps.  Tiled weights of at least 4,096 tiles
-// run workgroups of 16 waves x 4 tiles at every T (with the argmax too) when
-// that fills the CUs (the vocabulary head), else 8 waves x 2 tiles; mid-size matrices shared workgroups of one tile
-// per wave, four waves at small T and sixteen from T = 5 (tiled) or T = 8
-// (row-major), where one staging of the activations then serves 16 tiles
-// (gate_up at T = 8: 27 us against 34, at T = 16: 31 against 53).  Row-major weights: the full vocabulary head (15,520
-// tiles) is fastest with eight waves of four tiles each.  Shorter matrices
-// split K over the waves of a workgroup so that they still put ~12 waves of
-// weight loads on every CU, up to 8 token rows; above that a wave's staged
-// slice would hold too few groups, and shared workgroups of four waves win.
-// W4A16_TILE="split|shared|run,rt,waves" overrides the choice (for
-// measurement).
+// device), from the MI355X sweeps over the workload shapes and a grid of
+// others (N 512 - 131,072, K 1,024 - 17,408, T 1 - 8).  Tiled weights of at
+// least 4,096 tiles run workgroups of 16 waves x 4 tiles when one round of
+// them fills the CUs (the vocabulary head), else 8 waves x 2 tiles, and
+// where the staging is dear one round of 16-wave runs of as many tiles per
+// wave as that takes (while it keeps three quarters of the CUs busy);
+// row-major ones shared workgroups of 8 waves x 4 (>= 8,192 tiles) or x 2.
+// Mid-size matrices (1,024 - 4,095 tiles) run shared workgroups of one tile
+// per wave: 4 waves, or where the staging is dear (see below) one round of
+// 4, 8 or 16 waves.  Shorter matrices split K over the waves of a workgroup
+// so that they still put ~12 waves of weight loads on every CU, up to 8
+// token rows; above that a wave's staged slice would hold too few groups,
+// and shared workgroups of four waves win.  W4A16_TILE =
+// "split|shared|run,rt,waves" overrides the choice (for measurement).
 Plan plan_mfma(GemvArgs& a, int T, int cus) {
   const int64_t tiles = cdiv(a.n_out, 16);
   Tile t;
-  if (tiles >= 4096 && a.tiled)
-    // one round of 16-wave runs of 4 tiles when it fills nine tenths of the
-    // CUs (the vocabulary head: 243 workgroups); shorter matrices run 8-wave
-    // runs of 2 tiles, two workgroups per CU (65,536 x 5,120: 32 us against
-    // 73 us for the 64 workgroups of 4 x 16; 131,072 rows: 58 against 89)
-    t = cdiv(tiles, 64) * 10 >= 9LL * std::max(cus, 1) ? Tile{kRun, 4, 16} : Tile{kRun, 2, 8};
-  else if (tiles >= 8192)
+  const int64_t ncu = std::max(cus, 1);
+  // Where the staging is dear (tiled from T = 5, row-major from T = 8, and
+  // wherever T rows of K do not fit half a CU's LDS, so that smaller
+  // workgroups would stage in slices), one round of workgroups, one per CU,
+  // each staging the activations once for as many tiles as the CU's share:
+  // the fewest waves (4, 8, 16) whose workgroups fit one round, then runs of
+  // several tiles per wave.  (Mid-size shapes at T = 8: 16,384 x 5,120
+  // tiled 16.7 us against 24.7 for 16-wave workgroups, row-major 21 against
+  // 37; at T = 4, 32,768 x 17,408 tiled 54 against 65.)
+  const bool dear = (a.tiled ? T > 4 : T >= 8) || (int64_t)T * ring_groups(a.G) * kGroup * 2 > shared_cap(8);
+  if (tiles >= 4096 && a.tiled) {
+    if (dear) {  // 6,250 tiles: 2 per wave; the vocabulary head: 4
+      const int rt = (int)std::min<int64_t>(16, cdiv(tiles, 16 * ncu));
+      // a round that would leave a quarter of the CUs idle: 8-wave runs of 2
+      t = cdiv(tiles, 16LL * rt) * 4 >= 3 * ncu ? Tile{kRun, rt, 16} : Tile{kRun, 2, 8};
+    } else  // one round of 16-wave runs of 4 tiles when it fills nine tenths of
+          // the CUs (the vocabulary head: 243 workgroups), else 8-wave runs
+          // of 2 tiles, two workgroups per CU (65,536 x 5,120: 32 us against
+          // 73 us for the 64 workgroups of 4 x 16; 131,072 rows: 58 vs 89)
+      t = cdiv(tiles, 64) * 10 >= 9 * ncu ? Tile{kRun, 4, 16} : Tile{kRun, 2, 8};
+  } else if (tiles >= 8192)
     t = Tile{kShared, 4, 8};
   else if (tiles >= 4096)
     t = Tile{kShared, 2, 8};
-  else if (tiles >= 1024 && (a.tiled ? T > 4 : T >= 8))  // 16 waves share one staging of the activations
-    t = Tile{kShared, 1, 16};
+  else if (tiles >= 1024 && dear)
+    t = Tile{kShared, 1, cdiv(tiles, 4) <= ncu ? 4 : cdiv(tiles, 8) <= ncu ? 8 : 16};
   else if (tiles >= 1024 || T > 8)  // above 8 rows a split wave stages too little K per slice
     t = Tile{kShared, 1, 4};
   else

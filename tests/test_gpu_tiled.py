@@ -177,6 +177,22 @@ def test_tall_tiled_below_head_size(w4, T):
     assert np.array_equal(host(w4.matmul_tiled(tw, dev(x))), y), "matmul and head scores differ"
 
 
+@pytest.mark.parametrize("N,K,T", [(16384, 5120, 8), (16400, 1024, 5), (32768, 2048, 6), (33000, 1024, 8),
+                                   (100000, 1024, 7)])
+def test_mid_size_one_round_tilings(w4, N, K, T):
+    """Mid-size and tall tiled matrices at T >= 5 take the one-round tilings
+    (4, 8 or 16 waves of one tile; runs of 2 tiles per wave for 6,250 tiles):
+    sampled rows against the oracle, including the tile edges."""
+    p, s, pd, sd = weight_dev(4600 + T, N, K)
+    tw = w4.repack_tiled(pd, sd)
+    x = synth.activations(4600 + T, T, K)
+    say(f"one-round tiling {N}x{K} T={T}")
+    y = host(w4.matmul_tiled(tw, dev(x)))
+    rows = sample_rows(N, 512, seed=N + T)
+    y_ref, a_ref = oracle.gather(rows, p, s, x)
+    assert_parity(y[:, rows], y_ref, a_ref, f"tiled {N}x{K} T={T}")
+
+
 @pytest.mark.parametrize("T", [1, 4, 8])
 def test_batch_mixed_layouts(w4, T):
     shapes = [(1024, 1024), (300, 5120), (17, 1152), (4099, 1280), (2000, 17408)]

@@ -71,9 +71,9 @@ typedef enum {
 } w4a16_status;
 
 /* Kernel variants.  Both compute the same values within the tolerance above.
- * AUTO runs the matrix-core kernels: on MI355X they are faster at every T
- * except on short matrices at T = 1 (where the dot variant is a few percent
- * faster), and 1.7-11x faster from T = 4.  The dot variant covers T <= 8;
+ * AUTO runs the matrix-core kernels: on MI355X they are faster on every
+ * workload shape at every T (1-3% on the short projections at T = 1, 2.4-11x
+ * from T = 4).  The dot variant covers T <= 8;
  * calls with more activation rows run the matrix-core kernels whatever the
  * selection. */
 typedef enum {

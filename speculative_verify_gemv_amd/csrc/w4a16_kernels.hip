@@ -327,10 +327,12 @@ int shared_waves(int T, int64_t K) {
 // row-major ones shared workgroups of 8 waves x 4 (>= 8,192 tiles) or x 2.
 // Mid-size matrices (1,024 - 4,095 tiles) run shared workgroups of one tile
 // per wave: 4 waves, or where the staging is dear (see below) one round of
-// 4, 8 or 16 waves.  Shorter matrices split K over the waves of a workgroup
-// so that they still put ~12 waves of weight loads on every CU, up to 8
-// token rows; above that a wave's staged slice would hold too few groups,
-// and shared workgroups of four waves win.  W4A16_TILE =
+// 4, 8 or 16 waves.  Shorter matrices, up to 8 token rows: from T = 2 and
+// three quarters of a round of them, 4-wave shared workgroups too; else
+// split workgroups that cut K over their waves so as to put ~12 waves of
+// weight loads on every CU (row-major weights from 1.25 tiles per CU: two
+// tiles per workgroup, 8 waves).  Above 8 token rows a split wave's staged
+// slice would hold too few groups, and shared workgroups of four waves win.  W4A16_TILE =
 // "split|shared|run,rt,waves" overrides the choice (for measurement).
 Plan plan_mfma(GemvArgs& a, int T, int cus) {
   const int64_t tiles = cdiv(a.n_out, 16);
@@ -363,6 +365,10 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
     t = Tile{kShared, 1, cdiv(tiles, 4) <= ncu ? 4 : cdiv(tiles, 8) <= ncu ? 8 : 16};
   else if (tiles >= 1024 || T > 8)  // above 8 rows a split wave stages too little K per slice
     t = Tile{kShared, 1, 4};
+  else if (T >= 2 && tiles >= 3 * ncu)  // still three quarters of a round of 4-wave workgroups,
+    t = Tile{kShared, 1, 4};             // each staging once for 4 tiles (12,288 x 5,120 at T = 8: 16 us vs 23)
+  else if (!a.tiled && 4 * tiles >= 5 * ncu)  // row-major: split workgroups of 2 tiles (5,120 x 17,408:
+    t = Tile{kSplit, 2, 8};                   // 44 us vs 65 at T = 8, 19 vs 21 at T = 1; the tiled kernels take one tile)
   else
     t = Tile{kSplit, 1, (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(12LL * std::max(cus, 1), tiles)))};
   Tile o;

@@ -52,7 +52,10 @@ RAGGED = [(1, 128, 1), (17, 384, 3), (33, 1152, 8), (100, 256, 5), (1003, 640, 2
           (257, 5120, 7), (31, 17408, 8), (2049, 128, 6),
           # tall enough for the streaming kernel: 8-group scale loads, and the
           # one-scale-per-load path (G = 9 groups, not a multiple of 8)
-          (16400, 1024, 1), (17003, 1152, 3), (16413, 2304, 8)]
+          (16400, 1024, 1), (17003, 1152, 3), (16413, 2304, 8),
+          # short matrices near a round of 4-wave workgroups, and of 2-tile
+          # split workgroups (row-major)
+          (12301, 1152, 3), (5121, 2048, 1), (8191, 1280, 6)]
 
 
 @pytest.mark.parametrize("variant", VARIANTS)

@@ -1219,9 +1219,11 @@ hipError_t launch_tiles(const GemvArgs& a, const GemvArgs* table, int count, con
 
 template <int TT, bool SHARED>
 hipError_t launch_rt(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
-  if (p.tiled) {  // tiled-only kernels are built with one tile per wave
-    if (p.rt != 1) return hipErrorInvalidValue;
-    return launch_tiles<TT, 1, SHARED, kLayTiled>(a, table, count, p, s);
+  if (p.tiled) {  // tiled-only kernels: one tile per wave, or two in split workgroups
+    if (p.rt == 1) return launch_tiles<TT, 1, SHARED, kLayTiled>(a, table, count, p, s);
+    if constexpr (!SHARED)
+      if (p.rt == 2) return launch_tiles<TT, 2, false, kLayTiled>(a, table, count, p, s);
+    return hipErrorInvalidValue;
   }
   switch (p.rt) {
     case 1: return launch_tiles<TT, 1, SHARED, kLayAny>(a, table, count, p, s);

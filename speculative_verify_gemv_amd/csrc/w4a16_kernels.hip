@@ -291,7 +291,8 @@ static bool plan_run(GemvArgs& a, int T, int nt, int nwv, Plan* p) {
 Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel, bool batch) {
   Plan p{};
   p.variant = t.shape;
-  p.rt = tiled_kernel ? 1 : t.rt;  // the tiled-layout kernels stream one tile per wave
+  // the tiled-layout kernels stream one tile per wave (two in split workgroups)
+  p.rt = tiled_kernel && !(t.shape == kSplit && t.rt == 2) ? 1 : t.rt;
   p.tiled = tiled_kernel;
   a.vec_scales = (a.tiled || (a.G % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15) == 0)) ? 1 : 0;
   if (t.shape == kRun) {
@@ -330,8 +331,8 @@ int shared_waves(int T, int64_t K) {
 // 4, 8 or 16 waves.  Shorter matrices, up to 8 token rows: from T = 2 and
 // three quarters of a round of them, 4-wave shared workgroups too; else
 // split workgroups that cut K over their waves so as to put ~12 waves of
-// weight loads on every CU (row-major weights from 1.25 tiles per CU: two
-// tiles per workgroup, 8 waves).  Above 8 token rows a split wave's staged
+// weight loads on every CU (from 1.25 tiles per CU: two tiles per
+// workgroup, 8 waves).  Above 8 token rows a split wave's staged
 // slice would hold too few groups, and shared workgroups of four waves win.  W4A16_TILE =
 // "split|shared|run,rt,waves" overrides the choice (for measurement).
 Plan plan_mfma(GemvArgs& a, int T, int cus) {
@@ -367,8 +368,8 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
     t = Tile{kShared, 1, 4};
   else if (T >= 2 && tiles >= 3 * ncu)  // still three quarters of a round of 4-wave workgroups,
     t = Tile{kShared, 1, 4};             // each staging once for 4 tiles (12,288 x 5,120 at T = 8: 16 us vs 23)
-  else if (!a.tiled && 4 * tiles >= 5 * ncu)  // row-major: split workgroups of 2 tiles (5,120 x 17,408:
-    t = Tile{kSplit, 2, 8};                   // 44 us vs 65 at T = 8, 19 vs 21 at T = 1; the tiled kernels take one tile)
+  else if (4 * tiles >= 5 * ncu)  // split workgroups of 2 tiles: 5,120 x 17,408 row-major 44 us vs 65 at
+    t = Tile{kSplit, 2, 8};       // T = 8, 19 vs 21 at T = 1; tiled 34 vs 40 at T = 8, 16.0 vs 16.8 at T = 1
   else
     t = Tile{kSplit, 1, (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(12LL * std::max(cus, 1), tiles)))};
   Tile o;

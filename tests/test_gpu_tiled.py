@@ -77,7 +77,7 @@ def test_matmul_tiled_matches_oracle(w4, N, K, T):
     assert_parity(host(w4.matmul_tiled(tw, dev(x))), y_ref, a_ref, f"tiled N={N} K={K} T={T}")
 
 
-@pytest.mark.parametrize("tile", ["split,1,8", "split,2,3", "shared,1,1", "shared,4,8", "shared,2,4", "shared,1,16", "shared,1,12", "run,4,8", "run,2,16"])
+@pytest.mark.parametrize("tile", ["split,1,8", "split,2,3", "split,2,8", "shared,1,1", "shared,4,8", "shared,2,4", "shared,1,16", "shared,1,12", "run,4,8", "run,2,16"])
 def test_matmul_tiled_every_tile_shape(w4, tile, monkeypatch):
     monkeypatch.setenv("W4A16_TILE", tile)
     for N, K, T in [(37, 1152, 3), (300, 17408, 8), (2000, 2304, 8), (4099, 5120, 4)]:

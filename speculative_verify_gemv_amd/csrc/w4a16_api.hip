@@ -171,8 +171,9 @@ constexpr int kWorkspaceMinT = 9;
 // 27B-class body pass: +2.8% at T = 5, +0.8% at T = 8 against sixteen waves
 // of four), sixteen waves of four above T = 8, a problem whose activations
 // do not fit running shared workgroups inside the same kernel.
-// Otherwise (some row-major problem) at T <= 2 four waves of two 16-row
-// tiles, above that eight waves of four.  W4A16_BATCH_TILE =
+// Otherwise (some row-major problem) four waves of two 16-row tiles at
+// T = 1, of four from T = 2 (27B-class body pass, row-major: +5.6% at
+// T = 8, +8.3% at T = 4 against eight waves of four).  W4A16_BATCH_TILE =
 // "split|shared|run,rt,waves" overrides it (for measurement).
 w4a16::Tile batch_tile(int T, bool all_tiled, int64_t kmax) {
   w4a16::Tile t;
@@ -180,7 +181,7 @@ w4a16::Tile batch_tile(int T, bool all_tiled, int64_t kmax) {
     t = T <= 2 ? w4a16::Tile{w4a16::kShared, 1, w4a16::shared_waves(T, kmax)}
                : w4a16::Tile{w4a16::kRun, T <= 4 ? 4 : T <= 8 ? 6 : 4, T <= 8 ? 8 : 16};
   else
-    t = T <= 2 ? w4a16::Tile{w4a16::kShared, 2, 4} : w4a16::Tile{w4a16::kShared, 4, 8};
+    t = T == 1 ? w4a16::Tile{w4a16::kShared, 2, 4} : w4a16::Tile{w4a16::kShared, 4, 4};
   w4a16::Tile o;
   if (w4a16::parse_tile(std::getenv("W4A16_BATCH_TILE"), &o)) t = o;
   return t;

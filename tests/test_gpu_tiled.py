@@ -178,13 +178,17 @@ def test_tall_tiled_below_head_size(w4, T):
 
 
 @pytest.mark.parametrize("N,K,T", [(16384, 5120, 8), (16400, 1024, 5), (32768, 2048, 6), (33000, 1024, 8),
-                                   (100000, 1024, 7), (12301, 1152, 3), (14000, 17408, 2)])
+                                   (100000, 1024, 7), (12301, 1152, 3), (14000, 17408, 2),
+                                   # odd tile counts in 2-tile split workgroups
+                                   (5121, 17408, 8), (7183, 5120, 1), (6001, 2304, 4)])
 def test_mid_size_one_round_tilings(w4, N, K, T):
     """Mid-size and tall tiled matrices where the staging is dear take the
     one-round tilings (4, 8 or 16 waves of one tile; runs of 2 tiles per
-    wave for 6,250 tiles), and short ones from three quarters of a round at
-    T >= 2 shared workgroups of 4 waves: sampled rows against the oracle,
-    including the tile edges."""
+    wave for 6,250 tiles), short ones from three quarters of a round at
+    T >= 2 shared workgroups of 4 waves, and shorter ones from 1.25 tiles
+    per CU split workgroups of 2 tiles (odd tile counts leave the last
+    workgroup half empty): sampled rows against the oracle, including the
+    tile edges."""
     p, s, pd, sd = weight_dev(4600 + T, N, K)
     tw = w4.repack_tiled(pd, sd)
     x = synth.activations(4600 + T, T, K)

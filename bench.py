@@ -371,7 +371,8 @@ def single_launches(torch, w4a16, weights, head_p, head_s, head_tw, stream):
     workload: the 1024 x 1024 matrix (T = 1), each 27B-class projection at
     T = 1, 4, 8 (tiled, copies from all 64 layers rotated), the lm_head at
     T = 1 and 4 with argmax, and the 32,768-row draft head at T = 1, gathered
-    from the head and repacked once as its own matrix."""
+    from the row-major head (and, for comparison, from the tiled one) and
+    repacked once as its own matrix."""
     out = {}
     # small matrix: too small for any cache effect to matter; its figure is latency
     p, s = synth.weight(synth.TID_SMALL, *synth.SMALL)
@@ -402,15 +403,22 @@ def single_launches(torch, w4a16, weights, head_p, head_s, head_tw, stream):
         us = time_rotating(torch, fns, stream)
         out[f"lm_head_argmax_T{T}"] = {"us": round(us, 2),
                                        "weight_GBps": round(metrics.gbps(metrics.weight_bytes(hn, hk), us / 1000), 1)}
-    ids = [to_dev(synth.distinct_ids(synth.RID_DRAFT + i, synth.DRAFT_IDS, hn), torch) for i in range(4)]
+    ids = [to_dev(synth.distinct_ids(synth.RID_DRAFT + i, synth.DRAFT_IDS, hn), torch) for i in range(8)]
     x = to_dev(synth.activations(synth.TID_LM_HEAD + 2, 1, hk), torch)
     y = torch.empty((1, synth.DRAFT_IDS), dtype=torch.float32, device="cuda")
     ws = torch.empty(w4a16.workspace_bytes(synth.DRAFT_IDS, 1), dtype=torch.uint8, device="cuda")
-    fns = [lambda t=t, r=r: w4a16.head_gather_tiled(t, x, row_ids=r, scores=True, argmax=True, out=y, workspace=ws,
-                                                    stream=stream) for t in (head_tw, head_tw2) for r in ids]
+    # gathered from the row-major head (a row's consecutive groups share
+    # 128-byte lines), eight id sets rotated; and from the tiled head
+    fns = [lambda r=r: w4a16.head_gather(head_p, head_s, x, row_ids=r, scores=True, argmax=True, out=y, workspace=ws,
+                                         stream=stream) for r in ids]
     us = time_rotating(torch, fns, stream)
     out["draft_head_32768_argmax_T1"] = {"us": round(us, 2), "weight_GBps": round(
-        metrics.gbps(metrics.weight_bytes(synth.DRAFT_IDS, hk), us / 1000), 1)}
+        metrics.gbps(metrics.weight_bytes(synth.DRAFT_IDS, hk), us / 1000), 1), "layout": "row-major head"}
+    fns = [lambda t=t, r=r: w4a16.head_gather_tiled(t, x, row_ids=r, scores=True, argmax=True, out=y, workspace=ws,
+                                                    stream=stream) for t in (head_tw, head_tw2) for r in ids[:4]]
+    us = time_rotating(torch, fns, stream)
+    out["draft_head_32768_argmax_T1_tiled_head"] = {"us": round(us, 2), "weight_GBps": round(
+        metrics.gbps(metrics.weight_bytes(synth.DRAFT_IDS, hk), us / 1000), 1), "layout": "tiled head"}
     # the same draft head repacked once into its own tiled matrix (ascending
     # ids, so the argmax position indexes them); 12 copies rotated (1 GB)
     sid = [torch.sort(r)[0] for r in ids[:1]]

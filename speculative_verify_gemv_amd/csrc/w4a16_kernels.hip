@@ -327,8 +327,8 @@ int shared_waves(int T, int64_t K) {
 // wave as that takes (while it keeps three quarters of the CUs busy);
 // row-major ones shared workgroups of 8 waves x 4 (>= 8,192 tiles) or x 2.
 // Mid-size matrices (1,024 - 4,095 tiles) run shared workgroups of one tile
-// per wave: 4 waves, or where the staging is dear (see below) one round of
-// 4, 8 or 16 waves.  Shorter matrices, up to 8 token rows: from T = 2 and
+// per wave: 4 waves (8 where that makes one full round), or where the
+// staging is dear (see below) one round of 4, 8 or 16 waves.  Shorter matrices, up to 8 token rows: from T = 2 and
 // three quarters of a round of them, 4-wave shared workgroups too; else
 // split workgroups that cut K over their waves so as to put ~12 waves of
 // weight loads on every CU (from 1.25 tiles per CU: two tiles per
@@ -364,6 +364,8 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
     t = Tile{kShared, 2, 8};
   else if (tiles >= 1024 && dear)
     t = Tile{kShared, 1, cdiv(tiles, 4) <= ncu ? 4 : cdiv(tiles, 8) <= ncu ? 8 : 16};
+  else if (tiles >= 1024 && T <= 8 && cdiv(tiles, 8) <= ncu && cdiv(tiles, 8) * 10 >= 9 * ncu)
+    t = Tile{kShared, 1, 8};  // one full round of 8-wave workgroups (the 32,768-row draft head: 256)
   else if (tiles >= 1024 || T > 8)  // above 8 rows a split wave stages too little K per slice
     t = Tile{kShared, 1, 4};
   else if (T >= 2 && tiles >= 3 * ncu)  // still three quarters of a round of 4-wave workgroups,

@@ -602,8 +602,19 @@ def cpu_baseline(T, target_s):
             break
     g = done_bytes / spent / 1e9
     log(f"CPU oracle: {layers} layers at T={T} in {spent:.1f} s on {threads} threads: {g:.3f} GB/s")
+    # the same oracle on one thread, on the qkv projection of layer 0
+    N, K = synth.PROJECTIONS["qkv"]
+    p, s = synth.weight(synth.tid_layer(0, "qkv"), N, K)
+    x = synth.activations(synth.tid_layer(0, "qkv"), T, K)
+    t = time.time()
+    oracle.matmul(p, s, x, nthreads=1, want_abs=False)
+    t1 = time.time() - t
+    g1 = metrics.weight_bytes(N, K) / t1 / 1e9
+    log(f"CPU oracle, one thread: layer 0 qkv at T={T} in {t1:.1f} s: {g1:.4f} GB/s")
     return {"value": round(g, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{layers} of 64 layers (qkv, o, gate_up, down) at T={T}, fp64 oracle, {spent:.1f} s"}
+            "sample": f"{layers} of 64 layers (qkv, o, gate_up, down) at T={T}, fp64 oracle, {spent:.1f} s",
+            "single_thread": {"value": round(g1, 4), "unit": "GB/s", "cores": 1,
+                              "sample": f"layer 0 qkv at T={T}, {t1:.1f} s"}}
 
 
 if __name__ == "__main__":

@@ -337,21 +337,24 @@ int shared_waves(int T, int64_t K) {
 
 // Default matrix-core tiling of a single launch (cus: compute units of the
 // device), from the MI355X sweeps over the workload shapes and a grid of
-// others (N 512 - 131,072, K 1,024 - 17,408, T 1 - 8).  Tiled weights of at
-// least 4,096 tiles run workgroups of 16 waves x 4 tiles when one round of
-// them fills the CUs (the vocabulary head), else 8 waves x 2 tiles, and
-// where the staging is dear one round of 16-wave runs of as many tiles per
-// wave as that takes (while it keeps three quarters of the CUs busy);
-// row-major ones shared workgroups of 8 waves x 4 (>= 8,192 tiles) or x 2.
-// Mid-size matrices (1,024 - 4,095 tiles) run shared workgroups of one tile
-// per wave: 4 waves (8 where that makes one full round), or where the
-// staging is dear (see below) one round of 4, 8 or 16 waves.  Shorter matrices, up to 8 token rows: from T = 2 and
-// three quarters of a round of them, 4-wave shared workgroups too; else
-// split workgroups that cut K over their waves so as to put ~12 waves of
-// weight loads on every CU (from 1.25 tiles per CU: two tiles per
-// workgroup, 8 waves).  Above 8 token rows a split wave's staged
-// slice would hold too few groups, and shared workgroups of four waves win.  W4A16_TILE =
-// "split|shared|run,rt,waves" overrides the choice (for measurement).
+// others (N 512 - 131,072, K 1,024 - 17,408, T 1 - 16, both layouts):
+//   - tiled, >= 4,096 tiles: runs of 4 tiles x 16 waves when one round of
+//     them fills the CUs (the vocabulary head), else 2 tiles x 8 waves; where
+//     the staging is dear (below), one round of 16-wave runs of as many tiles
+//     per wave as that takes, while it keeps three quarters of the CUs busy;
+//   - row-major, >= 4,096 tiles: shared workgroups of 8 waves x 4 tiles
+//     (>= 8,192 tiles) or x 2;
+//   - 1,024 - 4,095 tiles: shared workgroups of one tile per wave, 4 waves
+//     (8 where that makes one full round); where the staging is dear, one
+//     round of 4, 8 or 16 waves;
+//   - shorter matrices, T <= 8: from T = 2 and three quarters of a round,
+//     4-wave shared workgroups too; else split workgroups that cut K over
+//     their waves to put ~12 waves of weight loads on every CU, two tiles
+//     per workgroup from 1.25 tiles per CU;
+//   - shorter matrices, T > 8: shared workgroups of 4 waves (a split wave's
+//     staged slice would hold too few groups).
+// W4A16_TILE = "split|shared|run,rt,waves" overrides the choice (for
+// measurement).
 Plan plan_mfma(GemvArgs& a, int T, int cus) {
   const int64_t tiles = cdiv(a.n_out, 16);
   Tile t;
@@ -370,11 +373,13 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
       const int rt = (int)std::min<int64_t>(16, cdiv(tiles, 16 * ncu));
       // a round that would leave a quarter of the CUs idle: 8-wave runs of 2
       t = cdiv(tiles, 16LL * rt) * 4 >= 3 * ncu ? Tile{kRun, rt, 16} : Tile{kRun, 2, 8};
-    } else  // one round of 16-wave runs of 4 tiles when it fills nine tenths of
-          // the CUs (the vocabulary head: 243 workgroups), else 8-wave runs
-          // of 2 tiles, two workgroups per CU (65,536 x 5,120: 32 us against
-          // 73 us for the 64 workgroups of 4 x 16; 131,072 rows: 58 vs 89)
+    } else {
+      // one round of 16-wave runs of 4 tiles when it fills nine tenths of the
+      // CUs (the vocabulary head: 243 workgroups), else 8-wave runs of 2
+      // tiles, two workgroups per CU (65,536 x 5,120: 32 us against 73 us for
+      // the 64 workgroups of 4 x 16; 131,072 rows: 58 against 89)
       t = cdiv(tiles, 64) * 10 >= 9 * ncu ? Tile{kRun, 4, 16} : Tile{kRun, 2, 8};
+    }
   } else if (tiles >= 8192)
     t = Tile{kShared, 4, 8};
   else if (tiles >= 4096)

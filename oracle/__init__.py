@@ -94,8 +94,11 @@ def matmul_dequant_first(packed, scales, x):
     return y
 
 
-def argmax(y, ids=None):
-    """Per row t of y[T][n]: (id, value, gap to the best other id)."""
+def argmax(y, ids=None, lib=None):
+    """Per row t of y[T][n]: (id, value, gap to the best other id).
+
+    lib: a ctypes handle of another build of oracle.c exporting the same
+    oracle_argmax (the mutation pins load deliberately broken copies)."""
     y, yp = _c(y, np.float64)
     T, n = y.shape
     if ids is not None:
@@ -106,7 +109,12 @@ def argmax(y, ids=None):
     out_id = np.empty(T, np.int32)
     out_val = np.empty(T, np.float64)
     gap = np.empty(T, np.float64)
-    _load().oracle_argmax(yp, ip, n, T, out_id.ctypes.data, out_val.ctypes.data, gap.ctypes.data)
+    if lib is None:
+        lib = _load()
+    else:
+        lib.oracle_argmax.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int,
+                                      ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.oracle_argmax(yp, ip, n, T, out_id.ctypes.data, out_val.ctypes.data, gap.ctypes.data)
     return out_id, out_val, gap
 
 

@@ -76,7 +76,7 @@ def body_problems(w4, weights, T):
 
 def test_step_at_t4_with_lm_head_argmax(w4, resident):
     """The bench step: body + lm_head with argmax in one grouped launch."""
-    from test_gpu_parity import check_argmax
+    from gpu_util import check_argmax
 
     weights, head, (hp, hs) = resident
     T = 4

@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import assert_parity, dev, host, say, sample_rows, weight_dev
+from gpu_util import assert_parity, check_argmax, dev, host, say, sample_rows, weight_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -186,24 +186,6 @@ def test_extreme_activation_ranges(w4, variant):
 
 
 # ------------------------------------------------------------ heads + argmax ----
-
-def check_argmax(ids_gpu, y_gpu_full, y_ref, ids_map, what):
-    """GPU argmax vs (a) the host argmax over the GPU's own scores, bit-exact, and
-    (b) the oracle's argmax, exact unless the oracle's top-2 gap is below the
-    GPU's measured error on those two rows."""
-    T = y_ref.shape[0]
-    own_id, _, _ = oracle.argmax(y_gpu_full.astype(np.float64), ids_map)
-    assert np.array_equal(ids_gpu, own_id), f"{what}: GPU argmax != host argmax of GPU scores"
-    ref_id, _, gap = oracle.argmax(y_ref, ids_map)
-    for t in range(T):
-        if ids_gpu[t] == ref_id[t]:
-            continue
-        pos = {int(v): i for i, v in enumerate(ids_map if ids_map is not None else range(y_ref.shape[1]))}
-        i_g, i_r = pos[int(ids_gpu[t])], pos[int(ref_id[t])]
-        err = abs(y_gpu_full[t, i_g] - y_ref[t, i_g]) + abs(y_gpu_full[t, i_r] - y_ref[t, i_r])
-        assert gap[t] < err, f"{what}: argmax {ids_gpu[t]} != oracle {ref_id[t]} (gap {gap[t]}, err {err})"
-        say(f"  near-tie accepted at t={t}: gap {gap[t]:.3g} < err {err:.3g}")
-
 
 _LM = {}
 

@@ -180,7 +180,8 @@ def test_lm_head_argmax_t16(w4):
     """Full 248,320 x 5,120 head at T = 16 (tiled): every score vs the oracle,
     argmax equal to the host argmax of the GPU scores and to the oracle's
     (up to a near-tie narrower than the measured error)."""
-    from test_gpu_parity import check_argmax, lm_head
+    from gpu_util import check_argmax
+    from test_gpu_parity import lm_head
 
     T = 16
     p, s, pd, sd = lm_head()
@@ -199,7 +200,8 @@ def test_lm_head_argmax_t16(w4):
 
 
 def test_draft_head_t16(w4):
-    from test_gpu_parity import check_argmax, lm_head
+    from gpu_util import check_argmax
+    from test_gpu_parity import lm_head
 
     T = 16
     p, s, pd, sd = lm_head()

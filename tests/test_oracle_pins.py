@@ -278,6 +278,87 @@ def test_argmax_planted_maximum():
     assert got[0] == r_star and gap[0] == 0.0 and val[0] > others.max()
 
 
+def _gap_case(c):
+    y = np.array([[float(v) for v in c["y"]]], np.float64)
+    ids = None if c["ids"] is None else np.array(c["ids"], np.int32)
+    return y, ids, float(c["gap"])
+
+
+def test_argmax_gap_hand_examples():
+    """Non-zero gaps, a best id held at two positions, one id everywhere (+inf),
+    NaN and negative scores: the gap is exact, with the right sign, against
+    the second id rather than the second position."""
+    for c in load("argmax_gap.json")["cases"]:
+        y, ids, gap_ref = _gap_case(c)
+        got, val, gap = oracle.argmax(y, ids)
+        assert got[0] == c["id"] and val[0] == c["val"], c["name"]
+        assert gap[0] == gap_ref, (c["name"], gap[0], gap_ref)
+
+
+def test_argmax_gap_brute_force_tiny():
+    """The gap against a brute force over the distinct ids of random rows with
+    repeated ids, ties and NaNs."""
+    rng = np.random.default_rng(16)
+    for _ in range(300):
+        n = int(rng.integers(1, 10))
+        y = rng.integers(-4, 5, size=(2, n)).astype(np.float64) / 2
+        y[rng.random((2, n)) < 0.2] = np.nan
+        ids = rng.integers(0, 5, size=n).astype(np.int32)
+        got, val, gap = oracle.argmax(y, ids)
+        for t in range(2):
+            per_id = {}
+            for v, i in zip(y[t], ids):
+                if not np.isnan(v):
+                    per_id[int(i)] = max(per_id.get(int(i), -np.inf), v)
+            if not per_id:
+                assert got[t] == -1 and np.isnan(gap[t])
+                continue
+            best = max(per_id.values())
+            best_id = min(i for i, v in per_id.items() if v == best)
+            others = [v for i, v in per_id.items() if i != best_id]
+            assert got[t] == best_id and val[t] == best
+            assert gap[t] == (best - max(others) if others else np.inf)
+
+
+# Plausible slips in the gap, planted in a copy of the oracle's own source
+# (the line as written, then the mistake).
+GAP_MUTATIONS = {
+    "sign_flipped": ("gap_out[t] = have_second ? row[best] - second : INFINITY;",
+                     "gap_out[t] = have_second ? second - row[best] : INFINITY;"),
+    "second_by_position": ("if (isnan(row[i]) || id == best_id) continue;",
+                           "if (isnan(row[i]) || i == best) continue;"),
+    "no_other_id_gives_zero": ("gap_out[t] = have_second ? row[best] - second : INFINITY;",
+                               "gap_out[t] = have_second ? row[best] - second : 0.0;"),
+}
+
+
+@pytest.mark.parametrize("mutation", sorted(GAP_MUTATIONS))
+def test_planted_gap_mistakes_are_caught(tmp_path, mutation):
+    """Each planted mistake, compiled from the oracle's source, fails the gap
+    pins (and gives the value the fixture says it would)."""
+    import ctypes
+    import subprocess
+
+    src = open(os.path.join(os.path.dirname(oracle.__file__), "oracle.c")).read()
+    before, after = GAP_MUTATIONS[mutation]
+    assert src.count(before) == 1, "the line the mutation edits has changed"
+    path = tmp_path / "oracle_mutant.c"
+    path.write_text(src.replace(before, after))
+    lib_path = tmp_path / "liboracle_mutant.so"
+    subprocess.run(["gcc", "-O1", "-std=c11", "-fPIC", "-shared", "-o", str(lib_path), str(path), "-lm",
+                    "-lpthread"], check=True)
+    lib = ctypes.CDLL(str(lib_path))
+    caught = 0
+    for c in load("argmax_gap.json")["cases"]:
+        y, ids, gap_ref = _gap_case(c)
+        _, _, gap = oracle.argmax(y, ids, lib=lib)
+        if gap[0] != gap_ref:
+            caught += 1
+        if mutation in c.get("wrong", {}):
+            assert gap[0] == c["wrong"][mutation], (c["name"], gap[0])
+    assert caught > 0, f"the gap pins do not catch {mutation}"
+
+
 # -------------------------------------------------- planted oracle mistakes ----
 
 def _planted_wrong_order(packed):

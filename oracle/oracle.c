@@ -26,10 +26,11 @@
  * only rounding is the summation, about K * 2^-53 relative.
  *
  * The gathered head (swift-qwen3.8 project page, "Body, heads and drafter":
- * the draft head is "a slice of the lm_head with rows only for the tokens in
- * the draft vocabulary") scores output row i with weight row row_ids[i].
- * Greedy acceptance compares argmaxes over the verify rows (article section
- * "What each one calls the same answer"); the argmax here returns, per
+ * the drafter's head keeps only those lm_head rows that belong to the draft
+ * vocabulary) scores output row i with weight row row_ids[i].  Greedy
+ * verification keeps a draft that equals the argmax of its verify row
+ * (article section "What each one calls the same answer"); the argmax here
+ * returns, per
  * activation row t, the maximum and the lowest vocabulary id attaining it,
  * never a NaN.  Ids outside [0, n_rows) give a NaN output row.
  */
@@ -204,10 +205,10 @@ void oracle_argmax(const double* y, const int32_t* ids, int64_t n, int T, int32_
 
 /* ------------------------------------------------------ verify epilogue ----
  *
- * Per-row top-k.  The OpenJet engine page ("How it gets its speed") keeps
- * the 32 best logits of each verified row for its sampler, and the
- * qwen-warp article ("What each one calls the same answer") rescores the
- * quantized head's 16 best candidates.  Definition used here: for each
+ * Per-row top-k.  The OpenJet engine page ("How it gets its speed") hands
+ * its sampler the highest 32 scores of every verified row, and the
+ * qwen-warp article ("What each one calls the same answer") rescores the 16
+ * highest candidates of the quantized head.  Definition used here: for each
  * activation row t of y[T][n], the k largest non-NaN scores with their
  * vocabulary ids (ids[i], or i when ids is NULL), in descending order of
  * score, equal scores in ascending order of id -- so entry 0 is the argmax
@@ -250,9 +251,9 @@ void oracle_topk(const double* y, const int32_t* ids, int64_t n, int T, int k, i
 }
 
 /* Greedy verification.  qwen-warp article, "What each one calls the same
- * answer": greedy acceptance is an argmax equality over the verify rows;
- * OpenJet engine page, "How it works": verification runs on the device and
- * the host reads back only the accepted tokens.
+ * answer": under greedy decoding a draft is kept when it equals the target's
+ * argmax on its verify row; OpenJet engine page, "How it works": the check
+ * runs on the GPU, and only the tokens it accepts are copied to the host.
  *
  * n_seq sequences of `rows` verify rows each.  Row r of sequence s carries
  * the target model's greedy choice target[s*rows + r] for the token after
@@ -275,9 +276,9 @@ void oracle_greedy_accept(const int32_t* target, const int32_t* draft, int n_seq
 }
 
 /* Draft-head id list with the sequence's tokens.  OpenJet engine page ("How
- * it gets its speed"): the draft lm_head is restricted to the 32,768 most
- * frequent tokens plus the tokens of the current sequence missing from that
- * list, added on the fly; verification still uses the full vocabulary.
+ * it gets its speed"): the drafter's head scores a fixed list of 32,768
+ * common tokens, extended at run time by whichever ids of the current
+ * sequence the list lacks; verification scores every vocabulary id.
  * Definition used here: the base list as given, then every id of seq in
  * order of first appearance that lies in [0, n_rows) and is neither in the
  * base list nor already added.  out has n_base + n_seq slots; the slots

@@ -1,10 +1,10 @@
 // Verify epilogue of libw4a16 (gfx950): per-row top-k of head scores and
 // greedy acceptance of drafted tokens.
 //
-// Top-k.  The OpenJet engine page ("How it gets its speed") keeps the 32
-// best logits of each verified row for its sampler; the qwen-warp article
-// ("What each one calls the same answer") rescores the quantized head's 16
-// best candidates.  For each activation row t of scores[T][n]: the k largest
+// Top-k.  The OpenJet engine page ("How it gets its speed") hands its
+// sampler the highest 32 scores of every verified row; the qwen-warp article
+// ("What each one calls the same answer") rescores the 16 highest
+// candidates of the quantized head.  For each activation row t of scores[T][n]: the k largest
 // non-NaN scores with their vocabulary ids, score descending, equal scores
 // by ascending id (entry 0 is the head's argmax).  Every candidate is one
 // 64-bit key whose unsigned order is that order: an order-preserving image
@@ -16,13 +16,14 @@
 // k-th largest of part maxima, rank the few keys at or above the bound by
 // counting, and fall back to a bitonic sort in LDS when many keys tie.
 //
-// Greedy acceptance.  The same article section: greedy acceptance is an
-// argmax equality over the verify rows; the OpenJet page ("How it works"):
-// the host reads back only the accepted tokens.  One thread per sequence.
+// Greedy acceptance.  The same article section: under greedy decoding a
+// draft is kept when it equals the target's argmax on its verify row; the
+// OpenJet page ("How it works"): only the accepted tokens travel to the
+// host.  One thread per sequence.
 //
-// Draft-head id list.  The OpenJet page ("How it gets its speed"): the draft
-// head covers the 32,768 most frequent tokens plus the tokens of the current
-// sequence missing from them, added on the fly.  One workgroup: the base
+// Draft-head id list.  The OpenJet page ("How it gets its speed"): the
+// drafter's head scores a fixed list of 32,768 common tokens, extended at
+// run time by whichever ids of the current sequence the list lacks.  One workgroup: the base
 // ids go into a vocabulary bitmap in LDS; an LDS hash table keeps the first
 // position of every sequence id (atomic insert, atomic minimum); a prefix
 // count over positions then places the new ids in order of first

@@ -1,8 +1,8 @@
 """GPU parity for T = 9..16 activation rows in one weight read.
 
 Several sequences with their drafts verified in one pass (the qwen-warp
-article's multi-user outlook: the W4 product takes up to 16 rows per weight
-read, e.g. four sequences with three drafts each).  Every case runs the
+article's outlook for several users: one weight read can serve as many as
+16 activation rows, for instance 4 sequences carrying 3 drafts apiece).  Every case runs the
 matrix-core kernels (the dot variant is built for T <= 8; selecting it at
 larger T still runs the matrix cores), in both weight layouts, single and
 grouped launches, and on the heads with argmax.  Expected values come only

@@ -4,9 +4,10 @@
  *
  * The operation.  Single-stream decode reads every weight once per cycle and
  * verifies T = 1 + n_draft tokens against it (qwen-warp/llamAmpere article,
- * "The arithmetic every claim answers to": decode is a weight read, and a
- * verify pass costs about the same as a one-token pass when the kernel reads
- * the weights once for all T rows).  Weights are W4A16 with group 128, in the
+ * "The arithmetic every claim answers to": a decode step lasts as long as
+ * reading the weights takes, so scoring several drafted tokens costs about
+ * as much as one token when each weight is read a single time for the whole
+ * block of T rows).  Weights are W4A16 with group 128, in the
  * format that article describes under "qwen-warp: keep the activations in
  * bf16": 4-bit codes packed as little-endian words of eight nibbles, level =
  * code - 8, one bf16 scale per 128 columns of a row.  For T activation rows
@@ -14,11 +15,14 @@
  *
  *     y[t][n] = sum_k (q[n][k] - 8) * scale[n][k/128] * x[t][k].
  *
- * Each level (q - 8) and each product with x is formed exactly; sums are fp32,
- * with a fresh partial per 128-column group multiplied by that group's scale
- * (the same section: the group scale is applied in fp32 after each group's
- * accumulate).  Results agree with the exact sum within
- * 1e-3 * sum_k |w*x| + 1e-6 per element.
+ * Each level (q - 8) and each product with x is formed exactly, for every
+ * finite bf16 x (the activations stay bf16; the matrix cores multiply them
+ * with bf16 levels); sums are fp32, with a fresh partial per 128-column group
+ * multiplied by that group's scale (the same section: the scale multiplies,
+ * in fp32, the sum of the group's products).  Results agree with the exact
+ * sum within 1e-3 * sum_k |w*x| + 1e-6 per element, for any finite inputs
+ * whose partial sums stay inside the fp32 range (beyond about 3.4e38 a sum
+ * overflows to infinity, as the fp32 output itself must).
  *
  * Layout (all row-major, all device memory owned by the caller):
  *   packed_u4    uint8   [rows][K/2]    byte j of a row holds column 2j in bits
@@ -57,7 +61,7 @@ typedef struct ihipStream_t* hipStream_t; /* same definition as the HIP runtime'
 
 #define W4A16_GROUP 128      /* columns per bf16 scale */
 #define W4A16_MAX_T 16       /* activation rows per weight read */
-#define W4A16_ABI_VERSION 5
+#define W4A16_ABI_VERSION 6
 
 typedef enum {
   W4A16_OK = 0,
@@ -72,14 +76,12 @@ typedef enum {
 
 /* Kernel variants.  Both compute the same values within the tolerance above.
  * AUTO runs the matrix-core kernels: on MI355X they are faster on every
- * workload shape at every T (1-3% on the short projections at T = 1, 2.4-11x
- * from T = 4).  The dot variant covers T <= 8;
- * calls with more activation rows run the matrix-core kernels whatever the
- * selection. */
+ * workload shape at every T.  The dot variant covers T <= 8; calls with more
+ * activation rows run the matrix-core kernels whatever the selection. */
 typedef enum {
   W4A16_VARIANT_AUTO = 0,
-  W4A16_VARIANT_DOT = 1, /* VALU dot products, split-K across lanes, cross-lane reduction */
-  W4A16_VARIANT_MFMA = 2 /* fp16 matrix cores, tokens padded to 16 rows */
+  W4A16_VARIANT_DOT = 1, /* VALU bf16 dot products, split-K across lanes, cross-lane reduction */
+  W4A16_VARIANT_MFMA = 2 /* bf16 matrix cores, tokens padded to 16 rows */
 } w4a16_variant;
 
 /*
@@ -94,10 +96,10 @@ w4a16_status w4a16_matmul(const uint8_t* packed_u4, const uint16_t* scales_bf16,
 /*
  * Scores a subset of the rows of an output head (e.g. the lm_head) and
  * optionally takes the per-row argmax.  Follows the draft head of the
- * swift-qwen3.8-rtx3090 project page ("Body, heads and drafter": a slice of
- * the lm_head with rows only for the draft-vocabulary tokens) and the OpenJet
- * engine page ("How it gets its speed": the draft head restricted to a token
- * list; verification still scores the full vocabulary).
+ * swift-qwen3.8-rtx3090 project page ("Body, heads and drafter": the
+ * drafter's head keeps only the lm_head rows of the draft vocabulary) and the
+ * OpenJet engine page ("How it gets its speed": the drafter scores a token
+ * list, verification every vocabulary id).
  *
  *   row_ids   int32 [n_ids] device ids into [0, n_rows); output row i uses
  *             weight row row_ids[i].  NULL means the identity, n_ids = n_rows
@@ -107,9 +109,9 @@ w4a16_status w4a16_matmul(const uint8_t* packed_u4, const uint16_t* scales_bf16,
  *   argmax_id [T] or NULL (no argmax); argmax_val [T] or NULL (needs
  *             argmax_id).  For each t: the largest
  *             non-NaN score and the lowest vocabulary id (row_ids value)
- *             attaining it -- greedy acceptance is an argmax equality over the
- *             verify rows (article section "What each one calls the same
- *             answer").  No valid row: id -1, value NaN.
+ *             attaining it; greedy verification accepts a draft when it
+ *             equals this argmax (qwen-warp/llamAmpere article, "What each
+ *             one calls the same answer").  No valid row: id -1, value NaN.
  *   workspace device scratch of at least w4a16_workspace_bytes(n_ids, T) bytes
  *             (16-byte aligned), required when argmax is requested; its
  *             contents need no initialisation and are meaningless afterwards.
@@ -129,10 +131,11 @@ size_t w4a16_workspace_bytes(int64_t n_out, int32_t T);
  * Tiled weight layout: a one-time repack of the same codes and scales so
  * that each group of 16 rows x 128 columns is one contiguous 1 KB block and
  * each row's scales travel with its codes.  Follows the OpenJet engine page
- * ("How it gets its speed"): some weight formats are re-laid-out once at load
- * time, values unchanged, so every lane does aligned wide loads and a block's
- * scales arrive with its data.  On MI355X a wave's 16-byte-per-lane load then
- * covers one contiguous 1 KB block instead of 64 bytes of 16 rows.
+ * ("How it gets its speed"), whose engine rearranges some weight formats a
+ * single time when the model loads -- the numbers stay the same -- so that
+ * the loads are wide and aligned and the scales come in the same block as
+ * the codes.  On MI355X a wave's 16-byte-per-lane load then covers one
+ * contiguous 1 KB block instead of 64 bytes of 16 rows.
  *
  * Definition (G = K/128 groups, rows padded to a multiple of 16 with zero
  * bytes): for tile i (rows 16i .. 16i+15), chunk c (groups 8c .. 8c+ng-1,
@@ -164,14 +167,16 @@ w4a16_status w4a16_repack_tiled(const uint8_t* packed_u4, const uint16_t* scales
  * The tiled layout of a subset of a weight's rows: output row i holds input
  * row row_ids[i] of packed_u4 [n_rows][K/2] / scales_bf16 [n_rows][K/128].
  * For a head restricted to a fixed id list (the swift-qwen3.8-rtx3090 page,
- * "Body, heads and drafter": the draft head is a slice of the lm_head with
- * rows only for the draft-vocabulary tokens), built once at load: the slice
- * is then a plain tiled matrix of n_ids rows, read in whole 1 KB blocks
- * instead of 64-byte pieces of scattered rows.  Scores and argmax of calls on
- * it are by position i; the vocabulary id is row_ids[i] (with row_ids in
- * ascending order, the lowest-position tie rule is the lowest-id rule).
- *   row_ids  int32 [n_ids] device, each in [0, n_rows) (an id outside gives
- *            an all-zero row, i.e. scores of 0); duplicates allowed.
+ * "Body, heads and drafter": the drafter's head keeps only the lm_head rows
+ * of the draft vocabulary), built once at load: the subset is then a plain
+ * tiled matrix of n_ids rows, read in whole 1 KB blocks instead of 64-byte
+ * pieces of scattered rows.  Scores and argmax of calls on it are by
+ * position i; the vocabulary id is row_ids[i] (with row_ids in ascending
+ * order, the lowest-position tie rule is the lowest-id rule).
+ *   row_ids  int32 [n_ids] device, each in [0, n_rows); duplicates allowed.
+ *            An id outside gives a row of zero codes and NaN scales, whose
+ *            scores are NaN and never win an argmax (as the same id does in
+ *            w4a16_head_gather).
  *   tiled    device, 16-byte aligned, >= w4a16_tiled_bytes(n_ids, K) bytes.
  *   Shapes: 1 <= n_rows, n_ids <= 2^31-1; K as for w4a16_matmul.
  */
@@ -241,21 +246,13 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
 w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, hipStream_t stream);
 
 /*
- * The same grouped launch with a device workspace for the activations: from
- * T = 9 on, the plan converts every problem's activations once per launch
- * (a small kernel before the grouped one, on the same stream) into the
- * workspace, and the workgroups copy them from there straight into LDS
- * instead of each converting its own copy (exact fp16 times a power of two
- * per activation row, chosen over the row's whole K; results within the
- * tolerance of w4a16_matmul, and bit for bit those of w4a16_matmul_batch
- * unless a row's values span more than about 2^28 and the workgroups stage
- * its K in slices, each with its own power of two).  w4a16_batch_workspace_bytes(table_host) gives
- * the size (0 when the plan stages without one, and for a table that is not
- * one): T * K * 2 + 16 bytes per problem, plus 16.  The workspace is device
- * memory, 16-byte aligned, needs no initialisation, holds nothing between
- * launches, and must not be shared by launches that may run concurrently.
- * With a size-0 plan, workspace may be NULL and the call is
- * w4a16_matmul_batch.
+ * The grouped launch with a device workspace for the activations.  No
+ * plan needs one: the workgroups copy every problem's bf16 activations
+ * straight into LDS (no conversion), so w4a16_batch_workspace_bytes returns
+ * 0 for every table (and for anything that is not a table), the workspace
+ * arguments of w4a16_matmul_batch_ws are ignored (NULL and 0 are fine), and
+ * the call is w4a16_matmul_batch.  Kept so that callers written against the
+ * workspace form keep working.
  */
 size_t w4a16_batch_workspace_bytes(const void* table_host);
 w4a16_status w4a16_matmul_batch_ws(const void* table_host, const void* table_dev, void* workspace,
@@ -266,10 +263,10 @@ w4a16_status w4a16_matmul_batch_ws(const void* table_host, const void* table_dev
  * before the host reads anything back (OpenJet engine page, "How it works":
  * verification on the device, only the accepted tokens go to the host).
  *
- * Per-row top-k.  The OpenJet page ("How it gets its speed") keeps the 32
- * best logits of each verified row for its sampler; the qwen-warp article
- * ("What each one calls the same answer") rescores the quantized head's 16
- * best candidates.  For each activation row t of scores [T][n] (e.g. the y
+ * Per-row top-k.  The OpenJet page ("How it gets its speed") hands its
+ * sampler the highest 32 scores of every row it verifies; the qwen-warp
+ * article ("What each one calls the same answer") rescores the 16 highest
+ * candidates of the quantized head.  For each activation row t of scores [T][n] (e.g. the y
  * of w4a16_head_gather): the k largest non-NaN scores and their vocabulary
  * ids, score descending, equal scores by ascending id, so entry 0 is the
  * argmax of w4a16_head_gather.  -0 and +0 are equal.  Position i has
@@ -293,7 +290,8 @@ w4a16_status w4a16_topk(const float* scores, int64_t n, int32_t T, const int32_t
 
 /*
  * Greedy acceptance (qwen-warp article, "What each one calls the same
- * answer": greedy acceptance is an argmax equality over the verify rows).
+ * answer": under greedy decoding a draft is kept when it equals the target
+ * model's argmax on its verify row).
  * n_seq sequences of `rows` verify rows each, e.g. the T = n_seq * rows rows
  * of one head call.  Row r of sequence s carries the target model's greedy
  * choice target_ids[s*rows + r] (the argmax ids of w4a16_head_gather) for
@@ -313,9 +311,9 @@ w4a16_status w4a16_greedy_accept(const int32_t* target_ids, const int32_t* draft
 
 /*
  * Draft-head id list with the sequence's tokens (OpenJet engine page, "How
- * it gets its speed": the draft lm_head covers the 32,768 most frequent
- * tokens plus the tokens of the current sequence missing from them, added
- * on the fly; verification still scores the full vocabulary).  Writes into
+ * it gets its speed": the drafter's head scores a fixed list of 32,768
+ * common tokens, extended at run time by whichever ids of the current
+ * sequence the list lacks, while verification scores every vocabulary id).  Writes into
  * union_ids [n_base + n_seq]: base_ids verbatim, then every id of seq_ids in
  * order of first appearance that lies in [0, n_rows) and is neither in the
  * base list nor already added, then -1 in the remaining slots; *n_union (one

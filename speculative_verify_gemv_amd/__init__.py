@@ -7,6 +7,7 @@ built, or the device is not gfx950, calls raise.
 """
 from __future__ import annotations
 
+import contextlib
 import ctypes
 import os
 
@@ -121,6 +122,13 @@ def _stream(stream) -> int:
     return stream.cuda_stream
 
 
+def _on(stream):
+    """Context in which the tensors a call allocates (outputs, scratch) belong
+    to the stream its kernels run on, so that the caching allocator orders
+    their reuse after that work."""
+    return contextlib.nullcontext() if stream is None else torch.cuda.stream(stream)
+
+
 def _check_bits(t: torch.Tensor, what: str) -> None:
     if t.dtype not in (torch.bfloat16, torch.int16, torch.uint16):
         raise TypeError(f"{what} must hold bf16 bit patterns (bfloat16/int16/uint16), got {t.dtype}")
@@ -148,7 +156,8 @@ def matmul(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, out: tor
         raise ValueError(f"x must be [T][{K}]")
     T = x.shape[0]
     if out is None:
-        out = torch.empty((T, N), dtype=torch.float32, device=packed.device)
+        with _on(stream):
+            out = torch.empty((T, N), dtype=torch.float32, device=packed.device)
     elif out.dtype != torch.float32 or out.shape != (T, N) or not out.is_contiguous():
         raise ValueError("out must be a contiguous float32 tensor [T][N]")
     s = load_library().w4a16_matmul(_ptr(packed), _ptr(scales), _ptr(x), _ptr(out), N, K, T, _stream(stream))
@@ -194,7 +203,8 @@ def head_gather(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, row
         raise ValueError(f"x must be [T][{K}]")
     T = x.shape[0]
     n = _row_ids(row_ids, n_rows)
-    y, ids, vals, workspace, ws_bytes = _gather_outputs(n, T, packed.device, scores, argmax, out, workspace)
+    with _on(stream):
+        y, ids, vals, workspace, ws_bytes = _gather_outputs(n, T, packed.device, scores, argmax, out, workspace)
     s = load_library().w4a16_head_gather(_ptr(row_ids), n, _ptr(packed), _ptr(scales), n_rows, _ptr(x), K, T,
                                          _ptr(y), _ptr(ids), _ptr(vals), _ptr(workspace), ws_bytes,
                                          _stream(stream))
@@ -222,7 +232,8 @@ def repack_tiled(packed: torch.Tensor, scales: torch.Tensor, stream=None) -> Til
     """Tiled-layout copy of a row-major weight (runs on the GPU)."""
     N, K = _check_weight(packed, scales)
     nbytes = tiled_bytes(N, K)
-    data = torch.empty(nbytes, dtype=torch.uint8, device=packed.device)
+    with _on(stream):
+        data = torch.empty(nbytes, dtype=torch.uint8, device=packed.device)
     s = load_library().w4a16_repack_tiled(_ptr(packed), _ptr(scales), N, K, _ptr(data), nbytes, _stream(stream))
     if s:
         raise W4A16Error(s, "w4a16_repack_tiled")
@@ -237,7 +248,8 @@ def repack_tiled_rows(packed: torch.Tensor, scales: torch.Tensor, row_ids: torch
         raise ValueError("row_ids must be a contiguous CUDA int32 vector")
     n = row_ids.shape[0]
     nbytes = tiled_bytes(n, K)
-    data = torch.empty(nbytes, dtype=torch.uint8, device=packed.device)
+    with _on(stream):
+        data = torch.empty(nbytes, dtype=torch.uint8, device=packed.device)
     s = load_library().w4a16_repack_tiled_rows(_ptr(packed), _ptr(scales), n_rows, K, _ptr(row_ids), n, _ptr(data),
                                                nbytes, _stream(stream))
     if s:
@@ -251,7 +263,8 @@ def matmul_tiled(w: TiledWeight, x: torch.Tensor, out: torch.Tensor | None = Non
     if x.dim() != 2 or x.shape[1] != w.K:
         raise ValueError(f"x must be [T][{w.K}]")
     T = x.shape[0]
-    y = out if out is not None else torch.empty((T, w.N), dtype=torch.float32, device=w.device)
+    with _on(stream):
+        y = out if out is not None else torch.empty((T, w.N), dtype=torch.float32, device=w.device)
     if y.dtype != torch.float32 or y.shape != (T, w.N) or not (y.is_cuda and y.is_contiguous()):
         raise ValueError("out must be a contiguous CUDA float32 tensor [T][N]")
     s = load_library().w4a16_matmul_tiled(_ptr(w.data), _ptr(x), _ptr(y), w.N, w.K, T, _stream(stream))
@@ -269,7 +282,8 @@ def head_gather_tiled(w: TiledWeight, x: torch.Tensor, row_ids: torch.Tensor | N
         raise ValueError(f"x must be [T][{w.K}]")
     T = x.shape[0]
     n = _row_ids(row_ids, w.N)
-    y, ids, vals, workspace, ws_bytes = _gather_outputs(n, T, w.device, scores, argmax, out, workspace)
+    with _on(stream):
+        y, ids, vals, workspace, ws_bytes = _gather_outputs(n, T, w.device, scores, argmax, out, workspace)
     s = load_library().w4a16_head_gather_tiled(_ptr(row_ids), n, _ptr(w.data), w.N, _ptr(x), w.K, T, _ptr(y),
                                                _ptr(ids), _ptr(vals), _ptr(workspace), ws_bytes, _stream(stream))
     if s:
@@ -331,19 +345,15 @@ class Batch:
         self.device = self.host.to(problems[0][2].device, non_blocking=False)
         self.T = T
         self.count = len(problems)
-        wsb = lib.w4a16_batch_workspace_bytes(self.host.data_ptr())
-        self.workspace = torch.empty(wsb, dtype=torch.uint8, device=self.device.device) if wsb else None
+        # no plan needs an activation workspace: the workgroups copy the bf16
+        # activations straight into LDS (w4a16_batch_workspace_bytes is 0)
+        self.workspace = None
+        if lib.w4a16_batch_workspace_bytes(self.host.data_ptr()) != 0:
+            raise RuntimeError("the library planned an activation workspace; this binding passes none")
 
-    def run(self, stream=None, staged: bool = True) -> None:
-        """One grouped launch.  staged: with the plan's activation workspace
-        (w4a16_matmul_batch_ws) when it has one; False: every workgroup
-        converts its own activations (w4a16_matmul_batch)."""
-        lib = load_library()
-        if staged and self.workspace is not None:
-            s = lib.w4a16_matmul_batch_ws(self.host.data_ptr(), self.device.data_ptr(), self.workspace.data_ptr(),
-                                          self.workspace.numel(), _stream(stream))
-        else:
-            s = lib.w4a16_matmul_batch(self.host.data_ptr(), self.device.data_ptr(), _stream(stream))
+    def run(self, stream=None) -> None:
+        """One grouped launch (w4a16_matmul_batch) on `stream` (default: the current stream)."""
+        s = load_library().w4a16_matmul_batch(self.host.data_ptr(), self.device.data_ptr(), _stream(stream))
         if s:
             raise W4A16Error(s, "w4a16_matmul_batch")
 
@@ -367,10 +377,11 @@ def topk(scores: torch.Tensor, k: int, row_ids: torch.Tensor | None = None, work
     nbytes = topk_workspace_bytes(n, T, k)
     if nbytes == 0:
         raise ValueError("topk: size out of range")
-    if workspace is None:
-        workspace = torch.empty(nbytes, dtype=torch.uint8, device=scores.device)
-    ids = torch.empty((T, k), dtype=torch.int32, device=scores.device)
-    vals = torch.empty((T, k), dtype=torch.float32, device=scores.device)
+    with _on(stream):
+        if workspace is None:
+            workspace = torch.empty(nbytes, dtype=torch.uint8, device=scores.device)
+        ids = torch.empty((T, k), dtype=torch.int32, device=scores.device)
+        vals = torch.empty((T, k), dtype=torch.float32, device=scores.device)
     st = load_library().w4a16_topk(scores.data_ptr(), n, T, _ptr(row_ids), k, ids.data_ptr(), vals.data_ptr(),
                                    workspace.data_ptr(), workspace.numel() * workspace.element_size(),
                                    _stream(stream))
@@ -388,8 +399,9 @@ def greedy_accept(target_ids: torch.Tensor, draft_ids: torch.Tensor | None, n_se
             raise ValueError(f"{what} must be a contiguous CUDA int32 tensor")
     if target_ids.numel() != n_seq * rows or (draft_ids is not None and draft_ids.numel() != n_seq * (rows - 1)):
         raise ValueError("target_ids must hold n_seq*rows ids and draft_ids n_seq*(rows-1)")
-    acc = torch.empty(n_seq, dtype=torch.int32, device=target_ids.device)
-    tok = torch.empty((n_seq, rows), dtype=torch.int32, device=target_ids.device)
+    with _on(stream):
+        acc = torch.empty(n_seq, dtype=torch.int32, device=target_ids.device)
+        tok = torch.empty((n_seq, rows), dtype=torch.int32, device=target_ids.device)
     st = load_library().w4a16_greedy_accept(target_ids.data_ptr(), _ptr(draft_ids), n_seq, rows, acc.data_ptr(),
                                             tok.data_ptr(), _stream(stream))
     if st:
@@ -407,8 +419,9 @@ def draft_union(base_ids: torch.Tensor | None, seq_ids: torch.Tensor | None, n_r
     nb = 0 if base_ids is None else base_ids.numel()
     ns = 0 if seq_ids is None else seq_ids.numel()
     device = (base_ids if base_ids is not None else seq_ids).device
-    out = torch.empty(nb + ns, dtype=torch.int32, device=device)
-    length = torch.empty(1, dtype=torch.int32, device=device)
+    with _on(stream):
+        out = torch.empty(nb + ns, dtype=torch.int32, device=device)
+        length = torch.empty(1, dtype=torch.int32, device=device)
     st = load_library().w4a16_draft_union(_ptr(base_ids) if nb else None, nb, _ptr(seq_ids) if ns else None, ns,
                                           n_rows, out.data_ptr(), length.data_ptr(), _stream(stream))
     if st:

@@ -157,13 +157,6 @@ struct ArgmaxRecord {
 };
 static_assert(sizeof(ArgmaxRecord) == 32 && sizeof(w4a16::GemvArgs) == 144, "batch table record sizes");
 
-// Grouped launches from this many activation rows on stage the activations
-// from a workspace converted once per launch (direct global-to-LDS copies
-// in the workgroups); below it the workgroups convert their own.  Measured
-// on the 27B-class body pass: +0.6% at T = 12, +2.5% at T = 16; at T = 8 the
-// conversion launch costs what the copies save.
-constexpr int kWorkspaceMinT = 9;
-
 // Tile of grouped launches, from the MI355X sweeps.  All problems tiled:
 // at T <= 2 shared workgroups of one tile per wave; above, run workgroups
 // of eight waves, four tiles per wave at T <= 4 and six at T <= 8 (two such
@@ -182,8 +175,7 @@ w4a16::Tile batch_tile(int T, bool all_tiled, int64_t kmax) {
                : w4a16::Tile{w4a16::kRun, T <= 4 ? 4 : T <= 8 ? 6 : 4, T <= 8 ? 8 : 16};
   else
     t = T == 1 ? w4a16::Tile{w4a16::kShared, 2, 4} : w4a16::Tile{w4a16::kShared, 4, 4};
-  w4a16::Tile o;
-  if (w4a16::parse_tile(std::getenv("W4A16_BATCH_TILE"), &o)) t = o;
+  w4a16::tile_override(true, &t);
   return t;
 }
 
@@ -198,17 +190,13 @@ const TableHeader* valid_table(const void* table_host) {
   return hdr;
 }
 
-// A planned grouped launch: with_ws (w4a16_matmul_batch_ws) and a table that
-// plans a workspace convert the activations into it first.
-w4a16_status run_batch(const void* table_host, const void* table_dev, void* workspace, size_t workspace_bytes,
-                       bool with_ws, hipStream_t stream) {
+// A planned grouped launch.  Plans need no workspace (ws_bytes 0): the
+// workgroups copy every problem's bf16 activations straight into LDS.
+w4a16_status run_batch(const void* table_host, const void* table_dev, hipStream_t stream) {
   if (!table_host || !table_dev) return W4A16_ERR_NULL_POINTER;
   if (!aligned(table_dev, 16) || !aligned(table_host, 8)) return W4A16_ERR_MISALIGNED;
   const TableHeader* hdr = valid_table(table_host);
   if (!hdr) return W4A16_ERR_BAD_SHAPE;
-  const bool staged = with_ws && hdr->ws_bytes > 0;
-  if (staged && (!workspace || !aligned(workspace, 16) || workspace_bytes < (size_t)hdr->ws_bytes))
-    return W4A16_ERR_WORKSPACE;
   w4a16::Plan p{};
   if (hdr->variant != w4a16::kSplit && hdr->variant != w4a16::kShared && hdr->variant != w4a16::kRun)
     return W4A16_ERR_BAD_SHAPE;
@@ -224,12 +212,6 @@ w4a16_status run_batch(const void* table_host, const void* table_dev, void* work
   p.grid = hdr->grid;
   p.lds = hdr->lds;
   const auto* args = reinterpret_cast<const w4a16::GemvArgs*>(static_cast<const TableHeader*>(table_dev) + 1);
-  if (staged) {
-    p.ws = static_cast<const unsigned char*>(workspace);
-    if (w4a16::launch_stage_x(args, hdr->count, hdr->T, static_cast<unsigned char*>(workspace), stream) !=
-        hipSuccess)
-      return W4A16_ERR_HIP;
-  }
   if (w4a16::launch_batch(args, hdr->count, p, hdr->T, stream) != hipSuccess) return W4A16_ERR_HIP;
   const auto* recs = reinterpret_cast<const ArgmaxRecord*>(reinterpret_cast<const w4a16::GemvArgs*>(hdr + 1) +
                                                            hdr->count);
@@ -386,7 +368,7 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
   // not fit runs shared workgroups inside the run kernel); a plan that still
   // differs between problems falls back to shared workgroups.
   for (int attempt = 0; attempt < 2; ++attempt) {
-    int64_t grid = 0, ws_bytes = 16;  // the workspace starts with 16 zero bytes
+    int64_t grid = 0;
     int lds = 0, threads = 64, rt = 0, n_argmax = 0;
     bool uniform = true;
     for (int32_t i = 0; i < count; ++i) {
@@ -395,9 +377,6 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
       w4a16::GemvArgs a = gemv_args(q.packed_u4, tiled ? nullptr : q.scales_bf16, tiled, q.x_bf16, q.y_f32,
                                     nullptr, q.N, q.N, q.K);
       a.partial = q.argmax_id ? static_cast<int2*>(q.workspace) : nullptr;
-      a.x16_off = ws_bytes;  // pre-converted activations, then the row exponents
-      a.e_off = ws_bytes + (int64_t)T * q.K * 2;
-      ws_bytes = a.e_off + (((int64_t)T * 4 + 15) & ~15LL);
       const w4a16::Plan p = w4a16::plan_tile(a, T, bt, all_tiled, true);
       uniform = uniform && p.variant == bt.shape;
       rt = p.rt;
@@ -414,7 +393,7 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
     }
     if (grid > 0x7fffffffLL) return W4A16_ERR_BAD_SHAPE;
     *hdr = TableHeader{kTableMagic, W4A16_ABI_VERSION, count, T, bt.shape, rt, all_tiled ? 1 : 0, threads, lds,
-                       n_argmax, grid, T >= kWorkspaceMinT && bt.shape != w4a16::kSplit ? ws_bytes : 0, 0};
+                       n_argmax, grid, 0, 0};
     return W4A16_OK;
   }
   return W4A16_ERR_BAD_SHAPE;  // not reached: shared tiles always plan
@@ -426,12 +405,14 @@ size_t w4a16_batch_workspace_bytes(const void* table_host) {
 }
 
 w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, hipStream_t stream) {
-  return run_batch(table_host, table_dev, nullptr, 0, false, stream);
+  return run_batch(table_host, table_dev, stream);
 }
 
 w4a16_status w4a16_matmul_batch_ws(const void* table_host, const void* table_dev, void* workspace,
                                    size_t workspace_bytes, hipStream_t stream) {
-  return run_batch(table_host, table_dev, workspace, workspace_bytes, true, stream);
+  (void)workspace;  // no plan needs one (w4a16_batch_workspace_bytes is 0)
+  (void)workspace_bytes;
+  return run_batch(table_host, table_dev, stream);
 }
 
 size_t w4a16_topk_workspace_bytes(int64_t n, int32_t T, int32_t k) {

@@ -11,28 +11,45 @@
 // The weight format -- little-endian words of eight nibbles, level = nibble
 // minus 8, one bf16 scale per 128 columns applied after the group's sum -- is
 // the one the qwen-warp/llamAmpere article gives under "qwen-warp: keep the
-// activations in bf16".  That engine turns a nibble pair into exact bf16
-// levels with one OR and one packed bf16 FMA; gfx950 has no packed bf16 add
-// or FMA, so here the exact levels are formed in fp16 instead:
+// activations in bf16".  As in that engine, the activations stay bf16 and
+// the matrix cores multiply them with bf16 levels, so every product
+// (q - 8) * x is exact in fp32 for every finite bf16 x: the activations are
+// copied into LDS as they are, with no conversion and no range rule.  That
+// engine makes a bf16 level pair with one OR and one packed bf16 FMA; gfx950
+// has no packed bf16 arithmetic, so here a word w of eight codes becomes
+// eight exact levels like this:
+//
+//   e = w ^ 0x88888888   every nibble becomes the 4-bit two's complement of
+//                        q - 8 (q ^ 8 read as a signed nibble)
+//   v_cvt_off_f32_i4     a signed nibble n (bits 0-3 of a byte picked by an
+//                        SDWA byte select, of e and of e >> 4) -> n / 16 as an
+//                        fp32, exact
+//   v_perm_b32           the high halves of two such floats -> one bf16 pair
+//                        (a float with at most 4 significant bits equals its
+//                        own top 16 bits read as a bf16)
+//
+// 14 VALU operations per word, levels in natural k order.  The levels carry
+// a factor 1/16, which is taken back when a tile's sum is folded (a power of
+// two), so the result is the fp32 arithmetic of the unscaled levels.
+//
+// Where the loop is tight (up to kF16MaxT activation rows) those 14
+// operations cost about 4.5% of the bandwidth, so the kernels for those row
+// counts first try a cheaper exact form: fp16 levels, 9 operations per word,
 //
 //   (w & 0x000F000F) | 0x6400_6400  is the fp16 pair (1024 + q0, 1024 + q4)
 //   (w & 0x00F000F0) | 0x5400_5400  is the fp16 pair (  64 + q1,   64 + q5)
 //
 // (at 1024 the fp16 spacing is 1, at 64 it is 1/16 and the nibble sits four
-// bits higher), and one v_pk_add_f16 with -1032 / -72 gives (q - 8) exactly.
-// A 32-bit word of codes becomes eight exact fp16 levels in the slot order
-// k+0, k+4, k+1, k+5, k+2, k+6, k+3, k+7 with 9 VALU operations.
-//
-// Activations are converted once per workgroup slice to fp16 in the same
-// slot order, scaled by 2^E (a fixed E when that is exact for every value of
-// the slice, else E chosen per token row and slice from the largest |x|), so
-// every bf16 value that matters is represented exactly; the
-// power of two is removed again when the slice's partial sums are folded, so
-// the result equals the unscaled fp32 arithmetic.  Every product (q-8)*x is
-// exact in fp32; sums are fp32.
+// bits higher), then one v_pk_add_f16 with -1032 / -72 each, against
+// activations converted to fp16 times 2^kDirectE.  That conversion is exact
+// only for magnitudes in [2^-21, 4080] (and zero), so a workgroup uses it
+// only when every activation of its staged slice lies there; otherwise it
+// stages the bf16 activations as they are and runs the bf16 levels.  Both
+// forms give exact products and fp32 sums, so the choice changes rounding
+// order at most, never the tolerance.
 //
 // Two variants:
-//  * matrix core: tokens are the A operand of v_mfma_f32_16x16x32_f16 (T
+//  * matrix core: tokens are the A operand of v_mfma_f32_16x16x32_bf16 (T
 //    padded to 16 rows), weights the B operand (16 output rows x 32 k).  A
 //    lane owns one output row and a quarter of each 128-column group, loads
 //    its 16 bytes of that group with one 128-bit load, and feeds the four
@@ -42,7 +59,7 @@
 //    workgroup the waves own different tiles and share one staged copy of
 //    the activations; in a "split" workgroup they split K over the same
 //    tiles and add their partial sums through LDS in wave order.
-//  * dot: lanes split a row's K in 16-byte chunks; v_dot2_f32_f16 forms each
+//  * dot: lanes split a row's K in 16-byte chunks; v_dot2_f32_bf16 forms each
 //    chunk's partial, which is scaled by its group scale; the 32 lanes of a
 //    row are reduced with DPP row operations and one ds_swizzle.
 //
@@ -52,6 +69,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
@@ -62,11 +80,13 @@
 namespace w4a16 {
 namespace {
 
+typedef __bf16 b8_t __attribute__((ext_vector_type(8)));  // the bf16 MFMA builtin's operand type
+typedef __bf16 b2_t __attribute__((ext_vector_type(2)));
+typedef __fp16 h8_t __attribute__((ext_vector_type(8)));  // the fp16 MFMA builtin's operand type
 typedef _Float16 h2_t __attribute__((ext_vector_type(2)));
-typedef __fp16 h8_t __attribute__((ext_vector_type(8)));  // the MFMA builtin's operand type
+typedef unsigned short us2_t __attribute__((ext_vector_type(2)));
 typedef float f4_t __attribute__((ext_vector_type(4)));
 typedef unsigned u4_t __attribute__((ext_vector_type(4)));
-typedef unsigned short us2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kGroup = 128;
 constexpr int kLdsCap = 65536;  // dynamic LDS per workgroup (several workgroups per CU)
@@ -74,6 +94,14 @@ constexpr int kCuLds = 163840;  // LDS of a CU (one workgroup per CU)
 constexpr int kRing = 8;        // groups of weight codes in flight per wave
 // s_waitcnt immediate (gfx9 encoding) waiting for vmcnt = 0 only.
 constexpr int kWaitVmcnt0 = 0x0F70;
+// The bf16 levels are (q - 8) / 16; a tile's sum is multiplied by this.
+constexpr float kLevelScale = 16.0f;
+// Kernels for up to this many activation rows try the fp16 form first.
+constexpr int kF16MaxT = 4;
+// The fp16 form's activations are x * 2^kDirectE; a tile's sum is
+// multiplied by 2^-kDirectE.
+constexpr int kDirectE = 4;
+constexpr float kDirectScale = 1.0f / (1 << kDirectE);
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
 
@@ -112,6 +140,35 @@ __device__ __forceinline__ void st_partial(int2* p, float v, int id) {
             (unsigned long long)__float_as_uint(v) | ((unsigned long long)(unsigned)id << 32));
 }
 
+// v_cvt_off_f32_i4 on bits 0-3 of byte B of v: the signed nibble n as n / 16.
+// Written out so that every nibble costs one instruction (the SDWA byte
+// select); left to itself the compiler shifts first for some of them.
+template <int B>
+__device__ __forceinline__ float nibble_f32(unsigned v) {
+  float r;
+  if constexpr (B == 0) asm("v_cvt_off_f32_i4_e32 %0, %1" : "=v"(r) : "v"(v));
+  if constexpr (B == 1)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(v));
+  if constexpr (B == 2)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(v));
+  if constexpr (B == 3)
+    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(v));
+  return r;
+}
+
+// The bf16 pair (lo, hi) made of the top halves of two floats.
+__device__ __forceinline__ unsigned bf16_pair(float lo, float hi) {
+  return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+}
+
+// Eight exact bf16 levels (q - 8) / 16 of one word, in k order.
+__device__ __forceinline__ u4_t levels8(unsigned w) {
+  const unsigned e = w ^ 0x88888888u;  // even k in bits 0-3 of each byte
+  const unsigned o = e >> 4;           // odd k
+  return u4_t{bf16_pair(nibble_f32<0>(e), nibble_f32<0>(o)), bf16_pair(nibble_f32<1>(e), nibble_f32<1>(o)),
+              bf16_pair(nibble_f32<2>(e), nibble_f32<2>(o)), bf16_pair(nibble_f32<3>(e), nibble_f32<3>(o))};
+}
+
 template <typename V>
 __device__ __forceinline__ unsigned as_u32(V h) {
   static_assert(sizeof(V) == 4, "packed pair");
@@ -126,7 +183,7 @@ __device__ __forceinline__ unsigned and_or(unsigned w, unsigned m, unsigned c) {
 }
 
 // Eight exact fp16 levels (q - 8) of one word, slot order 0,4,1,5,2,6,3,7.
-__device__ __forceinline__ u4_t levels8(unsigned w) {
+__device__ __forceinline__ u4_t levels8_f16(unsigned w) {
   const unsigned w8 = w >> 8;
   const h2_t lo_bias = {(_Float16)-1032.0f, (_Float16)-1032.0f};
   const h2_t hi_bias = {(_Float16)-72.0f, (_Float16)-72.0f};
@@ -135,15 +192,6 @@ __device__ __forceinline__ u4_t levels8(unsigned w) {
   const h2_t c = __builtin_bit_cast(h2_t, and_or(w8, 0x000F000Fu, 0x64006400u)) + lo_bias;
   const h2_t d = __builtin_bit_cast(h2_t, and_or(w8, 0x00F000F0u, 0x54005400u)) + hi_bias;
   return u4_t{as_u32(a), as_u32(b), as_u32(c), as_u32(d)};
-}
-
-// Largest bf16 magnitude (bit pattern) among the eight values of v.
-__device__ __forceinline__ unsigned absmax8(u4_t v) {
-  us2_t m = __builtin_bit_cast(us2_t, v.x & 0x7FFF7FFFu);
-  m = __builtin_elementwise_max(m, __builtin_bit_cast(us2_t, v.y & 0x7FFF7FFFu));
-  m = __builtin_elementwise_max(m, __builtin_bit_cast(us2_t, v.z & 0x7FFF7FFFu));
-  m = __builtin_elementwise_max(m, __builtin_bit_cast(us2_t, v.w & 0x7FFF7FFFu));
-  return max((unsigned)m.x, (unsigned)m.y);
 }
 
 // One DPP lane move (row-local control; every lane of every row written).
@@ -167,36 +215,9 @@ __device__ __forceinline__ float sum32(float v) {
   return v + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, v), 0x401F));
 }
 
-__device__ __forceinline__ unsigned wave_max(unsigned m) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) m = max(m, (unsigned)__shfl_xor((int)m, off));
-  return m;
-}
-
-// Power-of-two exponent E that maps the largest |x| (bf16 magnitude bits)
-// into [2^14, 2^15): every bf16 within 2^-28 of the maximum is then an exact
-// fp16 normal.  0 for an all-zero or non-finite slice.
-__device__ __forceinline__ int slice_exponent(unsigned mag) {
-  const int e = (int)(mag >> 7);
-  if (mag == 0 || e == 255) return 0;
-  const int unbiased = (e == 0) ? -127 : e - 127;
-  return 14 - unbiased;
-}
-
-// Eight bf16 (natural order) -> eight fp16 scaled by 2^E in slot order.
-__device__ __forceinline__ u4_t convert8(u4_t v, int E) {
-  const float x0 = ldexpf(__uint_as_float(v.x << 16), E), x1 = ldexpf(__uint_as_float(v.x & 0xFFFF0000u), E);
-  const float x2 = ldexpf(__uint_as_float(v.y << 16), E), x3 = ldexpf(__uint_as_float(v.y & 0xFFFF0000u), E);
-  const float x4 = ldexpf(__uint_as_float(v.z << 16), E), x5 = ldexpf(__uint_as_float(v.z & 0xFFFF0000u), E);
-  const float x6 = ldexpf(__uint_as_float(v.w << 16), E), x7 = ldexpf(__uint_as_float(v.w & 0xFFFF0000u), E);
-  return u4_t{as_u32(__builtin_amdgcn_cvt_pkrtz(x0, x4)), as_u32(__builtin_amdgcn_cvt_pkrtz(x1, x5)),
-              as_u32(__builtin_amdgcn_cvt_pkrtz(x2, x6)), as_u32(__builtin_amdgcn_cvt_pkrtz(x3, x7))};
-}
-
-// v_dot2_f32_f16 on two words of packed fp16 pairs: c + a.lo*b.lo + a.hi*b.hi.
+// v_dot2_f32_bf16 on two words of packed bf16 pairs: c + a.lo*b.lo + a.hi*b.hi.
 __device__ __forceinline__ float dot2(unsigned a, unsigned b, float c) {
-  typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
-  return __builtin_amdgcn_fdot2(__builtin_bit_cast(fp16x2_t, a), __builtin_bit_cast(fp16x2_t, b), c, false);
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(b2_t, a), __builtin_bit_cast(b2_t, b), c, false);
 }
 
 __device__ __forceinline__ void lds_fence() {
@@ -256,7 +277,7 @@ __device__ __forceinline__ void workgroup_argmax(const GemvArgs& a, const float*
 // ---------------------------------------------------------- staging ----
 //
 // A staged slice holds token row t at xs + t * xs_stride as a run of 16-byte
-// chunks (eight fp16 in slot order, 16 chunks per 128-column group).  Chunk c
+// chunks (eight bf16 in k order, 16 chunks per 128-column group).  Chunk c
 // of row t sits at position c ^ g(t) of the row, where g keeps bits 0-1 of t
 // and swaps bits 2 and 3.  A lane (row r, quarter kq) of the matrix-core
 // loop reads chunk 4 kq + j of its row; with g, the 32 lanes of quarters
@@ -268,49 +289,44 @@ __device__ __forceinline__ void workgroup_argmax(const GemvArgs& a, const float*
 
 __device__ __forceinline__ int swz(int t, int c) { return c ^ ((t & 3) | ((t & 4) << 1) | ((t & 8) >> 1)); }
 
-// Stages x[t][gs*128 .. ge*128) of all TT token rows into this wave's LDS
-// area as scaled fp16 in slot order; E[t] receives each row's exponent.
+// Stages x[t][gs*128 .. ge*128) of the TT token rows, bf16 as they are, by
+// direct global-to-LDS copies (global_load_lds_dwordx4: no registers, no
+// conversion).  Wave `wave` of `nwaves` fills 64 consecutive chunk positions
+// of one staged row per copy: position p of row t takes chunk swz(t, p) (the
+// swizzle is its own inverse).  A staged row holds a multiple of 64 chunk
+// positions; positions past the slice (the load ring's padding up to whole
+// cycles of eight groups) are written as zeros, which keeps the padded
+// slots' products zero (their scale is zero too).  Returns once this
+// thread's copies have landed (vmcnt 0, so also every load issued before);
+// the caller then makes them visible to the other waves that read them.
 template <int TT>
-__device__ __forceinline__ void stage_wave(const GemvArgs& a, _Float16* xs, int gs, int ge, int lane, int (&E)[TT]) {
-  const int n8 = (ge - gs) * (kGroup / 8);
-#pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)t * a.K + (int64_t)gs * kGroup);
-    unsigned m = 0;
-    for (int b = lane; b < n8; b += 64) m = max(m, absmax8(ld_global(src + b)));
-    E[t] = slice_exponent(wave_max(m));
-    u4_t* dst = reinterpret_cast<u4_t*>(xs + t * a.xs_stride);
-    for (int b = lane; b < n8; b += 64) dst[swz(t, b)] = convert8(ld_global(src + b), E[t]);
+__device__ __forceinline__ void stage_x(const GemvArgs& a, __bf16* xs, int gs, int ge, int wave, int nwaves) {
+  const int lane = threadIdx.x & 63;
+  const int n = (ge - gs) * (kGroup / 8);  // chunks of the slice per token row
+  const int dst_row = a.xs_stride / 8;     // chunk positions per staged row: a multiple of 64
+  const int total = TT * dst_row;
+  const uint16_t* src = a.x + (int64_t)gs * kGroup;
+  unsigned char* lds = reinterpret_cast<unsigned char*>(xs);
+  for (int base = wave * 64; base < total; base += nwaves * 64) {
+    const int t = base / dst_row;
+    const int c = swz(t, base - t * dst_row + lane);
+    if (c < n)
+      __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(src + (int64_t)t * a.K + c * 8),
+                                       (__attribute__((address_space(3))) void*)(lds + (int64_t)base * 16), 16, 0, 0);
+    else
+      *reinterpret_cast<u4_t*>(lds + (int64_t)(base + lane) * 16) = u4_t{0u, 0u, 0u, 0u};
   }
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 }
 
-// Zeroes groups [n, next multiple of 8) of every staged row: the load ring
-// runs whole cycles of eight groups, and its padded slots read these (their
-// scale is zero, so zero activations keep their products finite and zero).
-template <int TT>
-__device__ __forceinline__ void zero_pad(const GemvArgs& a, _Float16* xs, int n, int tid, int nthreads) {
-  const int b0 = n * (kGroup / 8), b1 = ((n + kRing - 1) / kRing) * kRing * (kGroup / 8);
-  const int per_row = b1 - b0;
-  if (per_row == 0) return;
-  u4_t* dst = reinterpret_cast<u4_t*>(xs);
-  const int dst_row = a.xs_stride / 8;
-  for (int i = tid; i < TT * per_row; i += nthreads) {
-    const int t = i / per_row, b = b0 + i % per_row;
-    dst[t * dst_row + swz(t, b)] = u4_t{0u, 0u, 0u, 0u};
-  }
-}
-
-// Power of two of the one-pass staging: x * 2^kDirectE is an exact fp16 for
-// every bf16 magnitude in [2^-21, 4080].  Scaling by a power of two changes
-// no rounding of the products or sums (it is undone exactly at the end), so
-// it only moves the window of magnitudes that need no per-row scale: with
-// N(0,1) activations, 2^-17 (unscaled) is undershot by some value in a
-// quarter of the 8 x 5120 blocks, 2^-21 in about 1.5%.
-constexpr int kDirectE = 4;
+// ------------------------------------- fp16 staging (up to kF16MaxT rows) ----
+//
+// The same staged layout with fp16 values times 2^kDirectE, each chunk's
+// eight values in the fp16 levels' slot order 0,4,1,5,2,6,3,7.
 
 // Eight bf16 (natural order) -> eight fp16 in slot order, scaled by
 // 2^kDirectE; exact for every value that passes range8 / range_ok.
-__device__ __forceinline__ u4_t convert8_exact(u4_t v) {
+__device__ __forceinline__ u4_t convert8_f16(u4_t v) {
   constexpr float k = (float)(1 << kDirectE);
   const float x0 = __uint_as_float(v.x << 16) * k, x1 = __uint_as_float(v.x & 0xFFFF0000u) * k;
   const float x2 = __uint_as_float(v.y << 16) * k, x3 = __uint_as_float(v.y & 0xFFFF0000u) * k;
@@ -343,17 +359,31 @@ __device__ __forceinline__ bool range_ok(us2_t mx, us2_t mn) {
   return max((unsigned)mx.x, (unsigned)mx.y) <= 0x457Fu && min((unsigned)mn.x, (unsigned)mn.y) >= 0x34FFu;
 }
 
-// One-pass staging of x[t][gs*128 .. ge*128) by threads tid = 0..nthreads-1:
-// four 16-byte chunks per thread in flight at a time, converted to fp16
-// with the fixed scale 2^kDirectE.  Returns true when some value of this
-// thread's chunks is not exact that way (the caller then stages again with a power-of-two
-// scale per token row; both give the same products, scaled by 2^E).  A chunk
-// whose position is in [hold_from, hold_from + 4) is not stored but returned
-// in held / held_at (a thread meets at most one: they are four of one
-// group's 16 chunks and nthreads >= 64).
+// Zeroes groups [n, next multiple of 8) of every staged row: the load ring
+// runs whole cycles of eight groups, and its padded slots read these.
 template <int TT>
-__device__ __forceinline__ bool stage_direct(const GemvArgs& a, _Float16* xs, int gs, int ge, int tid, int nthreads,
-                                             int hold_from, u4_t& held, int& held_at) {
+__device__ __forceinline__ void zero_pad(const GemvArgs& a, unsigned char* xs, int n, int tid, int nthreads) {
+  const int b0 = n * (kGroup / 8), b1 = ((n + kRing - 1) / kRing) * kRing * (kGroup / 8);
+  const int per_row = b1 - b0;
+  if (per_row == 0) return;
+  u4_t* dst = reinterpret_cast<u4_t*>(xs);
+  const int dst_row = a.xs_stride / 8;
+  for (int i = tid; i < TT * per_row; i += nthreads) {
+    const int t = i / per_row, b = b0 + i % per_row;
+    dst[t * dst_row + swz(t, b)] = u4_t{0u, 0u, 0u, 0u};
+  }
+}
+
+// fp16 staging of x[t][gs*128 .. ge*128) by threads tid = 0..nthreads-1:
+// four 16-byte chunks per thread in flight at a time.  Returns true when
+// some value of this thread's chunks is outside the exact window (the
+// caller then stages bf16 instead).  A chunk whose position is in
+// [hold_from, hold_from + 4) is not stored but returned in held / held_at
+// (a thread meets at most one: they are four of one group's 16 chunks and
+// nthreads >= 64).
+template <int TT>
+__device__ __forceinline__ bool stage_direct(const GemvArgs& a, unsigned char* xs, int gs, int ge, int tid,
+                                             int nthreads, int hold_from, u4_t& held, int& held_at) {
   constexpr int kBatch = 4;
   const int n8 = (ge - gs) * (kGroup / 8);  // chunks per token row
   const int total = TT * n8;
@@ -383,7 +413,7 @@ __device__ __forceinline__ bool stage_direct(const GemvArgs& a, _Float16* xs, in
     for (int i = 0; i < kBatch; ++i) {
       if (d[i] >= 0) {
         range8(v[i], mx, mn);
-        const u4_t c = convert8_exact(v[i]);
+        const u4_t c = convert8_f16(v[i]);
         if (d[i] >= hold_from) {
           held = c;
           held_at = d[i];
@@ -396,54 +426,16 @@ __device__ __forceinline__ bool stage_direct(const GemvArgs& a, _Float16* xs, in
   return !range_ok(mx, mn);
 }
 
-// ----------------------------------------------------------------- dot ----
-
-// Workgroup-cooperative staging of x[t][gs*128 .. ge*128) with a power-of-two
-// scale per token row (E[t]).  maxbuf (waves * TT words) may lie inside the
-// staged block: it is read into registers before any chunk is stored.  Ends
-// with a barrier.
+// fp16 staging of a slice for the whole workgroup.  Returns true (uniform)
+// when every value of the slice was exact in fp16: the slice and its ring
+// padding are then staged.  Otherwise nothing usable is staged and the
+// caller stages bf16.  The workgroup-wide decision needs one word per wave;
+// the words borrow the last four chunks of the last row, whose values the
+// threads that own them hold back until the decision is made.  Ends with a
+// barrier after the decision, before any padding store; the caller's barrier
+// publishes the staged values.
 template <int TT>
-__device__ __forceinline__ void stage_block(const GemvArgs& a, _Float16* xs, unsigned* maxbuf, int gs, int ge,
-                                            int (&E)[TT]) {
-  const int n8 = (ge - gs) * (kGroup / 8);
-  const int lane = threadIdx.x & 63, nw = blockDim.x >> 6;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-#pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)t * a.K + (int64_t)gs * kGroup);
-    unsigned m = 0;
-    for (int b = threadIdx.x; b < n8; b += blockDim.x) m = max(m, absmax8(ld_global(src + b)));
-    m = wave_max(m);
-    if (lane == 0) maxbuf[wave * TT + t] = m;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    unsigned m = 0;
-    for (int w = 0; w < nw; ++w) m = max(m, maxbuf[w * TT + t]);
-    E[t] = slice_exponent(m);
-  }
-  __syncthreads();  // every wave has read the maxima before the block is written
-#pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)t * a.K + (int64_t)gs * kGroup);
-    u4_t* dst = reinterpret_cast<u4_t*>(xs + t * a.xs_stride);
-    for (int b = threadIdx.x; b < n8; b += blockDim.x) dst[swz(t, b)] = convert8(ld_global(src + b), E[t]);
-  }
-  __syncthreads();
-}
-
-// Stages x[t][gs*128 .. ge*128) of all TT token rows once for the whole
-// workgroup, plus the zeroed ring padding (zero_pad).  One pass with the
-// fixed 2^kDirectE when every value of the slice converts exactly, else the
-// per-row scaled
-// two-pass staging.  The workgroup-wide decision needs one word per wave; the
-// words are borrowed from the last four chunks of the last row, whose values
-// the threads that own them hold back until the decision is made, so the
-// staged block needs no LDS beyond its own T * xs_stride halves.  Ends with
-// a barrier.
-template <int TT>
-__device__ __forceinline__ void stage_shared(const GemvArgs& a, _Float16* xs, int gs, int ge, int (&E)[TT]) {
+__device__ __forceinline__ bool stage_f16_shared(const GemvArgs& a, unsigned char* xs, int gs, int ge) {
   const int n8 = (ge - gs) * (kGroup / 8);
   const int flag_at = (TT - 1) * (a.xs_stride / 8) + n8 - 4;  // chunk position of the flag words
   u4_t held = {0u, 0u, 0u, 0u};
@@ -457,49 +449,14 @@ __device__ __forceinline__ void stage_shared(const GemvArgs& a, _Float16* xs, in
   __syncthreads();
   unsigned any = 0;
   for (int i = 0; i < (int)(blockDim.x >> 6); ++i) any |= flags[i];
+  // the same in every lane; said so, the caller's choice of loop is a scalar
+  // branch (as a divergent one, both loops' registers would be live at once)
+  any = __builtin_amdgcn_readfirstlane(any);
   __syncthreads();  // every wave has read the flags before they are overwritten
-  if (any == 0) {
-    if (held_at >= 0) dst[held_at] = held;
-#pragma unroll
-    for (int t = 0; t < TT; ++t) E[t] = kDirectE;
-  } else {
-    stage_block<TT>(a, xs, reinterpret_cast<unsigned*>(xs), gs, ge, E);
-  }
+  if (any != 0) return false;
+  if (held_at >= 0) dst[held_at] = held;
   zero_pad<TT>(a, xs, ge - gs, threadIdx.x, blockDim.x);
-  __syncthreads();
-}
-
-// Staging from a grouped launch's workspace: the activations were converted
-// once for the whole launch (w4a16_stage_x_kernel): row t of the problem is
-// K/8 16-byte chunks of fp16 in slot order, scaled by 2^E[t].  The chunks of
-// slice [gs, ge) go straight from global memory into LDS
-// (global_load_lds_dwordx4: no registers, no conversion, no decision to
-// share), each wave filling 64 consecutive chunk positions of one staged
-// row: position p of row t takes chunk swz(t, p) (the swizzle is its own
-// inverse), and the ring padding takes the workspace's zero chunk.  Ends
-// with a barrier.
-template <int TT>
-__device__ __forceinline__ void stage_dma(const GemvArgs& a, const unsigned char* ws, _Float16* xs, int gs, int ge,
-                                          int (&E)[TT]) {
-  const int lane = threadIdx.x & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int n8 = a.K / 8, n = (ge - gs) * (kGroup / 8);
-  const int dst_row = a.xs_stride / 8, total = TT * dst_row;  // dst_row: a multiple of 128 chunks
-  const u4_t* src = reinterpret_cast<const u4_t*>(ws + a.x16_off) + gs * (kGroup / 8);
-  const u4_t* zero = reinterpret_cast<const u4_t*>(ws);
-  unsigned char* lds = reinterpret_cast<unsigned char*>(xs);
-  for (int base = wave * 64; base < total; base += (int)blockDim.x) {
-    const int t = base / dst_row;
-    const int c = swz(t, base - t * dst_row + lane);
-    const u4_t* from = c < n ? src + t * n8 + c : zero;
-    __builtin_amdgcn_global_load_lds(reinterpret_cast<const void*>(from),
-                                     (__attribute__((address_space(3))) void*)(lds + (int64_t)base * 16), 16, 0, 0);
-  }
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  __syncthreads();
-  const int* ep = reinterpret_cast<const int*>(ws + a.e_off);
-#pragma unroll
-  for (int t = 0; t < TT; ++t) E[t] = __builtin_amdgcn_readfirstlane(ep[t]);
+  return true;
 }
 
 // RW rows per wave, L = 64/RW lanes per row; a lane takes the row's 16-byte
@@ -522,13 +479,11 @@ __global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
   if (bad) w = 0;
   const u4_t* cp = reinterpret_cast<const u4_t*>(a.packed + w * (int64_t)(a.K >> 1));
   const uint16_t* sp = a.scales + w * a.G;
-  _Float16* xs = reinterpret_cast<_Float16*>(smem);
-  unsigned* maxbuf = reinterpret_cast<unsigned*>(smem + a.fin_offset);
+  __bf16* xs = reinterpret_cast<__bf16*>(smem);
 
-  float acc[TT], accs[TT];
+  float acc[TT];
 #pragma unroll
-  for (int t = 0; t < TT; ++t) acc[t] = accs[t] = 0.0f;
-  int E[TT];
+  for (int t = 0; t < TT; ++t) acc[t] = 0.0f;
 
   for (int gs = 0; gs < a.G; gs += a.sk) {
     const int ge = min(a.G, gs + a.sk);
@@ -544,7 +499,8 @@ __global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
       }
     }
     if (gs > 0) __syncthreads();  // every wave is done with the previous slice
-    stage_block<TT>(a, xs, maxbuf, gs, ge, E);
+    stage_x<TT>(a, xs, gs, ge, wave, nw);
+    __syncthreads();
 #pragma unroll
     for (int i = 0; i < CPL; ++i) {
       const int c = li + i * L;
@@ -563,21 +519,17 @@ __global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
             p = dot2(lv[j].z, xw.z, p);
             p = dot2(lv[j].w, xw.w, p);
           }
-          accs[t] = fmaf(p, sc, accs[t]);
+          acc[t] = fmaf(p, sc, acc[t]);
         }
       }
     }
-#pragma unroll
-    for (int t = 0; t < TT; ++t) {
-      acc[t] += ldexpf(accs[t], -E[t]);
-      accs[t] = 0.0f;
-    }
   }
 
-  // Sum across the L = 32 lanes of a row (fixed order).
+  // Sum across the L = 32 lanes of a row (fixed order), with the levels'
+  // factor 1/16 taken back first (a power of two: no rounding changes).
   static_assert(L == 32, "the lane reduction covers 32 lanes per row");
 #pragma unroll
-  for (int t = 0; t < TT; ++t) acc[t] = sum32(acc[t]);
+  for (int t = 0; t < TT; ++t) acc[t] = sum32(acc[t] * kLevelScale);
 
   float* fin = reinterpret_cast<float*>(smem);  // reused after the last slice
   __syncthreads();
@@ -639,6 +591,169 @@ __device__ __forceinline__ int scale_off(const GemvArgs& a, int g) {
 }
 
 
+// One group of one 16-row tile for this lane: four MFMAs over its four
+// words of codes and its four staged activation chunks (xb[j] + group gl);
+// H selects the level form (fp16 against the fp16 staging, else bf16).
+template <bool H>
+__device__ __forceinline__ f4_t group_mfma(const unsigned char* const (&xb)[4], int gl, u4_t w) {
+  f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
+  const unsigned ww[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    if constexpr (H)
+      d = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const h8_t*>(xb[j] + gl * (kGroup * 2)),
+                                                 __builtin_bit_cast(h8_t, levels8_f16(ww[j])), d, 0, 0, 0);
+    else
+      d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(*reinterpret_cast<const b8_t*>(xb[j] + gl * (kGroup * 2)),
+                                                  __builtin_bit_cast(b8_t, levels8(ww[j])), d, 0, 0, 0);
+    // bf16: one word's levels at a time (the MFMAs chain on d anyway, and
+    // forming all four words' levels first would hold 32 more registers);
+    // the fp16 levels are cheap enough to interleave freely
+    if constexpr (!H) __builtin_amdgcn_sched_barrier(0);
+  }
+  return d;
+}
+
+// The factor that turns a tile's sum of the H form back into the unscaled
+// result (a power of two: the same roundings as unscaled arithmetic).
+template <bool H>
+constexpr float fold_scale() {
+  return H ? kDirectScale : kLevelScale;
+}
+
+// This lane's four activation chunks of group 0 of a staged slice (row trow,
+// chunks 4 kq .. 4 kq + 3 of the group, swizzled), as byte pointers.
+__device__ __forceinline__ void lane_chunks(const GemvArgs& a, const unsigned char* xs, int trow, int kq,
+                                            const unsigned char* (&xb)[4]) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) xb[j] = xs + (trow * a.xs_stride + swz(trow, kq * 4 + j) * 8) * 2;
+}
+
+// Stages the slice [sb, se) of the activations for a workgroup (SHARED) or
+// for this wave alone, and returns which level form runs on it: the fp16
+// form when the kernel tries it (up to kF16MaxT rows) and every value is
+// exact in it, else bf16.  Returns after the staged values are visible to
+// every wave that reads them and every load issued before has landed.
+template <int TT, bool SHARED>
+__device__ __forceinline__ bool stage_slice(const GemvArgs& a, unsigned char* xs, int sb, int se) {
+  bool h = false;
+  if constexpr (SHARED) {
+    if constexpr (TT <= kF16MaxT) h = stage_f16_shared<TT>(a, xs, sb, se);
+    if (!h) stage_x<TT>(a, reinterpret_cast<__bf16*>(xs), sb, se, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
+                        blockDim.x >> 6);
+    __syncthreads();
+  } else {
+    const int lane = threadIdx.x & 63;
+    lds_fence();
+    if constexpr (TT <= kF16MaxT) {
+      u4_t held;
+      int held_at = -1;
+      h = __ballot(stage_direct<TT>(a, xs, sb, se, lane, 64, 0x7fffffff, held, held_at)) == 0;
+      if (h)
+        zero_pad<TT>(a, xs, se - sb, lane, 64);
+      else
+        lds_fence();
+    }
+    if (!h) stage_x<TT>(a, reinterpret_cast<__bf16*>(xs), sb, se, 0, 1);
+    lds_fence();
+  }
+  // the staging waited for its loads, issued after the weight loads in
+  // flight; saying so lets the loop wait for exactly one group at a time
+  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  return h;
+}
+
+// The tiles of one staged slice (n groups from sb, np = n rounded up to
+// whole ring cycles): the wave streams tile 0's groups, then tile 1's, ...
+// with the load ring running across tile boundaries; the ring (q, sq, sv)
+// holds tile 0's first groups on entry.
+template <int TT, int RT, bool VS, int LAY, bool H>
+__device__ __forceinline__ void slice_tiles(const GemvArgs& a, const u4_t* const (&cp)[RT],
+                                            const uint16_t* const (&sp)[RT], const unsigned char* const (&xb)[4],
+                                            int sb, int n, int np, u4_t (&q)[kRing], unsigned short (&sq)[kRing],
+                                            u4_t& sv, float (&acc)[RT][4]) {
+  constexpr int PD = kRing;
+#pragma unroll
+  for (int tl = 0; tl < RT; ++tl) {
+    // next tile of the ring (the last tile re-reads its own last group)
+    const u4_t* cpn = cp[tl + 1 < RT ? tl + 1 : tl];
+    const uint16_t* spn = sp[tl + 1 < RT ? tl + 1 : tl];
+    const bool has_next = tl + 1 < RT;
+    float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    for (int fi = 0; fi < np; fi += PD) {
+      const bool last = fi + PD >= np;  // uniform: this cycle prefetches the next tile
+      u4_t svn;
+      if constexpr (VS) {
+        const uint16_t* base = (last && has_next) ? spn : sp[tl];
+        const int gv = last ? (has_next ? sb : sb + fi) : sb + fi + PD;
+        svn = ld_global(reinterpret_cast<const u4_t*>(base) + scale_off<LAY>(a, gv));
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int s = 0; s < PD; ++s) {
+        const int gl = fi + s;  // groups past n read the zeroed padding
+        float sc;
+        if constexpr (VS)
+          sc = scale_of(sv, s);
+        else
+          sc = bf16_to_f32(sq[s]);
+        sc = (gl < n) ? sc : 0.0f;
+        const f4_t d = group_mfma<H>(xb, gl, q[s]);
+#pragma unroll
+        for (int r = 0; r < 4; ++r) accs[r] = fmaf(d[r], sc, accs[r]);
+        // reload this slot with the group PD positions ahead
+        const int tgt = gl + PD;
+        const bool nxt = tgt >= np;
+        const u4_t* cpl = (nxt && has_next) ? cpn : cp[tl];
+        const int gg = sb + (nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1));
+        if constexpr (!VS) sq[s] = ld_global(((nxt && has_next) ? spn : sp[tl]) + gg);
+        q[s] = load_codes<LAY>(cpl + code_off<LAY>(a, gg));
+        // keep this slot's reload here: sunk to the end of the loop, the
+        // reloads would make every iteration wait for the whole ring
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (VS) sv = svn;
+    }
+    // fold this tile's slice sum, undoing the level form's power of two
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[tl][r] += accs[r] * fold_scale<H>();
+  }
+}
+
+// The exact fallback of the kernels that try the fp16 form: groups
+// [g0, g0 + n) of one tile, one group at a time with bf16 levels against
+// the bf16 staging (xb: this lane's chunks of the staged slice's group 0),
+// added into accs.  A short loop with no load ring: it holds few registers,
+// so it leaves the fast loop's register allocation alone, and it runs only
+// for a slice holding an activation outside the fp16 window.
+template <int LAY>
+__device__ __forceinline__ void exact_groups(const GemvArgs& a, const u4_t* cp, const uint16_t* sp,
+                                             const unsigned char* const (&xb)[4], int g0, int n, float (&accs)[4]) {
+  for (int g = 0; g < n; ++g) {
+    const int gg = g0 + g;
+    const u4_t w = load_codes<LAY>(cp + code_off<LAY>(a, gg));
+    // scale of group gg: in its 8-scale block (tiled), or the row's gg-th
+    const int si = (LAY == kLayTiled || a.tiled) ? scale_off<LAY>(a, gg & ~7) * 8 + (gg & 7) : gg;
+    const float sc = bf16_to_f32(ld_global(sp + si));
+    const f4_t d = group_mfma<false>(xb, g, w);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) accs[r] = fmaf(d[r], sc, accs[r]);
+  }
+}
+
+template <int TT, int RT, int LAY>
+__device__ __forceinline__ void exact_slice(const GemvArgs& a, const u4_t* const (&cp)[RT],
+                                            const uint16_t* const (&sp)[RT], const unsigned char* const (&xb)[4],
+                                            int sb, int n, float (&acc)[RT][4]) {
+#pragma unroll
+  for (int tl = 0; tl < RT; ++tl) {
+    float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    exact_groups<LAY>(a, cp[tl], sp[tl], xb, sb, n, accs);
+#pragma unroll
+    for (int r = 0; r < 4; ++r) acc[tl][r] += accs[r] * kLevelScale;
+  }
+}
+
 // The K loop of one wave: groups [g_begin, g_end) of RT 16-row tiles.  The
 // range is cut into slices that fit the staged activations; within a slice
 // the wave streams tile 0's groups, then tile 1's, ... with kRing groups of
@@ -646,21 +761,16 @@ __device__ __forceinline__ int scale_off(const GemvArgs& a, int g) {
 // output row r16 of a tile and quarter kq of each 128-column group: one
 // 16-byte load per group feeds four MFMAs (tokens as the A operand, padded to
 // 16 rows; weights as the B operand), whose sum gets the group's scale.
-// SHARED: the slice is staged once for the whole workgroup (stage_shared);
-// otherwise each wave stages its own range (no barrier).  Staging is one pass
-// with the fixed 2^kDirectE when every activation converts to fp16 exactly
-// that way, else the per-row scaled two-pass staging (stage_block /
-// stage_wave).
+// SHARED: the slice is staged once for the whole workgroup; otherwise each
+// wave stages its own range (no barrier).
 // VS: scales are read eight groups (16 bytes) per load (needs G % 8 == 0,
 // 16-byte aligned scale rows and g_begin % 8 == 0); otherwise one 2-byte
 // load per group.
 template <int TT, int RT, bool VS, bool SHARED, int LAY>
 __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* const (&cp)[RT],
-                                             const uint16_t* const (&sp)[RT], _Float16* xs, int g_begin, int g_end,
-                                             int lane, int trow, int kq, float (&acc)[RT][4],
-                                             const unsigned char* ws = nullptr) {
+                                             const uint16_t* const (&sp)[RT], unsigned char* xs, int g_begin,
+                                             int g_end, int trow, int kq, float (&acc)[RT][4]) {
   constexpr int PD = kRing;
-  int E[TT];
   u4_t q[PD];
   unsigned short sq[PD];
   u4_t sv;
@@ -678,92 +788,19 @@ __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* cons
       q[s] = load_codes<LAY>(cp[0] + code_off<LAY>(a, g));
       __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
     }
-    if constexpr (SHARED) {
+    if constexpr (SHARED)
       if (sb != g_begin) __syncthreads();  // every wave is done with the previous slice
-      if (ws)
-        stage_dma<TT>(a, ws, xs, sb, se, E);
+    const bool h = stage_slice<TT, SHARED>(a, xs, sb, se);
+    const unsigned char* xb[4];
+    lane_chunks(a, xs, trow, kq, xb);
+    if constexpr (TT <= kF16MaxT) {
+      if (h)
+        slice_tiles<TT, RT, VS, LAY, true>(a, cp, sp, xb, sb, n, np, q, sq, sv, acc);
       else
-        stage_shared<TT>(a, xs, sb, se, E);
+        exact_slice<TT, RT, LAY>(a, cp, sp, xb, sb, n, acc);
     } else {
-      lds_fence();
-      u4_t held;
-      int held_at = -1;
-      const bool bad = stage_direct<TT>(a, xs, sb, se, lane, 64, 0x7fffffff, held, held_at);
-      if (__ballot(bad) != 0) {
-        lds_fence();
-        stage_wave<TT>(a, xs, sb, se, lane, E);
-      } else {
-#pragma unroll
-        for (int t = 0; t < TT; ++t) E[t] = kDirectE;
-      }
-      zero_pad<TT>(a, xs, n, lane, 64);
-      lds_fence();
-    }
-    // Staging waited for its activation loads, issued after the weight loads
-    // in flight; saying so lets the loop wait for exactly one group at a time.
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    // this lane's four 16-byte activation chunks of group 0 (row trow, chunks
-    // 4 kq .. 4 kq + 3 of the group, swizzled)
-    const _Float16* xb[4];
-#pragma unroll
-    for (int j = 0; j < 4; ++j) xb[j] = xs + trow * a.xs_stride + swz(trow, kq * 4 + j) * 8;
-#pragma unroll
-    for (int tl = 0; tl < RT; ++tl) {
-      // next tile of the ring (the last tile re-reads its own last group)
-      const u4_t* cpn = cp[tl + 1 < RT ? tl + 1 : tl];
-      const uint16_t* spn = sp[tl + 1 < RT ? tl + 1 : tl];
-      const bool has_next = tl + 1 < RT;
-      float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-      for (int fi = 0; fi < np; fi += PD) {
-        const bool last = fi + PD >= np;  // uniform: this cycle prefetches the next tile
-        u4_t svn;
-        if constexpr (VS) {
-          const uint16_t* base = (last && has_next) ? spn : sp[tl];
-          const int gv = last ? (has_next ? sb : sb + fi) : sb + fi + PD;
-          svn = ld_global(reinterpret_cast<const u4_t*>(base) + scale_off<LAY>(a, gv));
-          __builtin_amdgcn_sched_barrier(0);
-        }
-#pragma unroll
-        for (int s = 0; s < PD; ++s) {
-          const int gl = fi + s;  // groups past n read the zeroed padding
-          h8_t xa[4];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xb[j] + gl * kGroup);
-          float sc;
-          if constexpr (VS)
-            sc = scale_of(sv, s);
-          else
-            sc = bf16_to_f32(sq[s]);
-          sc = (gl < n) ? sc : 0.0f;
-          f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], __builtin_bit_cast(h8_t, levels8(q[s].x)), d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], __builtin_bit_cast(h8_t, levels8(q[s].y)), d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], __builtin_bit_cast(h8_t, levels8(q[s].z)), d, 0, 0, 0);
-          d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], __builtin_bit_cast(h8_t, levels8(q[s].w)), d, 0, 0, 0);
-#pragma unroll
-          for (int r = 0; r < 4; ++r) accs[r] = fmaf(d[r], sc, accs[r]);
-          // reload this slot with the group PD positions ahead
-          const int tgt = gl + PD;
-          const bool nxt = tgt >= np;
-          const u4_t* cpl = (nxt && has_next) ? cpn : cp[tl];
-          const int gg = sb + (nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1));
-          if constexpr (!VS) sq[s] = ld_global(((nxt && has_next) ? spn : sp[tl]) + gg);
-          q[s] = load_codes<LAY>(cpl + code_off<LAY>(a, gg));
-          // keep this slot's reload here: sunk to the end of the loop, the
-          // reloads would make every iteration wait for the whole ring
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        if constexpr (VS) sv = svn;
-      }
-      // fold this tile's slice sum, undoing the activations' power of two
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int t = kq * 4 + r;
-        int e = E[0];
-#pragma unroll
-        for (int i = 1; i < TT; ++i) e = (t == i) ? E[i] : e;
-        acc[tl][r] += ldexpf(accs[r], -e);
-      }
+      (void)h;
+      slice_tiles<TT, RT, VS, LAY, false>(a, cp, sp, xb, sb, n, np, q, sq, sv, acc);
     }
   }
 }
@@ -806,7 +843,7 @@ __device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, u
   tile_pointers<RT, LAY>(a, row0, r16, kq, cp, sp);
   const int g_begin = wave * a.gpw;
   const int g_end = (wave < a.nw) ? min(a.G, g_begin + a.gpw) : g_begin;  // uniform
-  _Float16* xs = reinterpret_cast<_Float16*>(smem + wave * a.wave_lds);
+  unsigned char* xs = smem + wave * a.wave_lds;
 
   float acc[RT][4];
 #pragma unroll
@@ -815,9 +852,9 @@ __device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, u
     for (int r = 0; r < 4; ++r) acc[tl][r] = 0.0f;
   if (g_end > g_begin) {
     if (LAY == kLayTiled || a.vec_scales)
-      stream_tiles<TT, RT, true, false, LAY>(a, cp, sp, xs, g_begin, g_end, lane, trow, kq, acc);
+      stream_tiles<TT, RT, true, false, LAY>(a, cp, sp, xs, g_begin, g_end, trow, kq, acc);
     else if constexpr (LAY != kLayTiled)
-      stream_tiles<TT, RT, false, false, LAY>(a, cp, sp, xs, g_begin, g_end, lane, trow, kq, acc);
+      stream_tiles<TT, RT, false, false, LAY>(a, cp, sp, xs, g_begin, g_end, trow, kq, acc);
   }
 
   // Split-K partials of this wave -> its own LDS area: red[(tl*TT + t)*16 + row].
@@ -857,11 +894,10 @@ __device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, u
 
 // Shared workgroup: each of its waves owns RT tiles of its own over all of K
 // (rows (wg*waves + wave)*16*RT ..); the waves share one staged copy of the
-// activations per K slice, so the fp16 conversion is paid once per
-// 16 * RT * waves rows.  Every output comes straight from one wave.
+// activations per K slice, so the staging is paid once per 16 * RT * waves
+// rows.  Every output comes straight from one wave.
 template <int TT, int RT, int LAY>
-__device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem,
-                                                 const unsigned char* ws = nullptr) {
+__device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwv = blockDim.x >> 6;
@@ -871,7 +907,7 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
   const u4_t* cp[RT];
   const uint16_t* sp[RT];
   tile_pointers<RT, LAY>(a, row_w, r16, kq, cp, sp);
-  _Float16* xs = reinterpret_cast<_Float16*>(smem);
+  unsigned char* xs = smem;
 
   float acc[RT][4];
 #pragma unroll
@@ -879,9 +915,9 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[tl][r] = 0.0f;
   if (LAY == kLayTiled || a.vec_scales)
-    stream_tiles<TT, RT, true, true, LAY>(a, cp, sp, xs, 0, a.G, lane, trow, kq, acc, ws);
+    stream_tiles<TT, RT, true, true, LAY>(a, cp, sp, xs, 0, a.G, trow, kq, acc);
   else if constexpr (LAY != kLayTiled)
-    stream_tiles<TT, RT, false, true, LAY>(a, cp, sp, xs, 0, a.G, lane, trow, kq, acc, ws);
+    stream_tiles<TT, RT, false, true, LAY>(a, cp, sp, xs, 0, a.G, trow, kq, acc);
 
   float bv[TT];
   int bi[TT];
@@ -984,17 +1020,54 @@ __device__ __forceinline__ void ring_prologue(const GemvArgs& a, const u4_t* cp,
   }
 }
 
+// Tile v done: this lane's outputs (row 16 v + r16, token rows t = 4 kq + r,
+// the tile's sums accs times fold) are stored, and the lane's running argmax
+// candidates bv[r] / bi[r] updated when the launch takes the argmax.
+template <int TT>
+__device__ __forceinline__ void tile_outputs(const GemvArgs& a, int64_t v, int r16, int kq, int w_cur,
+                                             const float (&accs)[4], float fold, float (&bv)[4], int (&bi)[4]) {
+  const int64_t orow = v * 16 + r16;
+  const bool in_range = orow < a.n_out;
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int t = kq * 4 + r;
+    const float val = accs[r] * fold;  // the level form's power of two undone
+    if (t < TT && in_range && a.y) st_out<TT>(a.y + (int64_t)t * a.n_out + orow, w_cur < 0 ? __builtin_nanf("") : val);
+    if (a.partial && t < TT && w_cur >= 0 && !__builtin_isnan(val) && better(val, w_cur, bv[r], bi[r])) {
+      bv[r] = val;
+      bi[r] = w_cur;
+    }
+  }
+}
+
+// The exact fallback of run_tiles (see exact_groups): tiles v, v + step, ...
+// (< v_end), all of K each, one group at a time.
 template <int TT, int LAY>
-__device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t v_end, int step, const _Float16* xs,
-                                          const int (&E)[TT], int r16, int kq, int trow, const u4_t* cp,
+__device__ __forceinline__ void exact_run_tiles(const GemvArgs& a, int64_t v, int64_t v_end, int step,
+                                                const unsigned char* xs, int r16, int kq, int trow, float (&bv)[4],
+                                                int (&bi)[4]) {
+  const unsigned char* xb[4];
+  lane_chunks(a, xs, trow, kq, xb);
+  for (; v < v_end; v += step) {  // uniform
+    const u4_t* cp;
+    const uint16_t* sp;
+    const int w_cur = tile_ptr<LAY>(a, v, r16, kq, cp, sp);
+    float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    exact_groups<LAY>(a, cp, sp, xb, 0, a.G, accs);
+    tile_outputs<TT>(a, v, r16, kq, w_cur, accs, kLevelScale, bv, bi);
+  }
+}
+
+template <int TT, int LAY, bool H>
+__device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t v_end, int step,
+                                          const unsigned char* xs, int r16, int kq, int trow, const u4_t* cp,
                                           const uint16_t* sp, u4_t (&q)[kRing], u4_t& sv, float (&bv)[4],
                                           int (&bi)[4]) {
   constexpr int PD = kRing;
   const int n = a.G;
   const int np = (n + PD - 1) / PD * PD;
-  const _Float16* xb[4];  // this lane's activation chunks of group 0 (see stream_tiles)
-#pragma unroll
-  for (int j = 0; j < 4; ++j) xb[j] = xs + trow * a.xs_stride + swz(trow, kq * 4 + j) * 8;
+  const unsigned char* xb[4];  // this lane's activation chunks of group 0
+  lane_chunks(a, xs, trow, kq, xb);
   int w_cur = (int)weight_row(a, v * 16 + r16);
   while (v < v_end) {  // uniform
     const int64_t vn = v + step;
@@ -1013,15 +1086,8 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
 #pragma unroll
       for (int s = 0; s < PD; ++s) {
         const int gl = fi + s;  // groups past n read the zeroed padding
-        h8_t xa[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) xa[j] = *reinterpret_cast<const h8_t*>(xb[j] + gl * kGroup);
         const float sc = (gl < n) ? scale_of(sv, s) : 0.0f;
-        f4_t d = {0.0f, 0.0f, 0.0f, 0.0f};
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[0], __builtin_bit_cast(h8_t, levels8(q[s].x)), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[1], __builtin_bit_cast(h8_t, levels8(q[s].y)), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[2], __builtin_bit_cast(h8_t, levels8(q[s].z)), d, 0, 0, 0);
-        d = __builtin_amdgcn_mfma_f32_16x16x32_f16(xa[3], __builtin_bit_cast(h8_t, levels8(q[s].w)), d, 0, 0, 0);
+        const f4_t d = group_mfma<H>(xb, gl, q[s]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) accs[r] = fmaf(d[r], sc, accs[r]);
         // reload this slot with the group PD positions ahead (the next
@@ -1035,22 +1101,7 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
       }
       sv = svn;
     }
-    // tile v done: this lane's row for t = 4 kq + r
-    const int64_t orow = v * 16 + r16;
-    const bool in_range = orow < a.n_out;
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      const int t = kq * 4 + r;
-      int e = E[0];
-#pragma unroll
-      for (int i = 1; i < TT; ++i) e = (t == i) ? E[i] : e;
-      const float val = ldexpf(accs[r], -e);
-      if (t < TT && in_range && a.y) st_out<TT>(a.y + (int64_t)t * a.n_out + orow, w_cur < 0 ? __builtin_nanf("") : val);
-      if (a.partial && t < TT && w_cur >= 0 && !__builtin_isnan(val) && better(val, w_cur, bv[r], bi[r])) {
-        bv[r] = val;
-        bi[r] = w_cur;
-      }
-    }
+    tile_outputs<TT>(a, v, r16, kq, w_cur, accs, fold_scale<H>(), bv, bi);
     v = vn;
     cp = cpn;
     sp = spn;
@@ -1063,8 +1114,7 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
 // so the waves stay on adjacent tiles.  All of K is staged once (the planner
 // guarantees it fits).
 template <int TT, int LAY>
-__device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem,
-                                              const unsigned char* ws = nullptr) {
+__device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwv = blockDim.x >> 6;
@@ -1073,7 +1123,7 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
   const int64_t tiles = (a.n_out + 15) / 16;
   const int64_t span = (int64_t)nwv * a.run_tiles;
   const int64_t v0 = wg * span + wave, v_end = min(tiles, (wg + 1) * span);
-  _Float16* xs = reinterpret_cast<_Float16*>(smem);
+  unsigned char* xs = smem;
   const u4_t* cp = nullptr;
   const uint16_t* sp = nullptr;
   u4_t q[kRing];
@@ -1082,12 +1132,7 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
     tile_ptr<LAY>(a, v0, r16, kq, cp, sp);
     ring_prologue<LAY>(a, cp, sp, q, sv);
   }
-  int E[TT];
-  if (ws)
-    stage_dma<TT>(a, ws, xs, 0, a.G, E);
-  else
-    stage_shared<TT>(a, xs, 0, a.G, E);
-  __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+  const bool h = stage_slice<TT, true>(a, xs, 0, a.G);  // also waits for the ring's loads
   float bv[4];
   int bi[4];
 #pragma unroll
@@ -1095,7 +1140,16 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
     bv[r] = __builtin_nanf("");
     bi[r] = -1;
   }
-  if (v0 < v_end) run_tiles<TT, LAY>(a, v0, v_end, nwv, xs, E, r16, kq, trow, cp, sp, q, sv, bv, bi);
+  if (v0 < v_end) {
+    if constexpr (TT <= kF16MaxT) {
+      if (h)
+        run_tiles<TT, LAY, true>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, sp, q, sv, bv, bi);
+      else
+        exact_run_tiles<TT, LAY>(a, v0, v_end, nwv, xs, r16, kq, trow, bv, bi);
+    } else {
+      run_tiles<TT, LAY, false>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, sp, q, sv, bv, bi);
+    }
+  }
   if (a.partial) {
     // per t: best of the lanes, of the waves, then of the workgroup
     int2* fin = reinterpret_cast<int2*>(smem);
@@ -1140,11 +1194,10 @@ __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4))) 
 // Grouped launch of run workgroups: workgroup b runs workgroup b - wg_start of
 // the last problem whose wg_start <= b; a problem planned without a run
 // (its activations do not fit the LDS at once) runs a shared workgroup of one
-// tile per wave instead.  With ws set, the activations come pre-converted
-// from that workspace (stage_dma).
+// tile per wave instead.
 template <int TT, int LAY>
 __global__ void __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu(4)))
-w4a16_run_batch_kernel(const GemvArgs* __restrict__ table, int count, const unsigned char* __restrict__ ws) {
+w4a16_run_batch_kernel(const GemvArgs* __restrict__ table, int count) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int64_t b = blockIdx.x;
   int lo = 0, hi = count - 1;
@@ -1157,16 +1210,15 @@ w4a16_run_batch_kernel(const GemvArgs* __restrict__ table, int count, const unsi
   }
   const GemvArgs a = table[lo];
   if (a.run_tiles > 0)
-    run_workgroup<TT, LAY>(a, b - a.wg_start, smem, ws);
+    run_workgroup<TT, LAY>(a, b - a.wg_start, smem);
   else  // activations too large for one staging: whole-K slices, one tile per wave
-    shared_workgroup<TT, 1, LAY>(a, b - a.wg_start, smem, ws);
+    shared_workgroup<TT, 1, LAY>(a, b - a.wg_start, smem);
 }
 
 template <int TT, int RT, bool SHARED, int LAY>
-__device__ __forceinline__ void tile_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem,
-                                               const unsigned char* ws = nullptr) {
+__device__ __forceinline__ void tile_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
   if constexpr (SHARED)
-    shared_workgroup<TT, RT, LAY>(a, wg, smem, ws);
+    shared_workgroup<TT, RT, LAY>(a, wg, smem);
   else
     split_workgroup<TT, RT, LAY>(a, wg, smem);
 }
@@ -1179,12 +1231,11 @@ __global__ void __launch_bounds__(SHARED && RT == 1 ? 1024 : 512)
 }
 
 // Grouped launch: workgroup b runs tile b - wg_start of the last problem whose
-// wg_start <= b (shared workgroups stage from the workspace ws when it is set).
+// wg_start <= b.
 template <int TT, int RT, bool SHARED, int LAY>
 __global__ void __launch_bounds__(SHARED && RT == 1 ? 1024 : 512)
-    __attribute__((amdgpu_waves_per_eu(SHARED && RT == 1 ? 4 : 1))) w4a16_tile_batch_kernel(const GemvArgs* __restrict__ table,
-                                                                                    int count,
-                                                                                    const unsigned char* __restrict__ ws) {
+    __attribute__((amdgpu_waves_per_eu(SHARED && RT == 1 ? 4 : 1)))
+    w4a16_tile_batch_kernel(const GemvArgs* __restrict__ table, int count) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   const int64_t b = blockIdx.x;
   int lo = 0, hi = count - 1;
@@ -1196,22 +1247,38 @@ __global__ void __launch_bounds__(SHARED && RT == 1 ? 1024 : 512)
       hi = mid - 1;
   }
   const GemvArgs a = table[lo];
-  tile_workgroup<TT, RT, SHARED, LAY>(a, b - a.wg_start, smem, ws);
+  tile_workgroup<TT, RT, SHARED, LAY>(a, b - a.wg_start, smem);
 }
 
 // ------------------------------------------------------------- dispatch ----
 
+// Above 64 KB of dynamic LDS a kernel has to opt in.  Each kernel function
+// opts in once per device for the CU's whole LDS (the attribute is a
+// property of the function on that device, so one call covers every later
+// launch of it there); later launches check one bit.
+template <typename F>
+hipError_t allow_cu_lds(F* fn) {
+  static std::atomic<unsigned long long> done{0};  // bit d: set on device d
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return hipErrorInvalidDevice;
+  const unsigned long long bit = dev < 64 ? 1ull << dev : 0ull;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  const hipError_t e =
+      hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, kCuLds);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_acq_rel);
+  return e;
+}
+
 template <int TT, int RT, bool SHARED, int LAY>
 hipError_t launch_tiles(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
   const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
-  if (p.lds > kLdsCap) {  // above 64 KB of dynamic LDS the kernel has to opt in
-    const void* fn = table ? reinterpret_cast<const void*>(&w4a16_tile_batch_kernel<TT, RT, SHARED, LAY>)
-                           : reinterpret_cast<const void*>(&w4a16_tile_kernel<TT, RT, SHARED, LAY>);
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds);
+  if (p.lds > kLdsCap) {
+    const hipError_t e = table ? allow_cu_lds(&w4a16_tile_batch_kernel<TT, RT, SHARED, LAY>)
+                               : allow_cu_lds(&w4a16_tile_kernel<TT, RT, SHARED, LAY>);
     if (e != hipSuccess) return e;
   }
   if (table)
-    hipLaunchKernelGGL((w4a16_tile_batch_kernel<TT, RT, SHARED, LAY>), grid, block, p.lds, s, table, count, p.ws);
+    hipLaunchKernelGGL((w4a16_tile_batch_kernel<TT, RT, SHARED, LAY>), grid, block, p.lds, s, table, count);
   else
     hipLaunchKernelGGL((w4a16_tile_kernel<TT, RT, SHARED, LAY>), grid, block, p.lds, s, a);
   return hipGetLastError();
@@ -1236,14 +1303,13 @@ hipError_t launch_rt(const GemvArgs& a, const GemvArgs* table, int count, const 
 template <int TT, int LAY>
 hipError_t launch_run(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
   const dim3 grid((unsigned)p.grid), block((unsigned)p.threads);
-  if (p.lds > kLdsCap) {  // above 64 KB of dynamic LDS the kernel has to opt in
-    const void* fn = table ? reinterpret_cast<const void*>(&w4a16_run_batch_kernel<TT, LAY>)
-                           : reinterpret_cast<const void*>(&w4a16_run_kernel<TT, LAY>);
-    const hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, p.lds);
+  if (p.lds > kLdsCap) {
+    const hipError_t e =
+        table ? allow_cu_lds(&w4a16_run_batch_kernel<TT, LAY>) : allow_cu_lds(&w4a16_run_kernel<TT, LAY>);
     if (e != hipSuccess) return e;
   }
   if (table)
-    hipLaunchKernelGGL((w4a16_run_batch_kernel<TT, LAY>), grid, block, p.lds, s, table, count, p.ws);
+    hipLaunchKernelGGL((w4a16_run_batch_kernel<TT, LAY>), grid, block, p.lds, s, table, count);
   else
     hipLaunchKernelGGL((w4a16_run_kernel<TT, LAY>), grid, block, p.lds, s, a);
   return hipGetLastError();

@@ -25,17 +25,17 @@ struct GemvArgs {
   int32_t nw;              // waves that hold K ranges
   int32_t gpw;             // groups per wave (split-K share)
   int32_t sk;              // groups per staged activation slice
-  int32_t xs_stride;       // halves per staged token row
+  int32_t xs_stride;       // bf16 values per staged token row (a multiple of 512)
   int32_t wave_lds;        // bytes of LDS per wave
-  int32_t fin_offset;      // byte offset of the final-value area
+  int32_t fin_offset;      // unused (0)
   int32_t vec_scales;      // 1: eight scales per 16-byte load (tiled layout, or row-major rows
                            //    16-byte aligned with G % 8 == 0)
   int32_t tiled;           // 1: packed points at the tiled layout (scales inside it)
   int64_t tile_bytes;      // tiled layout: bytes per 16-row tile
   int32_t run_tiles;       // run workgroups: tiles per wave
   int32_t reserved;
-  int64_t x16_off;         // grouped launch with a workspace: byte offsets in it of this
-  int64_t e_off;           //    problem's pre-converted activations and their row exponents
+  int64_t reserved1;       // unused (keeps the table record at 144 bytes)
+  int64_t reserved2;
 };
 
 // Tiled weight layout (see include/w4a16.h): per 16-row tile, chunks of up
@@ -71,13 +71,15 @@ struct Plan {
   int64_t grid;  // workgroups
   int lds;       // dynamic LDS bytes
   bool tiled;    // every problem is in the tiled layout: kernels built for it alone
-  const unsigned char* ws = nullptr;  // grouped launch: workspace with pre-converted activations
 };
 
 // Parse "split,rt,waves" or "shared,rt,waves" (rt 1, 2 or 4; waves 1-8, or
 // 1-16 for shared workgroups of one tile per wave), or "run,tiles,waves"
 // (tiles per wave 1-16, waves 1-16).
 bool parse_tile(const char* text, Tile* t);
+// Replaces *t by the process's measurement override, if its environment set
+// one (W4A16_BATCH_TILE for grouped launches, else W4A16_TILE; read once).
+bool tile_override(bool batch, Tile* t);
 
 // Fill the tiling fields of `a` and return the launch plan.
 Plan plan_mfma(GemvArgs& a, int T, int cus);  // default matrix-core tiling of one launch (cus: CUs of the device)
@@ -101,9 +103,6 @@ hipError_t launch_batch(const GemvArgs* table_dev, int count, const Plan& p, int
 hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, const int32_t* row_ids, int64_t n_rows,
                          int64_t N, int32_t K, uint8_t* tiled, hipStream_t s);
 hipError_t launch_argmax_final(const int2* partial, int64_t nparts, int T, int32_t* id, float* val, hipStream_t s);
-// Grouped launch with a workspace: every problem's activations converted
-// once (stage_x_kernel) into the workspace, T rows per problem.
-hipError_t launch_stage_x(const GemvArgs* table_dev, int count, int T, unsigned char* ws, hipStream_t s);
 
 // Streaming read of bytes (a multiple of 16) over `workgroups` workgroups
 // of 256 threads; sink holds workgroups * 256 words.

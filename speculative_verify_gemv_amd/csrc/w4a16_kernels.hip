@@ -24,6 +24,8 @@ extern template hipError_t launch_t<16>(const GemvArgs&, const GemvArgs*, int, c
 
 namespace {
 
+constexpr unsigned short kBf16NaN = 0x7FC0;  // quiet NaN as a bf16 bit pattern
+
 // ---------------------------------------------------------------- repack ----
 
 // Row-major codes and scales -> tiled layout, one thread per 16 output bytes.
@@ -31,8 +33,10 @@ namespace {
 // quarter q: bytes 64g + 16q .. of output row 16*tile + r) and then
 // ceil(G/8) * 16 scale pieces (chunk c, row r: the bf16 scales of groups
 // 8c .. 8c+7).  Output row o is input row row_ids[o] (o itself when row_ids
-// is null); rows past N and ids outside [0, n_rows) are written as zeros, as
-// are groups past G.
+// is null).  Rows past N are written as zeros, as are groups past G; an
+// output row whose id lies outside [0, n_rows) gets zero codes and NaN
+// scales, so that its scores are NaN and never win an argmax (as a bad id
+// of a gathered call gives).
 __global__ void __launch_bounds__(256) w4a16_repack_kernel(const uint8_t* __restrict__ packed,
                                                            const uint16_t* __restrict__ scales,
                                                            const int32_t* __restrict__ row_ids, int64_t n_rows,
@@ -60,10 +64,12 @@ __global__ void __launch_bounds__(256) w4a16_repack_kernel(const uint8_t* __rest
     const int64_t o = tile * 16 + r;
     const int64_t row = o >= N ? -1 : row_ids ? (int64_t)row_ids[o] : o;
     const bool ok = row >= 0 && row < n_rows;
+    const bool bad_id = o < N && !ok;
     const int ng = min(kTileChunkGroups, G - c * kTileChunkGroups);
     unsigned short sc[8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sc[e] = (ok && e < ng) ? scales[row * G + c * kTileChunkGroups + e] : 0;
+    for (int e = 0; e < 8; ++e)
+      sc[e] = e >= ng ? 0 : ok ? scales[row * G + c * kTileChunkGroups + e] : bad_id ? kBf16NaN : 0;
     v = u4_t{sc[0] | ((unsigned)sc[1] << 16), sc[2] | ((unsigned)sc[3] << 16), sc[4] | ((unsigned)sc[5] << 16),
              sc[6] | ((unsigned)sc[7] << 16)};
     *reinterpret_cast<u4_t*>(tb + (int64_t)c * kTileChunkBytes + ng * kTileGroupBytes + r * 16) = v;
@@ -120,59 +126,6 @@ __global__ void __launch_bounds__(kArgmaxThreads) w4a16_argmax_final(const int2*
     if (id_out) id_out[t] = bi;
     if (val_out) val_out[t] = bi < 0 ? __builtin_nanf("") : bv;
   }
-}
-
-// -------------------------------------------------- activation staging ----
-
-// The activations of every problem of a grouped launch, converted once into
-// the launch's workspace: workgroup b converts row t = b % T of problem
-// b / T to fp16 in slot order (chunk c of the row at 16-byte index c from
-// a.x16_off), scaled by 2^E with E = kDirectE when every value of the row
-// converts exactly that way, else the row's own exponent from its largest
-// magnitude (slice_exponent), and stores E at a.e_off + 4t.  The same
-// conversions as the workgroups' own staging, decided per row over all of K.
-// Workgroup 0 also writes the 16 zero bytes at the start of the workspace
-// that the staging's ring padding reads.
-__global__ void __launch_bounds__(256) w4a16_stage_x_kernel(const GemvArgs* __restrict__ table, int T,
-                                                            unsigned char* __restrict__ ws) {
-  __shared__ unsigned any_bad;
-  __shared__ unsigned wave_m[4];
-  const int i = blockIdx.x / T, t = blockIdx.x % T;
-  const GemvArgs& a = table[i];
-  const int n8 = a.K / 8;
-  const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)t * a.K);
-  u4_t* dst = reinterpret_cast<u4_t*>(ws + a.x16_off) + (int64_t)t * n8;
-  if (blockIdx.x == 0 && threadIdx.x == 0) st_global(reinterpret_cast<u4_t*>(ws), u4_t{0u, 0u, 0u, 0u});
-  if (threadIdx.x == 0) any_bad = 0;
-  __syncthreads();
-  us2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
-  constexpr int kInFlight = 4;  // independent 16-byte loads per thread at a time
-  for (int c0 = threadIdx.x; c0 < n8; c0 += kInFlight * 256) {
-    u4_t v[kInFlight];
-#pragma unroll
-    for (int j = 0; j < kInFlight; ++j)
-      if (c0 + j * 256 < n8) v[j] = ld_global(src + c0 + j * 256);
-#pragma unroll
-    for (int j = 0; j < kInFlight; ++j)
-      if (c0 + j * 256 < n8) {
-        range8(v[j], mx, mn);
-        st_global(dst + c0 + j * 256, convert8_exact(v[j]));
-      }
-  }
-  if (!range_ok(mx, mn)) atomicOr(&any_bad, 1u);
-  __syncthreads();
-  int E = kDirectE;
-  if (any_bad) {  // uniform: the row again with its own power of two
-    unsigned m = 0;
-    for (int c = threadIdx.x; c < n8; c += 256) m = max(m, absmax8(ld_global(src + c)));
-    m = wave_max(m);
-    if ((threadIdx.x & 63) == 0) wave_m[threadIdx.x >> 6] = m;
-    __syncthreads();
-    m = max(max(wave_m[0], wave_m[1]), max(wave_m[2], wave_m[3]));
-    E = slice_exponent(m);
-    for (int c = threadIdx.x; c < n8; c += 256) st_global(dst + c, convert8(ld_global(src + c), E));
-  }
-  if (threadIdx.x == 0) st_global(reinterpret_cast<int*>(ws + a.e_off) + t, E);
 }
 
 template <typename F>
@@ -330,6 +283,24 @@ Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel, bool batch)
   return p;
 }
 
+// The measurement overrides W4A16_TILE (single launches) and
+// W4A16_BATCH_TILE (grouped launches), read once per process.
+bool tile_override(bool batch, Tile* t) {
+  struct Env {
+    bool single_ok, batch_ok;
+    Tile single, batch;
+  };
+  static const Env env = [] {
+    Env e{};
+    e.single_ok = parse_tile(std::getenv("W4A16_TILE"), &e.single);
+    e.batch_ok = parse_tile(std::getenv("W4A16_BATCH_TILE"), &e.batch);
+    return e;
+  }();
+  if (batch ? !env.batch_ok : !env.single_ok) return false;
+  *t = batch ? env.batch : env.single;
+  return true;
+}
+
 int shared_waves(int T, int64_t K) {
   if ((int64_t)T * ring_groups((int)(K / kGroup)) * kGroup * 2 > shared_cap(8)) return 16;
   return T <= 2 ? 4 : 8;
@@ -396,13 +367,15 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
     t = Tile{kSplit, 2, 8};       // T = 8, 19 vs 21 at T = 1; tiled 34 vs 40 at T = 8, 16.0 vs 16.8 at T = 1
   else
     t = Tile{kSplit, 1, (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(12LL * std::max(cus, 1), tiles)))};
-  Tile o;
-  if (parse_tile(std::getenv("W4A16_TILE"), &o)) t = o;
+  tile_override(false, &t);
   return plan_tile(a, T, t, a.tiled != 0, false);
 }
 
 // Tiling of the dot variant: 2 rows per wave (32 lanes per row), 8 waves,
-// activations staged per workgroup in slices of at most 8 chunks per lane.
+// activations staged per workgroup in slices of at most 8 chunks per lane
+// (64 groups), each staged row a whole number of 4-group blocks (the
+// staging fills 64 chunk positions per copy); the final values reuse the
+// staging area.
 Plan plan_dot(GemvArgs& a, int T) {
   Plan p{};
   p.variant = kDot;
@@ -411,18 +384,16 @@ Plan plan_dot(GemvArgs& a, int T) {
   p.threads = nw * 64;
   const int L = 64 / p.rt;
   p.grid = cdiv(a.n_out, (int64_t)p.rt * nw);
-  const int max_sk_regs = 8 * L / 4;  // CPL chunks per lane, 4 chunks per group
-  const int fin_bytes = std::max(nw * T * 4, (int)cdiv(nw * p.rt, 16) * T * 16 * 4);
-  int sk_lds = ((kLdsCap - fin_bytes) / T - 16) / (kGroup * 2);
+  const int max_sk_regs = 8 * L / 4;                   // CPL chunks per lane, 4 chunks per group
+  const int sk_lds = (kLdsCap / (T * kGroup * 2)) & ~3;  // whole 4-group blocks per row
   a.nw = nw;
   a.sk = std::max(1, std::min({a.G, max_sk_regs, sk_lds}));
   a.gpw = a.G;
-  a.xs_stride = a.sk * kGroup + 8;
+  a.xs_stride = (int)cdiv(a.sk, 4) * 4 * kGroup;
   a.wave_lds = 0;
-  int xs_bytes = T * a.xs_stride * 2;
-  xs_bytes = std::max(xs_bytes, (int)cdiv(nw * p.rt, 16) * T * 16 * 4);  // also holds final values
-  a.fin_offset = (xs_bytes + 15) & ~15;                                 // max buffer follows
-  p.lds = a.fin_offset + nw * T * 4;
+  a.fin_offset = 0;
+  const int fin_bytes = (int)cdiv(nw * p.rt, 16) * T * 16 * 4;
+  p.lds = std::max(T * a.xs_stride * 2, fin_bytes);
   return p;
 }
 
@@ -477,11 +448,6 @@ hipError_t launch_repack(const uint8_t* packed, const uint16_t* scales, const in
   const int64_t total = tiles * ((int64_t)G * 64 + cdiv(G, kTileChunkGroups) * 16);
   hipLaunchKernelGGL(w4a16_repack_kernel, dim3((unsigned)cdiv(total, 256)), dim3(256), 0, s, packed, scales, row_ids,
                      n_rows, N, K, tiled, tiled_tile_bytes(G), total);
-  return hipGetLastError();
-}
-
-hipError_t launch_stage_x(const GemvArgs* table_dev, int count, int T, unsigned char* ws, hipStream_t s) {
-  hipLaunchKernelGGL(w4a16_stage_x_kernel, dim3((unsigned)(count * T)), dim3(256), 0, s, table_dev, T, ws);
   return hipGetLastError();
 }
 

@@ -62,7 +62,7 @@ def test_exports_every_declared_function(lib):
 
 
 def test_abi_version_and_strings(lib):
-    assert lib.w4a16_abi_version() == 5
+    assert lib.w4a16_abi_version() == 6
     for s in range(8):
         assert lib.w4a16_status_string(s)
     assert lib.w4a16_status_string(99) == b"unknown status"
@@ -261,10 +261,11 @@ def test_stream_read_arguments_rejected_on_the_host(lib):
 
 
 def test_batch_workspace_planning_and_checks(lib):
-    """The activation workspace of a grouped launch: planned from T = 9 on,
-    T * K * 2 + 16 bytes per problem (activations, then the row exponents
-    padded to 16 bytes) after 16 zero bytes; w4a16_matmul_batch_ws rejects a
-    missing, misaligned or short workspace before touching the device."""
+    """Grouped launches need no activation workspace at any T (the
+    workgroups copy the bf16 activations straight into LDS):
+    w4a16_batch_workspace_bytes is 0, and w4a16_matmul_batch_ws accepts a
+    NULL workspace and checks the tables as w4a16_matmul_batch does, before
+    touching the device."""
     vp, i32, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     lib.w4a16_batch_workspace_bytes.argtypes = [vp]
     lib.w4a16_batch_workspace_bytes.restype = sz
@@ -280,16 +281,12 @@ def test_batch_workspace_planning_and_checks(lib):
         assert lib.w4a16_batch_plan(ctypes.cast(arr, vp), len(probs), T, ctypes.addressof(buf), nbytes) == OK
         return buf
 
-    for T in (9, 12, 16):
-        need = 16 + sum(T * k * 2 + (T * 4 + 15) // 16 * 16 for _, k in shapes)
+    for T in (1, 4, 8, 9, 12, 16):
         tb = table(T)
-        assert lib.w4a16_batch_workspace_bytes(ctypes.addressof(tb)) == need
-        run = lambda ws=A, n=need, t=ctypes.addressof(tb), d=A: lib.w4a16_matmul_batch_ws(t, d, ws, n, None)
-        assert run(ws=None) == WS and run(ws=A + 8) == WS and run(n=need - 1) == WS
+        assert lib.w4a16_batch_workspace_bytes(ctypes.addressof(tb)) == 0
+        run = lambda ws=None, n=0, t=ctypes.addressof(tb), d=A: lib.w4a16_matmul_batch_ws(t, d, ws, n, None)
         assert run(t=None) == NULLP and run(d=None) == NULLP and run(d=A + 8) == ALIGN
-        assert run() in (UNSUP, HIP)                      # arguments fine: the device check is next
-    for T in (1, 4, 8):
-        assert lib.w4a16_batch_workspace_bytes(ctypes.addressof(table(T))) == 0
+        assert run() in (UNSUP, HIP) and run(ws=A, n=64) in (UNSUP, HIP)  # the device check is next
     junk = (ctypes.c_uint64 * 16)()
     assert lib.w4a16_batch_workspace_bytes(ctypes.addressof(junk)) == 0
     assert lib.w4a16_batch_workspace_bytes(None) == 0

@@ -137,14 +137,12 @@ def test_batch_with_lm_head_argmax(w4, T, tiled):
 
 
 @pytest.mark.parametrize("T", [9, 12, 16])
-def test_batch_workspace_staging_equals_workgroup_staging(w4, T):
-    """From T = 9 the grouped launch converts the activations once into its
-    workspace and the workgroups copy them straight into LDS.  Same products
-    and sums as the workgroups' own staging, so the outputs are equal bit for
-    bit; rows that need their own power of two (values scaled by 2^40 and
-    2^-40, a row far below the fixed window) included, in both layouts, with
-    a problem's argmax, and all against the oracle."""
-    say(f"workspace staging T={T}")
+def test_batch_workspace_form_equals_plain_form(w4, T):
+    """The workspace form of the grouped launch (w4a16_matmul_batch_ws) needs
+    no workspace at any T and gives the plain launch's outputs bit for bit:
+    rows scaled by 2^40 and 2^-40 and a row spanning 2^20, both layouts, a
+    problem's argmax, all against the oracle."""
+    say(f"workspace form T={T}")
     shapes = [(1000, 5120), (2000, 17408), (300, 1152), (17, 128)]
     probs, host_side = [], []
     for i, (N, K) in enumerate(shapes):
@@ -166,22 +164,16 @@ def test_batch_workspace_staging_equals_workgroup_staging(w4, T):
     ws = torch.empty(w4.workspace_bytes(n_h, T), dtype=torch.uint8, device="cuda")
     probs[0] = probs[0] + (am_id, am_val, ws)
     b = w4.Batch(probs, T)
-    assert b.workspace is not None
-    b.run(staged=True)
-    staged = [host(pr[3]).copy() for pr in probs] + [host(am_id).copy(), host(am_val).copy()]
+    assert b.workspace is None
+    lib = w4.load_library()
+    st = lib.w4a16_matmul_batch_ws(b.host.data_ptr(), b.device.data_ptr(), None, 0,
+                                   torch.cuda.current_stream().cuda_stream)
+    assert st == 0, w4.status_string(st)
+    with_ws = [host(pr[3]).copy() for pr in probs] + [host(am_id).copy(), host(am_val).copy()]
     for pr in probs:
         pr[3].fill_(-1.0)
-    b.run(staged=False)
+    b.run()
     plain = [host(pr[3]).copy() for pr in probs] + [host(am_id).copy(), host(am_val).copy()]
-    for i, (a_, b_) in enumerate(zip(staged, plain)):
-        if i == 1:
-            # the down-sized problem is staged in K slices by its workgroups, each slice
-            # with its own power of two; the workspace takes one per row over all of K.
-            # Row T // 2 spans 2^20 across K, so its smallest values round differently.
-            keep = np.arange(T) != T // 2
-            a_, b_ = a_[keep], b_[keep]
-        assert np.array_equal(a_, b_, equal_nan=True), f"output {i} differs between the staging paths"
-    check_outputs([(None, None, None, pr[3]) for pr in probs], host_side, f"workspace staging T={T}")
-    for pr, out in zip(probs, plain):
-        pr[3].copy_(torch.from_numpy(out))
-    check_outputs([(None, None, None, pr[3]) for pr in probs], host_side, f"workgroup staging T={T}")
+    for i, (a_, b_) in enumerate(zip(with_ws, plain)):
+        assert np.array_equal(a_, b_, equal_nan=True), f"output {i} differs between the two forms"
+    check_outputs([(None, None, None, pr[3]) for pr in probs], host_side, f"grouped launch T={T}")

@@ -54,13 +54,12 @@ def test_graph_replays_match_eager(w4):
     ba_ws = torch.empty(w4.workspace_bytes(40000, T), dtype=torch.uint8, device="cuda")
     yb1t = torch.empty_like(yb1)
     batch_am = w4.Batch([(tw1, None, x1, yb1t), (twh, None, xh, yba, ba_id, ba_val, ba_ws)], T)
-    T8 = 12  # T >= 9: a grouped launch that converts its activations into its workspace first
+    T8 = 12  # a wider grouped launch, mixed layouts
     x8a = dev(synth.activations(6005, T8, 5120))
     x8b = dev(synth.activations(6006, T8, 17408))
     y8a = torch.empty((T8, 7168), dtype=torch.float32, device="cuda")
     y8b = torch.empty((T8, 5120), dtype=torch.float32, device="cuda")
     batch8 = w4.Batch([(tw1, None, x8a, y8a), (pd2, sd2, x8b, y8b)], T8)
-    assert batch8.workspace is not None
     state = {}
 
     def calls(stream):

@@ -214,7 +214,8 @@ def test_batch_mixed_layouts(w4, T):
 @pytest.mark.parametrize("N,K,n_ids", [(300, 5120, 77), (37, 1152, 1), (1000, 2304, 2500)])
 def test_repack_rows_matches_layout_of_gathered_rows(w4, N, K, n_ids):
     """The gathered repack is the layout of the host-gathered rows, byte for
-    byte (duplicates included); an id outside [0, N) gives an all-zero row."""
+    byte (duplicates included); an id outside [0, N) gives a row of zero
+    codes whose scales are the bf16 quiet NaN 0x7FC0 (its scores are NaN)."""
     p, s, pd, sd = weight_dev(4300 + N + K, N, K)
     rng = np.random.default_rng(n_ids)
     ids = rng.integers(0, N, n_ids).astype(np.int32)
@@ -227,7 +228,7 @@ def test_repack_rows_matches_layout_of_gathered_rows(w4, N, K, n_ids):
     bad[min(1, n_ids - 1)] = N + 5
     pz, sz = p[ids].copy(), s[ids].copy()
     pz[min(1, n_ids - 1)] = 0
-    sz[min(1, n_ids - 1)] = 0
+    sz[min(1, n_ids - 1)] = 0x7FC0
     assert np.array_equal(host(w4.repack_tiled_rows(pd, sd, dev(bad)).data), layout_by_definition(pz, sz))
 
 
@@ -249,3 +250,26 @@ def test_compact_draft_head_matches_oracle(w4, T):
     assert_parity(y, y_ref, a_ref, f"compact draft head T={T}")
     own, _, _ = oracle.argmax(y.astype(np.float64), ids)
     assert np.array_equal(ids[am], own)
+
+
+def test_compact_head_bad_ids_never_win(w4):
+    """A compact head (w4a16_repack_tiled_rows) whose list holds ids outside
+    the head: those rows score NaN, so with every valid score negative the
+    argmax is still the best valid row (an all-zero row scoring 0 would win)."""
+    N, K, T = 3000, 1024, 2
+    p = synth.codes(4600, N, K) & 0x77  # every code in 0..7: levels -8..-1
+    s = synth.scales(4600, N, K)
+    xf = np.abs(synth.bf16_to_f32(synth.activations(4600, T, K)).astype(np.float64)) + 0.25
+    x = np.array([synth.bf16_from_double(v) for v in xf.ravel()], np.uint16).reshape(T, K)
+    ids = synth.distinct_ids(4601, 700, N).copy()
+    ids[[0, 5, 333, 699]] = [-3, N, N + 100, -(2 ** 31)]
+    y_ref, a_ref = oracle.gather(ids, p, s, x)
+    assert np.all(y_ref[~np.isnan(y_ref)] < 0)
+    tw = w4.repack_tiled_rows(dev(p), dev(s), dev(ids))
+    say("compact head with bad ids")
+    y, am, av = w4.head_gather_tiled(tw, dev(x), argmax=True)
+    y, am, av = host(y), host(am), host(av)
+    assert np.array_equal(np.isnan(y), np.isnan(y_ref)), "bad-id rows must score NaN"
+    assert_parity(y, y_ref, a_ref, "compact head with bad ids")
+    check_argmax(am, y, y_ref, None, "compact head with bad ids")
+    assert np.all(am >= 0) and np.all(ids[am] >= 0) and np.array_equal(av, y[np.arange(T), am])

@@ -61,6 +61,8 @@ def _load():
         lib.synth_normal_bf16.argtypes = [u64, u64, vp, u64, i32]
         lib.synth_distinct_ids.argtypes = [u64, u64, vp, i64, i64]
         lib.synth_distinct_ids.restype = i32
+        lib.synth_codes_range.argtypes = [u64, u64, vp, u64, u64]
+        lib.synth_scales_range.argtypes = [u64, u64, vp, u64, u64]
         lib.synth_bf16_from_double.argtypes = [ctypes.c_double]
         lib.synth_bf16_from_double.restype = ctypes.c_uint16
         _lib = lib
@@ -111,6 +113,21 @@ def distinct_ids(rid: int, n_ids: int, n_rows: int, seed: int = SEED) -> np.ndar
 
 def weight(tid: int, n_rows: int, k: int, seed: int = SEED):
     return codes(tid, n_rows, k, seed), scales(tid, n_rows, k, seed)
+
+
+def weight_rows(tid: int, rows, k: int, seed: int = SEED):
+    """Rows `rows` of weight tensor `tid` (row-major [n_rows][k/2] codes and
+    [n_rows][k/128] scales), the same bits as weight(...)[0][rows] and
+    [1][rows], generated without the other rows."""
+    rows = np.asarray(rows, dtype=np.int64)
+    kb, g = k // 2, k // GROUP
+    p = np.empty((rows.size, kb), dtype=np.uint8)
+    s = np.empty((rows.size, g), dtype=np.uint16)
+    lib = _load()
+    for i, r in enumerate(rows):
+        lib.synth_codes_range(seed, 4 * tid + 0, p[i].ctypes.data, int(r) * kb, kb)
+        lib.synth_scales_range(seed, 4 * tid + 1, s[i].ctypes.data, int(r) * g, g)
+    return p, s
 
 
 def bf16_to_f32(bits: np.ndarray) -> np.ndarray:

@@ -74,8 +74,8 @@ uint16_t synth_bf16_from_double(double v) {
 typedef struct {
   int kind;
   uint64_t state;
-  void* out;
-  uint64_t begin, end;
+  void* out;       /* element i of the stream goes to out[i - base] */
+  uint64_t begin, end, base;
 } job_t;
 
 enum { KIND_BYTES = 0, KIND_SCALES = 1, KIND_NORMAL_BF16 = 2 };
@@ -83,7 +83,7 @@ enum { KIND_BYTES = 0, KIND_SCALES = 1, KIND_NORMAL_BF16 = 2 };
 static void* run_job(void* p) {
   job_t* j = (job_t*)p;
   if (j->kind == KIND_BYTES) {
-    uint8_t* o = (uint8_t*)j->out;
+    uint8_t* o = (uint8_t*)j->out - j->base;
     /* byte i comes from bits 8*(i%8).. of draw i/8 */
     uint64_t i = j->begin;
     while (i < j->end) {
@@ -92,15 +92,18 @@ static void* run_job(void* p) {
     }
   } else if (j->kind == KIND_SCALES) {
     uint16_t* o = (uint16_t*)j->out;
-    for (uint64_t i = j->begin; i < j->end; ++i) o[i] = synth_bf16_from_double(0.02 * fabs(normal_at(j->state, i)) + 1e-3);
+    for (uint64_t i = j->begin; i < j->end; ++i)
+      o[i - j->base] = synth_bf16_from_double(0.02 * fabs(normal_at(j->state, i)) + 1e-3);
   } else {
     uint16_t* o = (uint16_t*)j->out;
-    for (uint64_t i = j->begin; i < j->end; ++i) o[i] = synth_bf16_from_double(normal_at(j->state, i));
+    for (uint64_t i = j->begin; i < j->end; ++i) o[i - j->base] = synth_bf16_from_double(normal_at(j->state, i));
   }
   return NULL;
 }
 
-static void fill(int kind, uint64_t seed, uint64_t stream_id, void* out, uint64_t count, int nthreads) {
+/* Elements [start, start + count) of a stream into out[0 .. count). */
+static void fill(int kind, uint64_t seed, uint64_t stream_id, void* out, uint64_t start, uint64_t count,
+                 int nthreads) {
   uint64_t state = stream_state(seed, stream_id);
   if (nthreads < 1) nthreads = 1;
   if (nthreads > 256) nthreads = 256;
@@ -114,7 +117,7 @@ static void fill(int kind, uint64_t seed, uint64_t stream_id, void* out, uint64_
     uint64_t b = per * t, e = b + per;
     if (b >= count) break;
     if (e > count) e = count;
-    jobs[t] = (job_t){kind, state, out, b, e};
+    jobs[t] = (job_t){kind, state, out, start + b, start + e, start};
     if (t == 0) continue;
     if (pthread_create(&th[t], NULL, run_job, &jobs[t]) != 0) { run_job(&jobs[t]); th[t] = 0; }
     launched = t + 1;
@@ -126,17 +129,27 @@ static void fill(int kind, uint64_t seed, uint64_t stream_id, void* out, uint64_
 
 /* Uniform bytes (two 4-bit codes per byte). */
 void synth_codes(uint64_t seed, uint64_t stream_id, uint8_t* out, uint64_t n_bytes, int nthreads) {
-  fill(KIND_BYTES, seed, stream_id, out, n_bytes, nthreads);
+  fill(KIND_BYTES, seed, stream_id, out, 0, n_bytes, nthreads);
 }
 
 /* bf16 scales 0.02*|z| + 1e-3. */
 void synth_scales(uint64_t seed, uint64_t stream_id, uint16_t* out, uint64_t n, int nthreads) {
-  fill(KIND_SCALES, seed, stream_id, out, n, nthreads);
+  fill(KIND_SCALES, seed, stream_id, out, 0, n, nthreads);
 }
 
 /* bf16 standard normals. */
 void synth_normal_bf16(uint64_t seed, uint64_t stream_id, uint16_t* out, uint64_t n, int nthreads) {
-  fill(KIND_NORMAL_BF16, seed, stream_id, out, n, nthreads);
+  fill(KIND_NORMAL_BF16, seed, stream_id, out, 0, n, nthreads);
+}
+
+/* Bytes [start, start + n_bytes) and scales [start, start + n) of the same
+ * streams: any rows of a weight without generating the rest. */
+void synth_codes_range(uint64_t seed, uint64_t stream_id, uint8_t* out, uint64_t start, uint64_t n_bytes) {
+  fill(KIND_BYTES, seed, stream_id, out, start, n_bytes, 1);
+}
+
+void synth_scales_range(uint64_t seed, uint64_t stream_id, uint16_t* out, uint64_t start, uint64_t n) {
+  fill(KIND_SCALES, seed, stream_id, out, start, n, 1);
 }
 
 /* Floyd's algorithm: n_ids distinct values from [0, n_rows), in draw order.

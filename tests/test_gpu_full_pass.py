@@ -2,23 +2,20 @@
 configuration bench.py times: 64 layers x {qkv, o, gate_up, down} with
 distinct seeded weights, repacked to the tiled layout, plus the 248,320-row
 lm_head with its per-row argmax, in one grouped launch (the grouped launch's
-own tiling for each T).  Outputs are compared with the oracle on sampled rows
-of sampled problems (every projection kind, first and last layers, rows at
-tile edges); the head's scores in full and its argmax bit for bit.
+own tiling for each T).  Every one of the 256 body problems is compared with
+the oracle on its first and last 16-row tiles and a few random rows; the
+head's scores in full and its argmax bit for bit.  Outputs start as NaN, so
+an unwritten row fails.
 """
 import numpy as np
 import pytest
 
 import oracle
 import synth
-from gpu_util import assert_parity, dev, host, sample_rows, say
+from gpu_util import assert_parity, check_argmax, dev, host, say
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
-
-# (layer, projection) pairs whose outputs are checked
-CHECKED = [(0, "qkv"), (0, "down"), (17, "gate_up"), (31, "o"), (38, "down"), (63, "gate_up"), (63, "down"),
-           (63, "o")]
 
 
 @pytest.fixture(scope="module")
@@ -32,8 +29,8 @@ def w4():
 
 @pytest.fixture(scope="module")
 def resident(w4):
-    """The bench's resident tiled weights (device only; host copies are
-    regenerated from the seeds where a check needs them)."""
+    """The bench's resident tiled weights (device only; the rows a check
+    needs are regenerated on the host from the seeds)."""
     say("full pass: 64 layers + lm_head to the device ...")
     weights = []
     for layer in range(synth.LAYERS):
@@ -51,18 +48,26 @@ def resident(w4):
     torch.cuda.empty_cache()
 
 
-def check_problems(probs, weights, T, what):
-    index = {(layer, proj): i for i, (layer, proj, _) in enumerate(weights)}
-    for layer, proj in CHECKED:
+def checked_rows(N: int, seed: int, extra: int = 6) -> np.ndarray:
+    """The first and last 16-row tiles and `extra` random rows of an N-row matrix."""
+    rng = np.random.default_rng(seed)
+    rows = np.concatenate([np.arange(16), np.arange(N - 16, N), rng.choice(np.arange(16, N - 16), extra, False)])
+    return np.unique(rows).astype(np.int64)
+
+
+def check_all_problems(probs, weights, T, what):
+    """Every body problem against the oracle on its checked rows."""
+    worst = 0.0
+    for (layer, proj, _), prob in zip(weights, probs):
         N, K = synth.PROJECTIONS[proj]
         tid = synth.tid_layer(layer, proj)
-        p, s = synth.weight(tid, N, K)
+        rows = checked_rows(N, seed=tid * 31 + T)
+        p, s = synth.weight_rows(tid, rows, K)
         x = synth.activations(tid, T, K)
-        rows = sample_rows(N, 48, seed=tid)
-        y_ref, a_ref = oracle.gather(rows, p, s, x)
-        y = host(probs[index[(layer, proj)]][3])
-        r = assert_parity(y[:, rows], y_ref, a_ref, f"{what} layer {layer} {proj}")
-        say(f"  layer {layer} {proj}: max err/tol {r:.3g}")
+        y_ref, a_ref = oracle.matmul(p, s, x)
+        y = host(prob[3])
+        worst = max(worst, assert_parity(y[:, rows], y_ref, a_ref, f"{what} layer {layer} {proj}"))
+    say(f"  {what}: all {len(probs)} body problems checked, max err/tol {worst:.3g}")
 
 
 def body_problems(w4, weights, T):
@@ -74,12 +79,11 @@ def body_problems(w4, weights, T):
     return probs
 
 
-def test_step_at_t4_with_lm_head_argmax(w4, resident):
-    """The bench step: body + lm_head with argmax in one grouped launch."""
-    from gpu_util import check_argmax
-
+@pytest.mark.parametrize("T", [1, 4, 8])
+def test_step_with_lm_head_argmax(w4, resident, T):
+    """The bench step at T = 1, 4 and 8: body + lm_head with argmax in one
+    grouped launch; all 257 problems checked."""
     weights, head, (hp, hs) = resident
-    T = 4
     hn, hk = synth.LM_HEAD
     probs = body_problems(w4, weights, T)
     hx = synth.activations(synth.TID_LM_HEAD, T, hk)
@@ -88,17 +92,17 @@ def test_step_at_t4_with_lm_head_argmax(w4, resident):
     hval = torch.full((T,), 7.0, dtype=torch.float32, device="cuda")
     hws = torch.empty(w4.workspace_bytes(hn, T), dtype=torch.uint8, device="cuda")
     step = w4.Batch(probs + [(head, None, dev(hx), hy, hid, hval, hws)], T)
-    say("full pass step T=4 ...")
+    say(f"full pass step T={T} ...")
     step.run()
     torch.cuda.synchronize()
-    check_problems(probs, weights, T, "step T=4")
-    say("  oracle lm_head T=4 ...")
+    check_all_problems(probs, weights, T, f"step T={T}")
+    say(f"  oracle lm_head T={T} ...")
     y_ref, a_ref = oracle.matmul(hp, hs, hx)
     yh = host(hy)
-    r = assert_parity(yh, y_ref, a_ref, "step lm_head T=4")
+    r = assert_parity(yh, y_ref, a_ref, f"step lm_head T={T}")
     say(f"  lm_head: max err/tol {r:.3g}")
     ids = host(hid)
-    check_argmax(ids, yh, y_ref, None, "step lm_head T=4")
+    check_argmax(ids, yh, y_ref, None, f"step lm_head T={T}")
     assert np.array_equal(host(hval), yh[np.arange(T), ids])
     # the step again: identical bits (no state carried between launches)
     first = [host(y).copy() for *_, y in probs[:8]]
@@ -109,12 +113,12 @@ def test_step_at_t4_with_lm_head_argmax(w4, resident):
     assert np.array_equal(host(hid), ids)
 
 
-@pytest.mark.parametrize("T", [1, 8, 16])
-def test_body_pass_other_widths(w4, resident, T):
-    """The body pass alone at the other verify widths bench.py reports."""
+def test_body_pass_t16(w4, resident):
+    """The body pass alone at T = 16 (the widest verify block), every problem checked."""
     weights, _, _ = resident
+    T = 16
     probs = body_problems(w4, weights, T)
     say(f"full pass body T={T} ...")
     w4.Batch(probs, T).run()
     torch.cuda.synchronize()
-    check_problems(probs, weights, T, f"body T={T}")
+    check_all_problems(probs, weights, T, f"body T={T}")

@@ -55,3 +55,13 @@ def test_distinct_ids():
     assert not np.all(np.diff(ids) > 0)  # kept in draw order, not sorted
     full = synth.distinct_ids(8, 50, 50)
     assert sorted(full.tolist()) == list(range(50))
+
+
+def test_weight_rows_equal_rows_of_the_full_weight():
+    """The range form of the generator gives the same bits as the whole
+    tensor, at any row (stream positions not a multiple of 8 included)."""
+    N, K = 300, 1152
+    p, s = synth.weight(77, N, K)
+    rows = np.array([0, 1, 7, 8, 150, 298, 299])
+    pr, sr = synth.weight_rows(77, rows, K)
+    assert np.array_equal(pr, p[rows]) and np.array_equal(sr, s[rows])

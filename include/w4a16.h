@@ -71,7 +71,8 @@ typedef enum {
   W4A16_ERR_WORKSPACE = 4,    /* argmax workspace (or batch table buffer) missing or too small */
   W4A16_ERR_UNSUPPORTED = 5,  /* the current device is not gfx950 */
   W4A16_ERR_HIP = 6,          /* a HIP runtime call returned an error */
-  W4A16_ERR_BAD_VARIANT = 7   /* unknown kernel variant */
+  W4A16_ERR_BAD_VARIANT = 7,  /* unknown kernel variant */
+  W4A16_ERR_SCRATCH = 8       /* w4a16_head_gather_noalloc: argmax partials larger than its static scratch */
 } w4a16_status;
 
 /* Kernel variants.  Both compute the same values within the tolerance above.
@@ -126,6 +127,32 @@ w4a16_status w4a16_head_gather(const int32_t* row_ids, int64_t n_ids, const uint
 /* Workspace bytes w4a16_head_gather needs for n_out scored rows at T
  * (0 for arguments out of range). */
 size_t w4a16_workspace_bytes(int64_t n_out, int32_t T);
+
+/*
+ * w4a16_head_gather without a workspace argument and without any
+ * allocation, for callers that cannot allocate device memory: code being
+ * captured into a HIP graph, tight serving loops, harnesses that forbid
+ * hipMalloc.  The argmax partials go to a static device array of
+ * W4A16_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends; its device address is looked up once per device
+ * (hipGetSymbolAddress).  Same arguments, kernels and results as
+ * w4a16_head_gather otherwise.
+ *   Limit: with argmax_id set, w4a16_workspace_bytes(n_ids, T) must not
+ *   exceed W4A16_NOALLOC_SCRATCH_BYTES (2 MiB: e.g. 262,144 rows at T = 16,
+ *   enough for a 248,320-row vocabulary head), else W4A16_ERR_SCRATCH and
+ *   nothing is enqueued.  Without argmax the array is not used.
+ *   The array needs no initialisation (each workgroup writes its own
+ *   partials before the reduction reads them) and keeps the last call's
+ *   contents.  Every call on one GPU shares it: calls that may overlap on
+ *   one GPU (different streams, or different host threads) race and must be
+ *   serialised by the caller.
+ */
+#define W4A16_NOALLOC_SCRATCH_BYTES (2u << 20)
+
+w4a16_status w4a16_head_gather_noalloc(const int32_t* row_ids, int64_t n_ids, const uint8_t* packed_u4,
+                                       const uint16_t* scales_bf16, int64_t n_rows, const uint16_t* x_bf16,
+                                       int64_t K, int32_t T, float* y_f32, int32_t* argmax_id, float* argmax_val,
+                                       hipStream_t stream);
 
 /*
  * Tiled weight layout: a one-time repack of the same codes and scales so

@@ -43,6 +43,8 @@ def load_library():
         lib.w4a16_matmul.restype = i32
         lib.w4a16_head_gather.argtypes = [vp, i64, vp, vp, i64, vp, i64, i32, vp, vp, vp, vp, sz, vp]
         lib.w4a16_head_gather.restype = i32
+        lib.w4a16_head_gather_noalloc.argtypes = [vp, i64, vp, vp, i64, vp, i64, i32, vp, vp, vp, vp]
+        lib.w4a16_head_gather_noalloc.restype = i32
         lib.w4a16_workspace_bytes.argtypes = [i64, i32]
         lib.w4a16_workspace_bytes.restype = sz
         lib.w4a16_set_variant.argtypes = [i32]
@@ -211,6 +213,33 @@ def head_gather(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor, row
     if s:
         raise W4A16Error(s, "w4a16_head_gather")
     return y, ids, vals
+
+
+NOALLOC_SCRATCH_BYTES = 2 << 20
+
+
+def head_gather_noalloc(packed: torch.Tensor, scales: torch.Tensor, x: torch.Tensor,
+                        row_ids: torch.Tensor | None = None, out: torch.Tensor | None = None,
+                        argmax_id: torch.Tensor | None = None, argmax_val: torch.Tensor | None = None, stream=None):
+    """head_gather() through w4a16_head_gather_noalloc: the library allocates
+    nothing (the argmax partials live in its static device scratch); the
+    caller passes every output it wants (out [T][n] float32, argmax_id [T]
+    int32, argmax_val [T] float32), so the call itself allocates nothing
+    either.  Calls that may overlap on one GPU race on the scratch."""
+    n_rows, K = _check_weight(packed, scales)
+    _check_bits(x, "x")
+    if x.dim() != 2 or x.shape[1] != K:
+        raise ValueError(f"x must be [T][{K}]")
+    T = x.shape[0]
+    n = _row_ids(row_ids, n_rows)
+    for t, shape, dt, what in ((out, (T, n), torch.float32, "out"), (argmax_id, (T,), torch.int32, "argmax_id"),
+                               (argmax_val, (T,), torch.float32, "argmax_val")):
+        if t is not None and (t.dtype != dt or tuple(t.shape) != shape or not (t.is_cuda and t.is_contiguous())):
+            raise ValueError(f"{what} must be a contiguous CUDA {dt} tensor of shape {shape}")
+    s = load_library().w4a16_head_gather_noalloc(_ptr(row_ids), n, _ptr(packed), _ptr(scales), n_rows, _ptr(x), K,
+                                                 T, _ptr(out), _ptr(argmax_id), _ptr(argmax_val), _stream(stream))
+    if s:
+        raise W4A16Error(s, "w4a16_head_gather_noalloc")
 
 
 class TiledWeight:

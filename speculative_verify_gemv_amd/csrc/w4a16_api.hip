@@ -14,6 +14,10 @@
 namespace {
 
 constexpr int64_t kMaxRows = 2147483647LL;
+// Stands in for the static scratch in the host-side argument checks of
+// w4a16_head_gather_noalloc (they test a workspace pointer for null and
+// alignment only; the kernels get the real device address).
+constexpr uintptr_t kScratchAligned = 256;
 constexpr int64_t kMaxK = 1LL << 20;
 
 std::atomic<int32_t> g_variant{-1};
@@ -122,6 +126,26 @@ w4a16_status run(w4a16::GemvArgs& a, int32_t T, int32_t* argmax_id, float* argma
   if (argmax_id && w4a16::launch_argmax_final(a.partial, p.grid, T, argmax_id, argmax_val, stream) != hipSuccess)
     return W4A16_ERR_HIP;
   return W4A16_OK;
+}
+
+// Argmax partials of w4a16_head_gather_noalloc: a static device array, one
+// per GPU the library runs on, held until the process ends.  Its host-side
+// name is only a stand-in: kernels get the device address that
+// hipGetSymbolAddress returns, looked up once per device.
+constexpr size_t kScratchBytes = size_t(1) << 21;  // 2 MiB = W4A16_NOALLOC_SCRATCH_BYTES
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+std::atomic<void*> g_scratch[kMaxDevices];
+
+// The device address of this device's scratch array (the current device, as
+// check_device found it), or nullptr if HIP cannot give it.
+void* scratch_ptr() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  void* p = g_scratch[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+  g_scratch[dev].store(p, std::memory_order_release);
+  return p;
 }
 
 }  // namespace
@@ -268,6 +292,28 @@ w4a16_status w4a16_head_gather(const int32_t* row_ids, int64_t n_ids, const uint
     return s;
   w4a16::GemvArgs a = gemv_args(packed_u4, scales_bf16, false, x_bf16, y_f32, row_ids, n_ids, n_rows, K);
   a.partial = argmax_id ? static_cast<int2*>(workspace) : nullptr;
+  const w4a16::Plan p = make_plan(a, T);
+  return run(a, T, argmax_id, argmax_val, p, stream);
+}
+
+w4a16_status w4a16_head_gather_noalloc(const int32_t* row_ids, int64_t n_ids, const uint8_t* packed_u4,
+                                       const uint16_t* scales_bf16, int64_t n_rows, const uint16_t* x_bf16,
+                                       int64_t K, int32_t T, float* y_f32, int32_t* argmax_id, float* argmax_val,
+                                       hipStream_t stream) {
+  static_assert(kScratchBytes == W4A16_NOALLOC_SCRATCH_BYTES, "scratch size in the header");
+  if (!packed_u4 || !scales_bf16) return W4A16_ERR_NULL_POINTER;
+  if (!aligned(packed_u4, 16) || !aligned(scales_bf16, 2)) return W4A16_ERR_MISALIGNED;
+  // the argmax partials must fit the static array; checked before anything else uses it
+  if (argmax_id && n_ids >= 1 && n_ids <= kMaxRows && T >= 1 && T <= W4A16_MAX_T &&
+      w4a16_workspace_bytes(n_ids, T) > kScratchBytes)
+    return W4A16_ERR_SCRATCH;
+  if (w4a16_status s = check_gather(row_ids, n_ids, n_rows, x_bf16, K, T, y_f32, argmax_id, argmax_val,
+                                    argmax_id ? reinterpret_cast<void*>(kScratchAligned) : nullptr, kScratchBytes))
+    return s;
+  void* ws = nullptr;
+  if (argmax_id && !(ws = scratch_ptr())) return W4A16_ERR_HIP;
+  w4a16::GemvArgs a = gemv_args(packed_u4, scales_bf16, false, x_bf16, y_f32, row_ids, n_ids, n_rows, K);
+  a.partial = argmax_id ? static_cast<int2*>(ws) : nullptr;
   const w4a16::Plan p = make_plan(a, T);
   return run(a, T, argmax_id, argmax_val, p, stream);
 }
@@ -495,6 +541,8 @@ const char* w4a16_status_string(int32_t status) {
     case W4A16_ERR_UNSUPPORTED: return "the current device is not gfx950";
     case W4A16_ERR_HIP: return "a HIP runtime call failed";
     case W4A16_ERR_BAD_VARIANT: return "unknown kernel variant";
+    case W4A16_ERR_SCRATCH:
+      return "the argmax partials need more than the library's static scratch (W4A16_NOALLOC_SCRATCH_BYTES)";
     default: return "unknown status";
   }
 }

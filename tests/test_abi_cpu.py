@@ -11,7 +11,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w4a16.h")
 LIB = os.path.join(ROOT, "speculative_verify_gemv_amd", "libw4a16.so")
 
-OK, NULLP, SHAPE, ALIGN, WS, UNSUP, HIP, VARIANT = range(8)
+OK, NULLP, SHAPE, ALIGN, WS, UNSUP, HIP, VARIANT, SCRATCH = range(9)
 
 
 def declared_functions():
@@ -63,7 +63,7 @@ def test_exports_every_declared_function(lib):
 
 def test_abi_version_and_strings(lib):
     assert lib.w4a16_abi_version() == 6
-    for s in range(8):
+    for s in range(9):
         assert lib.w4a16_status_string(s)
     assert lib.w4a16_status_string(99) == b"unknown status"
 
@@ -290,3 +290,23 @@ def test_batch_workspace_planning_and_checks(lib):
     junk = (ctypes.c_uint64 * 16)()
     assert lib.w4a16_batch_workspace_bytes(ctypes.addressof(junk)) == 0
     assert lib.w4a16_batch_workspace_bytes(None) == 0
+
+
+def test_head_gather_noalloc_limits(lib):
+    """The allocation-free head call checks its arguments like
+    w4a16_head_gather, needs no workspace, and refuses (before the device
+    is touched) argmax partials larger than its static scratch."""
+    vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32
+    f = lib.w4a16_head_gather_noalloc
+    f.argtypes = [vp, i64, vp, vp, i64, vp, i64, i32, vp, vp, vp, vp]
+    f.restype = i32
+    call = lambda ids=A, n_ids=10, p=A, s=A, n_rows=100, x=A, K=256, T=2, y=A, am=None, av=None: \
+        f(ids, n_ids, p, s, n_rows, x, K, T, y, am, av, None)
+    assert call(p=None) == NULLP and call(y=None) == NULLP and call(av=A) == NULLP
+    assert call(n_ids=0) == SHAPE and call(T=17) == SHAPE and call(ids=A + 2) == ALIGN
+    limit = 2 << 20
+    assert lib.w4a16_workspace_bytes(262144, 16) == limit
+    assert call(n_ids=262145, n_rows=300000, T=16, am=A) == SCRATCH
+    assert call(n_ids=262145, n_rows=300000, T=16, am=None) in (UNSUP, HIP)  # no argmax: no scratch used
+    assert call(n_ids=262144, n_rows=300000, T=16, am=A) in (UNSUP, HIP)     # exactly the limit
+    assert call(am=A) in (UNSUP, HIP)                                       # no workspace needed

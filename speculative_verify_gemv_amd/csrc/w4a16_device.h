@@ -319,6 +319,37 @@ __device__ __forceinline__ void stage_x(const GemvArgs& a, __bf16* xs, int gs, i
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 }
 
+// The same staging by one wave through its registers (16-byte loads, four
+// in flight per lane, then swizzled LDS stores), for waves that stage their
+// own K range.  Such a wave's K loop follows with no workgroup barrier; with
+// direct global-to-LDS copies in the kernel the compiler made that loop
+// wait for every load in flight at each cycle of the ring (it cannot tell
+// the copies have landed), so these kernels copy through registers.
+template <int TT>
+__device__ __forceinline__ void stage_x_wave(const GemvArgs& a, unsigned char* xs, int gs, int ge) {
+  constexpr int kBatch = 4;
+  const int lane = threadIdx.x & 63;
+  const int n = (ge - gs) * (kGroup / 8);      // chunks of the slice per token row
+  const int dst_row = a.xs_stride / 8;         // chunk positions per staged row
+  const int total = TT * dst_row;
+  const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)gs * kGroup);
+  u4_t* dst = reinterpret_cast<u4_t*>(xs);
+  const int src_row = a.K / 8;
+  for (int base = lane; base < total; base += kBatch * 64) {
+    u4_t v[kBatch];
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i) {
+      const int pos = base + i * 64;
+      const int t = pos / dst_row;
+      const int c = swz(t, pos - t * dst_row);
+      v[i] = (pos < total && c < n) ? ld_global(src + t * src_row + c) : u4_t{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int i = 0; i < kBatch; ++i)
+      if (base + i * 64 < total) dst[base + i * 64] = v[i];
+  }
+}
+
 // ------------------------------------- fp16 staging (up to kF16MaxT rows) ----
 //
 // The same staged layout with fp16 values times 2^kDirectE, each chunk's
@@ -654,7 +685,7 @@ __device__ __forceinline__ bool stage_slice(const GemvArgs& a, unsigned char* xs
       else
         lds_fence();
     }
-    if (!h) stage_x<TT>(a, reinterpret_cast<__bf16*>(xs), sb, se, 0, 1);
+    if (!h) stage_x_wave<TT>(a, xs, sb, se);
     lds_fence();
   }
   // the staging waited for its loads, issued after the weight loads in

@@ -188,30 +188,54 @@ def main():
             f"body pass at T = 1, 4, 8, 16")
         return
 
-    for _ in range(args.warmup):
-        step.run(stream)
-    torch.cuda.synchronize()
+    def time_step(st, steps, warmup):
+        """Whole-loop and per-launch times of `steps` grouped launches (each
+        followed by its argmax reduction), after `warmup` untimed ones."""
+        for _ in range(warmup):
+            st.run(stream)
+        torch.cuda.synchronize()
+        ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+        start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        start.record(stream)
+        for i in range(steps):
+            ev[i][0].record(stream)
+            st.run(stream)
+            ev[i][1].record(stream)
+        end.record(stream)
+        torch.cuda.synchronize()
+        per = [a.elapsed_time(b) for a, b in ev]
+        return start.elapsed_time(end) / steps, per
 
-    K_steps = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K_steps)]
-    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(K_steps):
-        ev[i][0].record(stream)
-        step.run(stream)
-        ev[i][1].record(stream)
-    end.record(stream)
-    torch.cuda.synchronize()
-    ms_total = start.elapsed_time(end)
-    ms_step = ms_total / K_steps
-    launch_ms = [a.elapsed_time(b) for a, b in ev]
-    launch_ms_avg = float(np.mean(launch_ms))
     step_bytes = body_bytes + head_bytes
+    ms_step, launch_ms = time_step(step, args.steps, args.warmup)
+    K_steps = args.steps
+    launch_ms_avg = float(np.mean(launch_ms))
     value = metrics.gbps(step_bytes, ms_step)
     achieved = metrics.gbps(step_bytes, launch_ms_avg)
     log(f"step {ms_step:.4f} ms, grouped launch + argmax reduction {launch_ms_avg:.4f} ms "
-        f"(min {min(launch_ms):.4f}), {value:.0f} GB/s per step, kernel {achieved:.0f} GB/s")
+        f"(median {np.median(launch_ms):.4f}, min {min(launch_ms):.4f}), {value:.0f} GB/s per step, "
+        f"kernel {achieved:.0f} GB/s")
+
+    # the same step (body + lm_head with argmax, one grouped launch) at the
+    # other verify widths: T = 1 (plain decode) and T = 8
+    per_t_step = {f"T{T}": step_summary(step_bytes, ms_step, launch_ms)}
+    for Tp in (1, 8):
+        if Tp == T:
+            continue
+        b_probs = make_pass(Tp)[1]
+        hxp = to_dev(synth.activations(synth.TID_LM_HEAD, Tp, hk), torch)
+        hyp = torch.empty((Tp, hn), dtype=torch.float32, device="cuda")
+        hwp = torch.empty(w4a16.workspace_bytes(hn, Tp), dtype=torch.uint8, device="cuda")
+        hip_ = torch.empty(Tp, dtype=torch.int32, device="cuda")
+        hvp = torch.empty(Tp, dtype=torch.float32, device="cuda")
+        st = w4a16.Batch(b_probs + [(head_tw, None, hxp, hyp, hip_, hvp, hwp)], Tp)
+        ms_p, per_p = time_step(st, args.steps, args.warmup)
+        per_t_step[f"T{Tp}"] = step_summary(step_bytes, ms_p, per_p)
+        log(f"step T={Tp}: {ms_p:.4f} ms ({per_t_step[f'T{Tp}']['cycles_per_s']} cycles/s), launch "
+            f"{np.mean(per_p):.4f} ms, {per_t_step[f'T{Tp}']['roofline']['frac']:.4f} of 8 TB/s")
+        del st, b_probs
+    per_t_step = {k: per_t_step[k] for k in sorted(per_t_step, key=lambda k: int(k[1:]))}
 
     # the same step as two launches (body pass, then the lm_head with argmax)
     for _ in range(5):
@@ -271,12 +295,16 @@ def main():
         f"greedy acceptance {epilogue['greedy_us']:.1f} us, draft-head id list {epilogue['draft_union_us']:.1f} us")
 
     # ---- the same step as 257 separate launches, replayed from a HIP graph ----
-    graph_pass = None
+    graph_pass = plain_pass = None
     if not args.no_graph:
         graph_pass = graph_step(torch, w4a16, probs, head, reps=10)
         g = metrics.gbps(step_bytes, graph_pass["ms_per_step"])
         graph_pass["weight_GBps"] = round(g, 1)
         log(f"257-launch graph step: {graph_pass['ms_per_step']:.4f} ms, {g:.0f} GB/s")
+        plain_pass = plain_launch_step(torch, w4a16, probs, head, stream, reps=10)
+        g = metrics.gbps(step_bytes, plain_pass["ms_per_step"])
+        plain_pass["weight_GBps"] = round(g, 1)
+        log(f"257 plain stream launches: {plain_pass['ms_per_step']:.4f} ms, {g:.0f} GB/s")
 
     # ---- CPU baseline: the oracle on a bounded sample of the same pass ----
     cpu = None
@@ -308,11 +336,13 @@ def main():
         },
         "cycles_per_s": round(1000.0 / ms_step, 2),
         "pct_hbm_peak": round(100 * value / PEAK_GBPS, 2),
+        "per_T_step": per_t_step,
         "per_T_body_pass": per_t,
         "per_T_body_pass_row_major": per_t_rm,
         "step_two_launches": {"ms_per_step": round(ms_two, 4),
                               "weight_GBps": round(metrics.gbps(step_bytes, ms_two), 1)},
         "graph_257_launches": graph_pass,
+        "plain_257_launches": plain_pass,
         "verify_epilogue": epilogue,
         "single_launches": singles,
         "variants_dot_vs_matrix_core": variants,
@@ -329,10 +359,25 @@ def main():
             "traffic": measured_traffic(),
             "algorithmic_bytes_per_launch": step_bytes,
             "avg_launch_ms": round(launch_ms_avg, 4),
+            "median_launch_ms": round(float(np.median(launch_ms)), 4),
+            "min_launch_ms": round(float(min(launch_ms)), 4),
         },
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)
+
+
+def step_summary(step_bytes, ms_step, launch_ms):
+    """cycles/s and the roofline of one verify width's step: the launch
+    (grouped kernel + argmax reduction) timed with HIP events on its stream."""
+    avg = float(np.mean(launch_ms))
+    g = metrics.gbps(step_bytes, avg)
+    return {"ms_per_step": round(ms_step, 4), "cycles_per_s": round(1000.0 / ms_step, 2),
+            "weight_GBps": round(metrics.gbps(step_bytes, ms_step), 1),
+            "roofline": {"bound": "hbm", "achieved": round(g, 1), "peak": PEAK_GBPS, "unit": "GB/s",
+                         "frac": round(g / PEAK_GBPS, 4), "avg_launch_ms": round(avg, 4),
+                         "median_launch_ms": round(float(np.median(launch_ms)), 4),
+                         "min_launch_ms": round(float(min(launch_ms)), 4)}}
 
 
 def device_info(torch):
@@ -575,6 +620,25 @@ def graph_step(torch, w4a16, probs, head, reps):
     for _ in range(reps):
         g.replay()
     e1.record()
+    torch.cuda.synchronize()
+    return {"ms_per_step": round(e0.elapsed_time(e1) / reps, 4), "launches": len(probs) + 2}
+
+
+def plain_launch_step(torch, w4a16, probs, head, stream, reps):
+    """One step as 256 matmul calls plus the lm_head call, each a separate
+    launch issued from the host on one stream (no graph)."""
+    def one():
+        for tw, _, x, y in probs:
+            w4a16.matmul_tiled(tw, x, out=y, stream=stream)
+        head(stream)
+    for _ in range(3):
+        one()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        one()
+    e1.record(stream)
     torch.cuda.synchronize()
     return {"ms_per_step": round(e0.elapsed_time(e1) / reps, 4), "launches": len(probs) + 2}
 

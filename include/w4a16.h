@@ -372,6 +372,17 @@ w4a16_status w4a16_draft_union(const int32_t* base_ids, int32_t n_base, const in
 w4a16_status w4a16_stream_read(const void* src, size_t bytes, uint32_t* sink, int32_t workgroups,
                                hipStream_t stream);
 
+/* Measurement helper (not a step of the path): replaces the planner's tile
+ * choice for subsequent calls in this process, of single launches (batch 0)
+ * or grouped launches (batch 1), by spec = "split,rt,waves" or
+ * "shared,rt,waves" (rt 1, 2 or 4; waves 1-8, or 1-16 for shared workgroups
+ * of one tile) or "run,tiles,waves" (tiles per wave 1-16, waves 1-16);
+ * NULL or "" restores the planner's choice.  The environment variables
+ * W4A16_TILE and W4A16_BATCH_TILE, read once per process, set the initial
+ * overrides.  Results stay within the tolerance whatever the tiling.
+ * W4A16_ERR_BAD_SHAPE for a batch value or spec that does not parse. */
+w4a16_status w4a16_set_tile(int32_t batch, const char* spec);
+
 /* Selects the kernel variant for subsequent calls in this process (initially
  * taken from the environment variable W4A16_VARIANT = auto|dot|mfma). */
 w4a16_status w4a16_set_variant(int32_t variant);

@@ -47,6 +47,8 @@ def load_library():
         lib.w4a16_head_gather_noalloc.restype = i32
         lib.w4a16_workspace_bytes.argtypes = [i64, i32]
         lib.w4a16_workspace_bytes.restype = sz
+        lib.w4a16_set_tile.argtypes = [i32, ctypes.c_char_p]
+        lib.w4a16_set_tile.restype = i32
         lib.w4a16_set_variant.argtypes = [i32]
         lib.w4a16_set_variant.restype = i32
         lib.w4a16_get_variant.argtypes = []
@@ -103,6 +105,14 @@ def set_variant(name: str) -> None:
     s = load_library().w4a16_set_variant(VARIANTS[name])
     if s:
         raise W4A16Error(s, "set_variant")
+
+
+def set_tile(spec: str | None, batch: bool = False) -> None:
+    """Measurement helper: force the tiling of later single (or grouped)
+    launches, e.g. "split,1,8"; None restores the planner's choice."""
+    s = load_library().w4a16_set_tile(1 if batch else 0, None if spec is None else spec.encode())
+    if s:
+        raise W4A16Error(s, "set_tile")
 
 
 def get_variant() -> str:

@@ -510,6 +510,11 @@ w4a16_status w4a16_draft_union(const int32_t* base_ids, int32_t n_base, const in
              : W4A16_ERR_HIP;
 }
 
+w4a16_status w4a16_set_tile(int32_t batch, const char* spec) {
+  if (batch != 0 && batch != 1) return W4A16_ERR_BAD_SHAPE;
+  return w4a16::set_tile_override(batch == 1, spec) ? W4A16_OK : W4A16_ERR_BAD_SHAPE;
+}
+
 w4a16_status w4a16_set_variant(int32_t variant) {
   if (variant != W4A16_VARIANT_AUTO && variant != W4A16_VARIANT_DOT && variant != W4A16_VARIANT_MFMA)
     return W4A16_ERR_BAD_VARIANT;

@@ -77,9 +77,12 @@ struct Plan {
 // 1-16 for shared workgroups of one tile per wave), or "run,tiles,waves"
 // (tiles per wave 1-16, waves 1-16).
 bool parse_tile(const char* text, Tile* t);
-// Replaces *t by the process's measurement override, if its environment set
-// one (W4A16_BATCH_TILE for grouped launches, else W4A16_TILE; read once).
+// Replaces *t by the measurement override of grouped (batch) or single
+// launches, if one is set: initially from W4A16_BATCH_TILE / W4A16_TILE
+// (read once per process), then by set_tile_override ("" or null: none;
+// false for a spec that does not parse).
 bool tile_override(bool batch, Tile* t);
+bool set_tile_override(bool batch, const char* spec);
 
 // Fill the tiling fields of `a` and return the launch plan.
 Plan plan_mfma(GemvArgs& a, int T, int cus);  // default matrix-core tiling of one launch (cus: CUs of the device)

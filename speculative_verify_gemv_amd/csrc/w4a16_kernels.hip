@@ -1,6 +1,8 @@
 // Planning, dispatch and the non-template kernels of libw4a16 (gfx950).
 // The kernel templates live in w4a16_device.h; w4a16_kernels_tt.hip
 // instantiates launch_t<TT> once per activation-row count.
+#include <mutex>
+
 #include "w4a16_device.h"
 
 namespace w4a16 {
@@ -283,21 +285,39 @@ Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel, bool batch)
   return p;
 }
 
-// The measurement overrides W4A16_TILE (single launches) and
-// W4A16_BATCH_TILE (grouped launches), read once per process.
+// The measurement overrides of the tile choice: one for single launches,
+// one for grouped launches, each packed into one word (0: none) so that
+// plans read them without a lock.  Set from W4A16_TILE / W4A16_BATCH_TILE
+// once per process, and by set_tile_override (w4a16_set_tile).
+namespace {
+uint32_t pack_tile(const Tile& t) { return 1u | (uint32_t)t.shape << 1 | (uint32_t)t.rt << 4 | (uint32_t)t.nw << 10; }
+Tile unpack_tile(uint32_t w) { return Tile{(int)(w >> 1 & 7), (int)(w >> 4 & 63), (int)(w >> 10 & 63)}; }
+std::atomic<uint32_t> g_tile_override[2];
+std::once_flag g_tile_env_once;
+void read_tile_env() {
+  Tile t;
+  if (parse_tile(std::getenv("W4A16_TILE"), &t)) g_tile_override[0].store(pack_tile(t));
+  if (parse_tile(std::getenv("W4A16_BATCH_TILE"), &t)) g_tile_override[1].store(pack_tile(t));
+}
+}  // namespace
+
 bool tile_override(bool batch, Tile* t) {
-  struct Env {
-    bool single_ok, batch_ok;
-    Tile single, batch;
-  };
-  static const Env env = [] {
-    Env e{};
-    e.single_ok = parse_tile(std::getenv("W4A16_TILE"), &e.single);
-    e.batch_ok = parse_tile(std::getenv("W4A16_BATCH_TILE"), &e.batch);
-    return e;
-  }();
-  if (batch ? !env.batch_ok : !env.single_ok) return false;
-  *t = batch ? env.batch : env.single;
+  std::call_once(g_tile_env_once, read_tile_env);
+  const uint32_t w = g_tile_override[batch ? 1 : 0].load(std::memory_order_relaxed);
+  if (!w) return false;
+  *t = unpack_tile(w);
+  return true;
+}
+
+bool set_tile_override(bool batch, const char* spec) {
+  std::call_once(g_tile_env_once, read_tile_env);
+  if (!spec || !*spec) {
+    g_tile_override[batch ? 1 : 0].store(0);
+    return true;
+  }
+  Tile t;
+  if (!parse_tile(spec, &t)) return false;
+  g_tile_override[batch ? 1 : 0].store(pack_tile(t));
   return true;
 }
 

@@ -310,3 +310,17 @@ def test_head_gather_noalloc_limits(lib):
     assert call(n_ids=262145, n_rows=300000, T=16, am=None) in (UNSUP, HIP)  # no argmax: no scratch used
     assert call(n_ids=262144, n_rows=300000, T=16, am=A) in (UNSUP, HIP)     # exactly the limit
     assert call(am=A) in (UNSUP, HIP)                                       # no workspace needed
+
+
+def test_tile_override_parsing(lib):
+    """The measurement tile override: bad specs and batch values are rejected,
+    valid ones accepted, NULL or "" restores the planner's choice."""
+    f = lib.w4a16_set_tile
+    f.argtypes = [ctypes.c_int32, ctypes.c_char_p]
+    assert f(2, b"split,1,8") == SHAPE
+    for spec in (b"split,3,8", b"split,1,9", b"run,0,4", b"run,17,4", b"shared,1,17", b"bogus,1,1", b"split,1"):
+        assert f(0, spec) == SHAPE, spec
+    for batch in (0, 1):
+        for spec in (b"split,1,8", b"shared,4,2", b"run,16,16"):
+            assert f(batch, spec) == OK, spec
+        assert f(batch, b"") == OK and f(batch, None) == OK

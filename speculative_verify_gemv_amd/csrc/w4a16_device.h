@@ -141,19 +141,20 @@ __device__ __forceinline__ void st_partial(int2* p, float v, int id) {
 }
 
 // v_cvt_off_f32_i4 on bits 0-3 of byte B of v: the signed nibble n as n / 16.
-// Written out so that every nibble costs one instruction (the SDWA byte
-// select); left to itself the compiler shifts first for some of them.
+// The byte is masked out so that the compiler folds its selection into the
+// conversion (an SDWA byte select: one instruction per nibble).  No inline
+// assembly here or in the other level helpers: the hazard checks that keep
+// VALU work clear of in-flight matrix-core results cannot see into it.
 template <int B>
 __device__ __forceinline__ float nibble_f32(unsigned v) {
-  float r;
-  if constexpr (B == 0) asm("v_cvt_off_f32_i4_e32 %0, %1" : "=v"(r) : "v"(v));
-  if constexpr (B == 1)
-    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_1" : "=v"(r) : "v"(v));
-  if constexpr (B == 2)
-    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_2" : "=v"(r) : "v"(v));
-  if constexpr (B == 3)
-    asm("v_cvt_off_f32_i4_sdwa %0, %1 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:BYTE_3" : "=v"(r) : "v"(v));
-  return r;
+  return __builtin_amdgcn_cvt_off_f32_i4(B == 3 ? v >> 24 : (v >> (8 * B)) & 0xFFu);
+}
+
+// The value of x, opaque to the optimiser (no instruction): keeps a shifted
+// word from being merged into later shifts, and a constant in a register.
+__device__ __forceinline__ unsigned opaque_v(unsigned x) {
+  asm("" : "+v"(x));
+  return x;
 }
 
 // The bf16 pair (lo, hi) made of the top halves of two floats.
@@ -164,7 +165,7 @@ __device__ __forceinline__ unsigned bf16_pair(float lo, float hi) {
 // Eight exact bf16 levels (q - 8) / 16 of one word, in k order.
 __device__ __forceinline__ u4_t levels8(unsigned w) {
   const unsigned e = w ^ 0x88888888u;  // even k in bits 0-3 of each byte
-  const unsigned o = e >> 4;           // odd k
+  const unsigned o = opaque_v(e >> 4);  // odd k
   return u4_t{bf16_pair(nibble_f32<0>(e), nibble_f32<0>(o)), bf16_pair(nibble_f32<1>(e), nibble_f32<1>(o)),
               bf16_pair(nibble_f32<2>(e), nibble_f32<2>(o)), bf16_pair(nibble_f32<3>(e), nibble_f32<3>(o))};
 }
@@ -175,11 +176,17 @@ __device__ __forceinline__ unsigned as_u32(V h) {
   return __builtin_bit_cast(unsigned, h);
 }
 
-// (w & m) | c in one VALU operation (v_and_or_b32: one SGPR operand, one VGPR).
+// The value of x in a scalar register, opaque to the optimiser.
+__device__ __forceinline__ unsigned opaque_s(unsigned x) {
+  asm("" : "+s"(x));
+  return x;
+}
+
+// (w & m) | c as one v_and_or_b32: with m and c held in registers (opaque
+// to the optimiser, so not folded back into literals, which this VOP3 form
+// cannot take) the compiler selects it over an and and an or.
 __device__ __forceinline__ unsigned and_or(unsigned w, unsigned m, unsigned c) {
-  unsigned r;
-  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(w), "s"(m), "v"(c));
-  return r;
+  return (w & opaque_s(m)) | opaque_v(c);
 }
 
 // Eight exact fp16 levels (q - 8) of one word, slot order 0,4,1,5,2,6,3,7.
@@ -457,6 +464,70 @@ __device__ __forceinline__ bool stage_direct(const GemvArgs& a, unsigned char* x
   return !range_ok(mx, mn);
 }
 
+// A wave's own staging with its activations loaded ahead of its weights:
+// kXPre 16-byte chunks per lane cover T rows of a slice of up to 64 / T
+// groups (e.g. the 8-group share of a split wave at K = 5120 up to T = 8).
+// Loaded first, they complete first, so the wave stages them and starts
+// its first group while its weight loads, issued after them, are still in
+// flight (staged after the weights, the wave would wait for all of them).
+constexpr int kXPre = 16;
+
+// Row of chunk c (c < 1024) of a slice of n8 chunks per row (n8 <= 1024):
+// c * ceil(2^20 / n8) >> 20 is exact while c * n8 < 2^20.
+__device__ __forceinline__ int chunk_row(int c, uint32_t inv) { return (int)(__umul24((uint32_t)c, inv) >> 20); }
+
+// Chunk c = lane + 64 i of x[t][gs*128 .. ge*128) (row t = c / n8, chunk
+// c % n8 of the row) into xr[i].  Whole instructions past the slice are
+// skipped (a uniform test); lanes past its end re-read its last chunk, so
+// that every load the wave issues is unconditional.
+template <int TT>
+__device__ __forceinline__ void prefetch_x(const GemvArgs& a, int gs, int ge, u4_t (&xr)[kXPre]) {
+  const int lane = threadIdx.x & 63;
+  const int n8 = (ge - gs) * (kGroup / 8), total = TT * n8;
+  const uint32_t inv = ((1u << 20) + n8 - 1) / n8;
+  const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)gs * kGroup);
+#pragma unroll
+  for (int i = 0; i < kXPre; ++i) {
+    if (64 * i < total) {
+      const int c = min(lane + 64 * i, total - 1);
+      const int t = chunk_row(c, inv);
+      xr[i] = ld_global(src + t * (a.K / 8) + (c - t * n8));
+    }
+  }
+}
+
+// Stages the prefetched slice into this wave's LDS area (and the ring
+// padding) and returns the level form to run: fp16 when the kernel tries it
+// and every value is exact in it, else the bf16 values as they are.
+template <int TT>
+__device__ __forceinline__ bool stage_wave_regs(const GemvArgs& a, unsigned char* xs, int gs, int ge,
+                                                const u4_t (&xr)[kXPre]) {
+  const int lane = threadIdx.x & 63;
+  const int n8 = (ge - gs) * (kGroup / 8), total = TT * n8;
+  const uint32_t inv = ((1u << 20) + n8 - 1) / n8;
+  const int dst_row = a.xs_stride / 8;
+  u4_t* dst = reinterpret_cast<u4_t*>(xs);
+  bool h = false;
+  if constexpr (TT <= kF16MaxT) {
+    // lanes past the end hold the last chunk again: harmless to the range
+    us2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+#pragma unroll
+    for (int i = 0; i < kXPre; ++i)
+      if (64 * i < total) range8(xr[i], mx, mn);
+    h = __ballot(!range_ok(mx, mn)) == 0;
+  }
+#pragma unroll
+  for (int i = 0; i < kXPre; ++i) {
+    if (64 * i < total) {
+      const int c = lane + 64 * i;
+      const int t = chunk_row(c, inv);
+      if (c < total) dst[t * dst_row + swz(t, c - t * n8)] = h ? convert8_f16(xr[i]) : xr[i];
+    }
+  }
+  zero_pad<TT>(a, xs, ge - gs, lane, 64);
+  return h;
+}
+
 // fp16 staging of a slice for the whole workgroup.  Returns true (uniform)
 // when every value of the slice was exact in fp16: the slice and its ring
 // padding are then staged.  Otherwise nothing usable is staged and the
@@ -706,15 +777,17 @@ __device__ __forceinline__ void slice_tiles(const GemvArgs& a, const u4_t* const
   constexpr int PD = kRing;
 #pragma unroll
   for (int tl = 0; tl < RT; ++tl) {
-    // next tile of the ring (the last tile re-reads its own last group)
+    // the ring runs on into the next tile; the last tile's final cycle
+    // reloads nothing, so that no load is left in flight past the slice
     const u4_t* cpn = cp[tl + 1 < RT ? tl + 1 : tl];
     const uint16_t* spn = sp[tl + 1 < RT ? tl + 1 : tl];
     const bool has_next = tl + 1 < RT;
     float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    for (int fi = 0; fi < np; fi += PD) {
+    auto cycle = [&](int fi, auto reload) {
+      constexpr bool R = decltype(reload)::value;
       const bool last = fi + PD >= np;  // uniform: this cycle prefetches the next tile
       u4_t svn;
-      if constexpr (VS) {
+      if constexpr (VS && R) {
         const uint16_t* base = (last && has_next) ? spn : sp[tl];
         const int gv = last ? (has_next ? sb : sb + fi) : sb + fi + PD;
         svn = ld_global(reinterpret_cast<const u4_t*>(base) + scale_off<LAY>(a, gv));
@@ -732,19 +805,25 @@ __device__ __forceinline__ void slice_tiles(const GemvArgs& a, const u4_t* const
         const f4_t d = group_mfma<H>(xb, gl, q[s]);
 #pragma unroll
         for (int r = 0; r < 4; ++r) accs[r] = fmaf(d[r], sc, accs[r]);
-        // reload this slot with the group PD positions ahead
-        const int tgt = gl + PD;
-        const bool nxt = tgt >= np;
-        const u4_t* cpl = (nxt && has_next) ? cpn : cp[tl];
-        const int gg = sb + (nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1));
-        if constexpr (!VS) sq[s] = ld_global(((nxt && has_next) ? spn : sp[tl]) + gg);
-        q[s] = load_codes<LAY>(cpl + code_off<LAY>(a, gg));
-        // keep this slot's reload here: sunk to the end of the loop, the
-        // reloads would make every iteration wait for the whole ring
-        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (R) {
+          // reload this slot with the group PD positions ahead
+          const int tgt = gl + PD;
+          const bool nxt = tgt >= np;
+          const u4_t* cpl = (nxt && has_next) ? cpn : cp[tl];
+          const int gg = sb + (nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1));
+          if constexpr (!VS) sq[s] = ld_global(((nxt && has_next) ? spn : sp[tl]) + gg);
+          q[s] = load_codes<LAY>(cpl + code_off<LAY>(a, gg));
+          // keep this slot's reload here: sunk to the end of the loop, the
+          // reloads would make every iteration wait for the whole ring
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
-      if constexpr (VS) sv = svn;
-    }
+      if constexpr (VS && R) sv = svn;
+    };
+    const int reloading = has_next ? np : np - PD;  // cycles that reload their slots
+    int fi = 0;
+    for (; fi < reloading; fi += PD) cycle(fi, std::true_type{});
+    if (!has_next) cycle(fi, std::false_type{});
     // fold this tile's slice sum, undoing the level form's power of two
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[tl][r] += accs[r] * fold_scale<H>();
@@ -797,43 +876,69 @@ __device__ __forceinline__ void exact_slice(const GemvArgs& a, const u4_t* const
 // VS: scales are read eight groups (16 bytes) per load (needs G % 8 == 0,
 // 16-byte aligned scale rows and g_begin % 8 == 0); otherwise one 2-byte
 // load per group.
-template <int TT, int RT, bool VS, bool SHARED, int LAY>
-__device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* const (&cp)[RT],
-                                             const uint16_t* const (&sp)[RT], unsigned char* xs, int g_begin,
-                                             int g_end, int trow, int kq, float (&acc)[RT][4]) {
+template <int TT, int RT, bool VS, bool SHARED, int LAY, bool PRE>
+__device__ __forceinline__ void stream_slice(const GemvArgs& a, const u4_t* const (&cp)[RT],
+                                             const uint16_t* const (&sp)[RT], unsigned char* xs, int sb, int se,
+                                             bool first, int trow, int kq, float (&acc)[RT][4]) {
   constexpr int PD = kRing;
   u4_t q[PD];
   unsigned short sq[PD];
   u4_t sv;
-  for (int sb = g_begin; sb < g_end; sb += a.sk) {
-    const int se = min(g_end, sb + a.sk);
-    const int n = se - sb;                  // groups of this slice
-    const int np = (n + PD - 1) / PD * PD;  // padded to whole ring cycles
-    // Ring prologue (tile 0 of the slice), issued before the activations are
-    // staged so that the weight latency overlaps the activation round trip.
-    if constexpr (VS) sv = ld_global(reinterpret_cast<const u4_t*>(sp[0]) + scale_off<LAY>(a, sb));
+  const int n = se - sb;                  // groups of this slice
+  const int np = (n + PD - 1) / PD * PD;  // padded to whole ring cycles
+  // PRE: the wave's activations are loaded first, into registers
+  u4_t xr[kXPre];
+  if constexpr (PRE) prefetch_x<TT>(a, sb, se, xr);
+  // Ring prologue (tile 0 of the slice), issued before the activations are
+  // staged so that the weight latency overlaps the activation round trip.
+  if constexpr (VS) sv = ld_global(reinterpret_cast<const u4_t*>(sp[0]) + scale_off<LAY>(a, sb));
 #pragma unroll
-    for (int s = 0; s < PD; ++s) {
-      const int g = sb + min(s, n - 1);
-      if constexpr (!VS) sq[s] = ld_global(sp[0] + g);
-      q[s] = load_codes<LAY>(cp[0] + code_off<LAY>(a, g));
-      __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
-    }
-    if constexpr (SHARED)
-      if (sb != g_begin) __syncthreads();  // every wave is done with the previous slice
-    const bool h = stage_slice<TT, SHARED>(a, xs, sb, se);
-    const unsigned char* xb[4];
-    lane_chunks(a, xs, trow, kq, xb);
-    if constexpr (TT <= kF16MaxT) {
-      if (h)
-        slice_tiles<TT, RT, VS, LAY, true>(a, cp, sp, xb, sb, n, np, q, sq, sv, acc);
-      else
-        exact_slice<TT, RT, LAY>(a, cp, sp, xb, sb, n, acc);
-    } else {
-      (void)h;
-      slice_tiles<TT, RT, VS, LAY, false>(a, cp, sp, xb, sb, n, np, q, sq, sv, acc);
+  for (int s = 0; s < PD; ++s) {
+    const int g = sb + min(s, n - 1);
+    if constexpr (!VS) sq[s] = ld_global(sp[0] + g);
+    q[s] = load_codes<LAY>(cp[0] + code_off<LAY>(a, g));
+    __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
+  }
+  if constexpr (SHARED)
+    if (!first) __syncthreads();  // every wave is done with the previous slice
+  bool h;
+  if constexpr (PRE) {
+    lds_fence();
+    h = stage_wave_regs<TT>(a, xs, sb, se, xr);
+    lds_fence();
+  } else {
+    h = stage_slice<TT, SHARED>(a, xs, sb, se);
+  }
+  const unsigned char* xb[4];
+  lane_chunks(a, xs, trow, kq, xb);
+  if constexpr (TT <= kF16MaxT) {
+    if (h)
+      slice_tiles<TT, RT, VS, LAY, true>(a, cp, sp, xb, sb, n, np, q, sq, sv, acc);
+    else
+      exact_slice<TT, RT, LAY>(a, cp, sp, xb, sb, n, acc);
+  } else {
+    (void)h;
+    slice_tiles<TT, RT, VS, LAY, false>(a, cp, sp, xb, sb, n, np, q, sq, sv, acc);
+  }
+}
+
+// The slices of [g_begin, g_end) in turn.  A wave staging its own range (not
+// SHARED) in one slice that fits kXPre loads per lane takes the prefetching
+// form: its activations are loaded ahead of its weights and staged as soon
+// as they land, while the weights are still in flight.
+template <int TT, int RT, bool VS, bool SHARED, int LAY>
+__device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* const (&cp)[RT],
+                                             const uint16_t* const (&sp)[RT], unsigned char* xs, int g_begin,
+                                             int g_end, int trow, int kq, float (&acc)[RT][4]) {
+  if constexpr (!SHARED && TT <= 8) {
+    if (g_end - g_begin <= a.sk && TT * (g_end - g_begin) * (kGroup / 8) <= kXPre * 64) {  // uniform
+      stream_slice<TT, RT, VS, SHARED, LAY, true>(a, cp, sp, xs, g_begin, g_end, true, trow, kq, acc);
+      return;
     }
   }
+  for (int sb = g_begin; sb < g_end; sb += a.sk)
+    stream_slice<TT, RT, VS, SHARED, LAY, false>(a, cp, sp, xs, sb, min(g_end, sb + a.sk), sb == g_begin, trow,
+                                                 kq, acc);
 }
 
 // Code and scale pointers of the RT tiles starting at output row row0 for

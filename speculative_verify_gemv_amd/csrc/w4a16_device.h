@@ -470,6 +470,14 @@ __device__ __forceinline__ bool stage_direct(const GemvArgs& a, unsigned char* x
 // Loaded first, they complete first, so the wave stages them and starts
 // its first group while its weight loads, issued after them, are still in
 // flight (staged after the weights, the wave would wait for all of them).
+// Prefetching waves with more than one activation row stage them before
+// issuing any weight load: their activation loads then no longer queue
+// behind the CU's weight traffic (5,120 x 5,120 at T = 4: 9.0 us against
+// 9.9).  A single row is cheaper to wait for behind the weights (8.0 us
+// against 8.8 staged first).
+template <int TT>
+constexpr bool stage_first() { return TT >= 2; }
+
 constexpr int kXPre = 16;
 
 // Row of chunk c (c < 1024) of a slice of n8 chunks per row (n8 <= 1024):
@@ -886,27 +894,33 @@ __device__ __forceinline__ void stream_slice(const GemvArgs& a, const u4_t* cons
   u4_t sv;
   const int n = se - sb;                  // groups of this slice
   const int np = (n + PD - 1) / PD * PD;  // padded to whole ring cycles
-  // PRE: the wave's activations are loaded first, into registers
-  u4_t xr[kXPre];
-  if constexpr (PRE) prefetch_x<TT>(a, sb, se, xr);
-  // Ring prologue (tile 0 of the slice), issued before the activations are
-  // staged so that the weight latency overlaps the activation round trip.
-  if constexpr (VS) sv = ld_global(reinterpret_cast<const u4_t*>(sp[0]) + scale_off<LAY>(a, sb));
+  // Ring prologue (tile 0 of the slice): slot order, as the loop reloads them.
+  auto prologue = [&]() {
+    if constexpr (VS) sv = ld_global(reinterpret_cast<const u4_t*>(sp[0]) + scale_off<LAY>(a, sb));
 #pragma unroll
-  for (int s = 0; s < PD; ++s) {
-    const int g = sb + min(s, n - 1);
-    if constexpr (!VS) sq[s] = ld_global(sp[0] + g);
-    q[s] = load_codes<LAY>(cp[0] + code_off<LAY>(a, g));
-    __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
-  }
-  if constexpr (SHARED)
-    if (!first) __syncthreads();  // every wave is done with the previous slice
+    for (int s = 0; s < PD; ++s) {
+      const int g = sb + min(s, n - 1);
+      if constexpr (!VS) sq[s] = ld_global(sp[0] + g);
+      q[s] = load_codes<LAY>(cp[0] + code_off<LAY>(a, g));
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
   bool h;
   if constexpr (PRE) {
+    // the wave's activations are loaded first, into registers
+    u4_t xr[kXPre];
+    prefetch_x<TT>(a, sb, se, xr);
+    if constexpr (!stage_first<TT>()) prologue();
     lds_fence();
     h = stage_wave_regs<TT>(a, xs, sb, se, xr);
     lds_fence();
+    if constexpr (stage_first<TT>()) prologue();
   } else {
+    // issued before the activations are staged, so that the weight latency
+    // overlaps the activation round trip
+    prologue();
+    if constexpr (SHARED)
+      if (!first) __syncthreads();  // every wave is done with the previous slice
     h = stage_slice<TT, SHARED>(a, xs, sb, se);
   }
   const unsigned char* xb[4];

@@ -371,7 +371,9 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
       // the 64 workgroups of 4 x 16; 131,072 rows: 58 against 89)
       t = cdiv(tiles, 64) * 10 >= 9 * ncu ? Tile{kRun, 4, 16} : Tile{kRun, 2, 8};
     }
-  } else if (tiles >= 8192)
+  } else if (T == 1 && tiles >= 1024 && tiles < 4096 && !a.partial && !a.row_ids)
+    t = Tile{kSplit, 1, 4};  // a plain matmul (34,816 x 5,120: 20.3 us against 23.8 for shared workgroups of 4 waves)
+  else if (tiles >= 8192)
     t = Tile{kShared, 4, 8};
   else if (tiles >= 4096)
     t = Tile{kShared, 2, 8};
@@ -383,8 +385,14 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
     t = Tile{kShared, 1, 4};
   else if (T >= 2 && tiles >= 3 * ncu)  // still three quarters of a round of 4-wave workgroups,
     t = Tile{kShared, 1, 4};             // each staging once for 4 tiles (12,288 x 5,120 at T = 8: 16 us vs 23)
-  else if (4 * tiles >= 5 * ncu)  // split workgroups of 2 tiles: 5,120 x 17,408 row-major 44 us vs 65 at
-    t = Tile{kSplit, 2, 8};       // T = 8, 19 vs 21 at T = 1; tiled 34 vs 40 at T = 8, 16.0 vs 16.8 at T = 1
+  else if (4 * tiles >= 5 * ncu)
+    // Up to 64 groups of K, 8-wave split workgroups of one tile, each wave
+    // staging and streaming 8 groups (5,120 x 5,120 tiled at T = 1: 7.6 us
+    // against 8.0 for 2 tiles per workgroup; 9.0 against 9.9 at T = 4).
+    // Longer K: at T = 1 four waves of one tile (5,120 x 17,408: 15.4 us
+    // against 16.8), above it split workgroups of 2 tiles (row-major 44 us
+    // against 65 for shared workgroups at T = 8; tiled 25 against 27 at T = 4)
+    t = a.G <= 64 ? Tile{kSplit, 1, 8} : T == 1 ? Tile{kSplit, 1, 4} : Tile{kSplit, 2, 8};
   else
     t = Tile{kSplit, 1, (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(12LL * std::max(cus, 1), tiles)))};
   tile_override(false, &t);

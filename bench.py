@@ -68,6 +68,8 @@ def parse():
     ap.add_argument("--pmc-pass", action="store_true", help="one untimed pass for counter collection")
     ap.add_argument("--variants-pass", action="store_true",
                     help="one untimed launch per shape, T and kernel variant (dot / matrix core), for counters")
+    ap.add_argument("--singles-pass", metavar="ORDER_JSON",
+                    help="run only the single launches and write their launch order here (for a kernel trace)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
     return ap.parse_args()
 
@@ -171,6 +173,14 @@ def main():
 
     if args.variants_pass:
         variants_pass(torch, w4a16, weights, head_p, head_s, stream)
+        return
+
+    if args.singles_pass:
+        single_launches(torch, w4a16, weights, head_p, head_s, head_tw, stream)
+        read_floors(torch, w4a16, stream)
+        with open(args.singles_pass, "w") as f:
+            json.dump(LAUNCH_ORDER, f, indent=1)
+        log(f"singles pass done: launch order of {len(LAUNCH_ORDER)} workloads in {args.singles_pass}")
         return
 
     if args.pmc_pass:
@@ -392,12 +402,19 @@ def device_info(torch):
     return info
 
 
-def time_rotating(torch, fns, stream, rounds=4):
+# (workload, untimed calls, timed calls, dispatches per call, weight bytes)
+# of every time_rotating call in order: maps a kernel trace back to them
+LAUNCH_ORDER = []
+
+
+def time_rotating(torch, fns, stream, rounds=4, tag=None, dispatches=1, nbytes=0):
     """Average µs per call of fns called round-robin (distinct weight copies,
     so that the 256 MB Infinity Cache cannot serve a repeat), after one
     untimed round per copy and enough calls to leave the clock ramp."""
     n = len(fns)
     warm = max(3 * n, 30)
+    LAUNCH_ORDER.append({"workload": tag, "untimed": warm, "timed": max(rounds * n, 40), "dispatches": dispatches,
+                         "weight_bytes": nbytes})
     for i in range(warm):
         fns[i % n]()
     torch.cuda.synchronize()
@@ -424,7 +441,8 @@ def single_launches(torch, w4a16, weights, head_p, head_s, head_tw, stream):
     tw = w4a16.repack_tiled(to_dev(p, torch), to_dev(s, torch))
     x = to_dev(synth.activations(synth.TID_SMALL, 1, synth.SMALL[1]), torch)
     y = torch.empty((1, synth.SMALL[0]), dtype=torch.float32, device="cuda")
-    us = time_rotating(torch, [lambda: w4a16.matmul_tiled(tw, x, out=y, stream=stream)], stream)
+    us = time_rotating(torch, [lambda: w4a16.matmul_tiled(tw, x, out=y, stream=stream)], stream,
+                       tag="small_1024x1024_T1", nbytes=metrics.weight_bytes(*synth.SMALL))
     out["small_1024x1024_T1"] = {"us": round(us, 2),
                                  "weight_GBps": round(metrics.gbps(metrics.weight_bytes(*synth.SMALL), us / 1000), 1)}
     for proj in synth.PROJ_ORDER:
@@ -435,7 +453,7 @@ def single_launches(torch, w4a16, weights, head_p, head_s, head_tw, stream):
             x = to_dev(synth.activations(synth.tid_layer(0, proj), T, K), torch)
             y = torch.empty((T, N), dtype=torch.float32, device="cuda")
             fns = [lambda tw=tw: w4a16.matmul_tiled(tw, x, out=y, stream=stream) for tw in tws]
-            us = time_rotating(torch, fns, stream)
+            us = time_rotating(torch, fns, stream, tag=f"{proj}_T{T}", nbytes=wb)
             out[f"{proj}_T{T}"] = {"us": round(us, 2), "weight_GBps": round(metrics.gbps(wb, us / 1000), 1)}
     hn, hk = synth.LM_HEAD
     head_tw2 = w4a16.repack_tiled(head_p, head_s)  # a second copy: 1.3 GB rotated
@@ -445,7 +463,8 @@ def single_launches(torch, w4a16, weights, head_p, head_s, head_tw, stream):
         ws = torch.empty(w4a16.workspace_bytes(hn, T), dtype=torch.uint8, device="cuda")
         fns = [lambda t=t: w4a16.head_gather_tiled(t, x, scores=True, argmax=True, out=y, workspace=ws, stream=stream)
                for t in (head_tw, head_tw2)]
-        us = time_rotating(torch, fns, stream)
+        us = time_rotating(torch, fns, stream, tag=f"lm_head_argmax_T{T}", dispatches=2,
+                           nbytes=metrics.weight_bytes(hn, hk))
         out[f"lm_head_argmax_T{T}"] = {"us": round(us, 2),
                                        "weight_GBps": round(metrics.gbps(metrics.weight_bytes(hn, hk), us / 1000), 1)}
     ids = [to_dev(synth.distinct_ids(synth.RID_DRAFT + i, synth.DRAFT_IDS, hn), torch) for i in range(8)]
@@ -456,12 +475,14 @@ def single_launches(torch, w4a16, weights, head_p, head_s, head_tw, stream):
     # 128-byte lines), eight id sets rotated; and from the tiled head
     fns = [lambda r=r: w4a16.head_gather(head_p, head_s, x, row_ids=r, scores=True, argmax=True, out=y, workspace=ws,
                                          stream=stream) for r in ids]
-    us = time_rotating(torch, fns, stream)
+    us = time_rotating(torch, fns, stream, tag="draft_head_32768_argmax_T1", dispatches=2,
+                       nbytes=metrics.weight_bytes(synth.DRAFT_IDS, hk))
     out["draft_head_32768_argmax_T1"] = {"us": round(us, 2), "weight_GBps": round(
         metrics.gbps(metrics.weight_bytes(synth.DRAFT_IDS, hk), us / 1000), 1), "layout": "row-major head"}
     fns = [lambda t=t, r=r: w4a16.head_gather_tiled(t, x, row_ids=r, scores=True, argmax=True, out=y, workspace=ws,
                                                     stream=stream) for t in (head_tw, head_tw2) for r in ids[:4]]
-    us = time_rotating(torch, fns, stream)
+    us = time_rotating(torch, fns, stream, tag="draft_head_32768_argmax_T1_tiled_head", dispatches=2,
+                       nbytes=metrics.weight_bytes(synth.DRAFT_IDS, hk))
     out["draft_head_32768_argmax_T1_tiled_head"] = {"us": round(us, 2), "weight_GBps": round(
         metrics.gbps(metrics.weight_bytes(synth.DRAFT_IDS, hk), us / 1000), 1), "layout": "tiled head"}
     # the same draft head repacked once into its own tiled matrix (ascending
@@ -470,7 +491,8 @@ def single_launches(torch, w4a16, weights, head_p, head_s, head_tw, stream):
     compact = [w4a16.repack_tiled_rows(head_p, head_s, sid[0]) for _ in range(12)]
     fns = [lambda t=t: w4a16.head_gather_tiled(t, x, scores=True, argmax=True, out=y, workspace=ws, stream=stream)
            for t in compact]
-    us = time_rotating(torch, fns, stream)
+    us = time_rotating(torch, fns, stream, tag="draft_head_compact_32768_argmax_T1", dispatches=2,
+                       nbytes=metrics.weight_bytes(synth.DRAFT_IDS, hk))
     out["draft_head_compact_32768_argmax_T1"] = {"us": round(us, 2), "weight_GBps": round(
         metrics.gbps(metrics.weight_bytes(synth.DRAFT_IDS, hk), us / 1000), 1)}
     del head_tw2, compact
@@ -543,6 +565,30 @@ def variants_pass(torch, w4a16, weights, head_p, head_s, stream):
     finally:
         w4a16.set_variant("auto")
     log("variants pass done: T = 1, 4, 8 x {dot, matrix core} x {qkv, o, gate_up, down, lm_head}")
+
+
+def read_floors(torch, w4a16, stream):
+    """For a kernel trace: the library's streaming-read kernel over buffers of
+    each single-launch workload's weight bytes (8 workgroups per CU, copies
+    rotated past the Infinity Cache), the floor of one launch of that size."""
+    hn, hk = synth.LM_HEAD
+    sizes = [("small_1024x1024", metrics.weight_bytes(*synth.SMALL))]
+    sizes += [(proj, metrics.weight_bytes(*synth.PROJECTIONS[proj])) for proj in synth.PROJ_ORDER]
+    sizes += [("draft_head_32768", metrics.weight_bytes(synth.DRAFT_IDS, hk)), ("lm_head", metrics.weight_bytes(hn, hk))]
+    wg = 8 * torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(wg * 256, dtype=torch.int32, device="cuda")
+    out = {}
+    for name, nbytes in sizes:
+        n = (nbytes + 15) // 16 * 16
+        copies = 2 if n > (128 << 20) else 20
+        bufs = [torch.ones(n, dtype=torch.uint8, device="cuda") for _ in range(copies)]
+        fns = [lambda b=b: w4a16.stream_read(b, sink, wg, stream=stream) for b in bufs]
+        us = time_rotating(torch, fns, stream, tag=f"read_floor_{name}", nbytes=n)
+        out[name] = round(us, 2)
+        del bufs, fns
+        torch.cuda.empty_cache()
+    log(f"read floors (event-timed, us): {out}")
+    return out
 
 
 def read_ceiling(torch, w4a16, stream, gib=4, reps=10):

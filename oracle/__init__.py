@@ -12,7 +12,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "liboracle.so")
+# ORACLE_LIB: an instrumented build of the same source (sanitizer runs)
+_LIB_PATH = os.environ.get("ORACLE_LIB") or os.path.join(HERE, "liboracle.so")
 _lib = None
 
 

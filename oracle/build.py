@@ -10,17 +10,18 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB = os.path.join(HERE, "liboracle.so")
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, cc: str = "gcc", extra=(), lib: str = LIB) -> str:
+    """extra flags and another output place an instrumented build beside this one."""
     src = os.path.join(HERE, "oracle.c")
-    tmp = LIB + ".tmp"
+    tmp = lib + ".tmp"
     # -ffp-contract=off: no fused multiply-adds, every operation rounds as written.
-    cmd = ["gcc", "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-Wall", "-Wextra",
+    cmd = [cc, *extra, "-O2", "-std=c11", "-ffp-contract=off", "-fPIC", "-shared", "-Wall", "-Wextra",
            "-o", tmp, src, "-lm", "-lpthread"]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -14,7 +14,8 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libw4a16.so")
+# W4A16_LIB: an instrumented build of the same sources (host sanitizer runs)
+LIB_PATH = os.environ.get("W4A16_LIB") or os.path.join(HERE, "libw4a16.so")
 
 GROUP = 128
 MAX_T = 16

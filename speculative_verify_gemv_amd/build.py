@@ -40,21 +40,24 @@ def _run(cmd, verbose):
     return r.returncode, err
 
 
-def _units():
+def _units(obj_dir=OBJ_DIR):
     """(source, object, extra flags) of every translation unit."""
-    units = [(os.path.join(CSRC, "w4a16_kernels_tt.hip"), os.path.join(OBJ_DIR, f"kernels_t{t}.o"),
+    units = [(os.path.join(CSRC, "w4a16_kernels_tt.hip"), os.path.join(obj_dir, f"kernels_t{t}.o"),
               [f"-DW4A16_TT={t}"]) for t in range(1, MAX_T + 1)]
-    units.append((os.path.join(CSRC, "w4a16_kernels.hip"), os.path.join(OBJ_DIR, "kernels.o"), []))
-    units.append((os.path.join(CSRC, "w4a16_epilogue.hip"), os.path.join(OBJ_DIR, "epilogue.o"), []))
-    units.append((os.path.join(CSRC, "w4a16_api.hip"), os.path.join(OBJ_DIR, "api.o"), []))
+    units.append((os.path.join(CSRC, "w4a16_kernels.hip"), os.path.join(obj_dir, "kernels.o"), []))
+    units.append((os.path.join(CSRC, "w4a16_epilogue.hip"), os.path.join(obj_dir, "epilogue.o"), []))
+    units.append((os.path.join(CSRC, "w4a16_api.hip"), os.path.join(obj_dir, "api.o"), []))
     return units
 
 
-def build(verbose: bool = False, extra=()) -> str:
-    os.makedirs(OBJ_DIR, exist_ok=True)
+def build(verbose: bool = False, extra=(), link_extra=(), lib: str = LIB, obj_dir: str = OBJ_DIR) -> str:
+    """Builds the library; extra / link_extra are added to every compile / to
+    the link, lib and obj_dir place another build (an instrumented one) beside
+    the product's."""
+    os.makedirs(obj_dir, exist_ok=True)
     inc = ["-I", os.path.join(ROOT, "include")]
     jobs = []
-    for src, obj, flags in _units():
+    for src, obj, flags in _units(obj_dir):
         jobs.append([hipcc(), *HIPCC_FLAGS, *extra, *flags, *inc, "-c", "-o", obj, src])
     workers = max(1, min(len(jobs), os.cpu_count() or 1, 16))
     with ThreadPoolExecutor(max_workers=workers) as pool:
@@ -68,14 +71,14 @@ def build(verbose: bool = False, extra=()) -> str:
         for rc, e in results:
             if e.strip():
                 sys.stderr.write(e + "\n")
-    tmp = LIB + ".tmp"
-    rc, err = _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp,
-                    *[obj for _, obj, _ in _units()]], verbose)
+    tmp = lib + ".tmp"
+    rc, err = _run([hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", *link_extra, "-o", tmp,
+                    *[obj for _, obj, _ in _units(obj_dir)]], verbose)
     if rc != 0:
         sys.stderr.write(err + "\n")
         raise RuntimeError("hipcc failed linking libw4a16.so")
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":

@@ -18,7 +18,8 @@ import os
 import numpy as np
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(HERE, "libsynth.so")
+# SYNTH_LIB: an instrumented build of the same source (sanitizer runs)
+_LIB_PATH = os.environ.get("SYNTH_LIB") or os.path.join(HERE, "libsynth.so")
 _lib = None
 
 SEED = 20261202

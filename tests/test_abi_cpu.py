@@ -9,7 +9,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "w4a16.h")
-LIB = os.path.join(ROOT, "speculative_verify_gemv_amd", "libw4a16.so")
+LIB = os.environ.get("W4A16_LIB") or os.path.join(ROOT, "speculative_verify_gemv_amd", "libw4a16.so")
 
 OK, NULLP, SHAPE, ALIGN, WS, UNSUP, HIP, VARIANT, SCRATCH = range(9)
 

@@ -32,9 +32,10 @@
 // a factor 1/16, which is taken back when a tile's sum is folded (a power of
 // two), so the result is the fp32 arithmetic of the unscaled levels.
 //
-// Where the loop is tight (up to kF16MaxT activation rows) those 14
-// operations cost about 4.5% of the bandwidth, so the kernels for those row
-// counts first try a cheaper exact form: fp16 levels, 9 operations per word,
+// Where the loop is tight those 14 operations cost about 4.5% of the
+// bandwidth, so the kernels first try a cheaper exact form (all row counts
+// where a workgroup stages the activations for its waves, up to four rows
+// where each wave stages its own): fp16 levels, 9 operations per word,
 //
 //   (w & 0x000F000F) | 0x6400_6400  is the fp16 pair (1024 + q0, 1024 + q4)
 //   (w & 0x00F000F0) | 0x5400_5400  is the fp16 pair (  64 + q1,   64 + q5)
@@ -96,8 +97,17 @@ constexpr int kRing = 8;        // groups of weight codes in flight per wave
 constexpr int kWaitVmcnt0 = 0x0F70;
 // The bf16 levels are (q - 8) / 16; a tile's sum is multiplied by this.
 constexpr float kLevelScale = 16.0f;
-// Kernels for up to this many activation rows try the fp16 form first.
-constexpr int kF16MaxT = 4;
+// Workgroups that stage activations for all their waves try the fp16 form
+// first at every row count (16,384 rows of the decode pass at T = 8: 72 %
+// of 8 TB/s against 70 % with bf16 levels); a wave that stages its own
+// range converts its share itself, which the fp16 form repays up to four
+// rows only (5,120 x 5,120 split at T = 8: 12.2 us against 9.4).
+constexpr int kF16MaxT = 16;
+constexpr int kF16MaxSplitT = 4;
+template <int TT, bool SHARED>
+constexpr bool tries_f16() {
+  return TT <= (SHARED ? kF16MaxT : kF16MaxSplitT);
+}
 // The fp16 form's activations are x * 2^kDirectE; a tile's sum is
 // multiplied by 2^-kDirectE.
 constexpr int kDirectE = 4;
@@ -357,7 +367,7 @@ __device__ __forceinline__ void stage_x_wave(const GemvArgs& a, unsigned char* x
   }
 }
 
-// ------------------------------------- fp16 staging (up to kF16MaxT rows) ----
+// ------------------------------------------------------------ fp16 staging ----
 //
 // The same staged layout with fp16 values times 2^kDirectE, each chunk's
 // eight values in the fp16 levels' slot order 0,4,1,5,2,6,3,7.
@@ -516,7 +526,7 @@ __device__ __forceinline__ bool stage_wave_regs(const GemvArgs& a, unsigned char
   const int dst_row = a.xs_stride / 8;
   u4_t* dst = reinterpret_cast<u4_t*>(xs);
   bool h = false;
-  if constexpr (TT <= kF16MaxT) {
+  if constexpr (tries_f16<TT, false>()) {
     // lanes past the end hold the last chunk again: harmless to the range
     us2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
 #pragma unroll
@@ -741,21 +751,21 @@ __device__ __forceinline__ void lane_chunks(const GemvArgs& a, const unsigned ch
 
 // Stages the slice [sb, se) of the activations for a workgroup (SHARED) or
 // for this wave alone, and returns which level form runs on it: the fp16
-// form when the kernel tries it (up to kF16MaxT rows) and every value is
+// form when the kernel tries it (tries_f16) and every value is
 // exact in it, else bf16.  Returns after the staged values are visible to
 // every wave that reads them and every load issued before has landed.
 template <int TT, bool SHARED>
 __device__ __forceinline__ bool stage_slice(const GemvArgs& a, unsigned char* xs, int sb, int se) {
   bool h = false;
   if constexpr (SHARED) {
-    if constexpr (TT <= kF16MaxT) h = stage_f16_shared<TT>(a, xs, sb, se);
+    if constexpr (tries_f16<TT, true>()) h = stage_f16_shared<TT>(a, xs, sb, se);
     if (!h) stage_x<TT>(a, reinterpret_cast<__bf16*>(xs), sb, se, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
                         blockDim.x >> 6);
     __syncthreads();
   } else {
     const int lane = threadIdx.x & 63;
     lds_fence();
-    if constexpr (TT <= kF16MaxT) {
+    if constexpr (tries_f16<TT, false>()) {
       u4_t held;
       int held_at = -1;
       h = __ballot(stage_direct<TT>(a, xs, sb, se, lane, 64, 0x7fffffff, held, held_at)) == 0;
@@ -925,7 +935,7 @@ __device__ __forceinline__ void stream_slice(const GemvArgs& a, const u4_t* cons
   }
   const unsigned char* xb[4];
   lane_chunks(a, xs, trow, kq, xb);
-  if constexpr (TT <= kF16MaxT) {
+  if constexpr (tries_f16<TT, SHARED>()) {
     if (h)
       slice_tiles<TT, RT, VS, LAY, true>(a, cp, sp, xb, sb, n, np, q, sq, sv, acc);
     else
@@ -1291,7 +1301,7 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
     bi[r] = -1;
   }
   if (v0 < v_end) {
-    if constexpr (TT <= kF16MaxT) {
+    if constexpr (tries_f16<TT, true>()) {
       if (h)
         run_tiles<TT, LAY, true>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, sp, q, sv, bv, bi);
       else

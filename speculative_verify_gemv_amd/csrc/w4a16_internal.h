@@ -95,7 +95,7 @@ Plan plan_dot(GemvArgs& a, int T);
 Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel, bool batch);
 // Waves of a shared workgroup of one tile per wave: 16 (one workgroup per CU,
 // up to 160 KB of LDS) when T rows of K activations need more than 80 KB,
-// else 4 at T <= 2 and 8 above (MI355X sweeps of the tiled layout).
+// else 4 at T = 1 and 8 above (MI355X sweeps of the tiled layout).
 int shared_waves(int T, int64_t K);
 
 

@@ -34,8 +34,8 @@
 //
 // Where the loop is tight those 14 operations cost about 4.5% of the
 // bandwidth, so the kernels first try a cheaper exact form (all row counts
-// where a workgroup stages the activations for its waves, one row where each
-// wave stages its own): fp16 levels, 9 operations per word,
+// where a workgroup stages the activations for its waves, up to two rows
+// where each wave stages its own): fp16 levels, 9 operations per word,
 //
 //   (w & 0x000F000F) | 0x6400_6400  is the fp16 pair (1024 + q0, 1024 + q4)
 //   (w & 0x00F000F0) | 0x5400_5400  is the fp16 pair (  64 + q1,   64 + q5)
@@ -100,11 +100,12 @@ constexpr float kLevelScale = 16.0f;
 // Workgroups that stage activations for all their waves try the fp16 form
 // first at every row count (the decode pass at T = 8: 72 % of 8 TB/s
 // against 70 % with bf16 levels); a wave that stages its own range converts
-// its share itself, which the fp16 form repays at one row only (5,120 x
-// 5,120 split at T = 4: 8.9 us with bf16 levels against 9.2; at T = 8 9.4
-// against 12.2).
+// its share itself, which the fp16 form repays up to two rows (5,120 x
+// 17,408 split at T = 2: 17.5 us against 20.2 with bf16 levels; 5,120 x
+// 5,120 8.0 against 8.3) but not above (at T = 4 8.9 us with bf16 levels
+// against 9.2, at T = 8 9.4 against 12.2).
 constexpr int kF16MaxT = 16;
-constexpr int kF16MaxSplitT = 1;
+constexpr int kF16MaxSplitT = 2;
 template <int TT, bool SHARED>
 constexpr bool tries_f16() {
   return TT <= (SHARED ? kF16MaxT : kF16MaxSplitT);

@@ -40,7 +40,9 @@
  *     device query).
  *   - No allocation, no synchronisation, no printing, and no state kept
  *     between calls apart from the process-wide variant selection
- *     (w4a16_set_variant).  Outputs must not alias inputs or each other.
+ *     (w4a16_set_variant), the measurement tile override (w4a16_set_tile)
+ *     and the static argmax scratch of w4a16_head_gather_noalloc.  Outputs
+ *     must not alias inputs or each other.
  *   - Thread-safe; calls on different streams may run concurrently.
  *   - Activations should be finite; a non-finite x gives non-finite outputs
  *     for the rows it reaches.
@@ -274,8 +276,8 @@ w4a16_status w4a16_matmul_batch(const void* table_host, const void* table_dev, h
 
 /*
  * The grouped launch with a device workspace for the activations.  No
- * plan needs one: the workgroups copy every problem's bf16 activations
- * straight into LDS (no conversion), so w4a16_batch_workspace_bytes returns
+ * plan needs one: the workgroups stage every problem's activations into LDS
+ * themselves, so w4a16_batch_workspace_bytes returns
  * 0 for every table (and for anything that is not a table), the workspace
  * arguments of w4a16_matmul_batch_ws are ignored (NULL and 0 are fine), and
  * the call is w4a16_matmul_batch.  Kept so that callers written against the

@@ -23,12 +23,15 @@ rate, the verify epilogue, and the CPU oracle's rate on a bounded sample.
 --pmc-pass runs one untimed step after a 1 GiB device copy (the calibration
 kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE), then one body pass alone at
 each of T = 1, 4, 8, 16;
---variants-pass one untimed launch per shape, T and variant.
+--variants-pass [ORDER_JSON] one untimed launch per shape, T and variant
+(writing their launch order when given); --singles-pass ORDER_JSON the
+single launches alone, then the streaming-read floor of each size, writing
+their launch order (trace_summary maps kernel traces and counter passes
+back to either order).
 """
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -46,9 +49,6 @@ from speculative_verify_gemv_amd import metrics  # noqa: E402
 METRIC = "weight GB/s and % of HBM peak at T=1/4/8 (27B-class shapes); decode cycles/s"
 PEAK_GBPS = 8000.0
 WORKLOAD = "decode_weight_pass_64x(qkv,o,gate_up,down)+lm_head_T4"
-KERNEL_SOURCES = [os.path.join(ROOT, "speculative_verify_gemv_amd", "csrc", f)
-                  for f in ("w4a16_device.h", "w4a16_internal.h", "w4a16_kernels.hip", "w4a16_kernels_tt.hip",
-                            "w4a16_api.hip")]
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_body_pass_T4.md")
 COPY_BYTES = 1 << 30
 
@@ -66,8 +66,9 @@ def parse():
     ap.add_argument("--no-singles", action="store_true")
     ap.add_argument("--no-variants", action="store_true")
     ap.add_argument("--pmc-pass", action="store_true", help="one untimed pass for counter collection")
-    ap.add_argument("--variants-pass", action="store_true",
-                    help="one untimed launch per shape, T and kernel variant (dot / matrix core), for counters")
+    ap.add_argument("--variants-pass", nargs="?", const="", default=None, metavar="ORDER_JSON",
+                    help="one untimed launch per shape, T and kernel variant (dot / matrix core), for counters; "
+                         "writes the launch order to ORDER_JSON when given")
     ap.add_argument("--singles-pass", metavar="ORDER_JSON",
                     help="run only the single launches and write their launch order here (for a kernel trace)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0, help="target CPU time of the oracle sample")
@@ -85,19 +86,6 @@ def to_dev(a, torch):
     return t.cuda()
 
 
-def kernel_source_hash():
-    """sha256 of the kernel sources with comments and blank space removed (a
-    comment edit does not change the kernels the counters were taken on)."""
-    text = ""
-    for path in KERNEL_SOURCES:
-        with open(path) as f:
-            text += f.read() + "\n"
-    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    text = re.sub(r"//[^\n]*", "", text)
-    code = "\n".join(line.strip() for line in text.splitlines() if line.strip())
-    return hashlib.sha256(code.encode()).hexdigest()
-
-
 def measured_traffic():
     """HBM bytes per body-pass launch from the committed counter summary, or
     None when it is absent or was taken on a different kernel source."""
@@ -107,7 +95,7 @@ def measured_traffic():
         return None
     h = re.search(r"kernel_source_sha256:\s*([0-9a-f]{64})", text)
     b = re.search(r"traffic_bytes_per_launch:\s*([0-9]+)", text)
-    if not h or not b or h.group(1) != kernel_source_hash():
+    if not h or not b or h.group(1) != metrics.kernel_source_hash():
         return None
     return int(b.group(1))
 
@@ -171,8 +159,11 @@ def main():
     # grouped launch (then the argmax reduction, a small launch of T workgroups)
     step = w4a16.Batch(probs + [(head_tw, None, head_x, head_y, head_id, head_val, head_ws)], T)
 
-    if args.variants_pass:
-        variants_pass(torch, w4a16, weights, head_p, head_s, stream)
+    if args.variants_pass is not None:
+        order = variants_pass(torch, w4a16, weights, head_p, head_s, stream)
+        if args.variants_pass:
+            with open(args.variants_pass, "w") as f:
+                json.dump(order, f, indent=1)
         return
 
     if args.singles_pass:
@@ -548,8 +539,10 @@ def variant_launches(torch, w4a16, weights, head_p, head_s, stream):
 def variants_pass(torch, w4a16, weights, head_p, head_s, stream):
     """Untimed: for T = 1, 4, 8, each projection (layer 0) and the lm_head
     with argmax, one launch with the dot-product variant, then one with the
-    matrix-core variant (counter collection)."""
+    matrix-core variant (counter collection).  Returns the launch order
+    (workload, calls, dispatches per call, weight bytes)."""
     hn, hk = synth.LM_HEAD
+    order = []
     try:
         for T in (1, 4, 8):
             for v in ("dot", "mfma"):
@@ -559,12 +552,17 @@ def variants_pass(torch, w4a16, weights, head_p, head_s, stream):
                     w = next(w for w in weights if w[0] == proj)
                     x = to_dev(synth.activations(synth.tid_layer(0, proj), T, K), torch)
                     w4a16.matmul(w[2], w[3], x, stream=stream)
+                    order.append({"workload": f"{proj} T={T} {v}", "untimed": 0, "timed": 1, "dispatches": 1,
+                                  "weight_bytes": metrics.weight_bytes(N, K)})
                 x = to_dev(synth.activations(synth.TID_LM_HEAD + 3, T, hk), torch)
                 w4a16.head_gather(head_p, head_s, x, scores=True, argmax=True, stream=stream)
+                order.append({"workload": f"lm_head T={T} {v}", "untimed": 0, "timed": 1, "dispatches": 2,
+                              "weight_bytes": metrics.weight_bytes(hn, hk)})
         torch.cuda.synchronize()
     finally:
         w4a16.set_variant("auto")
     log("variants pass done: T = 1, 4, 8 x {dot, matrix core} x {qkv, o, gate_up, down, lm_head}")
+    return order
 
 
 def read_floors(torch, w4a16, stream):

@@ -9,7 +9,29 @@ extracted text, its symbols are defined in the same paragraph and its
 printed examples fix this reading).
 """
 
+import hashlib
+import os
+import re
+
 GROUP = 128
+
+# the sources whose compiled form the committed counter summaries describe
+KERNEL_SOURCES = [os.path.join(os.path.dirname(os.path.abspath(__file__)), "csrc", f)
+                  for f in ("w4a16_device.h", "w4a16_internal.h", "w4a16_kernels.hip", "w4a16_kernels_tt.hip",
+                            "w4a16_api.hip")]
+
+
+def kernel_source_hash() -> str:
+    """sha256 of the kernel sources with comments and blank space removed (a
+    comment edit does not change the kernels the counters were taken on)."""
+    text = ""
+    for path in KERNEL_SOURCES:
+        with open(path) as f:
+            text += f.read() + "\n"
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", "", text)
+    code = "\n".join(line.strip() for line in text.splitlines() if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()
 
 
 def weight_bytes(n_rows: int, k: int) -> int:

@@ -106,9 +106,10 @@ constexpr float kLevelScale = 16.0f;
 // against 9.2, at T = 8 9.4 against 12.2).
 constexpr int kF16MaxT = 16;
 constexpr int kF16MaxSplitT = 2;
-template <int TT, bool SHARED>
+constexpr int kF16MaxSharedRt4T = 8;
+template <int TT, bool SHARED, int RT = 1>
 constexpr bool tries_f16() {
-  return TT <= (SHARED ? kF16MaxT : kF16MaxSplitT);
+  return TT <= (SHARED ? (RT >= 4 ? kF16MaxSharedRt4T : kF16MaxT) : kF16MaxSplitT);
 }
 // The fp16 form's activations are x * 2^kDirectE; a tile's sum is
 // multiplied by 2^-kDirectE.
@@ -753,21 +754,21 @@ __device__ __forceinline__ void lane_chunks(const GemvArgs& a, const unsigned ch
 
 // Stages the slice [sb, se) of the activations for a workgroup (SHARED) or
 // for this wave alone, and returns which level form runs on it: the fp16
-// form when the kernel tries it (tries_f16) and every value is
+// form when the kernel tries it (F16, from tries_f16) and every value is
 // exact in it, else bf16.  Returns after the staged values are visible to
 // every wave that reads them and every load issued before has landed.
-template <int TT, bool SHARED>
+template <int TT, bool SHARED, bool F16>
 __device__ __forceinline__ bool stage_slice(const GemvArgs& a, unsigned char* xs, int sb, int se) {
   bool h = false;
   if constexpr (SHARED) {
-    if constexpr (tries_f16<TT, true>()) h = stage_f16_shared<TT>(a, xs, sb, se);
+    if constexpr (F16) h = stage_f16_shared<TT>(a, xs, sb, se);
     if (!h) stage_x<TT>(a, reinterpret_cast<__bf16*>(xs), sb, se, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
                         blockDim.x >> 6);
     __syncthreads();
   } else {
     const int lane = threadIdx.x & 63;
     lds_fence();
-    if constexpr (tries_f16<TT, false>()) {
+    if constexpr (F16) {
       u4_t held;
       int held_at = -1;
       h = __ballot(stage_direct<TT>(a, xs, sb, se, lane, 64, 0x7fffffff, held, held_at)) == 0;
@@ -933,11 +934,11 @@ __device__ __forceinline__ void stream_slice(const GemvArgs& a, const u4_t* cons
     prologue();
     if constexpr (SHARED)
       if (!first) __syncthreads();  // every wave is done with the previous slice
-    h = stage_slice<TT, SHARED>(a, xs, sb, se);
+    h = stage_slice<TT, SHARED, tries_f16<TT, SHARED, RT>()>(a, xs, sb, se);
   }
   const unsigned char* xb[4];
   lane_chunks(a, xs, trow, kq, xb);
-  if constexpr (tries_f16<TT, SHARED>()) {
+  if constexpr (tries_f16<TT, SHARED, RT>()) {
     if (h)
       slice_tiles<TT, RT, VS, LAY, true>(a, cp, sp, xb, sb, n, np, q, sq, sv, acc);
     else
@@ -1294,7 +1295,7 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
     tile_ptr<LAY>(a, v0, r16, kq, cp, sp);
     ring_prologue<LAY>(a, cp, sp, q, sv);
   }
-  const bool h = stage_slice<TT, true>(a, xs, 0, a.G);  // also waits for the ring's loads
+  const bool h = stage_slice<TT, true, tries_f16<TT, true>()>(a, xs, 0, a.G);  // also waits for the ring's loads
   float bv[4];
   int bi[4];
 #pragma unroll

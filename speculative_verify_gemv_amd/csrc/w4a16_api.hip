@@ -228,6 +228,7 @@ w4a16_status run_batch(const void* table_host, const void* table_dev, hipStream_
   if (hdr->threads < 64 || hdr->threads > 1024 || hdr->threads % 64 || hdr->lds < 0 || hdr->lds > 163840)
     return W4A16_ERR_BAD_SHAPE;
   if (hdr->tiled != 0 && (hdr->tiled != 1 || hdr->rt != 1)) return W4A16_ERR_BAD_SHAPE;
+  if (hdr->variant == w4a16::kRun && hdr->tiled != 1) return W4A16_ERR_BAD_SHAPE;  // runs read tiled weights only
   if (w4a16_status s = check_device()) return s;
   p.variant = hdr->variant;
   p.rt = hdr->rt;

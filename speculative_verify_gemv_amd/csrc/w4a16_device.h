@@ -1275,7 +1275,7 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
 // Run workgroup: a.run_tiles tiles per wave.  Workgroup b owns tiles
 // [b*waves*nt, (b+1)*waves*nt); wave i streams tiles i, i + waves, ... of them,
 // so the waves stay on adjacent tiles.  All of K is staged once (the planner
-// guarantees it fits).
+// guarantees it fits).  Built for tiled weights only (LAY = kLayTiled).
 template <int TT, int LAY>
 __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
   const int lane = threadIdx.x & 63;
@@ -1484,8 +1484,7 @@ hipError_t launch_run(const GemvArgs& a, const GemvArgs* table, int count, const
 // with table set, a grouped launch over `count` problems.
 template <int TT>
 hipError_t launch_t(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
-  if (p.variant == kRun)
-    return p.tiled ? launch_run<TT, kLayTiled>(a, table, count, p, s) : launch_run<TT, kLayAny>(a, table, count, p, s);
+  if (p.variant == kRun) return p.tiled ? launch_run<TT, kLayTiled>(a, table, count, p, s) : hipErrorInvalidValue;
   if (p.variant == kSplit) return launch_rt<TT, false>(a, table, count, p, s);
   if (p.variant == kShared) return launch_rt<TT, true>(a, table, count, p, s);
   if (table || p.variant != kDot || p.rt != 2) return hipErrorInvalidValue;

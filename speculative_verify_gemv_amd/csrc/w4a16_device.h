@@ -111,10 +111,28 @@ template <int TT, bool SHARED, int RT = 1>
 constexpr bool tries_f16() {
   return TT <= (SHARED ? (RT >= 4 ? kF16MaxSharedRt4T : kF16MaxT) : kF16MaxSplitT);
 }
-// The fp16 form's activations are x * 2^kDirectE; a tile's sum is
-// multiplied by 2^-kDirectE.
+// The fp16 form's activations are x * 2^E, first tried with E = kDirectE;
+// a tile's sum is multiplied by 2^-E.
 constexpr int kDirectE = 4;
-constexpr float kDirectScale = 1.0f / (1 << kDirectE);
+constexpr int kNoDirect = 1 << 20;  // no E fits the slice
+
+// 2^e as an fp32 bit pattern (|e| <= 126; for e uniform, scalar arithmetic).
+__device__ __forceinline__ float pow2(int e) { return __int_as_float((127 + e) << 23); }
+
+// The E of a slice whose values missed the window of 2^kDirectE, or
+// kNoDirect.  x * 2^E is exact in fp16 for every value of 8 significant bits
+// from 2^-17 to 65280 (subnormals hold 8 bits down to 2^-17), i.e. for bf16
+// magnitude bits b with 0x3700 <= b + 128 E <= 0x477F.  b_max is the
+// slice's largest magnitude; mn_min its smallest nonzero magnitude minus 1
+// (0xFFFF: no nonzero value).  |E| <= 100 keeps 2^E and 2^-E normal fp32
+// numbers.  Of the exponents that fit, the one nearest kDirectE.  No E fits
+// an infinity or NaN, a bf16 subnormal, or a span of more than 33 binades.
+__device__ __forceinline__ int direct_exponent(unsigned b_max, unsigned mn_min) {
+  if (b_max >= 0x7F80u) return kNoDirect;
+  const int hi = min(((int)0x477F - (int)b_max) >> 7, 100);        // floor
+  const int lo = mn_min >= 0xFFFFu ? -100 : max(-(((int)mn_min + 1 - 0x3700) >> 7), -100);  // ceil
+  return lo <= hi ? max(lo, min(kDirectE, hi)) : kNoDirect;
+}
 
 __device__ __forceinline__ float bf16_to_f32(unsigned short b) { return __uint_as_float((unsigned)b << 16); }
 
@@ -375,10 +393,10 @@ __device__ __forceinline__ void stage_x_wave(const GemvArgs& a, unsigned char* x
 // The same staged layout with fp16 values times 2^kDirectE, each chunk's
 // eight values in the fp16 levels' slot order 0,4,1,5,2,6,3,7.
 
-// Eight bf16 (natural order) -> eight fp16 in slot order, scaled by
-// 2^kDirectE; exact for every value that passes range8 / range_ok.
-__device__ __forceinline__ u4_t convert8_f16(u4_t v) {
-  constexpr float k = (float)(1 << kDirectE);
+// Eight bf16 (natural order) -> eight fp16 in slot order, scaled by k (a
+// power of two); exact for every value inside its window (range_ok for
+// 2^kDirectE, direct_exponent for the others).
+__device__ __forceinline__ u4_t convert8_f16(u4_t v, float k) {
   const float x0 = __uint_as_float(v.x << 16) * k, x1 = __uint_as_float(v.x & 0xFFFF0000u) * k;
   const float x2 = __uint_as_float(v.y << 16) * k, x3 = __uint_as_float(v.y & 0xFFFF0000u) * k;
   const float x4 = __uint_as_float(v.z << 16) * k, x5 = __uint_as_float(v.z & 0xFFFF0000u) * k;
@@ -434,7 +452,8 @@ __device__ __forceinline__ void zero_pad(const GemvArgs& a, unsigned char* xs, i
 // nthreads >= 64).
 template <int TT>
 __device__ __forceinline__ bool stage_direct(const GemvArgs& a, unsigned char* xs, int gs, int ge, int tid,
-                                             int nthreads, int hold_from, u4_t& held, int& held_at) {
+                                             int nthreads, int hold_from, u4_t& held, int& held_at, float k,
+                                             unsigned& b_max, unsigned& mn_min) {
   constexpr int kBatch = 4;
   const int n8 = (ge - gs) * (kGroup / 8);  // chunks per token row
   const int total = TT * n8;
@@ -464,7 +483,7 @@ __device__ __forceinline__ bool stage_direct(const GemvArgs& a, unsigned char* x
     for (int i = 0; i < kBatch; ++i) {
       if (d[i] >= 0) {
         range8(v[i], mx, mn);
-        const u4_t c = convert8_f16(v[i]);
+        const u4_t c = convert8_f16(v[i], k);
         if (d[i] >= hold_from) {
           held = c;
           held_at = d[i];
@@ -474,7 +493,21 @@ __device__ __forceinline__ bool stage_direct(const GemvArgs& a, unsigned char* x
       }
     }
   }
+  b_max = max(mx.x, mx.y);
+  mn_min = min(mn.x, mn.y);
   return !range_ok(mx, mn);
+}
+
+// Largest / smallest value over the wave (uniform).
+__device__ __forceinline__ unsigned wave_umax(unsigned v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (unsigned)__shfl_xor((int)v, o));
+  return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ unsigned wave_umin(unsigned v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (unsigned)__shfl_xor((int)v, o));
+  return __builtin_amdgcn_readfirstlane(v);
 }
 
 // A wave's own staging with its activations loaded ahead of its weights:
@@ -518,52 +551,62 @@ __device__ __forceinline__ void prefetch_x(const GemvArgs& a, int gs, int ge, u4
 }
 
 // Stages the prefetched slice into this wave's LDS area (and the ring
-// padding) and returns the level form to run: fp16 when the kernel tries it
-// and every value is exact in it, else the bf16 values as they are.
+// padding) and returns the level form to run: the fp16 form's fold 2^-E
+// when the kernel tries it and some E makes every value exact (kDirectE
+// first), else 0 with the bf16 values staged as they are.
 template <int TT>
-__device__ __forceinline__ bool stage_wave_regs(const GemvArgs& a, unsigned char* xs, int gs, int ge,
-                                                const u4_t (&xr)[kXPre]) {
+__device__ __forceinline__ float stage_wave_regs(const GemvArgs& a, unsigned char* xs, int gs, int ge,
+                                                 const u4_t (&xr)[kXPre]) {
   const int lane = threadIdx.x & 63;
   const int n8 = (ge - gs) * (kGroup / 8), total = TT * n8;
   const uint32_t inv = ((1u << 20) + n8 - 1) / n8;
   const int dst_row = a.xs_stride / 8;
   u4_t* dst = reinterpret_cast<u4_t*>(xs);
-  bool h = false;
+  int e = kNoDirect;
   if constexpr (tries_f16<TT, false>()) {
     // lanes past the end hold the last chunk again: harmless to the range
     us2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
 #pragma unroll
     for (int i = 0; i < kXPre; ++i)
       if (64 * i < total) range8(xr[i], mx, mn);
-    h = __ballot(!range_ok(mx, mn)) == 0;
+    if (__ballot(!range_ok(mx, mn)) == 0)
+      e = kDirectE;
+    else
+      e = direct_exponent(wave_umax(max(mx.x, mx.y)), wave_umin(min(mn.x, mn.y)));
   }
+  const bool h = e != kNoDirect;
+  const float k = h ? pow2(e) : 0.0f;
 #pragma unroll
   for (int i = 0; i < kXPre; ++i) {
     if (64 * i < total) {
       const int c = lane + 64 * i;
       const int t = chunk_row(c, inv);
-      if (c < total) dst[t * dst_row + swz(t, c - t * n8)] = h ? convert8_f16(xr[i]) : xr[i];
+      if (c < total) dst[t * dst_row + swz(t, c - t * n8)] = h ? convert8_f16(xr[i], k) : xr[i];
     }
   }
   zero_pad<TT>(a, xs, ge - gs, lane, 64);
-  return h;
+  return h ? pow2(-e) : 0.0f;
 }
 
-// fp16 staging of a slice for the whole workgroup.  Returns true (uniform)
-// when every value of the slice was exact in fp16: the slice and its ring
-// padding are then staged.  Otherwise nothing usable is staged and the
+// fp16 staging of a slice for the whole workgroup.  Returns (uniform) the
+// fp16 form's fold 2^-E when some E makes every value of the slice exact in
+// fp16 (kDirectE is tried first; when it misses, the workgroup's range picks
+// another and the slice is staged again): the slice and its ring padding
+// are then staged.  Otherwise it returns 0, nothing usable is staged and the
 // caller stages bf16.  The workgroup-wide decision needs one word per wave;
 // the words borrow the last four chunks of the last row, whose values the
 // threads that own them hold back until the decision is made.  Ends with a
 // barrier after the decision, before any padding store; the caller's barrier
 // publishes the staged values.
 template <int TT>
-__device__ __forceinline__ bool stage_f16_shared(const GemvArgs& a, unsigned char* xs, int gs, int ge) {
+__device__ __forceinline__ float stage_f16_shared(const GemvArgs& a, unsigned char* xs, int gs, int ge) {
   const int n8 = (ge - gs) * (kGroup / 8);
   const int flag_at = (TT - 1) * (a.xs_stride / 8) + n8 - 4;  // chunk position of the flag words
   u4_t held = {0u, 0u, 0u, 0u};
   int held_at = -1;
-  const bool bad = stage_direct<TT>(a, xs, gs, ge, threadIdx.x, blockDim.x, flag_at, held, held_at);
+  unsigned b_max, mn_min;
+  const bool bad = stage_direct<TT>(a, xs, gs, ge, threadIdx.x, blockDim.x, flag_at, held, held_at,
+                                    pow2(kDirectE), b_max, mn_min);
   u4_t* dst = reinterpret_cast<u4_t*>(xs);
   unsigned* flags = reinterpret_cast<unsigned*>(dst + flag_at);  // 16 words: up to 16 waves
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -576,10 +619,27 @@ __device__ __forceinline__ bool stage_f16_shared(const GemvArgs& a, unsigned cha
   // branch (as a divergent one, both loops' registers would be live at once)
   any = __builtin_amdgcn_readfirstlane(any);
   __syncthreads();  // every wave has read the flags before they are overwritten
-  if (any != 0) return false;
-  if (held_at >= 0) dst[held_at] = held;
+  if (any == 0) {
+    if (held_at >= 0) dst[held_at] = held;
+    zero_pad<TT>(a, xs, ge - gs, threadIdx.x, blockDim.x);
+    return pow2(-kDirectE);
+  }
+  // Some value missed: the workgroup's range, in two of the flag words,
+  // picks another power of two if one fits, and the slice is staged again.
+  if (threadIdx.x == 0) {
+    flags[0] = 0u;
+    flags[1] = 0xFFFFFFFFu;
+  }
+  __syncthreads();
+  atomicMax(&flags[0], b_max);
+  atomicMin(&flags[1], mn_min);
+  __syncthreads();
+  const int e = direct_exponent(__builtin_amdgcn_readfirstlane(flags[0]), __builtin_amdgcn_readfirstlane(flags[1]));
+  __syncthreads();  // every wave has read the range before the staging overwrites it
+  if (e == kNoDirect) return 0.0f;
+  stage_direct<TT>(a, xs, gs, ge, threadIdx.x, blockDim.x, 0x7fffffff, held, held_at, pow2(e), b_max, mn_min);
   zero_pad<TT>(a, xs, ge - gs, threadIdx.x, blockDim.x);
-  return true;
+  return pow2(-e);
 }
 
 // RW rows per wave, L = 64/RW lanes per row; a lane takes the row's 16-byte
@@ -737,13 +797,6 @@ __device__ __forceinline__ f4_t group_mfma(const unsigned char* const (&xb)[4], 
   return d;
 }
 
-// The factor that turns a tile's sum of the H form back into the unscaled
-// result (a power of two: the same roundings as unscaled arithmetic).
-template <bool H>
-constexpr float fold_scale() {
-  return H ? kDirectScale : kLevelScale;
-}
-
 // This lane's four activation chunks of group 0 of a staged slice (row trow,
 // chunks 4 kq .. 4 kq + 3 of the group, swizzled), as byte pointers.
 __device__ __forceinline__ void lane_chunks(const GemvArgs& a, const unsigned char* xs, int trow, int kq,
@@ -754,16 +807,19 @@ __device__ __forceinline__ void lane_chunks(const GemvArgs& a, const unsigned ch
 
 // Stages the slice [sb, se) of the activations for a workgroup (SHARED) or
 // for this wave alone, and returns which level form runs on it: the fp16
-// form when the kernel tries it (F16, from tries_f16) and every value is
-// exact in it, else bf16.  Returns after the staged values are visible to
-// every wave that reads them and every load issued before has landed.
+// form's fold 2^-E when the kernel tries it (F16, from tries_f16) and some
+// power of two 2^E makes every value exact in fp16 (2^kDirectE first), else
+// 0 with the bf16 values staged.  Returns after the staged values are
+// visible to every wave that reads them and every load issued before has
+// landed.
 template <int TT, bool SHARED, bool F16>
-__device__ __forceinline__ bool stage_slice(const GemvArgs& a, unsigned char* xs, int sb, int se) {
-  bool h = false;
+__device__ __forceinline__ float stage_slice(const GemvArgs& a, unsigned char* xs, int sb, int se) {
+  float fold = 0.0f;
   if constexpr (SHARED) {
-    if constexpr (F16) h = stage_f16_shared<TT>(a, xs, sb, se);
-    if (!h) stage_x<TT>(a, reinterpret_cast<__bf16*>(xs), sb, se, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
-                        blockDim.x >> 6);
+    if constexpr (F16) fold = stage_f16_shared<TT>(a, xs, sb, se);
+    if (fold == 0.0f)
+      stage_x<TT>(a, reinterpret_cast<__bf16*>(xs), sb, se, __builtin_amdgcn_readfirstlane(threadIdx.x >> 6),
+                  blockDim.x >> 6);
     __syncthreads();
   } else {
     const int lane = threadIdx.x & 63;
@@ -771,19 +827,31 @@ __device__ __forceinline__ bool stage_slice(const GemvArgs& a, unsigned char* xs
     if constexpr (F16) {
       u4_t held;
       int held_at = -1;
-      h = __ballot(stage_direct<TT>(a, xs, sb, se, lane, 64, 0x7fffffff, held, held_at)) == 0;
-      if (h)
+      unsigned b_max, mn_min;
+      int e = kDirectE;
+      if (__ballot(stage_direct<TT>(a, xs, sb, se, lane, 64, 0x7fffffff, held, held_at, pow2(kDirectE), b_max,
+                                    mn_min)) != 0) {
+        // some value missed: the wave's range picks another power of two
+        e = direct_exponent(wave_umax(b_max), wave_umin(mn_min));
+        if (e != kNoDirect) {
+          lds_fence();
+          stage_direct<TT>(a, xs, sb, se, lane, 64, 0x7fffffff, held, held_at, pow2(e), b_max, mn_min);
+        }
+      }
+      if (e != kNoDirect) {
         zero_pad<TT>(a, xs, se - sb, lane, 64);
-      else
+        fold = pow2(-e);
+      } else {
         lds_fence();
+      }
     }
-    if (!h) stage_x_wave<TT>(a, xs, sb, se);
+    if (fold == 0.0f) stage_x_wave<TT>(a, xs, sb, se);
     lds_fence();
   }
   // the staging waited for its loads, issued after the weight loads in
   // flight; saying so lets the loop wait for exactly one group at a time
   __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-  return h;
+  return fold;
 }
 
 // The tiles of one staged slice (n groups from sb, np = n rounded up to
@@ -794,7 +862,7 @@ template <int TT, int RT, bool VS, int LAY, bool H>
 __device__ __forceinline__ void slice_tiles(const GemvArgs& a, const u4_t* const (&cp)[RT],
                                             const uint16_t* const (&sp)[RT], const unsigned char* const (&xb)[4],
                                             int sb, int n, int np, u4_t (&q)[kRing], unsigned short (&sq)[kRing],
-                                            u4_t& sv, float (&acc)[RT][4]) {
+                                            u4_t& sv, float fold, float (&acc)[RT][4]) {
   constexpr int PD = kRing;
 #pragma unroll
   for (int tl = 0; tl < RT; ++tl) {
@@ -847,7 +915,7 @@ __device__ __forceinline__ void slice_tiles(const GemvArgs& a, const u4_t* const
     if (!has_next) cycle(fi, std::false_type{});
     // fold this tile's slice sum, undoing the level form's power of two
 #pragma unroll
-    for (int r = 0; r < 4; ++r) acc[tl][r] += accs[r] * fold_scale<H>();
+    for (int r = 0; r < 4; ++r) acc[tl][r] += accs[r] * fold;
   }
 }
 
@@ -918,14 +986,14 @@ __device__ __forceinline__ void stream_slice(const GemvArgs& a, const u4_t* cons
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-  bool h;
+  float fold;  // the fp16 form's 2^-E, or 0: bf16 staged
   if constexpr (PRE) {
     // the wave's activations are loaded first, into registers
     u4_t xr[kXPre];
     prefetch_x<TT>(a, sb, se, xr);
     if constexpr (!stage_first<TT>()) prologue();
     lds_fence();
-    h = stage_wave_regs<TT>(a, xs, sb, se, xr);
+    fold = stage_wave_regs<TT>(a, xs, sb, se, xr);
     lds_fence();
     if constexpr (stage_first<TT>()) prologue();
   } else {
@@ -934,18 +1002,18 @@ __device__ __forceinline__ void stream_slice(const GemvArgs& a, const u4_t* cons
     prologue();
     if constexpr (SHARED)
       if (!first) __syncthreads();  // every wave is done with the previous slice
-    h = stage_slice<TT, SHARED, tries_f16<TT, SHARED, RT>()>(a, xs, sb, se);
+    fold = stage_slice<TT, SHARED, tries_f16<TT, SHARED, RT>()>(a, xs, sb, se);
   }
   const unsigned char* xb[4];
   lane_chunks(a, xs, trow, kq, xb);
   if constexpr (tries_f16<TT, SHARED, RT>()) {
-    if (h)
-      slice_tiles<TT, RT, VS, LAY, true>(a, cp, sp, xb, sb, n, np, q, sq, sv, acc);
+    if (fold != 0.0f)
+      slice_tiles<TT, RT, VS, LAY, true>(a, cp, sp, xb, sb, n, np, q, sq, sv, fold, acc);
     else
       exact_slice<TT, RT, LAY>(a, cp, sp, xb, sb, n, acc);
   } else {
-    (void)h;
-    slice_tiles<TT, RT, VS, LAY, false>(a, cp, sp, xb, sb, n, np, q, sq, sv, acc);
+    (void)fold;
+    slice_tiles<TT, RT, VS, LAY, false>(a, cp, sp, xb, sb, n, np, q, sq, sv, kLevelScale, acc);
   }
 }
 
@@ -1224,8 +1292,8 @@ __device__ __forceinline__ void exact_run_tiles(const GemvArgs& a, int64_t v, in
 template <int TT, int LAY, bool H>
 __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t v_end, int step,
                                           const unsigned char* xs, int r16, int kq, int trow, const u4_t* cp,
-                                          const uint16_t* sp, u4_t (&q)[kRing], u4_t& sv, float (&bv)[4],
-                                          int (&bi)[4]) {
+                                          const uint16_t* sp, u4_t (&q)[kRing], u4_t& sv, float fold,
+                                          float (&bv)[4], int (&bi)[4]) {
   constexpr int PD = kRing;
   const int n = a.G;
   const int np = (n + PD - 1) / PD * PD;
@@ -1264,7 +1332,7 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
       }
       sv = svn;
     }
-    tile_outputs<TT>(a, v, r16, kq, w_cur, accs, fold_scale<H>(), bv, bi);
+    tile_outputs<TT>(a, v, r16, kq, w_cur, accs, fold, bv, bi);
     v = vn;
     cp = cpn;
     sp = spn;
@@ -1295,7 +1363,8 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
     tile_ptr<LAY>(a, v0, r16, kq, cp, sp);
     ring_prologue<LAY>(a, cp, sp, q, sv);
   }
-  const bool h = stage_slice<TT, true, tries_f16<TT, true>()>(a, xs, 0, a.G);  // also waits for the ring's loads
+  // also waits for the ring's loads; fold: the fp16 form's 2^-E, or 0
+  const float fold = stage_slice<TT, true, tries_f16<TT, true>()>(a, xs, 0, a.G);
   float bv[4];
   int bi[4];
 #pragma unroll
@@ -1305,12 +1374,12 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
   }
   if (v0 < v_end) {
     if constexpr (tries_f16<TT, true>()) {
-      if (h)
-        run_tiles<TT, LAY, true>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, sp, q, sv, bv, bi);
+      if (fold != 0.0f)
+        run_tiles<TT, LAY, true>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, sp, q, sv, fold, bv, bi);
       else
         exact_run_tiles<TT, LAY>(a, v0, v_end, nwv, xs, r16, kq, trow, bv, bi);
     } else {
-      run_tiles<TT, LAY, false>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, sp, q, sv, bv, bi);
+      run_tiles<TT, LAY, false>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, sp, q, sv, kLevelScale, bv, bi);
     }
   }
   if (a.partial) {

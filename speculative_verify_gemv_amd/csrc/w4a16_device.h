@@ -42,12 +42,13 @@
 //
 // (at 1024 the fp16 spacing is 1, at 64 it is 1/16 and the nibble sits four
 // bits higher), then one v_pk_add_f16 with -1032 / -72 each, against
-// activations converted to fp16 times 2^kDirectE.  That conversion is exact
-// only for magnitudes in [2^-21, 4080] (and zero), so a workgroup uses it
-// only when every activation of its staged slice lies there; otherwise it
-// stages the bf16 activations as they are and runs the bf16 levels.  Both
-// forms give exact products and fp32 sums, so the choice changes rounding
-// order at most, never the tolerance.
+// activations converted to fp16 times a power of two 2^E.  That conversion
+// is exact when every scaled magnitude lies in [2^-17, 65280] (or is zero):
+// a staged slice tries E = kDirectE (magnitudes in [2^-21, 4080]), then the
+// E its own range allows; a slice that no E fits is staged as the bf16
+// values they are and runs the bf16 levels.  Both forms give exact products
+// and fp32 sums, so the choice changes rounding order at most, never the
+// tolerance.
 //
 // Two variants:
 //  * matrix core: tokens are the A operand of v_mfma_f32_16x16x32_bf16 (T
@@ -390,8 +391,8 @@ __device__ __forceinline__ void stage_x_wave(const GemvArgs& a, unsigned char* x
 
 // ------------------------------------------------------------ fp16 staging ----
 //
-// The same staged layout with fp16 values times 2^kDirectE, each chunk's
-// eight values in the fp16 levels' slot order 0,4,1,5,2,6,3,7.
+// The same staged layout with fp16 values times 2^E, each chunk's eight
+// values in the fp16 levels' slot order 0,4,1,5,2,6,3,7.
 
 // Eight bf16 (natural order) -> eight fp16 in slot order, scaled by k (a
 // power of two); exact for every value inside its window (range_ok for

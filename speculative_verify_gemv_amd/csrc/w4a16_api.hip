@@ -162,7 +162,7 @@ struct TableHeader {
   int32_t T;
   int32_t variant;
   int32_t rt;
-  int32_t tiled;  // 1: every problem tiled (tiled-layout kernels, one tile per wave)
+  int32_t tiled;  // 1: every problem tiled (tiled-layout kernels, one tile per wave); 2: every problem row-major
   int32_t threads;
   int32_t lds;
   int32_t n_argmax;  // argmax records after the count argument records (host copy)
@@ -188,15 +188,21 @@ static_assert(sizeof(ArgmaxRecord) == 32 && sizeof(w4a16::GemvArgs) == 144, "bat
 // 27B-class body pass: +2.8% at T = 5, +0.8% at T = 8 against sixteen waves
 // of four), sixteen waves of four above T = 8, a problem whose activations
 // do not fit running shared workgroups inside the same kernel.
-// Otherwise (some row-major problem) four waves of two 16-row tiles at
-// T = 1, of four from T = 2 (27B-class body pass, row-major: +5.6% at
-// T = 8, +8.3% at T = 4 against eight waves of four).  W4A16_BATCH_TILE =
-// "split|shared|run,rt,waves" overrides it (for measurement).
-w4a16::Tile batch_tile(int T, bool all_tiled, int64_t kmax) {
+// Every problem row-major: shared workgroups of two 16-row tiles per wave,
+// four waves at T = 1 and eight above (27B-class body pass: 75.3 / 71.7 /
+// 66.3 / 58.1% of 8 TB/s at T = 2 / 4 / 8 / 16 against 70.7 / 66.3 / 60.3 /
+// 56.1% for four waves of four tiles).  Both layouts mixed: four waves of
+// two tiles at T = 1, of four from T = 2 (the same pass row-major with the
+// either-layout kernels: +5.6% at T = 8, +8.3% at T = 4 against eight waves
+// of four).  W4A16_BATCH_TILE = "split|shared|run,rt,waves" overrides it
+// (for measurement).
+w4a16::Tile batch_tile(int T, bool all_tiled, bool all_row, int64_t kmax) {
   w4a16::Tile t;
   if (all_tiled)
     t = T <= 2 ? w4a16::Tile{w4a16::kShared, 1, w4a16::shared_waves(T, kmax)}
                : w4a16::Tile{w4a16::kRun, T <= 4 ? 4 : T <= 8 ? 6 : 4, T <= 8 ? 8 : 16};
+  else if (all_row)
+    t = w4a16::Tile{w4a16::kShared, 2, T == 1 ? 4 : 8};
   else
     t = T == 1 ? w4a16::Tile{w4a16::kShared, 2, 4} : w4a16::Tile{w4a16::kShared, 4, 4};
   w4a16::tile_override(true, &t);
@@ -227,12 +233,14 @@ w4a16_status run_batch(const void* table_host, const void* table_dev, hipStream_
   if (hdr->rt != 1 && hdr->rt != 2 && hdr->rt != 4) return W4A16_ERR_BAD_SHAPE;
   if (hdr->threads < 64 || hdr->threads > 1024 || hdr->threads % 64 || hdr->lds < 0 || hdr->lds > 163840)
     return W4A16_ERR_BAD_SHAPE;
-  if (hdr->tiled != 0 && (hdr->tiled != 1 || hdr->rt != 1)) return W4A16_ERR_BAD_SHAPE;
+  // layout of the launch's kernels: 0 either (mixed), 1 tiled (one tile per wave), 2 row-major
+  if (hdr->tiled < 0 || hdr->tiled > 2 || (hdr->tiled == 1 && hdr->rt != 1)) return W4A16_ERR_BAD_SHAPE;
   if (hdr->variant == w4a16::kRun && hdr->tiled != 1) return W4A16_ERR_BAD_SHAPE;  // runs read tiled weights only
   if (w4a16_status s = check_device()) return s;
   p.variant = hdr->variant;
   p.rt = hdr->rt;
   p.tiled = hdr->tiled == 1;
+  p.rowmajor = hdr->tiled == 2;
   p.threads = hdr->threads;
   p.grid = hdr->grid;
   p.lds = hdr->lds;
@@ -404,13 +412,14 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
   auto* hdr = static_cast<TableHeader*>(table_host);
   auto* args = reinterpret_cast<w4a16::GemvArgs*>(hdr + 1);
   auto* recs = reinterpret_cast<ArgmaxRecord*>(args + count);
-  bool all_tiled = true;
+  bool all_tiled = true, all_row = true;
   int64_t kmax = 0;
   for (int32_t i = 0; i < count; ++i) {
     all_tiled = all_tiled && problems[i].layout == W4A16_LAYOUT_TILED;
+    all_row = all_row && problems[i].layout == W4A16_LAYOUT_ROW_MAJOR;
     kmax = std::max(kmax, problems[i].K);
   }
-  w4a16::Tile bt = batch_tile(T, all_tiled, kmax);
+  w4a16::Tile bt = batch_tile(T, all_tiled, all_row, kmax);
   // Every problem runs the same kernel (a run problem whose activations do
   // not fit runs shared workgroups inside the run kernel); a plan that still
   // differs between problems falls back to shared workgroups.
@@ -424,7 +433,7 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
       w4a16::GemvArgs a = gemv_args(q.packed_u4, tiled ? nullptr : q.scales_bf16, tiled, q.x_bf16, q.y_f32,
                                     nullptr, q.N, q.N, q.K);
       a.partial = q.argmax_id ? static_cast<int2*>(q.workspace) : nullptr;
-      const w4a16::Plan p = w4a16::plan_tile(a, T, bt, all_tiled, true);
+      const w4a16::Plan p = w4a16::plan_tile(a, T, bt, all_tiled, all_row, true);
       uniform = uniform && p.variant == bt.shape;
       rt = p.rt;
       a.wg_start = grid;
@@ -439,8 +448,8 @@ w4a16_status w4a16_batch_plan(const w4a16_problem* problems, int32_t count, int3
       continue;
     }
     if (grid > 0x7fffffffLL) return W4A16_ERR_BAD_SHAPE;
-    *hdr = TableHeader{kTableMagic, W4A16_ABI_VERSION, count, T, bt.shape, rt, all_tiled ? 1 : 0, threads, lds,
-                       n_argmax, grid, 0, 0};
+    *hdr = TableHeader{kTableMagic, W4A16_ABI_VERSION, count, T, bt.shape, rt, all_tiled ? 1 : all_row ? 2 : 0, threads,
+                       lds, n_argmax, grid, 0, 0};
     return W4A16_OK;
   }
   return W4A16_ERR_BAD_SHAPE;  // not reached: shared tiles always plan

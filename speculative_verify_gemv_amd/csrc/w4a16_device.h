@@ -238,6 +238,10 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_move(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, 0xF, 0xF, false));
 }
+template <int CTRL>
+__device__ __forceinline__ unsigned dpp_u32(unsigned v) {
+  return (unsigned)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, false);
+}
 
 // Sum over the 32 lanes of each half-wave, every lane receiving the same
 // total: within each 16-lane DPP row, row_mirror (lane i with 15 - i), then
@@ -735,21 +739,29 @@ __global__ void __launch_bounds__(512) w4a16_dot_kernel(GemvArgs a) {
 // ---------------------------------------------------------- matrix core ----
 
 // Layout template argument: kLayAny reads either layout (a.tiled decides at
-// run time); kLayTiled is compiled for the tiled layout only.
-constexpr int kLayAny = 0, kLayTiled = 1;
+// run time, for grouped launches that mix them); kLayTiled is compiled for
+// the tiled layout only, kLayRow for the row-major layout only.
+constexpr int kLayAny = 0, kLayTiled = 1, kLayRow = 2;
 
-// Weight-code load.  Row-major codes use the default cache policy: the two
-// 64-byte halves of a 128-byte line (groups g and g+1 of a row) then merge
-// into one L2 request in the vector L1, which the nontemporal hint would
-// prevent (measured 20% slower).  A tiled wave load covers whole lines of a
-// 1 KB block that is read once, so it is marked nontemporal (measured 5-9%
-// faster).
+template <int LAY>
+__device__ __forceinline__ bool tiled_rows(const GemvArgs& a) {
+  return LAY == kLayTiled || (LAY == kLayAny && a.tiled);
+}
+
+// Weight-code load.  kLayAny's row-major loads use the default cache policy:
+// its wave load covers 64 bytes of each of 16 rows, and the two 64-byte
+// halves of a 128-byte line (groups g and g+1 of a row, loaded by
+// consecutive ring slots) then merge into one L2 request in the vector L1,
+// which the nontemporal hint would prevent (measured 20% slower).  A tiled
+// wave load covers whole lines of a 1 KB block that is read once, and a
+// kLayRow wave load whole 128-byte lines of 8 rows: both are marked
+// nontemporal (measured 5-9% faster on tiled weights).
 template <int LAY>
 __device__ __forceinline__ u4_t load_codes(const u4_t* p) {
-  if constexpr (LAY == kLayTiled)
-    return ld_global_nt(p);
-  else
+  if constexpr (LAY == kLayAny)
     return ld_global(p);
+  else
+    return ld_global_nt(p);
 }
 
 // bf16 scale e of eight packed in v (element order = memory order) -> fp32.
@@ -761,19 +773,53 @@ __device__ __forceinline__ float scale_of(u4_t v, int e) {
 // Offset, in 16-byte units, of group g's codes from a lane's code pointer.
 template <int LAY>
 __device__ __forceinline__ int code_off(const GemvArgs& a, int g) {
-  return (LAY == kLayTiled || a.tiled) ? (g >> 3) * (kTileChunkBytes / 16) + (g & 7) * (kTileGroupBytes / 16)
-                                       : 4 * g;
+  return tiled_rows<LAY>(a) ? (g >> 3) * (kTileChunkBytes / 16) + (g & 7) * (kTileGroupBytes / 16) : 4 * g;
 }
 
 // Offset, in 16-byte units, of the eight scales of groups g .. g+7 (g a
 // multiple of 8) from a lane's scale pointer.
 template <int LAY>
 __device__ __forceinline__ int scale_off(const GemvArgs& a, int g) {
-  return (LAY == kLayTiled || a.tiled)
+  return tiled_rows<LAY>(a)
              ? (g >> 3) * (kTileChunkBytes / 16) + min(kTileChunkGroups, a.G - g) * (kTileGroupBytes / 16)
              : g >> 3;
 }
 
+
+// kLayRow: ring slots 2j and 2j+1 hold the pair of groups (g, g+1), g even.
+// The even slot's load reads rows 0-7 of the tile and the odd slot's rows
+// 8-15, each as whole 128-byte lines (8 lanes per row: both groups of the
+// pair; a plain wave load of one group would cover 16 rows x 64 bytes, half
+// lines, which reads HBM at about three quarters of the rate: 5.4 against
+// 7.2 TB/s for a plain streaming read of rows 2,560 bytes apart).  In lane
+// l (b3 = bit 3 of l, kq = l / 16) the even slot holds row l & 7, group
+// g + b3, quarter kq; the odd slot row 8 + (l & 7), group g + 1 - b3.
+// pair_groups then hands every lane its own row's (l & 15) quarters of g
+// and of g + 1.  cp / cb point at rows l & 7 / 8 + (l & 7) of the tile
+// (quarter kq); groups past the row's last are read as its last.
+template <int LAY>
+__device__ __forceinline__ u4_t load_slot(const GemvArgs& a, const u4_t* cp, const u4_t* cb, int s, int g) {
+  if constexpr (LAY == kLayRow) {
+    const int b3 = (threadIdx.x >> 3) & 1;
+    const int gg = min((g & ~1) + ((s & 1) ? 1 - b3 : b3), a.G - 1);
+    return load_codes<LAY>(((s & 1) ? cb : cp) + 4 * gg);
+  } else {
+    (void)cb;
+    (void)s;
+    return load_codes<LAY>(cp + code_off<LAY>(a, g));
+  }
+}
+
+// The exchange after a kLayRow pair of loads (even slot ev, odd slot od):
+// lane l's own row l & 15 has group g's quarter in ev (rows 0-7, b3 = 0)
+// or od (rows 8-15, b3 = 1) of lane l itself, and group g + 1's in the other
+// slot of lane l ^ 8 (a row_ror:8 within the 16-lane DPP row).
+__device__ __forceinline__ void pair_groups(const u4_t& ev, const u4_t& od, u4_t& g0, u4_t& g1) {
+  const bool b3 = (threadIdx.x >> 3) & 1;
+  const u4_t other = b3 ? ev : od;
+  g0 = b3 ? od : ev;
+  g1 = u4_t{dpp_u32<0x128>(other.x), dpp_u32<0x128>(other.y), dpp_u32<0x128>(other.z), dpp_u32<0x128>(other.w)};
+}
 
 // One group of one 16-row tile for this lane: four MFMAs over its four
 // words of codes and its four staged activation chunks (xb[j] + group gl);
@@ -858,18 +904,22 @@ __device__ __forceinline__ float stage_slice(const GemvArgs& a, unsigned char* x
 // The tiles of one staged slice (n groups from sb, np = n rounded up to
 // whole ring cycles): the wave streams tile 0's groups, then tile 1's, ...
 // with the load ring running across tile boundaries; the ring (q, sq, sv)
-// holds tile 0's first groups on entry.
+// holds tile 0's first groups on entry.  cb: the second row pointers of
+// kLayRow (unused otherwise).
 template <int TT, int RT, bool VS, int LAY, bool H>
 __device__ __forceinline__ void slice_tiles(const GemvArgs& a, const u4_t* const (&cp)[RT],
-                                            const uint16_t* const (&sp)[RT], const unsigned char* const (&xb)[4],
-                                            int sb, int n, int np, u4_t (&q)[kRing], unsigned short (&sq)[kRing],
-                                            u4_t& sv, float fold, float (&acc)[RT][4]) {
+                                            const u4_t* const (&cb)[RT], const uint16_t* const (&sp)[RT],
+                                            const unsigned char* const (&xb)[4], int sb, int n, int np,
+                                            u4_t (&q)[kRing], unsigned short (&sq)[kRing], u4_t& sv, float fold,
+                                            float (&acc)[RT][4]) {
   constexpr int PD = kRing;
+  static_assert(PD % 2 == 0, "kLayRow loads pairs of ring slots");
 #pragma unroll
   for (int tl = 0; tl < RT; ++tl) {
     // the ring runs on into the next tile; the last tile's final cycle
     // reloads nothing, so that no load is left in flight past the slice
     const u4_t* cpn = cp[tl + 1 < RT ? tl + 1 : tl];
+    const u4_t* cbn = cb[tl + 1 < RT ? tl + 1 : tl];
     const uint16_t* spn = sp[tl + 1 < RT ? tl + 1 : tl];
     const bool has_next = tl + 1 < RT;
     float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -883,29 +933,58 @@ __device__ __forceinline__ void slice_tiles(const GemvArgs& a, const u4_t* const
         svn = ld_global(reinterpret_cast<const u4_t*>(base) + scale_off<LAY>(a, gv));
         __builtin_amdgcn_sched_barrier(0);
       }
-#pragma unroll
-      for (int s = 0; s < PD; ++s) {
-        const int gl = fi + s;  // groups past n read the zeroed padding
+      // the scale of slot s (group gl of the slice; groups past n read the
+      // zeroed padding and get scale 0)
+      auto scale_at = [&](int s, int gl) {
         float sc;
         if constexpr (VS)
           sc = scale_of(sv, s);
         else
           sc = bf16_to_f32(sq[s]);
-        sc = (gl < n) ? sc : 0.0f;
-        const f4_t d = group_mfma<H>(xb, gl, q[s]);
+        return (gl < n) ? sc : 0.0f;
+      };
+      // reload slot s (group gl) with the group PD positions ahead
+      auto reload_slot = [&](int s, int gl) {
+        const int tgt = gl + PD;
+        const bool nxt = tgt >= np;
+        const bool on = nxt && has_next;
+        const int gg = sb + (nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1));
+        if constexpr (!VS) sq[s] = ld_global((on ? spn : sp[tl]) + gg);
+        q[s] = load_slot<LAY>(a, on ? cpn : cp[tl], on ? cbn : cb[tl], s, gg);
+      };
+      if constexpr (LAY == kLayRow) {
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accs[r] = fmaf(d[r], sc, accs[r]);
-        if constexpr (R) {
-          // reload this slot with the group PD positions ahead
-          const int tgt = gl + PD;
-          const bool nxt = tgt >= np;
-          const u4_t* cpl = (nxt && has_next) ? cpn : cp[tl];
-          const int gg = sb + (nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1));
-          if constexpr (!VS) sq[s] = ld_global(((nxt && has_next) ? spn : sp[tl]) + gg);
-          q[s] = load_codes<LAY>(cpl + code_off<LAY>(a, gg));
-          // keep this slot's reload here: sunk to the end of the loop, the
-          // reloads would make every iteration wait for the whole ring
-          __builtin_amdgcn_sched_barrier(0);
+        for (int s = 0; s < PD; s += 2) {
+          const int gl = fi + s;
+          const float sc0 = scale_at(s, gl), sc1 = scale_at(s + 1, gl + 1);
+          u4_t w0, w1;
+          pair_groups(q[s], q[s + 1], w0, w1);
+          if constexpr (R) {
+            reload_slot(s, gl);
+            reload_slot(s + 1, gl + 1);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+          const f4_t d0 = group_mfma<H>(xb, gl, w0);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) accs[r] = fmaf(d0[r], sc0, accs[r]);
+          const f4_t d1 = group_mfma<H>(xb, gl + 1, w1);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) accs[r] = fmaf(d1[r], sc1, accs[r]);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < PD; ++s) {
+          const int gl = fi + s;
+          const float sc = scale_at(s, gl);
+          const f4_t d = group_mfma<H>(xb, gl, q[s]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) accs[r] = fmaf(d[r], sc, accs[r]);
+          if constexpr (R) {
+            reload_slot(s, gl);
+            // keep this slot's reload here: sunk to the end of the loop, the
+            // reloads would make every iteration wait for the whole ring
+            __builtin_amdgcn_sched_barrier(0);
+          }
         }
       }
       if constexpr (VS && R) sv = svn;
@@ -933,7 +1012,7 @@ __device__ __forceinline__ void exact_groups(const GemvArgs& a, const u4_t* cp, 
     const int gg = g0 + g;
     const u4_t w = load_codes<LAY>(cp + code_off<LAY>(a, gg));
     // scale of group gg: in its 8-scale block (tiled), or the row's gg-th
-    const int si = (LAY == kLayTiled || a.tiled) ? scale_off<LAY>(a, gg & ~7) * 8 + (gg & 7) : gg;
+    const int si = tiled_rows<LAY>(a) ? scale_off<LAY>(a, gg & ~7) * 8 + (gg & 7) : gg;
     const float sc = bf16_to_f32(ld_global(sp + si));
     const f4_t d = group_mfma<false>(xb, g, w);
 #pragma unroll
@@ -943,12 +1022,14 @@ __device__ __forceinline__ void exact_groups(const GemvArgs& a, const u4_t* cp, 
 
 template <int TT, int RT, int LAY>
 __device__ __forceinline__ void exact_slice(const GemvArgs& a, const u4_t* const (&cp)[RT],
-                                            const uint16_t* const (&sp)[RT], const unsigned char* const (&xb)[4],
-                                            int sb, int n, float (&acc)[RT][4]) {
+                                            const u4_t* const (&cb)[RT], const uint16_t* const (&sp)[RT],
+                                            const unsigned char* const (&xb)[4], int sb, int n, float (&acc)[RT][4]) {
+  // kLayRow: this lane's own row (l & 15) is row l & 7 of cp or 8 + (l & 7) of cb
+  const bool own_b = LAY == kLayRow && ((threadIdx.x >> 3) & 1);
 #pragma unroll
   for (int tl = 0; tl < RT; ++tl) {
     float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    exact_groups<LAY>(a, cp[tl], sp[tl], xb, sb, n, accs);
+    exact_groups<LAY>(a, own_b ? cb[tl] : cp[tl], sp[tl], xb, sb, n, accs);
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[tl][r] += accs[r] * kLevelScale;
   }
@@ -968,8 +1049,9 @@ __device__ __forceinline__ void exact_slice(const GemvArgs& a, const u4_t* const
 // load per group.
 template <int TT, int RT, bool VS, bool SHARED, int LAY, bool PRE>
 __device__ __forceinline__ void stream_slice(const GemvArgs& a, const u4_t* const (&cp)[RT],
-                                             const uint16_t* const (&sp)[RT], unsigned char* xs, int sb, int se,
-                                             bool first, int trow, int kq, float (&acc)[RT][4]) {
+                                             const u4_t* const (&cb)[RT], const uint16_t* const (&sp)[RT],
+                                             unsigned char* xs, int sb, int se, bool first, int trow, int kq,
+                                             float (&acc)[RT][4]) {
   constexpr int PD = kRing;
   u4_t q[PD];
   unsigned short sq[PD];
@@ -983,7 +1065,7 @@ __device__ __forceinline__ void stream_slice(const GemvArgs& a, const u4_t* cons
     for (int s = 0; s < PD; ++s) {
       const int g = sb + min(s, n - 1);
       if constexpr (!VS) sq[s] = ld_global(sp[0] + g);
-      q[s] = load_codes<LAY>(cp[0] + code_off<LAY>(a, g));
+      q[s] = load_slot<LAY>(a, cp[0], cb[0], s, g);
       __builtin_amdgcn_sched_barrier(0);
     }
   };
@@ -1009,12 +1091,12 @@ __device__ __forceinline__ void stream_slice(const GemvArgs& a, const u4_t* cons
   lane_chunks(a, xs, trow, kq, xb);
   if constexpr (tries_f16<TT, SHARED, RT>()) {
     if (fold != 0.0f)
-      slice_tiles<TT, RT, VS, LAY, true>(a, cp, sp, xb, sb, n, np, q, sq, sv, fold, acc);
+      slice_tiles<TT, RT, VS, LAY, true>(a, cp, cb, sp, xb, sb, n, np, q, sq, sv, fold, acc);
     else
-      exact_slice<TT, RT, LAY>(a, cp, sp, xb, sb, n, acc);
+      exact_slice<TT, RT, LAY>(a, cp, cb, sp, xb, sb, n, acc);
   } else {
     (void)fold;
-    slice_tiles<TT, RT, VS, LAY, false>(a, cp, sp, xb, sb, n, np, q, sq, sv, kLevelScale, acc);
+    slice_tiles<TT, RT, VS, LAY, false>(a, cp, cb, sp, xb, sb, n, np, q, sq, sv, kLevelScale, acc);
   }
 }
 
@@ -1024,32 +1106,47 @@ __device__ __forceinline__ void stream_slice(const GemvArgs& a, const u4_t* cons
 // as they land, while the weights are still in flight.
 template <int TT, int RT, bool VS, bool SHARED, int LAY>
 __device__ __forceinline__ void stream_tiles(const GemvArgs& a, const u4_t* const (&cp)[RT],
-                                             const uint16_t* const (&sp)[RT], unsigned char* xs, int g_begin,
-                                             int g_end, int trow, int kq, float (&acc)[RT][4]) {
+                                             const u4_t* const (&cb)[RT], const uint16_t* const (&sp)[RT],
+                                             unsigned char* xs, int g_begin, int g_end, int trow, int kq,
+                                             float (&acc)[RT][4]) {
   if constexpr (!SHARED && TT <= 8) {
     if (g_end - g_begin <= a.sk && TT * (g_end - g_begin) * (kGroup / 8) <= kXPre * 64) {  // uniform
-      stream_slice<TT, RT, VS, SHARED, LAY, true>(a, cp, sp, xs, g_begin, g_end, true, trow, kq, acc);
+      stream_slice<TT, RT, VS, SHARED, LAY, true>(a, cp, cb, sp, xs, g_begin, g_end, true, trow, kq, acc);
       return;
     }
   }
   for (int sb = g_begin; sb < g_end; sb += a.sk)
-    stream_slice<TT, RT, VS, SHARED, LAY, false>(a, cp, sp, xs, sb, min(g_end, sb + a.sk), sb == g_begin, trow,
-                                                 kq, acc);
+    stream_slice<TT, RT, VS, SHARED, LAY, false>(a, cp, cb, sp, xs, sb, min(g_end, sb + a.sk), sb == g_begin,
+                                                 trow, kq, acc);
 }
 
 // Code and scale pointers of the RT tiles starting at output row row0 for
-// this lane.  Row-major: the row's codes and scales.  Tiled: the lane's
-// 16 bytes in the first group block of the row's tile, and the row's 16
-// bytes in the first scale block.
+// this lane.  Row-major: the row's codes (quarter kq) and scales.  Tiled:
+// the lane's 16 bytes in the first group block of the row's tile, and the
+// row's 16 bytes in the first scale block.  kLayRow: cp and cb point at the
+// codes (quarter kq) of rows l & 7 and 8 + (l & 7) of the tile, one of which
+// is the lane's own row l & 15; sp at its own row's scales.  Elsewhere cb =
+// cp.
 template <int RT, int LAY>
 __device__ __forceinline__ void tile_pointers(const GemvArgs& a, int64_t row0, int r16, int kq,
-                                              const u4_t* (&cp)[RT], const uint16_t* (&sp)[RT]) {
+                                              const u4_t* (&cp)[RT], const u4_t* (&cb)[RT],
+                                              const uint16_t* (&sp)[RT]) {
   const int64_t kh = a.K >> 1;
 #pragma unroll
   for (int tl = 0; tl < RT; ++tl) {
+    if constexpr (LAY == kLayRow) {
+      const int64_t r0 = row0 + tl * 16 + (r16 & 7);
+      int64_t wa = weight_row(a, r0), wb = weight_row(a, r0 + 8);
+      wa = wa < 0 ? 0 : wa;  // read a valid row; the output is masked later
+      wb = wb < 0 ? 0 : wb;
+      cp[tl] = reinterpret_cast<const u4_t*>(a.packed + wa * kh) + kq;
+      cb[tl] = reinterpret_cast<const u4_t*>(a.packed + wb * kh) + kq;
+      sp[tl] = a.scales + (r16 >= 8 ? wb : wa) * a.G;
+      continue;
+    }
     int64_t w = weight_row(a, row0 + tl * 16 + r16);
     if (w < 0) w = 0;  // read a valid row; the output is masked later
-    if (LAY == kLayTiled || a.tiled) {
+    if (tiled_rows<LAY>(a)) {
       const uint8_t* tb = a.packed + (w >> 4) * a.tile_bytes;
       cp[tl] = reinterpret_cast<const u4_t*>(tb) + 4 * (w & 15) + kq;
       sp[tl] = reinterpret_cast<const uint16_t*>(tb) + 8 * (w & 15);
@@ -1057,6 +1154,7 @@ __device__ __forceinline__ void tile_pointers(const GemvArgs& a, int64_t row0, i
       cp[tl] = reinterpret_cast<const u4_t*>(a.packed + w * kh) + kq;
       sp[tl] = a.scales + w * a.G;
     }
+    cb[tl] = cp[tl];
   }
 }
 
@@ -1071,8 +1169,9 @@ __device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, u
   const int trow = min(r16, TT - 1);  // A rows >= TT only feed D rows that are never read
   const int64_t row0 = wg * (RT * 16);
   const u4_t* cp[RT];
+  const u4_t* cb[RT];
   const uint16_t* sp[RT];
-  tile_pointers<RT, LAY>(a, row0, r16, kq, cp, sp);
+  tile_pointers<RT, LAY>(a, row0, r16, kq, cp, cb, sp);
   const int g_begin = wave * a.gpw;
   const int g_end = (wave < a.nw) ? min(a.G, g_begin + a.gpw) : g_begin;  // uniform
   unsigned char* xs = smem + wave * a.wave_lds;
@@ -1084,9 +1183,9 @@ __device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, u
     for (int r = 0; r < 4; ++r) acc[tl][r] = 0.0f;
   if (g_end > g_begin) {
     if (LAY == kLayTiled || a.vec_scales)
-      stream_tiles<TT, RT, true, false, LAY>(a, cp, sp, xs, g_begin, g_end, trow, kq, acc);
+      stream_tiles<TT, RT, true, false, LAY>(a, cp, cb, sp, xs, g_begin, g_end, trow, kq, acc);
     else if constexpr (LAY != kLayTiled)
-      stream_tiles<TT, RT, false, false, LAY>(a, cp, sp, xs, g_begin, g_end, trow, kq, acc);
+      stream_tiles<TT, RT, false, false, LAY>(a, cp, cb, sp, xs, g_begin, g_end, trow, kq, acc);
   }
 
   // Split-K partials of this wave -> its own LDS area: red[(tl*TT + t)*16 + row].
@@ -1137,8 +1236,9 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
   const int trow = min(r16, TT - 1);
   const int64_t row_w = (wg * nwv + wave) * (int64_t)(RT * 16);  // first row of this wave
   const u4_t* cp[RT];
+  const u4_t* cb[RT];
   const uint16_t* sp[RT];
-  tile_pointers<RT, LAY>(a, row_w, r16, kq, cp, sp);
+  tile_pointers<RT, LAY>(a, row_w, r16, kq, cp, cb, sp);
   unsigned char* xs = smem;
 
   float acc[RT][4];
@@ -1147,9 +1247,9 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) acc[tl][r] = 0.0f;
   if (LAY == kLayTiled || a.vec_scales)
-    stream_tiles<TT, RT, true, true, LAY>(a, cp, sp, xs, 0, a.G, trow, kq, acc);
+    stream_tiles<TT, RT, true, true, LAY>(a, cp, cb, sp, xs, 0, a.G, trow, kq, acc);
   else if constexpr (LAY != kLayTiled)
-    stream_tiles<TT, RT, false, true, LAY>(a, cp, sp, xs, 0, a.G, trow, kq, acc);
+    stream_tiles<TT, RT, false, true, LAY>(a, cp, cb, sp, xs, 0, a.G, trow, kq, acc);
 
   float bv[TT];
   int bi[TT];
@@ -1525,7 +1625,15 @@ hipError_t launch_rt(const GemvArgs& a, const GemvArgs* table, int count, const 
       if (p.rt == 2) return launch_tiles<TT, 2, false, kLayTiled>(a, table, count, p, s);
     return hipErrorInvalidValue;
   }
-  switch (p.rt) {
+  if (p.rowmajor) {  // row-major-only kernels: paired whole-line loads
+    switch (p.rt) {
+      case 1: return launch_tiles<TT, 1, SHARED, kLayRow>(a, table, count, p, s);
+      case 2: return launch_tiles<TT, 2, SHARED, kLayRow>(a, table, count, p, s);
+      case 4: return launch_tiles<TT, 4, SHARED, kLayRow>(a, table, count, p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  switch (p.rt) {  // a grouped launch mixing both layouts
     case 1: return launch_tiles<TT, 1, SHARED, kLayAny>(a, table, count, p, s);
     case 2: return launch_tiles<TT, 2, SHARED, kLayAny>(a, table, count, p, s);
     case 4: return launch_tiles<TT, 4, SHARED, kLayAny>(a, table, count, p, s);

@@ -71,6 +71,7 @@ struct Plan {
   int64_t grid;  // workgroups
   int lds;       // dynamic LDS bytes
   bool tiled;    // every problem is in the tiled layout: kernels built for it alone
+  bool rowmajor; // every problem is row-major: kernels built for it alone
 };
 
 // Parse "split,rt,waves" or "shared,rt,waves" (rt 1, 2 or 4; waves 1-8, or
@@ -88,11 +89,12 @@ bool set_tile_override(bool batch, const char* spec);
 Plan plan_mfma(GemvArgs& a, int T, int cus);  // default matrix-core tiling of one launch (cus: CUs of the device)
 Plan plan_dot(GemvArgs& a, int T);
 // tiled_kernel: the launch runs the kernels built for the tiled layout only
-// (every problem tiled; one tile per wave), else the kernels that read
-// either layout.
+// (every problem tiled; one tile per wave); row_kernel: those built for the
+// row-major layout only (every problem row-major); neither: the kernels
+// that read either layout (a grouped launch mixing them).
 // batch: planning one problem of a grouped launch (a run tile whose
 // activations do not fit stays a run-kernel problem with run_tiles = 0).
-Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel, bool batch);
+Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel, bool row_kernel, bool batch);
 // Waves of a shared workgroup of one tile per wave: 16 (one workgroup per CU,
 // up to 160 KB of LDS) when T rows of K activations need more than 80 KB,
 // else 4 at T = 1 and 8 above (MI355X sweeps of the tiled layout).

@@ -260,9 +260,10 @@ static bool plan_run(GemvArgs& a, int T, int nt, int nwv, Plan* p) {
   return true;
 }
 
-Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel, bool batch) {
+Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel, bool row_kernel, bool batch) {
   Plan p{};
   p.variant = t.shape;
+  p.rowmajor = row_kernel && !tiled_kernel;
   // the tiled-layout kernels stream one tile per wave (two in split workgroups)
   p.rt = tiled_kernel && !(t.shape == kSplit && t.rt == 2) ? 1 : t.rt;
   p.tiled = tiled_kernel;
@@ -401,7 +402,7 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
   else
     t = Tile{kSplit, 1, (int)std::min<int64_t>(8, std::max<int64_t>(1, cdiv(12LL * std::max(cus, 1), tiles)))};
   tile_override(false, &t);
-  return plan_tile(a, T, t, a.tiled != 0, false);
+  return plan_tile(a, T, t, a.tiled != 0, a.tiled == 0, false);
 }
 
 // Tiling of the dot variant: 2 rows per wave (32 lanes per row), 8 waves,

@@ -378,8 +378,8 @@ w4a16_status w4a16_stream_read(const void* src, size_t bytes, uint32_t* sink, in
  * choice for subsequent calls in this process, of single launches (batch 0)
  * or grouped launches (batch 1), by spec = "split,rt,waves" or
  * "shared,rt,waves" (rt 1, 2 or 4; waves 1-8, or 1-16 for shared workgroups
- * of one tile) or "run,tiles,waves" (tiles per wave 1-16, waves 1-16;
- * tiled weights only: row-major weights take shared workgroups of one tile
+ * of one tile) or "run,tiles,waves" (tiles per wave 1-16, waves 1-16; a
+ * grouped launch mixing both layouts takes shared workgroups of one tile
  * per wave with that many waves instead); NULL or "" restores the planner's
  * choice.  The environment variables
  * W4A16_TILE and W4A16_BATCH_TILE, read once per process, set the initial

@@ -188,19 +188,21 @@ static_assert(sizeof(ArgmaxRecord) == 32 && sizeof(w4a16::GemvArgs) == 144, "bat
 // 27B-class body pass: +2.8% at T = 5, +0.8% at T = 8 against sixteen waves
 // of four), sixteen waves of four above T = 8, a problem whose activations
 // do not fit running shared workgroups inside the same kernel.
-// Every problem row-major: shared workgroups of two 16-row tiles per wave,
-// four waves at T = 1 and eight above (27B-class body pass: 75.3 / 71.7 /
-// 66.3 / 58.1% of 8 TB/s at T = 2 / 4 / 8 / 16 against 70.7 / 66.3 / 60.3 /
-// 56.1% for four waves of four tiles).  Both layouts mixed: four waves of
-// two tiles at T = 1, of four from T = 2 (the same pass row-major with the
-// either-layout kernels: +5.6% at T = 8, +8.3% at T = 4 against eight waves
-// of four).  W4A16_BATCH_TILE = "split|shared|run,rt,waves" overrides it
-// (for measurement).
+// Every problem row-major: up to T = 2 shared workgroups of two 16-row
+// tiles per wave, four waves at T = 1 and eight at T = 2 (27B-class body
+// pass: 75.3% of 8 TB/s at T = 2 against 70.7% for four waves of four
+// tiles), above that the tiled layout's runs (at T = 4 / 8 / 16: 71.4 /
+// 64.7 / 58.5% against 70.7 / 63.1 / 56.2% for eight waves of two tiles).
+// Both layouts mixed: four waves of two tiles at T = 1, of four from T = 2
+// (the same pass row-major with the either-layout kernels: +5.6% at T = 8,
+// +8.3% at T = 4 against eight waves of four).  W4A16_BATCH_TILE =
+// "split|shared|run,rt,waves" overrides it (for measurement).
 w4a16::Tile batch_tile(int T, bool all_tiled, bool all_row, int64_t kmax) {
   w4a16::Tile t;
-  if (all_tiled)
-    t = T <= 2 ? w4a16::Tile{w4a16::kShared, 1, w4a16::shared_waves(T, kmax)}
-               : w4a16::Tile{w4a16::kRun, T <= 4 ? 4 : T <= 8 ? 6 : 4, T <= 8 ? 8 : 16};
+  if ((all_tiled || all_row) && T > 2)
+    t = w4a16::Tile{w4a16::kRun, T <= 4 ? 4 : T <= 8 ? 6 : 4, T <= 8 ? 8 : 16};
+  else if (all_tiled)
+    t = w4a16::Tile{w4a16::kShared, 1, w4a16::shared_waves(T, kmax)};
   else if (all_row)
     t = w4a16::Tile{w4a16::kShared, 2, T == 1 ? 4 : 8};
   else
@@ -235,7 +237,7 @@ w4a16_status run_batch(const void* table_host, const void* table_dev, hipStream_
     return W4A16_ERR_BAD_SHAPE;
   // layout of the launch's kernels: 0 either (mixed), 1 tiled (one tile per wave), 2 row-major
   if (hdr->tiled < 0 || hdr->tiled > 2 || (hdr->tiled == 1 && hdr->rt != 1)) return W4A16_ERR_BAD_SHAPE;
-  if (hdr->variant == w4a16::kRun && hdr->tiled != 1) return W4A16_ERR_BAD_SHAPE;  // runs read tiled weights only
+  if (hdr->variant == w4a16::kRun && hdr->tiled == 0) return W4A16_ERR_BAD_SHAPE;  // runs read one layout
   if (w4a16_status s = check_device()) return s;
   p.variant = hdr->variant;
   p.rt = hdr->rt;

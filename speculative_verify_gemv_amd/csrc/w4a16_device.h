@@ -933,35 +933,34 @@ __device__ __forceinline__ void slice_tiles(const GemvArgs& a, const u4_t* const
         svn = ld_global(reinterpret_cast<const u4_t*>(base) + scale_off<LAY>(a, gv));
         __builtin_amdgcn_sched_barrier(0);
       }
-      // the scale of slot s (group gl of the slice; groups past n read the
-      // zeroed padding and get scale 0)
-      auto scale_at = [&](int s, int gl) {
-        float sc;
-        if constexpr (VS)
-          sc = scale_of(sv, s);
-        else
-          sc = bf16_to_f32(sq[s]);
-        return (gl < n) ? sc : 0.0f;
-      };
-      // reload slot s (group gl) with the group PD positions ahead
-      auto reload_slot = [&](int s, int gl) {
-        const int tgt = gl + PD;
-        const bool nxt = tgt >= np;
-        const bool on = nxt && has_next;
-        const int gg = sb + (nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1));
-        if constexpr (!VS) sq[s] = ld_global((on ? spn : sp[tl]) + gg);
-        q[s] = load_slot<LAY>(a, on ? cpn : cp[tl], on ? cbn : cb[tl], s, gg);
-      };
       if constexpr (LAY == kLayRow) {
 #pragma unroll
         for (int s = 0; s < PD; s += 2) {
-          const int gl = fi + s;
-          const float sc0 = scale_at(s, gl), sc1 = scale_at(s + 1, gl + 1);
+          const int gl = fi + s;  // groups past n read the zeroed padding
+          float sc0, sc1;
+          if constexpr (VS) {
+            sc0 = scale_of(sv, s);
+            sc1 = scale_of(sv, s + 1);
+          } else {
+            sc0 = bf16_to_f32(sq[s]);
+            sc1 = bf16_to_f32(sq[s + 1]);
+          }
+          sc0 = (gl < n) ? sc0 : 0.0f;
+          sc1 = (gl + 1 < n) ? sc1 : 0.0f;
           u4_t w0, w1;
           pair_groups(q[s], q[s + 1], w0, w1);
           if constexpr (R) {
-            reload_slot(s, gl);
-            reload_slot(s + 1, gl + 1);
+            // reload the pair's slots with the groups PD positions ahead
+            const int tgt = gl + PD;
+            const bool nxt = tgt >= np;
+            const bool on = nxt && has_next;
+            const int gg = sb + (nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1));
+            if constexpr (!VS) {
+              sq[s] = ld_global((on ? spn : sp[tl]) + gg);
+              sq[s + 1] = ld_global((on ? spn : sp[tl]) + min(gg + 1, a.G - 1));
+            }
+            q[s] = load_slot<LAY>(a, on ? cpn : cp[tl], on ? cbn : cb[tl], s, gg);
+            q[s + 1] = load_slot<LAY>(a, on ? cpn : cp[tl], on ? cbn : cb[tl], s + 1, gg);
             __builtin_amdgcn_sched_barrier(0);
           }
           const f4_t d0 = group_mfma<H>(xb, gl, w0);
@@ -974,13 +973,24 @@ __device__ __forceinline__ void slice_tiles(const GemvArgs& a, const u4_t* const
       } else {
 #pragma unroll
         for (int s = 0; s < PD; ++s) {
-          const int gl = fi + s;
-          const float sc = scale_at(s, gl);
+          const int gl = fi + s;  // groups past n read the zeroed padding
+          float sc;
+          if constexpr (VS)
+            sc = scale_of(sv, s);
+          else
+            sc = bf16_to_f32(sq[s]);
+          sc = (gl < n) ? sc : 0.0f;
           const f4_t d = group_mfma<H>(xb, gl, q[s]);
 #pragma unroll
           for (int r = 0; r < 4; ++r) accs[r] = fmaf(d[r], sc, accs[r]);
           if constexpr (R) {
-            reload_slot(s, gl);
+            // reload this slot with the group PD positions ahead
+            const int tgt = gl + PD;
+            const bool nxt = tgt >= np;
+            const u4_t* cpl = (nxt && has_next) ? cpn : cp[tl];
+            const int gg = sb + (nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1));
+            if constexpr (!VS) sq[s] = ld_global(((nxt && has_next) ? spn : sp[tl]) + gg);
+            q[s] = load_codes<LAY>(cpl + code_off<LAY>(a, gg));
             // keep this slot's reload here: sunk to the end of the loop, the
             // reloads would make every iteration wait for the whole ring
             __builtin_amdgcn_sched_barrier(0);
@@ -1324,13 +1334,25 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
 // bv[r] / bi[r].
 
 // Code and scale pointers of tile v (rows 16v .. 16v+15) for this lane; returns
-// the lane's weight row (-1: past the end or an invalid id).
+// the lane's weight row (-1: past the end or an invalid id).  kLayRow: cp and
+// cb point at rows l & 7 and 8 + (l & 7) of the tile (tile_pointers); else
+// cb = cp.
 template <int LAY>
 __device__ __forceinline__ int tile_ptr(const GemvArgs& a, int64_t v, int r16, int kq, const u4_t*& cp,
-                                        const uint16_t*& sp) {
+                                        const u4_t*& cb, const uint16_t*& sp) {
+  if constexpr (LAY == kLayRow) {
+    const int64_t r0 = v * 16 + (r16 & 7);
+    const int64_t wa_out = weight_row(a, r0), wb_out = weight_row(a, r0 + 8);
+    const int64_t wa = wa_out < 0 ? 0 : wa_out, wb = wb_out < 0 ? 0 : wb_out;  // valid rows; outputs masked
+    const int64_t kh = a.K >> 1;
+    cp = reinterpret_cast<const u4_t*>(a.packed + wa * kh) + kq;
+    cb = reinterpret_cast<const u4_t*>(a.packed + wb * kh) + kq;
+    sp = a.scales + (r16 >= 8 ? wb : wa) * a.G;
+    return (int)(r16 >= 8 ? wb_out : wa_out);
+  }
   const int64_t w_out = weight_row(a, v * 16 + r16);
   const int64_t w = w_out < 0 ? 0 : w_out;  // read a valid row; the output is masked
-  if (LAY == kLayTiled || a.tiled) {
+  if (tiled_rows<LAY>(a)) {
     const uint8_t* tb = a.packed + (w >> 4) * a.tile_bytes;
     cp = reinterpret_cast<const u4_t*>(tb) + 4 * (w & 15) + kq;
     sp = reinterpret_cast<const uint16_t*>(tb) + 8 * (w & 15);
@@ -1338,16 +1360,17 @@ __device__ __forceinline__ int tile_ptr(const GemvArgs& a, int64_t v, int r16, i
     cp = reinterpret_cast<const u4_t*>(a.packed + w * (int64_t)(a.K >> 1)) + kq;
     sp = a.scales + w * a.G;
   }
+  cb = cp;
   return (int)w_out;
 }
 
 template <int LAY>
-__device__ __forceinline__ void ring_prologue(const GemvArgs& a, const u4_t* cp, const uint16_t* sp,
+__device__ __forceinline__ void ring_prologue(const GemvArgs& a, const u4_t* cp, const u4_t* cb, const uint16_t* sp,
                                               u4_t (&q)[kRing], u4_t& sv) {
   sv = ld_global(reinterpret_cast<const u4_t*>(sp) + scale_off<LAY>(a, 0));
 #pragma unroll
   for (int s = 0; s < kRing; ++s) {
-    q[s] = load_codes<LAY>(cp + code_off<LAY>(a, min(s, a.G - 1)));
+    q[s] = load_slot<LAY>(a, cp, cb, s, min(s, a.G - 1));
     __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
   }
 }
@@ -1380,12 +1403,15 @@ __device__ __forceinline__ void exact_run_tiles(const GemvArgs& a, int64_t v, in
                                                 int (&bi)[4]) {
   const unsigned char* xb[4];
   lane_chunks(a, xs, trow, kq, xb);
+  // kLayRow: this lane's own row is row l & 7 of cp or 8 + (l & 7) of cb
+  const bool own_b = LAY == kLayRow && r16 >= 8;
   for (; v < v_end; v += step) {  // uniform
     const u4_t* cp;
+    const u4_t* cb;
     const uint16_t* sp;
-    const int w_cur = tile_ptr<LAY>(a, v, r16, kq, cp, sp);
+    const int w_cur = tile_ptr<LAY>(a, v, r16, kq, cp, cb, sp);
     float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    exact_groups<LAY>(a, cp, sp, xb, 0, a.G, accs);
+    exact_groups<LAY>(a, own_b ? cb : cp, sp, xb, 0, a.G, accs);
     tile_outputs<TT>(a, v, r16, kq, w_cur, accs, kLevelScale, bv, bi);
   }
 }
@@ -1393,8 +1419,8 @@ __device__ __forceinline__ void exact_run_tiles(const GemvArgs& a, int64_t v, in
 template <int TT, int LAY, bool H>
 __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t v_end, int step,
                                           const unsigned char* xs, int r16, int kq, int trow, const u4_t* cp,
-                                          const uint16_t* sp, u4_t (&q)[kRing], u4_t& sv, float fold,
-                                          float (&bv)[4], int (&bi)[4]) {
+                                          const u4_t* cb, const uint16_t* sp, u4_t (&q)[kRing], u4_t& sv,
+                                          float fold, float (&bv)[4], int (&bi)[4]) {
   constexpr int PD = kRing;
   const int n = a.G;
   const int np = (n + PD - 1) / PD * PD;
@@ -1405,9 +1431,10 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
     const int64_t vn = v + step;
     const bool has_next = vn < v_end;
     const u4_t* cpn = cp;
+    const u4_t* cbn = cb;
     const uint16_t* spn = sp;
     int w_next = -1;
-    if (has_next) w_next = tile_ptr<LAY>(a, vn, r16, kq, cpn, spn);
+    if (has_next) w_next = tile_ptr<LAY>(a, vn, r16, kq, cpn, cbn, spn);
     float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     for (int fi = 0; fi < np; fi += PD) {
       const bool last = fi + PD >= np;  // uniform: this cycle prefetches the next tile
@@ -1415,27 +1442,54 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
       const int gv = last ? (has_next ? 0 : fi) : fi + PD;
       const u4_t svn = ld_global(reinterpret_cast<const u4_t*>(sbase) + scale_off<LAY>(a, gv));
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (LAY == kLayRow) {
 #pragma unroll
-      for (int s = 0; s < PD; ++s) {
-        const int gl = fi + s;  // groups past n read the zeroed padding
-        const float sc = (gl < n) ? scale_of(sv, s) : 0.0f;
-        const f4_t d = group_mfma<H>(xb, gl, q[s]);
+        for (int s = 0; s < PD; s += 2) {
+          const int gl = fi + s;  // groups past n read the zeroed padding
+          const float sc0 = (gl < n) ? scale_of(sv, s) : 0.0f;
+          const float sc1 = (gl + 1 < n) ? scale_of(sv, s + 1) : 0.0f;
+          u4_t w0, w1;
+          pair_groups(q[s], q[s + 1], w0, w1);
+          // reload the pair's slots with the groups PD positions ahead (the
+          // next tile's first groups in the last cycle)
+          const int tgt = gl + PD;
+          const bool nxt = tgt >= np;
+          const bool on = nxt && has_next;
+          const int gg = nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1);
+          q[s] = load_slot<LAY>(a, on ? cpn : cp, on ? cbn : cb, s, gg);
+          q[s + 1] = load_slot<LAY>(a, on ? cpn : cp, on ? cbn : cb, s + 1, gg);
+          __builtin_amdgcn_sched_barrier(0);
+          const f4_t d0 = group_mfma<H>(xb, gl, w0);
 #pragma unroll
-        for (int r = 0; r < 4; ++r) accs[r] = fmaf(d[r], sc, accs[r]);
-        // reload this slot with the group PD positions ahead (the next
-        // tile's first groups in the last cycle)
-        const int tgt = gl + PD;
-        const bool nxt = tgt >= np;
-        const u4_t* cpl = (nxt && has_next) ? cpn : cp;
-        const int gg = nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1);
-        q[s] = load_codes<LAY>(cpl + code_off<LAY>(a, gg));
-        __builtin_amdgcn_sched_barrier(0);
+          for (int r = 0; r < 4; ++r) accs[r] = fmaf(d0[r], sc0, accs[r]);
+          const f4_t d1 = group_mfma<H>(xb, gl + 1, w1);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) accs[r] = fmaf(d1[r], sc1, accs[r]);
+        }
+      } else {
+#pragma unroll
+        for (int s = 0; s < PD; ++s) {
+          const int gl = fi + s;  // groups past n read the zeroed padding
+          const float sc = (gl < n) ? scale_of(sv, s) : 0.0f;
+          const f4_t d = group_mfma<H>(xb, gl, q[s]);
+#pragma unroll
+          for (int r = 0; r < 4; ++r) accs[r] = fmaf(d[r], sc, accs[r]);
+          // reload this slot with the group PD positions ahead (the next
+          // tile's first groups in the last cycle)
+          const int tgt = gl + PD;
+          const bool nxt = tgt >= np;
+          const u4_t* cpl = (nxt && has_next) ? cpn : cp;
+          const int gg = nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1);
+          q[s] = load_codes<LAY>(cpl + code_off<LAY>(a, gg));
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
       sv = svn;
     }
     tile_outputs<TT>(a, v, r16, kq, w_cur, accs, fold, bv, bi);
     v = vn;
     cp = cpn;
+    cb = cbn;
     sp = spn;
     w_cur = w_next;
   }
@@ -1444,7 +1498,8 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
 // Run workgroup: a.run_tiles tiles per wave.  Workgroup b owns tiles
 // [b*waves*nt, (b+1)*waves*nt); wave i streams tiles i, i + waves, ... of them,
 // so the waves stay on adjacent tiles.  All of K is staged once (the planner
-// guarantees it fits).  Built for tiled weights only (LAY = kLayTiled).
+// guarantees it fits).  Built for one layout at a time (kLayTiled or
+// kLayRow), eight scales per load.
 template <int TT, int LAY>
 __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
   const int lane = threadIdx.x & 63;
@@ -1457,12 +1512,13 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
   const int64_t v0 = wg * span + wave, v_end = min(tiles, (wg + 1) * span);
   unsigned char* xs = smem;
   const u4_t* cp = nullptr;
+  const u4_t* cb = nullptr;
   const uint16_t* sp = nullptr;
   u4_t q[kRing];
   u4_t sv;
   if (v0 < v_end) {  // the first tile's ring, issued before the staging
-    tile_ptr<LAY>(a, v0, r16, kq, cp, sp);
-    ring_prologue<LAY>(a, cp, sp, q, sv);
+    tile_ptr<LAY>(a, v0, r16, kq, cp, cb, sp);
+    ring_prologue<LAY>(a, cp, cb, sp, q, sv);
   }
   // also waits for the ring's loads; fold: the fp16 form's 2^-E, or 0
   const float fold = stage_slice<TT, true, tries_f16<TT, true>()>(a, xs, 0, a.G);
@@ -1476,11 +1532,11 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
   if (v0 < v_end) {
     if constexpr (tries_f16<TT, true>()) {
       if (fold != 0.0f)
-        run_tiles<TT, LAY, true>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, sp, q, sv, fold, bv, bi);
+        run_tiles<TT, LAY, true>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, cb, sp, q, sv, fold, bv, bi);
       else
         exact_run_tiles<TT, LAY>(a, v0, v_end, nwv, xs, r16, kq, trow, bv, bi);
     } else {
-      run_tiles<TT, LAY, false>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, sp, q, sv, kLevelScale, bv, bi);
+      run_tiles<TT, LAY, false>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, cb, sp, q, sv, kLevelScale, bv, bi);
     }
   }
   if (a.partial) {
@@ -1662,7 +1718,10 @@ hipError_t launch_run(const GemvArgs& a, const GemvArgs* table, int count, const
 // with table set, a grouped launch over `count` problems.
 template <int TT>
 hipError_t launch_t(const GemvArgs& a, const GemvArgs* table, int count, const Plan& p, hipStream_t s) {
-  if (p.variant == kRun) return p.tiled ? launch_run<TT, kLayTiled>(a, table, count, p, s) : hipErrorInvalidValue;
+  if (p.variant == kRun)
+    return p.tiled      ? launch_run<TT, kLayTiled>(a, table, count, p, s)
+           : p.rowmajor ? launch_run<TT, kLayRow>(a, table, count, p, s)
+                        : hipErrorInvalidValue;
   if (p.variant == kSplit) return launch_rt<TT, false>(a, table, count, p, s);
   if (p.variant == kShared) return launch_rt<TT, true>(a, table, count, p, s);
   if (table || p.variant != kDot || p.rt != 2) return hipErrorInvalidValue;

@@ -269,16 +269,17 @@ Plan plan_tile(GemvArgs& a, int T, const Tile& t, bool tiled_kernel, bool row_ke
   p.tiled = tiled_kernel;
   a.vec_scales = (a.tiled || (a.G % 8 == 0 && (reinterpret_cast<uintptr_t>(a.scales) & 15) == 0)) ? 1 : 0;
   if (t.shape == kRun) {
-    // runs are built for tiled weights only: row-major weights take shared
-    // workgroups of one tile per wave instead
+    // runs are built for one layout at a time: a grouped launch mixing the
+    // layouts takes shared workgroups of one tile per wave instead
+    const bool one_layout = tiled_kernel || p.rowmajor;
     p.rt = 1;
-    if (tiled_kernel && plan_run(a, T, t.rt, t.nw, &p)) return p;
+    if (one_layout && plan_run(a, T, t.rt, t.nw, &p)) return p;
     // The activations do not fit: a shared workgroup of one tile per wave
     // stages K in slices.  A grouped launch keeps the run kernel (which
     // runs such problems this way, run_tiles = 0); a single launch switches.
     a.run_tiles = 0;
     plan_shared(a, T, 1, t.nw, &p);
-    p.variant = batch && tiled_kernel ? kRun : kShared;
+    p.variant = batch && one_layout ? kRun : kShared;
     return p;
   }
   if (t.shape == kShared)

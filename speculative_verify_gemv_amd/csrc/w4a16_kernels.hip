@@ -340,8 +340,7 @@ int shared_waves(int T, int64_t K) {
 //     them fills the CUs (the vocabulary head), else 2 tiles x 8 waves; where
 //     the staging is dear (below), one round of 16-wave runs of as many tiles
 //     per wave as that takes, while it keeps three quarters of the CUs busy;
-//   - row-major, >= 4,096 tiles: shared workgroups of 8 waves x 4 tiles
-//     (>= 8,192 tiles) or x 2;
+//   - row-major, >= 4,096 tiles: shared workgroups of 8 waves x 2 tiles;
 //   - 1,024 - 4,095 tiles: shared workgroups of one tile per wave, 4 waves
 //     (8 where that makes one full round); where the staging is dear, one
 //     round of 4, 8 or 16 waves;
@@ -380,9 +379,7 @@ Plan plan_mfma(GemvArgs& a, int T, int cus) {
     }
   } else if (T == 1 && tiles >= 1024 && tiles < 4096 && !a.partial && !a.row_ids)
     t = Tile{kSplit, 1, 4};  // a plain matmul (34,816 x 5,120: 20.3 us against 23.8 for shared workgroups of 4 waves)
-  else if (tiles >= 8192)
-    t = Tile{kShared, 4, 8};
-  else if (tiles >= 4096)
+  else if (tiles >= 4096)  // row-major: 248,320 x 5,120 with argmax, 114.5 us against 118.9 for 4 x 8 at T = 1
     t = Tile{kShared, 2, 8};
   else if (tiles >= 1024 && dear)
     t = Tile{kShared, 1, cdiv(tiles, 4) <= ncu ? 4 : cdiv(tiles, 8) <= ncu ? 8 : 16};

@@ -65,7 +65,7 @@ struct Tile {
 };
 
 struct Plan {
-  int variant;   // kDot, kSplit or kShared
+  int variant;   // kDot, kSplit, kShared or kRun
   int rt;        // 16-row tiles per wave (matrix core) / rows per wave (dot)
   int threads;   // threads per workgroup
   int64_t grid;  // workgroups

@@ -324,3 +324,37 @@ def test_tile_override_parsing(lib):
         for spec in (b"split,1,8", b"shared,4,2", b"run,16,16"):
             assert f(batch, spec) == OK, spec
         assert f(batch, b"") == OK and f(batch, None) == OK
+
+
+def test_batch_plan_kernel_layout(lib):
+    """The table records which kernels a grouped launch runs: built for the
+    tiled layout (every problem tiled), for row-major weights (every problem
+    row-major) or for either (a mix); runs of tiles only for one layout, and
+    a table that asks for runs over both is refused before the device."""
+    lib.w4a16_matmul_batch.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_void_p]
+    lib.w4a16_matmul_batch.restype = ctypes.c_int32
+    K_SHARED, K_RUN = 3, 4  # the header's variant codes
+
+    def header(probs, T):
+        arr = (Problem * len(probs))(*probs)
+        nbytes = lib.w4a16_batch_table_bytes(len(probs))
+        buf = (ctypes.c_uint64 * (nbytes // 8 + 1))()
+        assert lib.w4a16_batch_plan(ctypes.cast(arr, ctypes.c_void_p), len(probs), T, ctypes.addressof(buf),
+                                    nbytes) == OK
+        words = (ctypes.c_int32 * 16).from_buffer(buf)
+        return buf, words  # words[4] variant, words[5] rt, words[6] kernel layout
+
+    row = [Problem(A, A, A, A, 7168, 5120, 0, 0), Problem(A, A, A, A, 5120, 17408, 0, 0)]
+    tiled = [Problem(A, None, A, A, 7168, 5120, 1, 0), Problem(A, None, A, A, 5120, 17408, 1, 0)]
+    mixed = [row[0], tiled[1]]
+    for T in (1, 2, 4, 8, 16):
+        _, w = header(row, T)
+        assert w[6] == 2 and w[4] == (K_SHARED if T <= 2 else K_RUN)
+        _, w = header(tiled, T)
+        assert w[6] == 1 and w[4] == (K_SHARED if T <= 2 else K_RUN)
+        buf, w = header(mixed, T)
+        assert w[6] == 0 and w[4] == K_SHARED
+        w[4] = K_RUN  # runs over a mix of layouts: refused
+        assert lib.w4a16_matmul_batch(ctypes.addressof(buf), A, None) == SHAPE
+        w[4], w[6] = K_SHARED, 3  # an unknown kernel layout: refused
+        assert lib.w4a16_matmul_batch(ctypes.addressof(buf), A, None) == SHAPE

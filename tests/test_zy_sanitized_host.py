@@ -7,14 +7,16 @@ and the CPU test suite runs again in a child process that loads those builds
 (ORACLE_LIB, SYNTH_LIB, W4A16_LIB) with the sanitizer runtime preloaded.  Any
 report (an out-of-bounds access, a use after free, a signed overflow, a bad
 shift, a misaligned access ...) aborts the child and fails this test.  The
-first run after a source change builds for a minute or two; later runs reuse
-the build.  Leak checking is off: the Python interpreter itself is not
-instrumented and keeps its allocations until exit.
+first run after a source change builds for a minute or two (and removes the
+builds of earlier sources); later runs reuse the build.  Leak checking is
+off: the Python interpreter itself is not instrumented and keeps its
+allocations until exit.
 """
 import ctypes
 import glob
 import hashlib
 import os
+import shutil
 import subprocess
 import sys
 
@@ -55,6 +57,12 @@ def _runtime():
 
 
 def _build(out_dir):
+    # builds of earlier sources are of no further use (about 150-250 MB each)
+    parent = os.path.dirname(out_dir)
+    if os.path.isdir(parent):
+        for name in os.listdir(parent):
+            if os.path.join(parent, name) != out_dir:
+                shutil.rmtree(os.path.join(parent, name), ignore_errors=True)
     sys.path.insert(0, ROOT)
     from oracle import build as oracle_build
     from synth import build as synth_build

@@ -18,7 +18,10 @@ replayed from a captured HIP graph, the body pass alone at T = 1, 4, 8 and
 each workload shape (the small matrix, every projection at T = 1, 4, 8, the
 lm_head with argmax, the draft head), the dot-product variant against the
 matrix-core one on the same single launches, the achievable streaming-read
-rate, the verify epilogue, and the CPU oracle's rate on a bounded sample.
+rate, the verify epilogue, and the CPU oracle's rate on a bounded sample
+(cpu_baseline), with the parity of the last timed step against the oracle
+(every output of layer 0 and every lm_head score, the argmax ids), checked
+after the timing.
 
 --pmc-pass runs one untimed step after a 1 GiB device copy (the calibration
 kernel for rocprofv3 FETCH_SIZE/WRITE_SIZE), then one body pass alone at
@@ -211,6 +214,11 @@ def main():
     step_bytes = body_bytes + head_bytes
     ms_step, launch_ms = time_step(step, args.steps, args.warmup)
     K_steps = args.steps
+    # the last timed step's outputs, kept for the parity check of the CPU
+    # baseline leg (layer 0's four projections and the lm_head)
+    torch.cuda.synchronize()
+    step_out = {"layer0": [(proj, y.cpu().numpy()) for (proj, layer, *_), (*_, y) in zip(weights, probs) if layer == 0],
+                "head_y": head_y.cpu().numpy(), "head_id": head_id.cpu().numpy()}
     launch_ms_avg = float(np.mean(launch_ms))
     value = metrics.gbps(step_bytes, ms_step)
     achieved = metrics.gbps(step_bytes, launch_ms_avg)
@@ -310,7 +318,7 @@ def main():
     # ---- CPU baseline: the oracle on a bounded sample of the same pass ----
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(T, args.cpu_seconds)
+        cpu = cpu_baseline(T, args.cpu_seconds, step_out)
 
     out = {
         "metric": METRIC,
@@ -687,9 +695,11 @@ def plain_launch_step(torch, w4a16, probs, head, stream, reps):
     return {"ms_per_step": round(e0.elapsed_time(e1) / reps, 4), "launches": len(probs) + 2}
 
 
-def cpu_baseline(T, target_s):
+def cpu_baseline(T, target_s, step_out=None):
     """The oracle (plain C, fp64) on the host cores, on whole layers of the same
-    pass until about target_s seconds of work, reported as weight GB/s."""
+    pass until about target_s seconds of work, reported as weight GB/s; then,
+    with step_out (host copies of the last timed step's outputs), the parity
+    of that step against the oracle (step_parity)."""
     import oracle
 
     threads = oracle.default_threads()
@@ -719,10 +729,51 @@ def cpu_baseline(T, target_s):
     t1 = time.time() - t
     g1 = metrics.weight_bytes(N, K) / t1 / 1e9
     log(f"CPU oracle, one thread: layer 0 qkv at T={T} in {t1:.1f} s: {g1:.4f} GB/s")
-    return {"value": round(g, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"{layers} of 64 layers (qkv, o, gate_up, down) at T={T}, fp64 oracle, {spent:.1f} s",
-            "single_thread": {"value": round(g1, 4), "unit": "GB/s", "cores": 1,
-                              "sample": f"layer 0 qkv at T={T}, {t1:.1f} s"}}
+    out = {"value": round(g, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"{layers} of 64 layers (qkv, o, gate_up, down) at T={T}, fp64 oracle, {spent:.1f} s",
+           "single_thread": {"value": round(g1, 4), "unit": "GB/s", "cores": 1,
+                             "sample": f"layer 0 qkv at T={T}, {t1:.1f} s"}}
+    if step_out is not None:
+        out["parity"] = step_parity(oracle, T, step_out)
+    return out
+
+
+def step_parity(oracle, T, step_out):
+    """The timed step's outputs against the oracle (after the timing): every
+    output of layer 0's four projections and every lm_head score, as the
+    largest |y_gpu - y_ref| / (1e-3 * sum_k |w*x| + 1e-6) (at most 1 passes),
+    and each row's argmax id against the oracle's, exact unless the oracle's
+    gap between its best and its best other id is below the GPU's error on
+    those two rows (a near tie, counted)."""
+    worst = 0.0
+
+    def ratio(y_gpu, y_ref, a_ref):
+        return float(np.max(np.abs(y_gpu.astype(np.float64) - y_ref) / (1e-3 * a_ref + 1e-6)))
+
+    for proj, y_gpu in step_out["layer0"]:
+        N, K = synth.PROJECTIONS[proj]
+        p, s = synth.weight(synth.tid_layer(0, proj), N, K)
+        x = synth.activations(synth.tid_layer(0, proj), T, K)
+        worst = max(worst, ratio(y_gpu, *oracle.matmul(p, s, x)))
+    hn, hk = synth.LM_HEAD
+    hp, hs = synth.weight(synth.TID_LM_HEAD, hn, hk)
+    hx = synth.activations(synth.TID_LM_HEAD, T, hk)
+    y_ref, a_ref = oracle.matmul(hp, hs, hx)
+    y_gpu = step_out["head_y"]
+    worst = max(worst, ratio(y_gpu, y_ref, a_ref))
+    ref_id, _, gap = oracle.argmax(y_ref)
+    ids = step_out["head_id"]
+    exact = int(np.sum(ids == ref_id))
+    near = 0
+    for t in range(T):
+        if ids[t] != ref_id[t] and ids[t] >= 0:
+            i, j = int(ids[t]), int(ref_id[t])
+            err = abs(float(y_gpu[t, i]) - y_ref[t, i]) + abs(float(y_gpu[t, j]) - y_ref[t, j])
+            near += int(gap[t] < err)
+    log(f"parity of the timed step: max err / tol {worst:.3g}; argmax {exact}/{T} exact, {near} near tie(s)")
+    return {"max_err_over_tol": float(f"{worst:.3g}"), "argmax_match": f"{exact}/{T}", "argmax_near_ties": near,
+            "checked": "every output of layer 0's qkv, o, gate_up and down and every lm_head score of the last "
+                       "timed step; the argmax id of each of its rows"}
 
 
 if __name__ == "__main__":

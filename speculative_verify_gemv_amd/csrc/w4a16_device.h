@@ -647,6 +647,98 @@ __device__ __forceinline__ float stage_f16_shared(const GemvArgs& a, unsigned ch
   return pow2(-e);
 }
 
+// Workgroup staging through registers, for slices of at most kStageRegs
+// 16-byte chunks per thread: every chunk load is issued up front, before
+// the weight ring, so the activations arrive in one memory round trip that
+// overlaps the ring's own instead of queueing behind it in dependent
+// batches.  Thread tid holds chunks c = tid + i * nthreads of the slice (row
+// t = c / n8, chunk c - t * n8 of the row); threads past the slice's end
+// re-read its last chunk (harmless to the range, never stored).
+constexpr int kStageRegs = 12;
+
+template <int TT>
+__device__ __forceinline__ void prefetch_slice(const GemvArgs& a, int gs, int ge, u4_t (&xr)[kStageRegs]) {
+  const int n8 = (ge - gs) * (kGroup / 8), total = TT * n8;
+  const int nthreads = blockDim.x;
+  const u4_t* src = reinterpret_cast<const u4_t*>(a.x + (int64_t)gs * kGroup);
+  int t = 0, b = threadIdx.x;  // t * n8 + b = this thread's chunk c
+  while (b >= n8 && t < TT) {
+    b -= n8;
+    ++t;
+  }
+#pragma unroll
+  for (int i = 0; i < kStageRegs; ++i) {
+    if (i * nthreads < total) {  // uniform
+      const bool in = t < TT;    // c < total (then b < n8)
+      xr[i] = ld_global(src + (in ? t * (a.K / 8) + b : (TT - 1) * (a.K / 8) + n8 - 1));
+      b += nthreads;
+      while (b >= n8 && t < TT) {
+        b -= n8;
+        ++t;
+      }
+    }
+  }
+}
+
+// Stages the prefetched slice for the whole workgroup (all of its values,
+// then the ring padding) and returns the level form to run: the fp16 form's
+// fold 2^-E when some E makes every value exact in fp16 (the one nearest
+// kDirectE: direct_exponent over the workgroup's range, reduced through two
+// LDS words per wave), else 0 with the bf16 values staged as they are.
+// Ends before the barrier that publishes the staged values (the caller's).
+template <int TT>
+__device__ __forceinline__ float stage_regs_shared(const GemvArgs& a, unsigned char* xs, int gs, int ge,
+                                                   const u4_t (&xr)[kStageRegs], bool f16) {
+  const int n8 = (ge - gs) * (kGroup / 8), total = TT * n8;
+  const int nthreads = blockDim.x;
+  const int dst_row = a.xs_stride / 8;
+  u4_t* dst = reinterpret_cast<u4_t*>(xs);
+  int e = kNoDirect;
+  if (f16) {
+    us2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};
+#pragma unroll
+    for (int i = 0; i < kStageRegs; ++i)
+      if (i * nthreads < total) range8(xr[i], mx, mn);
+    // the workgroup's range: two words per wave at the start of the staging
+    // area (nothing is staged before the decision)
+    unsigned* words = reinterpret_cast<unsigned*>(xs);
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const unsigned wmax = wave_umax(max(mx.x, mx.y)), wmin = wave_umin(min(mn.x, mn.y));
+    if ((threadIdx.x & 63) == 0) {
+      words[2 * wave] = wmax;
+      words[2 * wave + 1] = wmin;
+    }
+    __syncthreads();
+    unsigned gmax = 0, gmin = 0xFFFFFFFFu;
+    for (int w = 0; w < (nthreads >> 6); ++w) {
+      gmax = max(gmax, words[2 * w]);
+      gmin = min(gmin, words[2 * w + 1]);
+    }
+    e = direct_exponent(__builtin_amdgcn_readfirstlane(gmax), __builtin_amdgcn_readfirstlane(gmin));
+    __syncthreads();  // every wave has read the words before the staging overwrites them
+  }
+  const bool h = e != kNoDirect;
+  const float k = h ? pow2(e) : 0.0f;
+  int t = 0, b = threadIdx.x;
+  while (b >= n8 && t < TT) {
+    b -= n8;
+    ++t;
+  }
+#pragma unroll
+  for (int i = 0; i < kStageRegs; ++i) {
+    if (i * nthreads < total) {  // uniform
+      if (t < TT) dst[t * dst_row + swz(t, b)] = h ? convert8_f16(xr[i], k) : xr[i];
+      b += nthreads;
+      while (b >= n8 && t < TT) {
+        b -= n8;
+        ++t;
+      }
+    }
+  }
+  zero_pad<TT>(a, xs, ge - gs, threadIdx.x, nthreads);
+  return h ? pow2(-e) : 0.0f;
+}
+
 // RW rows per wave, L = 64/RW lanes per row; a lane takes the row's 16-byte
 // chunks li, li+L, li+2L, ...; CPL bounds the chunks per lane per slice.
 // Built for TT <= kDotMaxT (its per-lane sums grow with TT; more rows go to
@@ -1516,12 +1608,23 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
   const uint16_t* sp = nullptr;
   u4_t q[kRing];
   u4_t sv;
-  if (v0 < v_end) {  // the first tile's ring, issued before the staging
+  // activations that fit kStageRegs chunks per thread are loaded first, then
+  // the first tile's ring, then staged from the registers; larger ones are
+  // staged after the ring is issued.  fold: the fp16 form's 2^-E, or 0
+  const bool regs = TT * a.G * (kGroup / 8) <= kStageRegs * (int)blockDim.x;  // uniform
+  u4_t xr[kStageRegs];
+  if (regs) prefetch_slice<TT>(a, 0, a.G, xr);
+  if (v0 < v_end) {
     tile_ptr<LAY>(a, v0, r16, kq, cp, cb, sp);
     ring_prologue<LAY>(a, cp, cb, sp, q, sv);
   }
-  // also waits for the ring's loads; fold: the fp16 form's 2^-E, or 0
-  const float fold = stage_slice<TT, true, tries_f16<TT, true>()>(a, xs, 0, a.G);
+  float fold;
+  if (regs) {
+    fold = stage_regs_shared<TT>(a, xs, 0, a.G, xr, tries_f16<TT, true>());
+    __syncthreads();
+  } else {
+    fold = stage_slice<TT, true, tries_f16<TT, true>()>(a, xs, 0, a.G);  // also waits for the ring's loads
+  }
   float bv[4];
   int bi[4];
 #pragma unroll

@@ -16,8 +16,11 @@
  *     y[t][n] = sum_k (q[n][k] - 8) * scale[n][k/128] * x[t][k].
  *
  * Each level (q - 8) and each product with x is formed exactly, for every
- * finite bf16 x (the activations stay bf16; the matrix cores multiply them
- * with bf16 levels); sums are fp32, with a fresh partial per 128-column group
+ * finite bf16 x: the matrix cores multiply exact levels with the staged
+ * activations, as fp16 times a power of two where every value of the staged
+ * block converts exactly, else as the bf16 values they are; sums are fp32
+ * (scaled by that power of two and back, which rounds as the unscaled sums
+ * would), with a fresh partial per 128-column group
  * multiplied by that group's scale (the same section: the scale multiplies,
  * in fp32, the sum of the group's products).  Results agree with the exact
  * sum within 1e-3 * sum_k |w*x| + 1e-6 per element, for any finite inputs

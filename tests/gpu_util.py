@@ -1,4 +1,5 @@
 """Shared helpers of the GPU parity tests (host-side comparison only)."""
+import contextlib
 import sys
 
 import numpy as np
@@ -11,6 +12,26 @@ import synth
 def say(*a):
     print(*a, flush=True)
     sys.stdout.flush()
+
+
+@contextlib.contextmanager
+def forced_tile(w4, spec, batch: bool = False):
+    """Runs the body with the tiling of single launches (batch=True: grouped
+    launches) forced to `spec` through the library's run-time override, then
+    gives the choice back to the planner.  (W4A16_TILE / W4A16_BATCH_TILE are
+    read once per process, at the first plan: setting them inside a test does
+    not reach the library.)"""
+    w4.set_tile(spec, batch=batch)
+    try:
+        yield
+    finally:
+        w4.set_tile(None, batch=batch)
+
+
+def batch_variant(b) -> int:
+    """The kernel shape a grouped launch's table records (2 split, 3 shared,
+    4 runs of tiles): the fifth 32-bit word of its header."""
+    return int(b.host[16:20].view(torch.int32)[0])
 
 
 def dev(a: np.ndarray) -> torch.Tensor:

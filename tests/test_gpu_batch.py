@@ -6,7 +6,9 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import assert_parity, dev, host, say, sample_rows
+import contextlib
+
+from gpu_util import assert_parity, batch_variant, dev, forced_tile, host, say, sample_rows
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -45,14 +47,13 @@ def check_outputs(probs, host_side, what):
 
 @pytest.mark.parametrize("tile", [None, "shared,1,4", "split,1,4", "split,4,2", "split,2,8", "shared,1,16", "run,2,8", "run,6,8", "run,3,16"])
 @pytest.mark.parametrize("T", [1, 4, 8, 16])
-def test_batch_matches_oracle(w4, tile, T, monkeypatch):
-    if tile is not None:
-        monkeypatch.setenv("W4A16_BATCH_TILE", tile)
-    else:
-        monkeypatch.delenv("W4A16_BATCH_TILE", raising=False)
+def test_batch_matches_oracle(w4, tile, T):
     say(f"batch tile={tile} T={T}")
     probs, host_side = build_case(T, 600 + 10 * T)
-    b = w4.Batch(probs, T)
+    with forced_tile(w4, tile, batch=True) if tile else contextlib.nullcontext():
+        b = w4.Batch(probs, T)
+    if tile:  # the table runs the forced shape
+        assert batch_variant(b) == {"split": 2, "shared": 3, "run": 4}[tile.split(",")[0]]
     b.run()
     check_outputs(probs, host_side, f"batch {tile} T={T}")
     first = [host(y).copy() for *_, y in probs]
@@ -62,11 +63,10 @@ def test_batch_matches_oracle(w4, tile, T, monkeypatch):
 
 
 @pytest.mark.parametrize("T", [3, 5, 6, 7, 8])
-def test_batch_tiled_default_matches_oracle(w4, T, monkeypatch):
+def test_batch_tiled_default_matches_oracle(w4, T):
     """The grouped launch's own tiling for tiled weights around the switch
     between four and six tiles per wave (eight-wave run workgroups; the
     17,408-column problem runs sliced shared workgroups in the same kernel)."""
-    monkeypatch.delenv("W4A16_BATCH_TILE", raising=False)
     say(f"batch tiled default T={T}")
     probs, host_side = build_case(T, 650 + T)
     probs = [(w4.repack_tiled(pp, ss), None, xx, yy) for pp, ss, xx, yy in probs]

@@ -13,7 +13,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import assert_parity, dev, host, say, sample_rows, weight_dev
+from gpu_util import assert_parity, dev, forced_tile, host, say, sample_rows, weight_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -140,18 +140,18 @@ def test_dot_selection_runs_matrix_cores_above_8(w4):
 
 @pytest.mark.parametrize("tile", ["split,1,8", "split,2,3", "shared,1,1", "shared,4,4", "shared,1,16", "run,3,4",
                                   "run,4,16"])
-def test_tile_shapes_t16(w4, tile, monkeypatch):
-    monkeypatch.setenv("W4A16_TILE", tile)
-    for N, K, T in [(37, 1152, 16), (300, 17408, 16), (4099, 5120, 14)]:
-        say(f"tile {tile} N={N} K={K} T={T}")
-        tid = 5200 + N + K + T
-        p, s = synth.weight(tid, N, K)
-        x = synth.activations(tid, T, K)
-        rows = sample_rows(N, 300, seed=tid) if N > 2048 else np.arange(N, dtype=np.int32)
-        y_ref, a_ref = oracle.gather(rows, p, s, x)
-        y_rm, y_t = both_layouts(w4, p, s, x)
-        assert_parity(y_rm[:, rows], y_ref, a_ref, f"{tile} row-major N={N} K={K} T={T}")
-        assert_parity(y_t[:, rows], y_ref, a_ref, f"{tile} tiled N={N} K={K} T={T}")
+def test_tile_shapes_t16(w4, tile):
+    with forced_tile(w4, tile):
+        for N, K, T in [(37, 1152, 16), (300, 17408, 16), (4099, 5120, 14)]:
+            say(f"tile {tile} N={N} K={K} T={T}")
+            tid = 5200 + N + K + T
+            p, s = synth.weight(tid, N, K)
+            x = synth.activations(tid, T, K)
+            rows = sample_rows(N, 300, seed=tid) if N > 2048 else np.arange(N, dtype=np.int32)
+            y_ref, a_ref = oracle.gather(rows, p, s, x)
+            y_rm, y_t = both_layouts(w4, p, s, x)
+            assert_parity(y_rm[:, rows], y_ref, a_ref, f"{tile} row-major N={N} K={K} T={T}")
+            assert_parity(y_t[:, rows], y_ref, a_ref, f"{tile} tiled N={N} K={K} T={T}")
 
 
 @pytest.mark.parametrize("tiled", [True, False])

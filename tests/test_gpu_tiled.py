@@ -10,7 +10,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import assert_parity, check_argmax, dev, host, say, sample_rows, weight_dev
+from gpu_util import assert_parity, check_argmax, dev, forced_tile, host, say, sample_rows, weight_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -78,15 +78,15 @@ def test_matmul_tiled_matches_oracle(w4, N, K, T):
 
 
 @pytest.mark.parametrize("tile", ["split,1,8", "split,2,3", "split,2,8", "shared,1,1", "shared,4,8", "shared,2,4", "shared,1,16", "shared,1,12", "run,4,8", "run,2,16"])
-def test_matmul_tiled_every_tile_shape(w4, tile, monkeypatch):
-    monkeypatch.setenv("W4A16_TILE", tile)
-    for N, K, T in [(37, 1152, 3), (300, 17408, 8), (2000, 2304, 8), (4099, 5120, 4)]:
-        tid = 4200 + N + K + T
-        p, s, pd, sd = weight_dev(tid, N, K)
-        x = synth.activations(tid, T, K)
-        y_ref, a_ref = oracle.matmul(p, s, x)
-        y = host(w4.matmul_tiled(w4.repack_tiled(pd, sd), dev(x)))
-        assert_parity(y, y_ref, a_ref, f"{tile} tiled N={N} K={K} T={T}")
+def test_matmul_tiled_every_tile_shape(w4, tile):
+    with forced_tile(w4, tile):
+        for N, K, T in [(37, 1152, 3), (300, 17408, 8), (2000, 2304, 8), (4099, 5120, 4)]:
+            tid = 4200 + N + K + T
+            p, s, pd, sd = weight_dev(tid, N, K)
+            x = synth.activations(tid, T, K)
+            y_ref, a_ref = oracle.matmul(p, s, x)
+            y = host(w4.matmul_tiled(w4.repack_tiled(pd, sd), dev(x)))
+            assert_parity(y, y_ref, a_ref, f"{tile} tiled N={N} K={K} T={T}")
 
 
 @pytest.mark.parametrize("proj", synth.PROJ_ORDER)

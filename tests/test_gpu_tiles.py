@@ -1,4 +1,4 @@
-"""GPU parity of every matrix-core tile shape, forced with W4A16_TILE.
+"""GPU parity of every matrix-core tile shape, forced through w4a16_set_tile.
 
 The default planner picks one tile per problem; these tests run the other
 shapes (split-K over 1-8 waves, waves owning 1-4 tiles) on shapes that reach
@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from gpu_util import assert_parity, dev, host, say, sample_rows, weight_dev
+from gpu_util import assert_parity, dev, forced_tile, host, say, sample_rows, weight_dev
 
 torch = pytest.importorskip("torch")
 pytestmark = pytest.mark.gpu
@@ -37,56 +37,56 @@ def w4():
 
 
 @pytest.mark.parametrize("tile", TILES)
-def test_tile_shapes_match_oracle(w4, tile, monkeypatch):
-    monkeypatch.setenv("W4A16_TILE", tile)
-    for N, K, T in SHAPES:
-        say(f"tile {tile} N={N} K={K} T={T}")
-        tid = 3000 + N + K + T
-        p, s, pd, sd = weight_dev(tid, N, K)
-        x = synth.activations(tid, T, K)
-        y_ref, a_ref = oracle.matmul(p, s, x)
-        assert_parity(host(w4.matmul(pd, sd, dev(x))), y_ref, a_ref, f"{tile} N={N} K={K} T={T}")
+def test_tile_shapes_match_oracle(w4, tile):
+    with forced_tile(w4, tile):
+        for N, K, T in SHAPES:
+            say(f"tile {tile} N={N} K={K} T={T}")
+            tid = 3000 + N + K + T
+            p, s, pd, sd = weight_dev(tid, N, K)
+            x = synth.activations(tid, T, K)
+            y_ref, a_ref = oracle.matmul(p, s, x)
+            assert_parity(host(w4.matmul(pd, sd, dev(x))), y_ref, a_ref, f"{tile} N={N} K={K} T={T}")
 
 
 @pytest.mark.parametrize("tile", TILES)
-def test_tile_misaligned_scales(w4, tile, monkeypatch):
+def test_tile_misaligned_scales(w4, tile):
     """Scale rows 2 bytes past 16-byte alignment take the one-scale-per-load path."""
-    monkeypatch.setenv("W4A16_TILE", tile)
-    N, K, T = 520, 2048, 3
-    p, s = synth.weight(3100, N, K)
-    x = synth.activations(3100, T, K)
-    buf = torch.empty(s.size + 8, dtype=torch.int16, device="cuda")
-    sd = buf[1:1 + s.size].view(N, K // 128)
-    sd.copy_(dev(s))
-    assert sd.data_ptr() % 16 == 2
-    y_ref, a_ref = oracle.matmul(p, s, x)
-    assert_parity(host(w4.matmul(dev(p), sd, dev(x))), y_ref, a_ref, f"{tile} misaligned scales")
+    with forced_tile(w4, tile):
+        N, K, T = 520, 2048, 3
+        p, s = synth.weight(3100, N, K)
+        x = synth.activations(3100, T, K)
+        buf = torch.empty(s.size + 8, dtype=torch.int16, device="cuda")
+        sd = buf[1:1 + s.size].view(N, K // 128)
+        sd.copy_(dev(s))
+        assert sd.data_ptr() % 16 == 2
+        y_ref, a_ref = oracle.matmul(p, s, x)
+        assert_parity(host(w4.matmul(dev(p), sd, dev(x))), y_ref, a_ref, f"{tile} misaligned scales")
 
 
 @pytest.mark.parametrize("tile", TILES)
 @pytest.mark.parametrize("T", [2, 8])
-def test_tile_gather_argmax(w4, tile, T, monkeypatch):
-    monkeypatch.setenv("W4A16_TILE", tile)
-    N, K = 3000, 1280
-    p, s, pd, sd = weight_dev(3200 + T, N, K)
-    x = synth.activations(3200 + T, T, K)
-    rng = np.random.default_rng(T)
-    ids = rng.integers(0, N, 1500).astype(np.int32)
-    ids[[3, 700, 1499]] = [-1, N, 2**31 - 1]
-    y, am, av = w4.head_gather(pd, sd, dev(x), row_ids=dev(ids), scores=True, argmax=True)
-    y, am, av = host(y), host(am), host(av)
-    y_ref, a_ref = oracle.gather(ids, p, s, x)
-    assert_parity(y, y_ref, a_ref, f"{tile} gather T={T}")
-    # the GPU's own scores decide the argmax; the oracle's must agree up to a near-tie
-    id_ref, val_ref, _ = oracle.argmax(y_ref, ids)
-    for t in range(T):
-        valid = ~np.isnan(y[t])
-        best = np.max(y[t][valid])
-        cand = ids[valid][y[t][valid] == best]
-        assert am[t] == cand.min(), f"{tile} T={T} t={t}: id {am[t]} vs {cand.min()}"
-        assert av[t] == best
-        if am[t] != id_ref[t]:
-            j = np.flatnonzero(ids == am[t])[0]
-            k = np.flatnonzero(ids == id_ref[t])[0]
-            gap = abs(y_ref[t, j] - y_ref[t, k])
-            assert gap <= 1e-3 * (a_ref[t, j] + a_ref[t, k]), f"{tile} T={T} t={t}: not a near-tie"
+def test_tile_gather_argmax(w4, tile, T):
+    with forced_tile(w4, tile):
+        N, K = 3000, 1280
+        p, s, pd, sd = weight_dev(3200 + T, N, K)
+        x = synth.activations(3200 + T, T, K)
+        rng = np.random.default_rng(T)
+        ids = rng.integers(0, N, 1500).astype(np.int32)
+        ids[[3, 700, 1499]] = [-1, N, 2**31 - 1]
+        y, am, av = w4.head_gather(pd, sd, dev(x), row_ids=dev(ids), scores=True, argmax=True)
+        y, am, av = host(y), host(am), host(av)
+        y_ref, a_ref = oracle.gather(ids, p, s, x)
+        assert_parity(y, y_ref, a_ref, f"{tile} gather T={T}")
+        # the GPU's own scores decide the argmax; the oracle's must agree up to a near-tie
+        id_ref, val_ref, _ = oracle.argmax(y_ref, ids)
+        for t in range(T):
+            valid = ~np.isnan(y[t])
+            best = np.max(y[t][valid])
+            cand = ids[valid][y[t][valid] == best]
+            assert am[t] == cand.min(), f"{tile} T={T} t={t}: id {am[t]} vs {cand.min()}"
+            assert av[t] == best
+            if am[t] != id_ref[t]:
+                j = np.flatnonzero(ids == am[t])[0]
+                k = np.flatnonzero(ids == id_ref[t])[0]
+                gap = abs(y_ref[t, j] - y_ref[t, k])
+                assert gap <= 1e-3 * (a_ref[t, j] + a_ref[t, k]), f"{tile} T={T} t={t}: not a near-tie"

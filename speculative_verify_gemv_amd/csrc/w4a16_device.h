@@ -157,8 +157,9 @@ __device__ __forceinline__ void st_global(V* p, V v) {
 // Output store of a kernel for TT activation rows.  Up to 4 rows the outputs
 // are written nontemporal, so that fewer dirty lines wait in L2 for the
 // write-back at the end of the launch (27B-class step at T = 4: +1.0%,
-// body pass at T = 1: +0.3%); from 8 rows on plain stores measured faster
-// (T = 8: 0.2%, T = 16: 1.4%).
+// body pass at T = 1: +0.3%; run workgroups that collect their outputs
+// lose that gain with plain stores); from 8 rows on plain stores measured
+// faster (T = 8: 0.2%, T = 16: 1.4%).
 template <int TT>
 __device__ __forceinline__ void st_out(float* p, float v) {
   if constexpr (TT <= 4)
@@ -1467,19 +1468,36 @@ __device__ __forceinline__ void ring_prologue(const GemvArgs& a, const u4_t* cp,
   }
 }
 
+// Where a run workgroup's outputs go: with `block` null straight to y as
+// each tile completes; otherwise into the workgroup's LDS block (`rows` =
+// its span of 16 * tiles rows from tile v_base, token row t at
+// block[t * rows]), which the workgroup writes to y at its end.
+struct RunOut {
+  float* block;
+  int64_t v_base;
+  int rows;
+};
+
 // Tile v done: this lane's outputs (row 16 v + r16, token rows t = 4 kq + r,
-// the tile's sums accs times fold) are stored, and the lane's running argmax
-// candidates bv[r] / bi[r] updated when the launch takes the argmax.
+// the tile's sums accs times fold) are stored or collected, and the lane's
+// running argmax candidates bv[r] / bi[r] updated when the launch takes the
+// argmax.
 template <int TT>
 __device__ __forceinline__ void tile_outputs(const GemvArgs& a, int64_t v, int r16, int kq, int w_cur,
-                                             const float (&accs)[4], float fold, float (&bv)[4], int (&bi)[4]) {
+                                             const float (&accs)[4], float fold, float (&bv)[4], int (&bi)[4],
+                                             const RunOut& ro) {
   const int64_t orow = v * 16 + r16;
   const bool in_range = orow < a.n_out;
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int t = kq * 4 + r;
     const float val = accs[r] * fold;  // the level form's power of two undone
-    if (t < TT && in_range && a.y) st_out<TT>(a.y + (int64_t)t * a.n_out + orow, w_cur < 0 ? __builtin_nanf("") : val);
+    const float out = w_cur < 0 ? __builtin_nanf("") : val;
+    if (ro.block) {
+      if (t < TT) ro.block[t * ro.rows + (int)(v - ro.v_base) * 16 + r16] = out;  // rows past n_out: never written out
+    } else if (t < TT && in_range && a.y) {
+      st_out<TT>(a.y + (int64_t)t * a.n_out + orow, out);
+    }
     if (a.partial && t < TT && w_cur >= 0 && !__builtin_isnan(val) && better(val, w_cur, bv[r], bi[r])) {
       bv[r] = val;
       bi[r] = w_cur;
@@ -1492,7 +1510,7 @@ __device__ __forceinline__ void tile_outputs(const GemvArgs& a, int64_t v, int r
 template <int TT, int LAY>
 __device__ __forceinline__ void exact_run_tiles(const GemvArgs& a, int64_t v, int64_t v_end, int step,
                                                 const unsigned char* xs, int r16, int kq, int trow, float (&bv)[4],
-                                                int (&bi)[4]) {
+                                                int (&bi)[4], const RunOut& ro) {
   const unsigned char* xb[4];
   lane_chunks(a, xs, trow, kq, xb);
   // kLayRow: this lane's own row is row l & 7 of cp or 8 + (l & 7) of cb
@@ -1504,7 +1522,7 @@ __device__ __forceinline__ void exact_run_tiles(const GemvArgs& a, int64_t v, in
     const int w_cur = tile_ptr<LAY>(a, v, r16, kq, cp, cb, sp);
     float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
     exact_groups<LAY>(a, own_b ? cb : cp, sp, xb, 0, a.G, accs);
-    tile_outputs<TT>(a, v, r16, kq, w_cur, accs, kLevelScale, bv, bi);
+    tile_outputs<TT>(a, v, r16, kq, w_cur, accs, kLevelScale, bv, bi, ro);
   }
 }
 
@@ -1512,7 +1530,7 @@ template <int TT, int LAY, bool H>
 __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t v_end, int step,
                                           const unsigned char* xs, int r16, int kq, int trow, const u4_t* cp,
                                           const u4_t* cb, const uint16_t* sp, u4_t (&q)[kRing], u4_t& sv,
-                                          float fold, float (&bv)[4], int (&bi)[4]) {
+                                          float fold, float (&bv)[4], int (&bi)[4], const RunOut& ro) {
   constexpr int PD = kRing;
   const int n = a.G;
   const int np = (n + PD - 1) / PD * PD;
@@ -1578,7 +1596,7 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
       }
       sv = svn;
     }
-    tile_outputs<TT>(a, v, r16, kq, w_cur, accs, fold, bv, bi);
+    tile_outputs<TT>(a, v, r16, kq, w_cur, accs, fold, bv, bi, ro);
     v = vn;
     cp = cpn;
     cb = cbn;
@@ -1590,8 +1608,10 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
 // Run workgroup: a.run_tiles tiles per wave.  Workgroup b owns tiles
 // [b*waves*nt, (b+1)*waves*nt); wave i streams tiles i, i + waves, ... of them,
 // so the waves stay on adjacent tiles.  All of K is staged once (the planner
-// guarantees it fits).  Built for one layout at a time (kLayTiled or
-// kLayRow), eight scales per load.
+// guarantees it fits).  With a.fin_offset set the outputs are collected in
+// LDS behind the staged activations and written when every wave is done.
+// Built for one layout at a time (kLayTiled or kLayRow), eight scales per
+// load.
 template <int TT, int LAY>
 __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
   const int lane = threadIdx.x & 63;
@@ -1632,15 +1652,27 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
     bv[r] = __builtin_nanf("");
     bi[r] = -1;
   }
+  const RunOut ro{(a.fin_offset > 0 && a.y) ? reinterpret_cast<float*>(smem + a.fin_offset) : nullptr, wg * span,
+                  (int)span * 16};
   if (v0 < v_end) {
     if constexpr (tries_f16<TT, true>()) {
       if (fold != 0.0f)
-        run_tiles<TT, LAY, true>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, cb, sp, q, sv, fold, bv, bi);
+        run_tiles<TT, LAY, true>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, cb, sp, q, sv, fold, bv, bi, ro);
       else
-        exact_run_tiles<TT, LAY>(a, v0, v_end, nwv, xs, r16, kq, trow, bv, bi);
+        exact_run_tiles<TT, LAY>(a, v0, v_end, nwv, xs, r16, kq, trow, bv, bi, ro);
     } else {
-      run_tiles<TT, LAY, false>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, cb, sp, q, sv, kLevelScale, bv, bi);
+      run_tiles<TT, LAY, false>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, cb, sp, q, sv, kLevelScale, bv, bi, ro);
     }
+  }
+  if (ro.block) {
+    // every wave's tiles are in the block: write it row by row (consecutive
+    // threads on consecutive outputs, whole lines), clipped to n_out
+    __syncthreads();
+    const int64_t row0 = ro.v_base * 16;  // < n_out: the grid holds no empty workgroup
+    const int nr = (int)min((int64_t)ro.rows, a.n_out - row0);
+    for (int t = 0; t < TT; ++t)
+      for (int i = threadIdx.x; i < nr; i += (int)blockDim.x)
+        st_out<TT>(a.y + (int64_t)t * a.n_out + row0 + i, ro.block[t * ro.rows + i]);
   }
   if (a.partial) {
     // per t: best of the lanes, of the waves, then of the workgroup

@@ -27,7 +27,7 @@ struct GemvArgs {
   int32_t sk;              // groups per staged activation slice
   int32_t xs_stride;       // bf16 values per staged token row (a multiple of 512)
   int32_t wave_lds;        // bytes of LDS per wave
-  int32_t fin_offset;      // unused (0)
+  int32_t fin_offset;      // run workgroups: LDS byte offset of the collected outputs (0: stored per tile)
   int32_t vec_scales;      // 1: eight scales per 16-byte load (tiled layout, or row-major rows
                            //    16-byte aligned with G % 8 == 0)
   int32_t tiled;           // 1: packed points at the tiled layout (scales inside it)
@@ -56,6 +56,9 @@ inline int64_t tiled_tile_bytes(int64_t G) {
 // ring running from one tile into the next (all of K staged once).
 constexpr int kDot = 1, kSplit = 2, kShared = 3, kRun = 4;
 constexpr int kDotMaxT = 8;  // the dot kernel is built for T <= 8
+// Run workgroups of up to this many activation rows collect their outputs
+// in LDS and write them at the workgroup's end, when the LDS share allows.
+constexpr int kCollectMaxT = 4;
 
 // Matrix-core tile choice: shape, 16-row tiles per wave, waves per workgroup.
 struct Tile {

@@ -1,0 +1,118 @@
+"""GPU parity of run workgroups that collect their outputs in LDS.
+
+Up to four activation rows, a run workgroup (several whole tiles per wave,
+all of K staged once) keeps its outputs in LDS behind the staged
+activations and writes them row by row when all its waves are done, if its
+LDS share holds both; otherwise, and above four rows, each tile's outputs
+are stored as the tile completes.  These cases reach both sides of that
+rule: ragged row counts (the last workgroup's block clipped to n_out),
+K = 9,216 at T = 4 (activations and outputs fill an eight-wave workgroup's
+80 KB exactly), K = 9,472 (the activations alone fill it: stored per tile),
+gathered rows with invalid ids (NaN outputs through the block) with the
+argmax, the argmax without scores, and grouped launches of both layouts
+with a guard word after every output to catch a write past it.  Expected
+values come only from the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from gpu_util import assert_parity, check_argmax, dev, forced_tile, host, say, sample_rows, weight_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+GUARD = 7.0  # written after each output buffer; no kernel writes it
+
+
+@pytest.fixture(scope="module")
+def w4():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import speculative_verify_gemv_amd as w4a16
+    w4a16.load_library()
+    w4a16.set_variant("mfma")
+    yield w4a16
+    w4a16.set_variant("auto")
+
+
+def guarded_output(T, N):
+    """A NaN-filled [T][N] float32 tensor followed by 64 guard words."""
+    buf = torch.full((T * N + 64,), float("nan"), dtype=torch.float32, device="cuda")
+    buf[T * N:] = GUARD
+    return buf, buf[:T * N].view(T, N)
+
+
+def check_guard(buf, T, N, what):
+    assert torch.all(buf[T * N:] == GUARD).item(), f"{what}: write past the outputs"
+
+
+def rows_of(N, seed):
+    return sample_rows(N, 256, seed=seed) if N > 2048 else np.arange(N, dtype=np.int32)
+
+
+@pytest.mark.parametrize("tiled", [True, False])
+@pytest.mark.parametrize("tile", [None, "run,4,8", "run,1,8", "run,3,16", "run,2,4"])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5])
+def test_grouped_runs_collect_outputs(w4, tiled, tile, T):
+    shapes = [(17, 128), (300, 5120), (1100, 1280), (4099, 1280), (2000, 9216), (700, 9472)]
+    probs, refs, bufs = [], [], []
+    for i, (N, K) in enumerate(shapes):
+        tid = 9000 + 10 * i + T
+        p, s, pd, sd = weight_dev(tid, N, K)
+        x = synth.activations(tid, T, K)
+        buf, y = guarded_output(T, N)
+        w = (w4.repack_tiled(pd, sd), None) if tiled else (pd, sd)
+        probs.append((*w, dev(x), y))
+        rows = rows_of(N, tid)
+        refs.append((rows, oracle.gather(rows, p, s, x)))
+        bufs.append(buf)
+    say(f"collected outputs grouped tiled={tiled} tile={tile} T={T}")
+    with forced_tile(w4, tile, batch=True):
+        b = w4.Batch(probs, T)
+    b.run()
+    for (N, K), prob, buf, (rows, (y_ref, a_ref)) in zip(shapes, probs, bufs, refs):
+        what = f"grouped tiled={tiled} tile={tile} T={T} {N}x{K}"
+        assert_parity(host(prob[3])[:, rows], y_ref, a_ref, what)
+        check_guard(buf, T, N, what)
+
+
+@pytest.mark.parametrize("N,K,T", [(4099, 9216, 4), (4099, 9472, 4), (1003, 9216, 3), (300, 5120, 5), (37, 1152, 4)])
+def test_single_run_launch_at_the_lds_limit(w4, N, K, T):
+    tid = 9100 + N + K + T
+    p, s, pd, sd = weight_dev(tid, N, K)
+    x = synth.activations(tid, T, K)
+    rows = rows_of(N, tid)
+    y_ref, a_ref = oracle.gather(rows, p, s, x)
+    tw = w4.repack_tiled(pd, sd)
+    with forced_tile(w4, "run,4,8"):
+        for name, call in (("row-major", lambda out: w4.matmul(pd, sd, dev(x), out=out)),
+                           ("tiled", lambda out: w4.matmul_tiled(tw, dev(x), out=out))):
+            say(f"collected outputs single {name} N={N} K={K} T={T}")
+            buf, y = guarded_output(T, N)
+            call(y)
+            assert_parity(host(y)[:, rows], y_ref, a_ref, f"single {name} N={N} K={K} T={T}")
+            check_guard(buf, T, N, f"single {name} N={N} K={K} T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 2, 3, 4])
+def test_gathered_runs_bad_ids_and_argmax(w4, T):
+    """NaN rows (invalid ids) pass through the collected block and never win
+    the argmax; the argmax without scores takes the per-tile path."""
+    N, K = 3000, 1280
+    p, s, pd, sd = weight_dev(9200 + T, N, K)
+    x = synth.activations(9200 + T, T, K)
+    ids = np.random.default_rng(T).integers(0, N, 1999).astype(np.int32)
+    ids[[0, 700, 1998]] = [-5, N, 2**31 - 1]
+    tw = w4.repack_tiled(pd, sd)
+    y_ref, a_ref = oracle.gather(ids, p, s, x)
+    with forced_tile(w4, "run,2,8"):
+        say(f"collected outputs gather T={T}")
+        y, am, av = w4.head_gather_tiled(tw, dev(x), row_ids=dev(ids), scores=True, argmax=True)
+        y, am, av = host(y), host(am), host(av)
+        assert_parity(y, y_ref, a_ref, f"gather run T={T}")
+        check_argmax(am, y, y_ref, ids, f"gather run T={T}")
+        assert np.array_equal(av, np.nanmax(y, axis=1)), "argmax value is not the best score"
+        _, am2, av2 = w4.head_gather_tiled(tw, dev(x), row_ids=dev(ids), scores=False, argmax=True)
+        assert np.array_equal(host(am2), am) and np.array_equal(host(av2), av), "argmax without scores differs"

@@ -154,12 +154,12 @@ template <typename V>
 __device__ __forceinline__ void st_global(V* p, V v) {
   *(__attribute__((address_space(1))) V*)p = v;
 }
-// Output store of a kernel for TT activation rows.  Up to 4 rows the outputs
-// are written nontemporal, so that fewer dirty lines wait in L2 for the
-// write-back at the end of the launch (27B-class step at T = 4: +1.0%,
-// body pass at T = 1: +0.3%; run workgroups that collect their outputs
-// lose that gain with plain stores); from 8 rows on plain stores measured
-// faster (T = 8: 0.2%, T = 16: 1.4%).
+// Output store of a kernel for TT activation rows, as each tile completes.
+// Up to 4 rows the outputs are written nontemporal, so that fewer dirty
+// lines wait in L2 for the write-back at the end of the launch (27B-class
+// step at T = 4: +1.0%, body pass at T = 1: +0.3%); from 8 rows on plain
+// stores measured faster (T = 8: 0.2%, T = 16: 1.4%).  Run workgroups that
+// collect their outputs in LDS write them nontemporal at every row count.
 template <int TT>
 __device__ __forceinline__ void st_out(float* p, float v) {
   if constexpr (TT <= 4)
@@ -1468,14 +1468,15 @@ __device__ __forceinline__ void ring_prologue(const GemvArgs& a, const u4_t* cp,
   }
 }
 
-// Where a run workgroup's outputs go: with `block` null straight to y as
-// each tile completes; otherwise into the workgroup's LDS block (`rows` =
-// its span of 16 * tiles rows from tile v_base, token row t at
-// block[t * rows]), which the workgroup writes to y at its end.
+// Where a run workgroup's outputs go: with `lane` null straight to y as
+// each tile completes; otherwise into the workgroup's LDS block, output
+// (row 16 (v - v_base) + r, token row t) at block[row * TT + t], which the
+// workgroup writes to y at its end.  `lane` is this lane's slot of tile
+// v_base, block + r16 * TT + 4 kq: one address register, each tile's four
+// stores at fixed offsets from it.
 struct RunOut {
-  float* block;
+  float* lane;
   int64_t v_base;
-  int rows;
 };
 
 // Tile v done: this lane's outputs (row 16 v + r16, token rows t = 4 kq + r,
@@ -1493,8 +1494,8 @@ __device__ __forceinline__ void tile_outputs(const GemvArgs& a, int64_t v, int r
     const int t = kq * 4 + r;
     const float val = accs[r] * fold;  // the level form's power of two undone
     const float out = w_cur < 0 ? __builtin_nanf("") : val;
-    if (ro.block) {
-      if (t < TT) ro.block[t * ro.rows + (int)(v - ro.v_base) * 16 + r16] = out;  // rows past n_out: never written out
+    if (ro.lane) {
+      if (t < TT) ro.lane[(int)(v - ro.v_base) * (16 * TT) + r] = out;  // rows past n_out: never written out
     } else if (t < TT && in_range && a.y) {
       st_out<TT>(a.y + (int64_t)t * a.n_out + orow, out);
     }
@@ -1652,8 +1653,8 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
     bv[r] = __builtin_nanf("");
     bi[r] = -1;
   }
-  const RunOut ro{(a.fin_offset > 0 && a.y) ? reinterpret_cast<float*>(smem + a.fin_offset) : nullptr, wg * span,
-                  (int)span * 16};
+  float* const block = (a.fin_offset > 0 && a.y) ? reinterpret_cast<float*>(smem + a.fin_offset) : nullptr;
+  const RunOut ro{block ? block + r16 * TT + 4 * kq : nullptr, wg * span};
   if (v0 < v_end) {
     if constexpr (tries_f16<TT, true>()) {
       if (fold != 0.0f)
@@ -1664,15 +1665,18 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
       run_tiles<TT, LAY, false>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, cb, sp, q, sv, kLevelScale, bv, bi, ro);
     }
   }
-  if (ro.block) {
-    // every wave's tiles are in the block: write it row by row (consecutive
-    // threads on consecutive outputs, whole lines), clipped to n_out
+  if (block) {
+    // every wave's tiles are in the block: write it to y token row by token
+    // row (consecutive threads on consecutive outputs, whole lines), clipped
+    // to n_out, with nontemporal stores at every row count (plain ones lose
+    // the gain)
     __syncthreads();
     const int64_t row0 = ro.v_base * 16;  // < n_out: the grid holds no empty workgroup
-    const int nr = (int)min((int64_t)ro.rows, a.n_out - row0);
+    const int nr = (int)min(span * 16, a.n_out - row0);
     for (int t = 0; t < TT; ++t)
       for (int i = threadIdx.x; i < nr; i += (int)blockDim.x)
-        st_out<TT>(a.y + (int64_t)t * a.n_out + row0 + i, ro.block[t * ro.rows + i]);
+        __builtin_nontemporal_store(block[i * TT + t],
+                                    (__attribute__((address_space(1))) float*)(a.y + (int64_t)t * a.n_out + row0 + i));
   }
   if (a.partial) {
     // per t: best of the lanes, of the waves, then of the workgroup

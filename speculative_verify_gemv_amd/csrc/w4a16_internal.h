@@ -56,9 +56,6 @@ inline int64_t tiled_tile_bytes(int64_t G) {
 // ring running from one tile into the next (all of K staged once).
 constexpr int kDot = 1, kSplit = 2, kShared = 3, kRun = 4;
 constexpr int kDotMaxT = 8;  // the dot kernel is built for T <= 8
-// Run workgroups of up to this many activation rows collect their outputs
-// in LDS and write them at the workgroup's end, when the LDS share allows.
-constexpr int kCollectMaxT = 4;
 
 // Matrix-core tile choice: shape, 16-row tiles per wave, waves per workgroup.
 struct Tile {

@@ -244,15 +244,14 @@ static void plan_shared(GemvArgs& a, int T, int rt, int nwv, Plan* p) {
 // shared workgroup with sk = G), so it needs the activations to fit
 // (shared_cap) and eight scales per load.  Returns false otherwise.
 //
-// Up to kCollectMaxT rows, and when the LDS share still holds them behind
-// the staged activations, the workgroup's T x 16*nt*nwv outputs are
-// collected there and written at its end as whole rows of nontemporal
-// stores (fin_offset: their offset).  Output stores are far dearer than
-// their share of the bytes in the middle of the weight stream: a timing-only
-// copy of the T = 4 body pass that drops them runs 3.7 points of 8 TB/s
-// faster, and one that writes a quarter of them is as fast as none.
-// Collected, the pass gains 1.0-1.8 points at T = 4 and 0.7-1.4 at T = 3;
-// at T = 5 and 6 it loses 0.2, and from T = 7 the activations leave no room.
+// When the LDS share still holds them behind the staged activations, the
+// workgroup's T x 16*nt*nwv outputs are collected there and written at its
+// end as whole rows of nontemporal stores (fin_offset: their offset).
+// Output stores are far dearer than their share of the bytes in the middle
+// of the weight stream: timing-only copies of the body pass that drop them
+// run 3.7, 7 and 8 points of 8 TB/s faster at T = 4, 8 and 16, and one that
+// writes a quarter of them at T = 4 is as fast as none.  Collected, the
+// pass gains 1-2 points at T = 3-8 and about 4 at T = 9-10.
 static bool plan_run(GemvArgs& a, int T, int nt, int nwv, Plan* p) {
   if (!a.vec_scales) return false;
   const int64_t xs_bytes = (int64_t)T * ring_groups(a.G) * kGroup * 2;
@@ -264,7 +263,7 @@ static bool plan_run(GemvArgs& a, int T, int nt, int nwv, Plan* p) {
   a.wave_lds = 0;
   a.run_tiles = nt;
   const int64_t out_bytes = (int64_t)T * nwv * nt * 16 * 4;  // fp32 outputs of the workgroup's rows
-  const bool collect = T <= kCollectMaxT && xs_bytes + out_bytes <= shared_cap(nwv);  // xs_bytes: a multiple of 16
+  const bool collect = xs_bytes + out_bytes <= shared_cap(nwv);  // xs_bytes: a multiple of 16
   a.fin_offset = collect ? (int)xs_bytes : 0;
   p->lds = std::max((int)(collect ? xs_bytes + out_bytes : xs_bytes), nwv * T * 8);
   p->threads = nwv * 64;

@@ -1,17 +1,18 @@
 """GPU parity of run workgroups that collect their outputs in LDS.
 
-Up to four activation rows, a run workgroup (several whole tiles per wave,
-all of K staged once) keeps its outputs in LDS behind the staged
-activations and writes them row by row when all its waves are done, if its
-LDS share holds both; otherwise, and above four rows, each tile's outputs
-are stored as the tile completes.  These cases reach both sides of that
-rule: ragged row counts (the last workgroup's block clipped to n_out),
-K = 9,216 at T = 4 (activations and outputs fill an eight-wave workgroup's
-80 KB exactly), K = 9,472 (the activations alone fill it: stored per tile),
-gathered rows with invalid ids (NaN outputs through the block) with the
-argmax, the argmax without scores, and grouped launches of both layouts
-with a guard word after every output to catch a write past it.  Expected
-values come only from the oracle.
+A run workgroup (several whole tiles per wave, all of K staged once) keeps
+its outputs in LDS behind the staged activations and writes them token row
+by token row when all its waves are done, if its LDS share holds both;
+otherwise each tile's outputs are stored as the tile completes.  These
+cases reach both sides of that rule: ragged row counts (the last
+workgroup's block clipped to n_out); K = 9,216 at T = 4 (activations and
+outputs fill an eight-wave workgroup's 80 KB exactly) against K = 9,472
+(the activations alone fill it); K = 8,192 at T = 8 in sixteen-wave
+workgroups (160 KB exactly) against K = 8,320; T from 1 to 16 under the
+grouped launch's own run shapes and forced ones; gathered rows with invalid
+ids (NaN outputs through the block) with the argmax, the argmax without
+scores; a guard word after every output buffer to catch a write past it.
+Expected values come only from the oracle.
 """
 import numpy as np
 import pytest
@@ -54,7 +55,7 @@ def rows_of(N, seed):
 
 @pytest.mark.parametrize("tiled", [True, False])
 @pytest.mark.parametrize("tile", [None, "run,4,8", "run,1,8", "run,3,16", "run,2,4"])
-@pytest.mark.parametrize("T", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8, 9, 12, 16])
 def test_grouped_runs_collect_outputs(w4, tiled, tile, T):
     shapes = [(17, 128), (300, 5120), (1100, 1280), (4099, 1280), (2000, 9216), (700, 9472)]
     probs, refs, bufs = [], [], []
@@ -78,25 +79,27 @@ def test_grouped_runs_collect_outputs(w4, tiled, tile, T):
         check_guard(buf, T, N, what)
 
 
-@pytest.mark.parametrize("N,K,T", [(4099, 9216, 4), (4099, 9472, 4), (1003, 9216, 3), (300, 5120, 5), (37, 1152, 4)])
-def test_single_run_launch_at_the_lds_limit(w4, N, K, T):
+@pytest.mark.parametrize("N,K,T,tile", [(4099, 9216, 4, "run,4,8"), (4099, 9472, 4, "run,4,8"), (1003, 9216, 3, "run,4,8"),
+                                        (300, 5120, 5, "run,4,8"), (37, 1152, 4, "run,4,8"), (2100, 8192, 8, "run,4,16"),
+                                        (2100, 8320, 8, "run,4,16"), (700, 5120, 16, "run,4,16"), (700, 5120, 12, "run,3,16")])
+def test_single_run_launch_at_the_lds_limit(w4, N, K, T, tile):
     tid = 9100 + N + K + T
     p, s, pd, sd = weight_dev(tid, N, K)
     x = synth.activations(tid, T, K)
     rows = rows_of(N, tid)
     y_ref, a_ref = oracle.gather(rows, p, s, x)
     tw = w4.repack_tiled(pd, sd)
-    with forced_tile(w4, "run,4,8"):
+    with forced_tile(w4, tile):
         for name, call in (("row-major", lambda out: w4.matmul(pd, sd, dev(x), out=out)),
                            ("tiled", lambda out: w4.matmul_tiled(tw, dev(x), out=out))):
-            say(f"collected outputs single {name} N={N} K={K} T={T}")
+            say(f"collected outputs single {name} N={N} K={K} T={T} tile={tile}")
             buf, y = guarded_output(T, N)
             call(y)
             assert_parity(host(y)[:, rows], y_ref, a_ref, f"single {name} N={N} K={K} T={T}")
             check_guard(buf, T, N, f"single {name} N={N} K={K} T={T}")
 
 
-@pytest.mark.parametrize("T", [1, 2, 3, 4])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 8])
 def test_gathered_runs_bad_ids_and_argmax(w4, T):
     """NaN rows (invalid ids) pass through the collected block and never win
     the argmax; the argmax without scores takes the per-tile path."""

@@ -182,18 +182,16 @@ struct ArgmaxRecord {
 static_assert(sizeof(ArgmaxRecord) == 32 && sizeof(w4a16::GemvArgs) == 144, "batch table record sizes");
 
 // Tile of grouped launches, from the MI355X sweeps.  All problems tiled:
-// at T <= 2 shared workgroups of one tile per wave; above, run workgroups,
-// a problem whose activations do not fit running shared workgroups inside
-// the same kernel.  Eight waves of four tiles at T <= 4 and of six at
-// T <= 6: two such workgroups share a CU, and at K = 5,120 each still holds
-// its outputs in LDS beside the activations (27B-class body pass: +2.8% at
-// T = 5 against sixteen waves of four before outputs were collected).  At
-// T = 7 and 8 sixteen waves of five, one workgroup a CU, whose LDS holds
-// both (+1.9 points at T = 8 against eight waves of six, which must store
-// per tile); above, sixteen waves of four, of three at T = 12, the longest
-// run whose outputs still fit at K = 5,120 up to T = 12 (+4 points at
-// T = 9-10, +2 at T = 12); from T = 13 no run short enough to make room
-// pays (two tiles at T = 13: -2 points).
+// at T <= 2 shared workgroups of one tile per wave; above, run workgroups
+// of four tiles per wave, a problem whose activations do not fit running
+// shared workgroups inside the same kernel.  Eight waves up to T = 6: two
+// such workgroups share a CU, and at K = 5,120 each still holds its outputs
+// in LDS beside the activations (27B-class body pass at T = 5 and 6: +1.5
+// and +1.0 points against runs of six tiles).  From T = 7 sixteen waves,
+// one workgroup a CU, whose LDS holds both up to T = 11 (at T = 8: +1.7-2.3
+// points against eight waves of six, which must store per tile; at T = 9-10
+// about +4), and at T = 12 runs of three tiles, which still fit (+2); from
+// T = 13 no run short enough to make room pays (two tiles at T = 13: -2).
 // Every problem row-major: up to T = 2 shared workgroups of two 16-row
 // tiles per wave, four waves at T = 1 and eight at T = 2 (27B-class body
 // pass: 75.3% of 8 TB/s at T = 2 against 70.7% for four waves of four
@@ -206,9 +204,7 @@ static_assert(sizeof(ArgmaxRecord) == 32 && sizeof(w4a16::GemvArgs) == 144, "bat
 w4a16::Tile batch_tile(int T, bool all_tiled, bool all_row, int64_t kmax) {
   w4a16::Tile t;
   if ((all_tiled || all_row) && T > 2)
-    t = T <= 6   ? w4a16::Tile{w4a16::kRun, T <= 4 ? 4 : 6, 8}
-        : T <= 8 ? w4a16::Tile{w4a16::kRun, 5, 16}
-                 : w4a16::Tile{w4a16::kRun, T == 12 ? 3 : 4, 16};
+    t = w4a16::Tile{w4a16::kRun, T == 12 ? 3 : 4, T <= 6 ? 8 : 16};
   else if (all_tiled)
     t = w4a16::Tile{w4a16::kShared, 1, w4a16::shared_waves(T, kmax)};
   else if (all_row)

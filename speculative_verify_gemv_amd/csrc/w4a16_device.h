@@ -1329,7 +1329,7 @@ __device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, u
 // Shared workgroup: each of its waves owns RT tiles of its own over all of K
 // (rows (wg*waves + wave)*16*RT ..); the waves share one staged copy of the
 // activations per K slice, so the staging is paid once per 16 * RT * waves
-// rows.  Every output comes straight from one wave.
+// rows.  Every output is summed by one wave.
 template <int TT, int RT, int LAY>
 __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
   const int lane = threadIdx.x & 63;
@@ -1361,6 +1361,16 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
     bv[t] = __builtin_nanf("");
     bi[t] = -1;
   }
+  // From two token rows the workgroup's outputs go through the staging
+  // area, free once every wave is done, when it holds them (T x 16 * RT *
+  // waves fp32, output (row q of the workgroup's rows, token row t) at
+  // q * TT + t; the staging area holds T * xs_stride bf16), and are written
+  // token row by token row, as a run workgroup writes its collected block
+  // (grouped body pass: +0.3 to +0.9 points at T = 2-8, bit for bit the same
+  // results; at T = 1 no gain); otherwise each lane stores its own.
+  const bool collect = TT >= 2 && a.y && nwv * RT * 32 <= a.xs_stride;  // uniform
+  float* const block = reinterpret_cast<float*>(smem);
+  if (collect) __syncthreads();  // the staged activations are no longer read
 #pragma unroll
   for (int tl = 0; tl < RT; ++tl) {
     const int64_t orow = row_w + tl * 16 + r16;
@@ -1370,7 +1380,12 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
       const int t = kq * 4 + r;
-      if (t < TT && in_range && a.y) st_out<TT>(a.y + (int64_t)t * a.n_out + orow, bad ? __builtin_nanf("") : acc[tl][r]);
+      const float out = bad ? __builtin_nanf("") : acc[tl][r];
+      if (collect) {
+        if (t < TT) block[((wave * RT + tl) * 16 + r16) * TT + t] = out;  // rows past n_out: never written out
+      } else if (t < TT && in_range && a.y) {
+        st_out<TT>(a.y + (int64_t)t * a.n_out + orow, out);
+      }
     }
     if (a.partial) {
       // this lane's candidate for token rows t = 4*kq + r
@@ -1388,10 +1403,19 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
       }
     }
   }
+  if (collect) {
+    __syncthreads();
+    const int64_t row0 = wg * nwv * (int64_t)(RT * 16);  // < n_out: the grid holds no empty workgroup
+    const int nr = (int)min((int64_t)(nwv * RT * 16), a.n_out - row0);
+    for (int t = 0; t < TT; ++t)
+      for (int i = threadIdx.x; i < nr; i += (int)blockDim.x)
+        __builtin_nontemporal_store(block[i * TT + t],
+                                    (__attribute__((address_space(1))) float*)(a.y + (int64_t)t * a.n_out + row0 + i));
+  }
   if (a.partial) {
     // per t: best (value, id) of this wave's rows, then of the workgroup
     int2* fin = reinterpret_cast<int2*>(smem);
-    __syncthreads();  // the staging area is free now
+    __syncthreads();  // the staging area (and the output block) is free now
 #pragma unroll
     for (int t = 0; t < TT; ++t) {
       float v = bv[t];

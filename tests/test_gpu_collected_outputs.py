@@ -1,4 +1,4 @@
-"""GPU parity of run workgroups that collect their outputs in LDS.
+"""GPU parity of workgroups that collect their outputs in LDS.
 
 A run workgroup (several whole tiles per wave, all of K staged once) keeps
 its outputs in LDS behind the staged activations and writes them token row
@@ -12,7 +12,11 @@ workgroups (160 KB exactly) against K = 8,320; T from 1 to 16 under the
 grouped launch's own run shapes and forced ones; gathered rows with invalid
 ids (NaN outputs through the block) with the argmax, the argmax without
 scores; a guard word after every output buffer to catch a write past it.
-Expected values come only from the oracle.
+Shared workgroups (every wave its own tiles over all of K) from two token
+rows pass their outputs through the staging area once every wave is done,
+when it holds them: the grouped cases also force shared shapes (one tile
+per wave, and four in the row-major kernels).  Expected values come only
+from the oracle.
 """
 import numpy as np
 import pytest
@@ -54,7 +58,7 @@ def rows_of(N, seed):
 
 
 @pytest.mark.parametrize("tiled", [True, False])
-@pytest.mark.parametrize("tile", [None, "run,4,8", "run,1,8", "run,3,16", "run,2,4"])
+@pytest.mark.parametrize("tile", [None, "run,4,8", "run,1,8", "run,3,16", "run,2,4", "shared,1,16", "shared,4,4"])
 @pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8, 9, 12, 16])
 def test_grouped_runs_collect_outputs(w4, tiled, tile, T):
     shapes = [(17, 128), (300, 5120), (1100, 1280), (4099, 1280), (2000, 9216), (700, 9472)]

@@ -1329,9 +1329,10 @@ __device__ __forceinline__ void split_workgroup(const GemvArgs& a, int64_t wg, u
 // Shared workgroup: each of its waves owns RT tiles of its own over all of K
 // (rows (wg*waves + wave)*16*RT ..); the waves share one staged copy of the
 // activations per K slice, so the staging is paid once per 16 * RT * waves
-// rows.  Every output is summed by one wave.
+// rows.  Every output is summed by one wave.  grouped: the workgroup is one
+// of a grouped launch (its outputs may go through LDS, below).
 template <int TT, int RT, int LAY>
-__device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
+__device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem, bool grouped) {
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int nwv = blockDim.x >> 6;
@@ -1361,14 +1362,17 @@ __device__ __forceinline__ void shared_workgroup(const GemvArgs& a, int64_t wg, 
     bv[t] = __builtin_nanf("");
     bi[t] = -1;
   }
-  // From two token rows the workgroup's outputs go through the staging
-  // area, free once every wave is done, when it holds them (T x 16 * RT *
-  // waves fp32, output (row q of the workgroup's rows, token row t) at
-  // q * TT + t; the staging area holds T * xs_stride bf16), and are written
-  // token row by token row, as a run workgroup writes its collected block
-  // (grouped body pass: +0.3 to +0.9 points at T = 2-8, bit for bit the same
-  // results; at T = 1 no gain); otherwise each lane stores its own.
-  const bool collect = TT >= 2 && a.y && nwv * RT * 32 <= a.xs_stride;  // uniform
+  // In a grouped launch, from two token rows, the workgroup's outputs go
+  // through the staging area, free once every wave is done, when it holds
+  // them (T x 16 * RT * waves fp32, output (row q of the workgroup's rows,
+  // token row t) at q * TT + t; the staging area holds T * xs_stride bf16),
+  // and are written token row by token row, as a run workgroup writes its
+  // collected block (grouped body pass: +0.3 to +0.9 points at T = 2-8, bit
+  // for bit the same results; at T = 1 no gain).  Otherwise each lane stores
+  // its own: a single launch's workgroups all end together, and the extra
+  // barrier and round trip lengthen its tail (34,816 x 5,120 at T = 4 and
+  // 8: +0.3 and +0.7 us).
+  const bool collect = grouped && TT >= 2 && a.y && nwv * RT * 32 <= a.xs_stride;  // uniform
   float* const block = reinterpret_cast<float*>(smem);
   if (collect) __syncthreads();  // the staged activations are no longer read
 #pragma unroll
@@ -1764,13 +1768,13 @@ w4a16_run_batch_kernel(const GemvArgs* __restrict__ table, int count) {
   if (a.run_tiles > 0)
     run_workgroup<TT, LAY>(a, b - a.wg_start, smem);
   else  // activations too large for one staging: whole-K slices, one tile per wave
-    shared_workgroup<TT, 1, LAY>(a, b - a.wg_start, smem);
+    shared_workgroup<TT, 1, LAY>(a, b - a.wg_start, smem, true);
 }
 
 template <int TT, int RT, bool SHARED, int LAY>
-__device__ __forceinline__ void tile_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem) {
+__device__ __forceinline__ void tile_workgroup(const GemvArgs& a, int64_t wg, unsigned char* smem, bool grouped) {
   if constexpr (SHARED)
-    shared_workgroup<TT, RT, LAY>(a, wg, smem);
+    shared_workgroup<TT, RT, LAY>(a, wg, smem, grouped);
   else
     split_workgroup<TT, RT, LAY>(a, wg, smem);
 }
@@ -1779,7 +1783,7 @@ template <int TT, int RT, bool SHARED, int LAY>
 __global__ void __launch_bounds__(SHARED && RT == 1 ? 1024 : 512)
     __attribute__((amdgpu_waves_per_eu(SHARED && RT == 1 ? 4 : 1))) w4a16_tile_kernel(GemvArgs a) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  tile_workgroup<TT, RT, SHARED, LAY>(a, blockIdx.x, smem);
+  tile_workgroup<TT, RT, SHARED, LAY>(a, blockIdx.x, smem, false);
 }
 
 // Grouped launch: workgroup b runs tile b - wg_start of the last problem whose
@@ -1799,7 +1803,7 @@ __global__ void __launch_bounds__(SHARED && RT == 1 ? 1024 : 512)
       hi = mid - 1;
   }
   const GemvArgs a = table[lo];
-  tile_workgroup<TT, RT, SHARED, LAY>(a, b - a.wg_start, smem);
+  tile_workgroup<TT, RT, SHARED, LAY>(a, b - a.wg_start, smem, true);
 }
 
 // ------------------------------------------------------------- dispatch ----

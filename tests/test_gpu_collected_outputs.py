@@ -12,10 +12,10 @@ workgroups (160 KB exactly) against K = 8,320; T from 1 to 16 under the
 grouped launch's own run shapes and forced ones; gathered rows with invalid
 ids (NaN outputs through the block) with the argmax, the argmax without
 scores; a guard word after every output buffer to catch a write past it.
-Shared workgroups (every wave its own tiles over all of K) from two token
-rows pass their outputs through the staging area once every wave is done,
-when it holds them: the grouped cases also force shared shapes (one tile
-per wave, and four in the row-major kernels).  Expected values come only
+Shared workgroups (every wave its own tiles over all of K) of a grouped
+launch, from two token rows, pass their outputs through the staging area
+once every wave is done, when it holds them: the grouped cases also force
+shared shapes (one tile per wave, and four in the row-major kernels).  Expected values come only
 from the oracle.
 """
 import numpy as np

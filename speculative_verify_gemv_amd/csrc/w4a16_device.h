@@ -1485,13 +1485,15 @@ __device__ __forceinline__ int tile_ptr(const GemvArgs& a, int64_t v, int r16, i
   return (int)w_out;
 }
 
+// The first ring cycle of a tile over groups [sb, sb + n) (sb a multiple of
+// eight): its eight scales and its first eight groups.
 template <int LAY>
 __device__ __forceinline__ void ring_prologue(const GemvArgs& a, const u4_t* cp, const u4_t* cb, const uint16_t* sp,
-                                              u4_t (&q)[kRing], u4_t& sv) {
-  sv = ld_global(reinterpret_cast<const u4_t*>(sp) + scale_off<LAY>(a, 0));
+                                              int sb, int n, u4_t (&q)[kRing], u4_t& sv) {
+  sv = ld_global(reinterpret_cast<const u4_t*>(sp) + scale_off<LAY>(a, sb));
 #pragma unroll
   for (int s = 0; s < kRing; ++s) {
-    q[s] = load_slot<LAY>(a, cp, cb, s, min(s, a.G - 1));
+    q[s] = load_slot<LAY>(a, cp, cb, s, sb + min(s, n - 1));
     __builtin_amdgcn_sched_barrier(0);  // issue in slot order, as the loop reloads them
   }
 }
@@ -1501,10 +1503,13 @@ __device__ __forceinline__ void ring_prologue(const GemvArgs& a, const u4_t* cp,
 // (row 16 (v - v_base) + r, token row t) at block[row * TT + t], which the
 // workgroup writes to y at its end.  `lane` is this lane's slot of tile
 // v_base, block + r16 * TT + 4 kq: one address register, each tile's four
-// stores at fixed offsets from it.
+// stores at fixed offsets from it.  A run over K in slices carries its
+// partial sums there: the first slice writes them, later ones add theirs,
+// and the last one's sums are the outputs.
 struct RunOut {
   float* lane;
   int64_t v_base;
+  bool first, last;
 };
 
 // Tile v done: this lane's outputs (row 16 v + r16, token rows t = 4 kq + r,
@@ -1521,25 +1526,29 @@ __device__ __forceinline__ void tile_outputs(const GemvArgs& a, int64_t v, int r
   for (int r = 0; r < 4; ++r) {
     const int t = kq * 4 + r;
     const float val = accs[r] * fold;  // the level form's power of two undone
-    const float out = w_cur < 0 ? __builtin_nanf("") : val;
+    float out = w_cur < 0 ? __builtin_nanf("") : val;
     if (ro.lane) {
-      if (t < TT) ro.lane[(int)(v - ro.v_base) * (16 * TT) + r] = out;  // rows past n_out: never written out
+      if (t < TT) {  // rows past n_out: never written out
+        float* slot = ro.lane + (int)(v - ro.v_base) * (16 * TT) + r;
+        if (!ro.first) out = *slot + out;  // the earlier slices' sum, then this one's: their order fixed
+        *slot = out;
+      }
     } else if (t < TT && in_range && a.y) {
       st_out<TT>(a.y + (int64_t)t * a.n_out + orow, out);
     }
-    if (a.partial && t < TT && w_cur >= 0 && !__builtin_isnan(val) && better(val, w_cur, bv[r], bi[r])) {
-      bv[r] = val;
+    if (a.partial && ro.last && t < TT && w_cur >= 0 && !__builtin_isnan(out) && better(out, w_cur, bv[r], bi[r])) {
+      bv[r] = out;
       bi[r] = w_cur;
     }
   }
 }
 
 // The exact fallback of run_tiles (see exact_groups): tiles v, v + step, ...
-// (< v_end), all of K each, one group at a time.
+// (< v_end), groups [sb, sb + n) each, one group at a time.
 template <int TT, int LAY>
 __device__ __forceinline__ void exact_run_tiles(const GemvArgs& a, int64_t v, int64_t v_end, int step,
-                                                const unsigned char* xs, int r16, int kq, int trow, float (&bv)[4],
-                                                int (&bi)[4], const RunOut& ro) {
+                                                const unsigned char* xs, int r16, int kq, int trow, int sb, int n,
+                                                float (&bv)[4], int (&bi)[4], const RunOut& ro) {
   const unsigned char* xb[4];
   lane_chunks(a, xs, trow, kq, xb);
   // kLayRow: this lane's own row is row l & 7 of cp or 8 + (l & 7) of cb
@@ -1550,18 +1559,20 @@ __device__ __forceinline__ void exact_run_tiles(const GemvArgs& a, int64_t v, in
     const uint16_t* sp;
     const int w_cur = tile_ptr<LAY>(a, v, r16, kq, cp, cb, sp);
     float accs[4] = {0.0f, 0.0f, 0.0f, 0.0f};
-    exact_groups<LAY>(a, own_b ? cb : cp, sp, xb, 0, a.G, accs);
+    exact_groups<LAY>(a, own_b ? cb : cp, sp, xb, sb, n, accs);
     tile_outputs<TT>(a, v, r16, kq, w_cur, accs, kLevelScale, bv, bi, ro);
   }
 }
 
+// Tiles v, v + step, ... (< v_end) over groups [sb, sb + n) of K (the staged
+// slice; sb a multiple of eight), the ring running from each tile into the
+// next; the caller issued the first tile's ring (ring_prologue).
 template <int TT, int LAY, bool H>
 __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t v_end, int step,
-                                          const unsigned char* xs, int r16, int kq, int trow, const u4_t* cp,
-                                          const u4_t* cb, const uint16_t* sp, u4_t (&q)[kRing], u4_t& sv,
-                                          float fold, float (&bv)[4], int (&bi)[4], const RunOut& ro) {
+                                          const unsigned char* xs, int r16, int kq, int trow, int sb, int n,
+                                          const u4_t* cp, const u4_t* cb, const uint16_t* sp, u4_t (&q)[kRing],
+                                          u4_t& sv, float fold, float (&bv)[4], int (&bi)[4], const RunOut& ro) {
   constexpr int PD = kRing;
-  const int n = a.G;
   const int np = (n + PD - 1) / PD * PD;
   const unsigned char* xb[4];  // this lane's activation chunks of group 0
   lane_chunks(a, xs, trow, kq, xb);
@@ -1579,7 +1590,7 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
       const bool last = fi + PD >= np;  // uniform: this cycle prefetches the next tile
       const uint16_t* sbase = (last && has_next) ? spn : sp;
       const int gv = last ? (has_next ? 0 : fi) : fi + PD;
-      const u4_t svn = ld_global(reinterpret_cast<const u4_t*>(sbase) + scale_off<LAY>(a, gv));
+      const u4_t svn = ld_global(reinterpret_cast<const u4_t*>(sbase) + scale_off<LAY>(a, sb + gv));
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (LAY == kLayRow) {
 #pragma unroll
@@ -1595,8 +1606,8 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
           const bool nxt = tgt >= np;
           const bool on = nxt && has_next;
           const int gg = nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1);
-          q[s] = load_slot<LAY>(a, on ? cpn : cp, on ? cbn : cb, s, gg);
-          q[s + 1] = load_slot<LAY>(a, on ? cpn : cp, on ? cbn : cb, s + 1, gg);
+          q[s] = load_slot<LAY>(a, on ? cpn : cp, on ? cbn : cb, s, sb + gg);
+          q[s + 1] = load_slot<LAY>(a, on ? cpn : cp, on ? cbn : cb, s + 1, sb + gg);
           __builtin_amdgcn_sched_barrier(0);
           const f4_t d0 = group_mfma<H>(xb, gl, w0);
 #pragma unroll
@@ -1619,7 +1630,7 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
           const bool nxt = tgt >= np;
           const u4_t* cpl = (nxt && has_next) ? cpn : cp;
           const int gg = nxt ? (has_next ? min(tgt - np, n - 1) : n - 1) : min(tgt, n - 1);
-          q[s] = load_codes<LAY>(cpl + code_off<LAY>(a, gg));
+          q[s] = load_codes<LAY>(cpl + code_off<LAY>(a, sb + gg));
           __builtin_amdgcn_sched_barrier(0);
         }
       }
@@ -1631,6 +1642,24 @@ __device__ __forceinline__ void run_tiles(const GemvArgs& a, int64_t v, int64_t 
     cb = cbn;
     sp = spn;
     w_cur = w_next;
+  }
+}
+
+// The tiles of one staged slice [sb, sb + n) of a run: the fp16 loop when
+// the slice took the fp16 form (fold != 0), else the exact fallback.
+template <int TT, int LAY>
+__device__ __forceinline__ void run_slice(const GemvArgs& a, int64_t v0, int64_t v_end, int nwv,
+                                          const unsigned char* xs, int r16, int kq, int trow, int sb, int n,
+                                          const u4_t* cp, const u4_t* cb, const uint16_t* sp, u4_t (&q)[kRing],
+                                          u4_t& sv, float fold, float (&bv)[4], int (&bi)[4], const RunOut& ro) {
+  if (v0 >= v_end) return;  // uniform
+  if constexpr (tries_f16<TT, true>()) {
+    if (fold != 0.0f)
+      run_tiles<TT, LAY, true>(a, v0, v_end, nwv, xs, r16, kq, trow, sb, n, cp, cb, sp, q, sv, fold, bv, bi, ro);
+    else
+      exact_run_tiles<TT, LAY>(a, v0, v_end, nwv, xs, r16, kq, trow, sb, n, bv, bi, ro);
+  } else {
+    run_tiles<TT, LAY, false>(a, v0, v_end, nwv, xs, r16, kq, trow, sb, n, cp, cb, sp, q, sv, kLevelScale, bv, bi, ro);
   }
 }
 
@@ -1657,23 +1686,15 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
   const uint16_t* sp = nullptr;
   u4_t q[kRing];
   u4_t sv;
+  // All of K staged at once (a.sk == a.G), or K in slices of a.sk groups
+  // whose partial sums the LDS block carries from slice to slice.
+  const bool sliced = a.sk < a.G;  // uniform
   // activations that fit kStageRegs chunks per thread are loaded first, then
   // the first tile's ring, then staged from the registers; larger ones are
   // staged after the ring is issued.  fold: the fp16 form's 2^-E, or 0
-  const bool regs = TT * a.G * (kGroup / 8) <= kStageRegs * (int)blockDim.x;  // uniform
+  const bool regs = !sliced && TT * a.G * (kGroup / 8) <= kStageRegs * (int)blockDim.x;  // uniform
   u4_t xr[kStageRegs];
   if (regs) prefetch_slice<TT>(a, 0, a.G, xr);
-  if (v0 < v_end) {
-    tile_ptr<LAY>(a, v0, r16, kq, cp, cb, sp);
-    ring_prologue<LAY>(a, cp, cb, sp, q, sv);
-  }
-  float fold;
-  if (regs) {
-    fold = stage_regs_shared<TT>(a, xs, 0, a.G, xr, tries_f16<TT, true>());
-    __syncthreads();
-  } else {
-    fold = stage_slice<TT, true, tries_f16<TT, true>()>(a, xs, 0, a.G);  // also waits for the ring's loads
-  }
   float bv[4];
   int bi[4];
 #pragma unroll
@@ -1681,25 +1702,41 @@ __device__ __forceinline__ void run_workgroup(const GemvArgs& a, int64_t wg, uns
     bv[r] = __builtin_nanf("");
     bi[r] = -1;
   }
-  float* const block = (a.fin_offset > 0 && a.y) ? reinterpret_cast<float*>(smem + a.fin_offset) : nullptr;
-  const RunOut ro{block ? block + r16 * TT + 4 * kq : nullptr, wg * span};
-  if (v0 < v_end) {
-    if constexpr (tries_f16<TT, true>()) {
-      if (fold != 0.0f)
-        run_tiles<TT, LAY, true>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, cb, sp, q, sv, fold, bv, bi, ro);
-      else
-        exact_run_tiles<TT, LAY>(a, v0, v_end, nwv, xs, r16, kq, trow, bv, bi, ro);
-    } else {
-      run_tiles<TT, LAY, false>(a, v0, v_end, nwv, xs, r16, kq, trow, cp, cb, sp, q, sv, kLevelScale, bv, bi, ro);
+  float* const block = (a.fin_offset > 0 && (a.y || sliced)) ? reinterpret_cast<float*>(smem + a.fin_offset) : nullptr;
+  float* const lane_out = block ? block + r16 * TT + 4 * kq : nullptr;
+  float fold = 0.0f;
+  if (regs) {  // all of K, staged from the registers (one pass below)
+    if (v0 < v_end) {
+      tile_ptr<LAY>(a, v0, r16, kq, cp, cb, sp);
+      ring_prologue<LAY>(a, cp, cb, sp, 0, a.G, q, sv);
     }
+    fold = stage_regs_shared<TT>(a, xs, 0, a.G, xr, tries_f16<TT, true>());
+    __syncthreads();
   }
-  if (block) {
+  // runs over K slices are built for the tiled layout only (the planner
+  // slices no other; in the row-major kernels the loop's second pass cost
+  // register spills)
+  const int passes = LAY == kLayTiled ? (a.G + a.sk - 1) / a.sk : 1;
+  for (int i = 0; i < passes; ++i) {  // uniform; one pass unless sliced
+    const int sb = i * a.sk, n = min(a.G - sb, a.sk);
+    if (!regs) {
+      if (v0 < v_end) {
+        tile_ptr<LAY>(a, v0, r16, kq, cp, cb, sp);
+        ring_prologue<LAY>(a, cp, cb, sp, sb, n, q, sv);
+      }
+      if (sb > 0) __syncthreads();  // every wave is done with the previous slice
+      fold = stage_slice<TT, true, tries_f16<TT, true>()>(a, xs, sb, sb + n);  // also waits for the ring's loads
+    }
+    run_slice<TT, LAY>(a, v0, v_end, nwv, xs, r16, kq, trow, sb, n, cp, cb, sp, q, sv, fold, bv, bi,
+                       RunOut{lane_out, wg * span, sb == 0, sb + n == a.G});
+  }
+  if (block && a.y) {
     // every wave's tiles are in the block: write it to y token row by token
     // row (consecutive threads on consecutive outputs, whole lines), clipped
     // to n_out, with nontemporal stores at every row count (plain ones lose
     // the gain)
     __syncthreads();
-    const int64_t row0 = ro.v_base * 16;  // < n_out: the grid holds no empty workgroup
+    const int64_t row0 = wg * span * 16;  // < n_out: the grid holds no empty workgroup
     const int nr = (int)min(span * 16, a.n_out - row0);
     for (int t = 0; t < TT; ++t)
       for (int i = threadIdx.x; i < nr; i += (int)blockDim.x)

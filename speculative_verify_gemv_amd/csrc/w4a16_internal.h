@@ -56,6 +56,9 @@ inline int64_t tiled_tile_bytes(int64_t G) {
 // ring running from one tile into the next (all of K staged once).
 constexpr int kDot = 1, kSplit = 2, kShared = 3, kRun = 4;
 constexpr int kDotMaxT = 8;  // the dot kernel is built for T <= 8
+// Run workgroups whose activations fit but leave no room for their outputs
+// take K in slices, so that the outputs are still collected in LDS.
+constexpr bool kSlicedRuns = true;
 
 // Matrix-core tile choice: shape, 16-row tiles per wave, waves per workgroup.
 struct Tile {

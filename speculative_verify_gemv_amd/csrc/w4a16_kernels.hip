@@ -240,9 +240,15 @@ static void plan_shared(GemvArgs& a, int T, int rt, int nwv, Plan* p) {
   p->grid = cdiv(a.n_out, 16LL * nwv * rt);
 }
 
-// Run tiling: nwv waves of nt whole tiles each; all of K staged once (as a
-// shared workgroup with sk = G), so it needs the activations to fit
-// (shared_cap) and eight scales per load.  Returns false otherwise.
+// Run tiling: nwv waves of nt whole tiles each, eight scales per load, all
+// of K staged at once (shared_cap); returns false otherwise.  On the tiled
+// layout, when all of K fits but leaves no room for the output block below,
+// K goes in slices of sk groups (a multiple of the ring) and the partial
+// sums stay in the block from slice to slice (27B-class body pass at T = 13
+// and 16: +5 points against whole-K runs storing per tile).  Activations
+// that do not fit at all are not sliced into runs: the down projection
+// (K = 17,408) lost 4-5 points at T = 3-12 that way against the shared
+// workgroups a grouped launch runs for it.
 //
 // When the LDS share still holds them behind the staged activations, the
 // workgroup's T x 16*nt*nwv outputs are collected there and written at its
@@ -254,16 +260,28 @@ static void plan_shared(GemvArgs& a, int T, int rt, int nwv, Plan* p) {
 // pass gains 1-2 points at T = 3-8 and about 4 at T = 9-10.
 static bool plan_run(GemvArgs& a, int T, int nt, int nwv, Plan* p) {
   if (!a.vec_scales) return false;
-  const int64_t xs_bytes = (int64_t)T * ring_groups(a.G) * kGroup * 2;
-  if (xs_bytes > shared_cap(nwv)) return false;
+  const int64_t cap = shared_cap(nwv);
+  const int64_t row_bytes = (int64_t)T * kGroup * 2;          // one staged group of every token row
+  const int64_t out_bytes = (int64_t)T * nwv * nt * 16 * 4;  // fp32 outputs of the workgroup's rows
+  const int64_t whole = ring_groups(a.G) * row_bytes;
+  int sk = a.G;
+  bool collect = whole + out_bytes <= cap;
+  if (!collect) {
+    const int slice = cap > out_bytes ? (int)((cap - out_bytes) / row_bytes) / kRing * kRing : 0;
+    if (a.tiled && kSlicedRuns && whole <= cap && slice >= kRing && slice < a.G) {
+      sk = slice;
+      collect = true;
+    } else if (whole > cap) {
+      return false;
+    }
+  }
   a.nw = nwv;
   a.gpw = a.G;
-  a.sk = a.G;
-  a.xs_stride = ring_groups(a.G) * kGroup;
+  a.sk = sk;
+  a.xs_stride = ring_groups(sk) * kGroup;
   a.wave_lds = 0;
   a.run_tiles = nt;
-  const int64_t out_bytes = (int64_t)T * nwv * nt * 16 * 4;  // fp32 outputs of the workgroup's rows
-  const bool collect = xs_bytes + out_bytes <= shared_cap(nwv);  // xs_bytes: a multiple of 16
+  const int64_t xs_bytes = ring_groups(sk) * row_bytes;  // a multiple of 16
   a.fin_offset = collect ? (int)xs_bytes : 0;
   p->lds = std::max((int)(collect ? xs_bytes + out_bytes : xs_bytes), nwv * T * 8);
   p->threads = nwv * 64;

@@ -1,22 +1,26 @@
 """GPU parity of workgroups that collect their outputs in LDS.
 
-A run workgroup (several whole tiles per wave, all of K staged once) keeps
-its outputs in LDS behind the staged activations and writes them token row
-by token row when all its waves are done, if its LDS share holds both;
-otherwise each tile's outputs are stored as the tile completes.  These
-cases reach both sides of that rule: ragged row counts (the last
-workgroup's block clipped to n_out); K = 9,216 at T = 4 (activations and
-outputs fill an eight-wave workgroup's 80 KB exactly) against K = 9,472
-(the activations alone fill it); K = 8,192 at T = 8 in sixteen-wave
-workgroups (160 KB exactly) against K = 8,320; T from 1 to 16 under the
-grouped launch's own run shapes and forced ones; gathered rows with invalid
-ids (NaN outputs through the block) with the argmax, the argmax without
-scores; a guard word after every output buffer to catch a write past it.
-Shared workgroups (every wave its own tiles over all of K) of a grouped
-launch, from two token rows, pass their outputs through the staging area
-once every wave is done, when it holds them: the grouped cases also force
-shared shapes (one tile per wave, and four in the row-major kernels).  Expected values come only
-from the oracle.
+A run workgroup (several whole tiles per wave) keeps its outputs in LDS
+behind the staged activations and writes them token row by token row when
+all its waves are done.  If all of K and the block do not fit its LDS
+share together, on the tiled layout it stages K in slices that leave room
+for the block and carries the partial sums there from slice to slice; in
+the row-major kernels each tile's outputs are stored as the tile
+completes.  These cases reach every side of that rule: ragged row counts
+(the last workgroup's block clipped to n_out); K = 9,216 at T = 4
+(activations and outputs fill an eight-wave workgroup's 80 KB exactly)
+against K = 9,472 (the activations alone fill it); K = 8,192 at T = 8 in
+sixteen-wave workgroups (160 KB exactly) against K = 8,320; K = 5,120 from
+T = 13; T from 1 to 16 under the grouped launch's own run shapes and
+forced ones; gathered rows with invalid ids (NaN outputs through the
+block) with the argmax, the argmax without scores; a slice whose
+activations miss every fp16 window (the exact bf16 loop) beside one that
+keeps the fp16 form; a guard word after every output buffer to catch a
+write past it.  Shared workgroups (every wave its own tiles over all of K)
+of a grouped launch, from two token rows, pass their outputs through the
+staging area once every wave is done, when it holds them: the grouped
+cases also force shared shapes (one tile per wave, and four in the
+row-major kernels).  Expected values come only from the oracle.
 """
 import numpy as np
 import pytest
@@ -59,7 +63,7 @@ def rows_of(N, seed):
 
 @pytest.mark.parametrize("tiled", [True, False])
 @pytest.mark.parametrize("tile", [None, "run,4,8", "run,1,8", "run,3,16", "run,2,4", "shared,1,16", "shared,4,4"])
-@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8, 9, 12, 16])
+@pytest.mark.parametrize("T", [1, 2, 3, 4, 5, 8, 9, 12, 13, 16])
 def test_grouped_runs_collect_outputs(w4, tiled, tile, T):
     shapes = [(17, 128), (300, 5120), (1100, 1280), (4099, 1280), (2000, 9216), (700, 9472)]
     probs, refs, bufs = [], [], []
@@ -123,3 +127,30 @@ def test_gathered_runs_bad_ids_and_argmax(w4, T):
         assert np.array_equal(av, np.nanmax(y, axis=1)), "argmax value is not the best score"
         _, am2, av2 = w4.head_gather_tiled(tw, dev(x), row_ids=dev(ids), scores=False, argmax=True)
         assert np.array_equal(host(am2), am) and np.array_equal(host(av2), av), "argmax without scores differs"
+
+
+@pytest.mark.parametrize("T", [13, 16])
+def test_sliced_runs_mixed_level_forms(w4, T):
+    """K = 5,120 at T = 13 and 16 (tiled) runs in two slices; a value of
+    2^-60 in group 2 of token row 0, some 75 binades below the row's largest
+    values, leaves the first slice no fp16 window (bf16 levels) while the
+    second keeps the fp16 form."""
+    N, K = 1100, 5120
+    tid = 9300 + T
+    p, s, pd, sd = weight_dev(tid, N, K)
+    x = synth.activations(tid, T, K).copy()
+    x[0, 300] = 0x2180  # 2^-60
+    rows = rows_of(N, tid)
+    y_ref, a_ref = oracle.gather(rows, p, s, x)
+    tw = w4.repack_tiled(pd, sd)
+    say(f"sliced runs mixed forms single T={T}")
+    buf, y = guarded_output(T, N)
+    with forced_tile(w4, "run,4,16"):
+        w4.matmul_tiled(tw, dev(x), out=y)
+    assert_parity(host(y)[:, rows], y_ref, a_ref, f"sliced single T={T}")
+    check_guard(buf, T, N, f"sliced single T={T}")
+    say(f"sliced runs mixed forms grouped T={T}")
+    buf2, y2 = guarded_output(T, N)
+    w4.Batch([(tw, None, dev(x), y2)], T).run()
+    assert_parity(host(y2)[:, rows], y_ref, a_ref, f"sliced grouped T={T}")
+    check_guard(buf2, T, N, f"sliced grouped T={T}")

@@ -190,8 +190,8 @@ static_assert(sizeof(ArgmaxRecord) == 32 && sizeof(w4a16::GemvArgs) == 144, "bat
 // and +1.0 points against runs of six tiles).  From T = 7 sixteen waves,
 // one workgroup a CU, whose LDS holds both up to T = 11 (at T = 8: +1.7-2.3
 // points against eight waves of six, which must store per tile; at T = 9-10
-// about +4), and at T = 12 runs of three tiles, which still fit (+2); from
-// T = 13 no run short enough to make room pays (two tiles at T = 13: -2).
+// about +4); from T = 12 their runs take K in slices to keep the outputs in
+// LDS (at T = 12 +0.9 points against runs of three tiles, which fit whole).
 // Every problem row-major: up to T = 2 shared workgroups of two 16-row
 // tiles per wave, four waves at T = 1 and eight at T = 2 (27B-class body
 // pass: 75.3% of 8 TB/s at T = 2 against 70.7% for four waves of four
@@ -204,7 +204,7 @@ static_assert(sizeof(ArgmaxRecord) == 32 && sizeof(w4a16::GemvArgs) == 144, "bat
 w4a16::Tile batch_tile(int T, bool all_tiled, bool all_row, int64_t kmax) {
   w4a16::Tile t;
   if ((all_tiled || all_row) && T > 2)
-    t = w4a16::Tile{w4a16::kRun, T == 12 ? 3 : 4, T <= 6 ? 8 : 16};
+    t = w4a16::Tile{w4a16::kRun, 4, T <= 6 ? 8 : 16};
   else if (all_tiled)
     t = w4a16::Tile{w4a16::kShared, 1, w4a16::shared_waves(T, kmax)};
   else if (all_row)
